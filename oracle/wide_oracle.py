@@ -1,0 +1,251 @@
+"""Dense CPU oracle of WIDE's masked dynamic-width execution (test infrastructure).
+
+TEST INFRASTRUCTURE ONLY: see ``oracle/__init__.py`` for who may use it.
+
+Sources (the pages about "WIDE: Boosting Adaptive LLM Inference via Token-level
+Dynamic Width Pruning"):
+
+* [abstract]     the English abstract (arxivdaily.com, insight.artgrammer.co.kr and
+                 franklineh.com pages): each token picks attention-head groups and
+                 FFN-channel groups; the co-design splits acceleration into mask
+                 reordering, block-level skipping and intra-block skipping.
+* [gist §2A]     gist.science technical summary (zh and ja), section 2.A
+                 "fine-grained token-level routing": attention units are head
+                 groups aligned with GQA; FFN units are contiguous channel groups of
+                 the intermediate dimension D'; a router gives one binary
+                 execute/skip decision per group.
+* [gist §2B]     same page, section 2.B "unified mask-reordering preprocessing": per
+                 routing group the binary mask is sorted along the token dimension M
+                 so active tokens form a contiguous prefix, with no explicit
+                 gather-scatter and no token-specific sparse tensors.
+* [gist §2C]     same page, section 2.C "pruning-kernel co-design": a tile whose
+                 token block is inactive for a group exits (l=0); inactive load
+                 packets (l=1) and MMA fragments (l=2) are skipped.  Skipping only
+                 removes work whose result is unused, so the masked layer equals
+                 the dense layer with dropped groups zeroed.
+
+Readings taken where the pages are silent (each one is listed again in the
+design notes):
+
+* R1 reorder tie rule: the sort is stable, ascending token index inside the
+  active and inactive classes.  Bits pack little-endian (group 64w+j -> bit j of
+  word w); nonzero mask bytes mean "keep"; tile unions are ascending, padded -1.
+* R2 FFN activation: Llama SwiGLU, H = silu(X W_gate^T) * (X W_up^T), no bias.
+* R3 GQA index map: query head h belongs to KV group h // r, r = n_q / n_kv.
+* R4 attention over kept groups: a query kept in group g attends to the earlier
+  (and its own) tokens that also kept g; tokens that skipped g have no K/V in g.
+  Scale 1/sqrt(head_dim).  Outputs of skipped groups are exactly zero.
+* R5 decode: the K/V cache of each (sequence, group) holds kv_len valid entries;
+  a new token kept in g attends to all of them plus itself and is appended at slot
+  kv_len; a skipped (sequence, group) writes nothing and outputs zero.
+* R6 layer: pre-norm Llama block, RMSNorm x / sqrt(mean(x^2) + eps) * gamma,
+  rotate-half RoPE with angle pos * theta^(-2i/hd), no frequency scaling.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+
+def _f(a, dtype):
+    return np.asarray(a, dtype=dtype)
+
+
+# ------------------------------------------------------------------ reorder
+
+def mask_reorder(mask, tile_m: int) -> dict:
+    """Mask reordering [gist §2B], with reading R1.
+
+    For every group g the tokens are sorted on the binary key (0 = kept first),
+    stably, which puts the active tokens in a contiguous prefix of length
+    ``group_count[g]``.  ``group_rank`` is the inverse permutation.  For every tile
+    of ``tile_m`` consecutive tokens, ``tile_groups`` lists (ascending) the groups
+    that at least one token of the tile keeps; a (tile, group) block outside that
+    list is the block that [gist §2C] l=0 skips.
+    """
+    m = np.asarray(mask) != 0
+    if m.ndim != 2:
+        raise ValueError("mask must be [T, n_groups]")
+    if tile_m < 1:
+        raise ValueError("tile_m must be >= 1")
+    T, n = m.shape
+    nw = (n + 63) // 64
+
+    packed = np.zeros((T, nw), np.uint64)
+    for g in range(n):
+        w, j = divmod(g, 64)
+        packed[:, w] |= m[:, g].astype(np.uint64) << np.uint64(j)
+
+    count = np.zeros(n, np.int32)
+    perm = np.zeros((n, T), np.int32)
+    rank = np.zeros((n, T), np.int32)
+    for g in range(n):
+        active = [t for t in range(T) if m[t, g]]
+        inactive = [t for t in range(T) if not m[t, g]]
+        count[g] = len(active)
+        order = active + inactive
+        perm[g] = order
+        for i, t in enumerate(order):
+            rank[g, t] = i
+
+    n_tiles = (T + tile_m - 1) // tile_m
+    tile_count = np.zeros(n_tiles, np.int32)
+    tile_groups = np.full((n_tiles, n), -1, np.int32)
+    for i in range(n_tiles):
+        rows = m[i * tile_m:min(T, (i + 1) * tile_m)]
+        kept = [g for g in range(n) if rows[:, g].any()]
+        tile_count[i] = len(kept)
+        tile_groups[i, :len(kept)] = kept
+
+    return dict(packed=packed, group_count=count, group_perm=perm, group_rank=rank,
+                tile_count=tile_count, tile_groups=tile_groups)
+
+
+# ---------------------------------------------------------------------- FFN
+
+def _silu(a):
+    with np.errstate(over="ignore"):
+        return a / (1.0 + np.exp(-a))
+
+
+def ffn_masked(X, mask, W_gate, W_up, W_down, *, dtype=np.float64, return_h: bool = False):
+    """Masked SwiGLU FFN: FFN-channel groups of D' [gist §2A], reading R2.
+
+    X [T, d]; mask [T, n]; W_gate, W_up, W_down [F, d] with group g owning
+    channels gG .. gG+G-1 (G = F / n).  Dense gate/up, SwiGLU, zero the channels
+    of every group the token drops, then the down projection Y = H @ W_down.
+    """
+    X, Wg, Wu, Wd = (_f(a, dtype) for a in (X, W_gate, W_up, W_down))
+    m = np.asarray(mask) != 0
+    T, d = X.shape
+    F = Wg.shape[0]
+    n = m.shape[1]
+    if F % n:
+        raise ValueError("d_ff must be a multiple of n_groups")
+    G = F // n
+    A = X @ Wg.T
+    B = X @ Wu.T
+    H = _silu(A) * B
+    H = np.where(np.repeat(m, G, axis=1), H, 0.0)
+    Y = H @ Wd
+    return (Y, H) if return_h else Y
+
+
+# ---------------------------------------------------------------- attention
+
+def rmsnorm(x, gamma, eps: float, *, dtype=np.float64):
+    """RMSNorm of the Llama block (reading R6)."""
+    x = _f(x, dtype)
+    return x / np.sqrt(np.mean(x * x, axis=-1, keepdims=True) + eps) * _f(gamma, dtype)
+
+
+def rope(x, pos, theta: float, *, dtype=np.float64):
+    """Rotate-half RoPE (reading R6).  x [..., T, heads, hd], pos [T]."""
+    x = _f(x, dtype)
+    hd = x.shape[-1]
+    half = hd // 2
+    inv = float(theta) ** (-(2.0 * np.arange(half, dtype=dtype)) / hd)
+    ang = np.asarray(pos, dtype)[:, None] * inv[None, :]          # [T, half]
+    c = np.cos(ang)[:, None, :]
+    s = np.sin(ang)[:, None, :]
+    x1, x2 = x[..., :half], x[..., half:]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def _softmax_rows(S):
+    S = S - S.max(axis=-1, keepdims=True)
+    P = np.exp(S)
+    return P / P.sum(axis=-1, keepdims=True)
+
+
+def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
+                rope_theta: float = 0.0, decode: bool = False, K_cache=None, V_cache=None,
+                kv_len: int = 0, dtype=np.float64, return_o: bool = False):
+    """Masked attention sublayer: GQA-aligned head groups [gist §2A], readings R3-R5.
+
+    One group = one KV head and its r = n_q / n_kv query heads.  Projections are
+    computed densely and the columns of dropped groups zeroed; the attention core
+    follows R4 (prefill, positions 0..T-1, causal) or R5 (decode, one new token per
+    sequence at position kv_len); Y = O @ Wo with O zero in dropped groups.
+
+    Prefill returns Y [T, d].  Decode returns (Y, K_new, V_new) where K_new, V_new
+    [B, n_kv, hd] are the (roped) keys/values appended at slot kv_len for the kept
+    (sequence, group) pairs (zero rows elsewhere; nothing is appended there).
+    """
+    X, Wq, Wk, Wv, Wo = (_f(a, dtype) for a in (X, Wq, Wk, Wv, Wo))
+    keep = np.asarray(mask) != 0                                  # [T, n_kv]
+    T = X.shape[0]
+    hd = head_dim
+    if n_q % n_kv:
+        raise ValueError("n_q must be a multiple of n_kv")
+    r = n_q // n_kv
+    Eq = np.repeat(keep, r * hd, axis=1)
+    Ek = np.repeat(keep, hd, axis=1)
+    Q = np.where(Eq, X @ Wq.T, 0.0).reshape(T, n_q, hd)
+    K = np.where(Ek, X @ Wk.T, 0.0).reshape(T, n_kv, hd)
+    V = np.where(Ek, X @ Wv.T, 0.0).reshape(T, n_kv, hd)
+    pos = np.full(T, kv_len) if decode else np.arange(T)
+    if rope_theta:
+        Q = rope(Q, pos, rope_theta, dtype=dtype)
+        K = rope(K, pos, rope_theta, dtype=dtype)
+    scale = 1.0 / np.sqrt(hd)
+    O = np.zeros((T, n_q, hd), dtype)
+
+    if not decode:
+        tt = np.arange(T)
+        causal = tt[None, :] <= tt[:, None]                       # key s <= query t
+        for h in range(n_q):
+            g = h // r
+            rows = keep[:, g]
+            if not rows.any():
+                continue
+            allowed = causal[rows] & keep[None, :, g]
+            S = (Q[rows, h] @ K[:, g].T) * scale
+            P = _softmax_rows(np.where(allowed, S, -np.inf))
+            O[rows, h] = P @ V[:, g]
+        Y = O.reshape(T, n_q * hd) @ Wo
+        return (Y, O) if return_o else Y
+
+    Kc = _f(K_cache, dtype)
+    Vc = _f(V_cache, dtype)
+    for b in range(T):
+        for g in range(n_kv):
+            if not keep[b, g]:
+                continue
+            keys = np.concatenate([Kc[b, g, :kv_len], K[b, g][None]], axis=0)
+            vals = np.concatenate([Vc[b, g, :kv_len], V[b, g][None]], axis=0)
+            for h in range(g * r, (g + 1) * r):
+                p = _softmax_rows(((keys @ Q[b, h]) * scale)[None])[0]
+                O[b, h] = p @ vals
+    Y = O.reshape(T, n_q * hd) @ Wo
+    out = (Y, K, V)
+    return out + (O,) if return_o else out
+
+
+# -------------------------------------------------------------------- layer
+
+def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q: int, n_kv: int, head_dim: int,
+                 n_ffn: int, rope_theta: float, eps: float, decode: bool = False,
+                 K_cache=None, V_cache=None, kv_len: int = 0, dtype=np.float64,
+                 return_parts: bool = False):
+    """Pre-norm decoder layer with masked attention and masked FFN (reading R6).
+
+    u = RMSNorm(x; rms1); h = x + Attn(u; attn_mask); w = RMSNorm(h; rms2);
+    y = h + FFN(w; ffn_mask).  W holds rms1, rms2, Wq, Wk, Wv, Wo, W_gate, W_up,
+    W_down.  ``n_ffn`` is the FFN group count (the mask's width).
+    """
+    X = _f(X, dtype)
+    if np.asarray(ffn_mask).shape[1] != n_ffn:
+        raise ValueError("ffn_mask width must equal n_ffn")
+    u = rmsnorm(X, W["rms1"], eps, dtype=dtype)
+    att = attn_masked(u, attn_mask, W["Wq"], W["Wk"], W["Wv"], W["Wo"], n_q=n_q, n_kv=n_kv,
+                      head_dim=head_dim, rope_theta=rope_theta, decode=decode,
+                      K_cache=K_cache, V_cache=V_cache, kv_len=kv_len, dtype=dtype)
+    a = att[0] if decode else att
+    h = X + a
+    w = rmsnorm(h, W["rms2"], eps, dtype=dtype)
+    f = ffn_masked(w, ffn_mask, W["W_gate"], W["W_up"], W["W_down"], dtype=dtype)
+    y = h + f
+    parts = dict(u=u, a=a, h=h, w=w, f=f)
+    if decode:
+        parts.update(K_new=att[1], V_new=att[2])
+    return (y, parts) if return_parts else y
