@@ -1,0 +1,185 @@
+/*
+ * wide.h - C ABI of libwide: WIDE masked dynamic-width execution on MI355X (gfx950).
+ *
+ * What is computed (the pages about "WIDE: Boosting Adaptive LLM Inference via
+ * Token-level Dynamic Width Pruning"):
+ *   - every token keeps or skips each attention-head group and each FFN-channel
+ *     group through a binary mask (gist.science technical summary, section 2.A);
+ *   - the masks are reordered per group along the token dimension so the active
+ *     tokens form a contiguous prefix (section 2.B);
+ *   - kernels skip tiles, loads and matrix fragments that no kept token needs
+ *     (section 2.C; the abstract's "hardware-agnostic block-level skipping" and
+ *     "hardware-dependent intra-block skipping").
+ * The result equals the dense layer with the dropped groups zeroed.
+ *
+ * Conventions shared by every entry point
+ *   - All pointers except `cfg`/`W` structs are DEVICE pointers, owned by the
+ *     caller, 16-byte aligned.  The library allocates nothing and keeps no state.
+ *   - bf16 tensors are passed as uint16_t bit patterns, row-major, contiguous.
+ *   - Masks are uint8 [T, n_groups] row-major; any nonzero byte means "keep".
+ *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work:
+ *     no host synchronisation, no device-to-host copy.  Faults during execution
+ *     surface at the caller's next synchronisation.
+ *   - Arguments are validated on the host before anything is enqueued; a call that
+ *     returns an error has launched nothing.  T == 0 is a no-op returning WIDE_OK.
+ *   - Inputs are never written.  Outputs must not alias inputs.  Every element of
+ *     every output is written on success; dropped groups give an exact 0.
+ *   - `flags` must be 0.
+ *   - Concurrent calls are safe on different streams with distinct workspaces.
+ */
+#ifndef WIDE_H
+#define WIDE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum {
+  WIDE_OK = 0,
+  WIDE_EINVAL = 1,        /* NULL / misaligned pointer, inconsistent sizes       */
+  WIDE_EUNSUPPORTED = 2,  /* valid but outside what the kernels implement         */
+  WIDE_EWORKSPACE = 3,    /* workspace smaller than the matching *_workspace()   */
+  WIDE_EHIP = 4           /* a HIP launch reported an error                       */
+};
+enum { WIDE_PREFILL = 0, WIDE_DECODE = 1 };
+
+/* Limits: 1 <= n_groups <= 256, T <= 65536 (prefill) / 256 (decode). */
+#define WIDE_MAX_GROUPS 256
+#define WIDE_MAX_TOKENS 65536
+#define WIDE_MAX_DECODE_BATCH 256
+
+const char* wide_status_string(int status);
+int wide_version(void);
+
+/*
+ * wide_mask_reorder - mask reordering (gist.science technical summary §2.B).
+ *
+ * For each group g, the tokens are sorted stably on "dropped" (kept first):
+ *   group_count[g]     number of tokens that keep g
+ *   group_perm[g, i]   token at position i (i < count: kept, ascending; then the
+ *                      dropped ones, ascending) - a permutation of 0..T-1
+ *   group_rank[g, t]   position of token t in group_perm[g]  (inverse permutation)
+ * and for every tile of tile_m consecutive tokens (the last one may be short):
+ *   tile_count[i]      number of groups kept by at least one token of tile i
+ *   tile_groups[i, j]  those groups, ascending, then -1 up to n_groups
+ * packed[t, w] bit j = mask[t, 64w + j] != 0 (little-endian words).
+ *
+ * mask        [T, n_groups] uint8              (input)
+ * packed      [T, ceil(n_groups/64)] uint64    (output)
+ * group_count [n_groups] int32;  group_perm, group_rank [n_groups, T] int32
+ * tile_count  [ceil(T/tile_m)] int32;  tile_groups [ceil(T/tile_m), n_groups] int32
+ * 1 <= tile_m <= 1024.  Results are bit-exact and deterministic.
+ */
+int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m,
+                      uint64_t* packed, int32_t* group_count, int32_t* group_perm,
+                      int32_t* group_rank, int32_t* tile_count, int32_t* tile_groups,
+                      void* stream);
+
+/*
+ * wide_pack_kmajor - lay out a K-masked weight for the library (a pure permutation).
+ *
+ * W [n_groups * G, d_model] is the mathematical matrix of Y = H @ W (FFN down:
+ * W_down [d_ff, d_model]; attention out: Wo [n_q*head_dim, d_model], which is
+ * o_proj.weight transposed).  W_packed [n_groups, d_model, G] holds, for every
+ * group g, the block W[gG:(g+1)G, :] transposed, so each group's block is one
+ * contiguous region with the contraction index innermost.  Run once at weight load.
+ */
+int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16_t* W_packed,
+                     void* stream);
+
+/*
+ * wide_ffn_masked - masked SwiGLU FFN (gist.science §2.A: contiguous channel groups
+ * of the intermediate dimension D'; one binary execute/skip bit per token and group).
+ *
+ *   Y[t] = sum over groups g kept by t of  silu(X[t] Wg_g^T) * (X[t] Wu_g^T) @ Wd_g
+ *
+ * X             [T, d_model] bf16
+ * mask          [T, n_groups] uint8
+ * W_gate, W_up  [d_ff, d_model] bf16 (nn.Linear layout; group g = rows gG..gG+G-1)
+ * W_down_packed [n_groups, d_model, G] bf16 (wide_pack_kmajor of W_down [d_ff, d_model])
+ * Y             [T, d_model] bf16 (a token that keeps no group gets exact zeros)
+ * mode          WIDE_PREFILL (any T) or WIDE_DECODE (T = batch <= 256, weight streaming)
+ * Needs G = d_ff / n_groups a multiple of 64 and d_model a multiple of 64.
+ */
+size_t wide_ffn_masked_workspace(int T, int d_model, int d_ff, int n_groups, int mode);
+int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_gate,
+                    const uint16_t* W_up, const uint16_t* W_down_packed, int T, int d_model,
+                    int d_ff, int n_groups, int mode, uint16_t* Y, void* workspace,
+                    size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * wide_attn_proj_masked - masked attention sublayer over GQA-aligned head groups
+ * (gist.science §2.A).  Group g = KV head g and query heads g*r .. g*r+r-1,
+ * r = n_q_heads / n_kv_heads.  A token that drops g has no q/k/v in g and gets a
+ * zero output for g's heads; a token that keeps g attends (causally) to the tokens
+ * that also keep g.  Scale 1/sqrt(head_dim).  RoPE (rotate-half, angle
+ * pos * theta^(-2i/head_dim)) when rope_theta > 0.
+ *
+ * X        [T, d_model] bf16
+ * mask     [T, n_kv_heads] uint8
+ * Wq       [n_q*hd, d_model], Wk, Wv [n_kv*hd, d_model] bf16 (nn.Linear layout)
+ * Wo_packed[n_kv, d_model, r*hd] bf16 (wide_pack_kmajor of Wo [n_q*hd, d_model])
+ * Y        [T, d_model] bf16 = O @ Wo
+ * Prefill: positions 0..T-1; K_cache/V_cache may be NULL and are not touched.
+ * Decode : T = batch; one new token per sequence at position kv_len (0 <= kv_len <
+ *          kv_cap); K_cache, V_cache [T, n_kv, kv_cap, hd] bf16 hold kv_len valid
+ *          entries per (sequence, group).  For every kept (sequence, group) the new
+ *          roped k and v are written to slot kv_len; other slots are not written.
+ * Needs head_dim == 128.
+ */
+typedef struct {
+  int n_q_heads;
+  int n_kv_heads;
+  int head_dim;
+  float rope_theta; /* 0 = no RoPE */
+} wide_attn_cfg;
+
+size_t wide_attn_proj_masked_workspace(int T, int d_model, const wide_attn_cfg* cfg, int mode);
+int wide_attn_proj_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
+                          const uint16_t* Wk, const uint16_t* Wv, const uint16_t* Wo_packed,
+                          int T, int d_model, const wide_attn_cfg* cfg, int mode,
+                          uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
+                          uint16_t* Y, void* workspace, size_t workspace_bytes, uint32_t flags,
+                          void* stream);
+
+/*
+ * wide_layer_masked - one pre-norm decoder layer with both masked sublayers:
+ *   u = RMSNorm(x; rms1), h = x + Attn(u; attn_mask), w = RMSNorm(h; rms2),
+ *   y = h + FFN(w; ffn_mask),  RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma.
+ * Weights as in the two calls above; rms1, rms2 [d_model] bf16.  Same prefill /
+ * decode and cache rules as wide_attn_proj_masked.  With all-zero masks y == x.
+ */
+typedef struct {
+  const uint16_t* rms1;
+  const uint16_t* Wq;
+  const uint16_t* Wk;
+  const uint16_t* Wv;
+  const uint16_t* Wo_packed;
+  const uint16_t* rms2;
+  const uint16_t* W_gate;
+  const uint16_t* W_up;
+  const uint16_t* W_down_packed;
+} wide_layer_weights;
+
+typedef struct {
+  int d_model;
+  int d_ff;
+  int n_ffn_groups;
+  wide_attn_cfg attn;
+  float rms_eps;
+} wide_layer_cfg;
+
+size_t wide_layer_masked_workspace(int T, const wide_layer_cfg* cfg, int mode);
+int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_mask,
+                      const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
+                      uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap, uint16_t* Y,
+                      void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* WIDE_H */

@@ -1,0 +1,18 @@
+"""WIDE masked dynamic-width execution on MI355X (gfx950).
+
+A thin Python binding over ``libwide.so``, the C ABI declared in
+``include/wide.h``.  The functions here only marshal arguments (torch tensors
+-> device pointers, shapes, the current HIP stream) and raise on a non-zero
+status; every step of the computation runs in the HIP kernels of the library.
+There is no fallback: without the built library, or without a GPU, the calls
+raise.
+"""
+from .binding import (LIB_PATH, WideError, attn_proj_masked, attn_proj_masked_workspace,
+                      ffn_masked, ffn_masked_workspace, layer_masked, layer_masked_workspace,
+                      lib, mask_reorder, pack_kmajor, WIDE_DECODE, WIDE_PREFILL)
+
+__all__ = [
+    "LIB_PATH", "WideError", "lib", "mask_reorder", "pack_kmajor", "ffn_masked",
+    "ffn_masked_workspace", "attn_proj_masked", "attn_proj_masked_workspace", "layer_masked",
+    "layer_masked_workspace", "WIDE_PREFILL", "WIDE_DECODE",
+]

@@ -1,0 +1,257 @@
+"""ctypes binding of libwide (include/wide.h).  Argument marshalling only."""
+from __future__ import annotations
+
+import ctypes as C
+import os
+
+import torch
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwide.so")
+
+WIDE_OK, WIDE_EINVAL, WIDE_EUNSUPPORTED, WIDE_EWORKSPACE, WIDE_EHIP = range(5)
+WIDE_PREFILL, WIDE_DECODE = 0, 1
+
+_p = C.c_void_p
+_i = C.c_int
+_sz = C.c_size_t
+
+
+class WideAttnCfg(C.Structure):
+    _fields_ = [("n_q_heads", _i), ("n_kv_heads", _i), ("head_dim", _i), ("rope_theta", C.c_float)]
+
+
+class WideLayerWeights(C.Structure):
+    _fields_ = [(k, _p) for k in ("rms1", "Wq", "Wk", "Wv", "Wo_packed", "rms2", "W_gate", "W_up",
+                                  "W_down_packed")]
+
+
+class WideLayerCfg(C.Structure):
+    _fields_ = [("d_model", _i), ("d_ff", _i), ("n_ffn_groups", _i), ("attn", WideAttnCfg),
+                ("rms_eps", C.c_float)]
+
+
+_SIGS = {
+    "wide_status_string": ([_i], C.c_char_p),
+    "wide_version": ([], _i),
+    "wide_mask_reorder": ([_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
+    "wide_pack_kmajor": ([_p, _i, _i, _i, _p, _p], _i),
+    "wide_ffn_masked_workspace": ([_i, _i, _i, _i, _i], _sz),
+    "wide_ffn_masked": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+    "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i], _sz),
+    "wide_attn_proj_masked": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _i, _p, _p,
+                               _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+    "wide_layer_masked_workspace": ([_i, C.POINTER(WideLayerCfg), _i], _sz),
+    "wide_layer_masked": ([_p, _p, _p, C.POINTER(WideLayerWeights), C.POINTER(WideLayerCfg), _i, _i,
+                           _p, _p, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+}
+
+_lib = None
+
+
+def lib() -> C.CDLL:
+    """Load libwide.so (built by ``__graft_entry__.build()``); raises if absent."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"libwide.so not built ({LIB_PATH}); run __graft_entry__.build()")
+        L = C.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            f = getattr(L, name)
+            f.argtypes = args
+            f.restype = res
+        _lib = L
+    return _lib
+
+
+class WideError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        self.status = status
+        msg = lib().wide_status_string(status).decode()
+        super().__init__(f"{fn} failed: status {status} ({msg})")
+
+
+def _check(fn: str, status: int):
+    if status != WIDE_OK:
+        raise WideError(fn, status)
+
+
+def _ptr(t):
+    return None if t is None else C.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return C.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _dev(t: torch.Tensor, dtype, name: str):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a CUDA (HIP) tensor")
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return t
+
+
+def _mode(mode) -> int:
+    if mode in ("prefill", WIDE_PREFILL):
+        return WIDE_PREFILL
+    if mode in ("decode", WIDE_DECODE):
+        return WIDE_DECODE
+    raise ValueError(f"mode must be 'prefill' or 'decode', got {mode!r}")
+
+
+def _workspace(nbytes: int, device, workspace):
+    if workspace is not None:
+        return workspace
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+# ------------------------------------------------------------------ reorder
+
+def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None) -> dict:
+    """wide_mask_reorder on a uint8 [T, n] device mask; returns the six outputs."""
+    _dev(mask, torch.uint8, "mask")
+    T, n = mask.shape
+    dev = mask.device
+    nw = (n + 63) // 64
+    nt = -(-T // tile_m) if T else 0
+    if out is None:
+        out = dict(
+            packed=torch.empty((T, nw), dtype=torch.int64, device=dev),
+            group_count=torch.empty(n, dtype=torch.int32, device=dev),
+            group_perm=torch.empty((n, T), dtype=torch.int32, device=dev),
+            group_rank=torch.empty((n, T), dtype=torch.int32, device=dev),
+            tile_count=torch.empty(nt, dtype=torch.int32, device=dev),
+            tile_groups=torch.empty((nt, n), dtype=torch.int32, device=dev),
+        )
+    st = lib().wide_mask_reorder(_ptr(mask), T, n, tile_m, _ptr(out["packed"]),
+                                 _ptr(out["group_count"]), _ptr(out["group_perm"]),
+                                 _ptr(out["group_rank"]), _ptr(out["tile_count"]),
+                                 _ptr(out["tile_groups"]), _stream())
+    _check("wide_mask_reorder", st)
+    return out
+
+
+def pack_kmajor(W: torch.Tensor, n_groups: int, out: torch.Tensor | None = None) -> torch.Tensor:
+    """wide_pack_kmajor: W [n*G, d] bf16 -> [n, d, G]."""
+    _dev(W, torch.bfloat16, "W")
+    K, d = W.shape
+    if K % n_groups:
+        raise ValueError("rows of W must be a multiple of n_groups")
+    G = K // n_groups
+    if out is None:
+        out = torch.empty((n_groups, d, G), dtype=torch.bfloat16, device=W.device)
+    _check("wide_pack_kmajor", lib().wide_pack_kmajor(_ptr(W), n_groups, G, d, _ptr(out), _stream()))
+    return out
+
+
+# ---------------------------------------------------------------------- FFN
+
+def ffn_masked_workspace(T, d_model, d_ff, n_groups, mode="prefill") -> int:
+    return int(lib().wide_ffn_masked_workspace(T, d_model, d_ff, n_groups, _mode(mode)))
+
+
+def ffn_masked(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out=None, workspace=None):
+    """wide_ffn_masked.  X [T, d] bf16, mask [T, n] uint8, W_gate/W_up [F, d] bf16,
+    W_down_packed [n, d, G] bf16 (see pack_kmajor).  Returns Y [T, d] bf16."""
+    for t, nm in ((X, "X"), (W_gate, "W_gate"), (W_up, "W_up"), (W_down_packed, "W_down_packed")):
+        _dev(t, torch.bfloat16, nm)
+    _dev(mask, torch.uint8, "mask")
+    T, d = X.shape
+    F = W_gate.shape[0]
+    n = mask.shape[1]
+    if mask.shape[0] != T or W_gate.shape != (F, d) or W_up.shape != (F, d):
+        raise ValueError("shape mismatch")
+    if W_down_packed.shape != (n, d, F // n):
+        raise ValueError("W_down_packed must be [n_groups, d_model, d_ff / n_groups]")
+    m = _mode(mode)
+    ws_bytes = ffn_masked_workspace(T, d, F, n, m)
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_ffn_masked(_ptr(X), _ptr(mask), _ptr(W_gate), _ptr(W_up), _ptr(W_down_packed),
+                               T, d, F, n, m, _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_ffn_masked", st)
+    return Y
+
+
+# ---------------------------------------------------------------- attention
+
+def _attn_cfg(n_q, n_kv, hd, theta):
+    return WideAttnCfg(n_q, n_kv, hd, float(theta))
+
+
+def attn_proj_masked_workspace(T, d_model, n_q, n_kv, head_dim=128, rope_theta=0.0,
+                               mode="prefill") -> int:
+    cfg = _attn_cfg(n_q, n_kv, head_dim, rope_theta)
+    return int(lib().wide_attn_proj_masked_workspace(T, d_model, C.byref(cfg), _mode(mode)))
+
+
+def attn_proj_masked(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, head_dim=128, rope_theta=0.0,
+                     mode="prefill", K_cache=None, V_cache=None, kv_len=0, out=None,
+                     workspace=None):
+    """wide_attn_proj_masked.  Returns Y [T, d] bf16 (decode also writes the caches)."""
+    for t, nm in ((X, "X"), (Wq, "Wq"), (Wk, "Wk"), (Wv, "Wv"), (Wo_packed, "Wo_packed")):
+        _dev(t, torch.bfloat16, nm)
+    _dev(mask, torch.uint8, "mask")
+    m = _mode(mode)
+    T, d = X.shape
+    kv_cap = 0
+    if m == WIDE_DECODE:
+        _dev(K_cache, torch.bfloat16, "K_cache")
+        _dev(V_cache, torch.bfloat16, "V_cache")
+        kv_cap = K_cache.shape[2]
+    cfg = _attn_cfg(n_q, n_kv, head_dim, rope_theta)
+    ws_bytes = int(lib().wide_attn_proj_masked_workspace(T, d, C.byref(cfg), m))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_attn_proj_masked(_ptr(X), _ptr(mask), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                     _ptr(Wo_packed), T, d, C.byref(cfg), m, _ptr(K_cache),
+                                     _ptr(V_cache), kv_len, kv_cap, _ptr(Y), _ptr(ws), ws.numel(),
+                                     0, _stream())
+    _check("wide_attn_proj_masked", st)
+    return Y
+
+
+# -------------------------------------------------------------------- layer
+
+def _layer_cfg(d, F, n_ffn, n_q, n_kv, hd, theta, eps):
+    return WideLayerCfg(d, F, n_ffn, _attn_cfg(n_q, n_kv, hd, theta), float(eps))
+
+
+def layer_masked_workspace(T, d_model, d_ff, n_ffn, n_q, n_kv, head_dim=128, rope_theta=500000.0,
+                           eps=1e-5, mode="prefill") -> int:
+    cfg = _layer_cfg(d_model, d_ff, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
+    return int(lib().wide_layer_masked_workspace(T, C.byref(cfg), _mode(mode)))
+
+
+def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, head_dim=128,
+                 rope_theta=500000.0, eps=1e-5, mode="prefill", K_cache=None, V_cache=None,
+                 kv_len=0, out=None, workspace=None):
+    """wide_layer_masked.  W: rms1, rms2 [d]; Wq, Wk, Wv; Wo_packed; W_gate, W_up;
+    W_down_packed (all bf16 device tensors)."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(attn_mask, torch.uint8, "attn_mask")
+    _dev(ffn_mask, torch.uint8, "ffn_mask")
+    keys = ("rms1", "Wq", "Wk", "Wv", "Wo_packed", "rms2", "W_gate", "W_up", "W_down_packed")
+    for k in keys:
+        _dev(W[k], torch.bfloat16, k)
+    m = _mode(mode)
+    T, d = X.shape
+    F = W["W_gate"].shape[0]
+    n_ffn = ffn_mask.shape[1]
+    kv_cap = 0
+    if m == WIDE_DECODE:
+        _dev(K_cache, torch.bfloat16, "K_cache")
+        _dev(V_cache, torch.bfloat16, "V_cache")
+        kv_cap = K_cache.shape[2]
+    cfg = _layer_cfg(d, F, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
+    wts = WideLayerWeights(*[W[k].data_ptr() for k in keys])
+    ws_bytes = int(lib().wide_layer_masked_workspace(T, C.byref(cfg), m))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_layer_masked(_ptr(X), _ptr(attn_mask), _ptr(ffn_mask), C.byref(wts),
+                                 C.byref(cfg), T, m, _ptr(K_cache), _ptr(V_cache), kv_len, kv_cap,
+                                 _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_layer_masked", st)
+    return Y

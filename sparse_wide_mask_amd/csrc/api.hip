@@ -1,0 +1,185 @@
+// C ABI of libwide: argument validation, workspace carving and launch order.
+// Every check runs on the host before anything is enqueued.
+#include <stddef.h>
+#include <stdint.h>
+
+#include "../../include/wide.h"
+#include "internal.h"
+
+namespace {
+
+using namespace wide;
+
+bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t kAlign = 256;
+size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Bump allocator over the caller's workspace.  With base == nullptr it only
+// measures, which is how the *_workspace() queries are answered.
+struct Carver {
+  char* base;
+  size_t used = 0;
+  explicit Carver(void* b) : base(static_cast<char*>(b)) {}
+  template <class T>
+  T* take(size_t count) {
+    T* p = base ? reinterpret_cast<T*>(base + used) : nullptr;
+    used += round_up(count * sizeof(T));
+    return p;
+  }
+};
+
+int launch_status() {
+  hipError_t e = hipGetLastError();
+  return e == hipSuccess ? WIDE_OK : WIDE_EHIP;
+}
+
+hipStream_t as_stream(void* s) { return static_cast<hipStream_t>(s); }
+
+int ceil_div(int a, int b) { return (a + b - 1) / b; }
+
+ReorderView carve_reorder(Carver& c, int T, int n, int tile_m, bool with_rank) {
+  ReorderView v;
+  const int nw = ceil_div(n, 64);
+  v.packed = c.take<uint64_t>((size_t)T * nw);
+  v.count = c.take<int32_t>(n);
+  v.perm = c.take<int32_t>((size_t)n * T);
+  v.rank = with_rank ? c.take<int32_t>((size_t)n * T) : nullptr;
+  v.tile_m = tile_m;
+  v.tile_count = c.take<int32_t>(ceil_div(T, tile_m));
+  v.tile_groups = c.take<int32_t>((size_t)ceil_div(T, tile_m) * n);
+  return v;
+}
+
+void run_reorder(const uint8_t* mask, int T, int n, const ReorderView& v, hipStream_t s) {
+  launch_reorder(mask, T, n, v.tile_m, v.packed, v.count, v.perm, v.rank, v.tile_count,
+                 v.tile_groups, s);
+}
+
+// ---------------------------------------------------------------- FFN
+
+int ffn_check(int T, int d, int F, int n, int mode) {
+  if (T < 0 || d <= 0 || F <= 0 || n <= 0) return WIDE_EINVAL;
+  if (mode != WIDE_PREFILL && mode != WIDE_DECODE) return WIDE_EINVAL;
+  if (F % n) return WIDE_EINVAL;
+  if (n > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
+  if (mode == WIDE_DECODE) return WIDE_EUNSUPPORTED;
+  const int G = F / n;
+  if (G % 64 || d % 64) return WIDE_EUNSUPPORTED;
+  return WIDE_OK;
+}
+
+struct FfnWs {
+  ReorderView rv;
+  uint16_t* H = nullptr;
+};
+
+FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
+  (void)d;
+  (void)mode;
+  FfnWs w;
+  w.rv = carve_reorder(c, T, n, ffn_down_tile_m(), false);
+  w.H = c.take<uint16_t>((size_t)T * F);
+  return w;
+}
+
+int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const uint16_t* Wu,
+            const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
+            uint16_t* Y, const FfnWs& w, hipStream_t s) {
+  (void)mode;
+  run_reorder(mask, T, n, w.rv, s);
+  launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
+  return WIDE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* wide_status_string(int status) {
+  switch (status) {
+    case WIDE_OK: return "ok";
+    case WIDE_EINVAL: return "invalid argument";
+    case WIDE_EUNSUPPORTED: return "unsupported shape or mode";
+    case WIDE_EWORKSPACE: return "workspace too small";
+    case WIDE_EHIP: return "HIP launch error";
+    default: return "unknown status";
+  }
+}
+
+int wide_version(void) { return 1; }
+
+int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m, uint64_t* packed,
+                      int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                      int32_t* tile_count, int32_t* tile_groups, void* stream) {
+  if (T < 0 || n_groups < 1 || tile_m < 1 || tile_m > 1024) return WIDE_EINVAL;
+  if (n_groups > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(mask) || !aligned16(packed) || !aligned16(group_count) ||
+      !aligned16(group_perm) || !aligned16(group_rank) || !aligned16(tile_count) ||
+      !aligned16(tile_groups))
+    return WIDE_EINVAL;
+  (void)hipGetLastError();
+  launch_reorder(mask, T, n_groups, tile_m, packed, group_count, group_perm, group_rank,
+                 tile_count, tile_groups, as_stream(stream));
+  return launch_status();
+}
+
+int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16_t* W_packed,
+                     void* stream) {
+  if (n_groups < 1 || G < 1 || d_model < 1) return WIDE_EINVAL;
+  if (!aligned16(W) || !aligned16(W_packed) || W == W_packed) return WIDE_EINVAL;
+  if (G % 64 || d_model % 64 || n_groups > 65535) return WIDE_EUNSUPPORTED;
+  (void)hipGetLastError();
+  launch_pack_kmajor(W, n_groups, G, d_model, W_packed, as_stream(stream));
+  return launch_status();
+}
+
+size_t wide_ffn_masked_workspace(int T, int d_model, int d_ff, int n_groups, int mode) {
+  if (ffn_check(T, d_model, d_ff, n_groups, mode) != WIDE_OK) return 0;
+  Carver c(nullptr);
+  carve_ffn(c, T, d_model, d_ff, n_groups, mode);
+  return c.used;
+}
+
+int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_gate,
+                    const uint16_t* W_up, const uint16_t* W_down_packed, int T, int d_model,
+                    int d_ff, int n_groups, int mode, uint16_t* Y, void* workspace,
+                    size_t workspace_bytes, uint32_t flags, void* stream) {
+  int st = ffn_check(T, d_model, d_ff, n_groups, mode);
+  if (st != WIDE_OK) return st;
+  if (flags != 0) return WIDE_EINVAL;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(mask) || !aligned16(W_gate) || !aligned16(W_up) ||
+      !aligned16(W_down_packed) || !aligned16(Y) || (void*)Y == (void*)X)
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_ffn(probe, T, d_model, d_ff, n_groups, mode);
+  if (!aligned16(workspace)) return probe.used ? WIDE_EINVAL : WIDE_OK;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  FfnWs w = carve_ffn(c, T, d_model, d_ff, n_groups, mode);
+  (void)hipGetLastError();
+  ffn_run(X, mask, W_gate, W_up, W_down_packed, T, d_model, d_ff, n_groups, mode, nullptr, Y, w,
+          as_stream(stream));
+  return launch_status();
+}
+
+size_t wide_attn_proj_masked_workspace(int, int, const wide_attn_cfg*, int) { return 0; }
+
+int wide_attn_proj_masked(const uint16_t*, const uint8_t*, const uint16_t*, const uint16_t*,
+                          const uint16_t*, const uint16_t*, int, int, const wide_attn_cfg*, int,
+                          uint16_t*, uint16_t*, int, int, uint16_t*, void*, size_t, uint32_t,
+                          void*) {
+  return WIDE_EUNSUPPORTED;
+}
+
+size_t wide_layer_masked_workspace(int, const wide_layer_cfg*, int) { return 0; }
+
+int wide_layer_masked(const uint16_t*, const uint8_t*, const uint8_t*, const wide_layer_weights*,
+                      const wide_layer_cfg*, int, int, uint16_t*, uint16_t*, int, int, uint16_t*,
+                      void*, size_t, uint32_t, void*) {
+  return WIDE_EUNSUPPORTED;
+}
+
+}  // extern "C"

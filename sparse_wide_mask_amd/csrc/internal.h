@@ -1,0 +1,31 @@
+// Internal launch interfaces between the C ABI (api.hip) and the kernel files.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace wide {
+
+// Device buffers produced by the mask reordering, as the kernels consume them.
+struct ReorderView {
+  uint64_t* packed = nullptr;     // [T, nw]
+  int32_t* count = nullptr;       // [n]
+  int32_t* perm = nullptr;        // [n, T]
+  int32_t* rank = nullptr;        // [n, T] (may be null when no kernel needs it)
+  int32_t* tile_count = nullptr;  // [ceil(T / tile_m)]
+  int32_t* tile_groups = nullptr; // [ceil(T / tile_m), n]
+  int tile_m = 0;
+};
+
+void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
+                    int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                    int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
+
+void launch_pack_kmajor(const uint16_t* W, int n, int G, int d, uint16_t* Wp, hipStream_t s);
+
+int ffn_down_tile_m();
+void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
+                        const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
+                        const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
+
+}  // namespace wide

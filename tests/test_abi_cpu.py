@@ -1,0 +1,66 @@
+"""Host-side checks of the C ABI (no GPU needed).
+
+The library loads, exports every entry point include/wide.h declares, answers
+workspace queries and rejects bad arguments before touching the GPU.
+"""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "wide.h")
+
+
+@pytest.fixture(scope="module")
+def L():
+    from sparse_wide_mask_amd import binding
+    if not os.path.exists(binding.LIB_PATH):
+        pytest.skip("libwide.so not built")
+    return binding.lib()
+
+
+def declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"^(?:const char\*|int|size_t)\s+(wide_\w+)\(", src, re.M)))
+
+
+def test_header_declares_the_contract():
+    names = declared()
+    for fn in ("wide_mask_reorder", "wide_ffn_masked", "wide_attn_proj_masked", "wide_layer_masked"):
+        assert fn in names
+
+
+def test_every_declared_symbol_is_exported(L):
+    for name in declared():
+        assert hasattr(L, name), name
+
+
+def test_status_strings(L):
+    assert L.wide_status_string(0) == b"ok"
+    assert L.wide_status_string(3) == b"workspace too small"
+    assert L.wide_version() >= 1
+
+
+def test_ffn_workspace_queries(L):
+    from sparse_wide_mask_amd import binding as b
+    ws = b.ffn_masked_workspace(4096, 3072, 8192, 64)
+    assert ws >= 4096 * 8192 * 2                      # H is held in the workspace
+    assert b.ffn_masked_workspace(64, 256, 1000, 16) == 0   # d_ff % n != 0 -> invalid -> 0
+    assert b.ffn_masked_workspace(64, 256, 16 * 96, 16) == 0  # G = 96: unsupported -> 0
+
+
+def test_validation_before_any_launch(L):
+    # NULL pointers and bad shapes are rejected on the host: no GPU is touched.
+    z = C.c_void_p(0)
+    assert L.wide_mask_reorder(z, 10, 4, 4, z, z, z, z, z, z, z) == 1
+    assert L.wide_mask_reorder(z, 10, 0, 4, z, z, z, z, z, z, z) == 1
+    assert L.wide_mask_reorder(z, 10, 300, 4, z, z, z, z, z, z, z) == 2
+    assert L.wide_mask_reorder(z, 0, 4, 4, z, z, z, z, z, z, z) == 0     # T == 0: no-op
+    assert L.wide_ffn_masked(z, z, z, z, z, 8, 256, 1000, 16, 0, z, z, 0, 0, z) == 1
+    assert L.wide_ffn_masked(z, z, z, z, z, 8, 256, 1024, 16, 0, z, z, 0, 0, z) == 1
+    assert L.wide_ffn_masked(z, z, z, z, z, 8, 200, 1024, 16, 0, z, z, 0, 0, z) == 2
+    assert L.wide_ffn_masked(z, z, z, z, z, 8, 256, 1024, 16, 7, z, z, 0, 0, z) == 1
+    assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 0, z) == 0
+    assert L.wide_pack_kmajor(z, 4, 64, 256, z, z) == 1
