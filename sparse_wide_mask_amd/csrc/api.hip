@@ -58,11 +58,16 @@ void run_reorder(const uint8_t* mask, int T, int n, const ReorderView& v, hipStr
 
 // ---------------------------------------------------------------- FFN
 
+// Kernels address operands with 32-bit byte offsets below the skip sentinel.
+constexpr int64_t kMaxBytes = 0x7fffff00LL;
+bool fits(int64_t a, int64_t b) { return a * b * 2 <= kMaxBytes; }
+
 int ffn_check(int T, int d, int F, int n, int mode) {
   if (T < 0 || d <= 0 || F <= 0 || n <= 0) return WIDE_EINVAL;
   if (mode != WIDE_PREFILL && mode != WIDE_DECODE) return WIDE_EINVAL;
   if (F % n) return WIDE_EINVAL;
   if (n > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
+  if (!fits(T, d) || !fits(F, d) || !fits(T, F)) return WIDE_EUNSUPPORTED;
   if (mode == WIDE_DECODE) return WIDE_EUNSUPPORTED;
   const int G = F / n;
   if (G % 64 || d % 64) return WIDE_EUNSUPPORTED;

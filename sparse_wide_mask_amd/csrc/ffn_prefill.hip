@@ -21,17 +21,22 @@
 
 namespace wide {
 
-// Work-group id -> (group, rest) so that the tiles of one group land on one XCD
-// (work-groups are dealt to the 8 XCDs round-robin) and share its L2.
-WIDE_DEV void xcd_group_split(int bid, int n_groups, int per_group, int& g, int& rest) {
+// Work-group id -> (group, row tile, column tile) of the up projection.  Work-groups
+// are dealt to the 8 XCDs round-robin; when n_groups is a multiple of 8, XCD x
+// takes the groups x, x+8, ... and walks them in 4-row-tile x 8-column blocks:
+// tiles of one group share its weight rows, and the same row-tile index of
+// different groups gathers tokens from the same stretch of X.
+WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& mt, int& nt) {
+  int c;
   if ((n_groups & 7) == 0) {
-    const int x = bid & 7, l = bid >> 3;
-    g = (l / per_group) * 8 + x;
-    rest = l % per_group;
+    const int x = bid & 7;
+    block_raster(bid >> 3, mtiles, (n_groups >> 3) * ntn, 4, 8, mt, c);
+    g = x + 8 * (c / ntn);
   } else {
-    g = bid / per_group;
-    rest = bid % per_group;
+    block_raster(bid, mtiles, n_groups * ntn, 4, 8, mt, c);
+    g = c / ntn;
   }
+  nt = c % ntn;
 }
 
 template <int BM, int BN>
@@ -42,13 +47,12 @@ __global__ void __launch_bounds__(256, 1)
                    int mtiles, int ntn, uint16_t* __restrict__ H) {
   using C = TileCfg<BM, BN>;
   constexpr int BNH = BN / 2;  // channels per tile (gate and up each)
-  __shared__ __attribute__((aligned(16))) uint16_t sA[C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[C::LDS_B];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::LDS_A];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::LDS_B];
   __shared__ int sTok[BM];
 
-  int g, rest;
-  xcd_group_split(blockIdx.x, n, mtiles * ntn, g, rest);
-  const int mt = rest % mtiles, nt = rest / mtiles;
+  int g, mt, nt;
+  up_tile(blockIdx.x, n, mtiles, ntn, g, mt, nt);
   const int cnt = gcount[g];
   const int row0 = mt * BM;
   if (row0 >= cnt) return;  // l=0: no kept token left in this tile
@@ -58,22 +62,25 @@ __global__ void __launch_bounds__(256, 1)
   for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gperm[(size_t)g * T + row0 + r] : -1;
   __syncthreads();
 
-  // Chunk i of this thread: tile row (tid >> 3) + 32 i, 16-byte column kc = tid & 7.
+  // Chunk i of this thread: tile row crow + 32 i, 16-byte column kc8.
   const int crow = tid >> 3, kc8 = (tid & 7) * 8;
   const int dst0 = crow * kLdsLd + kc8;
-  int aOff[C::A_CHUNKS];
+  const rsrc_t rX = make_rsrc(X, (uint32_t)T * d * 2u);
+  const rsrc_t rG = make_rsrc(Wg, (uint32_t)F * d * 2u);
+  const rsrc_t rU = make_rsrc(Wu, (uint32_t)F * d * 2u);
+  uint32_t aOff[C::A_CHUNKS];
 #pragma unroll
   for (int i = 0; i < C::A_CHUNKS; ++i) {
     const int tok = sTok[crow + 32 * i];
-    aOff[i] = tok >= 0 ? tok * d + kc8 : -1;
+    aOff[i] = tok >= 0 ? (uint32_t)(tok * d + kc8) * 2u : (uint32_t)kSkip;  // l=1: no load
   }
-  const uint16_t* bSrc[C::B_CHUNKS];
+  // B row crow + 32 i: slab (i % (WN/32)) of wave column (32 i) / WN; even slabs gate, odd up.
+  uint32_t bOff[C::B_CHUNKS];
 #pragma unroll
   for (int i = 0; i < C::B_CHUNKS; ++i) {
-    const int nrow = crow + 32 * i;
-    const int w = nrow / C::WN, local = nrow % C::WN, blk = local >> 5;
-    const int ch = nt * BNH + w * (C::WN / 2) + (blk >> 1) * 32 + (local & 31);
-    bSrc[i] = ((blk & 1) ? Wu : Wg) + (size_t)(g * G + ch) * d + kc8;
+    const int w = (32 * i) / C::WN, blk = i % (C::WN / 32);
+    const int ch = nt * BNH + w * (C::WN / 2) + (blk >> 1) * 32 + crow;
+    bOff[i] = (uint32_t)((g * G + ch) * d + kc8) * 2u;
   }
 
   uint32_t rb_live = 0;
@@ -83,30 +90,39 @@ __global__ void __launch_bounds__(256, 1)
 
   u32x4 ra[C::A_CHUNKS], rbuf[C::B_CHUNKS];
   auto gload = [&](int k0) {
+    const uint32_t kb = (uint32_t)k0 * 2u;
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = aOff[i] >= 0 ? ld16(X + aOff[i] + k0) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = ldbuf16(rX, aOff[i] + kb);
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) rbuf[i] = ld16(bSrc[i] + k0);
+    for (int i = 0; i < C::B_CHUNKS; ++i) rbuf[i] = ldbuf16((i & 1) ? rU : rG, bOff[i] + kb);
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA + dst0 + 32 * i * kLdsLd, ra[i]);
+    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA[buf] + dst0 + 32 * i * kLdsLd, ra[i]);
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB + dst0 + 32 * i * kLdsLd, rbuf[i]);
+    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB[buf] + dst0 + 32 * i * kLdsLd, rbuf[i]);
   };
 
   WaveAcc<BM, BN> acc;
   acc.zero();
   const int nk = d / kBK;
   gload(0);
-  lstore();
+  lstore(0);
   __syncthreads();
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload((kt + 1) * kBK);
-    acc.sweep(sA, sB, wm, wn, lane, rb_live);
-    __syncthreads();
-    if (kt + 1 < nk) {
-      lstore();
+  if (rb_live == C::kAllRows) {  // every row block of this wave holds kept rows
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload((kt + 1) * kBK);
+      acc.sweep_full(sA[cur], sB[cur], wm, wn, lane);
+      if (kt + 1 < nk) lstore(cur ^ 1);
+      __syncthreads();
+    }
+  } else {  // tail tile of the group: l=2 skips the empty row blocks
+    for (int kt = 0; kt < nk; ++kt) {
+      const int cur = kt & 1;
+      if (kt + 1 < nk) gload((kt + 1) * kBK);
+      acc.sweep_masked(sA[cur], sB[cur], wm, wn, lane, rb_live);
+      if (kt + 1 < nk) lstore(cur ^ 1);
       __syncthreads();
     }
   }
@@ -136,12 +152,17 @@ __global__ void __launch_bounds__(256, 1)
                      int nw, int ntn, const uint16_t* __restrict__ residual,
                      uint16_t* __restrict__ Y) {
   using C = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[C::LDS_B];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::LDS_A];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::LDS_B];
   __shared__ uint64_t sBits[BM * 4];
   __shared__ int sGroups[256];
 
-  const int mt = blockIdx.x / ntn, nt = blockIdx.x % ntn;
+  // XCD x takes a contiguous stretch of the block-rasterised tile order.
+  const int mtiles = (T + BM - 1) / BM, n_tiles = mtiles * ntn;
+  const int p = (blockIdx.x & 7) * ((n_tiles + 7) >> 3) + (blockIdx.x >> 3);
+  if (p >= n_tiles) return;
+  int mt, nt;
+  block_raster(p, mtiles, ntn, 4, 8, mt, nt);
   const int t0 = mt * BM, rows = min(BM, T - t0), n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int ng = tcount[mt];
@@ -152,11 +173,13 @@ __global__ void __launch_bounds__(256, 1)
   for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
   __syncthreads();
 
-  // Chunk i of this thread: tile row (tid >> 3) + 32 i, 16-byte column kc = tid & 7.
+  // Chunk i of this thread: tile row crow + 32 i, 16-byte column kc8.
   const int crow = tid >> 3, kc8 = (tid & 7) * 8;
   const int dst0 = crow * kLdsLd + kc8;
-  const size_t aBase = (size_t)(t0 + crow) * F + kc8;
-  const size_t bBase = (size_t)(n0 + crow) * G + kc8;
+  const rsrc_t rH = make_rsrc(H, (uint32_t)T * F * 2u);
+  const rsrc_t rW = make_rsrc(Wdp, (uint32_t)F * d * 2u);
+  const uint32_t aBase = (uint32_t)((t0 + crow) * F + kc8) * 2u;
+  const uint32_t bBase = (uint32_t)((n0 + crow) * G + kc8) * 2u;
 
   const int kpg = G / kBK;
   const int nk = ng * kpg;
@@ -165,22 +188,26 @@ __global__ void __launch_bounds__(256, 1)
     const int g = sGroups[it / kpg], kk = (it % kpg) * kBK;
     const uint64_t sel = 1ull << (g & 63);
     const int w = g >> 6;
+    const uint32_t ka = (uint32_t)(g * G + kk) * 2u;
 #pragma unroll
     for (int i = 0; i < C::A_CHUNKS; ++i) {
       const int row = crow + 32 * i;
       const bool keep = row < rows && (sBits[row * 4 + w] & sel);
-      ra[i] = keep ? ld16(H + aBase + (size_t)32 * i * F + g * G + kk) : u32x4{0, 0, 0, 0};
+      // l=1: rows of tokens that dropped g are not fetched (zeros)
+      ra[i] = ldbuf16(rH, keep ? aBase + (uint32_t)(32 * i * F) * 2u + ka : (uint32_t)kSkip);
     }
-    const uint16_t* wb = Wdp + (size_t)g * d * G + bBase + kk;
+    const uint32_t kb = (uint32_t)(g * d * G + kk) * 2u;
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i)
-      rbuf[i] = n0 + crow + 32 * i < d ? ld16(wb + (size_t)32 * i * G) : u32x4{0, 0, 0, 0};
+    for (int i = 0; i < C::B_CHUNKS; ++i) {
+      const bool ok = n0 + crow + 32 * i < d;
+      rbuf[i] = ldbuf16(rW, ok ? bBase + (uint32_t)(32 * i * G) * 2u + kb : (uint32_t)kSkip);
+    }
   };
-  auto lstore = [&]() {
+  auto lstore = [&](int buf) {
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA + dst0 + 32 * i * kLdsLd, ra[i]);
+    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA[buf] + dst0 + 32 * i * kLdsLd, ra[i]);
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB + dst0 + 32 * i * kLdsLd, rbuf[i]);
+    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB[buf] + dst0 + 32 * i * kLdsLd, rbuf[i]);
   };
   // Row blocks of this wave holding at least one token that keeps group g.
   auto live_blocks = [&](int g) {
@@ -200,19 +227,18 @@ __global__ void __launch_bounds__(256, 1)
   acc.zero();
   if (nk > 0) {
     gload(0);
-    lstore();
+    lstore(0);
     __syncthreads();
   }
   uint32_t rb_live = 0;
   for (int it = 0; it < nk; ++it) {
+    const int cur = it & 1;
+    // l=2: 32-row blocks without a token that keeps the group skip their MFMAs
     if (it % kpg == 0) rb_live = live_blocks(sGroups[it / kpg]);
     if (it + 1 < nk) gload(it + 1);
-    acc.sweep(sA, sB, wm, wn, lane, rb_live);
+    acc.sweep_masked(sA[cur], sB[cur], wm, wn, lane, rb_live);
+    if (it + 1 < nk) lstore(cur ^ 1);
     __syncthreads();
-    if (it + 1 < nk) {
-      lstore();
-      __syncthreads();
-    }
   }
 
   // The residual pointer passes through an empty asm here so its loads are not
@@ -238,7 +264,7 @@ __global__ void __launch_bounds__(256, 1)
     }
 }
 
-constexpr int kDownBM = 256, kDownBN = 256;
+constexpr int kDownBM = 256;
 int ffn_down_tile_m() { return kDownBM; }
 
 void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
@@ -258,10 +284,29 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
                                                              n, G, mtiles, ntn, H);
   }
-  // down
-  const int mtiles = (T + kDownBM - 1) / kDownBM, ntn = (d + kDownBN - 1) / kDownBN;
-  ffn_down_prefill<kDownBM, kDownBN><<<mtiles * ntn, 256, 0, s>>>(
-      H, Wdp, rv.packed, rv.tile_count, rv.tile_groups, T, d, F, n, G, nw, ntn, residual, Y);
+  // down: pick the column tile that fills the 256 CUs best (rounds x tile width)
+  const int mtiles = (T + kDownBM - 1) / kDownBM;
+  int best_bn = 256;
+  long best_cost = -1;
+  for (int bn : {256, 192, 128}) {
+    const long tiles = (long)mtiles * ((d + bn - 1) / bn);
+    const long cost = ((tiles + 255) / 256) * bn;
+    if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bn = bn;
+  }
+  const int ntn = (d + best_bn - 1) / best_bn;
+  const int grid = 8 * ((mtiles * ntn + 7) / 8);
+  if (best_bn == 256)
+    ffn_down_prefill<kDownBM, 256><<<grid, 256, 0, s>>>(H, Wdp, rv.packed, rv.tile_count,
+                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                        residual, Y);
+  else if (best_bn == 192)
+    ffn_down_prefill<kDownBM, 192><<<grid, 256, 0, s>>>(H, Wdp, rv.packed, rv.tile_count,
+                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                        residual, Y);
+  else
+    ffn_down_prefill<kDownBM, 128><<<grid, 256, 0, s>>>(H, Wdp, rv.packed, rv.tile_count,
+                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                        residual, Y);
 }
 
 }  // namespace wide
