@@ -159,7 +159,7 @@ def _softmax_rows(S):
 
 def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
                 rope_theta: float = 0.0, decode: bool = False, K_cache=None, V_cache=None,
-                kv_len: int = 0, dtype=np.float64, return_o: bool = False):
+                kv_len: int = 0, dtype=np.float64, return_o: bool = False, rows=None):
     """Masked attention sublayer: GQA-aligned head groups [gist §2A], readings R3-R5.
 
     One group = one KV head and its r = n_q / n_kv query heads.  Projections are
@@ -167,7 +167,9 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
     follows R4 (prefill, positions 0..T-1, causal) or R5 (decode, one new token per
     sequence at position kv_len); Y = O @ Wo with O zero in dropped groups.
 
-    Prefill returns Y [T, d].  Decode returns (Y, K_new, V_new) where K_new, V_new
+    Prefill returns Y [T, d]; with ``rows`` (prefill only) just those query rows are
+    produced, Y [len(rows), d], from the same keys and values.  Decode returns
+    (Y, K_new, V_new) where K_new, V_new
     [B, n_kv, hd] are the (roped) keys/values appended at slot kv_len for the kept
     (sequence, group) pairs (zero rows elsewhere; nothing is appended there).
     """
@@ -180,30 +182,40 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
     r = n_q // n_kv
     Eq = np.repeat(keep, r * hd, axis=1)
     Ek = np.repeat(keep, hd, axis=1)
-    Q = np.where(Eq, X @ Wq.T, 0.0).reshape(T, n_q, hd)
+    if rows is not None and not decode:
+        Q = np.zeros((T, n_q, hd), dtype)
+        R_ = np.asarray(rows)
+        Q[R_] = np.where(Eq[R_], X[R_] @ Wq.T, 0.0).reshape(len(R_), n_q, hd)
+    else:
+        Q = np.where(Eq, X @ Wq.T, 0.0).reshape(T, n_q, hd)
     K = np.where(Ek, X @ Wk.T, 0.0).reshape(T, n_kv, hd)
     V = np.where(Ek, X @ Wv.T, 0.0).reshape(T, n_kv, hd)
     pos = np.full(T, kv_len) if decode else np.arange(T)
     if rope_theta:
-        Q = rope(Q, pos, rope_theta, dtype=dtype)
+        if rows is not None and not decode:
+            R_ = np.asarray(rows)
+            Q[R_] = rope(Q[R_], pos[R_], rope_theta, dtype=dtype)
+        else:
+            Q = rope(Q, pos, rope_theta, dtype=dtype)
         K = rope(K, pos, rope_theta, dtype=dtype)
     scale = 1.0 / np.sqrt(hd)
     O = np.zeros((T, n_q, hd), dtype)
 
     if not decode:
-        tt = np.arange(T)
-        causal = tt[None, :] <= tt[:, None]                       # key s <= query t
+        R = np.arange(T) if rows is None else np.asarray(rows)
+        causal = np.arange(T)[None, :] <= R[:, None]               # key s <= query t
+        OR = np.zeros((len(R), n_q, hd), dtype)
         for h in range(n_q):
             g = h // r
-            rows = keep[:, g]
-            if not rows.any():
+            sel = keep[R, g]
+            if not sel.any():
                 continue
-            allowed = causal[rows] & keep[None, :, g]
-            S = (Q[rows, h] @ K[:, g].T) * scale
+            allowed = causal[sel] & keep[None, :, g]
+            S = (Q[R[sel], h] @ K[:, g].T) * scale
             P = _softmax_rows(np.where(allowed, S, -np.inf))
-            O[rows, h] = P @ V[:, g]
-        Y = O.reshape(T, n_q * hd) @ Wo
-        return (Y, O) if return_o else Y
+            OR[sel, h] = P @ V[:, g]
+        Y = OR.reshape(len(R), n_q * hd) @ Wo
+        return (Y, OR) if return_o else Y
 
     Kc = _f(K_cache, dtype)
     Vc = _f(V_cache, dtype)
@@ -226,12 +238,13 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
 def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q: int, n_kv: int, head_dim: int,
                  n_ffn: int, rope_theta: float, eps: float, decode: bool = False,
                  K_cache=None, V_cache=None, kv_len: int = 0, dtype=np.float64,
-                 return_parts: bool = False):
+                 return_parts: bool = False, rows=None):
     """Pre-norm decoder layer with masked attention and masked FFN (reading R6).
 
     u = RMSNorm(x; rms1); h = x + Attn(u; attn_mask); w = RMSNorm(h; rms2);
     y = h + FFN(w; ffn_mask).  W holds rms1, rms2, Wq, Wk, Wv, Wo, W_gate, W_up,
-    W_down.  ``n_ffn`` is the FFN group count (the mask's width).
+    W_down.  ``n_ffn`` is the FFN group count (the mask's width).  With ``rows``
+    (prefill only) just those token rows of y are produced.
     """
     X = _f(X, dtype)
     if np.asarray(ffn_mask).shape[1] != n_ffn:
@@ -239,11 +252,13 @@ def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q: int, n_kv: int, head_d
     u = rmsnorm(X, W["rms1"], eps, dtype=dtype)
     att = attn_masked(u, attn_mask, W["Wq"], W["Wk"], W["Wv"], W["Wo"], n_q=n_q, n_kv=n_kv,
                       head_dim=head_dim, rope_theta=rope_theta, decode=decode,
-                      K_cache=K_cache, V_cache=V_cache, kv_len=kv_len, dtype=dtype)
+                      K_cache=K_cache, V_cache=V_cache, kv_len=kv_len, dtype=dtype,
+                      rows=None if decode else rows)
     a = att[0] if decode else att
-    h = X + a
+    R = slice(None) if (rows is None or decode) else np.asarray(rows)
+    h = X[R] + a
     w = rmsnorm(h, W["rms2"], eps, dtype=dtype)
-    f = ffn_masked(w, ffn_mask, W["W_gate"], W["W_up"], W["W_down"], dtype=dtype)
+    f = ffn_masked(w, np.asarray(ffn_mask)[R], W["W_gate"], W["W_up"], W["W_down"], dtype=dtype)
     y = h + f
     parts = dict(u=u, a=a, h=h, w=w, f=f)
     if decode:

@@ -97,6 +97,77 @@ int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const ui
   return WIDE_OK;
 }
 
+// ---------------------------------------------------------------- attention
+
+constexpr int kHeadDim = 128;
+
+int attn_check(int T, int d, const wide_attn_cfg* cfg, int mode) {
+  if (!cfg || T < 0 || d <= 0) return WIDE_EINVAL;
+  if (mode != WIDE_PREFILL && mode != WIDE_DECODE) return WIDE_EINVAL;
+  const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  if (nq < 1 || nkv < 1 || nq % nkv || cfg->head_dim < 1) return WIDE_EINVAL;
+  if (!(cfg->rope_theta >= 0.f)) return WIDE_EINVAL;  // also rejects NaN
+  if (cfg->head_dim != kHeadDim || d % 64) return WIDE_EUNSUPPORTED;
+  if (nkv > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
+  const int64_t F = (int64_t)nq * kHeadDim;
+  if (!fits(T, d) || !fits(F, d) || !fits(T, F)) return WIDE_EUNSUPPORTED;
+  if (mode == WIDE_DECODE) return WIDE_EUNSUPPORTED;
+  return WIDE_OK;
+}
+
+struct AttnWs {
+  ReorderView rv;
+  uint16_t *Qc = nullptr, *Kc = nullptr, *Vt = nullptr, *O = nullptr;
+};
+
+AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode) {
+  (void)d;
+  (void)mode;
+  AttnWs w;
+  const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  w.rv = carve_reorder(c, T, nkv, ffn_down_tile_m(), false);
+  w.Qc = c.take<uint16_t>((size_t)nq * T * kHeadDim);
+  w.Kc = c.take<uint16_t>((size_t)nkv * T * kHeadDim);
+  w.Vt = c.take<uint16_t>((size_t)nkv * kHeadDim * vt_pitch(T));
+  w.O = c.take<uint16_t>((size_t)T * nq * kHeadDim);
+  return w;
+}
+
+void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
+              const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
+              const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s) {
+  const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
+  run_reorder(mask, T, nkv, w.rv, s);
+  launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
+  launch_kmask_gemm(w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
+}
+
+// -------------------------------------------------------------------- layer
+
+int layer_check(int T, const wide_layer_cfg* cfg, int mode) {
+  if (!cfg) return WIDE_EINVAL;
+  if (!(cfg->rms_eps >= 0.f)) return WIDE_EINVAL;
+  int st = attn_check(T, cfg->d_model, &cfg->attn, mode);
+  if (st != WIDE_OK) return st;
+  return ffn_check(T, cfg->d_model, cfg->d_ff, cfg->n_ffn_groups, mode);
+}
+
+struct LayerWs {
+  uint16_t *u = nullptr, *h = nullptr;
+  AttnWs attn;
+  FfnWs ffn;
+};
+
+LayerWs carve_layer(Carver& c, int T, const wide_layer_cfg* cfg, int mode) {
+  LayerWs w;
+  const int d = cfg->d_model;
+  w.u = c.take<uint16_t>((size_t)T * d);
+  w.h = c.take<uint16_t>((size_t)T * d);
+  w.attn = carve_attn(c, T, d, &cfg->attn, mode);
+  w.ffn = carve_ffn(c, T, d, cfg->d_ff, cfg->n_ffn_groups, mode);
+  return w;
+}
+
 }  // namespace
 
 extern "C" {
@@ -170,21 +241,80 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
   return launch_status();
 }
 
-size_t wide_attn_proj_masked_workspace(int, int, const wide_attn_cfg*, int) { return 0; }
-
-int wide_attn_proj_masked(const uint16_t*, const uint8_t*, const uint16_t*, const uint16_t*,
-                          const uint16_t*, const uint16_t*, int, int, const wide_attn_cfg*, int,
-                          uint16_t*, uint16_t*, int, int, uint16_t*, void*, size_t, uint32_t,
-                          void*) {
-  return WIDE_EUNSUPPORTED;
+size_t wide_attn_proj_masked_workspace(int T, int d_model, const wide_attn_cfg* cfg, int mode) {
+  if (attn_check(T, d_model, cfg, mode) != WIDE_OK) return 0;
+  Carver c(nullptr);
+  carve_attn(c, T, d_model, cfg, mode);
+  return c.used;
 }
 
-size_t wide_layer_masked_workspace(int, const wide_layer_cfg*, int) { return 0; }
+int wide_attn_proj_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
+                          const uint16_t* Wk, const uint16_t* Wv, const uint16_t* Wo_packed,
+                          int T, int d_model, const wide_attn_cfg* cfg, int mode,
+                          uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
+                          uint16_t* Y, void* workspace, size_t workspace_bytes, uint32_t flags,
+                          void* stream) {
+  (void)K_cache;
+  (void)V_cache;
+  (void)kv_len;
+  (void)kv_cap;
+  int st = attn_check(T, d_model, cfg, mode);
+  if (st != WIDE_OK) return st;
+  if (flags != 0) return WIDE_EINVAL;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(mask) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+      !aligned16(Wo_packed) || !aligned16(Y) || (void*)Y == (void*)X)
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_attn(probe, T, d_model, cfg, mode);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  AttnWs w = carve_attn(c, T, d_model, cfg, mode);
+  (void)hipGetLastError();
+  attn_run(X, mask, Wq, Wk, Wv, Wo_packed, T, d_model, cfg, nullptr, Y, w, as_stream(stream));
+  return launch_status();
+}
 
-int wide_layer_masked(const uint16_t*, const uint8_t*, const uint8_t*, const wide_layer_weights*,
-                      const wide_layer_cfg*, int, int, uint16_t*, uint16_t*, int, int, uint16_t*,
-                      void*, size_t, uint32_t, void*) {
-  return WIDE_EUNSUPPORTED;
+size_t wide_layer_masked_workspace(int T, const wide_layer_cfg* cfg, int mode) {
+  if (layer_check(T, cfg, mode) != WIDE_OK) return 0;
+  Carver c(nullptr);
+  carve_layer(c, T, cfg, mode);
+  return c.used;
+}
+
+int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_mask,
+                      const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
+                      uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap, uint16_t* Y,
+                      void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
+  (void)K_cache;
+  (void)V_cache;
+  (void)kv_len;
+  (void)kv_cap;
+  int st = layer_check(T, cfg, mode);
+  if (st != WIDE_OK) return st;
+  if (flags != 0 || !W) return WIDE_EINVAL;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(attn_mask) || !aligned16(ffn_mask) || !aligned16(Y) ||
+      (void*)Y == (void*)X || !aligned16(W->rms1) || !aligned16(W->rms2) || !aligned16(W->Wq) ||
+      !aligned16(W->Wk) || !aligned16(W->Wv) || !aligned16(W->Wo_packed) ||
+      !aligned16(W->W_gate) || !aligned16(W->W_up) || !aligned16(W->W_down_packed))
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_layer(probe, T, cfg, mode);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  LayerWs w = carve_layer(c, T, cfg, mode);
+  const int d = cfg->d_model;
+  hipStream_t s = as_stream(stream);
+  (void)hipGetLastError();
+  launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
+  attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, X, w.h, w.attn, s);
+  launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
+  ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, cfg->n_ffn_groups,
+          mode, w.h, Y, w.ffn, s);
+  return launch_status();
 }
 
 }  // extern "C"

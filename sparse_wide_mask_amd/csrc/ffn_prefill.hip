@@ -267,6 +267,37 @@ __global__ void __launch_bounds__(256, 1)
 constexpr int kDownBM = 256;
 int ffn_down_tile_m() { return kDownBM; }
 
+// K-masked GEMM Y[t] = sum over groups g kept by t of A[t, gG:(g+1)G] Wp[g]^T
+// (+ residual), A token-major [T, F], Wp packed [n, d, G].  The column tile is
+// chosen to fill the 256 CUs best (rounds x tile width).
+void launch_kmask_gemm(const uint16_t* A, const uint16_t* Wp, const ReorderView& rv, int T, int d,
+                       int F, int n, const uint16_t* residual, uint16_t* Y, hipStream_t s) {
+  const int G = F / n;
+  const int nw = (n + 63) / 64;
+  const int mtiles = (T + kDownBM - 1) / kDownBM;
+  int best_bn = 256;
+  long best_cost = -1;
+  for (int bn : {256, 192, 128}) {
+    const long tiles = (long)mtiles * ((d + bn - 1) / bn);
+    const long cost = ((tiles + 255) / 256) * bn;
+    if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bn = bn;
+  }
+  const int ntn = (d + best_bn - 1) / best_bn;
+  const int grid = 8 * ((mtiles * ntn + 7) / 8);
+  if (best_bn == 256)
+    ffn_down_prefill<kDownBM, 256><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
+                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                        residual, Y);
+  else if (best_bn == 192)
+    ffn_down_prefill<kDownBM, 192><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
+                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                        residual, Y);
+  else
+    ffn_down_prefill<kDownBM, 128><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
+                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                        residual, Y);
+}
+
 void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                         const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
                         const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s) {
@@ -284,29 +315,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
                                                              n, G, mtiles, ntn, H);
   }
-  // down: pick the column tile that fills the 256 CUs best (rounds x tile width)
-  const int mtiles = (T + kDownBM - 1) / kDownBM;
-  int best_bn = 256;
-  long best_cost = -1;
-  for (int bn : {256, 192, 128}) {
-    const long tiles = (long)mtiles * ((d + bn - 1) / bn);
-    const long cost = ((tiles + 255) / 256) * bn;
-    if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bn = bn;
-  }
-  const int ntn = (d + best_bn - 1) / best_bn;
-  const int grid = 8 * ((mtiles * ntn + 7) / 8);
-  if (best_bn == 256)
-    ffn_down_prefill<kDownBM, 256><<<grid, 256, 0, s>>>(H, Wdp, rv.packed, rv.tile_count,
-                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                        residual, Y);
-  else if (best_bn == 192)
-    ffn_down_prefill<kDownBM, 192><<<grid, 256, 0, s>>>(H, Wdp, rv.packed, rv.tile_count,
-                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                        residual, Y);
-  else
-    ffn_down_prefill<kDownBM, 128><<<grid, 256, 0, s>>>(H, Wdp, rv.packed, rv.tile_count,
-                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                        residual, Y);
+  launch_kmask_gemm(H, Wdp, rv, T, d, F, n, residual, Y, s);
 }
 
 }  // namespace wide

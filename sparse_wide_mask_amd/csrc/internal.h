@@ -28,4 +28,18 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
                         const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
                         const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
 
+void launch_kmask_gemm(const uint16_t* A, const uint16_t* Wp, const ReorderView& rv, int T, int d,
+                       int F, int n, const uint16_t* residual, uint16_t* Y, hipStream_t s);
+
+// Row pitch (elements) of the transposed per-group V buffer: T rounded up to 8.
+inline int vt_pitch(int T) { return (T + 7) / 8 * 8; }
+
+void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* Wk,
+                         const uint16_t* Wv, const ReorderView& rv, int T, int d, int n_kv, int r,
+                         float rope_theta, uint16_t* Qc, uint16_t* Kc, uint16_t* Vt, uint16_t* O,
+                         hipStream_t s);
+
+void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, int T, int d, float eps, uint16_t* y,
+                    hipStream_t s);
+
 }  // namespace wide

@@ -1,0 +1,110 @@
+"""GPU parity of wide_layer_masked (pre-norm layer: RMSNorm, masked GQA
+attention with RoPE, residual, RMSNorm, masked SwiGLU FFN, residual)."""
+import numpy as np
+import pytest
+import torch
+
+import sparse_wide_mask_amd as wide
+from oracle import attn_masked, ffn_masked, layer_masked
+from synth import bf16_round
+from synth.workloads import layer_case, layer_8b
+from tests._gpu import TOL, bf16, dev, host, log, nan_bf16, needs_gpu, rel_err, u8
+
+
+def gpu_weights(c):
+    m = c["meta"]
+    return dict(rms1=bf16(c["rms1"]), rms2=bf16(c["rms2"]), Wq=bf16(c["Wq"]), Wk=bf16(c["Wk"]),
+                Wv=bf16(c["Wv"]), Wo_packed=wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]),
+                W_gate=bf16(c["W_gate"]), W_up=bf16(c["W_up"]),
+                W_down_packed=wide.pack_kmajor(bf16(c["W_down"]), m["n_ffn"]))
+
+
+def gpu_layer(c, W=None, **kw):
+    m = c["meta"]
+    T, d = c["X"].shape
+    Y = nan_bf16((T, d))
+    wide.layer_masked(bf16(c["X"]), u8(c["attn_mask"]), u8(c["ffn_mask"]), W or gpu_weights(c),
+                      n_q=m["n_q"], n_kv=m["n_kv"], head_dim=128, rope_theta=m["rope_theta"],
+                      eps=m["eps"], out=Y, **kw)
+    torch.cuda.synchronize()
+    return host(Y)
+
+
+def oracle_layer(c, rows=None, parts=False):
+    m = c["meta"]
+    return layer_masked(c["X"], c["attn_mask"], c["ffn_mask"], c, n_q=m["n_q"], n_kv=m["n_kv"],
+                        head_dim=128, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"], eps=m["eps"],
+                        rows=rows, return_parts=parts)
+
+
+SHAPES = [
+    # T, d, F, n_ffn, n_q, n_kv, keep, kind
+    (200, 256, 1024, 8, 8, 2, 0.5, "router"),
+    (513, 512, 2048, 16, 16, 4, 0.5, "bernoulli"),
+    (300, 256, 1536, 12, 8, 8, 0.75, "clustered"),
+    (64, 256, 1024, 8, 8, 2, 1.0, "ones"),
+]
+
+
+@needs_gpu
+@pytest.mark.parametrize("T,d,F,n_ffn,n_q,n_kv,keep,kind", SHAPES)
+def test_layer_prefill_shapes(T, d, F, n_ffn, n_q, n_kv, keep, kind):
+    dev()
+    log(f"layer prefill T={T} d={d} F={F} n_ffn={n_ffn} n_q={n_q} n_kv={n_kv} {kind}")
+    c = layer_case(f"layer_{T}_{d}_{kind}", T, d, F, n_ffn, n_q, n_kv, 128, keep, kind)
+    got = gpu_layer(c)
+    ref, parts = oracle_layer(c, parts=True)
+    assert rel_err(got, ref) <= TOL
+    # y - x is dominated by the bf16 rounding of y at |x|, so the sublayers are also
+    # checked alone, on the oracle's own (bf16-rounded) intermediate inputs
+    _check_sublayers(c, parts)
+
+
+def _check_sublayers(c, parts, rows=None):
+    m = c["meta"]
+    R = slice(None) if rows is None else rows
+    u = bf16_round(parts["u"].astype(np.float32)) if rows is None else None
+    if u is not None:
+        Ya = nan_bf16(u.shape)
+        wide.attn_proj_masked(bf16(u), u8(c["attn_mask"]), bf16(c["Wq"]), bf16(c["Wk"]),
+                              bf16(c["Wv"]), wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]),
+                              n_q=m["n_q"], n_kv=m["n_kv"], rope_theta=m["rope_theta"], out=Ya)
+        torch.cuda.synchronize()
+        ra = attn_masked(u, c["attn_mask"], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
+                         n_kv=m["n_kv"], head_dim=128, rope_theta=m["rope_theta"])
+        assert rel_err(host(Ya), ra) <= TOL
+    w = bf16_round(parts["w"].astype(np.float32))
+    fm = c["ffn_mask"][R]
+    Yf = nan_bf16(w.shape)
+    wide.ffn_masked(bf16(w), u8(fm), bf16(c["W_gate"]), bf16(c["W_up"]),
+                    wide.pack_kmajor(bf16(c["W_down"]), m["n_ffn"]), out=Yf)
+    torch.cuda.synchronize()
+    assert rel_err(host(Yf), ffn_masked(w, fm, c["W_gate"], c["W_up"], c["W_down"])) <= TOL
+
+
+@needs_gpu
+def test_layer_all_zero_masks_is_identity():
+    dev()
+    c = layer_case("layer_zero", 300, 256, 1024, 8, 8, 2, 128, 0.0, "zeros")
+    got = gpu_layer(c)
+    assert np.array_equal(got, c["X"]), "all-zero masks must return x bit-exactly"
+
+
+@needs_gpu
+def test_layer_prefill_llama31_8b_sampled():
+    """Full Llama-3.1-8B layer shape at T=8192, router top-k masks keeping 50%;
+    the oracle computes 24 sampled token rows (keys/values of all tokens).  The FFN
+    sublayer is also checked alone at this shape on the oracle's intermediate
+    input (bf16-rounded), where the residual does not hide its error."""
+    dev()
+    log("layer prefill 8B T=8192 (sampled)")
+    c = layer_8b(8192)
+    m = c["meta"]
+    rows = np.sort(np.random.default_rng(2).choice(8192, 24, replace=False))
+    rows[0], rows[-1] = 0, 8191
+    got = gpu_layer(c)
+    assert np.all(np.isfinite(got))
+    ref, parts = oracle_layer(c, rows=rows, parts=True)
+    assert rel_err(got[rows], ref) <= TOL
+    # FFN sublayer at the layer shape on w = RMSNorm(h) of the oracle (sampled rows)
+    _check_sublayers(c, parts, rows=rows)

@@ -176,3 +176,17 @@ def test_decode_equals_last_prefill_row():
     Yd = _run(X[L:], np.ones((1, n_kv), np.uint8), W, n_q, n_kv, hd, theta, decode=True,
               K_cache=Kc, V_cache=Vc, kv_len=L)[0]
     np.testing.assert_allclose(Yd[0], Yp[L], rtol=0, atol=_tol(theta, L + 1))
+
+
+@pytest.mark.parametrize("theta", [0.0, 500000.0])
+def test_rows_option_selects_rows(theta):
+    """Sampled query rows equal the same rows of the full computation."""
+    T, d, n_q, n_kv, hd = 37, 24, 8, 2, 8
+    W = _w(d, n_q, n_kv, hd, 13)
+    rr = np.random.default_rng(14)
+    X = rr.standard_normal((T, d))
+    m = (rr.random((T, n_kv)) < 0.5).astype(np.uint8)
+    rows = np.array([0, 3, 17, 36])
+    full = _run(X, m, W, n_q, n_kv, hd, theta)
+    part = _run(X, m, W, n_q, n_kv, hd, theta, rows=rows)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-12)

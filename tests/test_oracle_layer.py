@@ -49,3 +49,17 @@ def test_all_zero_masks_return_input_exactly():
     y = layer_masked(X, np.zeros((T, n_kv), np.uint8), np.zeros((T, n_ffn), np.uint8), W,
                      n_q=n_q, n_kv=n_kv, head_dim=hd, n_ffn=n_ffn, rope_theta=500000.0, eps=1e-5)
     np.testing.assert_array_equal(y, X)
+
+
+def test_rows_option_selects_rows():
+    T, d, F, n_q, n_kv, hd, n_ffn = 23, 32, 64, 4, 2, 8, 8
+    W = _weights(d, F, n_q, n_kv, hd, 6)
+    rr = np.random.default_rng(7)
+    X = rr.standard_normal((T, d))
+    am = (rr.random((T, n_kv)) < 0.5).astype(np.uint8)
+    fm = (rr.random((T, n_ffn)) < 0.5).astype(np.uint8)
+    kw = dict(n_q=n_q, n_kv=n_kv, head_dim=hd, n_ffn=n_ffn, rope_theta=500000.0, eps=1e-5)
+    rows = np.array([1, 5, 22])
+    full = layer_masked(X, am, fm, W, **kw)
+    part = layer_masked(X, am, fm, W, rows=rows, **kw)
+    np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-12)
