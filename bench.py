@@ -1,0 +1,354 @@
+#!/usr/bin/env python3
+"""Benchmark of WIDE masked dynamic-width execution on one MI355X.
+
+A step is one pass of the whole masked path over one batch of synthetic input.
+The default workload is one Llama-3.1-8B-shaped decoder layer in prefill
+(T = 8192 tokens, d_model 4096, 32 query / 8 KV heads of 128, d_ff 14336 in 112
+FFN groups of 128, RoPE theta 5e5), whose masks keep 50% of the attention groups
+and 50% of the FFN groups per token (router top-k on the layer input).  The step
+runs mask reordering, RMSNorm, the masked QKV projections, the causal attention
+core, the masked output projection, RMSNorm, the masked SwiGLU up and down
+projections, and both residual adds.
+
+Output: one JSON line (metric, value = masked tokens/s, ms per step, the
+roofline of the dominant kernel timed by HIP events on the library's stream,
+the same kernels with all-ones masks, per-kernel times, and the CPU oracle
+timed on a bounded sample of the same inputs).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FLOP/clk
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+METRIC = "masked tokens/s + % of MFMA (prefill) / HBM (decode) roofline at 50% sparsity"
+HD = 128
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------- workloads
+
+class LayerPrefill:
+    """Llama-3.1-8B-shaped decoder layer, prefill."""
+
+    def __init__(self, T=8192, keep=0.5, kind="router"):
+        from synth.workloads import layer_8b
+        self.name = "layer_prefill_8b"
+        self.c = layer_8b(T, keep=keep, kind=kind)
+        m = self.c["meta"]
+        self.m = m
+        self.T = T
+        self.config = dict(workload=self.name, T=T, d_model=m["d"], d_ff=m["F"],
+                           n_ffn_groups=m["n_ffn"], n_q_heads=m["n_q"], n_kv_heads=m["n_kv"],
+                           head_dim=HD, rope_theta=m["rope_theta"], keep=keep,
+                           masks=f"{kind} top-k" if kind == "router" else kind)
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        self.W = dict(rms1=bf16(c["rms1"]), rms2=bf16(c["rms2"]), Wq=bf16(c["Wq"]), Wk=bf16(c["Wk"]),
+                      Wv=bf16(c["Wv"]), Wo_packed=wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]),
+                      W_gate=bf16(c["W_gate"]), W_up=bf16(c["W_up"]),
+                      W_down_packed=wide.pack_kmajor(bf16(c["W_down"]), m["n_ffn"]))
+        self.X = bf16(c["X"])
+        self.masks = (u8(c["attn_mask"]), u8(c["ffn_mask"]))
+        self.ones = (torch.ones_like(self.masks[0]), torch.ones_like(self.masks[1]))
+        self.Y = torch.empty_like(self.X)
+        ws = wide.layer_masked_workspace(self.T, m["d"], m["F"], m["n_ffn"], m["n_q"], m["n_kv"],
+                                         HD, m["rope_theta"], m["eps"])
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.wide = wide
+
+    def step(self, ones=False):
+        m = self.m
+        am, fm = self.ones if ones else self.masks
+        self.wide.layer_masked(self.X, am, fm, self.W, n_q=m["n_q"], n_kv=m["n_kv"], head_dim=HD,
+                               rope_theta=m["rope_theta"], eps=m["eps"], out=self.Y,
+                               workspace=self.ws)
+
+    def work(self, ones=False):
+        """Algorithmic FLOPs per launch of each kernel, from the actual masks."""
+        m = self.m
+        d, F, n_ffn, n_q, n_kv = m["d"], m["F"], m["n_ffn"], m["n_q"], m["n_kv"]
+        G, r = F // n_ffn, n_q // n_kv
+        am = np.ones_like(self.c["attn_mask"]) if ones else self.c["attn_mask"]
+        fm = np.ones_like(self.c["ffn_mask"]) if ones else self.c["ffn_mask"]
+        kf = float((fm != 0).sum())
+        cnt = (am != 0).sum(axis=0).astype(np.float64)
+        ka = float(cnt.sum())
+        pairs = float((cnt * (cnt + 1) / 2).sum())       # causal (query, key) pairs per group
+        return {
+            "ffn_up_prefill": 2 * 2 * d * G * kf,          # gate and up
+            "ffn_down": 2 * d * G * kf,
+            "attn_qkv_prefill": 2 * d * (r + 2) * HD * ka,
+            "attn_core_prefill": 4 * HD * r * pairs,       # QK^T and PV
+            "attn_o": 2 * d * r * HD * ka,
+        }
+
+    def oracle_sample(self, S):
+        """The dense oracle on the first S tokens of the same inputs (causal: these
+        rows of the layer output depend on nothing later)."""
+        from oracle import layer_masked
+        c, m = self.c, self.m
+        W = {k: c[k] for k in ("rms1", "rms2", "Wq", "Wk", "Wv", "Wo", "W_gate", "W_up", "W_down")}
+        t0 = time.perf_counter()
+        layer_masked(c["X"][:S], c["attn_mask"][:S], c["ffn_mask"][:S], W, n_q=m["n_q"],
+                     n_kv=m["n_kv"], head_dim=HD, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"],
+                     eps=m["eps"])
+        return time.perf_counter() - t0
+
+
+class FfnPrefill:
+    """Llama-3.2-3B-shaped FFN prefill (T=4096, d=3072, d_ff=8192 in 64 groups)."""
+
+    def __init__(self, T=4096):
+        from synth.workloads import ffn_prefill_3b
+        self.name = "ffn_prefill_3b"
+        self.c = ffn_prefill_3b(T)
+        m = self.c["meta"]
+        self.m, self.T = m, T
+        self.config = dict(workload=self.name, T=T, d_model=m["d"], d_ff=m["F"], n_groups=m["n"],
+                           keep=m["keep"], masks="router top-k")
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        self.X, self.Wg, self.Wu = bf16(c["X"]), bf16(c["W_gate"]), bf16(c["W_up"])
+        self.Wd = wide.pack_kmajor(bf16(c["W_down"]), m["n"])
+        self.mask = u8(c["mask"])
+        self.ones = torch.ones_like(self.mask)
+        self.Y = torch.empty_like(self.X)
+        self.ws = torch.empty(wide.ffn_masked_workspace(self.T, m["d"], m["F"], m["n"]),
+                              dtype=torch.uint8, device="cuda")
+        self.wide = wide
+
+    def step(self, ones=False):
+        self.wide.ffn_masked(self.X, self.ones if ones else self.mask, self.Wg, self.Wu, self.Wd,
+                             out=self.Y, workspace=self.ws)
+
+    def work(self, ones=False):
+        m = self.m
+        G = m["F"] // m["n"]
+        k = float(self.T * m["n"]) if ones else float((self.c["mask"] != 0).sum())
+        return {"ffn_up_prefill": 4 * m["d"] * G * k, "ffn_down": 2 * m["d"] * G * k}
+
+    def oracle_sample(self, S):
+        from oracle import ffn_masked
+        c = self.c
+        t0 = time.perf_counter()
+        ffn_masked(c["X"][:S], c["mask"][:S], c["W_gate"], c["W_up"], c["W_down"])
+        return time.perf_counter() - t0
+
+
+class AttnPrefill:
+    """Llama-3.1-8B-shaped attention sublayer, prefill T=2048, no RoPE."""
+
+    def __init__(self, T=2048):
+        from synth.workloads import attn_prefill_8b
+        self.name = "attn_prefill_8b"
+        self.c = attn_prefill_8b(T)
+        m = self.c["meta"]
+        self.m, self.T = m, T
+        self.config = dict(workload=self.name, T=T, d_model=m["d"], n_q_heads=m["n_q"],
+                           n_kv_heads=m["n_kv"], head_dim=HD, keep=m["keep"], masks="top-k")
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        self.X = bf16(c["X"])
+        self.Wq, self.Wk, self.Wv = bf16(c["Wq"]), bf16(c["Wk"]), bf16(c["Wv"])
+        self.Wo = wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"])
+        self.mask = u8(c["mask"])
+        self.ones = torch.ones_like(self.mask)
+        self.Y = torch.empty_like(self.X)
+        self.ws = torch.empty(wide.attn_proj_masked_workspace(self.T, m["d"], m["n_q"], m["n_kv"]),
+                              dtype=torch.uint8, device="cuda")
+        self.wide = wide
+
+    def step(self, ones=False):
+        m = self.m
+        self.wide.attn_proj_masked(self.X, self.ones if ones else self.mask, self.Wq, self.Wk,
+                                   self.Wv, self.Wo, n_q=m["n_q"], n_kv=m["n_kv"], out=self.Y,
+                                   workspace=self.ws)
+
+    def work(self, ones=False):
+        m = self.m
+        r = m["n_q"] // m["n_kv"]
+        am = np.ones_like(self.c["mask"]) if ones else self.c["mask"]
+        cnt = (am != 0).sum(axis=0).astype(np.float64)
+        ka, pairs = float(cnt.sum()), float((cnt * (cnt + 1) / 2).sum())
+        return {"attn_qkv_prefill": 2 * m["d"] * (r + 2) * HD * ka,
+                "attn_core_prefill": 4 * HD * r * pairs, "attn_o": 2 * m["d"] * r * HD * ka}
+
+    def oracle_sample(self, S):
+        from oracle import attn_masked
+        c, m = self.c, self.m
+        t0 = time.perf_counter()
+        attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
+                    n_kv=m["n_kv"], head_dim=HD)
+        return time.perf_counter() - t0
+
+
+WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
+             "attn_prefill_8b": AttnPrefill}
+
+
+# ------------------------------------------------------------- measurement
+
+def timed(torch, fn, steps, stream):
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
+def traffic_from_profiles(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
+    taken on the current kernel source (its recorded hash must match)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in sorted(rec.get("sources", [])):
+        h.update(open(os.path.join(ROOT, f), "rb").read())
+    if h.hexdigest() != rec.get("source_sha256"):
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        n = [p.get("num_threads", 0) for p in threadpool_info() if p.get("user_api") == "blas"]
+        return max(n) if n else None
+    except Exception:  # pragma: no cover
+        return None
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="layer_prefill_8b", choices=sorted(WORKLOADS))
+    ap.add_argument("--oracle-tokens", type=int, default=None,
+                    help="tokens of the CPU oracle sample (default: a quarter of T)")
+    ap.add_argument("--no-oracle", action="store_true")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py runs on one GPU only: this build measures the single-GPU masked path "
+              "(N > 1 is not supported).", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import sparse_wide_mask_amd as wide
+    from tests._gpu import bf16, u8
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(2)
+    wide.lib()
+
+    log(f"generating {args.workload} inputs")
+    W = WORKLOADS[args.workload]()
+    W.upload(torch, wide, bf16, u8)
+    stream = torch.cuda.current_stream()
+
+    for _ in range(args.warmup):
+        W.step()
+    torch.cuda.synchronize()
+
+    # timed region: K masked steps, kernel launches bracketed by HIP events
+    wide.trace_reset()
+    wide.trace_enable(True)
+    ms = timed(torch, W.step, args.steps, stream)
+    wide.trace_enable(False)
+    kern = wide.trace_collect()
+    wide.trace_reset()
+    log(f"masked: {ms:.3f} ms/step")
+
+    # the same kernels, grid policy and inputs with all-ones masks
+    for _ in range(2):
+        W.step(ones=True)
+    ms_ones = timed(torch, lambda: W.step(ones=True), max(3, args.steps // 2), stream)
+    log(f"all-ones: {ms_ones:.3f} ms/step")
+
+    work = W.work()
+    per_kernel = {}
+    for k, (n, tot) in sorted(kern.items(), key=lambda kv: -kv[1][1]):
+        avg = tot / max(n, 1)
+        e = dict(launches=n, avg_us=round(avg * 1e3, 2), share=round(tot / (ms * args.steps), 4))
+        if k in work:
+            e["tflops"] = round(work[k] / (avg * 1e-3) / 1e12, 1)
+            e["mfma_frac"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+        per_kernel[k] = e
+    dominant = max((k for k in kern if k in work), key=lambda k: kern[k][1])
+    n_dom, tot_dom = kern[dominant]
+    achieved = work[dominant] / (tot_dom / n_dom * 1e-3) / 1e12
+    total_flops = sum(work.values())
+
+    result = {
+        "metric": METRIC,
+        "value": round(W.T / (ms * 1e-3), 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded; random-init weights, router/top-k masks)",
+        "config": W.config,
+        "roofline": {
+            "bound": "mfma",
+            "kernel": dominant,
+            "achieved": round(achieved, 1),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "traffic": traffic_from_profiles(dominant, W.name),
+        },
+        "step_active_tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
+        "step_mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "all_ones_ms_per_step": round(ms_ones, 4),
+        "speedup_vs_all_ones": round(ms_ones / ms, 3),
+        "kernels": per_kernel,
+    }
+
+    if not args.no_oracle:
+        S = args.oracle_tokens or W.T
+        log(f"timing the CPU oracle on {S} tokens")
+        secs = W.oracle_sample(S)
+        result["cpu_baseline"] = {
+            "value": round(S / secs, 2),
+            "unit": "tokens/s",
+            "cores": blas_threads() or len(os.sched_getaffinity(0)),
+            "kind": "oracle",
+            "sample": f"first {S} of {W.T} tokens of the same inputs, dense fp64 NumPy oracle "
+                      f"({secs:.1f} s)",
+        }
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -178,6 +178,24 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
                       uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap, uint16_t* Y,
                       void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
 
+/*
+ * Kernel timing, for benchmarking (not part of the method).  While enabled, each
+ * kernel launch the library makes is bracketed by two HIP events on its stream.
+ *   wide_trace_enable(on)   start (on != 0) or stop recording; returns 0
+ *   wide_trace_collect()    waits for the recorded events, folds them into
+ *                           per-kernel totals; returns the number of distinct
+ *                           kernels, or -1 if a HIP event query failed
+ *   wide_trace_get(i, ...)  name (NUL-terminated, truncated to name_len), launch
+ *                           count and summed milliseconds of kernel i; 0 on
+ *                           success, 1 for a bad index or NULL argument
+ *   wide_trace_reset()      drops all records and totals
+ * The trace is process-wide state guarded by a mutex.
+ */
+int wide_trace_enable(int on);
+int wide_trace_collect(void);
+int wide_trace_get(int i, char* name, int name_len, int* launches, double* total_ms);
+void wide_trace_reset(void);
+
 #ifdef __cplusplus
 }
 #endif

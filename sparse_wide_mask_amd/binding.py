@@ -41,6 +41,10 @@ _SIGS = {
     "wide_attn_proj_masked": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _i, _p, _p,
                                _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
     "wide_layer_masked_workspace": ([_i, C.POINTER(WideLayerCfg), _i], _sz),
+    "wide_trace_enable": ([_i], _i),
+    "wide_trace_collect": ([], _i),
+    "wide_trace_get": ([_i, C.c_char_p, _i, C.POINTER(_i), C.POINTER(C.c_double)], _i),
+    "wide_trace_reset": ([], None),
     "wide_layer_masked": ([_p, _p, _p, C.POINTER(WideLayerWeights), C.POINTER(WideLayerCfg), _i, _i,
                            _p, _p, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
 }
@@ -105,6 +109,31 @@ def _workspace(nbytes: int, device, workspace):
     if workspace is not None:
         return workspace
     return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+# -------------------------------------------------------------------- trace
+
+def trace_enable(on: bool = True):
+    lib().wide_trace_enable(1 if on else 0)
+
+
+def trace_reset():
+    lib().wide_trace_reset()
+
+
+def trace_collect() -> dict:
+    """{kernel name: (launches, total ms)} of the launches recorded so far."""
+    L = lib()
+    n = L.wide_trace_collect()
+    if n < 0:
+        raise RuntimeError("wide_trace_collect: HIP event query failed")
+    out = {}
+    buf = C.create_string_buffer(256)
+    for i in range(n):
+        k, ms = _i(), C.c_double()
+        if L.wide_trace_get(i, buf, 256, C.byref(k), C.byref(ms)) == 0:
+            out[buf.value.decode()] = (k.value, ms.value)
+    return out
 
 
 # ------------------------------------------------------------------ reorder

@@ -139,7 +139,7 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   run_reorder(mask, T, nkv, w.rv, s);
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
-  launch_kmask_gemm(w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
+  launch_kmask_gemm("attn_o", w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
 }
 
 // -------------------------------------------------------------------- layer

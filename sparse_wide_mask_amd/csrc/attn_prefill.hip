@@ -399,12 +399,18 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
   const int ntn = (r + 1) / 2 + 1;
   const float log2_theta = rope_theta > 0.f ? log2f(rope_theta) : 0.f;
   const int vtp = vt_pitch(T);
-  attn_qkv_prefill<<<n_kv * mtiles * ntn, 256, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
-                                                       r, mtiles, vtp, log2_theta, Qc, Kc, Vt);
+  {
+    WIDE_TRACE("attn_qkv_prefill", s);
+    attn_qkv_prefill<<<n_kv * mtiles * ntn, 256, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
+                                                         r, mtiles, vtp, log2_theta, Qc, Kc, Vt);
+  }
   const int qtiles = (T + kBQ - 1) / kBQ;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHd);
-  attn_core_prefill<<<qtiles * n_kv * ((r + 3) / 4), 256, 0, s>>>(
-      Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, qtiles, vtp, scale_log2, O);
+  {
+    WIDE_TRACE("attn_core_prefill", s);
+    attn_core_prefill<<<qtiles * n_kv * ((r + 3) / 4), 256, 0, s>>>(
+        Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, qtiles, vtp, scale_log2, O);
+  }
 }
 
 }  // namespace wide

@@ -146,7 +146,7 @@ __global__ void __launch_bounds__(256, 1)
 
 template <int BM, int BN>
 __global__ void __launch_bounds__(256, 1)
-    ffn_down_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
+    kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
                      const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
                      const int32_t* __restrict__ tgroups, int T, int d, int F, int n, int G,
                      int nw, int ntn, const uint16_t* __restrict__ residual,
@@ -269,9 +269,11 @@ int ffn_down_tile_m() { return kDownBM; }
 
 // K-masked GEMM Y[t] = sum over groups g kept by t of A[t, gG:(g+1)G] Wp[g]^T
 // (+ residual), A token-major [T, F], Wp packed [n, d, G].  The column tile is
-// chosen to fill the 256 CUs best (rounds x tile width).
-void launch_kmask_gemm(const uint16_t* A, const uint16_t* Wp, const ReorderView& rv, int T, int d,
-                       int F, int n, const uint16_t* residual, uint16_t* Y, hipStream_t s) {
+// chosen to fill the 256 CUs best (rounds x tile width).  `tname` labels the
+// launch in the kernel trace (FFN down or attention output projection).
+void launch_kmask_gemm(const char* tname, const uint16_t* A, const uint16_t* Wp,
+                       const ReorderView& rv, int T, int d, int F, int n, const uint16_t* residual,
+                       uint16_t* Y, hipStream_t s) {
   const int G = F / n;
   const int nw = (n + 63) / 64;
   const int mtiles = (T + kDownBM - 1) / kDownBM;
@@ -284,38 +286,44 @@ void launch_kmask_gemm(const uint16_t* A, const uint16_t* Wp, const ReorderView&
   }
   const int ntn = (d + best_bn - 1) / best_bn;
   const int grid = 8 * ((mtiles * ntn + 7) / 8);
+  WIDE_TRACE(tname, s);
   if (best_bn == 256)
-    ffn_down_prefill<kDownBM, 256><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
-                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                        residual, Y);
+    kmask_gemm_prefill<kDownBM, 256><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
+                                                          rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                          residual, Y);
   else if (best_bn == 192)
-    ffn_down_prefill<kDownBM, 192><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
-                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                        residual, Y);
+    kmask_gemm_prefill<kDownBM, 192><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
+                                                          rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                          residual, Y);
   else
-    ffn_down_prefill<kDownBM, 128><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
-                                                        rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                        residual, Y);
+    kmask_gemm_prefill<kDownBM, 128><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
+                                                          rv.tile_groups, T, d, F, n, G, nw, ntn,
+                                                          residual, Y);
 }
 
 void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
                         const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
                         const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s) {
   const int G = F / n;
-  const int nw = (n + 63) / 64;
   // up
   if (G % 128 == 0) {
     constexpr int BM = 256, BN = 256;
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
-    ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
-                                                             n, G, mtiles, ntn, H);
+    {
+      WIDE_TRACE("ffn_up_prefill", s);
+      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
+                                                               n, G, mtiles, ntn, H);
+    }
   } else {
     constexpr int BM = 256, BN = 128;
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
-    ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
-                                                             n, G, mtiles, ntn, H);
+    {
+      WIDE_TRACE("ffn_up_prefill", s);
+      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
+                                                               n, G, mtiles, ntn, H);
+    }
   }
-  launch_kmask_gemm(H, Wdp, rv, T, d, F, n, residual, Y, s);
+  launch_kmask_gemm("ffn_down", H, Wdp, rv, T, d, F, n, residual, Y, s);
 }
 
 }  // namespace wide

@@ -6,6 +6,19 @@
 
 namespace wide {
 
+// Brackets one kernel launch with HIP events when tracing is enabled
+// (wide_trace_enable); a no-op otherwise.
+class TraceScope {
+ public:
+  TraceScope(const char* name, hipStream_t s);
+  ~TraceScope();
+
+ private:
+  hipStream_t s_;
+  bool active_;
+};
+#define WIDE_TRACE(name, stream) ::wide::TraceScope wide_trace_scope_(name, stream)
+
 // Device buffers produced by the mask reordering, as the kernels consume them.
 struct ReorderView {
   uint64_t* packed = nullptr;     // [T, nw]
@@ -28,8 +41,9 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
                         const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
                         const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
 
-void launch_kmask_gemm(const uint16_t* A, const uint16_t* Wp, const ReorderView& rv, int T, int d,
-                       int F, int n, const uint16_t* residual, uint16_t* Y, hipStream_t s);
+void launch_kmask_gemm(const char* tname, const uint16_t* A, const uint16_t* Wp,
+                       const ReorderView& rv, int T, int d, int F, int n, const uint16_t* residual,
+                       uint16_t* Y, hipStream_t s);
 
 // Row pitch (elements) of the transposed per-group V buffer: T rounded up to 8.
 inline int vt_pitch(int T) { return (T + 7) / 8 * 8; }

@@ -43,7 +43,10 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const uint16_t* __restrict__
 
 void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, int T, int d, float eps, uint16_t* y,
                     hipStream_t s) {
-  rmsnorm_rows<<<T, 256, 0, s>>>(x, gamma, d, eps, y);
+  {
+    WIDE_TRACE("rmsnorm_rows", s);
+    rmsnorm_rows<<<T, 256, 0, s>>>(x, gamma, d, eps, y);
+  }
 }
 
 }  // namespace wide

@@ -20,7 +20,10 @@ __global__ void __launch_bounds__(256) pack_kmajor(const uint16_t* __restrict__ 
 
 void launch_pack_kmajor(const uint16_t* W, int n, int G, int d, uint16_t* Wp, hipStream_t s) {
   dim3 grid(d / 64, G / 64, n);
-  pack_kmajor<<<grid, 256, 0, s>>>(W, G, d, Wp);
+  {
+    WIDE_TRACE("pack_kmajor", s);
+    pack_kmajor<<<grid, 256, 0, s>>>(W, G, d, Wp);
+  }
 }
 
 }  // namespace wide

@@ -131,13 +131,22 @@ void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* pac
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
   const int nw = (n + 63) / 64;
-  reorder_pack<<<(T + 255) / 256, 256, 0, s>>>(mask, T, n, nw, packed);
-  reorder_groups<<<n, kGroupThreads, 0, s>>>(packed, T, n, nw, group_count, group_perm,
-                                              group_rank);
+  {
+    WIDE_TRACE("reorder_pack", s);
+    reorder_pack<<<(T + 255) / 256, 256, 0, s>>>(mask, T, n, nw, packed);
+  }
+  {
+    WIDE_TRACE("reorder_groups", s);
+    reorder_groups<<<n, kGroupThreads, 0, s>>>(packed, T, n, nw, group_count, group_perm,
+                                                group_rank);
+  }
   if (tile_count && tile_groups) {
     const int n_tiles = (T + tile_m - 1) / tile_m;
-    reorder_tiles<<<(n_tiles + 3) / 4, 256, 0, s>>>(packed, T, n, nw, tile_m, n_tiles,
-                                                    tile_count, tile_groups);
+    {
+      WIDE_TRACE("reorder_tiles", s);
+      reorder_tiles<<<(n_tiles + 3) / 4, 256, 0, s>>>(packed, T, n, nw, tile_m, n_tiles,
+                                                      tile_count, tile_groups);
+    }
   }
 }
 

@@ -23,7 +23,7 @@ def L():
 
 def declared():
     src = open(HEADER).read()
-    return sorted(set(re.findall(r"^(?:const char\*|int|size_t)\s+(wide_\w+)\(", src, re.M)))
+    return sorted(set(re.findall(r"^(?:const char\*|int|size_t|void)\s+(wide_\w+)\(", src, re.M)))
 
 
 def test_header_declares_the_contract():
