@@ -46,10 +46,12 @@ enum {
 };
 enum { WIDE_PREFILL = 0, WIDE_DECODE = 1 };
 
-/* Limits: 1 <= n_groups <= 256, T <= 65536 (prefill) / 256 (decode). */
+/* Limits: 1 <= n_groups <= 256, T <= 65536 (prefill); attention decode batch
+ * <= 64 with at most 8 query heads per KV head.  A "decode" FFN call with more
+ * than 64 tokens runs the prefill kernels. */
 #define WIDE_MAX_GROUPS 256
 #define WIDE_MAX_TOKENS 65536
-#define WIDE_MAX_DECODE_BATCH 256
+#define WIDE_MAX_DECODE_BATCH 64
 
 const char* wide_status_string(int status);
 int wide_version(void);
@@ -101,7 +103,8 @@ int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16
  * W_gate, W_up  [d_ff, d_model] bf16 (nn.Linear layout; group g = rows gG..gG+G-1)
  * W_down_packed [n_groups, d_model, G] bf16 (wide_pack_kmajor of W_down [d_ff, d_model])
  * Y             [T, d_model] bf16 (a token that keeps no group gets exact zeros)
- * mode          WIDE_PREFILL (any T) or WIDE_DECODE (T = batch <= 256, weight streaming)
+ * mode          WIDE_PREFILL (any T) or WIDE_DECODE (T = batch; weight streaming over
+ *               the groups the batch keeps when T <= 64)
  * Needs G = d_ff / n_groups a multiple of 64 and d_model a multiple of 64.
  */
 size_t wide_ffn_masked_workspace(int T, int d_model, int d_ff, int n_groups, int mode);
@@ -137,7 +140,11 @@ typedef struct {
   float rope_theta; /* 0 = no RoPE */
 } wide_attn_cfg;
 
-size_t wide_attn_proj_masked_workspace(int T, int d_model, const wide_attn_cfg* cfg, int mode);
+/* Workspace bytes for a call with these sizes (0 for invalid arguments).  kv_cap is
+ * the cache capacity of decode calls (the split-KV partials scale with it); it is
+ * ignored in prefill. */
+size_t wide_attn_proj_masked_workspace(int T, int d_model, const wide_attn_cfg* cfg, int mode,
+                                       int kv_cap);
 int wide_attn_proj_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
                           const uint16_t* Wk, const uint16_t* Wv, const uint16_t* Wo_packed,
                           int T, int d_model, const wide_attn_cfg* cfg, int mode,
@@ -172,7 +179,7 @@ typedef struct {
   float rms_eps;
 } wide_layer_cfg;
 
-size_t wide_layer_masked_workspace(int T, const wide_layer_cfg* cfg, int mode);
+size_t wide_layer_masked_workspace(int T, const wide_layer_cfg* cfg, int mode, int kv_cap);
 int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_mask,
                       const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
                       uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap, uint16_t* Y,

@@ -37,10 +37,10 @@ _SIGS = {
     "wide_pack_kmajor": ([_p, _i, _i, _i, _p, _p], _i),
     "wide_ffn_masked_workspace": ([_i, _i, _i, _i, _i], _sz),
     "wide_ffn_masked": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
-    "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i], _sz),
+    "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i, _i], _sz),
     "wide_attn_proj_masked": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _i, _p, _p,
                                _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
-    "wide_layer_masked_workspace": ([_i, C.POINTER(WideLayerCfg), _i], _sz),
+    "wide_layer_masked_workspace": ([_i, C.POINTER(WideLayerCfg), _i, _i], _sz),
     "wide_trace_enable": ([_i], _i),
     "wide_trace_collect": ([], _i),
     "wide_trace_get": ([_i, C.c_char_p, _i, C.POINTER(_i), C.POINTER(C.c_double)], _i),
@@ -211,9 +211,9 @@ def _attn_cfg(n_q, n_kv, hd, theta):
 
 
 def attn_proj_masked_workspace(T, d_model, n_q, n_kv, head_dim=128, rope_theta=0.0,
-                               mode="prefill") -> int:
+                               mode="prefill", kv_cap=0) -> int:
     cfg = _attn_cfg(n_q, n_kv, head_dim, rope_theta)
-    return int(lib().wide_attn_proj_masked_workspace(T, d_model, C.byref(cfg), _mode(mode)))
+    return int(lib().wide_attn_proj_masked_workspace(T, d_model, C.byref(cfg), _mode(mode), kv_cap))
 
 
 def attn_proj_masked(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, head_dim=128, rope_theta=0.0,
@@ -231,7 +231,7 @@ def attn_proj_masked(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, head_dim=128,
         _dev(V_cache, torch.bfloat16, "V_cache")
         kv_cap = K_cache.shape[2]
     cfg = _attn_cfg(n_q, n_kv, head_dim, rope_theta)
-    ws_bytes = int(lib().wide_attn_proj_masked_workspace(T, d, C.byref(cfg), m))
+    ws_bytes = int(lib().wide_attn_proj_masked_workspace(T, d, C.byref(cfg), m, kv_cap))
     ws = _workspace(ws_bytes, X.device, workspace)
     Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
     st = lib().wide_attn_proj_masked(_ptr(X), _ptr(mask), _ptr(Wq), _ptr(Wk), _ptr(Wv),
@@ -249,9 +249,9 @@ def _layer_cfg(d, F, n_ffn, n_q, n_kv, hd, theta, eps):
 
 
 def layer_masked_workspace(T, d_model, d_ff, n_ffn, n_q, n_kv, head_dim=128, rope_theta=500000.0,
-                           eps=1e-5, mode="prefill") -> int:
+                           eps=1e-5, mode="prefill", kv_cap=0) -> int:
     cfg = _layer_cfg(d_model, d_ff, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
-    return int(lib().wide_layer_masked_workspace(T, C.byref(cfg), _mode(mode)))
+    return int(lib().wide_layer_masked_workspace(T, C.byref(cfg), _mode(mode), kv_cap))
 
 
 def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, head_dim=128,
@@ -276,7 +276,7 @@ def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, head_dim=128,
         kv_cap = K_cache.shape[2]
     cfg = _layer_cfg(d, F, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
     wts = WideLayerWeights(*[W[k].data_ptr() for k in keys])
-    ws_bytes = int(lib().wide_layer_masked_workspace(T, C.byref(cfg), m))
+    ws_bytes = int(lib().wide_layer_masked_workspace(T, C.byref(cfg), m, kv_cap))
     ws = _workspace(ws_bytes, X.device, workspace)
     Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
     st = lib().wide_layer_masked(_ptr(X), _ptr(attn_mask), _ptr(ffn_mask), C.byref(wts),

@@ -68,7 +68,6 @@ int ffn_check(int T, int d, int F, int n, int mode) {
   if (F % n) return WIDE_EINVAL;
   if (n > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
   if (!fits(T, d) || !fits(F, d) || !fits(T, F)) return WIDE_EUNSUPPORTED;
-  if (mode == WIDE_DECODE) return WIDE_EUNSUPPORTED;
   const int G = F / n;
   if (G % 64 || d % 64) return WIDE_EUNSUPPORTED;
   return WIDE_OK;
@@ -79,11 +78,15 @@ struct FfnWs {
   uint16_t* H = nullptr;
 };
 
+// Decode kernels take batches up to kMaxDecodeBatch; a larger "decode" batch runs
+// the prefill kernels (the FFN keeps no state, so the result is the same).
+bool ffn_streaming(int T, int mode) { return mode == WIDE_DECODE && T <= kMaxDecodeBatch; }
+
 FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
   (void)d;
-  (void)mode;
   FfnWs w;
-  w.rv = carve_reorder(c, T, n, ffn_down_tile_m(), false);
+  // streaming: one tile spans the batch, so tile_groups[0] is the batch's union
+  w.rv = carve_reorder(c, T, n, ffn_streaming(T, mode) ? (T > 0 ? T : 1) : ffn_down_tile_m(), false);
   w.H = c.take<uint16_t>((size_t)T * F);
   return w;
 }
@@ -91,9 +94,11 @@ FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
 int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const uint16_t* Wu,
             const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
             uint16_t* Y, const FfnWs& w, hipStream_t s) {
-  (void)mode;
   run_reorder(mask, T, n, w.rv, s);
-  launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
+  if (ffn_streaming(T, mode))
+    launch_ffn_decode(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
+  else
+    launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
   return WIDE_OK;
 }
 
@@ -111,20 +116,39 @@ int attn_check(int T, int d, const wide_attn_cfg* cfg, int mode) {
   if (nkv > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
   const int64_t F = (int64_t)nq * kHeadDim;
   if (!fits(T, d) || !fits(F, d) || !fits(T, F)) return WIDE_EUNSUPPORTED;
-  if (mode == WIDE_DECODE) return WIDE_EUNSUPPORTED;
+  if (mode == WIDE_DECODE && (T > kMaxDecodeBatch || nq / nkv > 8)) return WIDE_EUNSUPPORTED;
+  return WIDE_OK;
+}
+
+// Decode arguments: caches present, 0 <= kv_len < kv_cap, cache sizes addressable.
+int attn_decode_check(int T, const wide_attn_cfg* cfg, const uint16_t* K_cache,
+                      const uint16_t* V_cache, int kv_len, int kv_cap) {
+  if (!aligned16(K_cache) || !aligned16(V_cache) || K_cache == V_cache) return WIDE_EINVAL;
+  if (kv_cap < 1 || kv_len < 0 || kv_len >= kv_cap) return WIDE_EINVAL;
+  if (!fits((int64_t)T * cfg->n_kv_heads * kv_cap, kHeadDim)) return WIDE_EUNSUPPORTED;
   return WIDE_OK;
 }
 
 struct AttnWs {
   ReorderView rv;
   uint16_t *Qc = nullptr, *Kc = nullptr, *Vt = nullptr, *O = nullptr;
+  float *Opart = nullptr, *Mpart = nullptr, *Lpart = nullptr;
 };
 
-AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode) {
+AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, int kv_cap) {
   (void)d;
-  (void)mode;
   AttnWs w;
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
+  if (mode == WIDE_DECODE) {
+    const int nch = attn_decode_chunks(kv_cap > 0 ? kv_cap - 1 : 0);
+    w.rv = carve_reorder(c, T, nkv, T > 0 ? T : 1, false);
+    w.Qc = c.take<uint16_t>((size_t)T * nq * kHeadDim);
+    w.O = c.take<uint16_t>((size_t)T * nq * kHeadDim);
+    w.Opart = c.take<float>((size_t)T * nq * nch * kHeadDim);
+    w.Mpart = c.take<float>((size_t)T * nq * nch);
+    w.Lpart = c.take<float>((size_t)T * nq * nch);
+    return w;
+  }
   w.rv = carve_reorder(c, T, nkv, ffn_down_tile_m(), false);
   w.Qc = c.take<uint16_t>((size_t)nq * T * kHeadDim);
   w.Kc = c.take<uint16_t>((size_t)nkv * T * kHeadDim);
@@ -135,9 +159,16 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode) {
 
 void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
               const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
+              int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
               const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   run_reorder(mask, T, nkv, w.rv, s);
+  if (mode == WIDE_DECODE) {
+    launch_attn_decode(X, mask, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache,
+                       kv_len, kv_cap, w.Qc, w.Opart, w.Mpart, w.Lpart, w.O, s);
+    launch_kmask_decode("attn_o_decode", w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
+    return;
+  }
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
   launch_kmask_gemm("attn_o", w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
 }
@@ -158,12 +189,12 @@ struct LayerWs {
   FfnWs ffn;
 };
 
-LayerWs carve_layer(Carver& c, int T, const wide_layer_cfg* cfg, int mode) {
+LayerWs carve_layer(Carver& c, int T, const wide_layer_cfg* cfg, int mode, int kv_cap) {
   LayerWs w;
   const int d = cfg->d_model;
   w.u = c.take<uint16_t>((size_t)T * d);
   w.h = c.take<uint16_t>((size_t)T * d);
-  w.attn = carve_attn(c, T, d, &cfg->attn, mode);
+  w.attn = carve_attn(c, T, d, &cfg->attn, mode, kv_cap);
   w.ffn = carve_ffn(c, T, d, cfg->d_ff, cfg->n_ffn_groups, mode);
   return w;
 }
@@ -241,10 +272,12 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
   return launch_status();
 }
 
-size_t wide_attn_proj_masked_workspace(int T, int d_model, const wide_attn_cfg* cfg, int mode) {
+size_t wide_attn_proj_masked_workspace(int T, int d_model, const wide_attn_cfg* cfg, int mode,
+                                       int kv_cap) {
   if (attn_check(T, d_model, cfg, mode) != WIDE_OK) return 0;
+  if (mode == WIDE_DECODE && kv_cap < 1) return 0;
   Carver c(nullptr);
-  carve_attn(c, T, d_model, cfg, mode);
+  carve_attn(c, T, d_model, cfg, mode, kv_cap);
   return c.used;
 }
 
@@ -254,32 +287,34 @@ int wide_attn_proj_masked(const uint16_t* X, const uint8_t* mask, const uint16_t
                           uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
                           uint16_t* Y, void* workspace, size_t workspace_bytes, uint32_t flags,
                           void* stream) {
-  (void)K_cache;
-  (void)V_cache;
-  (void)kv_len;
-  (void)kv_cap;
   int st = attn_check(T, d_model, cfg, mode);
   if (st != WIDE_OK) return st;
   if (flags != 0) return WIDE_EINVAL;
+  if (mode == WIDE_DECODE) {
+    st = attn_decode_check(T, cfg, K_cache, V_cache, kv_len, kv_cap);
+    if (st != WIDE_OK) return st;
+  }
   if (T == 0) return WIDE_OK;
   if (!aligned16(X) || !aligned16(mask) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
       !aligned16(Wo_packed) || !aligned16(Y) || (void*)Y == (void*)X)
     return WIDE_EINVAL;
   Carver probe(nullptr);
-  carve_attn(probe, T, d_model, cfg, mode);
+  carve_attn(probe, T, d_model, cfg, mode, kv_cap);
   if (!aligned16(workspace)) return WIDE_EINVAL;
   if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
   Carver c(workspace);
-  AttnWs w = carve_attn(c, T, d_model, cfg, mode);
+  AttnWs w = carve_attn(c, T, d_model, cfg, mode, kv_cap);
   (void)hipGetLastError();
-  attn_run(X, mask, Wq, Wk, Wv, Wo_packed, T, d_model, cfg, nullptr, Y, w, as_stream(stream));
+  attn_run(X, mask, Wq, Wk, Wv, Wo_packed, T, d_model, cfg, mode, K_cache, V_cache, kv_len, kv_cap,
+           nullptr, Y, w, as_stream(stream));
   return launch_status();
 }
 
-size_t wide_layer_masked_workspace(int T, const wide_layer_cfg* cfg, int mode) {
+size_t wide_layer_masked_workspace(int T, const wide_layer_cfg* cfg, int mode, int kv_cap) {
   if (layer_check(T, cfg, mode) != WIDE_OK) return 0;
+  if (mode == WIDE_DECODE && kv_cap < 1) return 0;
   Carver c(nullptr);
-  carve_layer(c, T, cfg, mode);
+  carve_layer(c, T, cfg, mode, kv_cap);
   return c.used;
 }
 
@@ -287,13 +322,13 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
                       const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
                       uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap, uint16_t* Y,
                       void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
-  (void)K_cache;
-  (void)V_cache;
-  (void)kv_len;
-  (void)kv_cap;
   int st = layer_check(T, cfg, mode);
   if (st != WIDE_OK) return st;
   if (flags != 0 || !W) return WIDE_EINVAL;
+  if (mode == WIDE_DECODE) {
+    st = attn_decode_check(T, &cfg->attn, K_cache, V_cache, kv_len, kv_cap);
+    if (st != WIDE_OK) return st;
+  }
   if (T == 0) return WIDE_OK;
   if (!aligned16(X) || !aligned16(attn_mask) || !aligned16(ffn_mask) || !aligned16(Y) ||
       (void*)Y == (void*)X || !aligned16(W->rms1) || !aligned16(W->rms2) || !aligned16(W->Wq) ||
@@ -301,16 +336,17 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
       !aligned16(W->W_gate) || !aligned16(W->W_up) || !aligned16(W->W_down_packed))
     return WIDE_EINVAL;
   Carver probe(nullptr);
-  carve_layer(probe, T, cfg, mode);
+  carve_layer(probe, T, cfg, mode, kv_cap);
   if (!aligned16(workspace)) return WIDE_EINVAL;
   if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
   Carver c(workspace);
-  LayerWs w = carve_layer(c, T, cfg, mode);
+  LayerWs w = carve_layer(c, T, cfg, mode, kv_cap);
   const int d = cfg->d_model;
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
   launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
-  attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, X, w.h, w.attn, s);
+  attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode, K_cache,
+           V_cache, kv_len, kv_cap, X, w.h, w.attn, s);
   launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
   ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, cfg->n_ffn_groups,
           mode, w.h, Y, w.ffn, s);
