@@ -200,8 +200,210 @@ class AttnPrefill:
         return time.perf_counter() - t0
 
 
+# ---------------------------------------------------------------- decode
+#
+# Decode is bound by HBM: its work is counted in bytes actually touched (the weight
+# blocks of the groups some token of the batch keeps, the K/V of the kept
+# (token, group) pairs, activations).  Several copies of the inputs rotate between
+# steps so the 256 MB Infinity Cache cannot serve a repeated step.
+
+MALL_BYTES = 256 << 20
+
+
+def _copies(set_bytes):
+    return max(2, -(-(4 * MALL_BYTES) // max(set_bytes, 1)))
+
+
+class FfnDecode:
+    """Llama-3.1-8B-shaped FFN decode: B single tokens, d=4096, d_ff=14336 in 112 groups."""
+
+    def __init__(self, B=1):
+        from synth.workloads import ffn_decode_8b
+        self.name = f"ffn_decode_8b_B{B}"
+        self.c = ffn_decode_8b(B)
+        m = self.c["meta"]
+        self.m, self.T = m, B
+        self.config = dict(workload=self.name, B=B, d_model=m["d"], d_ff=m["F"], n_groups=m["n"],
+                           keep=m["keep"], masks="top-k")
+        self.bound = "hbm"
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        set_bytes = 3 * m["F"] * m["d"] * 2
+        self.sets = []
+        for _ in range(_copies(set_bytes)):
+            self.sets.append((bf16(c["W_gate"]), bf16(c["W_up"]),
+                              wide.pack_kmajor(bf16(c["W_down"]), m["n"])))
+        self.X = bf16(c["X"])
+        self.mask = u8(c["mask"])
+        self.ones = torch.ones_like(self.mask)
+        self.Y = torch.empty_like(self.X)
+        self.ws = torch.empty(wide.ffn_masked_workspace(self.T, m["d"], m["F"], m["n"], "decode"),
+                              dtype=torch.uint8, device="cuda")
+        self.wide, self.i = wide, 0
+
+    def step(self, ones=False):
+        Wg, Wu, Wd = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.wide.ffn_masked(self.X, self.ones if ones else self.mask, Wg, Wu, Wd, mode="decode",
+                             out=self.Y, workspace=self.ws)
+
+    def work(self, ones=False):
+        m = self.m
+        d, G, B = m["d"], m["F"] // m["n"], self.T
+        mk = np.ones_like(self.c["mask"]) if ones else (self.c["mask"] != 0)
+        U = float(mk.any(axis=0).sum())
+        kept = float(mk.sum())
+        return {"ffn_up_decode": U * 2 * G * d * 2 + B * d * 2 + kept * G * 2,
+                "ffn_down_decode": U * G * d * 2 + kept * G * 2 + B * d * 2}
+
+    def oracle_sample(self, S):
+        from oracle import ffn_masked
+        c = self.c
+        t0 = time.perf_counter()
+        ffn_masked(c["X"][:S], c["mask"][:S], c["W_gate"], c["W_up"], c["W_down"])
+        return time.perf_counter() - t0
+
+
+def _attn_decode_bytes(m, am, d, L):
+    """Touched bytes of the attention decode kernels (keys 0..L incl. the new one)."""
+    n_q, n_kv = m["n_q"], m["n_kv"]
+    r = n_q // n_kv
+    B = am.shape[0]
+    U = float(am.any(axis=0).sum())
+    kept = float(am.sum())
+    return {
+        "attn_qkv_decode": U * (r + 2) * HD * d * 2 + B * d * 2 + kept * (r + 2) * HD * 2,
+        "attn_core_decode": kept * 2 * (L + 1) * HD * 2 + kept * r * HD * 2,
+        "attn_o_decode": U * r * HD * d * 2 + kept * r * HD * 2 + B * d * 2,
+    }
+
+
+class AttnDecode:
+    """Llama-3.1-8B-shaped attention decode: batch 16 over a 4096-entry cache."""
+
+    def __init__(self, B=16, L=4096):
+        from synth.workloads import attn_decode_8b
+        self.name = "attn_decode_8b"
+        self.c = attn_decode_8b(B, L)
+        m = self.c["meta"]
+        self.m, self.T, self.L = m, B, L
+        self.config = dict(workload=self.name, B=B, kv_len=L, d_model=m["d"], n_q_heads=m["n_q"],
+                           n_kv_heads=m["n_kv"], head_dim=HD, keep=m["keep"], masks="top-k")
+        self.bound = "hbm"
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        set_bytes = (2 * m["n_q"] + 2 * m["n_kv"]) * HD * m["d"] * 2 + 2 * c["K_cache"].size * 2
+        self.sets = []
+        for _ in range(_copies(set_bytes)):
+            self.sets.append((bf16(c["Wq"]), bf16(c["Wk"]), bf16(c["Wv"]),
+                              wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]), bf16(c["K_cache"]),
+                              bf16(c["V_cache"])))
+        self.X = bf16(c["X"])
+        self.mask = u8(c["mask"])
+        self.ones = torch.ones_like(self.mask)
+        self.Y = torch.empty_like(self.X)
+        self.ws = torch.empty(wide.attn_proj_masked_workspace(self.T, m["d"], m["n_q"], m["n_kv"],
+                                                              mode="decode", kv_cap=m["kv_cap"]),
+                              dtype=torch.uint8, device="cuda")
+        self.wide, self.i = wide, 0
+
+    def step(self, ones=False):
+        m = self.m
+        Wq, Wk, Wv, Wo, Kc, Vc = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.wide.attn_proj_masked(self.X, self.ones if ones else self.mask, Wq, Wk, Wv, Wo,
+                                   n_q=m["n_q"], n_kv=m["n_kv"], mode="decode", K_cache=Kc,
+                                   V_cache=Vc, kv_len=self.L, out=self.Y, workspace=self.ws)
+
+    def work(self, ones=False):
+        am = np.ones_like(self.c["mask"]) if ones else (self.c["mask"] != 0)
+        return _attn_decode_bytes(self.m, am, self.m["d"], self.L)
+
+    def oracle_sample(self, S):
+        from oracle import attn_masked
+        c, m = self.c, self.m
+        t0 = time.perf_counter()
+        attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
+                    n_kv=m["n_kv"], head_dim=HD, decode=True, K_cache=c["K_cache"][:S],
+                    V_cache=c["V_cache"][:S], kv_len=self.L)
+        return time.perf_counter() - t0
+
+
+class LayerDecode:
+    """Llama-3.1-8B-shaped decoder layer, decode: batch 32 over an 8192-entry cache."""
+
+    def __init__(self, B=32, L=8192, keep=0.5, kind="router"):
+        from synth.workloads import layer_8b
+        self.name = "layer_decode_8b"
+        self.c = layer_8b(B, decode=True, L=L, keep=keep, kind=kind)
+        m = self.c["meta"]
+        self.m, self.T, self.L = m, B, L
+        self.config = dict(workload=self.name, B=B, kv_len=L, d_model=m["d"], d_ff=m["F"],
+                           n_ffn_groups=m["n_ffn"], n_q_heads=m["n_q"], n_kv_heads=m["n_kv"],
+                           head_dim=HD, rope_theta=m["rope_theta"], keep=keep,
+                           masks=f"{kind} top-k" if kind == "router" else kind)
+        self.bound = "hbm"
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        self.sets = []
+        for _ in range(2):
+            self.sets.append(dict(
+                rms1=bf16(c["rms1"]), rms2=bf16(c["rms2"]), Wq=bf16(c["Wq"]), Wk=bf16(c["Wk"]),
+                Wv=bf16(c["Wv"]), Wo_packed=wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]),
+                W_gate=bf16(c["W_gate"]), W_up=bf16(c["W_up"]),
+                W_down_packed=wide.pack_kmajor(bf16(c["W_down"]), m["n_ffn"]),
+                K_cache=bf16(c["K_cache"]), V_cache=bf16(c["V_cache"])))
+        self.X = bf16(c["X"])
+        self.masks = (u8(c["attn_mask"]), u8(c["ffn_mask"]))
+        self.ones = (torch.ones_like(self.masks[0]), torch.ones_like(self.masks[1]))
+        self.Y = torch.empty_like(self.X)
+        ws = wide.layer_masked_workspace(self.T, m["d"], m["F"], m["n_ffn"], m["n_q"], m["n_kv"],
+                                         HD, m["rope_theta"], m["eps"], mode="decode",
+                                         kv_cap=m["kv_cap"])
+        self.ws = torch.empty(ws, dtype=torch.uint8, device="cuda")
+        self.wide, self.i = wide, 0
+
+    def step(self, ones=False):
+        m = self.m
+        S = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        am, fm = self.ones if ones else self.masks
+        self.wide.layer_masked(self.X, am, fm, S, n_q=m["n_q"], n_kv=m["n_kv"], head_dim=HD,
+                               rope_theta=m["rope_theta"], eps=m["eps"], mode="decode",
+                               K_cache=S["K_cache"], V_cache=S["V_cache"], kv_len=self.L,
+                               out=self.Y, workspace=self.ws)
+
+    def work(self, ones=False):
+        m = self.m
+        d, G, B = m["d"], m["F"] // m["n_ffn"], self.T
+        am = np.ones_like(self.c["attn_mask"]) if ones else (self.c["attn_mask"] != 0)
+        fm = np.ones_like(self.c["ffn_mask"]) if ones else (self.c["ffn_mask"] != 0)
+        U, kept = float(fm.any(axis=0).sum()), float(fm.sum())
+        w = _attn_decode_bytes(m, am, d, self.L)
+        w["ffn_up_decode"] = U * 2 * G * d * 2 + B * d * 2 + kept * G * 2
+        w["ffn_down_decode"] = U * G * d * 2 + kept * G * 2 + B * d * 2
+        return w
+
+    def oracle_sample(self, S):
+        from oracle import layer_masked
+        c, m = self.c, self.m
+        W = {k: c[k] for k in ("rms1", "rms2", "Wq", "Wk", "Wv", "Wo", "W_gate", "W_up", "W_down")}
+        t0 = time.perf_counter()
+        layer_masked(c["X"][:S], c["attn_mask"][:S], c["ffn_mask"][:S], W, n_q=m["n_q"],
+                     n_kv=m["n_kv"], head_dim=HD, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"],
+                     eps=m["eps"], decode=True, K_cache=c["K_cache"][:S], V_cache=c["V_cache"][:S],
+                     kv_len=self.L)
+        return time.perf_counter() - t0
+
+
 WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
-             "attn_prefill_8b": AttnPrefill}
+             "attn_prefill_8b": AttnPrefill, "layer_decode_8b": LayerDecode,
+             "attn_decode_8b": AttnDecode, "ffn_decode_8b_B1": lambda: FfnDecode(1),
+             "ffn_decode_8b_B8": lambda: FfnDecode(8), "ffn_decode_8b_B32": lambda: FfnDecode(32),
+             "ffn_decode_8b_B64": lambda: FfnDecode(64)}
 
 
 # ------------------------------------------------------------- measurement
@@ -292,18 +494,22 @@ def main():
     log(f"all-ones: {ms_ones:.3f} ms/step")
 
     work = W.work()
+    hbm = getattr(W, "bound", "mfma") == "hbm"
+    scale, peak, unit = (1e9, PEAK_HBM_GBS, "GB/s") if hbm else (1e12, PEAK_BF16_TFLOPS, "TFLOP/s")
     per_kernel = {}
     for k, (n, tot) in sorted(kern.items(), key=lambda kv: -kv[1][1]):
         avg = tot / max(n, 1)
         e = dict(launches=n, avg_us=round(avg * 1e3, 2), share=round(tot / (ms * args.steps), 4))
         if k in work:
-            e["tflops"] = round(work[k] / (avg * 1e-3) / 1e12, 1)
-            e["mfma_frac"] = round(e["tflops"] / PEAK_BF16_TFLOPS, 4)
+            rate = work[k] / (avg * 1e-3) / scale
+            e["gbs" if hbm else "tflops"] = round(rate, 1)
+            e["frac"] = round(rate / peak, 4)
         per_kernel[k] = e
     dominant = max((k for k in kern if k in work), key=lambda k: kern[k][1])
     n_dom, tot_dom = kern[dominant]
-    achieved = work[dominant] / (tot_dom / n_dom * 1e-3) / 1e12
-    total_flops = sum(work.values())
+    achieved = work[dominant] / (tot_dom / n_dom * 1e-3) / scale
+    total_work = sum(work.values())
+    step_rate = total_work / (ms * 1e-3) / scale
 
     result = {
         "metric": METRIC,
@@ -320,16 +526,17 @@ def main():
         "data": "synthetic (seeded; random-init weights, router/top-k masks)",
         "config": W.config,
         "roofline": {
-            "bound": "mfma",
+            "bound": "hbm" if hbm else "mfma",
             "kernel": dominant,
             "achieved": round(achieved, 1),
-            "peak": PEAK_BF16_TFLOPS,
-            "unit": "TFLOP/s",
-            "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+            "peak": peak,
+            "unit": unit,
+            "frac": round(achieved / peak, 4),
             "traffic": traffic_from_profiles(dominant, W.name),
         },
-        "step_active_tflops": round(total_flops / (ms * 1e-3) / 1e12, 1),
-        "step_mfma_frac": round(total_flops / (ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "step_roofline": {"unit": unit, "achieved": round(step_rate, 1),
+                          "frac": round(step_rate / peak, 4),
+                          "work": "touched bytes" if hbm else "active FLOPs"},
         "all_ones_ms_per_step": round(ms_ones, 4),
         "speedup_vs_all_ones": round(ms_ones / ms, 3),
         "kernels": per_kernel,
