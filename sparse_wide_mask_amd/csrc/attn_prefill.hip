@@ -41,8 +41,9 @@ __global__ void __launch_bounds__(256, 1)
                      uint16_t* __restrict__ Vt) {
   constexpr int BM = 256, BN = 256;
   using C = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::LDS_B];
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages * C::SA];
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages * C::SB];
+  const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB);
   __shared__ int sTok[BM];
 
   const int ntn = (r + 1) / 2 + 1;  // q tiles (2 heads each) + one k|v tile
@@ -68,76 +69,54 @@ __global__ void __launch_bounds__(256, 1)
   for (int i = tid; i < BM; i += C::kThreads) sTok[i] = i < rows ? gperm[(size_t)g * T + row0 + i] : -1;
   __syncthreads();
 
-  const int crow = tid >> 3, kc8 = (tid & 7) * 8;
-  const int dst0 = crow * kLdsLd + kc8;
+  const int chunk8 = dma_chunk(lane) * 8;
   const int nq = n_kv * r;
-  const rsrc_t rX = make_rsrc(X, (uint32_t)T * d * 2u);
-  const rsrc_t rQ = make_rsrc(Wq, (uint32_t)nq * kHd * d * 2u);
-  const rsrc_t rK = make_rsrc(Wk, (uint32_t)n_kv * kHd * d * 2u);
-  const rsrc_t rV = make_rsrc(Wv, (uint32_t)n_kv * kHd * d * 2u);
-  uint32_t aOff[C::A_CHUNKS];
+  const i32x4 rX = make_srd(X, (uint32_t)T * d * 2u);
+  const i32x4 rQ = make_srd(Wq, (uint32_t)nq * kHd * d * 2u);
+  const i32x4 rK = make_srd(Wk, (uint32_t)n_kv * kHd * d * 2u);
+  const i32x4 rV = make_srd(Wv, (uint32_t)n_kv * kHd * d * 2u);
+  uint32_t aOff[C::A_INST];
 #pragma unroll
-  for (int i = 0; i < C::A_CHUNKS; ++i) {
-    const int tok = sTok[crow + 32 * i];
-    aOff[i] = tok >= 0 ? (uint32_t)(tok * d + kc8) * 2u : (uint32_t)kSkip;
+  for (int q = 0; q < C::A_INST; ++q) {
+    const int tok = sTok[dma_row(wave, q, lane)];
+    aOff[q] = tok >= 0 ? (uint32_t)(tok * d + chunk8) * 2u : kSkip;
   }
-  // B row crow + 32 i of the tile: q tile -> Wq row g*r*hd + nt*256 + row;
-  // k|v tile -> Wk row g*hd + row (row < 128) or Wv row g*hd + row - 128.
-  uint32_t bOff[C::B_CHUNKS];
+  // B row of the tile: q tile -> Wq row g*r*hd + nt*256 + row; k|v tile -> Wk row
+  // g*hd + row (row < 128: instructions q = 0, 1) or Wv row g*hd + row - 128.
+  uint32_t bOff[C::B_INST];
 #pragma unroll
-  for (int i = 0; i < C::B_CHUNKS; ++i) {
-    const int row = crow + 32 * i;
+  for (int q = 0; q < C::B_INST; ++q) {
+    const int row = dma_row(wave, q, lane);
     const int wrow = kv_tile ? g * kHd + (row & (kHd - 1)) : g * r * kHd + nt * BN + row;
-    bOff[i] = (uint32_t)(wrow * d + kc8) * 2u;
+    bOff[q] = (uint32_t)(wrow * d + chunk8) * 2u;
   }
+  auto issue = [&](int kt, int st) {
+    const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
+    const uint32_t kb = (uint32_t)kt * kBK * 2u;
+#pragma unroll
+    for (int q = 0; q < C::A_INST; ++q) lds_dma16(rX, dma_dst(a, wave, q), aOff[q] + kb);
+    if (kv_tile) {
+#pragma unroll
+      for (int q = 0; q < C::B_INST; ++q)
+        lds_dma16(q < C::B_INST / 2 ? rK : rV, dma_dst(b, wave, q), bOff[q] + kb);
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::B_INST; ++q) lds_dma16(rQ, dma_dst(b, wave, q), bOff[q] + kb);
+    }
+  };
   uint32_t rb_live = 0;
 #pragma unroll
   for (int i = 0; i < C::RB; ++i)
     if (wm * C::WM + i * 32 < rows) rb_live |= 1u << i;
 
-  u32x4 ra[C::A_CHUNKS], rbuf[C::B_CHUNKS];
-  auto gload = [&](int k0) {
-    const uint32_t kb = (uint32_t)k0 * 2u;
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = ldbuf16(rX, aOff[i] + kb);
-    if (kv_tile) {
-#pragma unroll
-      for (int i = 0; i < C::B_CHUNKS; ++i) rbuf[i] = ldbuf16(i < C::B_CHUNKS / 2 ? rK : rV, bOff[i] + kb);
-    } else {
-#pragma unroll
-      for (int i = 0; i < C::B_CHUNKS; ++i) rbuf[i] = ldbuf16(rQ, bOff[i] + kb);
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA[buf] + dst0 + 32 * i * kLdsLd, ra[i]);
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB[buf] + dst0 + 32 * i * kLdsLd, rbuf[i]);
-  };
-
   WaveAcc<BM, BN> acc;
   acc.zero();
   const int nk = d / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  if (rb_live == C::kAllRows) {
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * kBK);
-      acc.sweep_full(sA[cur], sB[cur], wm, wn, lane);
-      if (kt + 1 < nk) lstore(cur ^ 1);
-      __syncthreads();
-    }
-  } else {
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * kBK);
-      acc.sweep_masked(sA[cur], sB[cur], wm, wn, lane, rb_live);
-      if (kt + 1 < nk) lstore(cur ^ 1);
-      __syncthreads();
-    }
-  }
+  auto live = [&](int) { return rb_live; };
+  if (rb_live == C::kAllRows)
+    acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+  else
+    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
 
   // epilogue.  This wave's 128 columns are one head: q head 2*nt + wn, or k / v.
   // (With an odd head ratio the last q tile's second half reads zeros or the next

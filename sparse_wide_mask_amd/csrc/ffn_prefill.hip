@@ -39,6 +39,11 @@ WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& m
   nt = c % ntn;
 }
 
+#define WIDE_STAGE_ARRAYS(C)                                               \
+  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages * C::SA];      \
+  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages * C::SB];      \
+  const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB)
+
 template <int BM, int BN>
 __global__ void __launch_bounds__(256, 1)
     ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
@@ -47,8 +52,7 @@ __global__ void __launch_bounds__(256, 1)
                    int mtiles, int ntn, uint16_t* __restrict__ H) {
   using C = TileCfg<BM, BN>;
   constexpr int BNH = BN / 2;  // channels per tile (gate and up each)
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::LDS_B];
+  WIDE_STAGE_ARRAYS(C);
   __shared__ int sTok[BM];
 
   int g, mt, nt;
@@ -62,70 +66,50 @@ __global__ void __launch_bounds__(256, 1)
   for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gperm[(size_t)g * T + row0 + r] : -1;
   __syncthreads();
 
-  // Chunk i of this thread: tile row crow + 32 i, 16-byte column kc8.
-  const int crow = tid >> 3, kc8 = (tid & 7) * 8;
-  const int dst0 = crow * kLdsLd + kc8;
-  const rsrc_t rX = make_rsrc(X, (uint32_t)T * d * 2u);
-  const rsrc_t rG = make_rsrc(Wg, (uint32_t)F * d * 2u);
-  const rsrc_t rU = make_rsrc(Wu, (uint32_t)F * d * 2u);
-  uint32_t aOff[C::A_CHUNKS];
+  const int chunk8 = dma_chunk(lane) * 8;
+  const i32x4 rX = make_srd(X, (uint32_t)T * d * 2u);
+  const i32x4 rG = make_srd(Wg, (uint32_t)F * d * 2u);
+  const i32x4 rU = make_srd(Wu, (uint32_t)F * d * 2u);
+  uint32_t aOff[C::A_INST];
 #pragma unroll
-  for (int i = 0; i < C::A_CHUNKS; ++i) {
-    const int tok = sTok[crow + 32 * i];
-    aOff[i] = tok >= 0 ? (uint32_t)(tok * d + kc8) * 2u : (uint32_t)kSkip;  // l=1: no load
+  for (int q = 0; q < C::A_INST; ++q) {
+    const int tok = sTok[dma_row(wave, q, lane)];
+    aOff[q] = tok >= 0 ? (uint32_t)(tok * d + chunk8) * 2u : kSkip;  // l=1: no load
   }
-  // B row crow + 32 i: slab (i % (WN/32)) of wave column (32 i) / WN; even slabs gate, odd up.
-  uint32_t bOff[C::B_CHUNKS];
+  // B row nrow: wave column nrow / WN; 32-row slabs alternate gate / up so that a
+  // lane holds gate and up of the same channel.
+  uint32_t bOff[C::B_INST];
+  int bUp[C::B_INST];
 #pragma unroll
-  for (int i = 0; i < C::B_CHUNKS; ++i) {
-    const int w = (32 * i) / C::WN, blk = i % (C::WN / 32);
-    const int ch = nt * BNH + w * (C::WN / 2) + (blk >> 1) * 32 + crow;
-    bOff[i] = (uint32_t)((g * G + ch) * d + kc8) * 2u;
+  for (int q = 0; q < C::B_INST; ++q) {
+    const int nrow = dma_row(wave, q, lane);
+    const int w = nrow / C::WN, local = nrow % C::WN, blk = local >> 5;
+    const int ch = nt * BNH + w * (C::WN / 2) + (blk >> 1) * 32 + (local & 31);
+    bOff[q] = (uint32_t)((g * G + ch) * d + chunk8) * 2u;
+    bUp[q] = __builtin_amdgcn_readfirstlane(blk & 1);
   }
+  auto issue = [&](int kt, int st) {
+    const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
+    const uint32_t kb = (uint32_t)kt * kBK * 2u;
+#pragma unroll
+    for (int q = 0; q < C::A_INST; ++q) lds_dma16(rX, dma_dst(a, wave, q), aOff[q] + kb);
+#pragma unroll
+    for (int q = 0; q < C::B_INST; ++q) lds_dma16(bUp[q] ? rU : rG, dma_dst(b, wave, q), bOff[q] + kb);
+  };
 
   uint32_t rb_live = 0;
 #pragma unroll
   for (int i = 0; i < C::RB; ++i)
     if (wm * C::WM + i * 32 < rows) rb_live |= 1u << i;
 
-  u32x4 ra[C::A_CHUNKS], rbuf[C::B_CHUNKS];
-  auto gload = [&](int k0) {
-    const uint32_t kb = (uint32_t)k0 * 2u;
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) ra[i] = ldbuf16(rX, aOff[i] + kb);
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) rbuf[i] = ldbuf16((i & 1) ? rU : rG, bOff[i] + kb);
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA[buf] + dst0 + 32 * i * kLdsLd, ra[i]);
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB[buf] + dst0 + 32 * i * kLdsLd, rbuf[i]);
-  };
-
   WaveAcc<BM, BN> acc;
   acc.zero();
   const int nk = d / kBK;
-  gload(0);
-  lstore(0);
-  __syncthreads();
-  if (rb_live == C::kAllRows) {  // every row block of this wave holds kept rows
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * kBK);
-      acc.sweep_full(sA[cur], sB[cur], wm, wn, lane);
-      if (kt + 1 < nk) lstore(cur ^ 1);
-      __syncthreads();
-    }
-  } else {  // tail tile of the group: l=2 skips the empty row blocks
-    for (int kt = 0; kt < nk; ++kt) {
-      const int cur = kt & 1;
-      if (kt + 1 < nk) gload((kt + 1) * kBK);
-      acc.sweep_masked(sA[cur], sB[cur], wm, wn, lane, rb_live);
-      if (kt + 1 < nk) lstore(cur ^ 1);
-      __syncthreads();
-    }
-  }
+  auto live = [&](int) { return rb_live; };
+  if (rb_live == C::kAllRows)  // every row block of this wave holds kept rows
+    acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+  else  // tail tile of the group: l=2 skips the row blocks with no kept token
+    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
 
   // epilogue: H[token, gG + ch] = silu(gate) * up
 #pragma unroll
@@ -147,15 +131,15 @@ __global__ void __launch_bounds__(256, 1)
 template <int BM, int BN>
 __global__ void __launch_bounds__(256, 1)
     kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
-                     const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
-                     const int32_t* __restrict__ tgroups, int T, int d, int F, int n, int G,
-                     int nw, int ntn, const uint16_t* __restrict__ residual,
-                     uint16_t* __restrict__ Y) {
+                       const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
+                       const int32_t* __restrict__ tgroups, int T, int d, int F, int n, int G,
+                       int nw, int ntn, const uint16_t* __restrict__ residual,
+                       uint16_t* __restrict__ Y) {
   using C = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[2][C::LDS_A];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[2][C::LDS_B];
+  WIDE_STAGE_ARRAYS(C);
   __shared__ uint64_t sBits[BM * 4];
   __shared__ int sGroups[256];
+  __shared__ uint8_t sLive[256 * 4];
 
   // XCD x takes a contiguous stretch of the block-rasterised tile order.
   const int mtiles = (T + BM - 1) / BM, n_tiles = mtiles * ntn;
@@ -173,44 +157,46 @@ __global__ void __launch_bounds__(256, 1)
   for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
   __syncthreads();
 
-  // Chunk i of this thread: tile row crow + 32 i, 16-byte column kc8.
-  const int crow = tid >> 3, kc8 = (tid & 7) * 8;
-  const int dst0 = crow * kLdsLd + kc8;
-  const rsrc_t rH = make_rsrc(H, (uint32_t)T * F * 2u);
-  const rsrc_t rW = make_rsrc(Wdp, (uint32_t)F * d * 2u);
-  const uint32_t aBase = (uint32_t)((t0 + crow) * F + kc8) * 2u;
-  const uint32_t bBase = (uint32_t)((n0 + crow) * G + kc8) * 2u;
-
-  const int kpg = G / kBK;
+  const int chunk8 = dma_chunk(lane) * 8;
+  const i32x4 rH = make_srd(H, (uint32_t)T * F * 2u);
+  const i32x4 rW = make_srd(Wdp, (uint32_t)F * d * 2u);
+  int aRow[C::A_INST];
+  uint32_t aBase[C::A_INST], bOff[C::B_INST];
+#pragma unroll
+  for (int q = 0; q < C::A_INST; ++q) {
+    aRow[q] = dma_row(wave, q, lane);
+    aBase[q] = (uint32_t)((t0 + aRow[q]) * F + chunk8) * 2u;
+  }
+#pragma unroll
+  for (int q = 0; q < C::B_INST; ++q) {
+    const int nrow = n0 + dma_row(wave, q, lane);
+    bOff[q] = nrow < d ? (uint32_t)(nrow * G + chunk8) * 2u : kSkip;
+  }
+  const int kpg = G / kBK;  // K slices per group
   const int nk = ng * kpg;
-  u32x4 ra[C::A_CHUNKS], rbuf[C::B_CHUNKS];
-  auto gload = [&](int it) {
-    const int g = sGroups[it / kpg], kk = (it % kpg) * kBK;
+  auto issue = [&](int kt, int st) {
+    const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
+    const int g = sGroups[kt / kpg], kk = (kt % kpg) * kBK;
     const uint64_t sel = 1ull << (g & 63);
     const int w = g >> 6;
     const uint32_t ka = (uint32_t)(g * G + kk) * 2u;
 #pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) {
-      const int row = crow + 32 * i;
-      const bool keep = row < rows && (sBits[row * 4 + w] & sel);
-      // l=1: rows of tokens that dropped g are not fetched (zeros)
-      ra[i] = ldbuf16(rH, keep ? aBase + (uint32_t)(32 * i * F) * 2u + ka : (uint32_t)kSkip);
+    for (int q = 0; q < C::A_INST; ++q) {
+      // l=1: rows of tokens that dropped g (or past T) are not fetched (zeros)
+      const bool keep = aRow[q] < rows && (sBits[aRow[q] * 4 + w] & sel);
+      lds_dma16(rH, dma_dst(a, wave, q), keep ? aBase[q] + ka : kSkip);
     }
     const uint32_t kb = (uint32_t)(g * d * G + kk) * 2u;
 #pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) {
-      const bool ok = n0 + crow + 32 * i < d;
-      rbuf[i] = ldbuf16(rW, ok ? bBase + (uint32_t)(32 * i * G) * 2u + kb : (uint32_t)kSkip);
-    }
+    for (int q = 0; q < C::B_INST; ++q)
+      lds_dma16(rW, dma_dst(b, wave, q), bOff[q] == kSkip ? kSkip : bOff[q] + kb);
   };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < C::A_CHUNKS; ++i) st16(sA[buf] + dst0 + 32 * i * kLdsLd, ra[i]);
-#pragma unroll
-    for (int i = 0; i < C::B_CHUNKS; ++i) st16(sB[buf] + dst0 + 32 * i * kLdsLd, rbuf[i]);
-  };
-  // Row blocks of this wave holding at least one token that keeps group g.
-  auto live_blocks = [&](int g) {
+  // l=2: per group of the tile, the row blocks of each wave that hold at least one
+  // token keeping it (sLive[group index][wave]); a wave whose blocks are all live
+  // for every group runs the branch-free loop.
+  bool all_live = true;
+  for (int gi = 0; gi < ng; ++gi) {
+    const int g = sGroups[gi];
     const uint64_t sel = 1ull << (g & 63);
     const int w = g >> 6;
     uint32_t live = 0;
@@ -220,26 +206,18 @@ __global__ void __launch_bounds__(256, 1)
       const bool k = row < rows && (sBits[row * 4 + w] & sel);
       if (ballot(k)) live |= 1u << i;
     }
-    return live;
-  };
+    if (lane == 0) sLive[gi * 4 + wave] = (uint8_t)live;
+    all_live = all_live && live == C::kAllRows;
+  }
+  __syncthreads();
 
   WaveAcc<BM, BN> acc;
   acc.zero();
-  if (nk > 0) {
-    gload(0);
-    lstore(0);
-    __syncthreads();
-  }
-  uint32_t rb_live = 0;
-  for (int it = 0; it < nk; ++it) {
-    const int cur = it & 1;
-    // l=2: 32-row blocks without a token that keeps the group skip their MFMAs
-    if (it % kpg == 0) rb_live = live_blocks(sGroups[it / kpg]);
-    if (it + 1 < nk) gload(it + 1);
-    acc.sweep_masked(sA[cur], sB[cur], wm, wn, lane, rb_live);
-    if (it + 1 < nk) lstore(cur ^ 1);
-    __syncthreads();
-  }
+  if (all_live)
+    acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, [](int) { return 0u; });
+  else
+    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue,
+                                      [&](int kt) { return (uint32_t)sLive[(kt / kpg) * 4 + wave]; });
 
   // The residual pointer passes through an empty asm here so its loads are not
   // hoisted into the K loop, where they would push accumulators out of registers.

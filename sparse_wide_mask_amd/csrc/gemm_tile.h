@@ -1,26 +1,31 @@
 // Block-tile bf16 MFMA engine shared by the prefill GEMMs.
 //
-// A workgroup of 256 threads (4 waves, 2 x 2) owns a BM x BN output tile and
-// walks K in steps of BK = 64.  Both operands are K-contiguous in global memory
-// (activations row-major over d_model, weights as nn.Linear rows or as packed
-// K-major group blocks), so each lane moves 16-byte chunks and each wave feeds
-// v_mfma_f32_32x32x16_bf16 from padded LDS rows with 16-byte reads.
+// A work-group of 256 threads (4 waves, 2 x 2) owns a BM x BN output tile and
+// walks K in slices of BK = 32.  Both operands are K-contiguous in global memory,
+// so every lane moves 16-byte chunks, and each wave feeds
+// v_mfma_f32_32x32x16_bf16 from LDS.
 //
-// Global operands are read with raw buffer loads: a lane whose offset lies past
-// the buffer's num_records gets zeros without touching memory.  That is how rows
-// of tokens that dropped a group are skipped at load time (intra-block skipping
-// at the load stage) without a branch.  LDS is double-buffered: the loads of
-// step k+1 are issued before the MFMAs of step k and land in the other buffer,
-// so each K step needs one barrier.
+// Global -> LDS uses buffer loads that write LDS directly (no VGPR staging), so
+// slices can be fetched STAGES-1 = 3 steps ahead of the MFMAs that consume them.
+// A lane whose buffer offset is past num_records reads zeros without touching
+// memory: that is how rows of tokens that dropped a group are skipped at the load
+// stage.  Before a stage is read, every wave waits for its own loads of that
+// stage (vmcnt; a wave's loads complete in issue order) and then meets the others
+// at a barrier.
+//
+// LDS layout of a slice: rows of 32 bf16 (64 bytes = 4 chunks of 16 bytes);
+// chunk c of row r sits in slot c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3,
+// which keeps the 16-byte fragment reads of 32 consecutive rows free of bank
+// conflicts for both 32- and 64-bank LDS organisations.
 #pragma once
 
 #include "common.h"
 
 namespace wide {
 
-constexpr int kBK = 64;
-constexpr int kLdsLd = kBK + 8;  // LDS row pitch in bf16 (144 bytes: 16-byte aligned, skewed banks)
-constexpr int kSkip = 0x7fffff00;  // buffer offset past any num_records: load returns zeros
+constexpr int kBK = 32;
+constexpr int kStages = 4;
+constexpr uint32_t kSkip = 0x7fffff00u;  // buffer offset past any num_records: zeros
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
@@ -28,12 +33,40 @@ WIDE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
                                            0x00020000);
 }
-WIDE_DEV u32x4 ldbuf16(rsrc_t r, int byte_off) {
-  return __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, 0);
+WIDE_DEV u32x4 ldbuf16(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
-WIDE_DEV u32x4 ld16(const uint16_t* p) { return *reinterpret_cast<const u32x4*>(p); }
-WIDE_DEV void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
+typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) uint16_t lds_u16;
+
+// Buffer descriptor as four scalar dwords (base, stride 0, num_records, format).
+WIDE_DEV i32x4 make_srd(const void* base, uint32_t bytes) {
+  const uint64_t p = reinterpret_cast<uint64_t>(base);
+  return i32x4{(int32_t)(uint32_t)p, (int32_t)(uint32_t)(p >> 32), (int32_t)bytes, 0x00020000};
+}
+// LDS byte address of a pointer into __shared__ memory.
+WIDE_DEV uint32_t lds_addr(const uint16_t* p) {
+  return (uint32_t)reinterpret_cast<uintptr_t>((lds_u16*)(p));
+}
+// 16 bytes per lane from the buffer straight into LDS: lane l lands at
+// lds + 16 l (lds is wave-uniform).  Written as asm so the compiler does not
+// track the LDS write: the K loop orders it explicitly (vmcnt wait + barrier
+// before a stage is read, barrier before a stage is refilled).
+WIDE_DEV void lds_dma16(i32x4 srd, uint32_t lds, uint32_t byte_off) {
+  asm volatile("s_mov_b32 m0, %0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :
+               : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(srd)
+               : "memory", "m0");
+}
+WIDE_DEV int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
 WIDE_DEV bf16x8 lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
+
+// Wait until at most N of this wave's buffer loads are in flight (and its LDS
+// reads are done), then barrier.
+template <int N>
+WIDE_DEV void stage_barrier() {
+  asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
+}
 
 // Block rasterisation of a rows x cols tile grid: stripes of MB tile rows; inside
 // a stripe, blocks of CBk tile columns with the row index fastest.  Consecutive
@@ -55,20 +88,35 @@ struct TileCfg {
   static constexpr int kThreads = 256;
   static constexpr int WM = BM / 2, WN = BN / 2;   // per-wave tile
   static constexpr int RB = WM / 32, CB = WN / 32; // 32x32 MFMA blocks per wave
-  static constexpr int A_CHUNKS = BM * kBK / 8 / kThreads;
-  static constexpr int B_CHUNKS = BN * kBK / 8 / kThreads;
-  static constexpr int LDS_A = BM * kLdsLd;
-  static constexpr int LDS_B = BN * kLdsLd;
+  // buffer->LDS instructions per thread and slice: one instruction of a wave
+  // fills 16 rows (1 KB); the 4 waves share the rows of the tile.
+  static constexpr int A_INST = BM / 64;
+  static constexpr int B_INST = BN / 64;
+  static constexpr int LOADS = A_INST + B_INST;
+  static constexpr int SA = BM * kBK;  // elements per stage
+  static constexpr int SB = BN * kBK;
   static constexpr uint32_t kAllRows = (1u << RB) - 1u;
-  static_assert(WM % 32 == 0 && WN % 32 == 0, "wave tile must be whole 32x32 blocks");
-  static_assert(A_CHUNKS >= 1 && B_CHUNKS >= 1, "tile too small for 256 threads");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % 64 == 0 && BN % 64 == 0, "tile shape");
 };
 
-// Accumulators of one wave and the MFMA sweep over one BK slice held in LDS.
+// Row of the tile filled by lane `lane` of wave `wave` in its instruction q, and
+// the logical 16-byte chunk that lane fetches for the swizzled layout.
+WIDE_DEV int dma_row(int wave, int q, int lane) { return 16 * (4 * q + wave) + (lane >> 2); }
+WIDE_DEV int dma_chunk(int lane) { return (lane & 3) ^ swz(lane >> 2); }
+WIDE_DEV uint32_t dma_dst(uint32_t stage_addr, int wave, int q) {
+  return stage_addr + 16 * (4 * q + wave) * kBK * 2;
+}
+
+// Accumulators of one wave and its pipelined K loop.
 template <int BM, int BN>
 struct WaveAcc {
   using C = TileCfg<BM, BN>;
   f32x16 acc[C::RB][C::CB];
+
+  // fragments of one 16-wide K step: RB A blocks and CB B blocks
+  struct Frags {
+    bf16x8 a[C::RB], b[C::CB];
+  };
 
   WIDE_DEV void zero() {
 #pragma unroll
@@ -79,68 +127,72 @@ struct WaveAcc {
         for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.f;
   }
 
-  // Every row block live: fragments of slice ks+1 are read while slice ks multiplies.
-  WIDE_DEV void sweep_full(const uint16_t* sA, const uint16_t* sB, int wm, int wn, int lane) {
-    const int r = lane & 31, kh = (lane >> 5) * 8;
-    const uint16_t* pa = sA + (wm * C::WM + r) * kLdsLd + kh;
-    const uint16_t* pb = sB + (wn * C::WN + r) * kLdsLd + kh;
-    bf16x8 a[2][C::RB], b[2][C::CB];
+  WIDE_DEV static void read(Frags& f, const uint16_t* sA, const uint16_t* sB, int wm, int wn,
+                            int lane, int ks) {
+    const int r = lane & 31, slot = ((2 * ks + (lane >> 5)) ^ swz(r)) * 8;
+    const uint16_t* pa = sA + (wm * C::WM + r) * kBK + slot;
+    const uint16_t* pb = sB + (wn * C::WN + r) * kBK + slot;
 #pragma unroll
-    for (int i = 0; i < C::RB; ++i) a[0][i] = lds_frag(pa + i * 32 * kLdsLd);
+    for (int i = 0; i < C::RB; ++i) f.a[i] = lds_frag(pa + i * 32 * kBK);
 #pragma unroll
-    for (int j = 0; j < C::CB; ++j) b[0][j] = lds_frag(pb + j * 32 * kLdsLd);
+    for (int j = 0; j < C::CB; ++j) f.b[j] = lds_frag(pb + j * 32 * kBK);
+  }
+
+  // rb_live bit i = row block i of this wave has live rows; the other blocks skip
+  // their MFMAs (intra-block skipping at the MMA stage).
+  template <bool ALL>
+  WIDE_DEV void mma(const Frags& f, uint32_t rb_live) {
 #pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;
-      if (ks + 1 < kBK / 16) {
+    for (int i = 0; i < C::RB; ++i) {
+      if (!ALL && !((rb_live >> i) & 1u)) continue;
 #pragma unroll
-        for (int i = 0; i < C::RB; ++i) a[nxt][i] = lds_frag(pa + i * 32 * kLdsLd + (ks + 1) * 16);
-#pragma unroll
-        for (int j = 0; j < C::CB; ++j) b[nxt][j] = lds_frag(pb + j * 32 * kLdsLd + (ks + 1) * 16);
-      }
-      // keep the reads of slice ks+1 ahead of the MFMAs of slice ks
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < C::RB; ++i)
-#pragma unroll
-        for (int j = 0; j < C::CB; ++j) acc[i][j] = mfma32(a[cur][i], b[cur][j], acc[i][j]);
-      __builtin_amdgcn_sched_barrier(0);
+      for (int j = 0; j < C::CB; ++j) acc[i][j] = mfma32(f.a[i], f.b[j], acc[i][j]);
     }
   }
 
-  // Some row blocks may hold no live row: their MFMAs are skipped (intra-block
-  // skipping at the MMA stage).  rb_live bit i = row block i has work.  Fragments
-  // of slice ks+1 are read before the MFMAs of slice ks, as in sweep_full.
-  WIDE_DEV void sweep_masked(const uint16_t* sA, const uint16_t* sB, int wm, int wn, int lane,
-                             uint32_t rb_live) {
-    const int r = lane & 31, kh = (lane >> 5) * 8;
-    const uint16_t* pa = sA + (wm * C::WM + r) * kLdsLd + kh;
-    const uint16_t* pb = sB + (wn * C::WN + r) * kLdsLd + kh;
-    bf16x8 a[2][C::RB], b[2][C::CB];
+  // K slices 0..nk-1 with STAGES-1 slices of loads in flight.  sA/sB hold the
+  // STAGES slices back to back; issue(kt, stage) starts the loads of slice kt into
+  // that stage; live(kt) gives the live row blocks of slice kt.  The LDS reads of
+  // the next 16-wide step are issued before the MFMAs of the current one, across
+  // slice boundaries too: read(kt, hi); mma(kt, lo); barrier(kt+1);
+  // issue(kt+4); read(kt+1, lo); mma(kt, hi).  The barrier before slice kt+1 is
+  // read also guarantees every wave finished reading slice kt, whose stage the
+  // following issue refills.
+  template <bool ALL, int LOADS, class Issue, class Live>
+  WIDE_DEV void run(int nk, const uint16_t* sA, const uint16_t* sB, int wm, int wn, int lane,
+                    Issue&& issue, Live&& live) {
+    if (nk <= 0) return;
 #pragma unroll
-    for (int i = 0; i < C::RB; ++i) a[0][i] = lds_frag(pa + i * 32 * kLdsLd);
-#pragma unroll
-    for (int j = 0; j < C::CB; ++j) b[0][j] = lds_frag(pb + j * 32 * kLdsLd);
-#pragma unroll
-    for (int ks = 0; ks < kBK / 16; ++ks) {
-      const int cur = ks & 1, nxt = cur ^ 1;
-      if (ks + 1 < kBK / 16) {
-#pragma unroll
-        for (int i = 0; i < C::RB; ++i) a[nxt][i] = lds_frag(pa + i * 32 * kLdsLd + (ks + 1) * 16);
-#pragma unroll
-        for (int j = 0; j < C::CB; ++j) b[nxt][j] = lds_frag(pb + j * 32 * kLdsLd + (ks + 1) * 16);
+    for (int s = 0; s < kStages - 1; ++s)
+      if (s < nk) issue(s, s);
+    if (nk >= kStages - 1)
+      stage_barrier<(kStages - 2) * LOADS>();
+    else
+      stage_barrier<0>();
+    if (kStages - 1 < nk) issue(kStages - 1, kStages - 1);
+    Frags lo, hi;
+    read(lo, sA, sB, wm, wn, lane, 0);
+    for (int kt = 0; kt < nk; ++kt) {
+      const int st = kt & (kStages - 1);
+      const uint32_t lv = ALL ? C::kAllRows : live(kt);
+      read(hi, sA + st * C::SA, sB + st * C::SB, wm, wn, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(lo, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
+        if (kt + kStages - 1 < nk)
+          stage_barrier<(kStages - 2) * LOADS>();
+        else
+          stage_barrier<0>();
+        if (kt + kStages < nk) issue(kt + kStages, st);
+        const int nx = (st + 1) & (kStages - 1);
+        read(lo, sA + nx * C::SA, sB + nx * C::SB, wm, wn, lane, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < C::RB; ++i) {
-        if (!((rb_live >> i) & 1u)) continue;
-#pragma unroll
-        for (int j = 0; j < C::CB; ++j) acc[i][j] = mfma32(a[cur][i], b[cur][j], acc[i][j]);
-      }
+      mma<ALL>(hi, lv);
       __builtin_amdgcn_sched_barrier(0);
     }
   }
-
 };
 
 }  // namespace wide
