@@ -85,8 +85,8 @@ bool ffn_streaming(int T, int mode) { return mode == WIDE_DECODE && T <= kMaxDec
 FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
   (void)d;
   FfnWs w;
-  // streaming: one tile spans the batch, so tile_groups[0] is the batch's union
-  w.rv = carve_reorder(c, T, n, ffn_streaming(T, mode) ? (T > 0 ? T : 1) : ffn_down_tile_m(), false);
+  // streaming decode reorders inside its kernels
+  if (!ffn_streaming(T, mode)) w.rv = carve_reorder(c, T, n, ffn_down_tile_m(), false);
   w.H = c.take<uint16_t>((size_t)T * F);
   return w;
 }
@@ -94,11 +94,12 @@ FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
 int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const uint16_t* Wu,
             const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
             uint16_t* Y, const FfnWs& w, hipStream_t s) {
-  run_reorder(mask, T, n, w.rv, s);
-  if (ffn_streaming(T, mode))
-    launch_ffn_decode(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
-  else
+  if (ffn_streaming(T, mode)) {
+    launch_ffn_decode(X, mask, Wg, Wu, Wdp, T, d, F, n, residual, w.H, Y, s);
+  } else {
+    run_reorder(mask, T, n, w.rv, s);
     launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
+  }
   return WIDE_OK;
 }
 
@@ -141,7 +142,6 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
   if (mode == WIDE_DECODE) {
     const int nch = attn_decode_chunks(kv_cap > 0 ? kv_cap - 1 : 0);
-    w.rv = carve_reorder(c, T, nkv, T > 0 ? T : 1, false);
     w.Qc = c.take<uint16_t>((size_t)T * nq * kHeadDim);
     w.O = c.take<uint16_t>((size_t)T * nq * kHeadDim);
     w.Opart = c.take<float>((size_t)T * nq * nch * kHeadDim);
@@ -162,13 +162,13 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
               int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
               const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
-  run_reorder(mask, T, nkv, w.rv, s);
   if (mode == WIDE_DECODE) {
-    launch_attn_decode(X, mask, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache,
-                       kv_len, kv_cap, w.Qc, w.Opart, w.Mpart, w.Lpart, w.O, s);
-    launch_kmask_decode("attn_o_decode", w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
+    launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
+                       kv_cap, w.Qc, w.Opart, w.Mpart, w.Lpart, w.O, s);
+    launch_kmask_decode("attn_o_decode", w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, Y, s);
     return;
   }
+  run_reorder(mask, T, nkv, w.rv, s);
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
   launch_kmask_gemm("attn_o", w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
 }

@@ -1,26 +1,32 @@
 // Decode (a small batch of single tokens): weight streaming over the touched
 // groups only (gist.science technical summary §2.C, block-level skipping).
 //
-// The mask reordering runs with one tile spanning the batch, so tile_groups[0]
-// is the union of the groups any token of the batch keeps; a weight block
-// outside it is never read.  Kernels (batch B <= 64):
+// A decode batch has at most 64 tokens, so one wave holds a group's mask column
+// (lane = token) and the mask reordering is done inside the kernels that need
+// it: a ballot over the column gives the kept tokens, and their ranks among the
+// set bits give the stable kept-first order.  No separate reorder launch runs.
+// Kernels (batch B <= 64):
 //
 // nmask_decode   N-masked projection (FFN gate+up, or attention q/k/v).  One
-//                work-group = (group, 16 output rows); it exits at once when no
-//                token keeps the group (l=0).  The rows of the tokens that keep
-//                the group (group_perm prefix) are the MFMA rows (16x16x32),
-//                padded to 16 (l=2: row blocks past the count are skipped); the
-//                4 waves split d_model and reduce through LDS.  Epilogue: SwiGLU
-//                into H, or RoPE at position kv_len and the q / new k,v writes
-//                (k and v straight into the caches at slot kv_len).
+//                work-group = (group, 16 MFMA output columns); it exits at once
+//                when no token keeps the group (l=0).  The tokens that keep the
+//                group, in order, are the MFMA rows (16x16x32), padded to 16
+//                (l=2: row blocks past the count are skipped); the 4 waves split
+//                d_model and reduce through LDS.  FFN: the 16 columns are 8 gate
+//                and the matching 8 up channels, so SwiGLU pairs lanes ch and
+//                ch+8; epilogue writes H.  Attention: RoPE at position kv_len and
+//                the q / new k,v writes (k and v straight into the caches at slot
+//                kv_len).
 // kmask_decode   K-masked projection (FFN down, attention out).  One work-group =
-//                16 output columns; the waves split the union groups; rows of
-//                tokens that dropped a group are not loaded (l=1).
+//                16 output columns; it packs the batch's mask into bit words and
+//                their union in LDS, then its 8 waves split the union groups; rows
+//                of tokens that dropped a group are not loaded (l=1).
 // attn_decode_partial / attn_decode_combine
 //                split-KV attention of each kept (token, group) over cache slots
 //                0..kv_len (the new token included), 256 keys per work-group,
 //                then a log-sum-exp combine of the chunks.
 #include "common.h"
+#include "gemm_tile.h"
 #include "internal.h"
 
 namespace wide {
@@ -32,33 +38,51 @@ constexpr int kHdD = 128;
 // Mode of nmask_decode.
 enum { kNmFfn = 0, kNmQkv = 1 };
 
-template <int MODE>
+// Weight loads of this many 32-wide K steps are issued before their MFMAs, with
+// the matching activation loads: W takes 4 VGPRs per step and X 4 per step and
+// row block, so fewer steps are batched when the batch spans more row blocks.
+template <int NRB>
+constexpr int dec_unroll() { return NRB == 1 ? 16 : NRB == 2 ? 8 : 4; }
+
+// Activation operand of one 16x16x32 step: a buffer load whose offset is past the
+// buffer for rows without a token, so it returns zeros and is never a branch.
+WIDE_DEV bf16x8 xload(rsrc_t r, uint32_t off) {
+  const u32x4 v = ldbuf16(r, off);
+  return *reinterpret_cast<const bf16x8*>(&v);
+}
+
+template <int MODE, int NRB>
 __global__ void __launch_bounds__(256)
     nmask_decode(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W0,
                  const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
-                 const int32_t* __restrict__ gcount, const int32_t* __restrict__ gperm, int B,
-                 int d, int G, int chunks, int r, int kv_len, int kv_cap, float log2_theta,
-                 uint16_t* __restrict__ out0, uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc,
-                 int n_groups) {
-  constexpr int NM = MODE == kNmFfn ? 2 : 1;  // matrices per work-group
+                 const uint8_t* __restrict__ mask, int B, int d, int G, int chunks, int r,
+                 int kv_len, int kv_cap, float log2_theta, uint16_t* __restrict__ out0,
+                 uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc, int n_groups) {
   __shared__ int sTok[kDecRows];
-  __shared__ float sRed[3][kDecRows][16 * NM];
+  __shared__ float sRed[3][kDecRows][16];
 
   const int g = blockIdx.x / chunks, cb = blockIdx.x % chunks;
-  const int cnt = gcount[g];
-  if (cnt == 0) return;  // l=0: no token of the batch keeps g
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < kDecRows; i += 256) sTok[i] = i < cnt ? gperm[(size_t)g * B + i] : -1;
+  // mask column of g, one token per lane: kept tokens in order are the MFMA rows
+  const rsrc_t mr = make_rsrc(mask, (uint32_t)(B * n_groups));
+  const bool kept = ldbuf1(mr, lane < B ? (uint32_t)(lane * n_groups + g) : kSkip) != 0u;
+  const uint64_t col = ballot(kept);
+  const int cnt = popc64(col);
+  if (cnt == 0) return;  // l=0: no token of the batch keeps g
+  if (wave == 0) {
+    if (kept) sTok[popc64(col & ((1ull << lane) - 1ull))] = lane;
+    if (lane >= cnt) sTok[lane] = -1;
+  }
   __syncthreads();
-  const int nrb = (cnt + 15) / 16;
+  const int nrb = (cnt + 15) / 16;  // l=2: row blocks past the count are skipped
 
-  // output row (16 per work-group) -> weight row
+  // MFMA column (16 per work-group) -> weight row
   const int ch = lane & 15;
-  const uint16_t* wrow[NM];
+  const uint16_t* wrow;
   int hh = 0, jrow = 0;
   if (MODE == kNmFfn) {
-    wrow[0] = W0 + (size_t)(g * G + cb * 16 + ch) * d;
-    wrow[NM - 1] = W1 + (size_t)(g * G + cb * 16 + ch) * d;
+    // columns 0..7: gate channels cb*8 + ch; columns 8..15: the same up channels
+    wrow = (ch < 8 ? W0 : W1) + (size_t)(g * G + cb * 8 + (ch & 7)) * d;
   } else {
     // chunk cb of head hh (q heads 0..r-1, then k, then v) covers head dims
     // {8c..8c+7} and {64+8c..64+8c+7}, so each RoPE pair stays in the work-group
@@ -66,48 +90,58 @@ __global__ void __launch_bounds__(256)
     const int c = cb % 8;
     jrow = ch < 8 ? 8 * c + ch : 64 + 8 * c + (ch - 8);
     if (hh < r)
-      wrow[0] = W0 + ((size_t)(g * r + hh) * kHdD + jrow) * d;
+      wrow = W0 + ((size_t)(g * r + hh) * kHdD + jrow) * d;
     else
-      wrow[0] = (hh == r ? W1 : W2) + ((size_t)g * kHdD + jrow) * d;
+      wrow = (hh == r ? W1 : W2) + ((size_t)g * kHdD + jrow) * d;
   }
 
-  f32x4 acc[NM][kDecRB];
+  f32x4 acc[NRB];
 #pragma unroll
-  for (int m = 0; m < NM; ++m)
-#pragma unroll
-    for (int rb = 0; rb < kDecRB; ++rb) acc[m][rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 
   const int nsteps = d / 32;  // 32-wide K steps, split evenly over the 4 waves
   const int kbeg = (wave * nsteps / 4) * 32, kend = ((wave + 1) * nsteps / 4) * 32;
   const int koff = 8 * (lane >> 4);
-  int xrow[kDecRB];
+  // X byte offsets of this lane's rows (k = koff); kSkip for rows without a token
+  const rsrc_t xr = make_rsrc(X, (uint32_t)((size_t)B * d * 2));
+  uint32_t xoff[NRB];
 #pragma unroll
-  for (int rb = 0; rb < kDecRB; ++rb) xrow[rb] = sTok[min(rb * 16 + ch, kDecRows - 1)];
-#pragma unroll 4
-  for (int k0 = kbeg; k0 < kend; k0 += 32) {
-    bf16x8 wf[NM];
+  for (int rb = 0; rb < NRB; ++rb) {
+    const int tok = sTok[rb * 16 + ch];
+    xoff[rb] = tok >= 0 ? (uint32_t)(((size_t)tok * d + koff) * 2) : kSkip;
+  }
+  const uint16_t* wp = wrow + koff;
+  constexpr int U = dec_unroll<NRB>();
+  int k0 = kbeg;
+  for (; k0 + 32 * U <= kend; k0 += 32 * U) {
+    bf16x8 wf[U], xf[U][NRB];
 #pragma unroll
-    for (int m = 0; m < NM; ++m) wf[m] = *reinterpret_cast<const bf16x8*>(wrow[m] + k0 + koff);
+    for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * u);
 #pragma unroll
-    for (int rb = 0; rb < kDecRB; ++rb) {
-      if (rb >= nrb) break;  // l=2
-      bf16x8 xf = {};
-      if (xrow[rb] >= 0) xf = *reinterpret_cast<const bf16x8*>(X + (size_t)xrow[rb] * d + k0 + koff);
+    for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int m = 0; m < NM; ++m) acc[m][rb] = mfma16(xf, wf[m], acc[m][rb]);
-    }
+      for (int rb = 0; rb < NRB; ++rb) xf[u][rb] = xload(xr, xoff[rb] + (k0 + 32 * u) * 2);
+    __builtin_amdgcn_sched_barrier(0);  // all loads of the batch before its MFMAs
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        if (rb < nrb) acc[rb] = mfma16(xf[u][rb], wf[u], acc[rb]);
+  }
+  for (; k0 < kend; k0 += 32) {
+    const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wp + k0);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      if (rb < nrb) acc[rb] = mfma16(xload(xr, xoff[rb] + k0 * 2), wf, acc[rb]);
   }
 
   // reduce the 4 K-quarters: waves 1..3 park partials in LDS, wave 0 adds
   if (wave > 0) {
 #pragma unroll
-    for (int rb = 0; rb < kDecRB; ++rb) {
+    for (int rb = 0; rb < NRB; ++rb) {
       if (rb >= nrb) break;
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int m = 0; m < NM; ++m)
-          sRed[wave - 1][rb * 16 + acc16_row(lane, i)][m * 16 + ch] = acc[m][rb][i];
+      for (int i = 0; i < 4; ++i) sRed[wave - 1][rb * 16 + acc16_row(lane, i)][ch] = acc[rb][i];
     }
   }
   __syncthreads();
@@ -118,24 +152,23 @@ __global__ void __launch_bounds__(256)
   float sn = 0.f, cs = 1.f;
   if (theta_inv != 0.f) sincosf((float)kv_len * theta_inv, &sn, &cs);
 #pragma unroll
-  for (int rb = 0; rb < kDecRB; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     if (rb >= nrb) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = rb * 16 + acc16_row(lane, i);
-      float v[NM];
-#pragma unroll
-      for (int m = 0; m < NM; ++m)
-        v[m] = acc[m][rb][i] + sRed[0][row][m * 16 + ch] + sRed[1][row][m * 16 + ch] +
-               sRed[2][row][m * 16 + ch];
+      const float v = acc[rb][i] + sRed[0][row][ch] + sRed[1][row][ch] + sRed[2][row][ch];
       const int tok = row < cnt ? sTok[row] : -1;
       if (MODE == kNmFfn) {
-        if (tok >= 0) out0[(size_t)tok * (n_groups * G) + g * G + cb * 16 + ch] = f2bf(silu(v[0]) * v[NM - 1]);
+        // SwiGLU: gate in column ch, its up partner in column ch + 8 (lane + 8)
+        const float up = __shfl_xor(v, 8);
+        if (tok >= 0 && ch < 8)
+          out0[(size_t)tok * (n_groups * G) + g * G + cb * 8 + ch] = f2bf(silu(v) * up);
       } else {
         // RoPE pair partner: channel ch^8 of the same row, held by lane ^ 8
-        const float other = __shfl_xor(v[0], 8);
-        float o = v[0];
-        if (theta_inv != 0.f) o = ch < 8 ? v[0] * cs - other * sn : v[0] * cs + other * sn;
+        const float other = __shfl_xor(v, 8);
+        float o = v;
+        if (theta_inv != 0.f) o = ch < 8 ? v * cs - other * sn : v * cs + other * sn;
         if (tok < 0) continue;
         const uint16_t bits = f2bf(o);
         if (hh < r)
@@ -149,54 +182,114 @@ __global__ void __launch_bounds__(256)
 
 // K-masked decode projection: Y[b, n] = sum over union groups g of
 // sum_j A[b, gG + j] Wp[g, n, j] over the tokens b that keep g (+ residual).
-__global__ void __launch_bounds__(256)
+constexpr int kKmWaves = 8;
+
+template <int NRB>
+__global__ void __launch_bounds__(64 * kKmWaves)
     kmask_decode(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
-                 const uint64_t* __restrict__ packed, const int32_t* __restrict__ ucount,
-                 const int32_t* __restrict__ ugroups, int B, int d, int F, int G, int nw,
+                 const uint8_t* __restrict__ mask, int B, int d, int F, int G, int n,
                  const uint16_t* __restrict__ residual, uint16_t* __restrict__ Y) {
   __shared__ uint64_t sBits[kDecRows * 4];
-  __shared__ float sRed[3][kDecRows][16];
+  __shared__ uint32_t sU[8];
+  __shared__ int sGroups[256];
+  __shared__ int sNu;
+  __shared__ float sRed[kKmWaves - 1][kDecRows][16];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
-  for (int i = tid; i < kDecRows * nw; i += 256) {
-    const int b = i / nw, w = i % nw;
-    sBits[b * 4 + w] = b < B ? packed[(size_t)b * nw + w] : 0ull;
-  }
+  if (tid < 8) sU[tid] = 0u;
   __syncthreads();
-  const int nu = ucount[0];
-  const int nrb = (B + 15) / 16;
-  const int ch = lane & 15, koff = 8 * (lane >> 4);
-  f32x4 acc[kDecRB];
+  // pack the batch's mask rows into bit words (ballot over 64 groups) and OR
+  // them into the batch union; all of a wave's loads are issued first
+  {
+    constexpr int kPer = kDecRows / kKmWaves;
+    const rsrc_t mr = make_rsrc(mask, (uint32_t)(B * n));
+    uint32_t v[kPer][4];
 #pragma unroll
-  for (int rb = 0; rb < kDecRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (int u = wave; u < nu; u += 4) {
-    const int g = ugroups[u];
-    const uint64_t sel = 1ull << (g & 63);
-    const int w = g >> 6;
-    bool keep[kDecRB];
+    for (int k = 0; k < kPer; ++k) {
+      const int b = wave + k * kKmWaves;
 #pragma unroll
-    for (int rb = 0; rb < kDecRB; ++rb) {
-      const int b = rb * 16 + ch;
-      keep[rb] = b < B && (sBits[b * 4 + w] & sel);
-    }
-    const uint16_t* wrow = Wp + ((size_t)g * d + n0 + ch) * G + koff;
-    const uint16_t* arow = A + (size_t)g * G + koff;
-#pragma unroll 4
-    for (int j0 = 0; j0 < G; j0 += 32) {
-      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wrow + j0);
-#pragma unroll
-      for (int rb = 0; rb < kDecRB; ++rb) {
-        if (rb >= nrb) break;
-        bf16x8 af = {};
-        if (keep[rb]) af = *reinterpret_cast<const bf16x8*>(arow + (size_t)(rb * 16 + ch) * F + j0);
-        acc[rb] = mfma16(af, wf, acc[rb]);
+      for (int w = 0; w < 4; ++w) {
+        const int g = 64 * w + lane;
+        v[k][w] = ldbuf1(mr, (b < B && g < n) ? (uint32_t)(b * n + g) : kSkip);
       }
     }
+    uint64_t uni[4] = {0, 0, 0, 0};
+#pragma unroll
+    for (int k = 0; k < kPer; ++k) {
+      const int b = wave + k * kKmWaves;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const uint64_t word = ballot(v[k][w] != 0u);
+        if (lane == 0) sBits[b * 4 + w] = word;
+        uni[w] |= word;
+      }
+    }
+    if (lane == 0)
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if ((uint32_t)uni[w]) atomicOr(&sU[2 * w], (uint32_t)uni[w]);
+        if ((uint32_t)(uni[w] >> 32)) atomicOr(&sU[2 * w + 1], (uint32_t)(uni[w] >> 32));
+      }
+  }
+  __syncthreads();
+  if (wave == 0) {  // ascending list of the union's groups
+    int written = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint64_t u = ((uint64_t)sU[2 * w + 1] << 32) | sU[2 * w];
+      if ((u >> lane) & 1ull) sGroups[written + popc64(u & ((1ull << lane) - 1ull))] = 64 * w + lane;
+      written += popc64(u);
+    }
+    if (lane == 0) sNu = written;
+  }
+  __syncthreads();
+  const int nu = sNu;
+  const int nrb = (B + 15) / 16;
+  const int ch = lane & 15, koff = 8 * (lane >> 4);
+  f32x4 acc[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the union's (group, 32-wide K step) pairs, split evenly over the waves
+  const int SG = G / 32, S = nu * SG;
+  const int sbeg = wave * S / kKmWaves, send = (wave + 1) * S / kKmWaves;
+  const rsrc_t ar = make_rsrc(A, (uint32_t)((size_t)B * F * 2));
+  // operands of step s: W row n0 + ch of group g, and the A rows of tokens that
+  // keep g (kSkip offset, so zeros, for the others: l=1)
+  auto operands = [&](int s, bf16x8& wf, bf16x8 (&af)[NRB]) {
+    const int q = s / SG, j0 = (s - q * SG) * 32;
+    const int g = sGroups[q];
+    wf = *reinterpret_cast<const bf16x8*>(Wp + ((size_t)g * d + n0 + ch) * G + j0 + koff);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int b = rb * 16 + ch;
+      const bool keep = (sBits[b * 4 + (g >> 6)] >> (g & 63)) & 1ull;
+      af[rb] = xload(ar, keep ? (uint32_t)(((size_t)b * F + (size_t)g * G + j0 + koff) * 2) : kSkip);
+    }
+  };
+  constexpr int U = dec_unroll<NRB>() < 8 ? dec_unroll<NRB>() : 8;
+  int s0 = sbeg;
+  for (; s0 + U <= send; s0 += U) {
+    bf16x8 wf[U], af[U][NRB];
+#pragma unroll
+    for (int u = 0; u < U; ++u) operands(s0 + u, wf[u], af[u]);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        if (rb < nrb) acc[rb] = mfma16(af[u][rb], wf[u], acc[rb]);
+  }
+  for (; s0 < send; ++s0) {
+    bf16x8 wf, af[NRB];
+    operands(s0, wf, af);
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb)
+      if (rb < nrb) acc[rb] = mfma16(af[rb], wf, acc[rb]);
   }
   if (wave > 0) {
 #pragma unroll
-    for (int rb = 0; rb < kDecRB; ++rb) {
+    for (int rb = 0; rb < NRB; ++rb) {
       if (rb >= nrb) break;
 #pragma unroll
       for (int i = 0; i < 4; ++i) sRed[wave - 1][rb * 16 + acc16_row(lane, i)][ch] = acc[rb][i];
@@ -205,13 +298,15 @@ __global__ void __launch_bounds__(256)
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
-  for (int rb = 0; rb < kDecRB; ++rb) {
+  for (int rb = 0; rb < NRB; ++rb) {
     if (rb >= nrb) break;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = rb * 16 + acc16_row(lane, i);
       if (b >= B) continue;
-      float v = acc[rb][i] + sRed[0][b][ch] + sRed[1][b][ch] + sRed[2][b][ch];
+      float v = acc[rb][i];
+#pragma unroll
+      for (int w = 0; w < kKmWaves - 1; ++w) v += sRed[w][b][ch];
       const size_t o = (size_t)b * d + n0 + ch;
       if (residual) v += bf2f(residual[o]);
       Y[o] = f2bf(v);
@@ -220,18 +315,28 @@ __global__ void __launch_bounds__(256)
 }
 
 constexpr int kKeyChunk = 256;
+constexpr int kKeyBlocks = kKeyChunk / 16 / 4;  // 16-key MFMA blocks per wave
 
-// One work-group = (token b, group g, chunk of 256 cache keys).  Scores with 16
-// lanes per key (8 head dims each), then per-head softmax statistics of the
-// chunk, then P V with 64 threads per head.  Writes unnormalised partial outputs.
+// One work-group = (token b, group g, chunk of 256 cache keys).  All of the
+// chunk's bytes are requested up front: the K rows into registers as MFMA
+// operands, the V rows straight into LDS by buffer->LDS loads, which land while
+// the scores are computed.
+//   scores  S^T[key, h] = K[key, :] . Q[h, :] with v_mfma_f32_16x16x32_bf16:
+//           16 keys x 16 head columns (the group's r heads, the rest zero) per
+//           block, 4 blocks per wave;
+//   softmax per-head max and sum over the chunk (thread t = key t);
+//   P V     thread = (4 head dims, 32 keys) for all r heads, then a sum over
+//           the 8 key slices through LDS.
+// Writes unnormalised partial outputs and the chunk's (max, sum) per head.
 __global__ void __launch_bounds__(256)
     attn_decode_partial(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
                         const uint16_t* __restrict__ Vc, const uint8_t* __restrict__ mask, int B,
                         int n_kv, int r, int kv_len, int kv_cap, int nch, float scale_log2,
                         float* __restrict__ Opart, float* __restrict__ Mpart,
                         float* __restrict__ Lpart) {
-  __shared__ float sQ[8][kHdD];
-  __shared__ float sP[8][kKeyChunk];
+  // V rows (row-major, 256 B each); reused for the key-slice partial sums
+  __shared__ __attribute__((aligned(16))) uint16_t sV[kKeyChunk * kHdD];
+  __shared__ __attribute__((aligned(16))) float sP[8][kKeyChunk];
   __shared__ float sRed[8][4];
   const int c = blockIdx.x % nch, rest = blockIdx.x / nch;
   const int g = rest % n_kv, b = rest / n_kv;
@@ -240,41 +345,53 @@ __global__ void __launch_bounds__(256)
   const int nkeys = min(kKeyChunk, kv_len + 1 - k0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nq = n_kv * r;
-  for (int i = tid; i < r * kHdD; i += 256)
-    sQ[i / kHdD][i % kHdD] = bf2f(Q[((size_t)b * nq + g * r) * kHdD + i]);
-  __syncthreads();
+  const size_t kvbase = ((size_t)b * n_kv + g) * kv_cap + k0;  // first key row of the chunk
+  const uint32_t cache_bytes = (uint32_t)((size_t)B * n_kv * kv_cap * kHdD * 2);
+  const int m16 = lane & 15, q4 = lane >> 4;
 
-  const size_t kvbase = ((size_t)b * n_kv + g) * kv_cap;
-  // scores: each wave takes 4 keys per pass (16 lanes per key)
-  const int sub = lane >> 4, part = lane & 15;
-  for (int base = wave * 4; base < kKeyChunk; base += 16) {
-    const int kk = base + sub;
-    float s[8];
-    bool ok = kk < nkeys;
-    u32x4 kv = {0, 0, 0, 0};
-    if (ok) kv = *reinterpret_cast<const u32x4*>(Kc + (kvbase + k0 + kk) * kHdD + part * 8);
-    float kf[8];
+  // K operand: block i of wave w = keys 16 (4 w + i) + m16, dims 32 ks + 8 q4 .. +7
+  const rsrc_t kr = make_rsrc(Kc, cache_bytes);
+  bf16x8 kf[kKeyBlocks][4];
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      kf[2 * e] = __uint_as_float(kv[e] << 16);
-      kf[2 * e + 1] = __uint_as_float(kv[e] & 0xffff0000u);
+  for (int i = 0; i < kKeyBlocks; ++i) {
+    const int key = 16 * (kKeyBlocks * wave + i) + m16;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+      kf[i][ks] =
+          xload(kr, key < nkeys ? (uint32_t)(((kvbase + key) * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
+  }
+  // V: instruction q of wave w fills rows 16 q + 4 w .. +3 (1 KB); rows past the
+  // chunk's keys read as zeros
+  {
+    const i32x4 vsrd = make_srd(Vc, cache_bytes);
+    const uint32_t vlds = lds_addr(sV);
+#pragma unroll
+    for (int q = 0; q < kKeyChunk / 16; ++q) {
+      const int row = 16 * q + 4 * wave + q4;
+      const uint32_t off =
+          row < nkeys ? (uint32_t)(((kvbase + row) * kHdD + m16 * 8) * 2) : kSkip;
+      lds_dma16(vsrd, vlds + (16 * q + 4 * wave) * kHdD * 2, off);
     }
+  }
+  // Q operand: column m16 = head of the group (zero past r)
+  bf16x8 qf[4];
+  {
+    const rsrc_t qr = make_rsrc(Q + ((size_t)b * nq + g * r) * kHdD, (uint32_t)(r * kHdD * 2));
 #pragma unroll
-    for (int h = 0; h < 8; ++h) {
-      float a = 0.f;
-      if (h < r)
+    for (int ks = 0; ks < 4; ++ks)
+      qf[ks] = xload(qr, m16 < r ? (uint32_t)((m16 * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
+  }
 #pragma unroll
-        for (int e = 0; e < 8; ++e) a += kf[e] * sQ[h][part * 8 + e];
-      a += __shfl_xor(a, 8);
-      a += __shfl_xor(a, 4);
-      a += __shfl_xor(a, 2);
-      a += __shfl_xor(a, 1);
-      s[h] = a;
-    }
-    if (part == 0) {
+  for (int i = 0; i < kKeyBlocks; ++i) {
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int h = 0; h < 8; ++h)
-        if (h < r) sP[h][kk] = ok ? s[h] * scale_log2 : -INFINITY;
+    for (int ks = 0; ks < 4; ++ks) acc = mfma16(kf[i][ks], qf[ks], acc);
+    if (m16 < r) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int key = 16 * (kKeyBlocks * wave + i) + acc16_row(lane, e);
+        sP[m16][key] = key < nkeys ? acc[e] * scale_log2 : -INFINITY;
+      }
     }
   }
   __syncthreads();
@@ -283,8 +400,7 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     if (h >= r) break;
-    float v = sP[h][tid];
-    float m = v;
+    float m = sP[h][tid];
     for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
     if (lane == 0) sRed[h][wave] = m;
   }
@@ -304,27 +420,60 @@ __global__ void __launch_bounds__(256)
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) sRed[h][wave] = l;
   }
+  // the V rows of every wave have landed in LDS before anyone reads them
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     if (h >= r) break;
     lh[h] = sRed[h][0] + sRed[h][1] + sRed[h][2] + sRed[h][3];
   }
-  // P V: thread -> (head, pair of dims); V rows read 256 bytes per 64 threads
-  const size_t obase = ((size_t)b * nq + g * r) * nch;
-  for (int o = tid; o < r * 64; o += 256) {
-    const int h = o >> 6, jp = (o & 63) * 2;
-    float a0 = 0.f, a1 = 0.f;
-    const uint16_t* vp = Vc + (kvbase + k0) * kHdD + jp;
-    for (int kk = 0; kk < nkeys; ++kk) {
-      const uint32_t v2 = *reinterpret_cast<const uint32_t*>(vp + (size_t)kk * kHdD);
-      const float p = sP[h][kk];
-      a0 += p * __uint_as_float(v2 << 16);
-      a1 += p * __uint_as_float(v2 & 0xffff0000u);
+  // P V: thread = (dims 4 j4 .. +3, keys 32 ks .. +31); P is zero and V rows are
+  // zero past nkeys
+  const int j4 = tid & 31, kslice = tid >> 5;
+  float o[8][4];
+#pragma unroll
+  for (int h = 0; h < 8; ++h)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
+#pragma unroll 2
+  for (int kq = 0; kq < 32; kq += 4) {
+    const int kk = 32 * kslice + kq;
+    float vf[4][4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const u32x2 v2 = *reinterpret_cast<const u32x2*>(sV + (kk + e) * kHdD + 4 * j4);
+      vf[e][0] = __uint_as_float(v2[0] << 16);
+      vf[e][1] = __uint_as_float(v2[0] & 0xffff0000u);
+      vf[e][2] = __uint_as_float(v2[1] << 16);
+      vf[e][3] = __uint_as_float(v2[1] & 0xffff0000u);
     }
-    float* op = Opart + ((obase + (size_t)h * nch + c) * kHdD) + jp;
-    op[0] = a0;
-    op[1] = a1;
+#pragma unroll
+    for (int h = 0; h < 8; ++h) {
+      if (h >= r) break;
+      const f32x4 p = *reinterpret_cast<const f32x4*>(&sP[h][kk]);
+#pragma unroll
+      for (int e = 0; e < 4; ++e)
+#pragma unroll
+        for (int x = 0; x < 4; ++x) o[h][x] += p[e] * vf[e][x];
+    }
+  }
+  __syncthreads();  // every thread is done with sV
+  float* sO = reinterpret_cast<float*>(sV);  // [8 slices][r][128]
+#pragma unroll
+  for (int h = 0; h < 8; ++h) {
+    if (h >= r) break;
+    *reinterpret_cast<f32x4*>(sO + (kslice * r + h) * kHdD + 4 * j4) =
+        f32x4{o[h][0], o[h][1], o[h][2], o[h][3]};
+  }
+  __syncthreads();
+  const size_t obase = ((size_t)b * nq + g * r) * nch;
+  for (int x = tid; x < r * kHdD; x += 256) {
+    const int h = x / kHdD, j = x % kHdD;
+    float a = 0.f;
+#pragma unroll
+    for (int sl = 0; sl < 8; ++sl) a += sO[(sl * r + h) * kHdD + j];
+    Opart[(obase + (size_t)h * nch + c) * kHdD + j] = a;
   }
   if (tid < r) {
     Mpart[obase + (size_t)tid * nch + c] = mh[tid];
@@ -332,53 +481,82 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// (token b, query head h): O[b, h] = sum_c 2^(M_c - M) Opart_c / sum_c 2^(M_c - M) L_c.
+// (token b, query head h): O[b, h] = sum_c 2^(M_c - M) Opart_c / sum_c 2^(M_c - M) L_c,
+// M = max_c M_c.  Chunk weights are computed 128 at a time into LDS; the Opart
+// loads of a block of chunks are independent, so they overlap.
 __global__ void __launch_bounds__(128)
     attn_decode_combine(const float* __restrict__ Opart, const float* __restrict__ Mpart,
                         const float* __restrict__ Lpart, const uint8_t* __restrict__ mask,
                         int n_kv, int r, int nch, uint16_t* __restrict__ O) {
+  __shared__ float sW[128];
+  __shared__ float sM[2];
   const int nq = n_kv * r;
   const int b = blockIdx.x / nq, h = blockIdx.x % nq, g = h / r;
   if (!mask[(size_t)b * n_kv + g]) return;  // never read: the O projection skips it
   const size_t base = (size_t)b * nq * nch + (size_t)h * nch;
+  const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
   float m = -INFINITY;
-  for (int c = 0; c < nch; ++c) m = fmaxf(m, Mpart[base + c]);
+  for (int c = j; c < nch; c += 128) m = fmaxf(m, Mpart[base + c]);
+  for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if (lane == 0) sM[wave] = m;
+  __syncthreads();
+  m = fmaxf(sM[0], sM[1]);
   float l = 0.f, acc = 0.f;
-  const int j = threadIdx.x;
-  for (int c = 0; c < nch; ++c) {
-    const float w = exp2f(Mpart[base + c] - m);
-    l += w * Lpart[base + c];
-    acc += w * Opart[(base + c) * kHdD + j];
+  for (int c0 = 0; c0 < nch; c0 += 128) {
+    const int cn = min(128, nch - c0);
+    __syncthreads();
+    float lw = 0.f;
+    if (j < cn) {
+      const float w = exp2f(Mpart[base + c0 + j] - m);
+      sW[j] = w;
+      lw = w * Lpart[base + c0 + j];
+    }
+    for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+    __syncthreads();
+    if (lane == 0) sM[wave] = lw;
+    __syncthreads();
+    l += sM[0] + sM[1];
+#pragma unroll 8
+    for (int c = 0; c < cn; ++c) acc += sW[c] * Opart[(base + c0 + c) * kHdD + j];
   }
   O[((size_t)b * nq + h) * kHdD + j] = f2bf(acc / l);
 }
 
 // ------------------------------------------------------------------ launchers
 
-void launch_ffn_decode(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
-                       const uint16_t* Wdp, const ReorderView& rv, int B, int d, int F, int n,
+void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
+                       const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
                        const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s) {
-  const int G = F / n, chunks = G / 16;
+  const int G = F / n, chunks = G / 8;
   {
     WIDE_TRACE("ffn_up_decode", s);
-    nmask_decode<kNmFfn><<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, rv.count, rv.perm, B, d, G,
-                                                    chunks, 0, 0, 0, 0.f, H, nullptr, nullptr, n);
+    const int nrb = (B + 15) / 16;
+    auto k = nrb == 1   ? nmask_decode<kNmFfn, 1>
+             : nrb == 2 ? nmask_decode<kNmFfn, 2>
+             : nrb == 3 ? nmask_decode<kNmFfn, 3>
+                        : nmask_decode<kNmFfn, 4>;
+    k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
+                                 nullptr, nullptr, n);
   }
-  launch_kmask_decode("ffn_down_decode", H, Wdp, rv, B, d, F, n, residual, Y, s);
+  launch_kmask_decode("ffn_down_decode", H, Wdp, mask, B, d, F, n, residual, Y, s);
 }
 
 void launch_kmask_decode(const char* tname, const uint16_t* A, const uint16_t* Wp,
-                         const ReorderView& rv, int B, int d, int F, int n,
+                         const uint8_t* mask, int B, int d, int F, int n,
                          const uint16_t* residual, uint16_t* Y, hipStream_t s) {
   WIDE_TRACE(tname, s);
-  kmask_decode<<<d / 16, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, B, d, F,
-                                      F / n, (n + 63) / 64, residual, Y);
+  const int nrb = (B + 15) / 16;
+  auto k = nrb == 1   ? kmask_decode<1>
+           : nrb == 2 ? kmask_decode<2>
+           : nrb == 3 ? kmask_decode<3>
+                      : kmask_decode<4>;
+  k<<<d / 16, 64 * kKmWaves, 0, s>>>(A, Wp, mask, B, d, F, F / n, n, residual, Y);
 }
 
 int attn_decode_chunks(int kv_len) { return (kv_len + 1 + kKeyChunk - 1) / kKeyChunk; }
 
 void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
-                        const uint16_t* Wk, const uint16_t* Wv, const ReorderView& rv, int B, int d,
+                        const uint16_t* Wk, const uint16_t* Wv, int B, int d,
                         int n_kv, int r, float rope_theta, uint16_t* Kc, uint16_t* Vc, int kv_len,
                         int kv_cap, uint16_t* Qd, float* Opart, float* Mpart, float* Lpart,
                         uint16_t* O, hipStream_t s) {
@@ -386,9 +564,13 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
   const float log2_theta = rope_theta > 0.f ? log2f(rope_theta) : 0.f;
   {
     WIDE_TRACE("attn_qkv_decode", s);
-    nmask_decode<kNmQkv><<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, B, d, kHdD,
-                                                       chunks, r, kv_len, kv_cap, log2_theta, Qd,
-                                                       Kc, Vc, n_kv);
+    const int nrb = (B + 15) / 16;
+    auto k = nrb == 1   ? nmask_decode<kNmQkv, 1>
+             : nrb == 2 ? nmask_decode<kNmQkv, 2>
+             : nrb == 3 ? nmask_decode<kNmQkv, 3>
+                        : nmask_decode<kNmQkv, 4>;
+    k<<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, kv_len, kv_cap,
+                                    log2_theta, Qd, Kc, Vc, n_kv);
   }
   const int nch = attn_decode_chunks(kv_len);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHdD);

@@ -36,6 +36,10 @@ WIDE_DEV rsrc_t make_rsrc(const void* base, uint32_t bytes) {
 WIDE_DEV u32x4 ldbuf16(rsrc_t r, uint32_t byte_off) {
   return __builtin_amdgcn_raw_buffer_load_b128(r, (int)byte_off, 0, 0);
 }
+// One byte; an offset past num_records reads 0.
+WIDE_DEV uint32_t ldbuf1(rsrc_t r, uint32_t byte_off) {
+  return __builtin_amdgcn_raw_buffer_load_b8(r, (int)byte_off, 0, 0);
+}
 typedef int32_t i32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) uint16_t lds_u16;
 

@@ -54,15 +54,16 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
                          hipStream_t s);
 
 constexpr int kMaxDecodeBatch = 64;
-void launch_ffn_decode(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
-                       const uint16_t* Wdp, const ReorderView& rv, int B, int d, int F, int n,
+// Decode launchers read the [B, n] mask directly (no reorder launch).
+void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
+                       const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
                        const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
 void launch_kmask_decode(const char* tname, const uint16_t* A, const uint16_t* Wp,
-                         const ReorderView& rv, int B, int d, int F, int n,
+                         const uint8_t* mask, int B, int d, int F, int n,
                          const uint16_t* residual, uint16_t* Y, hipStream_t s);
 int attn_decode_chunks(int kv_len);
 void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
-                        const uint16_t* Wk, const uint16_t* Wv, const ReorderView& rv, int B, int d,
+                        const uint16_t* Wk, const uint16_t* Wv, int B, int d,
                         int n_kv, int r, float rope_theta, uint16_t* Kc, uint16_t* Vc, int kv_len,
                         int kv_cap, uint16_t* Qd, float* Opart, float* Mpart, float* Lpart,
                         uint16_t* O, hipStream_t s);
