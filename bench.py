@@ -451,8 +451,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="layer_prefill_8b", choices=sorted(WORKLOADS))
     ap.add_argument("--oracle-tokens", type=int, default=None,
-                    help="tokens of the CPU oracle sample (default: a quarter of T)")
+                    help="tokens of the CPU oracle sample (default: all T tokens)")
     ap.add_argument("--no-oracle", action="store_true")
+    ap.add_argument("--skip-ones", action="store_true",
+                    help="skip the all-ones comparison (profiler runs: only masked launches)")
+    ap.add_argument("--copy-bytes", type=int, default=0,
+                    help="instead of a workload, run 3 plain device copies of this many bytes "
+                         "(calibrates the HBM traffic counters) and exit")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -468,6 +473,17 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     wide.lib()
+
+    if args.copy_bytes:
+        n = args.copy_bytes // 4
+        src = torch.empty(n, dtype=torch.float32, device="cuda").uniform_()
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"copied {n * 4} bytes 3 times")
+        return
 
     log(f"generating {args.workload} inputs")
     W = WORKLOADS[args.workload]()
@@ -488,10 +504,12 @@ def main():
     log(f"masked: {ms:.3f} ms/step")
 
     # the same kernels, grid policy and inputs with all-ones masks
-    for _ in range(2):
-        W.step(ones=True)
-    ms_ones = timed(torch, lambda: W.step(ones=True), max(3, args.steps // 2), stream)
-    log(f"all-ones: {ms_ones:.3f} ms/step")
+    ms_ones = None
+    if not args.skip_ones:
+        for _ in range(2):
+            W.step(ones=True)
+        ms_ones = timed(torch, lambda: W.step(ones=True), max(3, args.steps // 2), stream)
+        log(f"all-ones: {ms_ones:.3f} ms/step")
 
     work = W.work()
     hbm = getattr(W, "bound", "mfma") == "hbm"
@@ -537,8 +555,8 @@ def main():
         "step_roofline": {"unit": unit, "achieved": round(step_rate, 1),
                           "frac": round(step_rate / peak, 4),
                           "work": "touched bytes" if hbm else "active FLOPs"},
-        "all_ones_ms_per_step": round(ms_ones, 4),
-        "speedup_vs_all_ones": round(ms_ones / ms, 3),
+        "all_ones_ms_per_step": round(ms_ones, 4) if ms_ones else None,
+        "speedup_vs_all_ones": round(ms_ones / ms, 3) if ms_ones else None,
         "kernels": per_kernel,
     }
 

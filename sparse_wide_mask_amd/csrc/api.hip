@@ -165,12 +165,12 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
                        kv_cap, w.Qc, w.Opart, w.Mpart, w.Lpart, w.O, s);
-    launch_kmask_decode("attn_o_decode", w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, Y, s);
+    launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, Y, s);
     return;
   }
   run_reorder(mask, T, nkv, w.rv, s);
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
-  launch_kmask_gemm("attn_o", w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
+  launch_kmask_gemm(kUseAttnO, w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
 }
 
 // -------------------------------------------------------------------- layer

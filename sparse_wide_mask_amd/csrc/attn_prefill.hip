@@ -12,9 +12,11 @@
 //                   one 128-wide head, so the RoPE pair (j, j+64) sits in the same
 //                   lane; rotation uses the token's original position.  Writes
 //                   Qc [n_kv][r][T][hd], Kc [n_kv][T][hd] and V transposed,
-//                   Vt [n_kv][hd][T] (row i = i-th kept token of the group).
-// attn_core_prefill one work-group = (group, 64 compacted queries), one wave per
-//                   query head.  S^T = K Q^T puts a query in each lane's column,
+//                   Vt [n_kv][hd][vtp] (column i = i-th kept token of the group,
+//                   permuted inside 16-key groups; zero up to a whole group).
+// attn_core_prefill one work-group = (group, a heavy and a light tile of 64
+//                   compacted queries), one wave per query head; K and V^T blocks
+//                   arrive by buffer->LDS loads one key step ahead.  S^T = K Q^T puts a query in each lane's column,
 //                   so the online softmax is per lane (+ one cross-half swap) and
 //                   P stays in registers as the B operand of O^T = V^T P^T; V is
 //                   read in the key order the S^T accumulator layout gives.
@@ -137,24 +139,24 @@ __global__ void __launch_bounds__(256, 1)
   for (int i = 0; i < C::RB; ++i) {
     if (!((rb_live >> i) & 1u)) continue;
     if (is_v) {
-      // V^T: lane holds hd column cb*32 + c0 and rows 4 (l/32) + 8 q + {0..3}
+      // V^T: lane holds hd column cb*32 + c0 and rows 4 (l/32) + 8 q + {0..3}.
+      // Keys are stored permuted inside 16-key groups (4-key quarter q -> slot
+      // [0, 2, 1, 3][q]) so that the attention core reads a lane's 8 keys as one
+      // 16-byte chunk.  Rows past the count hold zeros (their A rows were not
+      // loaded), and are written up to a whole 16-key group.
+      const int rows16 = (rows + 15) & ~15;
 #pragma unroll
       for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
         for (int q4 = 0; q4 < 4; ++q4) {
           const int rr = wm * C::WM + i * 32 + 8 * q4 + 4 * (lane >> 5);
+          if (rr >= rows16) continue;
           const f32x16& a = acc.acc[i][cb];
           const uint32_t lo = pack_bf2(a[4 * q4], a[4 * q4 + 1]);
           const uint32_t hi = pack_bf2(a[4 * q4 + 2], a[4 * q4 + 3]);
-          uint16_t* p = vdst + (size_t)(cb * 32 + c0) * vtp + row0 + rr;
-          if (rr + 3 < rows) {
-            *reinterpret_cast<u32x2*>(p) = u32x2{lo, hi};
-          } else {
-            const uint16_t v4[4] = {(uint16_t)lo, (uint16_t)(lo >> 16), (uint16_t)hi,
-                                    (uint16_t)(hi >> 16)};
-            for (int k = 0; k < 4; ++k)
-              if (rr + k < rows) p[k] = v4[k];
-          }
+          const int key = row0 + rr, qtr = (key >> 2) & 3;
+          const int slot = (key & ~15) | ((((qtr & 1) << 1) | (qtr >> 1)) << 2);
+          *reinterpret_cast<u32x2*>(vdst + (size_t)(cb * 32 + c0) * vtp + slot) = u32x2{lo, hi};
         }
       continue;
     }
@@ -184,189 +186,240 @@ __global__ void __launch_bounds__(256, 1)
 
 // ---------------------------------------------------------- attention core
 
-constexpr int kBQ = 64;     // queries per work-group (per wave: one head, 64 queries)
-constexpr int kBKey = 64;   // keys per step
-constexpr int kKPitch = kHd + 8;    // LDS pitch of K rows   (bf16)
-constexpr int kVPitch = kBKey + 8;  // LDS pitch of V^T rows (bf16)
-
-WIDE_DEV bf16x8 lds8(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
-WIDE_DEV bf16x4 lds4(const uint16_t* p) { return *reinterpret_cast<const bf16x4*>(p); }
+constexpr int kBQ = 64;    // queries per tile (per wave: one head, 64 queries)
+constexpr int kBKey = 64;  // keys per step
+// One LDS stage: K block [64 keys][128 hd] (16-byte chunk c of key row k at slot
+// c ^ (k & 15)) and V^T block [128 hd][64 keys] (chunk c of row j at slot
+// c ^ ((j >> 1) & 7)); both 16 KB, filled by buffer->LDS loads.
+constexpr int kStageK = kBKey * kHd;  // elements
+constexpr int kStageV = kHd * kBKey;
 
 __global__ void __launch_bounds__(256, 1)
     attn_core_prefill(const uint16_t* __restrict__ Qc, const uint16_t* __restrict__ Kc,
                       const uint16_t* __restrict__ Vt, const int32_t* __restrict__ gcount,
-                      const int32_t* __restrict__ gperm, int T, int n_kv, int r, int qtiles,
+                      const int32_t* __restrict__ gperm, int T, int n_kv, int r, int npairs,
                       int vtp, float scale_log2, uint16_t* __restrict__ O) {
-  __shared__ __attribute__((aligned(16))) uint16_t sK[kBKey * kKPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kHd * kVPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kStageK];
+  __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kStageV];
 
-  // work-group -> (group, query tile, chunk of 4 query heads); late (heavy) query
-  // tiles first
+  // work-group -> (group, pair of query tiles, chunk of 4 query heads).  A pair
+  // is the p-th heaviest and p-th lightest causal tile of the group, so every
+  // work-group of a group does about the same number of key steps.
   const int g = blockIdx.x % n_kv;
   const int rest = blockIdx.x / n_kv;
-  const int qt = qtiles - 1 - rest % qtiles;
-  const int hc = rest / qtiles;
+  const int p = rest % npairs;
+  const int hc = rest / npairs;
   const int cnt = gcount[g];
-  const int q0 = qt * kBQ;
-  if (q0 >= cnt) return;  // l=0
+  const int qtiles = (cnt + kBQ - 1) / kBQ;
+  if (2 * p >= qtiles) return;  // l=0: past the group's kept tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const bool head_ok = hc * 4 + wave < r;  // waves past the group's heads only help load
   const int h = g * r + min(hc * 4 + wave, r - 1);
   const int c0 = lane & 31, half = lane >> 5;
 
-  // Q^T fragments as B operands: lane holds query q0 + qb*32 + c0, hd 16 ks + 8 half.
-  bf16x8 qf[2][8];
-  const uint16_t* qbase = Qc + (size_t)h * T * kHd;
-#pragma unroll
-  for (int qb = 0; qb < 2; ++qb) {
-    const int q = q0 + qb * 32 + c0;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      if (q < cnt)
-        qf[qb][ks] = *reinterpret_cast<const bf16x8*>(qbase + (size_t)q * kHd + ks * 16 + half * 8);
-      else
-        qf[qb][ks] = bf16x8{};
-    }
-  }
-  f32x16 o[4][2];  // O^T: 4 hd blocks x 2 query blocks
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) o[a][b][e] = 0.f;
-  float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
-
-  const uint16_t* kbase = Kc + (size_t)g * T * kHd;
-  const uint16_t* vbase = Vt + (size_t)g * kHd * vtp;
-  const int q_last = min(cnt, q0 + kBQ) - 1;
-  const int nkb = q_last / kBKey + 1;
-  for (int kb = 0; kb < nkb; ++kb) {
+  const i32x4 kSrd = make_srd(Kc + (size_t)g * T * kHd, (uint32_t)((size_t)T * kHd * 2));
+  const i32x4 vSrd = make_srd(Vt + (size_t)g * kHd * vtp, (uint32_t)((size_t)kHd * vtp * 2));
+  const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
+  // buffer->LDS loads of key block kb into stage st: instruction i of wave w fills
+  // K rows 4 (4 i + w) .. +3 and V^T rows 8 (4 i + w) .. +7 (1 KB each)
+  auto issue = [&](int kb, int st) {
     const int k0 = kb * kBKey;
-    __syncthreads();
-    // K block [64 keys][128]: 1024 16-byte chunks, 4 per thread
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 4, col = (ch & 15) * 8;
-      u32x4 v = {0, 0, 0, 0};
-      if (k0 + row < cnt) v = *reinterpret_cast<const u32x4*>(kbase + (size_t)(k0 + row) * kHd + col);
-      *reinterpret_cast<u32x4*>(sK + row * kKPitch + col) = v;
+      const int n = 4 * i + wave;
+      const int krow = 4 * n + (lane >> 4), kslot = lane & 15;
+      const int kchunk = kslot ^ (krow & 15);
+      const uint32_t koff =
+          k0 + krow < cnt ? (uint32_t)(((k0 + krow) * kHd + kchunk * 8) * 2) : kSkip;
+      lds_dma16(kSrd, ldsK + (st * kStageK + n * 512) * 2, koff);
+      const int vrow = 8 * n + (lane >> 3), vslot = lane & 7;
+      const int vchunk = vslot ^ ((vrow >> 1) & 7);
+      // chunk c holds half of the 16-key group c / 2 (zero-padded past the count)
+      const int kg = k0 + 16 * (vchunk >> 1);
+      const uint32_t voff =
+          kg < cnt ? (uint32_t)((vrow * vtp + k0 + vchunk * 8) * 2) : kSkip;
+      lds_dma16(vSrd, ldsV + (st * kStageV + n * 512) * 2, voff);
     }
-    // V^T block [128 hd][64 keys]: 1024 chunks of 8 keys, keys >= cnt zeroed
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, col = (ch & 7) * 8;
-      u32x4 v = {0, 0, 0, 0};
-      const int key = k0 + col;
-      if (key < cnt) {
-        v = *reinterpret_cast<const u32x4*>(vbase + (size_t)row * vtp + key);
-        if (key + 8 > cnt) {
-          uint16_t* e = reinterpret_cast<uint16_t*>(&v);
-          for (int k = cnt - key; k < 8; ++k) e[k] = 0;
-        }
-      }
-      *reinterpret_cast<u32x4*>(sV + row * kVPitch + col) = v;
-    }
-    __syncthreads();
+  };
 
-    // S^T [64 keys x 64 queries] = K Q^T
-    f32x16 s[2][2];
+  for (int pass = 0; pass < 2; ++pass) {
+    const int qt = pass == 0 ? qtiles - 1 - p : p;
+    if (pass == 1 && qt == qtiles - 1 - p) break;  // the middle tile has no partner
+    const int q0 = qt * kBQ;
+    const int q_last = min(cnt, q0 + kBQ) - 1;
+    const int nkb = q_last / kBKey + 1;
+    lds_barrier();  // the previous tile's last stage reads are done
+    issue(0, 0);
+
+    // Q^T fragments as B operands: lane holds query q0 + qb*32 + c0, hd 16 ks + 8 half.
+    bf16x8 qf[2][8];
+    const uint16_t* qbase = Qc + (size_t)h * T * kHd;
 #pragma unroll
-    for (int a = 0; a < 2; ++a)
+    for (int qb = 0; qb < 2; ++qb) {
+      const int q = q0 + qb * 32 + c0;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+        if (q < cnt)
+          qf[qb][ks] =
+              *reinterpret_cast<const bf16x8*>(qbase + (size_t)q * kHd + ks * 16 + half * 8);
+        else
+          qf[qb][ks] = bf16x8{};
+      }
+    }
+    f32x16 o[4][2];  // O^T: 4 hd blocks x 2 query blocks
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
 #pragma unroll
       for (int b = 0; b < 2; ++b)
 #pragma unroll
-        for (int e = 0; e < 16; ++e) s[a][b][e] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+        for (int e = 0; e < 16; ++e) o[a][b][e] = 0.f;
+    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+
+    for (int kb = 0; kb < nkb; ++kb) {
+      const int k0 = kb * kBKey, st = kb & 1;
+      // every wave's loads of block kb have landed (this wave's 8 loads of block
+      // kb + 1 may stay in flight)
+      if (kb + 1 < nkb) {
+        issue(kb + 1, st ^ 1);
+        stage_barrier<8>();
+      } else {
+        stage_barrier<0>();
+      }
+      const uint16_t* cK = sK + st * kStageK;
+      const uint16_t* cV = sV + st * kStageV;
+
+      auto kfrag = [&](int ks, int a) {
+        const int row = a * 32 + c0;
+        return *reinterpret_cast<const bf16x8*>(cK + row * kHd +
+                                                (((2 * ks + half) ^ (row & 15)) * 8));
+      };
+      auto vfrag = [&](int a, int sp, int hb) {
+        const int row = hb * 32 + c0, chunk = 2 * (2 * a + sp) + half;
+        return *reinterpret_cast<const bf16x8*>(cV + row * kBKey +
+                                                ((chunk ^ ((row >> 1) & 7)) * 8));
+      };
+      // the stage's two 32-key halves in turn
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
-        const bf16x8 kf = lds8(sK + (a * 32 + c0) * kKPitch + ks * 16 + half * 8);
-#pragma unroll
-        for (int b = 0; b < 2; ++b) s[a][b] = mfma32(kf, qf[b][ks], s[a][b]);
-      }
-    }
-    // mask (causal in compacted order, keys past the count) and online softmax
-    const bool diag = k0 + kBKey > q0;
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int q = q0 + b * 32 + c0;
-      float mx = -INFINITY;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int key = k0 + a * 32 + acc32_row(lane, e);
-          float v = s[a][b][e] * scale_log2;
-          if (diag && key > q) v = -INFINITY;
-          if (key >= cnt) v = -INFINITY;
-          s[a][b][e] = v;
-          mx = fmaxf(mx, v);
-        }
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run[b], mx);
-      // a query past the count has no finite score; keep its state finite
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float corr = exp2f(m_run[b] - m_use);
-      float sum = 0.f;
-#pragma unroll
-      for (int a = 0; a < 2; ++a)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float p = exp2f(s[a][b][e] - m_use);
-          s[a][b][e] = p;
-          sum += p;
-        }
-      sum += __shfl_xor(sum, 32);
-      l_run[b] = l_run[b] * corr + sum;
-      m_run[b] = m_new;
-#pragma unroll
-      for (int a = 0; a < 4; ++a)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[a][b][e] *= corr;
-    }
-    // O^T [128 x 64] += V^T [128 x 64 keys] P^T [64 keys x 64 q]; the k-slots of a
-    // lane are the keys its S^T registers hold: 16 s' + 4 half + {0..3, 8..11}.
-#pragma unroll
-    for (int a = 0; a < 2; ++a)
-#pragma unroll
-      for (int sp = 0; sp < 2; ++sp) {
-        bf16x8 pf[2];
+        const int kk0 = k0 + a * 32;
+        // S^T [32 keys x 64 queries] = K Q^T; the K fragment of step ks + 1 is read
+        // from LDS before the MFMAs of step ks
+        f32x16 s[2];
 #pragma unroll
         for (int b = 0; b < 2; ++b)
 #pragma unroll
-          for (int k = 0; k < 8; ++k) pf[b][k] = (__bf16)s[a][b][8 * sp + k];
-        const int key0 = a * 32 + 16 * sp + 4 * half;
+          for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
+        bf16x8 kc = kfrag(0, a);
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) {
-          const uint16_t* vp = sV + (hb * 32 + c0) * kVPitch + key0;
-          const bf16x4 lo = lds4(vp), hi = lds4(vp + 8);
-          const bf16x8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        for (int ks = 0; ks < 8; ++ks) {
+          bf16x8 kn;
+          if (ks < 7) kn = kfrag(ks + 1, a);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-          for (int b = 0; b < 2; ++b) o[hb][b] = mfma32(vf, pf[b], o[hb][b]);
+          for (int b = 0; b < 2; ++b) s[b] = mfma32(kc, qf[b][ks], s[b]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (ks < 7) kc = kn;
+        }
+        // the V^T fragments of the first P V step, read while the softmax runs
+        bf16x8 vc[4];
+#pragma unroll
+        for (int hb = 0; hb < 4; ++hb) vc[hb] = vfrag(a, 0, hb);
+
+        // online softmax in the log2 domain.  Masks (causal in compacted order,
+        // keys past the count) only on the blocks that need them.  The running
+        // max is raised only when a score exceeds it by more than 8 (2^8 headroom
+        // for P in bf16 and the fp32 sums), so O and l are rescaled rarely; O / l
+        // is the same for any common offset.
+        const bool masked = kk0 + 32 > q0 || kk0 + 32 > cnt;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const int q = q0 + b * 32 + c0;
+          if (masked) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = kk0 + acc32_row(lane, e);
+              if (key > q || key >= cnt) s[b][e] = -INFINITY;
+            }
+          }
+          float mx = -INFINITY;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
+          mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+          const bool grow = mx > m_run[b] + 8.f;
+          if (ballot(grow)) {
+            const float m_set = grow ? mx : m_run[b];
+            const float corr =
+                m_set == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[b] - m_set);
+            l_run[b] *= corr;
+            m_run[b] = m_set;
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+              for (int e = 0; e < 16; ++e) o[hb][b][e] *= corr;
+          }
+          // a query past the count has no finite score; keep its state finite
+          const float m_use = m_run[b] == -INFINITY ? 0.f : m_run[b];
+          float sum = 0.f;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) {
+            const float pe = __builtin_amdgcn_exp2f(fmaf(s[b][e], scale_log2, -m_use));
+            s[b][e] = pe;
+            sum += pe;
+          }
+          l_run[b] += sum + __shfl_xor(sum, 32);
+        }
+        // O^T [128 x 64] += V^T [128 x 32 keys] P^T [32 keys x 64 q].  The k-slots
+        // of a lane are the keys its S^T registers hold, 16 s' + 4 half +
+        // {0..3, 8..11}; the permuted V^T layout stores exactly those 8 keys as
+        // chunk 2 (2 a + s') + half.
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+          bf16x8 vn[4];
+          if (sp == 0) {
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) vn[hb] = vfrag(a, 1, hb);
+          }
+          bf16x8 pf[2];
+#pragma unroll
+          for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int k = 0; k < 8; ++k) pf[b][k] = (__bf16)s[b][8 * sp + k];
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int b = 0; b < 2; ++b) o[hb][b] = mfma32(vc[hb], pf[b], o[hb][b]);
+          __builtin_amdgcn_sched_barrier(0);
+          if (sp == 0) {
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) vc[hb] = vn[hb];
+          }
         }
       }
-  }
+      lds_barrier();  // stage st is refilled by the next step's loads
+    }
 
-  // O[token, h*hd + j] = O^T[j][q] / l
-  if (!head_ok) return;
+    // O[token, h*hd + j] = O^T[j][q] / l
+    if (head_ok) {
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    const int q = q0 + b * 32 + c0;
-    if (q >= cnt) continue;
-    const int tok = gperm[(size_t)g * T + q];
-    const float inv = 1.f / l_run[b];
-    uint16_t* dst = O + (size_t)tok * (n_kv * r * kHd) + h * kHd;
+      for (int b = 0; b < 2; ++b) {
+        const int q = q0 + b * 32 + c0;
+        if (q >= cnt) continue;
+        const int tok = gperm[(size_t)g * T + q];
+        const float inv = 1.f / l_run[b];
+        uint16_t* dst = O + (size_t)tok * (n_kv * r * kHd) + h * kHd;
 #pragma unroll
-    for (int hb = 0; hb < 4; ++hb)
+        for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-      for (int q4 = 0; q4 < 4; ++q4) {
-        const int j = hb * 32 + 8 * q4 + 4 * half;
-        const f32x16& a = o[hb][b];
-        const uint32_t lo = pack_bf2(a[4 * q4] * inv, a[4 * q4 + 1] * inv);
-        const uint32_t hi = pack_bf2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
-        *reinterpret_cast<u32x2*>(dst + j) = u32x2{lo, hi};
+          for (int q4 = 0; q4 < 4; ++q4) {
+            const int j = hb * 32 + 8 * q4 + 4 * half;
+            const f32x16& a = o[hb][b];
+            const uint32_t lo = pack_bf2(a[4 * q4] * inv, a[4 * q4 + 1] * inv);
+            const uint32_t hi = pack_bf2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
+            *reinterpret_cast<u32x2*>(dst + j) = u32x2{lo, hi};
+          }
       }
+    }
   }
 }
 
@@ -383,12 +436,12 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
     attn_qkv_prefill<<<n_kv * mtiles * ntn, 256, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
                                                          r, mtiles, vtp, log2_theta, Qc, Kc, Vt);
   }
-  const int qtiles = (T + kBQ - 1) / kBQ;
+  const int npairs = ((T + kBQ - 1) / kBQ + 1) / 2;
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHd);
   {
     WIDE_TRACE("attn_core_prefill", s);
-    attn_core_prefill<<<qtiles * n_kv * ((r + 3) / 4), 256, 0, s>>>(
-        Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, qtiles, vtp, scale_log2, O);
+    attn_core_prefill<<<npairs * n_kv * ((r + 3) / 4), 256, 0, s>>>(
+        Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, npairs, vtp, scale_log2, O);
   }
 }
 

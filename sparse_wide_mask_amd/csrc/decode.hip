@@ -25,6 +25,8 @@
 //                split-KV attention of each kept (token, group) over cache slots
 //                0..kv_len (the new token included), 256 keys per work-group,
 //                then a log-sum-exp combine of the chunks.
+#include <type_traits>
+
 #include "common.h"
 #include "gemm_tile.h"
 #include "internal.h"
@@ -184,7 +186,7 @@ __global__ void __launch_bounds__(256)
 // sum_j A[b, gG + j] Wp[g, n, j] over the tokens b that keep g (+ residual).
 constexpr int kKmWaves = 8;
 
-template <int NRB>
+template <int NRB, int USE>
 __global__ void __launch_bounds__(64 * kKmWaves)
     kmask_decode(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
                  const uint8_t* __restrict__ mask, int B, int d, int F, int G, int n,
@@ -538,18 +540,23 @@ void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* W
     k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
                                  nullptr, nullptr, n);
   }
-  launch_kmask_decode("ffn_down_decode", H, Wdp, mask, B, d, F, n, residual, Y, s);
+  launch_kmask_decode(kUseFfnDown, H, Wdp, mask, B, d, F, n, residual, Y, s);
 }
 
-void launch_kmask_decode(const char* tname, const uint16_t* A, const uint16_t* Wp,
-                         const uint8_t* mask, int B, int d, int F, int n,
-                         const uint16_t* residual, uint16_t* Y, hipStream_t s) {
-  WIDE_TRACE(tname, s);
+void launch_kmask_decode(KmUse use, const uint16_t* A, const uint16_t* Wp, const uint8_t* mask,
+                         int B, int d, int F, int n, const uint16_t* residual, uint16_t* Y,
+                         hipStream_t s) {
+  WIDE_TRACE(use == kUseAttnO ? "attn_o_decode" : "ffn_down_decode", s);
   const int nrb = (B + 15) / 16;
-  auto k = nrb == 1   ? kmask_decode<1>
-           : nrb == 2 ? kmask_decode<2>
-           : nrb == 3 ? kmask_decode<3>
-                      : kmask_decode<4>;
+  auto pick = [&](auto tag) {
+    constexpr int U = decltype(tag)::value;
+    return nrb == 1   ? kmask_decode<1, U>
+           : nrb == 2 ? kmask_decode<2, U>
+           : nrb == 3 ? kmask_decode<3, U>
+                      : kmask_decode<4, U>;
+  };
+  auto k = use == kUseAttnO ? pick(std::integral_constant<int, kUseAttnO>{})
+                            : pick(std::integral_constant<int, kUseFfnDown>{});
   k<<<d / 16, 64 * kKmWaves, 0, s>>>(A, Wp, mask, B, d, F, F / n, n, residual, Y);
 }
 

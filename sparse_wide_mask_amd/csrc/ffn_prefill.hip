@@ -128,7 +128,7 @@ __global__ void __launch_bounds__(256, 1)
   }
 }
 
-template <int BM, int BN>
+template <int BM, int BN, int USE>
 __global__ void __launch_bounds__(256, 1)
     kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
                        const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
@@ -249,9 +249,10 @@ int ffn_down_tile_m() { return kDownBM; }
 // (+ residual), A token-major [T, F], Wp packed [n, d, G].  The column tile is
 // chosen to fill the 256 CUs best (rounds x tile width).  `tname` labels the
 // launch in the kernel trace (FFN down or attention output projection).
-void launch_kmask_gemm(const char* tname, const uint16_t* A, const uint16_t* Wp,
-                       const ReorderView& rv, int T, int d, int F, int n, const uint16_t* residual,
-                       uint16_t* Y, hipStream_t s) {
+template <int USE>
+void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderView& rv, int T,
+                          int d, int F, int n, const uint16_t* residual, uint16_t* Y,
+                          hipStream_t s) {
   const int G = F / n;
   const int nw = (n + 63) / 64;
   const int mtiles = (T + kDownBM - 1) / kDownBM;
@@ -264,19 +265,21 @@ void launch_kmask_gemm(const char* tname, const uint16_t* A, const uint16_t* Wp,
   }
   const int ntn = (d + best_bn - 1) / best_bn;
   const int grid = 8 * ((mtiles * ntn + 7) / 8);
-  WIDE_TRACE(tname, s);
-  if (best_bn == 256)
-    kmask_gemm_prefill<kDownBM, 256><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
-                                                          rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                          residual, Y);
-  else if (best_bn == 192)
-    kmask_gemm_prefill<kDownBM, 192><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
-                                                          rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                          residual, Y);
+  WIDE_TRACE(USE == kUseAttnO ? "attn_o" : "ffn_down", s);
+  auto k = best_bn == 256   ? kmask_gemm_prefill<kDownBM, 256, USE>
+           : best_bn == 192 ? kmask_gemm_prefill<kDownBM, 192, USE>
+                            : kmask_gemm_prefill<kDownBM, 128, USE>;
+  k<<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, T, d, F, n, G, nw, ntn,
+                         residual, Y);
+}
+
+void launch_kmask_gemm(KmUse use, const uint16_t* A, const uint16_t* Wp, const ReorderView& rv,
+                       int T, int d, int F, int n, const uint16_t* residual, uint16_t* Y,
+                       hipStream_t s) {
+  if (use == kUseAttnO)
+    launch_kmask_gemm_as<kUseAttnO>(A, Wp, rv, T, d, F, n, residual, Y, s);
   else
-    kmask_gemm_prefill<kDownBM, 128><<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count,
-                                                          rv.tile_groups, T, d, F, n, G, nw, ntn,
-                                                          residual, Y);
+    launch_kmask_gemm_as<kUseFfnDown>(A, Wp, rv, T, d, F, n, residual, Y, s);
 }
 
 void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* Wu,
@@ -301,7 +304,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
                                                                n, G, mtiles, ntn, H);
     }
   }
-  launch_kmask_gemm("ffn_down", H, Wdp, rv, T, d, F, n, residual, Y, s);
+  launch_kmask_gemm(kUseFfnDown, H, Wdp, rv, T, d, F, n, residual, Y, s);
 }
 
 }  // namespace wide

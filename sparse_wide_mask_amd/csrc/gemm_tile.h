@@ -72,6 +72,9 @@ WIDE_DEV void stage_barrier() {
   asm volatile("s_waitcnt vmcnt(%0) lgkmcnt(0)\n\ts_barrier" ::"n"(N) : "memory");
 }
 
+// Barrier once this wave's LDS reads are done (buffer loads may stay in flight).
+WIDE_DEV void lds_barrier() { asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory"); }
+
 // Block rasterisation of a rows x cols tile grid: stripes of MB tile rows; inside
 // a stripe, blocks of CBk tile columns with the row index fastest.  Consecutive
 // l form an MB x CBk block whose A rows and B columns are shared, so the ~32

@@ -41,12 +41,17 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
                         const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
                         const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
 
-void launch_kmask_gemm(const char* tname, const uint16_t* A, const uint16_t* Wp,
+// Which projection a K-masked kernel computes.  The kernels are the same; each
+// use gets its own instantiation so profilers report them apart.
+enum KmUse { kUseFfnDown = 0, kUseAttnO = 1 };
+
+void launch_kmask_gemm(KmUse use, const uint16_t* A, const uint16_t* Wp,
                        const ReorderView& rv, int T, int d, int F, int n, const uint16_t* residual,
                        uint16_t* Y, hipStream_t s);
 
-// Row pitch (elements) of the transposed per-group V buffer: T rounded up to 8.
-inline int vt_pitch(int T) { return (T + 7) / 8 * 8; }
+// Row pitch (keys) of the transposed V of the prefill attention: whole 16-key
+// groups, the unit of its in-group key permutation.
+inline int vt_pitch(int T) { return (T + 15) / 16 * 16; }
 
 void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* Wk,
                          const uint16_t* Wv, const ReorderView& rv, int T, int d, int n_kv, int r,
@@ -58,7 +63,7 @@ constexpr int kMaxDecodeBatch = 64;
 void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
                        const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
                        const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
-void launch_kmask_decode(const char* tname, const uint16_t* A, const uint16_t* Wp,
+void launch_kmask_decode(KmUse use, const uint16_t* A, const uint16_t* Wp,
                          const uint8_t* mask, int B, int d, int F, int n,
                          const uint16_t* residual, uint16_t* Y, hipStream_t s);
 int attn_decode_chunks(int kv_len);
