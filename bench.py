@@ -42,12 +42,27 @@ def log(msg):
 
 # ------------------------------------------------------------- workloads
 
+def layer_name(base, keep, kind):
+    """Workload name; the default structure (router top-k at 50%) keeps the base name."""
+    return base if (kind, keep) == ("router", 0.5) else f"{base}_{kind}_{int(round(keep * 100))}"
+
+
+def measured_keep(c):
+    """Kept fraction of (token, group) pairs and the batch union, per mask."""
+    out = {}
+    for k in ("attn_mask", "ffn_mask"):
+        m = c[k] != 0
+        out[f"{k}_keep"] = round(float(m.mean()), 4)
+        out[f"{k}_union"] = int(m.any(axis=0).sum())
+    return out
+
+
 class LayerPrefill:
     """Llama-3.1-8B-shaped decoder layer, prefill."""
 
     def __init__(self, T=8192, keep=0.5, kind="router"):
         from synth.workloads import layer_8b
-        self.name = "layer_prefill_8b"
+        self.name = layer_name("layer_prefill_8b", keep, kind)
         self.c = layer_8b(T, keep=keep, kind=kind)
         m = self.c["meta"]
         self.m = m
@@ -55,7 +70,8 @@ class LayerPrefill:
         self.config = dict(workload=self.name, T=T, d_model=m["d"], d_ff=m["F"],
                            n_ffn_groups=m["n_ffn"], n_q_heads=m["n_q"], n_kv_heads=m["n_kv"],
                            head_dim=HD, rope_theta=m["rope_theta"], keep=keep,
-                           masks=f"{kind} top-k" if kind == "router" else kind)
+                           masks=f"{kind} top-k" if kind == "router" else kind,
+                           **measured_keep(self.c))
 
     def upload(self, torch, wide, bf16, u8):
         c, m = self.c, self.m
@@ -336,14 +352,15 @@ class LayerDecode:
 
     def __init__(self, B=32, L=8192, keep=0.5, kind="router"):
         from synth.workloads import layer_8b
-        self.name = "layer_decode_8b"
+        self.name = layer_name("layer_decode_8b", keep, kind)
         self.c = layer_8b(B, decode=True, L=L, keep=keep, kind=kind)
         m = self.c["meta"]
         self.m, self.T, self.L = m, B, L
         self.config = dict(workload=self.name, B=B, kv_len=L, d_model=m["d"], d_ff=m["F"],
                            n_ffn_groups=m["n_ffn"], n_q_heads=m["n_q"], n_kv_heads=m["n_kv"],
                            head_dim=HD, rope_theta=m["rope_theta"], keep=keep,
-                           masks=f"{kind} top-k" if kind == "router" else kind)
+                           masks=f"{kind} top-k" if kind == "router" else kind,
+                           **measured_keep(self.c))
         self.bound = "hbm"
 
     def upload(self, torch, wide, bf16, u8):
@@ -453,6 +470,10 @@ def main():
     ap.add_argument("--oracle-tokens", type=int, default=None,
                     help="tokens of the CPU oracle sample (default: all T tokens)")
     ap.add_argument("--no-oracle", action="store_true")
+    ap.add_argument("--keep", type=float, default=0.5,
+                    help="layer workloads: kept fraction of groups per token")
+    ap.add_argument("--masks", default="router", choices=["router", "bernoulli", "clustered"],
+                    help="layer workloads: mask structure")
     ap.add_argument("--skip-ones", action="store_true",
                     help="skip the all-ones comparison (profiler runs: only masked launches)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -486,7 +507,10 @@ def main():
         return
 
     log(f"generating {args.workload} inputs")
-    W = WORKLOADS[args.workload]()
+    if args.workload.startswith("layer_"):
+        W = WORKLOADS[args.workload](keep=args.keep, kind=args.masks)
+    else:
+        W = WORKLOADS[args.workload]()
     W.upload(torch, wide, bf16, u8)
     stream = torch.cuda.current_stream()
 

@@ -132,12 +132,13 @@ template <int BM, int BN, int USE>
 __global__ void __launch_bounds__(256, 1)
     kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
                        const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
-                       const int32_t* __restrict__ tgroups, int T, int d, int F, int n, int G,
-                       int nw, int ntn, const uint16_t* __restrict__ residual,
-                       uint16_t* __restrict__ Y) {
+                       const int32_t* __restrict__ tgroups, const int32_t* __restrict__ order,
+                       int T, int d, int F, int n, int G, int nw, int ntn,
+                       const uint16_t* __restrict__ residual, uint16_t* __restrict__ Y) {
   using C = TileCfg<BM, BN>;
   WIDE_STAGE_ARRAYS(C);
   __shared__ uint64_t sBits[BM * 4];
+  __shared__ int sTok[BM];  // token of each tile row
   __shared__ int sGroups[256];
   __shared__ uint8_t sLive[256 * 4];
 
@@ -150,9 +151,14 @@ __global__ void __launch_bounds__(256, 1)
   const int t0 = mt * BM, rows = min(BM, T - t0), n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
   const int ng = tcount[mt];
+  // tile rows are tokens t0.. in order, or order[t0..] (tokens sorted by mask
+  // pattern, so row blocks share dropped groups)
+  for (int i = tid; i < BM; i += C::kThreads)
+    sTok[i] = i < rows ? (order ? order[t0 + i] : t0 + i) : 0;
+  __syncthreads();
   for (int i = tid; i < BM * nw; i += C::kThreads) {
     const int r = i / nw, w = i % nw;
-    sBits[r * 4 + w] = r < rows ? packed[(size_t)(t0 + r) * nw + w] : 0ull;
+    sBits[r * 4 + w] = r < rows ? packed[(size_t)sTok[r] * nw + w] : 0ull;
   }
   for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
   __syncthreads();
@@ -165,7 +171,7 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
   for (int q = 0; q < C::A_INST; ++q) {
     aRow[q] = dma_row(wave, q, lane);
-    aBase[q] = (uint32_t)((t0 + aRow[q]) * F + chunk8) * 2u;
+    aBase[q] = (uint32_t)(sTok[aRow[q]] * F + chunk8) * 2u;
   }
 #pragma unroll
   for (int q = 0; q < C::B_INST; ++q) {
@@ -174,22 +180,38 @@ __global__ void __launch_bounds__(256, 1)
   }
   const int kpg = G / kBK;  // K slices per group
   const int nk = ng * kpg;
-  auto issue = [&](int kt, int st) {
+  // The issues walk the slices in order, so the slice's group comes from running
+  // counters; the next group is read from LDS one call ahead, and each lane keeps
+  // the mask word of its A rows that holds the current group's bit (reloaded
+  // only when the group crosses a 64-group word).
+  int is_gi = 0, is_s = 0, is_w = -1;
+  int is_gv = ng > 0 ? sGroups[0] : 0;  // read ahead; made scalar when used
+  uint64_t rw[C::A_INST];
+  auto issue = [&](int, int st) {
+    const int g = __builtin_amdgcn_readfirstlane(is_gv);
+    if ((g >> 6) != is_w) {
+      is_w = g >> 6;
+#pragma unroll
+      for (int q = 0; q < C::A_INST; ++q)
+        rw[q] = aRow[q] < rows ? sBits[aRow[q] * 4 + is_w] : 0ull;
+    }
     const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
-    const int g = sGroups[kt / kpg], kk = (kt % kpg) * kBK;
-    const uint64_t sel = 1ull << (g & 63);
-    const int w = g >> 6;
+    const int kk = is_s * kBK;
     const uint32_t ka = (uint32_t)(g * G + kk) * 2u;
 #pragma unroll
     for (int q = 0; q < C::A_INST; ++q) {
       // l=1: rows of tokens that dropped g (or past T) are not fetched (zeros)
-      const bool keep = aRow[q] < rows && (sBits[aRow[q] * 4 + w] & sel);
+      const bool keep = (rw[q] >> (g & 63)) & 1ull;
       lds_dma16(rH, dma_dst(a, wave, q), keep ? aBase[q] + ka : kSkip);
     }
     const uint32_t kb = (uint32_t)(g * d * G + kk) * 2u;
 #pragma unroll
     for (int q = 0; q < C::B_INST; ++q)
       lds_dma16(rW, dma_dst(b, wave, q), bOff[q] == kSkip ? kSkip : bOff[q] + kb);
+    if (++is_s == kpg) {
+      is_s = 0;
+      if (++is_gi < ng) is_gv = sGroups[is_gi];
+    }
   };
   // l=2: per group of the tile, the row blocks of each wave that hold at least one
   // token keeping it (sLive[group index][wave]); a wave whose blocks are all live
@@ -213,11 +235,21 @@ __global__ void __launch_bounds__(256, 1)
 
   WaveAcc<BM, BN> acc;
   acc.zero();
-  if (all_live)
+  if (all_live) {
     acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, [](int) { return 0u; });
-  else
-    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue,
-                                      [&](int kt) { return (uint32_t)sLive[(kt / kpg) * 4 + wave]; });
+  } else {
+    // live row blocks of the slices in order, the next group's read one call ahead
+    int lv_gi = 0, lv_s = 0;
+    uint32_t lv = ng > 0 ? sLive[wave] : 0u;
+    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, [&](int) {
+      const uint32_t v = lv;
+      if (++lv_s == kpg) {
+        lv_s = 0;
+        if (++lv_gi < ng) lv = sLive[lv_gi * 4 + wave];
+      }
+      return v;
+    });
+  }
 
   // The residual pointer passes through an empty asm here so its loads are not
   // hoisted into the K loop, where they would push accumulators out of registers.
@@ -232,7 +264,7 @@ __global__ void __launch_bounds__(256, 1)
       for (int e = 0; e < 16; ++e) {
         const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
         if (row < rows && col < d) {
-          const size_t o = (size_t)(t0 + row) * d + col;
+          const size_t o = (size_t)sTok[row] * d + col;
           float v = acc.acc[i][j][e];
           if (res) v += bf2f(res[o]);
           Y[o] = f2bf(v);
@@ -269,8 +301,8 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   auto k = best_bn == 256   ? kmask_gemm_prefill<kDownBM, 256, USE>
            : best_bn == 192 ? kmask_gemm_prefill<kDownBM, 192, USE>
                             : kmask_gemm_prefill<kDownBM, 128, USE>;
-  k<<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, T, d, F, n, G, nw, ntn,
-                         residual, Y);
+  k<<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, rv.order, T, d, F, n,
+                         G, nw, ntn, residual, Y);
 }
 
 void launch_kmask_gemm(KmUse use, const uint16_t* A, const uint16_t* Wp, const ReorderView& rv,

@@ -27,12 +27,17 @@ struct ReorderView {
   int32_t* rank = nullptr;        // [n, T] (may be null when no kernel needs it)
   int32_t* tile_count = nullptr;  // [ceil(T / tile_m)]
   int32_t* tile_groups = nullptr; // [ceil(T / tile_m), n]
+  int32_t* order = nullptr;       // [T] token order of the tiles (null: 0..T-1)
   int tile_m = 0;
 };
 
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
+// Token order sorted by mask pattern (the bits of groups 0..7; stable), and the
+// group union of each tile of tile_m consecutive tokens in that order.
+void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
+                       int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
 
 void launch_pack_kmajor(const uint16_t* W, int n, int G, int d, uint16_t* Wp, hipStream_t s);
 

@@ -133,6 +133,107 @@ __global__ void __launch_bounds__(kGroupThreads)
   if (threadIdx.x == 0) group_count[g] = cnt;
 }
 
+constexpr int kSortThreads = 1024;
+constexpr int kSortWaves = kSortThreads / kWave;
+constexpr int kSortBins = 256;  // key = mask bits of groups 0..7
+
+// One work-group.  Wave w owns the contiguous tokens [w c, (w + 1) c) and
+// (1) counts its keys, (2) one scan over (key, wave) gives each wave's first
+// slot per key, (3) each wave places its tokens in order, 64 at a time; lanes
+// with equal keys are ranked by a ballot match.  Then the group union of every
+// tile of the new order.
+__global__ void __launch_bounds__(kSortThreads)
+    reorder_token_sort(const uint64_t* __restrict__ packed, int T, int n, int nw, int tile_m,
+                       int32_t* __restrict__ order, int32_t* __restrict__ tile_count,
+                       int32_t* __restrict__ tile_groups) {
+  __shared__ int sHist[kSortWaves][kSortBins];
+  __shared__ int sTot[kSortBins];
+  const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
+  for (int i = tid; i < kSortWaves * kSortBins; i += kSortThreads) (&sHist[0][0])[i] = 0;
+  __syncthreads();
+  const int per = (T + kSortWaves - 1) / kSortWaves;
+  const int c0 = min(T, wave * per), c1 = min(T, c0 + per);
+  auto key_of = [&](int t) { return (int)(packed[(size_t)t * nw] & 0xffull); };
+  for (int t = c0 + lane; t < c1; t += kWave) atomicAdd(&sHist[wave][key_of(t)], 1);
+  __syncthreads();
+  // exclusive scan in (key, wave) order: thread k < 256 owns key k
+  if (tid < kSortBins) {
+    int run = 0;
+    for (int w = 0; w < kSortWaves; ++w) {
+      const int v = sHist[w][tid];
+      sHist[w][tid] = run;
+      run += v;
+    }
+    sTot[tid] = run;
+  }
+  __syncthreads();
+  if (wave == 0) {  // scan of the per-key totals, 4 keys per lane
+    int v[4], sum = 0;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = sTot[4 * lane + i], sum += v[i];
+    int incl = sum;
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int u = __shfl_up(incl, off);
+      if (lane >= off) incl += u;
+    }
+    int base = incl - sum;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) sTot[4 * lane + i] = base, base += v[i];
+  }
+  __syncthreads();
+  for (int t0 = c0; t0 < c1; t0 += kWave) {
+    const int t = t0 + lane;
+    const bool ok = t < c1;
+    const int key = ok ? key_of(t) : -1;
+    uint64_t same = ballot(ok);
+#pragma unroll
+    for (int b = 0; b < 8; ++b) {
+      const uint64_t ones = ballot(ok && ((key >> b) & 1));
+      same &= ((key >> b) & 1) ? ones : ~ones;
+    }
+    if (ok) {
+      const uint64_t below = same & ((1ull << lane) - 1ull);
+      order[sTot[key] + sHist[wave][key] + popc64(below)] = t;
+      // the last lane of each key bumps the wave's slot for that key
+      if ((same >> lane) == 1ull) sHist[wave][key] += popc64(same);
+    }
+  }
+  __syncthreads();
+  // tile unions: wave w takes tiles w, w + 16, ...
+  const int n_tiles = (T + tile_m - 1) / tile_m;
+  for (int tile = wave; tile < n_tiles; tile += kSortWaves) {
+    const int r0 = tile * tile_m, r1 = min(T, r0 + tile_m);
+    uint64_t uni[4] = {0, 0, 0, 0};
+    for (int i = r0 + lane; i < r1; i += kWave) {
+      const int t = order[i];
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (w < nw) uni[w] |= packed[(size_t)t * nw + w];
+    }
+    int32_t* out = tile_groups + (size_t)tile * n;
+    int written = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w >= nw) break;
+      uint32_t lo = (uint32_t)uni[w], hi = (uint32_t)(uni[w] >> 32);
+      for (int off = 32; off >= 1; off >>= 1) lo |= __shfl_xor(lo, off), hi |= __shfl_xor(hi, off);
+      const uint64_t u = ((uint64_t)hi << 32) | lo;
+      const int g = 64 * w + lane;
+      if (g < n && ((u >> lane) & 1ull)) out[written + popc64(u & ((1ull << lane) - 1ull))] = g;
+      written += popc64(u);
+    }
+    for (int p = written + lane; p < n; p += kWave) out[p] = -1;
+    if (lane == 0) tile_count[tile] = written;
+  }
+}
+
+void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
+                       int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
+  WIDE_TRACE("reorder_token_sort", s);
+  reorder_token_sort<<<1, kSortThreads, 0, s>>>(packed, T, n, (n + 63) / 64, tile_m, order,
+                                                tile_count, tile_groups);
+}
+
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
