@@ -150,7 +150,7 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
     return w;
   }
   w.rv = carve_reorder(c, T, nkv, ffn_down_tile_m(), false);
-  w.rv.order = c.take<int32_t>(T);
+  if (nkv <= kSortMaxGroups) w.rv.order = c.take<int32_t>(T);
   w.Qc = c.take<uint16_t>((size_t)nq * T * kHeadDim);
   w.Kc = c.take<uint16_t>((size_t)nkv * T * kHeadDim);
   w.Vt = c.take<uint16_t>((size_t)nkv * kHeadDim * vt_pitch(T));
@@ -169,13 +169,17 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
     launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, Y, s);
     return;
   }
-  // group partitions for the QKV projection and the core; for the O projection,
-  // tiles of tokens sorted by their head-group pattern, so that row blocks and
-  // whole tiles share dropped groups
-  launch_reorder(mask, T, nkv, w.rv.tile_m, w.rv.packed, w.rv.count, w.rv.perm, w.rv.rank,
-                 nullptr, nullptr, s);
-  launch_token_sort(w.rv.packed, T, nkv, w.rv.tile_m, w.rv.order, w.rv.tile_count,
-                    w.rv.tile_groups, s);
+  // group partitions for the QKV projection and the core; for the O projection
+  // with few groups, tiles of tokens sorted by their head-group pattern, so that
+  // row blocks and whole tiles share dropped groups
+  if (nkv <= kSortMaxGroups) {
+    launch_reorder(mask, T, nkv, w.rv.tile_m, w.rv.packed, w.rv.count, w.rv.perm, w.rv.rank,
+                   nullptr, nullptr, s);
+    launch_token_sort(w.rv.packed, T, nkv, w.rv.tile_m, w.rv.order, w.rv.tile_count,
+                      w.rv.tile_groups, s);
+  } else {
+    run_reorder(mask, T, nkv, w.rv, s);
+  }
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
   launch_kmask_gemm(kUseAttnO, w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
 }

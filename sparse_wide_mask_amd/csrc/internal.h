@@ -34,8 +34,10 @@ struct ReorderView {
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
-// Token order sorted by mask pattern (the bits of groups 0..7; stable), and the
-// group union of each tile of tile_m consecutive tokens in that order.
+// Token order sorted by mask pattern (stable; n <= kSortMaxGroups, so the key is
+// the whole pattern), and the group union of each tile of tile_m consecutive
+// tokens in that order.  T <= WIDE_MAX_TOKENS (the keys take T bytes of LDS).
+constexpr int kSortMaxGroups = 8;
 void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
                        int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
 

@@ -12,6 +12,7 @@
 //                           consecutive tokens, a wave shuffle scan plus one LDS
 //                           pass over the waves gives the kept tokens before each
 //                           run, and the thread places its tokens.
+#include "wide.h"
 #include "common.h"
 #include "gemm_tile.h"
 #include "internal.h"
@@ -135,26 +136,40 @@ __global__ void __launch_bounds__(kGroupThreads)
 
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kSortBins = 256;  // key = mask bits of groups 0..7
+constexpr int kSortBins = 256;  // key = the whole mask pattern (n <= 8 groups)
 
-// One work-group.  Wave w owns the contiguous tokens [w c, (w + 1) c) and
-// (1) counts its keys, (2) one scan over (key, wave) gives each wave's first
-// slot per key, (3) each wave places its tokens in order, 64 at a time; lanes
-// with equal keys are ranked by a ballot match.  Then the group union of every
-// tile of the new order.
+// One work-group; keys (the tokens' 8-bit patterns) are staged in LDS.  Wave w
+// owns the contiguous tokens [w c, (w + 1) c) and (1) counts its keys, (2) one
+// scan over (key, wave) gives each wave's first slot per key, (3) each wave
+// places its tokens in order, 64 at a time; lanes with equal keys are ranked by a
+// ballot match.  (4) A tile of the new order covers a run of whole key ranges,
+// so its group union is the OR of the keys whose range meets it.
 __global__ void __launch_bounds__(kSortThreads)
     reorder_token_sort(const uint64_t* __restrict__ packed, int T, int n, int nw, int tile_m,
                        int32_t* __restrict__ order, int32_t* __restrict__ tile_count,
                        int32_t* __restrict__ tile_groups) {
+  extern __shared__ uint8_t sKey[];  // [T]
   __shared__ int sHist[kSortWaves][kSortBins];
-  __shared__ int sTot[kSortBins];
+  __shared__ int sStart[kSortBins + 1];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   for (int i = tid; i < kSortWaves * kSortBins; i += kSortThreads) (&sHist[0][0])[i] = 0;
+  for (int t0 = 0; t0 < T; t0 += 4 * kSortThreads) {
+    uint64_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kSortThreads + tid;
+      v[u] = t < T ? packed[(size_t)t * nw] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int t = t0 + u * kSortThreads + tid;
+      if (t < T) sKey[t] = (uint8_t)v[u];
+    }
+  }
   __syncthreads();
   const int per = (T + kSortWaves - 1) / kSortWaves;
   const int c0 = min(T, wave * per), c1 = min(T, c0 + per);
-  auto key_of = [&](int t) { return (int)(packed[(size_t)t * nw] & 0xffull); };
-  for (int t = c0 + lane; t < c1; t += kWave) atomicAdd(&sHist[wave][key_of(t)], 1);
+  for (int t = c0 + lane; t < c1; t += kWave) atomicAdd(&sHist[wave][sKey[t]], 1);
   __syncthreads();
   // exclusive scan in (key, wave) order: thread k < 256 owns key k
   if (tid < kSortBins) {
@@ -164,13 +179,13 @@ __global__ void __launch_bounds__(kSortThreads)
       sHist[w][tid] = run;
       run += v;
     }
-    sTot[tid] = run;
+    sStart[tid] = run;
   }
   __syncthreads();
   if (wave == 0) {  // scan of the per-key totals, 4 keys per lane
     int v[4], sum = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = sTot[4 * lane + i], sum += v[i];
+    for (int i = 0; i < 4; ++i) v[i] = sStart[4 * lane + i], sum += v[i];
     int incl = sum;
     for (int off = 1; off < kWave; off <<= 1) {
       const int u = __shfl_up(incl, off);
@@ -178,13 +193,14 @@ __global__ void __launch_bounds__(kSortThreads)
     }
     int base = incl - sum;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) sTot[4 * lane + i] = base, base += v[i];
+    for (int i = 0; i < 4; ++i) sStart[4 * lane + i] = base, base += v[i];
+    if (lane == kWave - 1) sStart[kSortBins] = incl;
   }
   __syncthreads();
   for (int t0 = c0; t0 < c1; t0 += kWave) {
     const int t = t0 + lane;
     const bool ok = t < c1;
-    const int key = ok ? key_of(t) : -1;
+    const int key = ok ? sKey[t] : -1;
     uint64_t same = ballot(ok);
 #pragma unroll
     for (int b = 0; b < 8; ++b) {
@@ -193,45 +209,43 @@ __global__ void __launch_bounds__(kSortThreads)
     }
     if (ok) {
       const uint64_t below = same & ((1ull << lane) - 1ull);
-      order[sTot[key] + sHist[wave][key] + popc64(below)] = t;
+      order[sStart[key] + sHist[wave][key] + popc64(below)] = t;
       // the last lane of each key bumps the wave's slot for that key
       if ((same >> lane) == 1ull) sHist[wave][key] += popc64(same);
     }
   }
-  __syncthreads();
-  // tile unions: wave w takes tiles w, w + 16, ...
+  // tile unions from the key ranges: wave w takes tiles w, w + 16, ...
   const int n_tiles = (T + tile_m - 1) / tile_m;
   for (int tile = wave; tile < n_tiles; tile += kSortWaves) {
-    const int r0 = tile * tile_m, r1 = min(T, r0 + tile_m);
-    uint64_t uni[4] = {0, 0, 0, 0};
-    for (int i = r0 + lane; i < r1; i += kWave) {
-      const int t = order[i];
+    const int p0 = tile * tile_m, p1 = min(T, p0 + tile_m);
+    uint32_t u = 0;
 #pragma unroll
-      for (int w = 0; w < 4; ++w)
-        if (w < nw) uni[w] |= packed[(size_t)t * nw + w];
+    for (int i = 0; i < 4; ++i) {
+      const int k = 4 * lane + i;
+      const int a = sStart[k], e = sStart[k + 1];
+      if (a < e && a < p1 && e > p0) u |= (uint32_t)k;
     }
+    for (int off = 32; off >= 1; off >>= 1) u |= __shfl_xor(u, off);
     int32_t* out = tile_groups + (size_t)tile * n;
-    int written = 0;
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      if (w >= nw) break;
-      uint32_t lo = (uint32_t)uni[w], hi = (uint32_t)(uni[w] >> 32);
-      for (int off = 32; off >= 1; off >>= 1) lo |= __shfl_xor(lo, off), hi |= __shfl_xor(hi, off);
-      const uint64_t u = ((uint64_t)hi << 32) | lo;
-      const int g = 64 * w + lane;
-      if (g < n && ((u >> lane) & 1ull)) out[written + popc64(u & ((1ull << lane) - 1ull))] = g;
-      written += popc64(u);
-    }
-    for (int p = written + lane; p < n; p += kWave) out[p] = -1;
+    const bool has = lane < n && ((u >> lane) & 1u);
+    const uint64_t hb = ballot(has);
+    if (has) out[popc64(hb & ((1ull << lane) - 1ull))] = lane;
+    const int written = popc64(hb);
+    for (int q = written + lane; q < n; q += kWave) out[q] = -1;
     if (lane == 0) tile_count[tile] = written;
   }
 }
 
 void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
                        int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
+  // the key array may take the whole 64 KB of dynamic LDS next to the static part
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&reorder_token_sort),
+      hipFuncAttributeMaxDynamicSharedMemorySize, WIDE_MAX_TOKENS);
+  (void)attr;
   WIDE_TRACE("reorder_token_sort", s);
-  reorder_token_sort<<<1, kSortThreads, 0, s>>>(packed, T, n, (n + 63) / 64, tile_m, order,
-                                                tile_count, tile_groups);
+  reorder_token_sort<<<1, kSortThreads, (size_t)T, s>>>(packed, T, n, (n + 63) / 64, tile_m,
+                                                        order, tile_count, tile_groups);
 }
 
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
