@@ -53,6 +53,61 @@ WIDE_DEV bf16x8 xload(rsrc_t r, uint32_t off) {
   return *reinterpret_cast<const bf16x8*>(&v);
 }
 
+// One MFMA output column of the N-masked decode projection: its weight row and,
+// at the end, where its value for a token goes.  FFN: columns 0..7 are gate
+// channels cb*8 + ch, columns 8..15 the same up channels, and SwiGLU pairs lane
+// ch with lane ch + 8.  Attention: chunk cb of head hh (q heads 0..r-1, then k,
+// then v) covers head dims {8c..8c+7} and {64+8c..64+8c+7}, so each RoPE pair
+// (j, j + 64) is a lane pair too; rotation is at position kv_len, and k and v go
+// straight into the caches at slot kv_len.
+template <int MODE>
+struct NmCol {
+  const uint16_t* wrow;
+  int hh = 0, jrow = 0;
+  float sn = 0.f, cs = 1.f;
+  bool rope = false;
+
+  WIDE_DEV NmCol(int g, int cb, int ch, const uint16_t* W0, const uint16_t* W1,
+                 const uint16_t* W2, int G, int d, int r, int kv_len, float log2_theta) {
+    if (MODE == kNmFfn) {
+      wrow = (ch < 8 ? W0 : W1) + (size_t)(g * G + cb * 8 + (ch & 7)) * d;
+    } else {
+      hh = cb / 8;
+      const int c = cb % 8;
+      jrow = ch < 8 ? 8 * c + ch : 64 + 8 * c + (ch - 8);
+      if (hh < r)
+        wrow = W0 + ((size_t)(g * r + hh) * kHdD + jrow) * d;
+      else
+        wrow = (hh == r ? W1 : W2) + ((size_t)g * kHdD + jrow) * d;
+      rope = hh < r + 1 && log2_theta > 0.f;
+      if (rope) {
+        const float inv = exp2f(-(2.f * (ch < 8 ? jrow : jrow - 64) / kHdD) * log2_theta);
+        sincosf((float)kv_len * inv, &sn, &cs);
+      }
+    }
+  }
+
+  // v = this lane's column value for token tok (tok < 0: no token).  Every lane
+  // of the wave calls it (the pairing is a lane shuffle).
+  WIDE_DEV void store(float v, int tok, int g, int cb, int ch, int G, int r, int n_groups,
+                      int kv_len, int kv_cap, uint16_t* out0, uint16_t* Kc, uint16_t* Vc) const {
+    const float other = __shfl_xor(v, 8);
+    if (MODE == kNmFfn) {
+      if (tok >= 0 && ch < 8)
+        out0[(size_t)tok * (n_groups * G) + g * G + cb * 8 + ch] = f2bf(silu(v) * other);
+    } else {
+      float o = v;
+      if (rope) o = ch < 8 ? v * cs - other * sn : v * cs + other * sn;
+      if (tok < 0) return;
+      const uint16_t bits = f2bf(o);
+      if (hh < r)
+        out0[((size_t)tok * (n_groups * r) + g * r + hh) * kHdD + jrow] = bits;
+      else
+        (hh == r ? Kc : Vc)[(((size_t)tok * n_groups + g) * kv_cap + kv_len) * kHdD + jrow] = bits;
+    }
+  }
+};
+
 template <int MODE, int NRB>
 __global__ void __launch_bounds__(256)
     nmask_decode(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W0,
@@ -68,34 +123,19 @@ __global__ void __launch_bounds__(256)
   // mask column of g, one token per lane: kept tokens in order are the MFMA rows
   const rsrc_t mr = make_rsrc(mask, (uint32_t)(B * n_groups));
   const bool kept = ldbuf1(mr, lane < B ? (uint32_t)(lane * n_groups + g) : kSkip) != 0u;
-  const uint64_t col = ballot(kept);
-  const int cnt = popc64(col);
+  const uint64_t mcol = ballot(kept);
+  const int cnt = popc64(mcol);
   if (cnt == 0) return;  // l=0: no token of the batch keeps g
   if (wave == 0) {
-    if (kept) sTok[popc64(col & ((1ull << lane) - 1ull))] = lane;
+    if (kept) sTok[popc64(mcol & ((1ull << lane) - 1ull))] = lane;
     if (lane >= cnt) sTok[lane] = -1;
   }
   __syncthreads();
   const int nrb = (cnt + 15) / 16;  // l=2: row blocks past the count are skipped
 
-  // MFMA column (16 per work-group) -> weight row
   const int ch = lane & 15;
-  const uint16_t* wrow;
-  int hh = 0, jrow = 0;
-  if (MODE == kNmFfn) {
-    // columns 0..7: gate channels cb*8 + ch; columns 8..15: the same up channels
-    wrow = (ch < 8 ? W0 : W1) + (size_t)(g * G + cb * 8 + (ch & 7)) * d;
-  } else {
-    // chunk cb of head hh (q heads 0..r-1, then k, then v) covers head dims
-    // {8c..8c+7} and {64+8c..64+8c+7}, so each RoPE pair stays in the work-group
-    hh = cb / 8;
-    const int c = cb % 8;
-    jrow = ch < 8 ? 8 * c + ch : 64 + 8 * c + (ch - 8);
-    if (hh < r)
-      wrow = W0 + ((size_t)(g * r + hh) * kHdD + jrow) * d;
-    else
-      wrow = (hh == r ? W1 : W2) + ((size_t)g * kHdD + jrow) * d;
-  }
+  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, kv_len, log2_theta);
+  const uint16_t* wrow = col.wrow;
 
   f32x4 acc[NRB];
 #pragma unroll
@@ -113,24 +153,83 @@ __global__ void __launch_bounds__(256)
     xoff[rb] = tok >= 0 ? (uint32_t)(((size_t)tok * d + koff) * 2) : kSkip;
   }
   const uint16_t* wp = wrow + koff;
+  // Every work-group reads the same activation rows; each starts its K walk at
+  // a different batch so that they do not all hit the same L2 lines at once.
   constexpr int U = dec_unroll<NRB>();
-  int k0 = kbeg;
-  for (; k0 + 32 * U <= kend; k0 += 32 * U) {
-    bf16x8 wf[U], xf[U][NRB];
+  const int S = (kend - kbeg) / 32;
+  const int nbat = S / U;
+  const int rot = nbat > 0 ? (int)((blockIdx.x * 7u) % (unsigned)nbat) * U : 0;
+  auto kat = [&](int j) {  // K offset of step j; a whole batch stays contiguous
+    if (j >= nbat * U) return kbeg + 32 * j;
+    const int s = j + rot;
+    return kbeg + 32 * (s >= nbat * U ? s - nbat * U : s);
+  };
+  if constexpr (NRB == 1) {
+    // few rows: MFMA fragments straight from global memory
+#pragma unroll 1
+    for (int j0 = 0; j0 < nbat * U; j0 += U) {
+      bf16x8 wf[U], xf[U][NRB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * u);
+      for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + kat(j0 + u));
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb) xf[u][rb] = xload(xr, xoff[rb] + (k0 + 32 * u) * 2);
-    __builtin_amdgcn_sched_barrier(0);  // all loads of the batch before its MFMAs
+        for (int rb = 0; rb < NRB; ++rb) xf[u][rb] = xload(xr, xoff[rb] + kat(j0 + u) * 2);
+      __builtin_amdgcn_sched_barrier(0);  // all loads of the batch before its MFMAs
 #pragma unroll
-    for (int u = 0; u < U; ++u)
+      for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        if (rb < nrb) acc[rb] = mfma16(xf[u][rb], wf[u], acc[rb]);
+        for (int rb = 0; rb < NRB; ++rb)
+          if (rb < nrb) acc[rb] = mfma16(xf[u][rb], wf[u], acc[rb]);
+    }
+  } else {
+    // Many rows (used when there are too few column blocks to fill the chip
+    // with nmask_decode_cols): 16-row fragment loads are slow from L2, so each
+    // wave copies its batch's rows (64 U bytes per row) with contiguous loads
+    // into its own LDS area (16-byte chunk c of row i at slot c ^ (i mod CPR))
+    // and reads the fragments from there.
+    constexpr int CPR = 4 * U;          // 16-byte chunks per row per batch
+    constexpr int RPI = 64 / CPR;       // rows per load instruction
+    constexpr int NI = 16 * NRB / RPI;  // load instructions per batch
+    __shared__ __attribute__((aligned(16))) uint16_t sX[4][16 * NRB * CPR * 8];
+    uint16_t* myX = sX[wave];
+    const int lrow = lane / CPR, lch = lane % CPR;
+    uint32_t rowoff[NI];
+#pragma unroll
+    for (int i = 0; i < NI; ++i) {
+      const int tok = sTok[i * RPI + lrow];
+      rowoff[i] = tok >= 0 ? (uint32_t)(((size_t)tok * d + lch * 8) * 2) : kSkip;
+    }
+#pragma unroll 1
+    for (int j0 = 0; j0 < nbat * U; j0 += U) {
+      const int k0 = kat(j0);
+      bf16x8 wf[U];
+      u32x4 xv[NI];
+#pragma unroll
+      for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * u);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) xv[i] = ldbuf16(xr, rowoff[i] + k0 * 2);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int row = i * RPI + lrow;
+        *reinterpret_cast<u32x4*>(myX + (row * CPR + (lch ^ (row % CPR))) * 8) = xv[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          if (rb >= nrb) continue;
+          const int row = rb * 16 + ch, c = 4 * u + (lane >> 4);
+          const bf16x8 xf =
+              *reinterpret_cast<const bf16x8*>(myX + (row * CPR + (c ^ (row % CPR))) * 8);
+          acc[rb] = mfma16(xf, wf[u], acc[rb]);
+        }
+      __builtin_amdgcn_wave_barrier();  // fragment reads before the next batch's writes
+    }
   }
-  for (; k0 < kend; k0 += 32) {
+  for (int j0 = nbat * U; j0 < S; ++j0) {
+    const int k0 = kat(j0);
     const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wp + k0);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
@@ -148,11 +247,6 @@ __global__ void __launch_bounds__(256)
   }
   __syncthreads();
   if (wave > 0) return;
-  const float theta_inv = (MODE == kNmQkv && hh < r + 1 && log2_theta > 0.f)
-                              ? exp2f(-(2.f * (ch < 8 ? jrow : jrow - 64) / kHdD) * log2_theta)
-                              : 0.f;
-  float sn = 0.f, cs = 1.f;
-  if (theta_inv != 0.f) sincosf((float)kv_len * theta_inv, &sn, &cs);
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) {
     if (rb >= nrb) break;
@@ -160,24 +254,140 @@ __global__ void __launch_bounds__(256)
     for (int i = 0; i < 4; ++i) {
       const int row = rb * 16 + acc16_row(lane, i);
       const float v = acc[rb][i] + sRed[0][row][ch] + sRed[1][row][ch] + sRed[2][row][ch];
-      const int tok = row < cnt ? sTok[row] : -1;
-      if (MODE == kNmFfn) {
-        // SwiGLU: gate in column ch, its up partner in column ch + 8 (lane + 8)
-        const float up = __shfl_xor(v, 8);
-        if (tok >= 0 && ch < 8)
-          out0[(size_t)tok * (n_groups * G) + g * G + cb * 8 + ch] = f2bf(silu(v) * up);
-      } else {
-        // RoPE pair partner: channel ch^8 of the same row, held by lane ^ 8
-        const float other = __shfl_xor(v, 8);
-        float o = v;
-        if (theta_inv != 0.f) o = ch < 8 ? v * cs - other * sn : v * cs + other * sn;
-        if (tok < 0) continue;
-        const uint16_t bits = f2bf(o);
-        if (hh < r)
-          out0[((size_t)tok * (n_groups * r) + g * r + hh) * kHdD + jrow] = bits;
-        else
-          (hh == r ? Kc : Vc)[(((size_t)tok * n_groups + g) * kv_cap + kv_len) * kHdD + jrow] = bits;
+      col.store(v, row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, kv_len, kv_cap, out0,
+                Kc, Vc);
+    }
+  }
+}
+
+// The same projection for batches over 16 tokens, where the activation rows
+// (up to 64 x d) are read as often as the weights: a work-group is 4 waves x 16
+// columns over the whole of K, and each batch of 8 K steps of the rows is copied
+// once per work-group, with contiguous loads, into an LDS tile that all 4 waves
+// read their fragments from (16-byte chunk c of row i at slot c ^ (i mod 32));
+// two tiles alternate so the next batch's rows and weights load during the
+// MFMAs of this one.
+template <int MODE, int NRB>
+__global__ void __launch_bounds__(256)
+    nmask_decode_cols(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W0,
+                      const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
+                      const uint8_t* __restrict__ mask, int B, int d, int G, int chunks, int r,
+                      int kv_len, int kv_cap, float log2_theta, uint16_t* __restrict__ out0,
+                      uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc, int n_groups) {
+  constexpr int U = 8;                  // 32-wide K steps per batch
+  constexpr int ROWS = 16 * NRB;
+  constexpr int CPR = 4 * U;            // 16-byte chunks of a row per batch
+  constexpr int XL = ROWS * CPR / 256;  // 16-byte loads per thread per batch
+  __shared__ int sTok[kDecRows];
+  __shared__ __attribute__((aligned(16))) uint16_t sX[2][ROWS * CPR * 8];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c4n = chunks / 4;
+  const int g = blockIdx.x / c4n, cb = (blockIdx.x % c4n) * 4 + wave;
+  const rsrc_t mr = make_rsrc(mask, (uint32_t)(B * n_groups));
+  const bool kept = ldbuf1(mr, lane < B ? (uint32_t)(lane * n_groups + g) : kSkip) != 0u;
+  const uint64_t mcol = ballot(kept);
+  const int cnt = popc64(mcol);
+  if (cnt == 0) return;  // l=0: no token of the batch keeps g
+  if (wave == 0) {
+    if (kept) sTok[popc64(mcol & ((1ull << lane) - 1ull))] = lane;
+    if (lane >= cnt) sTok[lane] = -1;
+  }
+  __syncthreads();
+  const int nrb = (cnt + 15) / 16;  // l=2: row blocks past the count are skipped
+  const int ch = lane & 15, koff = 8 * (lane >> 4);
+  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, kv_len, log2_theta);
+  const uint16_t* wp = col.wrow + koff;
+
+  // this thread's share of a batch copy: chunk q = tid + 256 i of the tile
+  const rsrc_t xr = make_rsrc(X, (uint32_t)((size_t)B * d * 2));
+  uint32_t xo[XL];
+  int xdst[XL];
+#pragma unroll
+  for (int i = 0; i < XL; ++i) {
+    const int q = tid + 256 * i, row = q / CPR, c = q % CPR;
+    const int tok = sTok[row];
+    xo[i] = tok >= 0 ? (uint32_t)(((size_t)tok * d + c * 8) * 2) : kSkip;
+    xdst[i] = (row * CPR + (c ^ (row % CPR))) * 8;
+  }
+  f32x4 acc[NRB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nb = d / (32 * U);
+  // work-groups start at different batches so they do not all read the same
+  // activation lines at once
+  const int rot = nb > 0 ? (int)((blockIdx.x * 7u) % (unsigned)nb) : 0;
+  auto kof = [&](int b) {
+    const int s = b + rot;
+    return 32 * U * (s >= nb ? s - nb : s);
+  };
+  u32x4 xv[XL];
+  bf16x8 wc[U];
+  if (nb > 0) {
+    const int k0 = kof(0);
+#pragma unroll
+    for (int i = 0; i < XL; ++i) xv[i] = ldbuf16(xr, xo[i] + k0 * 2);
+#pragma unroll
+    for (int u = 0; u < U; ++u) wc[u] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * u);
+#pragma unroll
+    for (int i = 0; i < XL; ++i) *reinterpret_cast<u32x4*>(&sX[0][xdst[i]]) = xv[i];
+    lds_barrier();
+  }
+#pragma unroll 1
+  for (int b = 0; b < nb; ++b) {
+    const bool more = b + 1 < nb;
+    bf16x8 wn[U];
+    if (more) {  // rows first: their LDS copy is waited for while the weights fly
+      const int k1 = kof(b + 1);
+#pragma unroll
+      for (int i = 0; i < XL; ++i) xv[i] = ldbuf16(xr, xo[i] + k1 * 2);
+#pragma unroll
+      for (int u = 0; u < U; ++u) wn[u] = *reinterpret_cast<const bf16x8*>(wp + k1 + 32 * u);
+    }
+    const uint16_t* cx = sX[b & 1];
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb) {
+        if (rb >= nrb) continue;
+        const int row = rb * 16 + ch, c = 4 * u + (lane >> 4);
+        const bf16x8 xf = *reinterpret_cast<const bf16x8*>(cx + (row * CPR + (c ^ (row % CPR))) * 8);
+        acc[rb] = mfma16(xf, wc[u], acc[rb]);
       }
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < XL; ++i) *reinterpret_cast<u32x4*>(&sX[(b + 1) & 1][xdst[i]]) = xv[i];
+    }
+    lds_barrier();
+    if (more) {
+#pragma unroll
+      for (int u = 0; u < U; ++u) wc[u] = wn[u];
+    }
+  }
+  // K steps past the last whole batch: fragments straight from global memory
+  {
+    uint32_t xof[NRB];
+#pragma unroll
+    for (int rb = 0; rb < NRB; ++rb) {
+      const int tok = sTok[rb * 16 + ch];
+      xof[rb] = tok >= 0 ? (uint32_t)(((size_t)tok * d + koff) * 2) : kSkip;
+    }
+    for (int k0 = nb * 32 * U; k0 < d; k0 += 32) {
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wp + k0);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        if (rb < nrb) acc[rb] = mfma16(xload(xr, xof[rb] + k0 * 2), wf, acc[rb]);
+    }
+  }
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb) {
+    if (rb >= nrb) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = rb * 16 + acc16_row(lane, i);
+      col.store(acc[rb][i], row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, kv_len,
+                kv_cap, out0, Kc, Vc);
     }
   }
 }
@@ -269,12 +479,19 @@ __global__ void __launch_bounds__(64 * kKmWaves)
       af[rb] = xload(ar, keep ? (uint32_t)(((size_t)b * F + (size_t)g * G + j0 + koff) * 2) : kSkip);
     }
   };
+  // every work-group reads the same A rows: rotate the start of the step walk
+  const int SW = send - sbeg;
+  const int rot = SW > 0 ? (int)((blockIdx.x * 7u) % (unsigned)SW) : 0;
+  auto sat = [&](int j) {
+    const int s = j + rot;
+    return sbeg + (s >= SW ? s - SW : s);
+  };
   constexpr int U = dec_unroll<NRB>() < 8 ? dec_unroll<NRB>() : 8;
-  int s0 = sbeg;
-  for (; s0 + U <= send; s0 += U) {
+  int s0 = 0;
+  for (; s0 + U <= SW; s0 += U) {
     bf16x8 wf[U], af[U][NRB];
 #pragma unroll
-    for (int u = 0; u < U; ++u) operands(s0 + u, wf[u], af[u]);
+    for (int u = 0; u < U; ++u) operands(sat(s0 + u), wf[u], af[u]);
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < U; ++u)
@@ -282,9 +499,9 @@ __global__ void __launch_bounds__(64 * kKmWaves)
       for (int rb = 0; rb < NRB; ++rb)
         if (rb < nrb) acc[rb] = mfma16(af[u][rb], wf[u], acc[rb]);
   }
-  for (; s0 < send; ++s0) {
+  for (; s0 < SW; ++s0) {
     bf16x8 wf, af[NRB];
-    operands(s0, wf, af);
+    operands(sat(s0), wf, af);
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
       if (rb < nrb) acc[rb] = mfma16(af[rb], wf, acc[rb]);
@@ -526,6 +743,11 @@ __global__ void __launch_bounds__(128)
 
 // ------------------------------------------------------------------ launchers
 
+// The column-block kernel (activation rows shared by 64 columns) once the batch
+// spans several row blocks and its work-groups still fill the 256 CUs;
+// otherwise the K-split kernel (16 columns per work-group, 4x the work-groups).
+static bool use_cols(int nrb, int col_blocks) { return nrb > 1 && col_blocks >= 256; }
+
 void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
                        const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
                        const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s) {
@@ -533,12 +755,20 @@ void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* W
   {
     WIDE_TRACE("ffn_up_decode", s);
     const int nrb = (B + 15) / 16;
-    auto k = nrb == 1   ? nmask_decode<kNmFfn, 1>
-             : nrb == 2 ? nmask_decode<kNmFfn, 2>
-             : nrb == 3 ? nmask_decode<kNmFfn, 3>
-                        : nmask_decode<kNmFfn, 4>;
-    k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
-                                 nullptr, nullptr, n);
+    if (!use_cols(nrb, n * (chunks / 4))) {
+      auto k = nrb == 1   ? nmask_decode<kNmFfn, 1>
+               : nrb == 2 ? nmask_decode<kNmFfn, 2>
+               : nrb == 3 ? nmask_decode<kNmFfn, 3>
+                          : nmask_decode<kNmFfn, 4>;
+      k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
+                                   nullptr, nullptr, n);
+    } else {
+      auto k = nrb == 2   ? nmask_decode_cols<kNmFfn, 2>
+               : nrb == 3 ? nmask_decode_cols<kNmFfn, 3>
+                          : nmask_decode_cols<kNmFfn, 4>;
+      k<<<n * (chunks / 4), 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
+                                         nullptr, nullptr, n);
+    }
   }
   launch_kmask_decode(kUseFfnDown, H, Wdp, mask, B, d, F, n, residual, Y, s);
 }
@@ -572,12 +802,20 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
   {
     WIDE_TRACE("attn_qkv_decode", s);
     const int nrb = (B + 15) / 16;
-    auto k = nrb == 1   ? nmask_decode<kNmQkv, 1>
-             : nrb == 2 ? nmask_decode<kNmQkv, 2>
-             : nrb == 3 ? nmask_decode<kNmQkv, 3>
-                        : nmask_decode<kNmQkv, 4>;
-    k<<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, kv_len, kv_cap,
-                                    log2_theta, Qd, Kc, Vc, n_kv);
+    if (!use_cols(nrb, n_kv * (chunks / 4))) {
+      auto k = nrb == 1   ? nmask_decode<kNmQkv, 1>
+               : nrb == 2 ? nmask_decode<kNmQkv, 2>
+               : nrb == 3 ? nmask_decode<kNmQkv, 3>
+                          : nmask_decode<kNmQkv, 4>;
+      k<<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, kv_len, kv_cap,
+                                      log2_theta, Qd, Kc, Vc, n_kv);
+    } else {
+      auto k = nrb == 2   ? nmask_decode_cols<kNmQkv, 2>
+               : nrb == 3 ? nmask_decode_cols<kNmQkv, 3>
+                          : nmask_decode_cols<kNmQkv, 4>;
+      k<<<n_kv * (chunks / 4), 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, kv_len,
+                                            kv_cap, log2_theta, Qd, Kc, Vc, n_kv);
+    }
   }
   const int nch = attn_decode_chunks(kv_len);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHdD);

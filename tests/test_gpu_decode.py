@@ -27,7 +27,8 @@ def _gpu_ffn(c, mode):
 @pytest.mark.parametrize("B,d,F,n,kind", [(1, 512, 2048, 16, "topk"), (5, 256, 1024, 8, "bernoulli"),
                                           (17, 384, 1536, 12, "topk"), (64, 256, 2048, 32, "clustered"),
                                           (33, 256, 1024, 8, "ones"), (9, 256, 1024, 8, "zeros"),
-                                          (100, 256, 1024, 8, "topk")])
+                                          (100, 256, 1024, 8, "topk"), (24, 128, 512, 8, "topk"),
+                                          (48, 448, 1024, 16, "bernoulli")])
 def test_ffn_decode_shapes(B, d, F, n, kind):
     dev()
     log(f"ffn decode B={B} d={d} F={F} n={n} {kind}")
@@ -90,6 +91,9 @@ ATT = [
     (2, 256, 16, 2, 300, 301, 0.75, "bernoulli", 0.0),    # r = 8
     (16, 256, 8, 8, 1000, 1001, 0.5, "clustered", 500000.0),
     (6, 256, 8, 2, 99, 100, 0.0, "zeros", 500000.0),
+    (40, 320, 8, 2, 130, 131, 0.5, "topk", 500000.0),     # batch over 16: LDS-shared rows
+    (20, 128, 8, 4, 10, 12, 0.5, "bernoulli", 0.0),       # d below one 256-wide K batch
+    (64, 512, 16, 4, 33, 40, 0.75, "clustered", 10000.0),
 ]
 
 
