@@ -405,7 +405,12 @@ __global__ void __launch_bounds__(64 * kKmWaves)
   __shared__ uint32_t sU[8];
   __shared__ int sGroups[256];
   __shared__ int sNu;
-  __shared__ float sRed[kKmWaves - 1][kDecRows][16];
+  // per-wave A staging (NRB = 2), later reused for the cross-wave sums
+  constexpr int kStageBytes = NRB == 2 ? kKmWaves * 16 * NRB * 256 : 0;
+  constexpr int kRedBytes = (kKmWaves - 1) * kDecRows * 16 * 4;
+  __shared__ __attribute__((aligned(16))) uint8_t
+      sStage[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
+  auto sRed = reinterpret_cast<float (*)[kDecRows][16]>(sStage);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int n0 = blockIdx.x * 16;
   if (tid < 8) sU[tid] = 0u;
@@ -479,6 +484,67 @@ __global__ void __launch_bounds__(64 * kKmWaves)
       af[rb] = xload(ar, keep ? (uint32_t)(((size_t)b * F + (size_t)g * G + j0 + koff) * 2) : kSkip);
     }
   };
+  if (NRB == 2 && G % 128 == 0) {
+    // Two row blocks: the A reads are as large as the weight stream, and 16-row
+    // fragment loads (64 B per row per instruction) are slow from L2.  The unit
+    // of work is (union group, 128-wide K block): its A rows (256 B each) are
+    // copied with contiguous loads into the wave's LDS area (16-byte chunk c of
+    // row b at slot c ^ (b mod 16)); the next unit's rows and weights load while
+    // this one's MFMAs run.
+    constexpr int CPR = 16, RPI = 4, NI = 16 * NRB / RPI;
+    uint16_t* myA = reinterpret_cast<uint16_t*>(sStage) + wave * (16 * NRB * CPR * 8);
+    const int lrow = lane / CPR, lch = lane % CPR;
+    const int UPG = G / 128, NU = nu * UPG;
+    const int ubeg = wave * NU / kKmWaves, uend = (wave + 1) * NU / kKmWaves;
+    const int UW = uend - ubeg;
+    const int rot = UW > 0 ? (int)((blockIdx.x * 7u) % (unsigned)UW) : 0;
+    auto unit_load = [&](int j, bf16x8 (&wf)[4], u32x4 (&av)[NI]) {
+      int un = j + rot;
+      un = ubeg + (un >= UW ? un - UW : un);
+      const int q = un / UPG, k0 = (un - q * UPG) * 128;
+      const int g = sGroups[q];
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+        wf[t] = *reinterpret_cast<const bf16x8*>(Wp + ((size_t)g * d + n0 + ch) * G + k0 + 32 * t +
+                                                 koff);
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int b = i * RPI + lrow;
+        const bool keep = (sBits[b * 4 + (g >> 6)] >> (g & 63)) & 1ull;
+        av[i] = ldbuf16(ar, keep ? (uint32_t)(((size_t)b * F + (size_t)g * G + k0 + lch * 8) * 2)
+                                 : kSkip);
+      }
+    };
+    bf16x8 wc[4];
+    u32x4 av[NI];
+    if (UW > 0) unit_load(0, wc, av);
+#pragma unroll 1
+    for (int j = 0; j < UW; ++j) {
+#pragma unroll
+      for (int i = 0; i < NI; ++i) {
+        const int b = i * RPI + lrow;
+        *reinterpret_cast<u32x4*>(myA + (b * CPR + (lch ^ (b % CPR))) * 8) = av[i];
+      }
+      __builtin_amdgcn_wave_barrier();
+      bf16x8 wn[4];
+      if (j + 1 < UW) unit_load(j + 1, wn, av);
+#pragma unroll
+      for (int t = 0; t < 4; ++t)
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+          if (rb >= nrb) continue;
+          const int row = rb * 16 + ch, c = 4 * t + (lane >> 4);
+          const bf16x8 af =
+              *reinterpret_cast<const bf16x8*>(myA + (row * CPR + (c ^ (row % CPR))) * 8);
+          acc[rb] = mfma16(af, wc[t], acc[rb]);
+        }
+      __builtin_amdgcn_wave_barrier();  // fragment reads before the next unit's writes
+      if (j + 1 < UW) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) wc[t] = wn[t];
+      }
+    }
+  } else {
   // every work-group reads the same A rows: rotate the start of the step walk
   const int SW = send - sbeg;
   const int rot = SW > 0 ? (int)((blockIdx.x * 7u) % (unsigned)SW) : 0;
@@ -506,6 +572,8 @@ __global__ void __launch_bounds__(64 * kKmWaves)
     for (int rb = 0; rb < NRB; ++rb)
       if (rb < nrb) acc[rb] = mfma16(af[rb], wf, acc[rb]);
   }
+  }
+  __syncthreads();  // every wave is done with its LDS staging area (sRed aliases it)
   if (wave > 0) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb) {
