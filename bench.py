@@ -425,6 +425,19 @@ WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
 
 # ------------------------------------------------------------- measurement
 
+def warm(torch, fn, steps, min_s=0.3):
+    """Untimed warm-up: at least `steps` steps and at least `min_s` seconds, so that
+    the clocks have settled before a short (decode) step is timed."""
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < min_s:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
 def timed(torch, fn, steps, stream):
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
@@ -514,9 +527,7 @@ def main():
     W.upload(torch, wide, bf16, u8)
     stream = torch.cuda.current_stream()
 
-    for _ in range(args.warmup):
-        W.step()
-    torch.cuda.synchronize()
+    warm(torch, W.step, args.warmup)
 
     # timed region: K masked steps, kernel launches bracketed by HIP events
     wide.trace_reset()
@@ -530,9 +541,13 @@ def main():
     # the same kernels, grid policy and inputs with all-ones masks
     ms_ones = None
     if not args.skip_ones:
-        for _ in range(2):
-            W.step(ones=True)
+        warm(torch, lambda: W.step(ones=True), args.warmup)
+        # traced like the masked region, so both carry the same event overhead
+        wide.trace_reset()
+        wide.trace_enable(True)
         ms_ones = timed(torch, lambda: W.step(ones=True), max(3, args.steps // 2), stream)
+        wide.trace_enable(False)
+        wide.trace_reset()
         log(f"all-ones: {ms_ones:.3f} ms/step")
 
     work = W.work()
