@@ -34,7 +34,7 @@ constexpr int kHd = 128;
 
 // ------------------------------------------------------------- QKV projection
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(kGemmThreads, 1)
     attn_qkv_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
                      const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
                      const int32_t* __restrict__ gcount, const int32_t* __restrict__ gperm, int T,
@@ -67,7 +67,7 @@ __global__ void __launch_bounds__(256, 1)
   const int rows = min(BM, cnt - row0);
   const bool kv_tile = nt == ntn - 1;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
   for (int i = tid; i < BM; i += C::kThreads) sTok[i] = i < rows ? gperm[(size_t)g * T + row0 + i] : -1;
   __syncthreads();
 
@@ -433,7 +433,7 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
   const int vtp = vt_pitch(T);
   {
     WIDE_TRACE("attn_qkv_prefill", s);
-    attn_qkv_prefill<<<n_kv * mtiles * ntn, 256, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
+    attn_qkv_prefill<<<n_kv * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
                                                          r, mtiles, vtp, log2_theta, Qc, Kc, Vt);
   }
   const int npairs = ((T + kBQ - 1) / kBQ + 1) / 2;

@@ -45,7 +45,7 @@ WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& m
   const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB)
 
 template <int BM, int BN>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(kGemmThreads, 1)
     ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
                    const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gcount,
                    const int32_t* __restrict__ gperm, int T, int d, int F, int n, int G,
@@ -62,7 +62,7 @@ __global__ void __launch_bounds__(256, 1)
   if (row0 >= cnt) return;  // l=0: no kept token left in this tile
   const int rows = min(BM, cnt - row0);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
   for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gperm[(size_t)g * T + row0 + r] : -1;
   __syncthreads();
 
@@ -129,7 +129,7 @@ __global__ void __launch_bounds__(256, 1)
 }
 
 template <int BM, int BN, int USE>
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(kGemmThreads, 1)
     kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
                        const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
                        const int32_t* __restrict__ tgroups, const int32_t* __restrict__ order,
@@ -140,7 +140,7 @@ __global__ void __launch_bounds__(256, 1)
   __shared__ uint64_t sBits[BM * 4];
   __shared__ int sTok[BM];  // token of each tile row
   __shared__ int sGroups[256];
-  __shared__ uint8_t sLive[256 * 4];
+  __shared__ uint8_t sLive[256 * C::kWaves];
 
   // XCD x takes a contiguous stretch of the block-rasterised tile order.
   const int mtiles = (T + BM - 1) / BM, n_tiles = mtiles * ntn;
@@ -149,7 +149,7 @@ __global__ void __launch_bounds__(256, 1)
   int mt, nt;
   block_raster(p, mtiles, ntn, 4, 8, mt, nt);
   const int t0 = mt * BM, rows = min(BM, T - t0), n0 = nt * BN;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave >> 1, wn = wave & 1;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
   const int ng = tcount[mt];
   // tile rows are tokens t0.. in order, or order[t0..] (tokens sorted by mask
   // pattern, so row blocks share dropped groups)
@@ -228,7 +228,7 @@ __global__ void __launch_bounds__(256, 1)
       const bool k = row < rows && (sBits[row * 4 + w] & sel);
       if (ballot(k)) live |= 1u << i;
     }
-    if (lane == 0) sLive[gi * 4 + wave] = (uint8_t)live;
+    if (lane == 0) sLive[gi * C::kWaves + wave] = (uint8_t)live;
     all_live = all_live && live == C::kAllRows;
   }
   __syncthreads();
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256, 1)
       const uint32_t v = lv;
       if (++lv_s == kpg) {
         lv_s = 0;
-        if (++lv_gi < ng) lv = sLive[lv_gi * 4 + wave];
+        if (++lv_gi < ng) lv = sLive[lv_gi * C::kWaves + wave];
       }
       return v;
     });
@@ -290,7 +290,7 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   const int mtiles = (T + kDownBM - 1) / kDownBM;
   int best_bn = 256;
   long best_cost = -1;
-  for (int bn : {256, 192, 128}) {
+  for (int bn : {256, 128}) {
     const long tiles = (long)mtiles * ((d + bn - 1) / bn);
     const long cost = ((tiles + 255) / 256) * bn;
     if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bn = bn;
@@ -298,10 +298,9 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   const int ntn = (d + best_bn - 1) / best_bn;
   const int grid = 8 * ((mtiles * ntn + 7) / 8);
   WIDE_TRACE(USE == kUseAttnO ? "attn_o" : "ffn_down", s);
-  auto k = best_bn == 256   ? kmask_gemm_prefill<kDownBM, 256, USE>
-           : best_bn == 192 ? kmask_gemm_prefill<kDownBM, 192, USE>
-                            : kmask_gemm_prefill<kDownBM, 128, USE>;
-  k<<<grid, 256, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, rv.order, T, d, F, n,
+  auto k = best_bn == 256 ? kmask_gemm_prefill<kDownBM, 256, USE>
+                          : kmask_gemm_prefill<kDownBM, 128, USE>;
+  k<<<grid, kGemmThreads, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, rv.order, T, d, F, n,
                          G, nw, ntn, residual, Y);
 }
 
@@ -324,7 +323,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
     {
       WIDE_TRACE("ffn_up_prefill", s);
-      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
+      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
                                                                n, G, mtiles, ntn, H);
     }
   } else {
@@ -332,7 +331,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
     {
       WIDE_TRACE("ffn_up_prefill", s);
-      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, 256, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
+      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
                                                                n, G, mtiles, ntn, H);
     }
   }
