@@ -71,7 +71,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   for (int i = tid; i < BM; i += C::kThreads) sTok[i] = i < rows ? gperm[(size_t)g * T + row0 + i] : -1;
   __syncthreads();
 
-  const int chunk8 = dma_chunk(lane) * 8;
+  const int chunk8 = dma_chunk(dma_row(wave, 0, lane), lane) * 8;
   const int nq = n_kv * r;
   const i32x4 rX = make_srd(X, (uint32_t)T * d * 2u);
   const i32x4 rQ = make_srd(Wq, (uint32_t)nq * kHd * d * 2u);

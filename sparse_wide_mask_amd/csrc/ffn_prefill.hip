@@ -66,7 +66,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gperm[(size_t)g * T + row0 + r] : -1;
   __syncthreads();
 
-  const int chunk8 = dma_chunk(lane) * 8;
+  const int chunk8 = dma_chunk(dma_row(wave, 0, lane), lane) * 8;
   const i32x4 rX = make_srd(X, (uint32_t)T * d * 2u);
   const i32x4 rG = make_srd(Wg, (uint32_t)F * d * 2u);
   const i32x4 rU = make_srd(Wu, (uint32_t)F * d * 2u);
@@ -163,7 +163,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
   __syncthreads();
 
-  const int chunk8 = dma_chunk(lane) * 8;
+  const int chunk8 = dma_chunk(dma_row(wave, 0, lane), lane) * 8;
   const i32x4 rH = make_srd(H, (uint32_t)T * F * 2u);
   const i32x4 rW = make_srd(Wdp, (uint32_t)F * d * 2u);
   int aRow[C::A_INST];

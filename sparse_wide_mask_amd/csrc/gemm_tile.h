@@ -1,24 +1,25 @@
 // Block-tile bf16 MFMA engine shared by the prefill GEMMs.
 //
 // A work-group of 512 threads (8 waves, 4 x 2, two per SIMD) owns a BM x BN
-// output tile and walks K in slices of BK = 32; each wave holds a 64 x 128
-// accumulator.  Two waves per SIMD let one wave's LDS reads and waits overlap the
-// other's MFMAs (measured on a dense 8192 x 8192 x 4096 GEMM: 1.43 PFLOP/s
-// against 1.25-1.31 with 4 waves of 128 x 128).  Both operands are K-contiguous in global memory,
-// so every lane moves 16-byte chunks, and each wave feeds
-// v_mfma_f32_32x32x16_bf16 from LDS.
+// output tile and walks K in slices of BK = 64; each wave holds a 64 x 128
+// accumulator and issues v_mfma_f32_32x32x16_bf16.  Two waves per SIMD let one
+// wave's LDS reads and waits overlap the other's MFMAs.
 //
-// Global -> LDS uses buffer loads that write LDS directly (no VGPR staging), so
-// slices can be fetched STAGES-1 = 3 steps ahead of the MFMAs that consume them.
-// A lane whose buffer offset is past num_records reads zeros without touching
+// Global -> LDS uses buffer loads that write LDS directly (no VGPR staging).  Two
+// LDS stages: slice kt+1 loads while slice kt computes.  One load instruction of
+// a wave fills 8 rows of 128 bytes (a whole cache line per row); 16 rows of 64
+// bytes per instruction, as 32-wide slices give, is about 3x slower from L2.  A
+// lane whose buffer offset is past num_records reads zeros without touching
 // memory: that is how rows of tokens that dropped a group are skipped at the load
-// stage.  Before a stage is read, every wave waits for its own loads of that
-// stage (vmcnt; a wave's loads complete in issue order) and then meets the others
-// at a barrier.
+// stage.  Before a stage is read, every wave waits for its own loads (vmcnt) and
+// then meets the others at a barrier.
 //
-// LDS layout of a slice: rows of 32 bf16 (64 bytes = 4 chunks of 16 bytes);
-// chunk c of row r sits in slot c ^ swz(r), swz(r) = ((r >> 1) ^ (r >> 2)) & 3,
-// which keeps the 16-byte fragment reads of 32 consecutive rows free of bank
+// Measured on a dense 8192 x 8192 x 4096 GEMM: 1.60-1.65 PFLOP/s (4 waves of
+// 128 x 128 with 32-wide slices and 4 stages: 1.25-1.31).
+//
+// LDS layout of a slice: rows of 64 bf16 (128 bytes = 8 chunks of 16 bytes);
+// chunk c of row r sits in slot c ^ swz(r), swz(r) = (r mod 8) ^ ((r >> 3) mod 4),
+// which keeps the 16-byte fragment reads of consecutive rows free of bank
 // conflicts for both 32- and 64-bank LDS organisations.
 #pragma once
 
@@ -26,8 +27,8 @@
 
 namespace wide {
 
-constexpr int kBK = 32;
-constexpr int kStages = 4;
+constexpr int kBK = 64;
+constexpr int kStages = 2;
 constexpr uint32_t kSkip = 0x7fffff00u;  // buffer offset past any num_records: zeros
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
@@ -65,7 +66,8 @@ WIDE_DEV void lds_dma16(i32x4 srd, uint32_t lds, uint32_t byte_off) {
                : "s"(__builtin_amdgcn_readfirstlane(lds)), "v"(byte_off), "s"(srd)
                : "memory", "m0");
 }
-WIDE_DEV int swz(int row) { return ((row >> 1) ^ (row >> 2)) & 3; }
+// depends on row mod 32 only, so a fragment read can use its row inside a 32-row block
+WIDE_DEV int swz(int row) { return (row & 7) ^ ((row >> 3) & 3); }
 WIDE_DEV bf16x8 lds_frag(const uint16_t* p) { return *reinterpret_cast<const bf16x8*>(p); }
 
 // Wait until at most N of this wave's buffer loads are in flight (and its LDS
@@ -104,23 +106,24 @@ struct TileCfg {
   static constexpr int RB = WM / 32, CB = WN / 32; // 32x32 MFMA blocks per wave
   // buffer->LDS instructions per thread and slice: one instruction of a wave
   // fills 16 rows (1 KB); the 4 waves share the rows of the tile.
-  static constexpr int A_INST = BM / (16 * kWaves);
-  static constexpr int B_INST = BN / (16 * kWaves);
+  static constexpr int A_INST = BM / (8 * kWaves);
+  static constexpr int B_INST = BN / (8 * kWaves);
   static constexpr int LOADS = A_INST + B_INST;
   static constexpr int SA = BM * kBK;  // elements per stage
   static constexpr int SB = BN * kBK;
   static constexpr uint32_t kAllRows = (1u << RB) - 1u;
-  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % (16 * kWaves) == 0 && BN % (16 * kWaves) == 0, "tile shape");
+  static_assert(WM % 32 == 0 && WN % 32 == 0 && BM % (8 * kWaves) == 0 && BN % (8 * kWaves) == 0, "tile shape");
 };
 
 // Row of the tile filled by lane `lane` of wave `wave` in its instruction q, and
 // the logical 16-byte chunk that lane fetches for the swizzled layout.
 template <int NW = kGemmWM * kGemmWN>
-WIDE_DEV int dma_row(int wave, int q, int lane) { return 16 * (NW * q + wave) + (lane >> 2); }
-WIDE_DEV int dma_chunk(int lane) { return (lane & 3) ^ swz(lane >> 2); }
+WIDE_DEV int dma_row(int wave, int q, int lane) { return 8 * (NW * q + wave) + (lane >> 3); }
+// the logical chunk fetched by `lane` for tile row `row` (its slot is lane & 7)
+WIDE_DEV int dma_chunk(int row, int lane) { return (lane & 7) ^ swz(row); }
 template <int NW = kGemmWM * kGemmWN>
 WIDE_DEV uint32_t dma_dst(uint32_t stage_addr, int wave, int q) {
-  return stage_addr + 16 * (NW * q + wave) * kBK * 2;
+  return stage_addr + 8 * (NW * q + wave) * kBK * 2;
 }
 
 // Accumulators of one wave and its pipelined K loop.
@@ -166,43 +169,36 @@ struct WaveAcc {
     }
   }
 
-  // K slices 0..nk-1 with STAGES-1 slices of loads in flight.  sA/sB hold the
-  // STAGES slices back to back; issue(kt, stage) starts the loads of slice kt into
-  // that stage; live(kt) gives the live row blocks of slice kt.  The LDS reads of
-  // the next 16-wide step are issued before the MFMAs of the current one, across
-  // slice boundaries too: read(kt, hi); mma(kt, lo); barrier(kt+1);
-  // issue(kt+4); read(kt+1, lo); mma(kt, hi).  The barrier before slice kt+1 is
-  // read also guarantees every wave finished reading slice kt, whose stage the
-  // following issue refills.
+  // Two stages of 64-wide slices: slice kt+1 loads while slice kt computes.
   template <bool ALL, int LOADS, class Issue, class Live>
   WIDE_DEV void run(int nk, const uint16_t* sA, const uint16_t* sB, int wm, int wn, int lane,
                     Issue&& issue, Live&& live) {
     if (nk <= 0) return;
-#pragma unroll
-    for (int s = 0; s < kStages - 1; ++s)
-      if (s < nk) issue(s, s);
-    if (nk >= kStages - 1)
-      stage_barrier<(kStages - 2) * LOADS>();
-    else
-      stage_barrier<0>();
-    if (kStages - 1 < nk) issue(kStages - 1, kStages - 1);
+    issue(0, 0);
+    stage_barrier<0>();
     Frags lo, hi;
     read(lo, sA, sB, wm, wn, lane, 0);
     for (int kt = 0; kt < nk; ++kt) {
-      const int st = kt & (kStages - 1);
+      const int st = kt & 1;
       const uint32_t lv = ALL ? C::kAllRows : live(kt);
-      read(hi, sA + st * C::SA, sB + st * C::SB, wm, wn, lane, 1);
+      const uint16_t* cA = sA + st * C::SA;
+      const uint16_t* cB = sB + st * C::SB;
+      if (kt + 1 < nk) issue(kt + 1, st ^ 1);
+      read(hi, cA, cB, wm, wn, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(lo, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      read(lo, cA, cB, wm, wn, lane, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(hi, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      read(hi, cA, cB, wm, wn, lane, 3);
       __builtin_amdgcn_sched_barrier(0);
       mma<ALL>(lo, lv);
       __builtin_amdgcn_sched_barrier(0);
       if (kt + 1 < nk) {
-        if (kt + kStages - 1 < nk)
-          stage_barrier<(kStages - 2) * LOADS>();
-        else
-          stage_barrier<0>();
-        if (kt + kStages < nk) issue(kt + kStages, st);
-        const int nx = (st + 1) & (kStages - 1);
-        read(lo, sA + nx * C::SA, sB + nx * C::SB, wm, wn, lane, 0);
+        stage_barrier<0>();
+        read(lo, sA + (st ^ 1) * C::SA, sB + (st ^ 1) * C::SB, wm, wn, lane, 0);
       }
       __builtin_amdgcn_sched_barrier(0);
       mma<ALL>(hi, lv);
