@@ -3,15 +3,12 @@
 // the per-tile union of kept groups that block-level skipping reads (§2.C, l=0).
 //
 // Two launches, no host synchronisation:
-//   1. reorder_pack_tiles : one work-group per token tile; a wave reads a token's
-//                           mask row with its 64 lanes and a ballot gives each
-//                           64-bit packed word; the tile's words are ORed in LDS
-//                           and the union's set bits compacted into an ascending
-//                           group list.
-//   2. reorder_groups     : one work-group per group; each thread owns a run of
-//                           consecutive tokens, a wave shuffle scan plus one LDS
-//                           pass over the waves gives the kept tokens before each
-//                           run, and the thread places its tokens.
+//   1. reorder_pack   : one thread per token packs its mask row into 64-bit words.
+//   2. reorder_groups : one work-group per group (each thread owns a run of
+//                       consecutive tokens; a wave shuffle scan plus one LDS pass
+//                       over the waves gives the kept tokens before each run, and
+//                       the thread places its tokens), plus one work-group per
+//                       token tile for the tile's union of kept groups.
 #include "wide.h"
 #include "common.h"
 #include "gemm_tile.h"
@@ -19,95 +16,119 @@
 
 namespace wide {
 
-// One work-group per token tile; the waves take its tokens in turn and read a
-// mask row with 64 lanes (byte g = 64 w + lane), so a ballot yields packed word
-// w directly.  kPackUnroll tokens' bytes are loaded before any is used, so a
-// wave has up to 4 kPackUnroll loads in flight.  The tile's words are ORed in
-// LDS, then the union's set bits are compacted into an ascending group list.
-constexpr int kPackThreads = 1024;
-constexpr int kPackUnroll = 4;
+// One thread per token: it reads its mask row with 4-byte loads (all issued
+// before any is used) and packs the nonzero bytes into 64-bit words.
+constexpr int kPackThreads = 256;
 
-__global__ void __launch_bounds__(kPackThreads) reorder_pack_tiles(
-    const uint8_t* __restrict__ mask, int T, int n, int nw, int tile_m,
-    uint64_t* __restrict__ packed, int32_t* __restrict__ tile_count,
-    int32_t* __restrict__ tile_groups) {
-  __shared__ uint32_t sU[8];  // union words as 32-bit halves (nw <= 4)
-  const int tile = blockIdx.x;
-  const int lane = lane_id(), wave = threadIdx.x / kWave, nwaves = blockDim.x / kWave;
-  if (threadIdx.x < 8) sU[threadIdx.x] = 0u;
-  __syncthreads();
-  const int t0 = tile * tile_m, t1 = min(T, t0 + tile_m);
-  uint64_t uni[4] = {0, 0, 0, 0};
-  // byte loads through a buffer descriptor: an offset past the mask reads 0, so
-  // the loads carry no branches and are all issued before the ballots
-  const rsrc_t mr = make_rsrc(mask + (size_t)t0 * n, (uint32_t)((t1 - t0) * n));
-  for (int t = wave; t < t1 - t0; t += nwaves * kPackUnroll) {
-    uint32_t v[kPackUnroll][4];
+template <bool ALIGNED4>
+__global__ void __launch_bounds__(kPackThreads)
+    reorder_pack(const uint8_t* __restrict__ mask, int T, int n, int nw,
+                 uint64_t* __restrict__ packed) {
+  const int t = blockIdx.x * kPackThreads + threadIdx.x;
+  if (t >= T) return;
+  const rsrc_t mr = make_rsrc(mask, (uint32_t)((size_t)T * n));
+  const uint32_t row = (uint32_t)((size_t)t * n);
 #pragma unroll
-    for (int u = 0; u < kPackUnroll; ++u) {
-      const int tt = t + u * nwaves;
+  for (int w = 0; w < 4; ++w) {
+    if (w >= nw) break;
+    uint64_t word = 0;
+    if (ALIGNED4) {
+      uint32_t v[16];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const int g = 64 * w + lane;
-        v[u][w] = ldbuf1(mr, (tt < t1 - t0 && g < n) ? (uint32_t)(tt * n + g) : kSkip);
+      for (int u = 0; u < 16; ++u) {
+        const int b = 64 * w + 4 * u;
+        v[u] = b < n ? __builtin_amdgcn_raw_buffer_load_b32(mr, (int)(row + b), 0, 0) : 0u;
       }
+#pragma unroll
+      for (int u = 0; u < 16; ++u)
+#pragma unroll
+        for (int k = 0; k < 4; ++k)
+          word |= (uint64_t)(((v[u] >> (8 * k)) & 0xffu) != 0u) << (4 * u + k);
+    } else {
+      uint32_t v[64];
+#pragma unroll
+      for (int u = 0; u < 64; ++u) {
+        const int b = 64 * w + u;
+        v[u] = b < n ? ldbuf1(mr, row + b) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < 64; ++u) word |= (uint64_t)(v[u] != 0u) << u;
     }
-#pragma unroll
-    for (int u = 0; u < kPackUnroll; ++u) {
-      const int tt = t0 + t + u * nwaves;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        const uint64_t word = ballot(v[u][w] != 0u);
-        if (lane == 0 && tt < t1 && w < nw) packed[(size_t)tt * nw + w] = word;
-        uni[w] |= word;
-      }
-    }
-  }
-  if (tile_count) {
-    if (lane == 0)
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if ((uint32_t)uni[w]) atomicOr(&sU[2 * w], (uint32_t)uni[w]);
-        if ((uint32_t)(uni[w] >> 32)) atomicOr(&sU[2 * w + 1], (uint32_t)(uni[w] >> 32));
-      }
-    __syncthreads();
-    if (wave == 0) {
-      int32_t* out = tile_groups + (size_t)tile * n;
-      int written = 0;
-      for (int w = 0; w < nw; ++w) {
-        const uint64_t u = ((uint64_t)sU[2 * w + 1] << 32) | sU[2 * w];
-        const int g = 64 * w + lane;
-        if (g < n && ((u >> lane) & 1ull)) {
-          const uint64_t below = lane ? (u & ((1ull << lane) - 1ull)) : 0ull;
-          out[written + popc64(below)] = g;
-        }
-        written += popc64(u);
-      }
-      for (int p = written + lane; p < n; p += kWave) out[p] = -1;
-      if (lane == 0) tile_count[tile] = written;
-    }
+    packed[(size_t)t * nw + w] = word;
   }
 }
 
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / kWave;
 
-// One work-group per group.  Thread i owns the contiguous tokens
-// [i*per, (i+1)*per): it counts its kept tokens, one work-group exclusive scan
-// gives the number kept before its run, and it then places its tokens: kept
-// ones at (#kept before t), dropped ones at cnt + (#dropped before t).
+// Work-groups 0..n-1: one per group.  Thread i owns the contiguous tokens
+// [i*per, (i+1)*per), per <= 64: it loads their mask bits once into a register
+// bitmask, one work-group exclusive scan of the kept counts gives the number
+// kept before its run, and it places its tokens: kept ones at (#kept before t),
+// dropped ones at cnt + (#dropped before t).
+// Work-groups n..: one per token tile (when tile unions are asked for): the OR of
+// the tile's packed words, compacted into an ascending group list, -1 padded.
 __global__ void __launch_bounds__(kGroupThreads)
-    reorder_groups(const uint64_t* __restrict__ packed, int T, int n, int nw,
+    reorder_groups(const uint64_t* __restrict__ packed, int T, int n, int nw, int tile_m,
                    int32_t* __restrict__ group_count, int32_t* __restrict__ group_perm,
-                   int32_t* __restrict__ group_rank) {
+                   int32_t* __restrict__ group_rank, int32_t* __restrict__ tile_count,
+                   int32_t* __restrict__ tile_groups) {
   __shared__ int sWave[kGroupWaves];
+  __shared__ uint32_t sU[8];
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  if ((int)blockIdx.x >= n) {
+    const int tile = blockIdx.x - n;
+    if (threadIdx.x < 8) sU[threadIdx.x] = 0u;
+    __syncthreads();
+    const int t0 = tile * tile_m, t1 = min(T, t0 + tile_m);
+    uint64_t uni[4] = {0, 0, 0, 0};
+    for (int t = t0 + (int)threadIdx.x; t < t1; t += kGroupThreads) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w)
+        if (w < nw) uni[w] |= packed[(size_t)t * nw + w];
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      uint32_t lo = (uint32_t)uni[w], hi = (uint32_t)(uni[w] >> 32);
+      for (int off = 32; off >= 1; off >>= 1) lo |= __shfl_xor(lo, off), hi |= __shfl_xor(hi, off);
+      if (lane == 0 && w < nw) {
+        if (lo) atomicOr(&sU[2 * w], lo);
+        if (hi) atomicOr(&sU[2 * w + 1], hi);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {
+      int32_t* out = tile_groups + (size_t)tile * n;
+      int written = 0;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        if (w >= nw) break;
+        const uint64_t u = ((uint64_t)sU[2 * w + 1] << 32) | sU[2 * w];
+        const int g = 64 * w + lane;
+        if (g < n && ((u >> lane) & 1ull)) out[written + popc64(u & ((1ull << lane) - 1ull))] = g;
+        written += popc64(u);
+      }
+      for (int p = written + lane; p < n; p += kWave) out[p] = -1;
+      if (lane == 0) tile_count[tile] = written;
+    }
+    return;
+  }
   const int g = blockIdx.x;
   const int w = g >> 6, j = g & 63;
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
   const int per = (T + kGroupThreads - 1) / kGroupThreads;
-  const int t0 = min(T, threadIdx.x * per), t1 = min(T, t0 + per);
-  int mine = 0;
-  for (int t = t0; t < t1; ++t) mine += (int)((packed[(size_t)t * nw + w] >> j) & 1ull);
+  const int t0 = min(T, (int)threadIdx.x * per), t1 = min(T, t0 + per);
+  uint64_t bits = 0;
+  for (int c = 0; c < t1 - t0; c += 8) {
+    uint64_t v[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = t0 + c + u;
+      v[u] = t < t1 ? packed[(size_t)t * nw + w] : 0ull;
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) bits |= ((v[u] >> j) & 1ull) << (c + u);
+  }
+  const int mine = popc64(bits);
   // inclusive scan inside the wave, then across the 16 waves
   int incl = mine;
   for (int off = 1; off < kWave; off <<= 1) {
@@ -124,8 +145,9 @@ __global__ void __launch_bounds__(kGroupThreads)
   }
   int32_t* perm = group_perm + (size_t)g * T;
   int32_t* rank = group_rank ? group_rank + (size_t)g * T : nullptr;
-  for (int t = t0; t < t1; ++t) {
-    const bool bit = (packed[(size_t)t * nw + w] >> j) & 1ull;
+  for (int i = 0; i < t1 - t0; ++i) {
+    const int t = t0 + i;
+    const bool bit = (bits >> i) & 1ull;
     const int r = bit ? before : cnt + (t - before);
     before += bit;
     if (rank) rank[t] = r;
@@ -252,17 +274,20 @@ void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* pac
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
   const int nw = (n + 63) / 64;
-  const int n_tiles = (T + tile_m - 1) / tile_m;
-  const int threads = kWave * min(kPackThreads / kWave, min(tile_m, T));
+  const int n_tiles = tile_count ? (T + tile_m - 1) / tile_m : 0;
   {
-    WIDE_TRACE("reorder_pack_tiles", s);
-    reorder_pack_tiles<<<n_tiles, threads, 0, s>>>(mask, T, n, nw, tile_m, packed, tile_count,
-                                                   tile_groups);
+    WIDE_TRACE("reorder_pack", s);
+    const int grid = (T + kPackThreads - 1) / kPackThreads;
+    if (n % 4 == 0)
+      reorder_pack<true><<<grid, kPackThreads, 0, s>>>(mask, T, n, nw, packed);
+    else
+      reorder_pack<false><<<grid, kPackThreads, 0, s>>>(mask, T, n, nw, packed);
   }
   {
     WIDE_TRACE("reorder_groups", s);
-    reorder_groups<<<n, kGroupThreads, 0, s>>>(packed, T, n, nw, group_count, group_perm,
-                                                group_rank);
+    reorder_groups<<<n + n_tiles, kGroupThreads, 0, s>>>(packed, T, n, nw, tile_m, group_count,
+                                                          group_perm, group_rank, tile_count,
+                                                          tile_groups);
   }
 }
 
