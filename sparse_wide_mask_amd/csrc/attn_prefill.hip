@@ -15,8 +15,9 @@
 //                   Vt [n_kv][hd][vtp] (column i = i-th kept token of the group,
 //                   permuted inside 16-key groups; zero up to a whole group).
 // attn_core_prefill one work-group = (group, a heavy and a light tile of 64
-//                   compacted queries), one wave per query head; K and V^T blocks
-//                   arrive by buffer->LDS loads one key step ahead.  S^T = K Q^T puts a query in each lane's column,
+//                   compacted queries), two waves per query head (32 queries
+//                   each, so two waves share each SIMD); K and V^T blocks arrive
+//                   by buffer->LDS loads one key step ahead.  S^T = K Q^T puts a query in each lane's column,
 //                   so the online softmax is per lane (+ one cross-half swap) and
 //                   P stays in registers as the B operand of O^T = V^T P^T; V is
 //                   read in the key order the S^T accumulator layout gives.
@@ -186,15 +187,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
 
 // ---------------------------------------------------------- attention core
 
-constexpr int kBQ = 64;    // queries per tile (per wave: one head, 64 queries)
+constexpr int kBQ = 64;    // queries per tile: 2 waves x 32 per head
 constexpr int kBKey = 64;  // keys per step
+constexpr int kCoreWaves = 8;  // 4 heads x 2 query halves
 // One LDS stage: K block [64 keys][128 hd] (16-byte chunk c of key row k at slot
 // c ^ (k & 15)) and V^T block [128 hd][64 keys] (chunk c of row j at slot
 // c ^ ((j >> 1) & 7)); both 16 KB, filled by buffer->LDS loads.
 constexpr int kStageK = kBKey * kHd;  // elements
 constexpr int kStageV = kHd * kBKey;
 
-__global__ void __launch_bounds__(256, 1)
+__global__ void __launch_bounds__(64 * kCoreWaves, 1)
     attn_core_prefill(const uint16_t* __restrict__ Qc, const uint16_t* __restrict__ Kc,
                       const uint16_t* __restrict__ Vt, const int32_t* __restrict__ gcount,
                       const int32_t* __restrict__ gperm, int T, int n_kv, int r, int npairs,
@@ -213,20 +215,22 @@ __global__ void __launch_bounds__(256, 1)
   const int qtiles = (cnt + kBQ - 1) / kBQ;
   if (2 * p >= qtiles) return;  // l=0: past the group's kept tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool head_ok = hc * 4 + wave < r;  // waves past the group's heads only help load
-  const int h = g * r + min(hc * 4 + wave, r - 1);
+  // wave = (head of the chunk, half of the 64 queries): two waves per SIMD
+  const int hw = wave & 3, qh = wave >> 2;
+  const bool head_ok = hc * 4 + hw < r;  // waves past the group's heads only help load
+  const int h = g * r + min(hc * 4 + hw, r - 1);
   const int c0 = lane & 31, half = lane >> 5;
 
   const i32x4 kSrd = make_srd(Kc + (size_t)g * T * kHd, (uint32_t)((size_t)T * kHd * 2));
   const i32x4 vSrd = make_srd(Vt + (size_t)g * kHd * vtp, (uint32_t)((size_t)kHd * vtp * 2));
   const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
   // buffer->LDS loads of key block kb into stage st: instruction i of wave w fills
-  // K rows 4 (4 i + w) .. +3 and V^T rows 8 (4 i + w) .. +7 (1 KB each)
+  // K rows 4 (8 i + w) .. +3 and V^T rows 8 (8 i + w) .. +7 (1 KB each)
   auto issue = [&](int kb, int st) {
     const int k0 = kb * kBKey;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int n = 4 * i + wave;
+    for (int i = 0; i < 2; ++i) {
+      const int n = kCoreWaves * i + wave;
       const int krow = 4 * n + (lane >> 4), kslot = lane & 15;
       const int kchunk = kslot ^ (krow & 15);
       const uint32_t koff =
@@ -248,46 +252,39 @@ __global__ void __launch_bounds__(256, 1)
     const int q0 = qt * kBQ;
     const int q_last = min(cnt, q0 + kBQ) - 1;
     const int nkb = q_last / kBKey + 1;
+    const int q = q0 + 32 * qh + c0;  // this lane's query (its S^T column)
     lds_barrier();  // the previous tile's last stage reads are done
     issue(0, 0);
 
-    // Q^T fragments as B operands: lane holds query q0 + qb*32 + c0, hd 16 ks + 8 half.
-    bf16x8 qf[2][8];
+    // Q^T fragments as B operands: lane holds query q, hd 16 ks + 8 half.
+    bf16x8 qf[8];
     const uint16_t* qbase = Qc + (size_t)h * T * kHd;
 #pragma unroll
-    for (int qb = 0; qb < 2; ++qb) {
-      const int q = q0 + qb * 32 + c0;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
-        if (q < cnt)
-          qf[qb][ks] =
-              *reinterpret_cast<const bf16x8*>(qbase + (size_t)q * kHd + ks * 16 + half * 8);
-        else
-          qf[qb][ks] = bf16x8{};
-      }
+    for (int ks = 0; ks < 8; ++ks) {
+      if (q < cnt)
+        qf[ks] = *reinterpret_cast<const bf16x8*>(qbase + (size_t)q * kHd + ks * 16 + half * 8);
+      else
+        qf[ks] = bf16x8{};
     }
-    f32x16 o[4][2];  // O^T: 4 hd blocks x 2 query blocks
+    f32x16 o[4];  // O^T: 4 hd blocks x this wave's 32 queries
 #pragma unroll
     for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int b = 0; b < 2; ++b)
-#pragma unroll
-        for (int e = 0; e < 16; ++e) o[a][b][e] = 0.f;
-    float m_run[2] = {-INFINITY, -INFINITY}, l_run[2] = {0.f, 0.f};
+      for (int e = 0; e < 16; ++e) o[a][e] = 0.f;
+    float m_run = -INFINITY, l_run = 0.f;
 
     for (int kb = 0; kb < nkb; ++kb) {
       const int k0 = kb * kBKey, st = kb & 1;
-      // every wave's loads of block kb have landed (this wave's 8 loads of block
+      // every wave's loads of block kb have landed (this wave's 4 loads of block
       // kb + 1 may stay in flight)
       if (kb + 1 < nkb) {
         issue(kb + 1, st ^ 1);
-        stage_barrier<8>();
+        stage_barrier<4>();
       } else {
         stage_barrier<0>();
       }
       const uint16_t* cK = sK + st * kStageK;
       const uint16_t* cV = sV + st * kStageV;
-
       auto kfrag = [&](int ks, int a) {
         const int row = a * 32 + c0;
         return *reinterpret_cast<const bf16x8*>(cK + row * kHd +
@@ -302,22 +299,17 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
       for (int a = 0; a < 2; ++a) {
         const int kk0 = k0 + a * 32;
-        // S^T [32 keys x 64 queries] = K Q^T; the K fragment of step ks + 1 is read
-        // from LDS before the MFMAs of step ks
-        f32x16 s[2];
+        // S^T [32 keys x 32 queries] = K Q^T; the K fragment of step ks + 1 is read
+        // from LDS before the MFMA of step ks
+        f32x16 s;
 #pragma unroll
-        for (int b = 0; b < 2; ++b)
-#pragma unroll
-          for (int e = 0; e < 16; ++e) s[b][e] = 0.f;
+        for (int e = 0; e < 16; ++e) s[e] = 0.f;
         bf16x8 kc = kfrag(0, a);
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks) {
           bf16x8 kn;
           if (ks < 7) kn = kfrag(ks + 1, a);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int b = 0; b < 2; ++b) s[b] = mfma32(kc, qf[b][ks], s[b]);
-          __builtin_amdgcn_sched_barrier(0);
+          s = mfma32(kc, qf[ks], s);
           if (ks < 7) kc = kn;
         }
         // the V^T fragments of the first P V step, read while the softmax runs
@@ -330,45 +322,39 @@ __global__ void __launch_bounds__(256, 1)
         // max is raised only when a score exceeds it by more than 8 (2^8 headroom
         // for P in bf16 and the fp32 sums), so O and l are rescaled rarely; O / l
         // is the same for any common offset.
-        const bool masked = kk0 + 32 > q0 || kk0 + 32 > cnt;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const int q = q0 + b * 32 + c0;
-          if (masked) {
-#pragma unroll
-            for (int e = 0; e < 16; ++e) {
-              const int key = kk0 + acc32_row(lane, e);
-              if (key > q || key >= cnt) s[b][e] = -INFINITY;
-            }
-          }
-          float mx = -INFINITY;
-#pragma unroll
-          for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[b][e]);
-          mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-          const bool grow = mx > m_run[b] + 8.f;
-          if (ballot(grow)) {
-            const float m_set = grow ? mx : m_run[b];
-            const float corr =
-                m_set == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run[b] - m_set);
-            l_run[b] *= corr;
-            m_run[b] = m_set;
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-              for (int e = 0; e < 16; ++e) o[hb][b][e] *= corr;
-          }
-          // a query past the count has no finite score; keep its state finite
-          const float m_use = m_run[b] == -INFINITY ? 0.f : m_run[b];
-          float sum = 0.f;
+        if (kk0 + 32 > q0 || kk0 + 32 > cnt) {
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const float pe = __builtin_amdgcn_exp2f(fmaf(s[b][e], scale_log2, -m_use));
-            s[b][e] = pe;
-            sum += pe;
+            const int key = kk0 + acc32_row(lane, e);
+            if (key > q || key >= cnt) s[e] = -INFINITY;
           }
-          l_run[b] += sum + __shfl_xor(sum, 32);
         }
-        // O^T [128 x 64] += V^T [128 x 32 keys] P^T [32 keys x 64 q].  The k-slots
+        float mx = -INFINITY;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
+        const bool grow = mx > m_run + 8.f;
+        if (ballot(grow)) {
+          const float m_set = grow ? mx : m_run;
+          const float corr = m_set == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_set);
+          l_run *= corr;
+          m_run = m_set;
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb)
+#pragma unroll
+            for (int e = 0; e < 16; ++e) o[hb][e] *= corr;
+        }
+        // a query past the count has no finite score; keep its state finite
+        const float m_use = m_run == -INFINITY ? 0.f : m_run;
+        float sum = 0.f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -m_use));
+          s[e] = pe;
+          sum += pe;
+        }
+        l_run += sum + __shfl_xor(sum, 32);
+        // O^T [128 x 32] += V^T [128 x 32 keys] P^T [32 keys x 32 q].  The k-slots
         // of a lane are the keys its S^T registers hold, 16 s' + 4 half +
         // {0..3, 8..11}; the permuted V^T layout stores exactly those 8 keys as
         // chunk 2 (2 a + s') + half.
@@ -379,17 +365,11 @@ __global__ void __launch_bounds__(256, 1)
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) vn[hb] = vfrag(a, 1, hb);
           }
-          bf16x8 pf[2];
+          bf16x8 pf;
 #pragma unroll
-          for (int b = 0; b < 2; ++b)
+          for (int k = 0; k < 8; ++k) pf[k] = (__bf16)s[8 * sp + k];
 #pragma unroll
-            for (int k = 0; k < 8; ++k) pf[b][k] = (__bf16)s[b][8 * sp + k];
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int b = 0; b < 2; ++b) o[hb][b] = mfma32(vc[hb], pf[b], o[hb][b]);
-          __builtin_amdgcn_sched_barrier(0);
+          for (int hb = 0; hb < 4; ++hb) o[hb] = mfma32(vc[hb], pf, o[hb]);
           if (sp == 0) {
 #pragma unroll
             for (int hb = 0; hb < 4; ++hb) vc[hb] = vn[hb];
@@ -400,25 +380,20 @@ __global__ void __launch_bounds__(256, 1)
     }
 
     // O[token, h*hd + j] = O^T[j][q] / l
-    if (head_ok) {
+    if (head_ok && q < cnt) {
+      const int tok = gperm[(size_t)g * T + q];
+      const float inv = 1.f / l_run;
+      uint16_t* dst = O + (size_t)tok * (n_kv * r * kHd) + h * kHd;
 #pragma unroll
-      for (int b = 0; b < 2; ++b) {
-        const int q = q0 + b * 32 + c0;
-        if (q >= cnt) continue;
-        const int tok = gperm[(size_t)g * T + q];
-        const float inv = 1.f / l_run[b];
-        uint16_t* dst = O + (size_t)tok * (n_kv * r * kHd) + h * kHd;
+      for (int hb = 0; hb < 4; ++hb)
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-          for (int q4 = 0; q4 < 4; ++q4) {
-            const int j = hb * 32 + 8 * q4 + 4 * half;
-            const f32x16& a = o[hb][b];
-            const uint32_t lo = pack_bf2(a[4 * q4] * inv, a[4 * q4 + 1] * inv);
-            const uint32_t hi = pack_bf2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
-            *reinterpret_cast<u32x2*>(dst + j) = u32x2{lo, hi};
-          }
-      }
+        for (int q4 = 0; q4 < 4; ++q4) {
+          const int j = hb * 32 + 8 * q4 + 4 * half;
+          const f32x16& a = o[hb];
+          const uint32_t lo = pack_bf2(a[4 * q4] * inv, a[4 * q4 + 1] * inv);
+          const uint32_t hi = pack_bf2(a[4 * q4 + 2] * inv, a[4 * q4 + 3] * inv);
+          *reinterpret_cast<u32x2*>(dst + j) = u32x2{lo, hi};
+        }
     }
   }
 }
@@ -440,7 +415,7 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHd);
   {
     WIDE_TRACE("attn_core_prefill", s);
-    attn_core_prefill<<<npairs * n_kv * ((r + 3) / 4), 256, 0, s>>>(
+    attn_core_prefill<<<npairs * n_kv * ((r + 3) / 4), 64 * kCoreWaves, 0, s>>>(
         Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, npairs, vtp, scale_log2, O);
   }
 }
