@@ -35,6 +35,29 @@ constexpr int kHd = 128;
 
 // ------------------------------------------------------------- QKV projection
 
+// A RoPE frequency (radians per position) as revolutions per position, split so
+// that the angle of any position below 2^16 reduces exactly: hi keeps 8
+// significant bits (pos * hi is exact in fp32), lo the rest (its product is
+// small).  sin and cos of the reduced angle come from v_sin/v_cos, which take
+// revolutions.  Angle error ~1e-5 rad up to position 65535 (sincosf on the raw
+// fp32 angle costs ~170 instructions per call through its large-argument path).
+struct RopeFreq {
+  float hi, lo;
+  WIDE_DEV explicit RopeFreq(float inv) {
+    const double rev = (double)inv * 0.15915494309189535;  // 1 / (2 pi)
+    hi = __uint_as_float(__float_as_uint((float)rev) & 0xffff0000u);
+    lo = (float)(rev - (double)hi);
+  }
+  WIDE_DEV void sincos(int pos, float& sn, float& cs) const {
+    const float p = (float)pos;
+    float t = p * hi;
+    t = (t - floorf(t)) + p * lo;
+    t -= floorf(t);
+    sn = __builtin_amdgcn_sinf(t);
+    cs = __builtin_amdgcn_cosf(t);
+  }
+};
+
 __global__ void __launch_bounds__(kGemmThreads, 1)
     attn_qkv_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
                      const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
@@ -128,11 +151,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   const bool is_v = kv_tile && wn == 1;
   const bool rope = log2_theta > 0.f && !is_v;
   const int c0 = lane & 31;
-  float inv0 = 0.f, inv1 = 0.f;  // theta^(-2j/hd) for j = c0 and c0 + 32
-  if (rope) {
-    inv0 = exp2f(-(2.f * c0 / kHd) * log2_theta);
-    inv1 = exp2f(-(2.f * (c0 + 32) / kHd) * log2_theta);
-  }
+  // theta^(-2j/hd) for j = c0 and c0 + 32, in revolutions per position
+  const RopeFreq f0 = rope ? RopeFreq(exp2f(-(2.f * c0 / kHd) * log2_theta)) : RopeFreq(0.f);
+  const RopeFreq f1 =
+      rope ? RopeFreq(exp2f(-(2.f * (c0 + 32) / kHd) * log2_theta)) : RopeFreq(0.f);
   uint16_t* qdst = Qc + ((size_t)(g * r + 2 * nt + wn) * T) * kHd;
   uint16_t* kdst = Kc + (size_t)g * T * kHd;
   uint16_t* vdst = Vt + (size_t)g * kHd * vtp;
@@ -168,10 +190,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
       float v0 = acc.acc[i][0][e], v1 = acc.acc[i][1][e];
       float v2 = acc.acc[i][2][e], v3 = acc.acc[i][3][e];
       if (rope) {
-        const float pos = (float)sTok[row];
+        const int pos = sTok[row];
         float s0, co0, s1, co1;
-        sincosf(pos * inv0, &s0, &co0);
-        sincosf(pos * inv1, &s1, &co1);
+        f0.sincos(pos, s0, co0);
+        f1.sincos(pos, s1, co1);
         const float r0 = v0 * co0 - v2 * s0, r2 = v2 * co0 + v0 * s0;
         const float r1 = v1 * co1 - v3 * s1, r3 = v3 * co1 + v1 * s1;
         v0 = r0, v1 = r1, v2 = r2, v3 = r3;

@@ -29,7 +29,11 @@ WIDE_DEV uint32_t pack_bf2(float lo, float hi) {
   return (uint32_t)f2bf(lo) | ((uint32_t)f2bf(hi) << 16);
 }
 
-WIDE_DEV float silu(float x) { return x / (1.0f + __expf(-x)); }
+// silu(x) = x / (1 + e^-x), with the hardware exp2 and reciprocal (about 1 ulp
+// each; the result is rounded to bf16).  x -> -inf gives -0, x -> +inf gives x.
+WIDE_DEV float silu(float x) {
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(x * -1.4426950408889634f));
+}
 
 // 64-bit wave ballot and the number of set lanes below this lane.
 WIDE_DEV uint64_t ballot(bool p) { return __ballot(p); }

@@ -111,21 +111,31 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   else  // tail tile of the group: l=2 skips the row blocks with no kept token
     acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
 
-  // epilogue: H[token, gG + ch] = silu(gate) * up
+  // epilogue: H[token, gG + ch] = silu(gate) * up, 32-bit byte offsets into H
+  // (T F 2 < 2^31); rows past the count only exist in a group's last tile
+  const rsrc_t hr = make_rsrc(H, (uint32_t)((size_t)T * F * 2));
+  auto store = [&](bool full) {
 #pragma unroll
-  for (int i = 0; i < C::RB; ++i) {
-    if (!((rb_live >> i) & 1u)) continue;
+    for (int i = 0; i < C::RB; ++i) {
+      if (!((rb_live >> i) & 1u)) continue;
 #pragma unroll
-    for (int jp = 0; jp < C::CB / 2; ++jp) {
-      const f32x16 gt = acc.acc[i][2 * jp], up = acc.acc[i][2 * jp + 1];
-      const int ch = nt * BNH + wn * (C::WN / 2) + jp * 32 + (lane & 31);
+      for (int jp = 0; jp < C::CB / 2; ++jp) {
+        const f32x16 gt = acc.acc[i][2 * jp], up = acc.acc[i][2 * jp + 1];
+        const int col = g * G + nt * BNH + wn * (C::WN / 2) + jp * 32 + (lane & 31);
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
-        if (row < rows) H[(size_t)sTok[row] * F + g * G + ch] = f2bf(silu(gt[e]) * up[e]);
+        for (int e = 0; e < 16; ++e) {
+          const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
+          const uint32_t off =
+              full || row < rows ? (uint32_t)(sTok[row] * F + col) * 2u : kSkip;
+          __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(gt[e]) * up[e]), hr, (int)off, 0, 0);
+        }
       }
     }
-  }
+  };
+  if (rows == BM)
+    store(true);
+  else
+    store(false);
 }
 
 template <int BM, int BN, int USE>
