@@ -76,6 +76,7 @@ int ffn_check(int T, int d, int F, int n, int mode) {
 struct FfnWs {
   ReorderView rv;
   uint16_t* H = nullptr;
+  float* kpart = nullptr;  // streaming decode: K-split partial sums
 };
 
 // Decode kernels take batches up to kMaxDecodeBatch; a larger "decode" batch runs
@@ -83,11 +84,13 @@ struct FfnWs {
 bool ffn_streaming(int T, int mode) { return mode == WIDE_DECODE && T <= kMaxDecodeBatch; }
 
 FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
-  (void)d;
   FfnWs w;
   // streaming decode reorders inside its kernels
   if (!ffn_streaming(T, mode)) w.rv = carve_reorder(c, T, n, ffn_down_tile_m(), false);
   w.H = c.take<uint16_t>((size_t)T * F);
+  if (ffn_streaming(T, mode)) {
+    w.kpart = c.take<float>(kmask_decode_part_floats(T, d, n, F / n));
+  }
   return w;
 }
 
@@ -95,7 +98,7 @@ int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const ui
             const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
             uint16_t* Y, const FfnWs& w, hipStream_t s) {
   if (ffn_streaming(T, mode)) {
-    launch_ffn_decode(X, mask, Wg, Wu, Wdp, T, d, F, n, residual, w.H, Y, s);
+    launch_ffn_decode(X, mask, Wg, Wu, Wdp, T, d, F, n, residual, w.H, w.kpart, Y, s);
   } else {
     run_reorder(mask, T, n, w.rv, s);
     launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
@@ -134,10 +137,10 @@ struct AttnWs {
   ReorderView rv;
   uint16_t *Qc = nullptr, *Kc = nullptr, *Vt = nullptr, *O = nullptr;
   float *Opart = nullptr, *Mpart = nullptr, *Lpart = nullptr;
+  float* kpart = nullptr;  // decode O projection: K-split partial sums
 };
 
 AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, int kv_cap) {
-  (void)d;
   AttnWs w;
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads;
   if (mode == WIDE_DECODE) {
@@ -147,6 +150,7 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
     w.Opart = c.take<float>((size_t)T * nq * nch * kHeadDim);
     w.Mpart = c.take<float>((size_t)T * nq * nch);
     w.Lpart = c.take<float>((size_t)T * nq * nch);
+    w.kpart = c.take<float>(kmask_decode_part_floats(T, d, nkv, nq * kHeadDim / nkv));
     return w;
   }
   w.rv = carve_reorder(c, T, nkv, ffn_down_tile_m(), false);
@@ -166,7 +170,8 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
                        kv_cap, w.Qc, w.Opart, w.Mpart, w.Lpart, w.O, s);
-    launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, Y, s);
+    launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, w.kpart,
+                        Y, s);
     return;
   }
   // group partitions for the QKV projection and the core; for the O projection

@@ -392,27 +392,56 @@ __global__ void __launch_bounds__(256)
   }
 }
 
-// K-masked decode projection: Y[b, n] = sum over union groups g of
-// sum_j A[b, gG + j] Wp[g, n, j] over the tokens b that keep g (+ residual).
-constexpr int kKmWaves = 8;
+// K-masked decode projection: Y[b, c] = sum over union groups g of
+// sum_j A[b, gG + j] Wp[g, c, j] over the tokens b that keep g (+ residual).
+//
+// One work-group = (128 output columns, one of S stretches of the union's K
+// units).  A unit is (union group, UK-wide K block).  Per unit the work-group
+// copies the batch's A rows of the unit (rows of tokens that dropped the group
+// are not fetched, l=1) into LDS once, and each wave multiplies them by the
+// weight rows of its 16 columns; weights and A rows are loaded two units ahead.
+// Splitting K over work-groups is what keeps the A traffic low: every
+// work-group reads only its stretch of A, so A crosses L2 d / 128 times in all
+// rather than d / 16 times.  With S > 1 each work-group writes fp32 partial
+// sums, and kmask_decode_reduce (the next launch) adds them and the residual.
+// A device-scope handshake inside the kernel would need a release fence per
+// work-group, which on this chip writes back the XCD's L2: the kernel boundary
+// is the cheaper synchronisation.
+constexpr int kKmWaves = 8;             // one 16-column MFMA tile per wave
+constexpr int kKmCols = 16 * kKmWaves;  // output columns per work-group
+constexpr int kKmThreads = 64 * kKmWaves;
 
-template <int NRB, int USE>
-__global__ void __launch_bounds__(64 * kKmWaves)
+int kmask_decode_col_blocks(int d) { return (d + kKmCols - 1) / kKmCols; }
+
+// K splits: enough work-groups to fill the 256 CUs, at most 16 partial sums, and
+// no more splits than the largest possible union has units.
+int kmask_decode_splits(int d, int n, int G) {
+  const int units = n * (G % 128 == 0 ? G / 128 : G / 64);
+  const int ncb = kmask_decode_col_blocks(d);
+  int s = (256 + ncb - 1) / ncb;
+  s = s < 16 ? s : 16;
+  s = s < units ? s : units;
+  return s > 1 ? s : 1;
+}
+
+template <int NRB, int KS, int USE>
+__global__ void __launch_bounds__(kKmThreads)
     kmask_decode(const uint16_t* __restrict__ A, const uint16_t* __restrict__ Wp,
-                 const uint8_t* __restrict__ mask, int B, int d, int F, int G, int n,
-                 const uint16_t* __restrict__ residual, uint16_t* __restrict__ Y) {
+                 const uint8_t* __restrict__ mask, int B, int d, int F, int G, int n, int S,
+                 const uint16_t* __restrict__ residual, float* __restrict__ part,
+                 uint16_t* __restrict__ Y) {
+  constexpr int UK = 32 * KS;   // K width of a unit
+  constexpr int CPR = UK / 8;   // 16-byte chunks per A row of a unit
+  constexpr int ROWS = 16 * NRB;
+  constexpr int ACH = ROWS * CPR;  // chunks of a unit's A tile
+  constexpr int AP = (ACH + kKmThreads - 1) / kKmThreads;
   __shared__ uint64_t sBits[kDecRows * 4];
   __shared__ uint32_t sU[8];
   __shared__ int sGroups[256];
   __shared__ int sNu;
-  // per-wave A staging (NRB = 2), later reused for the cross-wave sums
-  constexpr int kStageBytes = NRB == 2 ? kKmWaves * 16 * NRB * 256 : 0;
-  constexpr int kRedBytes = (kKmWaves - 1) * kDecRows * 16 * 4;
-  __shared__ __attribute__((aligned(16))) uint8_t
-      sStage[kStageBytes > kRedBytes ? kStageBytes : kRedBytes];
-  auto sRed = reinterpret_cast<float (*)[kDecRows][16]>(sStage);
+  __shared__ __attribute__((aligned(16))) uint16_t sA[2][ROWS * UK];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int n0 = blockIdx.x * 16;
+  const int cb = blockIdx.x / S, sp = blockIdx.x - cb * S;
   if (tid < 8) sU[tid] = 0u;
   __syncthreads();
   // pack the batch's mask rows into bit words (ballot over 64 groups) and OR
@@ -460,151 +489,135 @@ __global__ void __launch_bounds__(64 * kKmWaves)
     if (lane == 0) sNu = written;
   }
   __syncthreads();
-  const int nu = sNu;
-  const int nrb = (B + 15) / 16;
+
+  // this work-group's stretch of units; the work-groups of one stretch start at
+  // different units so that they do not read the same A lines at once
+  const int UPG = G / UK, NU = sNu * UPG;
+  const int u0 = sp * NU / S, UW = (sp + 1) * NU / S - u0;
+  const int rot = UW > 0 ? (int)((unsigned)cb % (unsigned)UW) : 0;
   const int ch = lane & 15, koff = 8 * (lane >> 4);
+  const int col = cb * kKmCols + wave * 16 + ch;
+  const rsrc_t ar = make_rsrc(A, (uint32_t)((size_t)B * F * 2));
+  const rsrc_t wr = make_rsrc(Wp, (uint32_t)((size_t)n * d * G * 2));
+  // unit j (j >= UW: padding, every load takes the kSkip offset)
+  auto load = [&](int j, bf16x8 (&wf)[KS], u32x4 (&av)[AP]) {
+    const bool live = j < UW;
+    int u = j + rot;
+    u = u0 + (u >= UW ? u - UW : u);
+    const int q = live ? u / UPG : 0, k0 = live ? (u - q * UPG) * UK : 0;
+    const int g = live ? sGroups[q] : 0;
+    const uint32_t wo = (uint32_t)((((size_t)g * d + col) * G + k0 + koff) * 2);
+    const bool wl = live && col < d;
+#pragma unroll
+    for (int t = 0; t < KS; ++t) {
+      const u32x4 v = ldbuf16(wr, wl ? wo + 64u * t : kSkip);
+      wf[t] = *reinterpret_cast<const bf16x8*>(&v);
+    }
+#pragma unroll
+    for (int k = 0; k < AP; ++k) {
+      const int c = tid + k * kKmThreads, b = c / CPR, cc = c % CPR;
+      const uint32_t kb =
+          (uint32_t)(sBits[(b & (kDecRows - 1)) * 4 + (g >> 6)] >> (g & 63)) & (uint32_t)live;
+      av[k] = ldbuf16(ar, (kb && c < ACH)
+                              ? (uint32_t)(((size_t)b * F + (size_t)g * G + k0 + cc * 8) * 2)
+                              : kSkip);
+    }
+  };
   f32x4 acc[NRB];
 #pragma unroll
   for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  // the union's (group, 32-wide K step) pairs, split evenly over the waves
-  const int SG = G / 32, S = nu * SG;
-  const int sbeg = wave * S / kKmWaves, send = (wave + 1) * S / kKmWaves;
-  const rsrc_t ar = make_rsrc(A, (uint32_t)((size_t)B * F * 2));
-  // operands of step s: W row n0 + ch of group g, and the A rows of tokens that
-  // keep g (kSkip offset, so zeros, for the others: l=1)
-  auto operands = [&](int s, bf16x8& wf, bf16x8 (&af)[NRB]) {
-    const int q = s / SG, j0 = (s - q * SG) * 32;
-    const int g = sGroups[q];
-    wf = *reinterpret_cast<const bf16x8*>(Wp + ((size_t)g * d + n0 + ch) * G + j0 + koff);
+  // unit j: its A rows (ac) into LDS buffer j & 1, the loads of unit j + 2 into
+  // the free register set, then the MFMAs of unit j.  Row b's chunk c sits at
+  // slot c ^ (b mod CPR), so the 16 rows of a fragment read spread over the banks.
+  auto step = [&](int j, const bf16x8 (&wc)[KS], const u32x4 (&ac)[AP], bf16x8 (&wn)[KS],
+                  u32x4 (&an)[AP]) {
+    uint16_t* st = sA[j & 1];
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      const int b = rb * 16 + ch;
-      const bool keep = (sBits[b * 4 + (g >> 6)] >> (g & 63)) & 1ull;
-      af[rb] = xload(ar, keep ? (uint32_t)(((size_t)b * F + (size_t)g * G + j0 + koff) * 2) : kSkip);
+    for (int k = 0; k < AP; ++k) {
+      const int c = tid + k * kKmThreads, b = c / CPR, cc = c % CPR;
+      if (ACH % kKmThreads == 0 || c < ACH)
+        *reinterpret_cast<u32x4*>(st + (b * CPR + (cc ^ (b % CPR))) * 8) = ac[k];
     }
-  };
-  if (NRB == 2 && G % 128 == 0) {
-    // Two row blocks: the A reads are as large as the weight stream, and 16-row
-    // fragment loads (64 B per row per instruction) are slow from L2.  The unit
-    // of work is (union group, 128-wide K block): its A rows (256 B each) are
-    // copied with contiguous loads into the wave's LDS area (16-byte chunk c of
-    // row b at slot c ^ (b mod 16)); the next unit's rows and weights load while
-    // this one's MFMAs run.
-    constexpr int CPR = 16, RPI = 4, NI = 16 * NRB / RPI;
-    uint16_t* myA = reinterpret_cast<uint16_t*>(sStage) + wave * (16 * NRB * CPR * 8);
-    const int lrow = lane / CPR, lch = lane % CPR;
-    const int UPG = G / 128, NU = nu * UPG;
-    const int ubeg = wave * NU / kKmWaves, uend = (wave + 1) * NU / kKmWaves;
-    const int UW = uend - ubeg;
-    const int rot = UW > 0 ? (int)((blockIdx.x * 7u) % (unsigned)UW) : 0;
-    auto unit_load = [&](int j, bf16x8 (&wf)[4], u32x4 (&av)[NI]) {
-      int un = j + rot;
-      un = ubeg + (un >= UW ? un - UW : un);
-      const int q = un / UPG, k0 = (un - q * UPG) * 128;
-      const int g = sGroups[q];
+    __syncthreads();
+    load(j + 2, wn, an);
 #pragma unroll
-      for (int t = 0; t < 4; ++t)
-        wf[t] = *reinterpret_cast<const bf16x8*>(Wp + ((size_t)g * d + n0 + ch) * G + k0 + 32 * t +
-                                                 koff);
+    for (int t = 0; t < KS; ++t)
 #pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int b = i * RPI + lrow;
-        const bool keep = (sBits[b * 4 + (g >> 6)] >> (g & 63)) & 1ull;
-        av[i] = ldbuf16(ar, keep ? (uint32_t)(((size_t)b * F + (size_t)g * G + k0 + lch * 8) * 2)
-                                 : kSkip);
+      for (int rb = 0; rb < NRB; ++rb) {
+        const int row = rb * 16 + ch, c = 4 * t + (lane >> 4);
+        const bf16x8 af = *reinterpret_cast<const bf16x8*>(st + (row * CPR + (c ^ (row % CPR))) * 8);
+        acc[rb] = mfma16(af, wc[t], acc[rb]);
       }
-    };
-    bf16x8 wc[4];
-    u32x4 av[NI];
-    if (UW > 0) unit_load(0, wc, av);
+  };
+  if (UW > 0) {
+    bf16x8 w0[KS], w1[KS], w2[KS];
+    u32x4 a0[AP], a1[AP], a2[AP];
+    load(0, w0, a0);
+    load(1, w1, a1);
 #pragma unroll 1
-    for (int j = 0; j < UW; ++j) {
-#pragma unroll
-      for (int i = 0; i < NI; ++i) {
-        const int b = i * RPI + lrow;
-        *reinterpret_cast<u32x4*>(myA + (b * CPR + (lch ^ (b % CPR))) * 8) = av[i];
-      }
-      __builtin_amdgcn_wave_barrier();
-      bf16x8 wn[4];
-      if (j + 1 < UW) unit_load(j + 1, wn, av);
-#pragma unroll
-      for (int t = 0; t < 4; ++t)
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-          if (rb >= nrb) continue;
-          const int row = rb * 16 + ch, c = 4 * t + (lane >> 4);
-          const bf16x8 af =
-              *reinterpret_cast<const bf16x8*>(myA + (row * CPR + (c ^ (row % CPR))) * 8);
-          acc[rb] = mfma16(af, wc[t], acc[rb]);
-        }
-      __builtin_amdgcn_wave_barrier();  // fragment reads before the next unit's writes
-      if (j + 1 < UW) {
-#pragma unroll
-        for (int t = 0; t < 4; ++t) wc[t] = wn[t];
-      }
+    for (int j = 0; j < UW; j += 3) {
+      step(j, w0, a0, w2, a2);
+      step(j + 1, w1, a1, w0, a0);
+      step(j + 2, w2, a2, w1, a1);
     }
-  } else {
-  // every work-group reads the same A rows: rotate the start of the step walk
-  const int SW = send - sbeg;
-  const int rot = SW > 0 ? (int)((blockIdx.x * 7u) % (unsigned)SW) : 0;
-  auto sat = [&](int j) {
-    const int s = j + rot;
-    return sbeg + (s >= SW ? s - SW : s);
-  };
-  constexpr int U = dec_unroll<NRB>() < 8 ? dec_unroll<NRB>() : 8;
-  int s0 = 0;
-  for (; s0 + U <= SW; s0 += U) {
-    bf16x8 wf[U], af[U][NRB];
-#pragma unroll
-    for (int u = 0; u < U; ++u) operands(sat(s0 + u), wf[u], af[u]);
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int u = 0; u < U; ++u)
-#pragma unroll
-      for (int rb = 0; rb < NRB; ++rb)
-        if (rb < nrb) acc[rb] = mfma16(af[u][rb], wf[u], acc[rb]);
   }
-  for (; s0 < SW; ++s0) {
-    bf16x8 wf, af[NRB];
-    operands(sat(s0), wf, af);
+
+  const uint16_t* res = residual;
+  if (S == 1) {
 #pragma unroll
     for (int rb = 0; rb < NRB; ++rb)
-      if (rb < nrb) acc[rb] = mfma16(af[rb], wf, acc[rb]);
-  }
-  }
-  __syncthreads();  // every wave is done with its LDS staging area (sRed aliases it)
-  if (wave > 0) {
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      if (rb >= nrb) break;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) sRed[wave - 1][rb * 16 + acc16_row(lane, i)][ch] = acc[rb][i];
-    }
+      for (int i = 0; i < 4; ++i) {
+        const int b = rb * 16 + acc16_row(lane, i);
+        if (b >= B || col >= d) continue;
+        const size_t o = (size_t)b * d + col;
+        float v = acc[rb][i];
+        if (res) v += bf2f(res[o]);
+        Y[o] = f2bf(v);
+      }
+    return;
   }
-  __syncthreads();
-  if (wave > 0) return;
+  float* mine = part + (size_t)sp * B * d;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    if (rb >= nrb) break;
+  for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int b = rb * 16 + acc16_row(lane, i);
-      if (b >= B) continue;
-      float v = acc[rb][i];
-#pragma unroll
-      for (int w = 0; w < kKmWaves - 1; ++w) v += sRed[w][b][ch];
-      const size_t o = (size_t)b * d + n0 + ch;
-      if (residual) v += bf2f(residual[o]);
-      Y[o] = f2bf(v);
+      if (b < B && col < d) mine[(size_t)b * d + col] = acc[rb][i];
     }
-  }
 }
 
-constexpr int kKeyChunk = 256;
-constexpr int kKeyBlocks = kKeyChunk / 16 / 4;  // 16-key MFMA blocks per wave
+// Y[b, c] = sum over the S partial sums (+ residual); 4 columns per thread.
+__global__ void __launch_bounds__(256)
+    kmask_decode_reduce(const float* __restrict__ part, int S, int B, int d,
+                        const uint16_t* __restrict__ residual, uint16_t* __restrict__ Y) {
+  const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
+  if (i >= B * d) return;
+  const size_t plane = (size_t)B * d;
+  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
+  for (int s2 = 1; s2 < S; ++s2) {
+    const f32x4 w = *reinterpret_cast<const f32x4*>(part + s2 * plane + i);
+    v[0] += w[0], v[1] += w[1], v[2] += w[2], v[3] += w[3];
+  }
+  if (residual) {
+    const u32x2 r = *reinterpret_cast<const u32x2*>(residual + i);
+    v[0] += __uint_as_float(r[0] << 16), v[1] += __uint_as_float(r[0] & 0xffff0000u);
+    v[2] += __uint_as_float(r[1] << 16), v[3] += __uint_as_float(r[1] & 0xffff0000u);
+  }
+  const uint32_t lo = (uint32_t)f2bf(v[0]) | ((uint32_t)f2bf(v[1]) << 16);
+  const uint32_t hi = (uint32_t)f2bf(v[2]) | ((uint32_t)f2bf(v[3]) << 16);
+  *reinterpret_cast<u32x2*>(Y + i) = u32x2{lo, hi};
+}
 
-// One work-group = (token b, group g, chunk of 256 cache keys).  All of the
+// One thread per cache key of a chunk; a chunk's V rows take kKeyChunk * 256 B of
+// LDS, so 128-key work-groups (32 KB) let four of them share a compute unit and
+// overlap one another's loads and arithmetic.
+constexpr int kKeyChunk = 128;
+constexpr int kAttnWaves = kKeyChunk / 64;
+constexpr int kKeyBlocks = kKeyChunk / 16 / kAttnWaves;  // 16-key MFMA blocks per wave
+constexpr int kKeySlices = kKeyChunk / 32;                // 32-key slices of the P V step
+
+// One work-group = (token b, group g, chunk of kKeyChunk cache keys).  All of the
 // chunk's bytes are requested up front: the K rows into registers as MFMA
 // operands, the V rows straight into LDS by buffer->LDS loads, which land while
 // the scores are computed.
@@ -613,9 +626,9 @@ constexpr int kKeyBlocks = kKeyChunk / 16 / 4;  // 16-key MFMA blocks per wave
 //           block, 4 blocks per wave;
 //   softmax per-head max and sum over the chunk (thread t = key t);
 //   P V     thread = (4 head dims, 32 keys) for all r heads, then a sum over
-//           the 8 key slices through LDS.
+//           the key slices through LDS.
 // Writes unnormalised partial outputs and the chunk's (max, sum) per head.
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(kKeyChunk)
     attn_decode_partial(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
                         const uint16_t* __restrict__ Vc, const uint8_t* __restrict__ mask, int B,
                         int n_kv, int r, int kv_len, int kv_cap, int nch, float scale_log2,
@@ -624,7 +637,7 @@ __global__ void __launch_bounds__(256)
   // V rows (row-major, 256 B each); reused for the key-slice partial sums
   __shared__ __attribute__((aligned(16))) uint16_t sV[kKeyChunk * kHdD];
   __shared__ __attribute__((aligned(16))) float sP[8][kKeyChunk];
-  __shared__ float sRed[8][4];
+  __shared__ float sRed[8][kAttnWaves];
   const int c = blockIdx.x % nch, rest = blockIdx.x / nch;
   const int g = rest % n_kv, b = rest / n_kv;
   if (!mask[(size_t)b * n_kv + g]) return;  // l=0: the token dropped this group
@@ -647,17 +660,17 @@ __global__ void __launch_bounds__(256)
       kf[i][ks] =
           xload(kr, key < nkeys ? (uint32_t)(((kvbase + key) * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
   }
-  // V: instruction q of wave w fills rows 16 q + 4 w .. +3 (1 KB); rows past the
-  // chunk's keys read as zeros
+  // V: instruction q of wave w fills the 4 rows from 4 (kAttnWaves q + w) (1 KB);
+  // rows past the chunk's keys read as zeros
   {
     const i32x4 vsrd = make_srd(Vc, cache_bytes);
     const uint32_t vlds = lds_addr(sV);
 #pragma unroll
-    for (int q = 0; q < kKeyChunk / 16; ++q) {
-      const int row = 16 * q + 4 * wave + q4;
+    for (int q = 0; q < kKeyChunk / (4 * kAttnWaves); ++q) {
+      const int row0 = 4 * (kAttnWaves * q + wave), row = row0 + q4;
       const uint32_t off =
           row < nkeys ? (uint32_t)(((kvbase + row) * kHdD + m16 * 8) * 2) : kSkip;
-      lds_dma16(vsrd, vlds + (16 * q + 4 * wave) * kHdD * 2, off);
+      lds_dma16(vsrd, vlds + row0 * kHdD * 2, off);
     }
   }
   // Q operand: column m16 = head of the group (zero past r)
@@ -695,7 +708,10 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     if (h >= r) break;
-    mh[h] = fmaxf(fmaxf(sRed[h][0], sRed[h][1]), fmaxf(sRed[h][2], sRed[h][3]));
+    float m = sRed[h][0];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) m = fmaxf(m, sRed[h][w]);
+    mh[h] = m;
   }
   __syncthreads();
 #pragma unroll
@@ -713,7 +729,10 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     if (h >= r) break;
-    lh[h] = sRed[h][0] + sRed[h][1] + sRed[h][2] + sRed[h][3];
+    float l = sRed[h][0];
+#pragma unroll
+    for (int w = 1; w < kAttnWaves; ++w) l += sRed[h][w];
+    lh[h] = l;
   }
   // P V: thread = (dims 4 j4 .. +3, keys 32 ks .. +31); P is zero and V rows are
   // zero past nkeys
@@ -746,7 +765,7 @@ __global__ void __launch_bounds__(256)
     }
   }
   __syncthreads();  // every thread is done with sV
-  float* sO = reinterpret_cast<float*>(sV);  // [8 slices][r][128]
+  float* sO = reinterpret_cast<float*>(sV);  // [kKeySlices][r][128]
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     if (h >= r) break;
@@ -755,11 +774,11 @@ __global__ void __launch_bounds__(256)
   }
   __syncthreads();
   const size_t obase = ((size_t)b * nq + g * r) * nch;
-  for (int x = tid; x < r * kHdD; x += 256) {
+  for (int x = tid; x < r * kHdD; x += kKeyChunk) {
     const int h = x / kHdD, j = x % kHdD;
     float a = 0.f;
 #pragma unroll
-    for (int sl = 0; sl < 8; ++sl) a += sO[(sl * r + h) * kHdD + j];
+    for (int sl = 0; sl < kKeySlices; ++sl) a += sO[(sl * r + h) * kHdD + j];
     Opart[(obase + (size_t)h * nch + c) * kHdD + j] = a;
   }
   if (tid < r) {
@@ -769,43 +788,59 @@ __global__ void __launch_bounds__(256)
 }
 
 // (token b, query head h): O[b, h] = sum_c 2^(M_c - M) Opart_c / sum_c 2^(M_c - M) L_c,
-// M = max_c M_c.  Chunk weights are computed 128 at a time into LDS; the Opart
-// loads of a block of chunks are independent, so they overlap.
-__global__ void __launch_bounds__(128)
+// M = max_c M_c.  Thread = (head dim, chunk slice): the chunks are dealt to
+// kCmbSlices slices so that each thread has few Opart loads to wait for, and the
+// slices are added through LDS at the end.  Chunk weights are computed
+// kCmbBlock at a time into LDS.
+constexpr int kCmbSlices = 4;
+constexpr int kCmbThreads = kHdD * kCmbSlices;
+constexpr int kCmbWaves = kCmbThreads / 64;
+constexpr int kCmbBlock = kCmbThreads;
+
+__global__ void __launch_bounds__(kCmbThreads)
     attn_decode_combine(const float* __restrict__ Opart, const float* __restrict__ Mpart,
                         const float* __restrict__ Lpart, const uint8_t* __restrict__ mask,
                         int n_kv, int r, int nch, uint16_t* __restrict__ O) {
-  __shared__ float sW[128];
-  __shared__ float sM[2];
+  __shared__ float sW[kCmbBlock];
+  __shared__ float sR[kCmbWaves];
+  __shared__ float sO[kCmbSlices - 1][kHdD];
   const int nq = n_kv * r;
   const int b = blockIdx.x / nq, h = blockIdx.x % nq, g = h / r;
   if (!mask[(size_t)b * n_kv + g]) return;  // never read: the O projection skips it
   const size_t base = (size_t)b * nq * nch + (size_t)h * nch;
-  const int j = threadIdx.x, lane = j & 63, wave = j >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int j = tid % kHdD, sl = tid / kHdD;
   float m = -INFINITY;
-  for (int c = j; c < nch; c += 128) m = fmaxf(m, Mpart[base + c]);
+  for (int c = tid; c < nch; c += kCmbThreads) m = fmaxf(m, Mpart[base + c]);
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-  if (lane == 0) sM[wave] = m;
+  if (lane == 0) sR[wave] = m;
   __syncthreads();
-  m = fmaxf(sM[0], sM[1]);
+  m = sR[0];
+#pragma unroll
+  for (int w = 1; w < kCmbWaves; ++w) m = fmaxf(m, sR[w]);
   float l = 0.f, acc = 0.f;
-  for (int c0 = 0; c0 < nch; c0 += 128) {
-    const int cn = min(128, nch - c0);
-    __syncthreads();
+  for (int c0 = 0; c0 < nch; c0 += kCmbBlock) {
+    const int cn = min(kCmbBlock, nch - c0);
+    __syncthreads();  // the previous block's reads of sW and sR are done
     float lw = 0.f;
-    if (j < cn) {
-      const float w = exp2f(Mpart[base + c0 + j] - m);
-      sW[j] = w;
-      lw = w * Lpart[base + c0 + j];
+    if (tid < cn) {
+      const float w = exp2f(Mpart[base + c0 + tid] - m);
+      sW[tid] = w;
+      lw = w * Lpart[base + c0 + tid];
     }
     for (int off = 32; off >= 1; off >>= 1) lw += __shfl_xor(lw, off);
+    if (lane == 0) sR[wave] = lw;
     __syncthreads();
-    if (lane == 0) sM[wave] = lw;
-    __syncthreads();
-    l += sM[0] + sM[1];
+#pragma unroll
+    for (int w = 0; w < kCmbWaves; ++w) l += sR[w];
 #pragma unroll 8
-    for (int c = 0; c < cn; ++c) acc += sW[c] * Opart[(base + c0 + c) * kHdD + j];
+    for (int c = sl; c < cn; c += kCmbSlices) acc += sW[c] * Opart[(base + c0 + c) * kHdD + j];
   }
+  if (sl > 0) sO[sl - 1][j] = acc;
+  __syncthreads();
+  if (sl > 0) return;
+#pragma unroll
+  for (int q = 0; q < kCmbSlices - 1; ++q) acc += sO[q][j];
   O[((size_t)b * nq + h) * kHdD + j] = f2bf(acc / l);
 }
 
@@ -818,7 +853,8 @@ static bool use_cols(int nrb, int col_blocks) { return nrb > 1 && col_blocks >= 
 
 void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
                        const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
-                       const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s) {
+                       const uint16_t* residual, uint16_t* H, float* kpart, uint16_t* Y,
+                       hipStream_t s) {
   const int G = F / n, chunks = G / 8;
   {
     WIDE_TRACE("ffn_up_decode", s);
@@ -838,24 +874,35 @@ void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* W
                                          nullptr, nullptr, n);
     }
   }
-  launch_kmask_decode(kUseFfnDown, H, Wdp, mask, B, d, F, n, residual, Y, s);
+  launch_kmask_decode(kUseFfnDown, H, Wdp, mask, B, d, F, n, residual, kpart, Y, s);
 }
 
 void launch_kmask_decode(KmUse use, const uint16_t* A, const uint16_t* Wp, const uint8_t* mask,
-                         int B, int d, int F, int n, const uint16_t* residual, uint16_t* Y,
-                         hipStream_t s) {
+                         int B, int d, int F, int n, const uint16_t* residual, float* part,
+                         uint16_t* Y, hipStream_t s) {
   WIDE_TRACE(use == kUseAttnO ? "attn_o_decode" : "ffn_down_decode", s);
-  const int nrb = (B + 15) / 16;
-  auto pick = [&](auto tag) {
-    constexpr int U = decltype(tag)::value;
-    return nrb == 1   ? kmask_decode<1, U>
-           : nrb == 2 ? kmask_decode<2, U>
-           : nrb == 3 ? kmask_decode<3, U>
-                      : kmask_decode<4, U>;
+  const int G = F / n, S = kmask_decode_splits(d, n, G), nrb = (B + 15) / 16;
+  auto pick = [&](auto use_tag, auto ks_tag) {
+    constexpr int U = decltype(use_tag)::value, KS = decltype(ks_tag)::value;
+    return nrb == 1   ? kmask_decode<1, KS, U>
+           : nrb == 2 ? kmask_decode<2, KS, U>
+           : nrb == 3 ? kmask_decode<3, KS, U>
+                      : kmask_decode<4, KS, U>;
   };
-  auto k = use == kUseAttnO ? pick(std::integral_constant<int, kUseAttnO>{})
-                            : pick(std::integral_constant<int, kUseFfnDown>{});
-  k<<<d / 16, 64 * kKmWaves, 0, s>>>(A, Wp, mask, B, d, F, F / n, n, residual, Y);
+  using O = std::integral_constant<int, kUseAttnO>;
+  using D = std::integral_constant<int, kUseFfnDown>;
+  using K4 = std::integral_constant<int, 4>;
+  using K2 = std::integral_constant<int, 2>;
+  auto k = use == kUseAttnO ? (G % 128 == 0 ? pick(O{}, K4{}) : pick(O{}, K2{}))
+                            : (G % 128 == 0 ? pick(D{}, K4{}) : pick(D{}, K2{}));
+  k<<<kmask_decode_col_blocks(d) * S, kKmThreads, 0, s>>>(A, Wp, mask, B, d, F, G, n, S, residual,
+                                                         part, Y);
+  if (S > 1) kmask_decode_reduce<<<(B * d / 4 + 255) / 256, 256, 0, s>>>(part, S, B, d, residual, Y);
+}
+
+size_t kmask_decode_part_floats(int B, int d, int n, int G) {
+  const int S = kmask_decode_splits(d, n, G);
+  return S > 1 ? (size_t)S * B * d : 0;
 }
 
 int attn_decode_chunks(int kv_len) { return (kv_len + 1 + kKeyChunk - 1) / kKeyChunk; }
@@ -889,12 +936,13 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHdD);
   {
     WIDE_TRACE("attn_core_decode", s);
-    attn_decode_partial<<<B * n_kv * nch, 256, 0, s>>>(Qd, Kc, Vc, mask, B, n_kv, r, kv_len, kv_cap,
+    attn_decode_partial<<<B * n_kv * nch, kKeyChunk, 0, s>>>(Qd, Kc, Vc, mask, B, n_kv, r, kv_len, kv_cap,
                                                        nch, scale_log2, Opart, Mpart, Lpart);
   }
   {
     WIDE_TRACE("attn_combine_decode", s);
-    attn_decode_combine<<<B * n_kv * r, kHdD, 0, s>>>(Opart, Mpart, Lpart, mask, n_kv, r, nch, O);
+    attn_decode_combine<<<B * n_kv * r, kCmbThreads, 0, s>>>(Opart, Mpart, Lpart, mask, n_kv, r,
+                                                             nch, O);
   }
 }
 

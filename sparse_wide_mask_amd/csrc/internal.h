@@ -67,12 +67,17 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
 
 constexpr int kMaxDecodeBatch = 64;
 // Decode launchers read the [B, n] mask directly (no reorder launch).
+// The K-masked decode projection splits K over work-groups and adds the fp32
+// partial sums in a second launch: it takes a workspace of
+// kmask_decode_part_floats() floats (0 when it does not split).
+size_t kmask_decode_part_floats(int B, int d, int n, int G);
 void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
                        const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
-                       const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
+                       const uint16_t* residual, uint16_t* H, float* kpart, uint16_t* Y,
+                       hipStream_t s);
 void launch_kmask_decode(KmUse use, const uint16_t* A, const uint16_t* Wp,
                          const uint8_t* mask, int B, int d, int F, int n,
-                         const uint16_t* residual, uint16_t* Y, hipStream_t s);
+                         const uint16_t* residual, float* part, uint16_t* Y, hipStream_t s);
 int attn_decode_chunks(int kv_len);
 void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
                         const uint16_t* Wk, const uint16_t* Wv, int B, int d,
