@@ -261,27 +261,51 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     });
   }
 
-  // The residual pointer passes through an empty asm here so its loads are not
-  // hoisted into the K loop, where they would push accumulators out of registers.
+  // Epilogue: Y[token, col] = acc (+ residual), with 32-bit byte offsets
+  // (T d 2 < 2^31).  Rows past the tile's tokens and columns past d take the
+  // kSkip offset, so their loads read 0 and their stores are dropped; without a
+  // residual the descriptor has no records and every load reads 0.  A row
+  // block's residual loads (32 per lane) are issued together before the stores.  The
+  // residual pointer passes through an empty asm so the loads are not scheduled
+  // into the K loop, where they would push accumulators out of registers.
   const uint16_t* res = residual;
   asm volatile("" : "+s"(res));
+  const rsrc_t yr = make_rsrc(Y, (uint32_t)((size_t)T * d * 2));
+  const rsrc_t rr = make_rsrc(res, res ? (uint32_t)((size_t)T * d * 2) : 0u);
 #pragma unroll
-  for (int i = 0; i < C::RB; ++i)
+  for (int i = 0; i < C::RB; ++i) {
+    uint32_t tok[16];
 #pragma unroll
-    for (int j = 0; j < C::CB; ++j) {
-      const int col = n0 + wn * C::WN + j * 32 + (lane & 31);
+    for (int e = 0; e < 16; ++e) {
+      const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
+      tok[e] = row < rows ? (uint32_t)(sTok[row] * d) * 2u : kSkip;
+    }
+    // two 32-column blocks (32 loads per lane) at a time
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
-        if (row < rows && col < d) {
-          const size_t o = (size_t)sTok[row] * d + col;
-          float v = acc.acc[i][j][e];
-          if (res) v += bf2f(res[o]);
-          Y[o] = f2bf(v);
+    for (int j0 = 0; j0 < C::CB; j0 += 2) {
+      uint32_t rv[2][16];
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = n0 + wn * C::WN + (j0 + jj) * 32 + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t off = col < d && tok[e] != kSkip ? tok[e] + 2u * col : kSkip;
+          rv[jj][e] = __builtin_amdgcn_raw_buffer_load_b16(rr, (int)off, 0, 0);
         }
       }
-      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj) {
+        const int col = n0 + wn * C::WN + (j0 + jj) * 32 + (lane & 31);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+          const uint32_t off = col < d && tok[e] != kSkip ? tok[e] + 2u * col : kSkip;
+          const float v = acc.acc[i][j0 + jj][e] + __uint_as_float(rv[jj][e] << 16);
+          __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), yr, (int)off, 0, 0);
+        }
+      }
     }
+    __builtin_amdgcn_sched_barrier(0);
+  }
 }
 
 constexpr int kDownBM = 256;
