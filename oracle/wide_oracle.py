@@ -40,6 +40,12 @@ design notes):
   kv_len; a skipped (sequence, group) writes nothing and outputs zero.
 * R6 layer: pre-norm Llama block, RMSNorm x / sqrt(mean(x^2) + eps) * gamma,
   rotate-half RoPE with angle pos * theta^(-2i/hd), no frequency scaling.
+* R9 router: a linear router without bias, logits = X R^T with R group-major
+  [n, d]; a token keeps the k groups with the largest logits, ties to the lower
+  group index (-0.0 and +0.0 are equal).  The pages say only that a router gives
+  one binary execute/skip decision per group [gist §2A] and that routing is
+  learned per token [abstract]; the router's form and the top-k rule are the
+  plainest reading of a fixed keep ratio.
 """
 from __future__ import annotations
 
@@ -264,3 +270,44 @@ def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q: int, n_kv: int, head_d
     if decode:
         parts.update(K_new=att[1], V_new=att[2])
     return (y, parts) if return_parts else y
+
+
+# ------------------------------------------------------------------- router
+
+def router_topk(X, R, k: int, *, logits=None, dtype=np.float64) -> dict:
+    """Router and top-k selection, the step before the path (reading R9).
+
+    logits[t, g] = sum_j X[t, j] R[g, j].  Token t keeps group g when fewer than k
+    groups rank before g, where g' ranks before g if its logit is larger, or equal
+    with a lower index.  With ``logits`` given, the selection is taken on those
+    values instead (the decision is then made on exactly the numbers another
+    implementation produced).  Returns logits, mask uint8 [T, n] and packed
+    little-endian bit words [T, ceil(n/64)].
+    """
+    if logits is None:
+        X = _f(X, dtype)
+        R = _f(R, dtype)
+        if X.ndim != 2 or R.ndim != 2 or X.shape[1] != R.shape[1]:
+            raise ValueError("X must be [T, d] and R [n, d]")
+        L = X @ R.T
+    else:
+        L = _f(logits, dtype)
+    T, n = L.shape
+    if not 0 <= k <= n:
+        raise ValueError("router_topk: k out of range")
+    mask = np.zeros((T, n), np.uint8)
+    for t in range(T):
+        row = L[t]
+        for g in range(n):
+            before = 0
+            for h in range(n):
+                if row[h] > row[g] or (row[h] == row[g] and h < g):
+                    before += 1
+            if before < k:
+                mask[t, g] = 1
+    nw = (n + 63) // 64
+    packed = np.zeros((T, nw), np.uint64)
+    for g in range(n):
+        w, j = divmod(g, 64)
+        packed[:, w] |= mask[:, g].astype(np.uint64) << np.uint64(j)
+    return dict(logits=L, mask=mask, packed=packed)
