@@ -416,11 +416,46 @@ class LayerDecode:
         return time.perf_counter() - t0
 
 
+class RouterPrefill:
+    """The layer's FFN router on the GPU: logits X R^T and the top-k mask (56 of 112
+    groups) for 8192 tokens of d_model 4096, with the mask's packed bit words."""
+
+    def __init__(self, T=8192):
+        import synth
+        self.name, self.T, self.d, self.n, self.k = "router_prefill_8b", T, 4096, 112, 56
+        self.X = synth.normal(self.name, "X", (T, self.d))
+        self.R = synth.normal(self.name, "R", (self.n, self.d), std=self.d ** -0.5)
+        self.config = dict(workload=self.name, T=T, d_model=self.d, n_groups=self.n, k=self.k,
+                           router="linear, bf16, fp32 logits, top-k with ties to the lower group")
+        self.bound = "hbm"
+
+    def upload(self, torch, wide, bf16, u8):
+        self.Xd, self.Rd = bf16(self.X), bf16(self.R)
+        self.out = dict(mask=torch.empty((self.T, self.n), dtype=torch.uint8, device="cuda"),
+                        packed=torch.empty((self.T, (self.n + 63) // 64), dtype=torch.int64,
+                                           device="cuda"))
+        self.wide = wide
+
+    def step(self, ones=False):
+        # all-ones: every group kept (k = n), the same logits work
+        self.wide.router_topk(self.Xd, self.Rd, self.n if ones else self.k, out=self.out)
+
+    def work(self, ones=False):
+        T, d, n = self.T, self.d, self.n
+        return {"router_topk": T * d * 2 + n * d * 2 + T * n + T * 8 * ((n + 63) // 64)}
+
+    def oracle_sample(self, S):
+        from oracle import router_topk
+        t0 = time.perf_counter()
+        router_topk(self.X[:S], self.R, self.k)
+        return time.perf_counter() - t0
+
+
 WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
              "attn_prefill_8b": AttnPrefill, "layer_decode_8b": LayerDecode,
              "attn_decode_8b": AttnDecode, "ffn_decode_8b_B1": lambda: FfnDecode(1),
              "ffn_decode_8b_B8": lambda: FfnDecode(8), "ffn_decode_8b_B32": lambda: FfnDecode(32),
-             "ffn_decode_8b_B64": lambda: FfnDecode(64)}
+             "ffn_decode_8b_B64": lambda: FfnDecode(64), "router_prefill_8b": RouterPrefill}
 
 
 # ------------------------------------------------------------- measurement
@@ -465,6 +500,33 @@ def traffic_from_profiles(kernel: str, workload: str):
     return rec.get("bytes_per_launch")
 
 
+def gemm_ceiling(torch):
+    """Dense bf16 C = A B with torch.matmul (hipBLASLt) at the layer's FFN shapes, on operands
+    with the workloads' scales (A ~ N(0, 1), B ~ N(0, 0.02)) and on zeros: the MFMA clock, and so
+    the dense rate, depends on the power the operand values draw."""
+    out = {"metric": "dense bf16 GEMM TFLOP/s (torch.matmul / hipBLASLt)", "peak": PEAK_BF16_TFLOPS,
+           "shapes": []}
+    gen = torch.Generator(device="cuda").manual_seed(0)
+    for (M, N, K) in [(8192, 8192, 4096), (8192, 28672, 4096), (8192, 4096, 14336)]:
+        row = {"M": M, "N": N, "K": K}
+        for kind in ("random", "zeros"):
+            if kind == "random":
+                A = torch.randn(M, K, device="cuda", generator=gen).to(torch.bfloat16)
+                B = (0.02 * torch.randn(K, N, device="cuda", generator=gen)).to(torch.bfloat16)
+            else:
+                A = torch.zeros(M, K, device="cuda", dtype=torch.bfloat16)
+                B = torch.zeros(K, N, device="cuda", dtype=torch.bfloat16)
+            stream = torch.cuda.current_stream()
+            warm(torch, lambda: A @ B, 3)
+            ms = timed(torch, lambda: A @ B, 10, stream)
+            tf = 2.0 * M * N * K / (ms * 1e-3) / 1e12
+            row[kind] = {"us": round(ms * 1e3, 1), "tflops": round(tf, 1),
+                         "frac": round(tf / PEAK_BF16_TFLOPS, 4)}
+            del A, B
+        out["shapes"].append(row)
+    return out
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -492,6 +554,10 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=0,
                     help="instead of a workload, run 3 plain device copies of this many bytes "
                          "(calibrates the HBM traffic counters) and exit")
+    ap.add_argument("--gemm-ceiling", action="store_true",
+                    help="instead of a workload, time the vendor dense bf16 GEMM (torch.matmul, "
+                         "hipBLASLt) on random and on zero operands at the 8B FFN shapes, print "
+                         "one JSON line and exit (the practical MFMA ceiling on these inputs)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -507,6 +573,10 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(2)
     wide.lib()
+
+    if args.gemm_ceiling:
+        print(json.dumps(gemm_ceiling(torch)), flush=True)
+        return
 
     if args.copy_bytes:
         n = args.copy_bytes // 4

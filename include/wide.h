@@ -89,6 +89,29 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m,
  * group g, the block W[gG:(g+1)G, :] transposed, so each group's block is one
  * contiguous region with the contraction index innermost.  Run once at weight load.
  */
+/*
+ * wide_router_topk - router and top-k selection, the step before the masked path
+ * (gist.science technical summary §2.A: a router gives every token one binary
+ * execute/skip decision per group; the abstract: each token selects its own
+ * attention-head and FFN-channel groups).  A linear router without bias:
+ *   logits[t, g] = sum_j X[t, j] R[g, j]      (bf16 inputs, fp32 accumulation)
+ *   mask[t, g]   = 1 for the k largest logits of token t, else 0; ties go to the
+ *                  lower group index, and -0.0 equals +0.0
+ *   packed[t, w] bit j = mask[t, 64w + j]    (little-endian words, as
+ *                  wide_mask_reorder packs them)
+ * The selection is exact on the fp32 logits the call computes (returned when
+ * `logits` is not NULL): every row keeps exactly k groups.
+ *
+ * X       [T, d_model] bf16                   (input)
+ * R       [n_groups, d_model] bf16, group-major (input)
+ * logits  [T, n_groups] float32 or NULL       (output)
+ * mask    [T, n_groups] uint8                 (output)
+ * packed  [T, ceil(n_groups/64)] uint64 or NULL (output)
+ * 1 <= n_groups <= 256, 0 <= k <= n_groups, d_model % 64 == 0, T <= 65536.
+ */
+int wide_router_topk(const uint16_t* X, const uint16_t* R, int T, int d_model, int n_groups,
+                     int k, float* logits, uint8_t* mask, uint64_t* packed, void* stream);
+
 int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16_t* W_packed,
                      void* stream);
 

@@ -35,6 +35,7 @@ _SIGS = {
     "wide_version": ([], _i),
     "wide_mask_reorder": ([_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
     "wide_pack_kmajor": ([_p, _i, _i, _i, _p, _p], _i),
+    "wide_router_topk": ([_p, _p, _i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wide_ffn_masked_workspace": ([_i, _i, _i, _i, _i], _sz),
     "wide_ffn_masked": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
     "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i, _i], _sz),
@@ -159,6 +160,28 @@ def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None) -> di
                                  _ptr(out["group_rank"]), _ptr(out["tile_count"]),
                                  _ptr(out["tile_groups"]), _stream())
     _check("wide_mask_reorder", st)
+    return out
+
+
+def router_topk(X: torch.Tensor, R: torch.Tensor, k: int, *, return_logits: bool = False,
+                out: dict | None = None) -> dict:
+    """wide_router_topk: X [T, d] bf16, R [n, d] bf16 -> mask uint8 [T, n], packed [T, nw]
+    (int64 view of the uint64 words) and, with ``return_logits``, fp32 logits [T, n]."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(R, torch.bfloat16, "R")
+    T, d = X.shape
+    n, dr = R.shape
+    if dr != d:
+        raise ValueError("R must be [n_groups, d_model] with the d_model of X")
+    dev = X.device
+    if out is None:
+        out = dict(mask=torch.empty((T, n), dtype=torch.uint8, device=dev),
+                   packed=torch.empty((T, (n + 63) // 64), dtype=torch.int64, device=dev))
+        if return_logits:
+            out["logits"] = torch.empty((T, n), dtype=torch.float32, device=dev)
+    st = lib().wide_router_topk(_ptr(X), _ptr(R), T, d, n, k, _ptr(out.get("logits")),
+                                _ptr(out["mask"]), _ptr(out.get("packed")), _stream())
+    _check("wide_router_topk", st)
     return out
 
 

@@ -248,6 +248,23 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m, uint
   return launch_status();
 }
 
+int wide_router_topk(const uint16_t* X, const uint16_t* R, int T, int d_model, int n_groups,
+                     int k, float* logits, uint8_t* mask, uint64_t* packed, void* stream) {
+  if (T < 0 || d_model <= 0 || n_groups < 1 || k < 0 || k > n_groups) return WIDE_EINVAL;
+  if (n_groups > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS || d_model % 64) return WIDE_EUNSUPPORTED;
+  if (!fits(T, d_model) || !fits(n_groups, d_model)) return WIDE_EUNSUPPORTED;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(R) || !aligned16(mask)) return WIDE_EINVAL;
+  if ((logits && !aligned16(logits)) || (packed && !aligned16(packed))) return WIDE_EINVAL;
+  if ((const void*)mask == (const void*)X || (const void*)mask == (const void*)R ||
+      (const void*)logits == (const void*)X || (const void*)logits == (const void*)R ||
+      (const void*)packed == (const void*)X || (const void*)packed == (const void*)R)
+    return WIDE_EINVAL;
+  (void)hipGetLastError();
+  launch_router_topk(X, R, T, d_model, n_groups, k, logits, mask, packed, as_stream(stream));
+  return launch_status();
+}
+
 int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16_t* W_packed,
                      void* stream) {
   if (n_groups < 1 || G < 1 || d_model < 1) return WIDE_EINVAL;

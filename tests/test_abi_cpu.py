@@ -64,3 +64,14 @@ def test_validation_before_any_launch(L):
     assert L.wide_ffn_masked(z, z, z, z, z, 8, 256, 1024, 16, 7, z, z, 0, 0, z) == 1
     assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 0, z) == 0
     assert L.wide_pack_kmajor(z, 4, 64, 256, z, z) == 1
+
+
+def test_router_validation_before_any_launch(L):
+    z = C.c_void_p(0)
+    assert L.wide_router_topk(z, z, 8, 256, 16, 8, z, z, z, z) == 1     # NULL X / R / mask
+    assert L.wide_router_topk(z, z, 8, 256, 16, 17, z, z, z, z) == 1    # k > n_groups
+    assert L.wide_router_topk(z, z, 8, 256, 16, -1, z, z, z, z) == 1
+    assert L.wide_router_topk(z, z, 8, 256, 0, 0, z, z, z, z) == 1      # no groups
+    assert L.wide_router_topk(z, z, 8, 200, 16, 8, z, z, z, z) == 2     # d_model % 64
+    assert L.wide_router_topk(z, z, 8, 256, 257, 8, z, z, z, z) == 2    # too many groups
+    assert L.wide_router_topk(z, z, 0, 256, 16, 8, z, z, z, z) == 0     # T == 0: no-op
