@@ -42,9 +42,11 @@ def log(msg):
 
 # ------------------------------------------------------------- workloads
 
-def layer_name(base, keep, kind):
-    """Workload name; the default structure (router top-k at 50%) keeps the base name."""
-    return base if (kind, keep) == ("router", 0.5) else f"{base}_{kind}_{int(round(keep * 100))}"
+def layer_name(base, keep, kind, ffn_group=128):
+    """Workload name; the default structure (router top-k at 50%, FFN groups of 128) keeps
+    the base name."""
+    name = base if (kind, keep) == ("router", 0.5) else f"{base}_{kind}_{int(round(keep * 100))}"
+    return name if ffn_group == 128 else f"{name}_g{ffn_group}"
 
 
 def measured_keep(c):
@@ -60,10 +62,10 @@ def measured_keep(c):
 class LayerPrefill:
     """Llama-3.1-8B-shaped decoder layer, prefill."""
 
-    def __init__(self, T=8192, keep=0.5, kind="router"):
+    def __init__(self, T=8192, keep=0.5, kind="router", ffn_group=128):
         from synth.workloads import layer_8b
-        self.name = layer_name("layer_prefill_8b", keep, kind)
-        self.c = layer_8b(T, keep=keep, kind=kind)
+        self.name = layer_name("layer_prefill_8b", keep, kind, ffn_group)
+        self.c = layer_8b(T, keep=keep, kind=kind, ffn_group=ffn_group)
         m = self.c["meta"]
         self.m = m
         self.T = T
@@ -350,10 +352,10 @@ class AttnDecode:
 class LayerDecode:
     """Llama-3.1-8B-shaped decoder layer, decode: batch 32 over an 8192-entry cache."""
 
-    def __init__(self, B=32, L=8192, keep=0.5, kind="router"):
+    def __init__(self, B=32, L=8192, keep=0.5, kind="router", ffn_group=128):
         from synth.workloads import layer_8b
-        self.name = layer_name("layer_decode_8b", keep, kind)
-        self.c = layer_8b(B, decode=True, L=L, keep=keep, kind=kind)
+        self.name = layer_name("layer_decode_8b", keep, kind, ffn_group)
+        self.c = layer_8b(B, decode=True, L=L, keep=keep, kind=kind, ffn_group=ffn_group)
         m = self.c["meta"]
         self.m, self.T, self.L = m, B, L
         self.config = dict(workload=self.name, B=B, kv_len=L, d_model=m["d"], d_ff=m["F"],
@@ -549,6 +551,8 @@ def main():
                     help="layer workloads: kept fraction of groups per token")
     ap.add_argument("--masks", default="router", choices=["router", "bernoulli", "clustered"],
                     help="layer workloads: mask structure")
+    ap.add_argument("--ffn-group", type=int, default=128,
+                    help="layer workloads: channels per FFN group (d_ff 14336 = groups x this)")
     ap.add_argument("--skip-ones", action="store_true",
                     help="skip the all-ones comparison (profiler runs: only masked launches)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -591,7 +595,7 @@ def main():
 
     log(f"generating {args.workload} inputs")
     if args.workload.startswith("layer_"):
-        W = WORKLOADS[args.workload](keep=args.keep, kind=args.masks)
+        W = WORKLOADS[args.workload](keep=args.keep, kind=args.masks, ffn_group=args.ffn_group)
     else:
         W = WORKLOADS[args.workload]()
     W.upload(torch, wide, bf16, u8)

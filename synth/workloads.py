@@ -148,7 +148,12 @@ def attn_decode_8b(B: int = 16, L: int = 4096):
                      kv_len=L, kv_cap=L + 1)
 
 
-def layer_8b(T: int, *, decode: bool = False, L: int = 0, keep: float = 0.5, kind: str = "router"):
+def layer_8b(T: int, *, decode: bool = False, L: int = 0, keep: float = 0.5, kind: str = "router",
+             ffn_group: int = 128):
+    """The 8B layer; ``ffn_group`` channels per FFN group (d_ff = 14336 in 14336 / ffn_group
+    groups).  Inputs and weights do not depend on the group size, only the FFN mask does."""
+    if 14336 % ffn_group:
+        raise ValueError("ffn_group must divide 14336")
     name = f"layer_8b_{'dec' if decode else 'pre'}_{kind}_{int(round(keep * 100))}"
-    return layer_case(name, T, keep=keep, mask_kind=kind, decode=decode, kv_len=L,
-                      kv_cap=(L + 1) if decode else 0)
+    return layer_case(name, T, n_ffn=14336 // ffn_group, keep=keep, mask_kind=kind, decode=decode,
+                      kv_len=L, kv_cap=(L + 1) if decode else 0)

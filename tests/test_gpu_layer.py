@@ -91,14 +91,16 @@ def test_layer_all_zero_masks_is_identity():
 
 
 @needs_gpu
-def test_layer_prefill_llama31_8b_sampled():
-    """Full Llama-3.1-8B layer shape at T=8192, router top-k masks keeping 50%;
-    the oracle computes 24 sampled token rows (keys/values of all tokens).  The FFN
+@pytest.mark.parametrize("ffn_group", [128, 64])
+def test_layer_prefill_llama31_8b_sampled(ffn_group):
+    """Full Llama-3.1-8B layer shape at T=8192, router top-k masks keeping 50%, FFN
+    groups of 128 (112 groups) and of 64 (224 groups, the group-size sweep); the
+    oracle computes 24 sampled token rows (keys/values of all tokens).  The FFN
     sublayer is also checked alone at this shape on the oracle's intermediate
     input (bf16-rounded), where the residual does not hide its error."""
     dev()
-    log("layer prefill 8B T=8192 (sampled)")
-    c = layer_8b(8192)
+    log(f"layer prefill 8B T=8192 G={ffn_group} (sampled)")
+    c = layer_8b(8192, ffn_group=ffn_group)
     m = c["meta"]
     rows = np.sort(np.random.default_rng(2).choice(8192, 24, replace=False))
     rows[0], rows[-1] = 0, 8191
