@@ -37,7 +37,11 @@ design notes):
   Scale 1/sqrt(head_dim).  Outputs of skipped groups are exactly zero.
 * R5 decode: the K/V cache of each (sequence, group) holds kv_len valid entries;
   a new token kept in g attends to all of them plus itself and is appended at slot
-  kv_len; a skipped (sequence, group) writes nothing and outputs zero.
+  kv_len; a skipped (sequence, group) writes nothing and outputs zero.  Across
+  decode steps R4 means the caches hold only the tokens that kept the group, so
+  each (sequence, group) has its own length (kv_len [B, n_kv]); the new token's
+  RoPE position is then a separate argument.  A length outside [0, kv_cap) makes
+  the pair write nothing and output zero.
 * R6 layer: pre-norm Llama block, RMSNorm x / sqrt(mean(x^2) + eps) * gamma,
   rotate-half RoPE with angle pos * theta^(-2i/hd), no frequency scaling.
 * R9 router: a linear router without bias, logits = X R^T with R group-major
@@ -165,7 +169,7 @@ def _softmax_rows(S):
 
 def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
                 rope_theta: float = 0.0, decode: bool = False, K_cache=None, V_cache=None,
-                kv_len: int = 0, dtype=np.float64, return_o: bool = False, rows=None):
+                kv_len=0, pos=None, dtype=np.float64, return_o: bool = False, rows=None):
     """Masked attention sublayer: GQA-aligned head groups [gist §2A], readings R3-R5.
 
     One group = one KV head and its r = n_q / n_kv query heads.  Projections are
@@ -178,6 +182,8 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
     (Y, K_new, V_new) where K_new, V_new
     [B, n_kv, hd] are the (roped) keys/values appended at slot kv_len for the kept
     (sequence, group) pairs (zero rows elsewhere; nothing is appended there).
+    ``kv_len`` is one length for the batch or an array [B, n_kv] of per-pair
+    lengths (then ``pos``, the new tokens' position, is required).
     """
     X, Wq, Wk, Wv, Wo = (_f(a, dtype) for a in (X, Wq, Wk, Wv, Wo))
     keep = np.asarray(mask) != 0                                  # [T, n_kv]
@@ -196,7 +202,10 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
         Q = np.where(Eq, X @ Wq.T, 0.0).reshape(T, n_q, hd)
     K = np.where(Ek, X @ Wk.T, 0.0).reshape(T, n_kv, hd)
     V = np.where(Ek, X @ Wv.T, 0.0).reshape(T, n_kv, hd)
-    pos = np.full(T, kv_len) if decode else np.arange(T)
+    L = np.asarray(kv_len)
+    if decode and L.ndim == 2 and pos is None:
+        raise ValueError("per-pair kv_len needs pos")
+    pos = np.full(T, int(L) if pos is None else pos) if decode else np.arange(T)
     if rope_theta:
         if rows is not None and not decode:
             R_ = np.asarray(rows)
@@ -225,12 +234,18 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
 
     Kc = _f(K_cache, dtype)
     Vc = _f(V_cache, dtype)
+    cap = Kc.shape[2]
     for b in range(T):
         for g in range(n_kv):
             if not keep[b, g]:
                 continue
-            keys = np.concatenate([Kc[b, g, :kv_len], K[b, g][None]], axis=0)
-            vals = np.concatenate([Vc[b, g, :kv_len], V[b, g][None]], axis=0)
+            lb = int(L[b, g]) if L.ndim == 2 else int(L)
+            if not 0 <= lb < cap:  # out-of-range length: nothing appended, zero output
+                K[b, g] = 0.0
+                V[b, g] = 0.0
+                continue
+            keys = np.concatenate([Kc[b, g, :lb], K[b, g][None]], axis=0)
+            vals = np.concatenate([Vc[b, g, :lb], V[b, g][None]], axis=0)
             for h in range(g * r, (g + 1) * r):
                 p = _softmax_rows(((keys @ Q[b, h]) * scale)[None])[0]
                 O[b, h] = p @ vals

@@ -190,3 +190,69 @@ def test_rows_option_selects_rows(theta):
     full = _run(X, m, W, n_q, n_kv, hd, theta)
     part = _run(X, m, W, n_q, n_kv, hd, theta, rows=rows)
     np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-12)
+
+
+def _decode_steps_with_masked_caches(X, M, W, n_q, n_kv, hd, theta):
+    """Run the sequences X [B, S, d] one token at a time from empty caches in which
+    tokens that skip a group leave no entry (per-pair lengths)."""
+    B, S, d = X.shape
+    Kc = np.zeros((B, n_kv, S, hd))
+    Vc = np.zeros((B, n_kv, S, hd))
+    L = np.zeros((B, n_kv), np.int64)
+    Ys = []
+    for s in range(S):
+        Y, Kn, Vn = attn_masked(X[:, s], M[:, s], W["Wq"], W["Wk"], W["Wv"], W["Wo"], n_q=n_q,
+                                n_kv=n_kv, head_dim=hd, rope_theta=theta, decode=True,
+                                K_cache=Kc, V_cache=Vc, kv_len=L, pos=s)
+        for b in range(B):
+            for g in range(n_kv):
+                if M[b, s, g]:
+                    Kc[b, g, L[b, g]] = Kn[b, g]
+                    Vc[b, g, L[b, g]] = Vn[b, g]
+                    L[b, g] += 1
+        Ys.append(Y)
+    return np.stack(Ys, axis=1), L
+
+
+@pytest.mark.parametrize("theta", [0.0, 10000.0])
+def test_masked_cache_decode_steps_reproduce_prefill(theta):
+    """Reading R4 across decode steps: decoding a sequence token by token over caches
+    that hold only the tokens which kept each group gives the prefill rows."""
+    rng = np.random.default_rng(11)
+    B, S, d, n_q, n_kv, hd = 3, 9, 16, 4, 2, 4
+    X = rng.standard_normal((B, S, d))
+    M = (rng.random((B, S, n_kv)) < 0.6).astype(np.uint8)
+    W = {k: rng.standard_normal(sh) * 0.3 for k, sh in
+         (("Wq", (n_q * hd, d)), ("Wk", (n_kv * hd, d)), ("Wv", (n_kv * hd, d)), ("Wo", (n_q * hd, d)))}
+    Yd, L = _decode_steps_with_masked_caches(X, M, W, n_q, n_kv, hd, theta)
+    np.testing.assert_array_equal(L, M.sum(axis=1))
+    for b in range(B):
+        Yp = attn_masked(X[b], M[b], W["Wq"], W["Wk"], W["Wv"], W["Wo"], n_q=n_q, n_kv=n_kv,
+                         head_dim=hd, rope_theta=theta)
+        np.testing.assert_allclose(Yd[b], Yp, rtol=1e-10, atol=1e-12)
+
+
+def test_per_pair_lengths_equal_the_uniform_length():
+    rng = np.random.default_rng(5)
+    B, d, n_q, n_kv, hd, L0, cap = 4, 8, 4, 2, 4, 5, 7
+    X = rng.standard_normal((B, d))
+    M = (rng.random((B, n_kv)) < 0.7).astype(np.uint8)
+    W = [rng.standard_normal(sh) for sh in ((n_q * hd, d), (n_kv * hd, d), (n_kv * hd, d), (n_q * hd, d))]
+    Kc, Vc = rng.standard_normal((2, B, n_kv, cap, hd))
+    a = attn_masked(X, M, *W, n_q=n_q, n_kv=n_kv, head_dim=hd, rope_theta=100.0, decode=True,
+                    K_cache=Kc, V_cache=Vc, kv_len=L0)
+    b = attn_masked(X, M, *W, n_q=n_q, n_kv=n_kv, head_dim=hd, rope_theta=100.0, decode=True,
+                    K_cache=Kc, V_cache=Vc, kv_len=np.full((B, n_kv), L0), pos=L0)
+    for x, y in zip(a, b):
+        np.testing.assert_array_equal(x, y)
+    # an out-of-range length is a dropped pair: zero output, nothing appended
+    Lbad = np.full((B, n_kv), L0)
+    Lbad[0, :] = cap
+    c = attn_masked(X, M, *W, n_q=n_q, n_kv=n_kv, head_dim=hd, rope_theta=100.0, decode=True,
+                    K_cache=Kc, V_cache=Vc, kv_len=Lbad, pos=L0)
+    M0 = M.copy()
+    M0[0, :] = 0
+    e = attn_masked(X, M0, *W, n_q=n_q, n_kv=n_kv, head_dim=hd, rope_theta=100.0, decode=True,
+                    K_cache=Kc, V_cache=Vc, kv_len=L0)
+    np.testing.assert_allclose(c[0], e[0], rtol=1e-12, atol=1e-12)
+    assert np.all(c[1][0] == 0) and np.all(c[2][0] == 0)
