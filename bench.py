@@ -349,6 +349,74 @@ class AttnDecode:
         return time.perf_counter() - t0
 
 
+class AttnDecodeMaskedCache:
+    """Llama-3.1-8B-shaped attention decode over masked caches: batch 16 at position 8192,
+    where each (sequence, group) cache holds only the earlier tokens that kept the group
+    (about half of 8192 at keep 4 of 8).  All-ones comparison: every group kept, every
+    cache full (kv_len = position)."""
+
+    def __init__(self, B=16, pos=8192):
+        from synth.workloads import attn_case
+        self.name = "attn_decode_masked_cache_8b"
+        self.c = attn_case(self.name, B, keep=0.5, mask_kind="topk", decode=True, kv_len=pos,
+                           kv_cap=pos + 1)
+        m = self.c["meta"]
+        self.m, self.T, self.pos = m, B, pos
+        rng = np.random.default_rng(8192)
+        self.lens = rng.binomial(pos, 0.5, size=(B, m["n_kv"])).astype(np.int32)
+        self.config = dict(workload=self.name, B=B, position=pos, kv_cap=pos + 1,
+                           mean_cache_len=round(float(self.lens.mean()), 1), d_model=m["d"],
+                           n_q_heads=m["n_q"], n_kv_heads=m["n_kv"], head_dim=HD, keep=m["keep"],
+                           masks="top-k")
+        self.bound = "hbm"
+
+    def upload(self, torch, wide, bf16, u8):
+        c, m = self.c, self.m
+        set_bytes = (2 * m["n_q"] + 2 * m["n_kv"]) * HD * m["d"] * 2 + 2 * c["K_cache"].size * 2
+        self.sets = []
+        for _ in range(_copies(set_bytes)):
+            self.sets.append((bf16(c["Wq"]), bf16(c["Wk"]), bf16(c["Wv"]),
+                              wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]), bf16(c["K_cache"]),
+                              bf16(c["V_cache"])))
+        self.X = bf16(c["X"])
+        self.mask = u8(c["mask"])
+        self.ones = torch.ones_like(self.mask)
+        self.L = torch.from_numpy(self.lens).cuda()
+        self.full = torch.full_like(self.L, self.pos)
+        self.Y = torch.empty_like(self.X)
+        self.ws = torch.empty(wide.attn_proj_masked_workspace(self.T, m["d"], m["n_q"], m["n_kv"],
+                                                              mode="decode", kv_cap=self.pos + 1),
+                              dtype=torch.uint8, device="cuda")
+        self.wide, self.i = wide, 0
+
+    def step(self, ones=False):
+        m = self.m
+        Wq, Wk, Wv, Wo, Kc, Vc = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.wide.attn_decode_masked_cache(self.X, self.ones if ones else self.mask, Wq, Wk, Wv,
+                                           Wo, n_q=m["n_q"], n_kv=m["n_kv"], K_cache=Kc,
+                                           V_cache=Vc, kv_len=self.full if ones else self.L,
+                                           pos=self.pos, out=self.Y, workspace=self.ws)
+
+    def work(self, ones=False):
+        am = np.ones_like(self.c["mask"]) if ones else (self.c["mask"] != 0)
+        lens = np.full_like(self.lens, self.pos) if ones else self.lens
+        w = _attn_decode_bytes(self.m, am, self.m["d"], 0)
+        r = self.m["n_q"] // self.m["n_kv"]
+        kept_len = float(((lens + 1) * am).sum())
+        w["attn_core_decode"] = kept_len * 2 * HD * 2 + float(am.sum()) * r * HD * 2
+        return w
+
+    def oracle_sample(self, S):
+        from oracle import attn_masked
+        c, m = self.c, self.m
+        t0 = time.perf_counter()
+        attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
+                    n_kv=m["n_kv"], head_dim=HD, decode=True, K_cache=c["K_cache"][:S],
+                    V_cache=c["V_cache"][:S], kv_len=self.lens[:S], pos=self.pos)
+        return time.perf_counter() - t0
+
+
 class LayerDecode:
     """Llama-3.1-8B-shaped decoder layer, decode: batch 32 over an 8192-entry cache."""
 
@@ -457,7 +525,8 @@ WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
              "attn_prefill_8b": AttnPrefill, "layer_decode_8b": LayerDecode,
              "attn_decode_8b": AttnDecode, "ffn_decode_8b_B1": lambda: FfnDecode(1),
              "ffn_decode_8b_B8": lambda: FfnDecode(8), "ffn_decode_8b_B32": lambda: FfnDecode(32),
-             "ffn_decode_8b_B64": lambda: FfnDecode(64), "router_prefill_8b": RouterPrefill}
+             "ffn_decode_8b_B64": lambda: FfnDecode(64), "router_prefill_8b": RouterPrefill,
+             "attn_decode_masked_cache_8b": AttnDecodeMaskedCache}
 
 
 # ------------------------------------------------------------- measurement

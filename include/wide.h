@@ -176,6 +176,31 @@ int wide_attn_proj_masked(const uint16_t* X, const uint8_t* mask, const uint16_t
                           void* stream);
 
 /*
+ * wide_attn_decode_masked_cache - one decode step of the masked attention sublayer
+ * over caches in which tokens that skipped a group left no entry (gist.science
+ * §2.A groups, with wide_attn_proj_masked's reading that a token sees only the
+ * earlier tokens that also kept its group, carried across decode steps).
+ *
+ * kv_len  [B, n_kv_heads] int32 (device, input): the number of valid entries of
+ *         each (sequence, group) cache, slots 0 .. kv_len-1.  A kept (b, g) writes
+ *         the new roped k and v at slot kv_len[b, g] and attends to slots
+ *         0 .. kv_len[b, g] (the new token included); a dropped pair writes nothing
+ *         and outputs zero.  A length outside [0, kv_cap) behaves like a dropped pair
+ *         (nothing written, zero output).  The library does not change kv_len: after
+ *         the call the caller advances it by the mask (kv_len += mask != 0).
+ * pos     RoPE position of the new tokens (>= 0; one position for the batch).
+ * Other arguments as wide_attn_proj_masked in decode mode (B <= 64, head_dim 128);
+ * workspace: wide_attn_proj_masked_workspace(B, d_model, cfg, WIDE_DECODE, kv_cap).
+ */
+int wide_attn_decode_masked_cache(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
+                                  const uint16_t* Wk, const uint16_t* Wv,
+                                  const uint16_t* Wo_packed, int B, int d_model,
+                                  const wide_attn_cfg* cfg, uint16_t* K_cache, uint16_t* V_cache,
+                                  int kv_cap, const int32_t* kv_len, int pos, uint16_t* Y,
+                                  void* workspace, size_t workspace_bytes, uint32_t flags,
+                                  void* stream);
+
+/*
  * wide_layer_masked - one pre-norm decoder layer with both masked sublayers:
  *   u = RMSNorm(x; rms1), h = x + Attn(u; attn_mask), w = RMSNorm(h; rms2),
  *   y = h + FFN(w; ffn_mask),  RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma.

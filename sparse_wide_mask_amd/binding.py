@@ -42,6 +42,8 @@ _SIGS = {
     "wide_attn_proj_masked": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _i, _p, _p,
                                _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
     "wide_layer_masked_workspace": ([_i, C.POINTER(WideLayerCfg), _i, _i], _sz),
+    "wide_attn_decode_masked_cache": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _p,
+                                       _p, _i, _p, _i, _p, _p, _sz, C.c_uint32, _p], _i),
     "wide_trace_enable": ([_i], _i),
     "wide_trace_collect": ([], _i),
     "wide_trace_get": ([_i, C.c_char_p, _i, C.POINTER(_i), C.POINTER(C.c_double)], _i),
@@ -262,6 +264,30 @@ def attn_proj_masked(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, head_dim=128,
                                      _ptr(V_cache), kv_len, kv_cap, _ptr(Y), _ptr(ws), ws.numel(),
                                      0, _stream())
     _check("wide_attn_proj_masked", st)
+    return Y
+
+
+def attn_decode_masked_cache(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, K_cache, V_cache,
+                             kv_len, pos, head_dim=128, rope_theta=0.0, out=None, workspace=None):
+    """wide_attn_decode_masked_cache: one decode step over per-(sequence, group) cache
+    lengths kv_len (int32 [B, n_kv] device tensor, not modified: advance it by the mask
+    after the call).  Returns Y [B, d] bf16; writes the kept pairs' new K/V."""
+    for t, nm in ((X, "X"), (Wq, "Wq"), (Wk, "Wk"), (Wv, "Wv"), (Wo_packed, "Wo_packed"),
+                  (K_cache, "K_cache"), (V_cache, "V_cache")):
+        _dev(t, torch.bfloat16, nm)
+    _dev(mask, torch.uint8, "mask")
+    _dev(kv_len, torch.int32, "kv_len")
+    B, d = X.shape
+    kv_cap = K_cache.shape[2]
+    cfg = _attn_cfg(n_q, n_kv, head_dim, rope_theta)
+    ws_bytes = int(lib().wide_attn_proj_masked_workspace(B, d, C.byref(cfg), WIDE_DECODE, kv_cap))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((B, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_attn_decode_masked_cache(_ptr(X), _ptr(mask), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                             _ptr(Wo_packed), B, d, C.byref(cfg), _ptr(K_cache),
+                                             _ptr(V_cache), kv_cap, _ptr(kv_len), int(pos), _ptr(Y),
+                                             _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_attn_decode_masked_cache", st)
     return Y
 
 

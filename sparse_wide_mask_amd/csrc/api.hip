@@ -165,11 +165,13 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
 void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
               const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
               int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
-              const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s) {
+              const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s,
+              const int32_t* pair_len = nullptr, int pos = -1) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
-                       kv_cap, w.Qc, w.Opart, w.Mpart, w.Lpart, w.O, s);
+                       kv_cap, pair_len, pos < 0 ? kv_len : pos, w.Qc, w.Opart, w.Mpart, w.Lpart,
+                       w.O, s);
     launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, w.kpart,
                         Y, s);
     return;
@@ -340,6 +342,37 @@ int wide_attn_proj_masked(const uint16_t* X, const uint8_t* mask, const uint16_t
   (void)hipGetLastError();
   attn_run(X, mask, Wq, Wk, Wv, Wo_packed, T, d_model, cfg, mode, K_cache, V_cache, kv_len, kv_cap,
            nullptr, Y, w, as_stream(stream));
+  return launch_status();
+}
+
+int wide_attn_decode_masked_cache(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
+                                  const uint16_t* Wk, const uint16_t* Wv,
+                                  const uint16_t* Wo_packed, int B, int d_model,
+                                  const wide_attn_cfg* cfg, uint16_t* K_cache, uint16_t* V_cache,
+                                  int kv_cap, const int32_t* kv_len, int pos, uint16_t* Y,
+                                  void* workspace, size_t workspace_bytes, uint32_t flags,
+                                  void* stream) {
+  int st = attn_check(B, d_model, cfg, WIDE_DECODE);
+  if (st != WIDE_OK) return st;
+  if (flags != 0 || pos < 0) return WIDE_EINVAL;
+  // the shape checks of a uniform-length call with the last slot in use
+  st = attn_decode_check(B, cfg, K_cache, V_cache, kv_cap - 1, kv_cap);
+  if (st != WIDE_OK) return st;
+  if (B == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(mask) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+      !aligned16(Wo_packed) || !aligned16(Y) || !aligned16(kv_len) || (void*)Y == (void*)X)
+    return WIDE_EINVAL;
+  if ((const void*)kv_len == (const void*)K_cache || (const void*)kv_len == (const void*)V_cache)
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_attn(probe, B, d_model, cfg, WIDE_DECODE, kv_cap);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  AttnWs w = carve_attn(c, B, d_model, cfg, WIDE_DECODE, kv_cap);
+  (void)hipGetLastError();
+  attn_run(X, mask, Wq, Wk, Wv, Wo_packed, B, d_model, cfg, WIDE_DECODE, K_cache, V_cache, 0,
+           kv_cap, nullptr, Y, w, as_stream(stream), kv_len, pos);
   return launch_status();
 }
 

@@ -60,6 +60,21 @@ WIDE_DEV bf16x8 xload(rsrc_t r, uint32_t off) {
 // then v) covers head dims {8c..8c+7} and {64+8c..64+8c+7}, so each RoPE pair
 // (j, j + 64) is a lane pair too; rotation is at position kv_len, and k and v go
 // straight into the caches at slot kv_len.
+// The decode K/V caches: where a kept (sequence, group) appends the new token's
+// K/V and how many earlier entries it attends to.  One length for the whole batch
+// (kvl null), or one per (sequence, group) (kvl [B, n_groups]: caches in which
+// tokens that skipped the group left no entry).  A length outside [0, kv_cap)
+// makes the pair write nothing and output zero.  pos is the new token's RoPE
+// position.
+struct DecCache {
+  const int32_t* kvl;
+  int kv_len, kv_cap, pos;
+  WIDE_DEV int len(int b, int g, int n_groups) const {
+    return kvl ? kvl[b * n_groups + g] : kv_len;
+  }
+  WIDE_DEV bool ok(int l) const { return l >= 0 && l < kv_cap; }
+};
+
 template <int MODE>
 struct NmCol {
   const uint16_t* wrow;
@@ -68,7 +83,7 @@ struct NmCol {
   bool rope = false;
 
   WIDE_DEV NmCol(int g, int cb, int ch, const uint16_t* W0, const uint16_t* W1,
-                 const uint16_t* W2, int G, int d, int r, int kv_len, float log2_theta) {
+                 const uint16_t* W2, int G, int d, int r, int pos, float log2_theta) {
     if (MODE == kNmFfn) {
       wrow = (ch < 8 ? W0 : W1) + (size_t)(g * G + cb * 8 + (ch & 7)) * d;
     } else {
@@ -82,7 +97,7 @@ struct NmCol {
       rope = hh < r + 1 && log2_theta > 0.f;
       if (rope) {
         const float inv = exp2f(-(2.f * (ch < 8 ? jrow : jrow - 64) / kHdD) * log2_theta);
-        sincosf((float)kv_len * inv, &sn, &cs);
+        sincosf((float)pos * inv, &sn, &cs);
       }
     }
   }
@@ -90,7 +105,7 @@ struct NmCol {
   // v = this lane's column value for token tok (tok < 0: no token).  Every lane
   // of the wave calls it (the pairing is a lane shuffle).
   WIDE_DEV void store(float v, int tok, int g, int cb, int ch, int G, int r, int n_groups,
-                      int kv_len, int kv_cap, uint16_t* out0, uint16_t* Kc, uint16_t* Vc) const {
+                      const DecCache& dc, uint16_t* out0, uint16_t* Kc, uint16_t* Vc) const {
     const float other = __shfl_xor(v, 8);
     if (MODE == kNmFfn) {
       if (tok >= 0 && ch < 8)
@@ -100,10 +115,13 @@ struct NmCol {
       if (rope) o = ch < 8 ? v * cs - other * sn : v * cs + other * sn;
       if (tok < 0) return;
       const uint16_t bits = f2bf(o);
-      if (hh < r)
+      if (hh < r) {
         out0[((size_t)tok * (n_groups * r) + g * r + hh) * kHdD + jrow] = bits;
-      else
-        (hh == r ? Kc : Vc)[(((size_t)tok * n_groups + g) * kv_cap + kv_len) * kHdD + jrow] = bits;
+      } else {
+        const int slot = dc.len(tok, g, n_groups);
+        if (dc.ok(slot))
+          (hh == r ? Kc : Vc)[(((size_t)tok * n_groups + g) * dc.kv_cap + slot) * kHdD + jrow] = bits;
+      }
     }
   }
 };
@@ -113,7 +131,7 @@ __global__ void __launch_bounds__(256)
     nmask_decode(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W0,
                  const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
                  const uint8_t* __restrict__ mask, int B, int d, int G, int chunks, int r,
-                 int kv_len, int kv_cap, float log2_theta, uint16_t* __restrict__ out0,
+                 DecCache dc, float log2_theta, uint16_t* __restrict__ out0,
                  uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc, int n_groups) {
   __shared__ int sTok[kDecRows];
   __shared__ float sRed[3][kDecRows][16];
@@ -134,7 +152,7 @@ __global__ void __launch_bounds__(256)
   const int nrb = (cnt + 15) / 16;  // l=2: row blocks past the count are skipped
 
   const int ch = lane & 15;
-  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, kv_len, log2_theta);
+  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, dc.pos, log2_theta);
   const uint16_t* wrow = col.wrow;
 
   f32x4 acc[NRB];
@@ -254,7 +272,7 @@ __global__ void __launch_bounds__(256)
     for (int i = 0; i < 4; ++i) {
       const int row = rb * 16 + acc16_row(lane, i);
       const float v = acc[rb][i] + sRed[0][row][ch] + sRed[1][row][ch] + sRed[2][row][ch];
-      col.store(v, row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, kv_len, kv_cap, out0,
+      col.store(v, row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, dc, out0,
                 Kc, Vc);
     }
   }
@@ -272,7 +290,7 @@ __global__ void __launch_bounds__(256)
     nmask_decode_cols(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W0,
                       const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
                       const uint8_t* __restrict__ mask, int B, int d, int G, int chunks, int r,
-                      int kv_len, int kv_cap, float log2_theta, uint16_t* __restrict__ out0,
+                      DecCache dc, float log2_theta, uint16_t* __restrict__ out0,
                       uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc, int n_groups) {
   constexpr int U = 8;                  // 32-wide K steps per batch
   constexpr int ROWS = 16 * NRB;
@@ -296,7 +314,7 @@ __global__ void __launch_bounds__(256)
   __syncthreads();
   const int nrb = (cnt + 15) / 16;  // l=2: row blocks past the count are skipped
   const int ch = lane & 15, koff = 8 * (lane >> 4);
-  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, kv_len, log2_theta);
+  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, dc.pos, log2_theta);
   const uint16_t* wp = col.wrow + koff;
 
   // this thread's share of a batch copy: chunk q = tid + 256 i of the tile
@@ -386,8 +404,8 @@ __global__ void __launch_bounds__(256)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = rb * 16 + acc16_row(lane, i);
-      col.store(acc[rb][i], row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, kv_len,
-                kv_cap, out0, Kc, Vc);
+      col.store(acc[rb][i], row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, dc, out0,
+                Kc, Vc);
     }
   }
 }
@@ -631,7 +649,7 @@ constexpr int kKeySlices = kKeyChunk / 32;                // 32-key slices of th
 __global__ void __launch_bounds__(kKeyChunk)
     attn_decode_partial(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
                         const uint16_t* __restrict__ Vc, const uint8_t* __restrict__ mask, int B,
-                        int n_kv, int r, int kv_len, int kv_cap, int nch, float scale_log2,
+                        int n_kv, int r, DecCache dc, int nch, float scale_log2,
                         float* __restrict__ Opart, float* __restrict__ Mpart,
                         float* __restrict__ Lpart) {
   // V rows (row-major, 256 B each); reused for the key-slice partial sums
@@ -641,10 +659,14 @@ __global__ void __launch_bounds__(kKeyChunk)
   const int c = blockIdx.x % nch, rest = blockIdx.x / nch;
   const int g = rest % n_kv, b = rest / n_kv;
   if (!mask[(size_t)b * n_kv + g]) return;  // l=0: the token dropped this group
+  // this pair's keys: its cache entries 0..len-1 and the new token at slot len
+  const int len = dc.len(b, g, n_kv);
   const int k0 = c * kKeyChunk;
-  const int nkeys = min(kKeyChunk, kv_len + 1 - k0);
+  if (!dc.ok(len) || k0 > len) return;  // no such chunk for this pair
+  const int nkeys = min(kKeyChunk, len + 1 - k0);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int nq = n_kv * r;
+  const int kv_cap = dc.kv_cap;
   const size_t kvbase = ((size_t)b * n_kv + g) * kv_cap + k0;  // first key row of the chunk
   const uint32_t cache_bytes = (uint32_t)((size_t)B * n_kv * kv_cap * kHdD * 2);
   const int m16 = lane & 15, q4 = lane >> 4;
@@ -800,7 +822,7 @@ constexpr int kCmbBlock = kCmbThreads;
 __global__ void __launch_bounds__(kCmbThreads)
     attn_decode_combine(const float* __restrict__ Opart, const float* __restrict__ Mpart,
                         const float* __restrict__ Lpart, const uint8_t* __restrict__ mask,
-                        int n_kv, int r, int nch, uint16_t* __restrict__ O) {
+                        int n_kv, int r, DecCache dc, int nch, uint16_t* __restrict__ O) {
   __shared__ float sW[kCmbBlock];
   __shared__ float sR[kCmbWaves];
   __shared__ float sO[kCmbSlices - 1][kHdD];
@@ -810,6 +832,12 @@ __global__ void __launch_bounds__(kCmbThreads)
   const size_t base = (size_t)b * nq * nch + (size_t)h * nch;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = tid % kHdD, sl = tid / kHdD;
+  const int len = dc.len(b, g, n_kv);
+  if (!dc.ok(len)) {  // a pair with an out-of-range length outputs zero
+    if (sl == 0) O[((size_t)b * nq + h) * kHdD + j] = 0;
+    return;
+  }
+  nch = (len + kKeyChunk) / kKeyChunk;  // this pair's chunks (the stride above stays)
   float m = -INFINITY;
   for (int c = tid; c < nch; c += kCmbThreads) m = fmaxf(m, Mpart[base + c]);
   for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -864,13 +892,13 @@ void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* W
                : nrb == 2 ? nmask_decode<kNmFfn, 2>
                : nrb == 3 ? nmask_decode<kNmFfn, 3>
                           : nmask_decode<kNmFfn, 4>;
-      k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
+      k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, DecCache{nullptr, 0, 0, 0}, 0.f, H,
                                    nullptr, nullptr, n);
     } else {
       auto k = nrb == 2   ? nmask_decode_cols<kNmFfn, 2>
                : nrb == 3 ? nmask_decode_cols<kNmFfn, 3>
                           : nmask_decode_cols<kNmFfn, 4>;
-      k<<<n * (chunks / 4), 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, 0, 0, 0.f, H,
+      k<<<n * (chunks / 4), 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, DecCache{nullptr, 0, 0, 0}, 0.f, H,
                                          nullptr, nullptr, n);
     }
   }
@@ -910,10 +938,11 @@ int attn_decode_chunks(int kv_len) { return (kv_len + 1 + kKeyChunk - 1) / kKeyC
 void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
                         const uint16_t* Wk, const uint16_t* Wv, int B, int d,
                         int n_kv, int r, float rope_theta, uint16_t* Kc, uint16_t* Vc, int kv_len,
-                        int kv_cap, uint16_t* Qd, float* Opart, float* Mpart, float* Lpart,
-                        uint16_t* O, hipStream_t s) {
+                        int kv_cap, const int32_t* kvl, int pos, uint16_t* Qd, float* Opart,
+                        float* Mpart, float* Lpart, uint16_t* O, hipStream_t s) {
   const int chunks = (r + 2) * 8;  // 16-row chunks of the group's q, k, v heads
   const float log2_theta = rope_theta > 0.f ? log2f(rope_theta) : 0.f;
+  const DecCache dc{kvl, kv_len, kv_cap, pos};
   {
     WIDE_TRACE("attn_qkv_decode", s);
     const int nrb = (B + 15) / 16;
@@ -922,27 +951,29 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
                : nrb == 2 ? nmask_decode<kNmQkv, 2>
                : nrb == 3 ? nmask_decode<kNmQkv, 3>
                           : nmask_decode<kNmQkv, 4>;
-      k<<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, kv_len, kv_cap,
-                                      log2_theta, Qd, Kc, Vc, n_kv);
+      k<<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, dc, log2_theta,
+                                      Qd, Kc, Vc, n_kv);
     } else {
       auto k = nrb == 2   ? nmask_decode_cols<kNmQkv, 2>
                : nrb == 3 ? nmask_decode_cols<kNmQkv, 3>
                           : nmask_decode_cols<kNmQkv, 4>;
-      k<<<n_kv * (chunks / 4), 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, kv_len,
-                                            kv_cap, log2_theta, Qd, Kc, Vc, n_kv);
+      k<<<n_kv * (chunks / 4), 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, dc,
+                                            log2_theta, Qd, Kc, Vc, n_kv);
     }
   }
-  const int nch = attn_decode_chunks(kv_len);
+  // chunk grid for the longest possible pair: the batch's length, or with per-pair
+  // lengths the last cache slot
+  const int nch = attn_decode_chunks(kvl ? kv_cap - 1 : kv_len);
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHdD);
   {
     WIDE_TRACE("attn_core_decode", s);
-    attn_decode_partial<<<B * n_kv * nch, kKeyChunk, 0, s>>>(Qd, Kc, Vc, mask, B, n_kv, r, kv_len, kv_cap,
-                                                       nch, scale_log2, Opart, Mpart, Lpart);
+    attn_decode_partial<<<B * n_kv * nch, kKeyChunk, 0, s>>>(Qd, Kc, Vc, mask, B, n_kv, r, dc, nch,
+                                                             scale_log2, Opart, Mpart, Lpart);
   }
   {
     WIDE_TRACE("attn_combine_decode", s);
     attn_decode_combine<<<B * n_kv * r, kCmbThreads, 0, s>>>(Opart, Mpart, Lpart, mask, n_kv, r,
-                                                             nch, O);
+                                                             dc, nch, O);
   }
 }
 

@@ -75,3 +75,15 @@ def test_router_validation_before_any_launch(L):
     assert L.wide_router_topk(z, z, 8, 200, 16, 8, z, z, z, z) == 2     # d_model % 64
     assert L.wide_router_topk(z, z, 8, 256, 257, 8, z, z, z, z) == 2    # too many groups
     assert L.wide_router_topk(z, z, 0, 256, 16, 8, z, z, z, z) == 0     # T == 0: no-op
+
+
+def test_masked_cache_decode_validation_before_any_launch(L):
+    from sparse_wide_mask_amd import binding as b
+    z = C.c_void_p(0)
+    cfg = b.WideAttnCfg(32, 8, 128, 0.0)
+    args = lambda B, d, cfgp, cap, pos: (z, z, z, z, z, z, B, d, cfgp, z, z, cap, z, pos, z, z, 0, 0, z)
+    assert L.wide_attn_decode_masked_cache(*args(4, 4096, None, 10, 0)) == 1       # no cfg
+    assert L.wide_attn_decode_masked_cache(*args(4, 4096, C.byref(cfg), 10, -1)) == 1  # pos < 0
+    assert L.wide_attn_decode_masked_cache(*args(4, 4096, C.byref(cfg), 0, 0)) == 1   # no slots
+    assert L.wide_attn_decode_masked_cache(*args(65, 4096, C.byref(cfg), 10, 0)) == 2  # batch > 64
+    assert L.wide_attn_decode_masked_cache(*args(4, 4096, C.byref(cfg), 10, 0)) == 1   # NULL caches
