@@ -42,10 +42,12 @@ def log(msg):
 
 # ------------------------------------------------------------- workloads
 
-def layer_name(base, keep, kind, ffn_group=128):
+def layer_name(base, keep, kind, ffn_group=128, attn_keep=None):
     """Workload name; the default structure (router top-k at 50%, FFN groups of 128) keeps
     the base name."""
     name = base if (kind, keep) == ("router", 0.5) else f"{base}_{kind}_{int(round(keep * 100))}"
+    if attn_keep is not None:
+        name += f"_attn{int(round(attn_keep * 100))}"
     return name if ffn_group == 128 else f"{name}_g{ffn_group}"
 
 
@@ -62,10 +64,10 @@ def measured_keep(c):
 class LayerPrefill:
     """Llama-3.1-8B-shaped decoder layer, prefill."""
 
-    def __init__(self, T=8192, keep=0.5, kind="router", ffn_group=128):
+    def __init__(self, T=8192, keep=0.5, kind="router", ffn_group=128, attn_keep=None):
         from synth.workloads import layer_8b
-        self.name = layer_name("layer_prefill_8b", keep, kind, ffn_group)
-        self.c = layer_8b(T, keep=keep, kind=kind, ffn_group=ffn_group)
+        self.name = layer_name("layer_prefill_8b", keep, kind, ffn_group, attn_keep)
+        self.c = layer_8b(T, keep=keep, kind=kind, ffn_group=ffn_group, attn_keep=attn_keep)
         m = self.c["meta"]
         self.m = m
         self.T = T
@@ -420,10 +422,11 @@ class AttnDecodeMaskedCache:
 class LayerDecode:
     """Llama-3.1-8B-shaped decoder layer, decode: batch 32 over an 8192-entry cache."""
 
-    def __init__(self, B=32, L=8192, keep=0.5, kind="router", ffn_group=128):
+    def __init__(self, B=32, L=8192, keep=0.5, kind="router", ffn_group=128, attn_keep=None):
         from synth.workloads import layer_8b
-        self.name = layer_name("layer_decode_8b", keep, kind, ffn_group)
-        self.c = layer_8b(B, decode=True, L=L, keep=keep, kind=kind, ffn_group=ffn_group)
+        self.name = layer_name("layer_decode_8b", keep, kind, ffn_group, attn_keep)
+        self.c = layer_8b(B, decode=True, L=L, keep=keep, kind=kind, ffn_group=ffn_group,
+                          attn_keep=attn_keep)
         m = self.c["meta"]
         self.m, self.T, self.L = m, B, L
         self.config = dict(workload=self.name, B=B, kv_len=L, d_model=m["d"], d_ff=m["F"],
@@ -620,6 +623,9 @@ def main():
                     help="layer workloads: kept fraction of groups per token")
     ap.add_argument("--masks", default="router", choices=["router", "bernoulli", "clustered"],
                     help="layer workloads: mask structure")
+    ap.add_argument("--attn-keep", type=float, default=None,
+                    help="layer workloads: the attention mask's own keep ratio (--keep is then "
+                         "the FFN's)")
     ap.add_argument("--ffn-group", type=int, default=128,
                     help="layer workloads: channels per FFN group (d_ff 14336 = groups x this)")
     ap.add_argument("--skip-ones", action="store_true",
@@ -664,7 +670,8 @@ def main():
 
     log(f"generating {args.workload} inputs")
     if args.workload.startswith("layer_"):
-        W = WORKLOADS[args.workload](keep=args.keep, kind=args.masks, ffn_group=args.ffn_group)
+        W = WORKLOADS[args.workload](keep=args.keep, kind=args.masks, ffn_group=args.ffn_group,
+                                     attn_keep=args.attn_keep)
     else:
         W = WORKLOADS[args.workload]()
     W.upload(torch, wide, bf16, u8)

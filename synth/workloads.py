@@ -94,14 +94,16 @@ def attn_case(cfg: str, T: int, d: int = 4096, n_q: int = 32, n_kv: int = 8, hd:
 def layer_case(cfg: str, T: int, d: int = 4096, F: int = 14336, n_ffn: int = 112,
                n_q: int = 32, n_kv: int = 8, hd: int = 128, keep: float = 0.5,
                mask_kind: str = "router", *, decode: bool = False, kv_len: int = 0,
-               kv_cap: int = 0, rope_theta: float = 500000.0, eps: float = 1e-5) -> dict:
+               kv_cap: int = 0, rope_theta: float = 500000.0, eps: float = 1e-5,
+               attn_keep: float | None = None) -> dict:
     """A Llama-style decoder layer: RMSNorm weights are 1, masks come from the layer
     input x (router kind: R std 1/64), K/V caches ~ N(0,1) in decode."""
     X = normal(cfg, "X", (T, d))
     rstd = 1.0 / 64.0
     out = dict(
         X=X,
-        attn_mask=make_mask(cfg, T, n_kv, keep, mask_kind, X, tag="attn_mask", router_std=rstd),
+        attn_mask=make_mask(cfg, T, n_kv, keep if attn_keep is None else attn_keep, mask_kind, X,
+                            tag="attn_mask", router_std=rstd),
         ffn_mask=make_mask(cfg, T, n_ffn, keep, mask_kind, X, tag="ffn_mask", router_std=rstd),
         rms1=np.ones(d, np.float32),
         rms2=np.ones(d, np.float32),
@@ -149,11 +151,12 @@ def attn_decode_8b(B: int = 16, L: int = 4096):
 
 
 def layer_8b(T: int, *, decode: bool = False, L: int = 0, keep: float = 0.5, kind: str = "router",
-             ffn_group: int = 128):
+             ffn_group: int = 128, attn_keep: float | None = None):
     """The 8B layer; ``ffn_group`` channels per FFN group (d_ff = 14336 in 14336 / ffn_group
-    groups).  Inputs and weights do not depend on the group size, only the FFN mask does."""
+    groups).  Inputs and weights do not depend on the group size, only the FFN mask does.
+    ``attn_keep`` gives the attention mask its own keep ratio (``keep`` is then the FFN's)."""
     if 14336 % ffn_group:
         raise ValueError("ffn_group must divide 14336")
     name = f"layer_8b_{'dec' if decode else 'pre'}_{kind}_{int(round(keep * 100))}"
     return layer_case(name, T, n_ffn=14336 // ffn_group, keep=keep, mask_kind=kind, decode=decode,
-                      kv_len=L, kv_cap=(L + 1) if decode else 0)
+                      kv_len=L, kv_cap=(L + 1) if decode else 0, attn_keep=attn_keep)

@@ -83,6 +83,20 @@ def _check_sublayers(c, parts, rows=None):
 
 
 @needs_gpu
+def test_layer_prefill_asymmetric_keep():
+    """The pages' asymmetric budget: attention keeps 3 of 8 groups, FFN about 72 % of
+    its groups (router masks from the same input)."""
+    dev()
+    log("layer prefill asymmetric keep")
+    c = layer_case("layer_asym", 400, 512, 2048, 16, 16, 8, 128, 0.72, "router", attn_keep=0.34)
+    assert c["attn_mask"].sum(axis=1).max() == 3 and c["ffn_mask"].sum(axis=1).max() == 12
+    got = gpu_layer(c)
+    ref, parts = oracle_layer(c, parts=True)
+    assert rel_err(got, ref) <= TOL
+    _check_sublayers(c, parts)
+
+
+@needs_gpu
 def test_layer_all_zero_masks_is_identity():
     dev()
     c = layer_case("layer_zero", 300, 256, 1024, 8, 8, 2, 128, 0.0, "zeros")
