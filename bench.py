@@ -503,7 +503,7 @@ class RouterPrefill:
         self.bound = "hbm"
 
     def upload(self, torch, wide, bf16, u8):
-        self.Xd, self.Rd = bf16(self.X), bf16(self.R)
+        self.Xd, self.Rp = bf16(self.X), wide.pack_router(bf16(self.R))
         self.out = dict(mask=torch.empty((self.T, self.n), dtype=torch.uint8, device="cuda"),
                         packed=torch.empty((self.T, (self.n + 63) // 64), dtype=torch.int64,
                                            device="cuda"))
@@ -511,7 +511,7 @@ class RouterPrefill:
 
     def step(self, ones=False):
         # all-ones: every group kept (k = n), the same logits work
-        self.wide.router_topk(self.Xd, self.Rd, self.n if ones else self.k, out=self.out)
+        self.wide.router_topk(self.Xd, self.Rp, self.n if ones else self.k, self.n, out=self.out)
 
     def work(self, ones=False):
         T, d, n = self.T, self.d, self.n

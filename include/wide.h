@@ -103,14 +103,27 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m,
  * `logits` is not NULL): every row keeps exactly k groups.
  *
  * X       [T, d_model] bf16                   (input)
- * R       [n_groups, d_model] bf16, group-major (input)
+ * R_packed the router weights R [n_groups, d_model] (group-major) in fragment
+ *         order (wide_pack_router), bf16   (input)
  * logits  [T, n_groups] float32 or NULL       (output)
  * mask    [T, n_groups] uint8                 (output)
  * packed  [T, ceil(n_groups/64)] uint64 or NULL (output)
  * 1 <= n_groups <= 256, 0 <= k <= n_groups, d_model % 64 == 0, T <= 65536.
  */
-int wide_router_topk(const uint16_t* X, const uint16_t* R, int T, int d_model, int n_groups,
-                     int k, float* logits, uint8_t* mask, uint64_t* packed, void* stream);
+int wide_router_topk(const uint16_t* X, const uint16_t* R_packed, int T, int d_model,
+                     int n_groups, int k, float* logits, uint8_t* mask, uint64_t* packed,
+                     void* stream);
+
+/*
+ * wide_pack_router - weight layout of wide_router_topk (done once per weight set):
+ * R [n_groups, d_model] bf16 -> R_packed [ceil(n_groups/16) * 16 * d_model] bf16 in
+ * the order the router's matrix-core fragments read it: block (j, s) for group tile
+ * j = 0 .. ceil(n/16)-1 and K step s = 0 .. d_model/32-1 holds 64 rows of 8 values,
+ * row l = R[16 j + (l mod 16), 32 s + 8 (l / 16) .. +7] (zeros past n_groups).
+ * 1 <= n_groups <= 256, d_model % 64 == 0.
+ */
+int wide_pack_router(const uint16_t* R, int n_groups, int d_model, uint16_t* R_packed,
+                     void* stream);
 
 int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16_t* W_packed,
                      void* stream);

@@ -10,11 +10,11 @@ raise.
 from .binding import (LIB_PATH, WideError, attn_decode_masked_cache, attn_proj_masked,
                       attn_proj_masked_workspace,
                       ffn_masked, ffn_masked_workspace, layer_masked, layer_masked_workspace,
-                      lib, mask_reorder, pack_kmajor, router_topk, trace_collect,
+                      lib, mask_reorder, pack_kmajor, pack_router, router_topk, trace_collect,
                       trace_enable, trace_reset, WIDE_DECODE, WIDE_PREFILL)
 
 __all__ = [
-    "LIB_PATH", "WideError", "lib", "mask_reorder", "pack_kmajor", "router_topk", "ffn_masked",
+    "LIB_PATH", "WideError", "lib", "mask_reorder", "pack_kmajor", "pack_router", "router_topk", "ffn_masked",
     "ffn_masked_workspace", "attn_proj_masked", "attn_proj_masked_workspace",
     "attn_decode_masked_cache", "layer_masked",
     "layer_masked_workspace", "trace_enable", "trace_reset", "trace_collect", "WIDE_PREFILL",

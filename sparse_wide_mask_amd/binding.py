@@ -36,6 +36,7 @@ _SIGS = {
     "wide_mask_reorder": ([_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
     "wide_pack_kmajor": ([_p, _i, _i, _i, _p, _p], _i),
     "wide_router_topk": ([_p, _p, _i, _i, _i, _i, _p, _p, _p, _p], _i),
+    "wide_pack_router": ([_p, _i, _i, _p, _p], _i),
     "wide_ffn_masked_workspace": ([_i, _i, _i, _i, _i], _sz),
     "wide_ffn_masked": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
     "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i, _i], _sz),
@@ -165,23 +166,34 @@ def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None) -> di
     return out
 
 
-def router_topk(X: torch.Tensor, R: torch.Tensor, k: int, *, return_logits: bool = False,
-                out: dict | None = None) -> dict:
-    """wide_router_topk: X [T, d] bf16, R [n, d] bf16 -> mask uint8 [T, n], packed [T, nw]
-    (int64 view of the uint64 words) and, with ``return_logits``, fp32 logits [T, n]."""
-    _dev(X, torch.bfloat16, "X")
+def pack_router(R: torch.Tensor, out: torch.Tensor | None = None) -> torch.Tensor:
+    """wide_pack_router: R [n, d] bf16 -> fragment order, returned as [ceil(n/16)*16, d]."""
     _dev(R, torch.bfloat16, "R")
+    n, d = R.shape
+    if out is None:
+        out = torch.empty(((n + 15) // 16 * 16, d), dtype=torch.bfloat16, device=R.device)
+    _check("wide_pack_router", lib().wide_pack_router(_ptr(R), n, d, _ptr(out), _stream()))
+    return out
+
+
+def router_topk(X: torch.Tensor, R_packed: torch.Tensor, k: int, n_groups: int, *,
+                return_logits: bool = False, out: dict | None = None) -> dict:
+    """wide_router_topk: X [T, d] bf16 and the router weights packed by pack_router ->
+    mask uint8 [T, n], packed [T, nw] (int64 view of the uint64 words) and, with
+    ``return_logits``, fp32 logits [T, n]."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(R_packed, torch.bfloat16, "R_packed")
     T, d = X.shape
-    n, dr = R.shape
-    if dr != d:
-        raise ValueError("R must be [n_groups, d_model] with the d_model of X")
+    n = n_groups
+    if tuple(R_packed.shape) != ((n + 15) // 16 * 16, d):
+        raise ValueError("R_packed must be pack_router of an [n_groups, d_model] R")
     dev = X.device
     if out is None:
         out = dict(mask=torch.empty((T, n), dtype=torch.uint8, device=dev),
                    packed=torch.empty((T, (n + 63) // 64), dtype=torch.int64, device=dev))
         if return_logits:
             out["logits"] = torch.empty((T, n), dtype=torch.float32, device=dev)
-    st = lib().wide_router_topk(_ptr(X), _ptr(R), T, d, n, k, _ptr(out.get("logits")),
+    st = lib().wide_router_topk(_ptr(X), _ptr(R_packed), T, d, n, k, _ptr(out.get("logits")),
                                 _ptr(out["mask"]), _ptr(out.get("packed")), _stream())
     _check("wide_router_topk", st)
     return out

@@ -250,6 +250,17 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m, uint
   return launch_status();
 }
 
+int wide_pack_router(const uint16_t* R, int n_groups, int d_model, uint16_t* R_packed,
+                     void* stream) {
+  if (n_groups < 1 || d_model <= 0) return WIDE_EINVAL;
+  if (n_groups > WIDE_MAX_GROUPS || d_model % 64 || !fits(n_groups, d_model))
+    return WIDE_EUNSUPPORTED;
+  if (!aligned16(R) || !aligned16(R_packed) || R == R_packed) return WIDE_EINVAL;
+  (void)hipGetLastError();
+  launch_pack_router(R, n_groups, d_model, R_packed, as_stream(stream));
+  return launch_status();
+}
+
 int wide_router_topk(const uint16_t* X, const uint16_t* R, int T, int d_model, int n_groups,
                      int k, float* logits, uint8_t* mask, uint64_t* packed, void* stream) {
   if (T < 0 || d_model <= 0 || n_groups < 1 || k < 0 || k > n_groups) return WIDE_EINVAL;

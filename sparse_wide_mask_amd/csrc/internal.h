@@ -87,8 +87,10 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
                         float* Mpart, float* Lpart, uint16_t* O, hipStream_t s);
 
 // Router logits X R^T and the top-k mask (ties to the lower group index), with
-// the mask's packed bit words; logits and packed may be null.  n <= 256.
-void launch_router_topk(const uint16_t* X, const uint16_t* R, int T, int d, int n, int k,
+// the mask's packed bit words; logits and packed may be null.  n <= 256.  R in
+// fragment order (launch_pack_router: [ceil(n/16)][d/32][64][8]).
+void launch_pack_router(const uint16_t* R, int n, int d, uint16_t* Rp, hipStream_t s);
+void launch_router_topk(const uint16_t* X, const uint16_t* Rp, int T, int d, int n, int k,
                         float* logits, uint8_t* mask, uint64_t* packed, hipStream_t s);
 
 void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, int T, int d, float eps, uint16_t* y,

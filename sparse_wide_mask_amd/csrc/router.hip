@@ -7,6 +7,11 @@
 //                  group index (-0.0 and +0.0 are equal)
 //   packed[t, w] = the mask's little-endian bit words (what the reorder packs)
 //
+// R is used in "fragment order" (wide_pack_router): for every 16-group tile j and
+// 32-wide K step s, the 64 lanes' 16-byte B fragments of v_mfma_f32_16x16x32_bf16
+// are one contiguous 1 KB block, so every work-group's reads of R (all of it, from
+// L2) are whole cache lines instead of 16 rows x 64 bytes.
+//
 // One work-group = 32 tokens, 8 waves.  The 32-wide K steps are dealt to the
 // waves round-robin, so each wave reads only its share of X and R and keeps
 // several steps of loads in flight (K is short and a step's MFMAs are few: the
@@ -21,6 +26,8 @@
 #include "gemm_tile.h"
 #include "internal.h"
 #include "wide.h"
+
+#include <algorithm>
 
 namespace wide {
 
@@ -40,7 +47,7 @@ WIDE_DEV uint32_t order_key(float v) {
 // whose loads are issued together.
 template <int NT, int U>
 __global__ void __launch_bounds__(kRtThreads)
-    router_topk_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ R, int T,
+    router_topk_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Rp, int T,
                        int d, int n, int k, float* __restrict__ logits,
                        uint8_t* __restrict__ mask, uint64_t* __restrict__ packed) {
   constexpr int NG = 16 * NT;
@@ -51,20 +58,21 @@ __global__ void __launch_bounds__(kRtThreads)
   const int rows = min(kRtTok, T - t0);
   const int ch = lane & 15, koff = 8 * (lane >> 4);
   const rsrc_t xr = make_rsrc(X + (size_t)t0 * d, (uint32_t)((size_t)rows * d * 2));
-  const rsrc_t rr = make_rsrc(R, (uint32_t)((size_t)n * d * 2));
+  const int ntiles = (n + 15) / 16, nsteps = d / 32;
+  const rsrc_t rr = make_rsrc(Rp, (uint32_t)((size_t)ntiles * 16 * d * 2));
 
   f32x4 acc[NT][2];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
   // this wave's K steps: wave, wave + 8, ...  (d % 64 == 0: d / 32 is even)
-  const int nsteps = d / 32;
   const int mine = (nsteps - wave + kRtWaves - 1) / kRtWaves;
   for (int i0 = 0; i0 < mine; i0 += U) {
     bf16x8 a[U][2], b[U][NT];
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const bool live = i0 + u < mine;
-      const int col = (wave + kRtWaves * (i0 + u)) * 32 + koff;
+      const int step = wave + kRtWaves * (i0 + u);
+      const int col = step * 32 + koff;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
         const u32x4 v = ldbuf16(xr, live ? (uint32_t)(((rb * 16 + ch) * d + col) * 2) : kSkip);
@@ -72,9 +80,9 @@ __global__ void __launch_bounds__(kRtThreads)
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const int g = j * 16 + ch;
-        const u32x4 v =
-            ldbuf16(rr, live && g < n ? (uint32_t)(((size_t)g * d + col) * 2) : kSkip);
+        const u32x4 v = ldbuf16(rr, live && j < ntiles
+                                        ? (uint32_t)((((size_t)j * nsteps + step) * 64 + lane) * 16)
+                                        : kSkip);
         b[u][j] = *reinterpret_cast<const bf16x8*>(&v);
       }
     }
@@ -171,6 +179,30 @@ __global__ void __launch_bounds__(kRtThreads)
       }
     }
   }
+}
+
+// R [n, d] -> fragment order [ceil(n/16)][d/32][64 lanes][8]: lane l of block
+// (j, s) holds R[16 j + (l mod 16)][32 s + 8 (l / 16) .. +7], zeros past n.
+__global__ void __launch_bounds__(256)
+    pack_router_kernel(const uint16_t* __restrict__ R, int n, int d, uint16_t* __restrict__ Rp) {
+  const int ntiles = (n + 15) / 16, nsteps = d / 32;
+  const size_t total = (size_t)ntiles * nsteps * 64;
+  for (size_t i = blockIdx.x * 256ull + threadIdx.x; i < total; i += (size_t)gridDim.x * 256) {
+    const int l = (int)(i % 64);
+    const size_t js = i / 64;
+    const int s = (int)(js % nsteps), j = (int)(js / nsteps);
+    const int g = j * 16 + (l & 15), k = s * 32 + 8 * (l >> 4);
+    u32x4 v = {0u, 0u, 0u, 0u};
+    if (g < n) v = *reinterpret_cast<const u32x4*>(R + (size_t)g * d + k);
+    *reinterpret_cast<u32x4*>(Rp + i * 8) = v;
+  }
+}
+
+void launch_pack_router(const uint16_t* R, int n, int d, uint16_t* Rp, hipStream_t s) {
+  WIDE_TRACE("pack_router", s);
+  const size_t chunks = (size_t)((n + 15) / 16) * (d / 32) * 64;
+  const int grid = (int)std::min<size_t>((chunks + 255) / 256, 4096);
+  pack_router_kernel<<<grid, 256, 0, s>>>(R, n, d, Rp);
 }
 
 void launch_router_topk(const uint16_t* X, const uint16_t* R, int T, int d, int n, int k,

@@ -87,3 +87,10 @@ def test_masked_cache_decode_validation_before_any_launch(L):
     assert L.wide_attn_decode_masked_cache(*args(4, 4096, C.byref(cfg), 0, 0)) == 1   # no slots
     assert L.wide_attn_decode_masked_cache(*args(65, 4096, C.byref(cfg), 10, 0)) == 2  # batch > 64
     assert L.wide_attn_decode_masked_cache(*args(4, 4096, C.byref(cfg), 10, 0)) == 1   # NULL caches
+
+
+def test_pack_router_validation(L):
+    z = C.c_void_p(0)
+    assert L.wide_pack_router(z, 16, 256, z, z) == 1
+    assert L.wide_pack_router(z, 300, 256, z, z) == 2
+    assert L.wide_pack_router(z, 16, 200, z, z) == 2

@@ -50,9 +50,10 @@ def _check_rows(L, mask, k):
 
 
 def _run(X, R, k, rows=None):
-    Xd, Rd = bf16(X), bf16(R)
-    out = wide.router_topk(Xd, Rd, k, return_logits=True)
-    bare = wide.router_topk(Xd, Rd, k)  # no logits requested: the same selection
+    Xd, Rp = bf16(X), wide.pack_router(bf16(R))
+    n = R.shape[0]
+    out = wide.router_topk(Xd, Rp, k, n, return_logits=True)
+    bare = wide.router_topk(Xd, Rp, k, n)  # no logits requested: the same selection
     torch.cuda.synchronize()
     L = host(out["logits"]).astype(np.float64)
     mask = host(out["mask"])
@@ -110,3 +111,18 @@ def test_router_llama31_8b_full(n, k):
     X, R = _inputs(f"full_{n}", 8192, 4096, n)
     rows = np.random.default_rng(n).choice(8192, 64, replace=False)
     _run(X, R, k, rows=np.sort(rows))
+
+
+@needs_gpu
+@pytest.mark.parametrize("n,d", [(112, 4096), (8, 256), (130, 320), (1, 64)])
+def test_pack_router_is_the_fragment_order(n, d):
+    """Block (j, s), row l of the packed weights is R[16 j + l % 16, 32 s + 8 (l // 16) :+8],
+    zeros past n; checked bit for bit against a NumPy rearrangement."""
+    dev()
+    _, R = _inputs(f"pack_{n}_{d}", 1, d, n)
+    got = host(wide.pack_router(bf16(R))).reshape(-1)
+    nt, ns = (n + 15) // 16, d // 32
+    Rpad = np.zeros((nt * 16, d), np.float32)
+    Rpad[:n] = R
+    ref = Rpad.reshape(nt, 16, ns, 4, 8).transpose(0, 2, 3, 1, 4).reshape(-1)
+    np.testing.assert_array_equal(got, ref)
