@@ -640,7 +640,7 @@ def main():
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
-        print("bench.py runs on one GPU only: this build measures the single-GPU masked path "
+        print("bench.py runs on one GPU only: it measures the single-GPU masked path "
               "(N > 1 is not supported).", file=sys.stderr)
         sys.exit(2)
 

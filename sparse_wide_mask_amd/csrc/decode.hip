@@ -14,17 +14,20 @@
 //                (l=2: row blocks past the count are skipped); the 4 waves split
 //                d_model and reduce through LDS.  FFN: the 16 columns are 8 gate
 //                and the matching 8 up channels, so SwiGLU pairs lanes ch and
-//                ch+8; epilogue writes H.  Attention: RoPE at position kv_len and
-//                the q / new k,v writes (k and v straight into the caches at slot
-//                kv_len).
+//                ch+8; epilogue writes H.  Attention: RoPE at the new token's
+//                position and the q / new k,v writes (k and v straight into the
+//                caches at the pair's slot: the batch's kv_len, or the
+//                (sequence, group)'s own length; see DecCache).
 // kmask_decode   K-masked projection (FFN down, attention out).  One work-group =
-//                16 output columns; it packs the batch's mask into bit words and
-//                their union in LDS, then its 8 waves split the union groups; rows
-//                of tokens that dropped a group are not loaded (l=1).
+//                (128 output columns, one stretch of the batch union's K); it
+//                packs the batch's mask into bit words and their union in LDS,
+//                stages each unit's activation rows in LDS once for its 8 waves
+//                (rows of tokens that dropped a group are not loaded, l=1), and
+//                writes fp32 partial sums that kmask_decode_reduce adds.
 // attn_decode_partial / attn_decode_combine
-//                split-KV attention of each kept (token, group) over cache slots
-//                0..kv_len (the new token included), 256 keys per work-group,
-//                then a log-sum-exp combine of the chunks.
+//                split-KV attention of each kept (token, group) over its cache
+//                slots and the new token, 128 keys per work-group, then a
+//                log-sum-exp combine of the chunks.
 #include <type_traits>
 
 #include "common.h"
