@@ -14,9 +14,10 @@
 //                   Qc [n_kv][r][T][hd], Kc [n_kv][T][hd] and V transposed,
 //                   Vt [n_kv][hd][vtp] (column i = i-th kept token of the group,
 //                   permuted inside 16-key groups; zero up to a whole group).
-// attn_core_prefill one work-group = (group, a heavy and a light tile of 64
-//                   compacted queries), two waves per query head (32 queries
-//                   each, so two waves share each SIMD); K and V^T blocks arrive
+// attn_core_prefill one work-group = (group, one of B bins of its tiles of 64
+//                   compacted queries, dealt heaviest first in snake order),
+//                   two waves per query head (32 queries each, so two waves
+//                   share each SIMD); K and V^T blocks arrive
 //                   by buffer->LDS loads one key step ahead.  S^T = K Q^T puts a query in each lane's column,
 //                   so the online softmax is per lane (+ one cross-half swap) and
 //                   P stays in registers as the B operand of O^T = V^T P^T; V is
@@ -28,6 +29,8 @@
 #include "common.h"
 #include "gemm_tile.h"
 #include "internal.h"
+
+#include <algorithm>
 
 namespace wide {
 
@@ -212,6 +215,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
 constexpr int kBQ = 64;    // queries per tile: 2 waves x 32 per head
 constexpr int kBKey = 64;  // keys per step
 constexpr int kCoreWaves = 8;  // 4 heads x 2 query halves
+constexpr int kCoreCUs = 256;   // compute units of the chip
 // One LDS stage: K block [64 keys][128 hd] (16-byte chunk c of key row k at slot
 // c ^ (k & 15)) and V^T block [128 hd][64 keys] (chunk c of row j at slot
 // c ^ ((j >> 1) & 7)); both 16 KB, filled by buffer->LDS loads.
@@ -221,21 +225,26 @@ constexpr int kStageV = kHd * kBKey;
 __global__ void __launch_bounds__(64 * kCoreWaves, 1)
     attn_core_prefill(const uint16_t* __restrict__ Qc, const uint16_t* __restrict__ Kc,
                       const uint16_t* __restrict__ Vt, const int32_t* __restrict__ gcount,
-                      const int32_t* __restrict__ gperm, int T, int n_kv, int r, int npairs,
+                      const int32_t* __restrict__ gperm, int T, int n_kv, int r, int nbins,
                       int vtp, float scale_log2, uint16_t* __restrict__ O) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kStageK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kStageV];
 
-  // work-group -> (group, pair of query tiles, chunk of 4 query heads).  A pair
-  // is the p-th heaviest and p-th lightest causal tile of the group, so every
-  // work-group of a group does about the same number of key steps.
+  // work-group -> (group, bin j of B = nbins, chunk of 4 query heads).  Query
+  // tile qt of a group takes qt + 1 key steps.  The group's tiles, heaviest
+  // first, are dealt to its B bins in snake order: bin j takes the tiles of rank
+  // j, 2B-1-j, 2B+j, 4B-1-j, ..., so the bins of a group do nearly the same
+  // number of key steps whatever the group's count (with B = half the tiles this
+  // is the heavy + light pairing; a count a little over 2B tiles adds at most one
+  // light tile to a bin instead of a second round of work-groups).  With one
+  // group per XCD, its K and V stay in that XCD's L2.
   const int g = blockIdx.x % n_kv;
   const int rest = blockIdx.x / n_kv;
-  const int p = rest % npairs;
-  const int hc = rest / npairs;
+  const int j = rest % nbins;
+  const int hc = rest / nbins;
   const int cnt = gcount[g];
   const int qtiles = (cnt + kBQ - 1) / kBQ;
-  if (2 * p >= qtiles) return;  // l=0: past the group's kept tokens
+  if (j >= qtiles) return;  // l=0: past the group's kept tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // wave = (head of the chunk, half of the 64 queries): two waves per SIMD
   const int hw = wave & 3, qh = wave >> 2;
@@ -268,9 +277,10 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
     }
   };
 
-  for (int pass = 0; pass < 2; ++pass) {
-    const int qt = pass == 0 ? qtiles - 1 - p : p;
-    if (pass == 1 && qt == qtiles - 1 - p) break;  // the middle tile has no partner
+  for (int it = 0;; ++it) {
+    const int rank = (it >> 1) * 2 * nbins + ((it & 1) ? 2 * nbins - 1 - j : j);
+    if (rank >= qtiles) break;
+    const int qt = qtiles - 1 - rank;
     const int q0 = qt * kBQ;
     const int q_last = min(cnt, q0 + kBQ) - 1;
     const int nkb = q_last / kBKey + 1;
@@ -433,12 +443,16 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
     attn_qkv_prefill<<<n_kv * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
                                                          r, mtiles, vtp, log2_theta, Qc, Kc, Vt);
   }
+  // bins per group: half the most tiles a group can have, but no more than fill
+  // the CUs once (256 CUs, one work-group each)
+  const int hcs = (r + 3) / 4;
   const int npairs = ((T + kBQ - 1) / kBQ + 1) / 2;
+  const int nbins = std::max(1, std::min(npairs, kCoreCUs / (n_kv * hcs)));
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHd);
   {
     WIDE_TRACE("attn_core_prefill", s);
-    attn_core_prefill<<<npairs * n_kv * ((r + 3) / 4), 64 * kCoreWaves, 0, s>>>(
-        Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, npairs, vtp, scale_log2, O);
+    attn_core_prefill<<<nbins * n_kv * hcs, 64 * kCoreWaves, 0, s>>>(
+        Qc, Kc, Vt, rv.count, rv.perm, T, n_kv, r, nbins, vtp, scale_log2, O);
   }
 }
 

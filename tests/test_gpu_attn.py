@@ -39,6 +39,11 @@ SHAPES = [
     (333, 256, 8, 2, 1.0, "ones", 500000.0),
     (190, 256, 8, 2, 0.0, "zeros", 0.0),
     (1100, 256, 8, 8, 0.5, "topk", 500000.0),
+    # many groups: fewer bins per group than tile pairs, so a bin takes 3 or more
+    # query tiles in snake order (8 bins of 32 tiles; 4 bins; 16 bins of 35 tiles)
+    (2048, 256, 32, 32, 1.0, "ones", 500000.0),
+    (1500, 256, 64, 64, 0.75, "bernoulli", 0.0),
+    (2200, 256, 64, 16, 1.0, "ones", 10000.0),
 ]
 
 
