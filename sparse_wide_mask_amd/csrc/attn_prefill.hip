@@ -17,11 +17,16 @@
 // attn_core_prefill one work-group = (group, one of B bins of its tiles of 64
 //                   compacted queries, dealt heaviest first in snake order),
 //                   two waves per query head (32 queries each, so two waves
-//                   share each SIMD); K and V^T blocks arrive
-//                   by buffer->LDS loads one key step ahead.  S^T = K Q^T puts a query in each lane's column,
-//                   so the online softmax is per lane (+ one cross-half swap) and
-//                   P stays in registers as the B operand of O^T = V^T P^T; V is
-//                   read in the key order the S^T accumulator layout gives.
+//                   share each SIMD); K and V^T blocks arrive by buffer->LDS
+//                   loads one key step ahead.  S^T = K Q^T puts a query in each
+//                   lane's column, so the softmax is per lane (+ one cross-half
+//                   swap, v_permlane32_swap) and P
+//                   stays in registers as the B operand of O^T = V^T P^T; V is
+//                   read in the key order the S^T accumulator layout gives.  A
+//                   row's reference max is fixed by its first keys, so O is never
+//                   rescaled in the key loop; a tile in which some row's scores
+//                   outgrow it by the headroom is recomputed once with the true
+//                   row maxima.
 //                   Output O is written token-major [T, n_q*hd] at the kept
 //                   (token, group) blocks only.
 // The O projection is the K-masked GEMM of the FFN down projection with group
@@ -221,6 +226,17 @@ constexpr int kCoreCUs = 256;   // compute units of the chip
 // c ^ ((j >> 1) & 7)); both 16 KB, filled by buffer->LDS loads.
 constexpr int kStageK = kBKey * kHd;  // elements
 constexpr int kStageV = kHd * kBKey;
+// P = 2^(s scale - m) may reach 2^kPHeadroom above the reference max m: bf16 P
+// and the fp32 sums stay finite
+constexpr float kPHeadroom = 64.f;
+
+// The values of x in lanes l and l ^ 32, in some order (v_permlane32_swap).
+WIDE_DEV void xhalf(float x, float& a, float& b) {
+  const auto v =
+      __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  a = __uint_as_float(v[0]);
+  b = __uint_as_float(v[1]);
+}
 
 __global__ void __launch_bounds__(64 * kCoreWaves, 1)
     attn_core_prefill(const uint16_t* __restrict__ Qc, const uint16_t* __restrict__ Kc,
@@ -229,6 +245,7 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
                       int vtp, float scale_log2, uint16_t* __restrict__ O) {
   __shared__ __attribute__((aligned(16))) uint16_t sK[2 * kStageK];
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kStageV];
+  __shared__ int sRedo;  // some wave's rows outgrew their reference max
 
   // work-group -> (group, bin j of B = nbins, chunk of 4 query heads).  Query
   // tile qt of a group takes qt + 1 key steps.  The group's tiles, heaviest
@@ -285,8 +302,6 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
     const int q_last = min(cnt, q0 + kBQ) - 1;
     const int nkb = q_last / kBKey + 1;
     const int q = q0 + 32 * qh + c0;  // this lane's query (its S^T column)
-    lds_barrier();  // the previous tile's last stage reads are done
-    issue(0, 0);
 
     // Q^T fragments as B operands: lane holds query q, hd 16 ks + 8 half.
     bf16x8 qf[8];
@@ -299,116 +314,126 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
         qf[ks] = bf16x8{};
     }
     f32x16 o[4];  // O^T: 4 hd blocks x this wave's 32 queries
+    float l_run;
+    // The reference max m of a query is the max of its first keys (O and l are
+    // still 0 then) and is not raised afterwards, so O is never rescaled inside
+    // the key loop (O / l is the same for any common offset).  A later score
+    // more than kPHeadroom above m sets `over`; then the tile is computed again
+    // with the true row max (m_true, tracked in the first pass) as m, which no
+    // score exceeds, so there are at most two passes.
+    float m_ref = -INFINITY, m_true = -INFINITY;
+    for (int pass = 0; pass < 2; ++pass) {
+      lds_barrier();  // the previous pass's or tile's last stage reads are done
+      if (tid == 0) sRedo = 0;
+      issue(0, 0);
 #pragma unroll
-    for (int a = 0; a < 4; ++a)
+      for (int a = 0; a < 4; ++a)
 #pragma unroll
-      for (int e = 0; e < 16; ++e) o[a][e] = 0.f;
-    float m_run = -INFINITY, l_run = 0.f;
+        for (int e = 0; e < 16; ++e) o[a][e] = 0.f;
+      l_run = 0.f;
+      bool over = false;
 
-    for (int kb = 0; kb < nkb; ++kb) {
-      const int k0 = kb * kBKey, st = kb & 1;
-      // every wave's loads of block kb have landed (this wave's 4 loads of block
-      // kb + 1 may stay in flight)
-      if (kb + 1 < nkb) {
-        issue(kb + 1, st ^ 1);
-        stage_barrier<4>();
-      } else {
-        stage_barrier<0>();
-      }
-      const uint16_t* cK = sK + st * kStageK;
-      const uint16_t* cV = sV + st * kStageV;
-      auto kfrag = [&](int ks, int a) {
-        const int row = a * 32 + c0;
-        return *reinterpret_cast<const bf16x8*>(cK + row * kHd +
-                                                (((2 * ks + half) ^ (row & 15)) * 8));
-      };
-      auto vfrag = [&](int a, int sp, int hb) {
-        const int row = hb * 32 + c0, chunk = 2 * (2 * a + sp) + half;
-        return *reinterpret_cast<const bf16x8*>(cV + row * kBKey +
-                                                ((chunk ^ ((row >> 1) & 7)) * 8));
-      };
-      // the stage's two 32-key halves in turn
-#pragma unroll
-      for (int a = 0; a < 2; ++a) {
-        const int kk0 = k0 + a * 32;
-        // S^T [32 keys x 32 queries] = K Q^T; the K fragment of step ks + 1 is read
-        // from LDS before the MFMA of step ks
-        f32x16 s;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) s[e] = 0.f;
-        bf16x8 kc = kfrag(0, a);
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-          bf16x8 kn;
-          if (ks < 7) kn = kfrag(ks + 1, a);
-          s = mfma32(kc, qf[ks], s);
-          if (ks < 7) kc = kn;
+      for (int kb = 0; kb < nkb; ++kb) {
+        const int k0 = kb * kBKey, st = kb & 1;
+        // every wave's loads of block kb have landed (this wave's 4 loads of block
+        // kb + 1 may stay in flight)
+        if (kb + 1 < nkb) {
+          issue(kb + 1, st ^ 1);
+          stage_barrier<4>();
+        } else {
+          stage_barrier<0>();
         }
-        // the V^T fragments of the first P V step, read while the softmax runs
-        bf16x8 vc[4];
+        const uint16_t* cK = sK + st * kStageK;
+        const uint16_t* cV = sV + st * kStageV;
+        auto kfrag = [&](int ks, int a) {
+          const int row = a * 32 + c0;
+          return *reinterpret_cast<const bf16x8*>(cK + row * kHd +
+                                                  (((2 * ks + half) ^ (row & 15)) * 8));
+        };
+        auto vfrag = [&](int a, int sp, int hb) {
+          const int row = hb * 32 + c0, chunk = 2 * (2 * a + sp) + half;
+          return *reinterpret_cast<const bf16x8*>(cV + row * kBKey +
+                                                  ((chunk ^ ((row >> 1) & 7)) * 8));
+        };
+        // the stage's two 32-key halves in turn
 #pragma unroll
-        for (int hb = 0; hb < 4; ++hb) vc[hb] = vfrag(a, 0, hb);
+        for (int a = 0; a < 2; ++a) {
+          const int kk0 = k0 + a * 32;
+          // S^T [32 keys x 32 queries] = K Q^T; the K fragment of step ks + 1 is read
+          // from LDS before the MFMA of step ks
+          f32x16 s;
+#pragma unroll
+          for (int e = 0; e < 16; ++e) s[e] = 0.f;
+          bf16x8 kc = kfrag(0, a);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            bf16x8 kn;
+            if (ks < 7) kn = kfrag(ks + 1, a);
+            s = mfma32(kc, qf[ks], s);
+            if (ks < 7) kc = kn;
+          }
+          // the V^T fragments of the first P V step, read while the softmax runs
+          bf16x8 vc[4];
+#pragma unroll
+          for (int hb = 0; hb < 4; ++hb) vc[hb] = vfrag(a, 0, hb);
 
-        // online softmax in the log2 domain.  Masks (causal in compacted order,
-        // keys past the count) only on the blocks that need them.  The running
-        // max is raised only when a score exceeds it by more than 8 (2^8 headroom
-        // for P in bf16 and the fp32 sums), so O and l are rescaled rarely; O / l
-        // is the same for any common offset.
-        if (kk0 + 32 > q0 || kk0 + 32 > cnt) {
+          // softmax numerators in the log2 domain.  Masks (causal in compacted
+          // order, keys past the count) only on the blocks that need them.
+          if (kk0 + 32 > q0 || kk0 + 32 > cnt) {
+#pragma unroll
+            for (int e = 0; e < 16; ++e) {
+              const int key = kk0 + acc32_row(lane, e);
+              if (key > q || key >= cnt) s[e] = -INFINITY;
+            }
+          }
+          float mx = s[0];
+#pragma unroll
+          for (int e = 1; e < 16; ++e) mx = fmaxf(mx, s[e]);
+          float xa, xb;
+          xhalf(mx, xa, xb);
+          mx = fmaxf(xa, xb) * scale_log2;
+          m_ref = m_ref == -INFINITY ? mx : m_ref;
+          m_true = fmaxf(m_true, mx);
+          over = over || mx > m_ref + kPHeadroom;
+          // a query with no finite score yet keeps a finite state
+          const float m_use = m_ref == -INFINITY ? 0.f : m_ref;
+          float sum = 0.f;
 #pragma unroll
           for (int e = 0; e < 16; ++e) {
-            const int key = kk0 + acc32_row(lane, e);
-            if (key > q || key >= cnt) s[e] = -INFINITY;
+            const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -m_use));
+            s[e] = pe;
+            sum += pe;
+          }
+          xhalf(sum, xa, xb);
+          l_run += xa + xb;
+          // O^T [128 x 32] += V^T [128 x 32 keys] P^T [32 keys x 32 q].  The k-slots
+          // of a lane are the keys its S^T registers hold, 16 s' + 4 half +
+          // {0..3, 8..11}; the permuted V^T layout stores exactly those 8 keys as
+          // chunk 2 (2 a + s') + half.
+#pragma unroll
+          for (int sp = 0; sp < 2; ++sp) {
+            bf16x8 vn[4];
+            if (sp == 0) {
+#pragma unroll
+              for (int hb = 0; hb < 4; ++hb) vn[hb] = vfrag(a, 1, hb);
+            }
+            bf16x8 pf;
+#pragma unroll
+            for (int k = 0; k < 8; ++k) pf[k] = (__bf16)s[8 * sp + k];
+#pragma unroll
+            for (int hb = 0; hb < 4; ++hb) o[hb] = mfma32(vc[hb], pf, o[hb]);
+            if (sp == 0) {
+#pragma unroll
+              for (int hb = 0; hb < 4; ++hb) vc[hb] = vn[hb];
+            }
           }
         }
-        float mx = -INFINITY;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) mx = fmaxf(mx, s[e]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32)) * scale_log2;
-        const bool grow = mx > m_run + 8.f;
-        if (ballot(grow)) {
-          const float m_set = grow ? mx : m_run;
-          const float corr = m_set == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_set);
-          l_run *= corr;
-          m_run = m_set;
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb)
-#pragma unroll
-            for (int e = 0; e < 16; ++e) o[hb][e] *= corr;
-        }
-        // a query past the count has no finite score; keep its state finite
-        const float m_use = m_run == -INFINITY ? 0.f : m_run;
-        float sum = 0.f;
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const float pe = __builtin_amdgcn_exp2f(fmaf(s[e], scale_log2, -m_use));
-          s[e] = pe;
-          sum += pe;
-        }
-        l_run += sum + __shfl_xor(sum, 32);
-        // O^T [128 x 32] += V^T [128 x 32 keys] P^T [32 keys x 32 q].  The k-slots
-        // of a lane are the keys its S^T registers hold, 16 s' + 4 half +
-        // {0..3, 8..11}; the permuted V^T layout stores exactly those 8 keys as
-        // chunk 2 (2 a + s') + half.
-#pragma unroll
-        for (int sp = 0; sp < 2; ++sp) {
-          bf16x8 vn[4];
-          if (sp == 0) {
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) vn[hb] = vfrag(a, 1, hb);
-          }
-          bf16x8 pf;
-#pragma unroll
-          for (int k = 0; k < 8; ++k) pf[k] = (__bf16)s[8 * sp + k];
-#pragma unroll
-          for (int hb = 0; hb < 4; ++hb) o[hb] = mfma32(vc[hb], pf, o[hb]);
-          if (sp == 0) {
-#pragma unroll
-            for (int hb = 0; hb < 4; ++hb) vc[hb] = vn[hb];
-          }
-        }
+        lds_barrier();  // stage st is refilled by the next step's loads
       }
-      lds_barrier();  // stage st is refilled by the next step's loads
+      if (ballot(over) && lane == 0) sRedo = 1;
+      __syncthreads();
+      if (sRedo == 0) break;
+      m_ref = m_true;
     }
 
     // O[token, h*hd + j] = O^T[j][q] / l

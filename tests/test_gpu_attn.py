@@ -70,3 +70,43 @@ def test_attn_prefill_llama31_8b_full():
     got = _gpu_attn(c, 0.0)
     ref = _oracle(c, 0.0)
     assert rel_err(got, ref) <= TOL
+
+
+@needs_gpu
+def test_attn_prefill_outlier_key_second_pass():
+    """One token's input scaled by 2^11 gives a key whose scores rise far above the
+    first keys' scores of most later rows, past the softmax headroom of the core's
+    first pass: those tiles are computed again with the true row max.  Every row
+    must be finite.  The check is per row, on the rows whose softmax is well
+    conditioned at this scale (in every head the outlier key's score is 30+ log2
+    units above or below all other keys' scores; elsewhere bf16 rounding of the
+    huge key moves the mix by more than the tolerance).  They include the rows
+    before the outlier and more than a hundred rows that need the second pass."""
+    dev()
+    log("attn prefill, outlier key")
+    T, d, n_q, n_kv, big = 300, 256, 8, 2, 70
+    c = dict(attn_case("attn_outlier", T, d, n_q, n_kv, 128, 1.0, "ones"))
+    X = c["X"].copy()
+    X[big] *= 2048.0  # exact in bf16
+    c["X"] = X
+    got = _gpu_attn(c, 0.0)
+    assert np.all(np.isfinite(got))
+    ref = _oracle(c, 0.0)
+    Xd = X.astype(np.float64)
+    Q = (Xd @ c["Wq"].T.astype(np.float64)).reshape(T, n_q, 128)
+    K = (Xd @ c["Wk"].T.astype(np.float64)).reshape(T, n_kv, 128)
+    scale = np.log2(np.e) / np.sqrt(128)
+    good = np.ones(T, bool)
+    second = np.zeros(T, bool)
+    for h in range(n_q):
+        S = (Q[:, h] @ K[:, h // (n_q // n_kv)].T) * scale
+        for t in range(big + 1, T):
+            row = S[t, :t + 1]
+            if abs(row[big] - np.delete(row, big).max()) < 30:
+                good[t] = False
+            second[t] |= row.max() > row[:32].max() + 64
+    good[big] = False
+    assert good[:big].all() and (good & second).sum() > 100
+    rows = np.flatnonzero(good)
+    err = np.abs(got[rows] - ref[rows]).max(axis=1) / np.abs(ref[rows]).max(axis=1)
+    assert err.max() <= TOL
