@@ -8,7 +8,10 @@
 //      and their MFMA row blocks are skipped (l=2).  B interleaves 32-channel
 //      slabs of W_gate and W_up so each lane holds gate and up of the same
 //      (token, channel) and applies silu(gate) * up in registers.  H is written
-//      token-major [T, d_ff] at the kept blocks only.
+//      token-major [T, d_ff] at the kept blocks only.  A group's last tile of at
+//      most 64 rows is done by one of the grid's last work-groups with 64-row
+//      tiles and three LDS stages, on a compute unit that is done with its full
+//      tiles.
 // down (K-masked): one output tile = (256 consecutive tokens, 256 columns of
 //      d_model); K runs over the groups that some token of the tile keeps
 //      (tile_groups, l=0 for the others), G channels each.  A rows of tokens that
@@ -18,6 +21,8 @@
 #include "common.h"
 #include "gemm_tile.h"
 #include "internal.h"
+
+#include <type_traits>
 
 namespace wide {
 
@@ -44,36 +49,36 @@ WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& m
   __shared__ __attribute__((aligned(16))) uint16_t sB[kStages * C::SB];      \
   const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB)
 
-template <int BM, int BN>
-__global__ void __launch_bounds__(kGemmThreads, 1)
-    ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
-                   const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gcount,
-                   const int32_t* __restrict__ gperm, int T, int d, int F, int n, int G,
-                   int mtiles, int ntn, uint16_t* __restrict__ H) {
-  using C = TileCfg<BM, BN>;
+// A group's last row tile with at most this many rows is left by ffn_up_prefill
+// to ffn_up_tail (64-row tiles, three LDS stages).  Such a tile streams all of the
+// group's weight columns for a few rows; with two 256-row stages in flight it is
+// bound by load latency and takes most of a full tile's time, in the last round.
+constexpr int kUpTailRows = 64;
+
+// One output tile of the up projection: rows row0 .. row0 + rows - 1 of group g's
+// kept-token list, channel tile nt.  NS = LDS stages (2 or 3).
+template <int BM, int BN, int NWM, int NWN, int NS>
+WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
+                          const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gperm,
+                          int T, int d, int F, int G, int g, int row0, int rows, int nt,
+                          uint16_t* sA, uint16_t* sB, int* sTok, uint16_t* __restrict__ H) {
+  using C = TileCfg<BM, BN, NWM, NWN>;
+  constexpr int NW = C::kWaves;
   constexpr int BNH = BN / 2;  // channels per tile (gate and up each)
-  WIDE_STAGE_ARRAYS(C);
-  __shared__ int sTok[BM];
+  const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB);
 
-  int g, mt, nt;
-  up_tile(blockIdx.x, n, mtiles, ntn, g, mt, nt);
-  const int cnt = gcount[g];
-  const int row0 = mt * BM;
-  if (row0 >= cnt) return;  // l=0: no kept token left in this tile
-  const int rows = min(BM, cnt - row0);
-
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / NWN, wn = wave % NWN;
   for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gperm[(size_t)g * T + row0 + r] : -1;
   __syncthreads();
 
-  const int chunk8 = dma_chunk(dma_row(wave, 0, lane), lane) * 8;
+  const int chunk8 = dma_chunk(dma_row<NW>(wave, 0, lane), lane) * 8;
   const i32x4 rX = make_srd(X, (uint32_t)T * d * 2u);
   const i32x4 rG = make_srd(Wg, (uint32_t)F * d * 2u);
   const i32x4 rU = make_srd(Wu, (uint32_t)F * d * 2u);
   uint32_t aOff[C::A_INST];
 #pragma unroll
   for (int q = 0; q < C::A_INST; ++q) {
-    const int tok = sTok[dma_row(wave, q, lane)];
+    const int tok = sTok[dma_row<NW>(wave, q, lane)];
     aOff[q] = tok >= 0 ? (uint32_t)(tok * d + chunk8) * 2u : kSkip;  // l=1: no load
   }
   // B row nrow: wave column nrow / WN; 32-row slabs alternate gate / up so that a
@@ -82,7 +87,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   int bUp[C::B_INST];
 #pragma unroll
   for (int q = 0; q < C::B_INST; ++q) {
-    const int nrow = dma_row(wave, q, lane);
+    const int nrow = dma_row<NW>(wave, q, lane);
     const int w = nrow / C::WN, local = nrow % C::WN, blk = local >> 5;
     const int ch = nt * BNH + w * (C::WN / 2) + (blk >> 1) * 32 + (local & 31);
     bOff[q] = (uint32_t)((g * G + ch) * d + chunk8) * 2u;
@@ -92,9 +97,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
     const uint32_t kb = (uint32_t)kt * kBK * 2u;
 #pragma unroll
-    for (int q = 0; q < C::A_INST; ++q) lds_dma16(rX, dma_dst(a, wave, q), aOff[q] + kb);
+    for (int q = 0; q < C::A_INST; ++q) lds_dma16(rX, dma_dst<NW>(a, wave, q), aOff[q] + kb);
 #pragma unroll
-    for (int q = 0; q < C::B_INST; ++q) lds_dma16(bUp[q] ? rU : rG, dma_dst(b, wave, q), bOff[q] + kb);
+    for (int q = 0; q < C::B_INST; ++q)
+      lds_dma16(bUp[q] ? rU : rG, dma_dst<NW>(b, wave, q), bOff[q] + kb);
   };
 
   uint32_t rb_live = 0;
@@ -102,14 +108,21 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   for (int i = 0; i < C::RB; ++i)
     if (wm * C::WM + i * 32 < rows) rb_live |= 1u << i;
 
-  WaveAcc<BM, BN> acc;
+  WaveAcc<BM, BN, NWM, NWN> acc;
   acc.zero();
   const int nk = d / kBK;
   auto live = [&](int) { return rb_live; };
+  auto run = [&](auto all_tag) {
+    constexpr bool ALL = decltype(all_tag)::value;
+    if constexpr (NS == 3)
+      acc.template run3<ALL, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+    else
+      acc.template run<ALL, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+  };
   if (rb_live == C::kAllRows)  // every row block of this wave holds kept rows
-    acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+    run(std::true_type{});
   else  // tail tile of the group: l=2 skips the row blocks with no kept token
-    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+    run(std::false_type{});
 
   // epilogue: H[token, gG + ch] = silu(gate) * up, 32-bit byte offsets into H
   // (T F 2 < 2^31); rows past the count only exist in a group's last tile
@@ -136,6 +149,52 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     store(true);
   else
     store(false);
+}
+
+// Tail tiles: 64 rows in a 2 x 4 wave layout (each wave still holds gate and up
+// of its 32 channels), three LDS stages.
+constexpr int kTailNWM = 2, kTailNWN = 4, kTailStages = 3;
+using TailCfg = TileCfg<kUpTailRows, 256, kTailNWM, kTailNWN>;
+static_assert(TailCfg::kThreads == kGemmThreads, "one launch shape");
+
+// The up projection.  Work-groups below n_main take the row tiles (up_tile) but,
+// when TAILS, not a group's last tile of at most kUpTailRows rows; the n * ntn
+// work-groups after them take exactly those tails, one per (group, channel tile).
+// Being last in the grid, the tails run on the compute units that finish their
+// share of full tiles first.
+template <int BM, int BN, bool TAILS>
+__global__ void __launch_bounds__(kGemmThreads, 1)
+    ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
+                   const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gcount,
+                   const int32_t* __restrict__ gperm, int T, int d, int F, int n, int G,
+                   int mtiles, int ntn, int n_main, uint16_t* __restrict__ H) {
+  using C = TileCfg<BM, BN>;
+  constexpr int kMain = kStages * (C::SA + C::SB);
+  constexpr int kTail = TAILS ? kTailStages * (TailCfg::SA + TailCfg::SB) : 0;
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[kMain > kTail ? kMain : kTail];
+  __shared__ int sTok[BM];
+  if (TAILS && (int)blockIdx.x >= n_main) {
+    const int id = blockIdx.x - n_main;
+    const int g = id / ntn, nt = id % ntn;
+    const int cnt = gcount[g];
+    if (cnt == 0) return;
+    const int row0 = (cnt - 1) / BM * BM;  // the group's last row tile
+    const int rows = cnt - row0;
+    if (rows > kUpTailRows) return;  // a large last tile is a row tile like the others
+    ffn_up_tile<kUpTailRows, 256, kTailNWM, kTailNWN, kTailStages>(
+        X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
+        sbuf + kTailStages * TailCfg::SA, sTok, H);
+    return;
+  }
+  int g, mt, nt;
+  up_tile(blockIdx.x, n, mtiles, ntn, g, mt, nt);
+  const int cnt = gcount[g];
+  const int row0 = mt * BM;
+  if (row0 >= cnt) return;  // l=0: no kept token left in this tile
+  const int rows = min(BM, cnt - row0);
+  if (TAILS && row0 + BM >= cnt && rows <= kUpTailRows) return;  // a tail work-group's
+  ffn_up_tile<BM, BN, kGemmWM, kGemmWN, kStages>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt,
+                                                  sbuf, sbuf + kStages * C::SA, sTok, H);
 }
 
 template <int BM, int BN, int USE>
@@ -357,16 +416,18 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
     {
       WIDE_TRACE("ffn_up_prefill", s);
-      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
-                                                               n, G, mtiles, ntn, H);
+      const int n_main = n * mtiles * ntn;
+      ffn_up_prefill<BM, BN, true><<<n_main + n * ntn, kGemmThreads, 0, s>>>(
+          X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   } else {
     constexpr int BM = 256, BN = 128;
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
     {
       WIDE_TRACE("ffn_up_prefill", s);
-      ffn_up_prefill<BM, BN><<<n * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wg, Wu, rv.count, rv.perm, T, d, F,
-                                                               n, G, mtiles, ntn, H);
+      const int n_main = n * mtiles * ntn;
+      ffn_up_prefill<BM, BN, false><<<n_main, kGemmThreads, 0, s>>>(
+          X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   }
   launch_kmask_gemm(kUseFfnDown, H, Wdp, rv, T, d, F, n, residual, Y, s);

@@ -205,6 +205,57 @@ struct WaveAcc {
       __builtin_amdgcn_sched_barrier(0);
     }
   }
+
+  // Three stages: slices kt+1 and kt+2 load while slice kt computes (for tiles
+  // whose few rows leave room in LDS, so that streaming B has more loads in
+  // flight).  Stage of slice kt = kt mod 3; slice kt+2 refills the stage that
+  // slice kt-1 used, whose reads all waves finished before the last barrier.
+  template <bool ALL, int LOADS, class Issue, class Live>
+  WIDE_DEV void run3(int nk, const uint16_t* sA, const uint16_t* sB, int wm, int wn, int lane,
+                     Issue&& issue, Live&& live) {
+    if (nk <= 0) return;
+    issue(0, 0);
+    if (nk > 1) {
+      issue(1, 1);
+      stage_barrier<LOADS>();
+    } else {
+      stage_barrier<0>();
+    }
+    Frags lo, hi;
+    read(lo, sA, sB, wm, wn, lane, 0);
+    int st = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const uint32_t lv = ALL ? C::kAllRows : live(kt);
+      const uint16_t* cA = sA + st * C::SA;
+      const uint16_t* cB = sB + st * C::SB;
+      const int st1 = st == 2 ? 0 : st + 1, st2 = st1 == 2 ? 0 : st1 + 1;
+      if (kt + 2 < nk) issue(kt + 2, st2);
+      read(hi, cA, cB, wm, wn, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(lo, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      read(lo, cA, cB, wm, wn, lane, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(hi, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      read(hi, cA, cB, wm, wn, lane, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(lo, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
+        // slice kt+1 has landed (slice kt+2 may stay in flight)
+        if (kt + 2 < nk)
+          stage_barrier<LOADS>();
+        else
+          stage_barrier<0>();
+        read(lo, sA + st1 * C::SA, sB + st1 * C::SB, wm, wn, lane, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(hi, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      st = st1;
+    }
+  }
 };
 
 }  // namespace wide
