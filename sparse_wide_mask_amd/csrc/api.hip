@@ -3,6 +3,8 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <mutex>
+
 #include "../../include/wide.h"
 #include "internal.h"
 
@@ -94,13 +96,15 @@ FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
   return w;
 }
 
+// reorder = false: the mask reorder of this call was already enqueued (by the
+// layer, on its side stream)
 int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const uint16_t* Wu,
             const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
-            uint16_t* Y, const FfnWs& w, hipStream_t s) {
+            uint16_t* Y, const FfnWs& w, hipStream_t s, bool reorder = true) {
   if (ffn_streaming(T, mode)) {
     launch_ffn_decode(X, mask, Wg, Wu, Wdp, T, d, F, n, residual, w.H, w.kpart, Y, s);
   } else {
-    run_reorder(mask, T, n, w.rv, s);
+    if (reorder) run_reorder(mask, T, n, w.rv, s);
     launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
   }
   return WIDE_OK;
@@ -162,11 +166,26 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
   return w;
 }
 
+// Prefill: group partitions for the QKV projection and the core; for the O
+// projection with few groups, tiles of tokens sorted by their head-group
+// pattern, so that row blocks and whole tiles share dropped groups.
+void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s) {
+  if (nkv <= kSortMaxGroups) {
+    launch_reorder(mask, T, nkv, w.rv.tile_m, w.rv.packed, w.rv.count, w.rv.perm, w.rv.rank,
+                   nullptr, nullptr, s);
+    launch_token_sort(w.rv.packed, T, nkv, w.rv.tile_m, w.rv.order, w.rv.tile_count,
+                      w.rv.tile_groups, s);
+  } else {
+    run_reorder(mask, T, nkv, w.rv, s);
+  }
+}
+
+// reorder = false: attn_reorder of this call was already enqueued
 void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
               const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
               int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
               const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s,
-              const int32_t* pair_len = nullptr, int pos = -1) {
+              const int32_t* pair_len = nullptr, int pos = -1, bool reorder = true) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
@@ -176,22 +195,42 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
                         Y, s);
     return;
   }
-  // group partitions for the QKV projection and the core; for the O projection
-  // with few groups, tiles of tokens sorted by their head-group pattern, so that
-  // row blocks and whole tiles share dropped groups
-  if (nkv <= kSortMaxGroups) {
-    launch_reorder(mask, T, nkv, w.rv.tile_m, w.rv.packed, w.rv.count, w.rv.perm, w.rv.rank,
-                   nullptr, nullptr, s);
-    launch_token_sort(w.rv.packed, T, nkv, w.rv.tile_m, w.rv.order, w.rv.tile_count,
-                      w.rv.tile_groups, s);
-  } else {
-    run_reorder(mask, T, nkv, w.rv, s);
-  }
+  if (reorder) attn_reorder(mask, T, nkv, w, s);
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
   launch_kmask_gemm(kUseAttnO, w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
 }
 
 // -------------------------------------------------------------------- layer
+
+// A second stream per device for the work of a layer call that reads only the
+// call's inputs (the two mask reorders): it runs beside the first RMSNorm and
+// the attention sublayer, and events join it back to the caller's stream before
+// the kernels that consume it.  Default priority.  Created on first use; the
+// events are shared, so a layer call enqueues under a lock.
+struct SideStream {
+  hipStream_t s = nullptr;
+  hipEvent_t fork = nullptr, attn_done = nullptr, ffn_done = nullptr;
+  bool tried = false, ok = false;
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;
+
+// The current device's side stream, or nullptr if it cannot be made (the layer
+// then runs on the caller's stream alone).  g_side_mu must be held.
+SideStream* side_stream() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  SideStream& x = g_side[dev];
+  if (!x.tried) {
+    x.tried = true;
+    x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
+           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&x.attn_done, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&x.ffn_done, hipEventDisableTiming) == hipSuccess;
+  }
+  return x.ok ? &x : nullptr;
+}
 
 int layer_check(int T, const wide_layer_cfg* cfg, int mode) {
   if (!cfg) return WIDE_EINVAL;
@@ -421,6 +460,28 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
   const int d = cfg->d_model;
   hipStream_t s = as_stream(stream);
   (void)hipGetLastError();
+  if (mode == WIDE_PREFILL) {
+    // the mask reorders on the side stream, beside RMSNorm and attention
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = side_stream();
+    if (side && hipEventRecord(side->fork, s) == hipSuccess &&
+        hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess) {
+      attn_reorder(attn_mask, T, cfg->attn.n_kv_heads, w.attn, side->s);
+      if (hipEventRecord(side->attn_done, side->s) != hipSuccess) return WIDE_EHIP;
+      run_reorder(ffn_mask, T, cfg->n_ffn_groups, w.ffn.rv, side->s);
+      if (hipEventRecord(side->ffn_done, side->s) != hipSuccess) return WIDE_EHIP;
+      launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
+      if (hipStreamWaitEvent(s, side->attn_done, 0) != hipSuccess) return WIDE_EHIP;
+      attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode,
+               K_cache, V_cache, kv_len, kv_cap, X, w.h, w.attn, s, nullptr, -1, false);
+      launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
+      if (hipStreamWaitEvent(s, side->ffn_done, 0) != hipSuccess) return WIDE_EHIP;
+      ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff,
+              cfg->n_ffn_groups, mode, w.h, Y, w.ffn, s, false);
+      return launch_status();
+    }
+    (void)hipGetLastError();
+  }
   launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
   attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode, K_cache,
            V_cache, kv_len, kv_cap, X, w.h, w.attn, s);
