@@ -66,40 +66,26 @@ struct RopeFreq {
   }
 };
 
-__global__ void __launch_bounds__(kGemmThreads, 1)
-    attn_qkv_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
-                     const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
-                     const int32_t* __restrict__ gcount, const int32_t* __restrict__ gperm, int T,
-                     int d, int n_kv, int r, int mtiles, int vtp, float log2_theta,
-                     uint16_t* __restrict__ Qc, uint16_t* __restrict__ Kc,
-                     uint16_t* __restrict__ Vt) {
-  constexpr int BM = 256, BN = 256;
-  using C = TileCfg<BM, BN>;
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages * C::SA];
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages * C::SB];
+// One tile of the QKV projection: rows row0 .. row0 + rows - 1 of group g's
+// kept-token list (at most 256), and BN / 128 heads of the 256-column tile nt of
+// the group's (q heads | k, v) columns, starting at head hsel0 of that tile.
+// Waves: 256 / (8 / NWN) rows x one 128-column head each, so the RoPE pair
+// (j, j + 64) of a head sits in one lane.
+template <int BN, int NWN>
+WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
+                       const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
+                       const int32_t* __restrict__ gperm, int T, int d, int n_kv, int r, int g,
+                       int row0, int rows, int nt, int hsel0, int vtp, float log2_theta,
+                       uint16_t* sA, uint16_t* sB, int* sTok, uint16_t* __restrict__ Qc,
+                       uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vt) {
+  constexpr int BM = 256, NWM = 8 / NWN;
+  using C = TileCfg<BM, BN, NWM, NWN>;
+  static_assert(C::WN == kHd, "one head per wave column");
   const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB);
-  __shared__ int sTok[BM];
-
   const int ntn = (r + 1) / 2 + 1;  // q tiles (2 heads each) + one k|v tile
-  int g, mt, nt;
-  {
-    int c;
-    if ((n_kv & 7) == 0) {
-      block_raster(blockIdx.x >> 3, mtiles, (n_kv >> 3) * ntn, 4, 8, mt, c);
-      g = (blockIdx.x & 7) + 8 * (c / ntn);
-    } else {
-      block_raster(blockIdx.x, mtiles, n_kv * ntn, 4, 8, mt, c);
-      g = c / ntn;
-    }
-    nt = c % ntn;
-  }
-  const int cnt = gcount[g];
-  const int row0 = mt * BM;
-  if (row0 >= cnt) return;  // l=0
-  const int rows = min(BM, cnt - row0);
   const bool kv_tile = nt == ntn - 1;
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / NWN, wn = wave % NWN;
   for (int i = tid; i < BM; i += C::kThreads) sTok[i] = i < rows ? gperm[(size_t)g * T + row0 + i] : -1;
   __syncthreads();
 
@@ -115,14 +101,18 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     const int tok = sTok[dma_row(wave, q, lane)];
     aOff[q] = tok >= 0 ? (uint32_t)(tok * d + chunk8) * 2u : kSkip;
   }
-  // B row of the tile: q tile -> Wq row g*r*hd + nt*256 + row; k|v tile -> Wk row
-  // g*hd + row (row < 128: instructions q = 0, 1) or Wv row g*hd + row - 128.
+  // B row of the tile: head hh = hsel0 + row / 128 of tile nt; q tile -> Wq row
+  // g*r*hd + (2 nt + hh)*hd + row % 128; k|v tile -> Wk (hh = 0) or Wv (hh = 1)
+  // row g*hd + row % 128.  An instruction's 64 rows lie in one head.
   uint32_t bOff[C::B_INST];
+  int bV[C::B_INST];
 #pragma unroll
   for (int q = 0; q < C::B_INST; ++q) {
     const int row = dma_row(wave, q, lane);
-    const int wrow = kv_tile ? g * kHd + (row & (kHd - 1)) : g * r * kHd + nt * BN + row;
+    const int hh = hsel0 + row / kHd, rr = row & (kHd - 1);
+    const int wrow = kv_tile ? g * kHd + rr : g * r * kHd + (2 * nt + hh) * kHd + rr;
     bOff[q] = (uint32_t)(wrow * d + chunk8) * 2u;
+    bV[q] = __builtin_amdgcn_readfirstlane(hh);
   }
   auto issue = [&](int kt, int st) {
     const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
@@ -132,7 +122,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     if (kv_tile) {
 #pragma unroll
       for (int q = 0; q < C::B_INST; ++q)
-        lds_dma16(q < C::B_INST / 2 ? rK : rV, dma_dst(b, wave, q), bOff[q] + kb);
+        lds_dma16(bV[q] ? rV : rK, dma_dst(b, wave, q), bOff[q] + kb);
     } else {
 #pragma unroll
       for (int q = 0; q < C::B_INST; ++q) lds_dma16(rQ, dma_dst(b, wave, q), bOff[q] + kb);
@@ -143,7 +133,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   for (int i = 0; i < C::RB; ++i)
     if (wm * C::WM + i * 32 < rows) rb_live |= 1u << i;
 
-  WaveAcc<BM, BN> acc;
+  WaveAcc<BM, BN, NWM, NWN> acc;
   acc.zero();
   const int nk = d / kBK;
   auto live = [&](int) { return rb_live; };
@@ -152,18 +142,19 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   else
     acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
 
-  // epilogue.  This wave's 128 columns are one head: q head 2*nt + wn, or k / v.
-  // (With an odd head ratio the last q tile's second half reads zeros or the next
-  // group's rows and is not written.)
-  if (!kv_tile && 2 * nt + wn >= r) return;
-  const bool is_v = kv_tile && wn == 1;
+  // epilogue.  This wave's 128 columns are one head, hsel = hsel0 + wn of the
+  // tile: q head 2*nt + hsel, or k / v.  (With an odd head ratio the last q
+  // tile's second head reads zeros or the next group's rows and is not written.)
+  const int hsel = hsel0 + wn;
+  if (!kv_tile && 2 * nt + hsel >= r) return;
+  const bool is_v = kv_tile && hsel == 1;
   const bool rope = log2_theta > 0.f && !is_v;
   const int c0 = lane & 31;
   // theta^(-2j/hd) for j = c0 and c0 + 32, in revolutions per position
   const RopeFreq f0 = rope ? RopeFreq(exp2f(-(2.f * c0 / kHd) * log2_theta)) : RopeFreq(0.f);
   const RopeFreq f1 =
       rope ? RopeFreq(exp2f(-(2.f * (c0 + 32) / kHd) * log2_theta)) : RopeFreq(0.f);
-  uint16_t* qdst = Qc + ((size_t)(g * r + 2 * nt + wn) * T) * kHd;
+  uint16_t* qdst = Qc + ((size_t)(g * r + 2 * nt + hsel) * T) * kHd;
   uint16_t* kdst = Kc + (size_t)g * T * kHd;
   uint16_t* vdst = Vt + (size_t)g * kHd * vtp;
 #pragma unroll
@@ -213,6 +204,60 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
       p[96] = f2bf(v3);
     }
   }
+}
+
+
+// The QKV projection.  A group's tiles are units of 256 kept tokens x 256
+// columns (two heads), U = ceil(count / 256) * ntn of them, dealt in row-major
+// order; P = compute units per group.  The units past the last full round of P,
+// rem = U mod P, are split into two one-head tiles each (256 x 128, eight waves
+// of 32 rows) when the 2 rem halves fit in one round: they then take about half
+// a unit's time instead of a whole second round of units.  The halves come after
+// all full units of every group in the grid.
+__global__ void __launch_bounds__(kGemmThreads, 1)
+    attn_qkv_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
+                     const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
+                     const int32_t* __restrict__ gcount, const int32_t* __restrict__ gperm, int T,
+                     int d, int n_kv, int r, int P, int vtp, float log2_theta,
+                     uint16_t* __restrict__ Qc, uint16_t* __restrict__ Kc,
+                     uint16_t* __restrict__ Vt) {
+  using Big = TileCfg<256, 256>;
+  using Half = TileCfg<256, 128, 8, 1>;
+  constexpr int kBig = kStages * (Big::SA + Big::SB), kHalf = kStages * (Half::SA + Half::SB);
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[kBig > kHalf ? kBig : kHalf];
+  __shared__ int sTok[256];
+  const int ntn = (r + 1) / 2 + 1;
+  int g, w;
+  if ((n_kv & 7) == 0) {  // groups g = x, x + 8, ... on XCD x
+    const int per = n_kv >> 3;
+    g = (blockIdx.x & 7) + 8 * ((blockIdx.x >> 3) % per);
+    w = (blockIdx.x >> 3) / per;
+  } else {
+    g = blockIdx.x % n_kv;
+    w = blockIdx.x / n_kv;
+  }
+  const int cnt = gcount[g];
+  const int U = ntn * ((cnt + 255) / 256);
+  int rem = U % P;
+  if (2 * rem > P) rem = 0;
+  const int nbig = U - rem;
+  int unit, half = -1;
+  if (w < nbig) {
+    unit = w;
+  } else if (w < nbig + 2 * rem) {
+    unit = nbig + (w - nbig) / 2;
+    half = (w - nbig) & 1;
+  } else {
+    return;  // l=0
+  }
+  const int mt = unit / ntn, nt = unit % ntn;
+  const int row0 = mt * 256, rows = min(256, cnt - row0);
+  if (half < 0)
+    qkv_tile<256, kGemmWN>(X, Wq, Wk, Wv, gperm, T, d, n_kv, r, g, row0, rows, nt, 0, vtp,
+                           log2_theta, sbuf, sbuf + kStages * Big::SA, sTok, Qc, Kc, Vt);
+  else
+    qkv_tile<128, 1>(X, Wq, Wk, Wv, gperm, T, d, n_kv, r, g, row0, rows, nt, half, vtp,
+                     log2_theta, sbuf, sbuf + kStages * Half::SA, sTok, Qc, Kc, Vt);
 }
 
 // ---------------------------------------------------------- attention core
@@ -464,9 +509,12 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
   const float log2_theta = rope_theta > 0.f ? log2f(rope_theta) : 0.f;
   const int vtp = vt_pitch(T);
   {
+    // compute units per group; a group has at most mtiles * ntn units and P / 2
+    // extra work-groups for halves
+    const int P = std::max(1, kCoreCUs / n_kv);
     WIDE_TRACE("attn_qkv_prefill", s);
-    attn_qkv_prefill<<<n_kv * mtiles * ntn, kGemmThreads, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
-                                                         r, mtiles, vtp, log2_theta, Qc, Kc, Vt);
+    attn_qkv_prefill<<<n_kv * (mtiles * ntn + P / 2), kGemmThreads, 0, s>>>(
+        X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv, r, P, vtp, log2_theta, Qc, Kc, Vt);
   }
   // bins per group: half the most tiles a group can have, but no more than fill
   // the CUs once (256 CUs, one work-group each)
