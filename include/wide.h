@@ -219,6 +219,15 @@ int wide_attn_decode_masked_cache(const uint16_t* X, const uint8_t* mask, const 
  *   y = h + FFN(w; ffn_mask),  RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma.
  * Weights as in the two calls above; rms1, rms2 [d_model] bf16.  Same prefill /
  * decode and cache rules as wide_attn_proj_masked.  With all-zero masks y == x.
+ * Streams (prefill): the two mask reorders, which read only the masks, run on a
+ * second stream of the current device that the library creates on first use;
+ * it is forked from `stream` by an event recorded at the start of the call and
+ * joined back by events before the kernels that read its results, so all of
+ * the call's work stays ordered after the caller's earlier work on `stream` and
+ * before its later work (this is also the fork/join pattern that stream capture
+ * accepts).  Calls that enqueue on one device at the same time are serialised
+ * by a lock while they enqueue.  If the second stream cannot be created the
+ * call runs on `stream` alone.
  */
 typedef struct {
   const uint16_t* rms1;
