@@ -14,14 +14,15 @@
 //                   Qc [n_kv][r][T][hd], Kc [n_kv][T][hd] and V transposed,
 //                   Vt [n_kv][hd][vtp] (column i = i-th kept token of the group,
 //                   permuted inside 16-key groups; zero up to a whole group).
-// attn_core_prefill one work-group = (group, one of B bins of its tiles of 64
+// attn_core_prefill one work-group = (group, one of B bins of its tiles of 32
 //                   compacted queries, dealt heaviest first in snake order),
-//                   two waves per query head (32 queries each, so two waves
-//                   share each SIMD); K and V^T blocks arrive by buffer->LDS
-//                   loads one key step ahead.  S^T = K Q^T puts a query in each
-//                   lane's column, so the softmax is per lane (+ one cross-half
-//                   swap, v_permlane32_swap) and P
-//                   stays in registers as the B operand of O^T = V^T P^T; V is
+//                   one wave per query head; two work-groups per CU, whose
+//                   waves share the SIMDs without sharing barriers.  K and V^T
+//                   blocks arrive by buffer->LDS loads one key step ahead.
+//                   S^T = K Q^T puts a query in each lane's column, so the
+//                   softmax is per lane (+ one cross-half swap,
+//                   v_permlane32_swap) and P stays in registers as the B
+//                   operand of O^T = V^T P^T; V is
 //                   read in the key order the S^T accumulator layout gives.  A
 //                   row's reference max is fixed by its first keys, so O is never
 //                   rescaled in the key loop; a tile in which some row's scores
@@ -262,9 +263,10 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
 
 // ---------------------------------------------------------- attention core
 
-constexpr int kBQ = 64;    // queries per tile: 2 waves x 32 per head
+constexpr int kBQ = 32;        // queries per tile: one wave of 32 per head
 constexpr int kBKey = 64;  // keys per step
-constexpr int kCoreWaves = 8;  // 4 heads x 2 query halves
+constexpr int kCoreWaves = 4;  // one per query head of a 4-head chunk
+constexpr int kCoreWgPerCU = 2;  // resident work-groups per CU (LDS 64 KB, <= 256 VGPRs each)
 constexpr int kCoreCUs = 256;   // compute units of the chip
 // One LDS stage: K block [64 keys][128 hd] (16-byte chunk c of key row k at slot
 // c ^ (k & 15)) and V^T block [128 hd][64 keys] (chunk c of row j at slot
@@ -283,7 +285,7 @@ WIDE_DEV void xhalf(float x, float& a, float& b) {
   b = __uint_as_float(v[1]);
 }
 
-__global__ void __launch_bounds__(64 * kCoreWaves, 1)
+__global__ void __launch_bounds__(64 * kCoreWaves, kCoreWgPerCU)
     attn_core_prefill(const uint16_t* __restrict__ Qc, const uint16_t* __restrict__ Kc,
                       const uint16_t* __restrict__ Vt, const int32_t* __restrict__ gcount,
                       const int32_t* __restrict__ gperm, int T, int n_kv, int r, int nbins,
@@ -293,7 +295,7 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
   __shared__ int sRedo;  // some wave's rows outgrew their reference max
 
   // work-group -> (group, bin j of B = nbins, chunk of 4 query heads).  Query
-  // tile qt of a group takes qt + 1 key steps.  The group's tiles, heaviest
+  // tile qt of a group takes qt / 2 + 1 key steps.  The group's tiles, heaviest
   // first, are dealt to its B bins in snake order: bin j takes the tiles of rank
   // j, 2B-1-j, 2B+j, 4B-1-j, ..., so the bins of a group do nearly the same
   // number of key steps whatever the group's count (with B = half the tiles this
@@ -308,8 +310,7 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
   const int qtiles = (cnt + kBQ - 1) / kBQ;
   if (j >= qtiles) return;  // l=0: past the group's kept tokens
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  // wave = (head of the chunk, half of the 64 queries): two waves per SIMD
-  const int hw = wave & 3, qh = wave >> 2;
+  const int hw = wave;  // head of the chunk
   const bool head_ok = hc * 4 + hw < r;  // waves past the group's heads only help load
   const int h = g * r + min(hc * 4 + hw, r - 1);
   const int c0 = lane & 31, half = lane >> 5;
@@ -318,11 +319,11 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
   const i32x4 vSrd = make_srd(Vt + (size_t)g * kHd * vtp, (uint32_t)((size_t)kHd * vtp * 2));
   const uint32_t ldsK = lds_addr(sK), ldsV = lds_addr(sV);
   // buffer->LDS loads of key block kb into stage st: instruction i of wave w fills
-  // K rows 4 (8 i + w) .. +3 and V^T rows 8 (8 i + w) .. +7 (1 KB each)
+  // K rows 4 (4 i + w) .. +3 and V^T rows 8 (4 i + w) .. +7 (1 KB each)
   auto issue = [&](int kb, int st) {
     const int k0 = kb * kBKey;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
+    for (int i = 0; i < 16 / kCoreWaves; ++i) {
       const int n = kCoreWaves * i + wave;
       const int krow = 4 * n + (lane >> 4), kslot = lane & 15;
       const int kchunk = kslot ^ (krow & 15);
@@ -346,7 +347,7 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
     const int q0 = qt * kBQ;
     const int q_last = min(cnt, q0 + kBQ) - 1;
     const int nkb = q_last / kBKey + 1;
-    const int q = q0 + 32 * qh + c0;  // this lane's query (its S^T column)
+    const int q = q0 + c0;  // this lane's query (its S^T column)
 
     // Q^T fragments as B operands: lane holds query q, hd 16 ks + 8 half.
     bf16x8 qf[8];
@@ -380,11 +381,11 @@ __global__ void __launch_bounds__(64 * kCoreWaves, 1)
 
       for (int kb = 0; kb < nkb; ++kb) {
         const int k0 = kb * kBKey, st = kb & 1;
-        // every wave's loads of block kb have landed (this wave's 4 loads of block
+        // every wave's loads of block kb have landed (this wave's loads of block
         // kb + 1 may stay in flight)
         if (kb + 1 < nkb) {
           issue(kb + 1, st ^ 1);
-          stage_barrier<4>();
+          stage_barrier<32 / kCoreWaves>();
         } else {
           stage_barrier<0>();
         }
@@ -517,10 +518,10 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
         X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv, r, P, vtp, log2_theta, Qc, Kc, Vt);
   }
   // bins per group: half the most tiles a group can have, but no more than fill
-  // the CUs once (256 CUs, one work-group each)
+  // the CUs once (256 CUs, kCoreWgPerCU work-groups each)
   const int hcs = (r + 3) / 4;
   const int npairs = ((T + kBQ - 1) / kBQ + 1) / 2;
-  const int nbins = std::max(1, std::min(npairs, kCoreCUs / (n_kv * hcs)));
+  const int nbins = std::max(1, std::min(npairs, kCoreWgPerCU * kCoreCUs / (n_kv * hcs)));
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHd);
   {
     WIDE_TRACE("attn_core_prefill", s);
