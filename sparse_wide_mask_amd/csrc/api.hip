@@ -158,7 +158,10 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
     return w;
   }
   w.rv = carve_reorder(c, T, nkv, ffn_down_tile_m(), false);
-  if (nkv <= kSortMaxGroups) w.rv.order = c.take<int32_t>(T);
+  if (nkv <= kSortMaxGroups) {
+    w.rv.order = c.take<int32_t>(T);
+    w.rv.tile_perm = c.take<int32_t>(ceil_div(T, w.rv.tile_m));
+  }
   w.Qc = c.take<uint16_t>((size_t)nq * T * kHeadDim);
   w.Kc = c.take<uint16_t>((size_t)nkv * T * kHeadDim);
   w.Vt = c.take<uint16_t>((size_t)nkv * kHeadDim * vt_pitch(T));
@@ -174,7 +177,7 @@ void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStrea
     launch_reorder(mask, T, nkv, w.rv.tile_m, w.rv.packed, w.rv.count, w.rv.perm, w.rv.rank,
                    nullptr, nullptr, s);
     launch_token_sort(w.rv.packed, T, nkv, w.rv.tile_m, w.rv.order, w.rv.tile_count,
-                      w.rv.tile_groups, s);
+                      w.rv.tile_groups, w.rv.tile_perm, s);
   } else {
     run_reorder(mask, T, nkv, w.rv, s);
   }

@@ -202,7 +202,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
                        const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
                        const int32_t* __restrict__ tgroups, const int32_t* __restrict__ order,
-                       int T, int d, int F, int n, int G, int nw, int ntn,
+                       const int32_t* __restrict__ tile_perm, int T, int d, int F, int n, int G,
+                       int nw, int ntn,
                        const uint16_t* __restrict__ residual, uint16_t* __restrict__ Y) {
   using C = TileCfg<BM, BN>;
   WIDE_STAGE_ARRAYS(C);
@@ -216,7 +217,15 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   const int p = (blockIdx.x & 7) * ((n_tiles + 7) >> 3) + (blockIdx.x >> 3);
   if (p >= n_tiles) return;
   int mt, nt;
-  block_raster(p, mtiles, ntn, 4, 8, mt, nt);
+  if (tile_perm) {
+    // row tiles balanced over the XCDs by group union, each XCD's in descending
+    // union order; walked row by row, so a compute unit that ran a large tile
+    // early takes a small one late
+    mt = tile_perm[p / ntn];
+    nt = p % ntn;
+  } else {
+    block_raster(p, mtiles, ntn, 4, 8, mt, nt);
+  }
   const int t0 = mt * BM, rows = min(BM, T - t0), n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
   const int ng = tcount[mt];
@@ -393,8 +402,8 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   WIDE_TRACE(USE == kUseAttnO ? "attn_o" : "ffn_down", s);
   auto k = best_bn == 256 ? kmask_gemm_prefill<kDownBM, 256, USE>
                           : kmask_gemm_prefill<kDownBM, 128, USE>;
-  k<<<grid, kGemmThreads, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, rv.order, T, d, F, n,
-                         G, nw, ntn, residual, Y);
+  k<<<grid, kGemmThreads, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, rv.order,
+                                  rv.tile_perm, T, d, F, n, G, nw, ntn, residual, Y);
 }
 
 void launch_kmask_gemm(KmUse use, const uint16_t* A, const uint16_t* Wp, const ReorderView& rv,

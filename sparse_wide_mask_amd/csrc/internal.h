@@ -28,6 +28,7 @@ struct ReorderView {
   int32_t* tile_count = nullptr;  // [ceil(T / tile_m)]
   int32_t* tile_groups = nullptr; // [ceil(T / tile_m), n]
   int32_t* order = nullptr;       // [T] token order of the tiles (null: 0..T-1)
+  int32_t* tile_perm = nullptr;   // [ceil(T / tile_m)] tile of each K-masked slot (null: identity)
   int tile_m = 0;
 };
 
@@ -39,7 +40,8 @@ void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* pac
 // tokens in that order.  T <= WIDE_MAX_TOKENS (the keys take T bytes of LDS).
 constexpr int kSortMaxGroups = 8;
 void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
-                       int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
+                       int32_t* tile_count, int32_t* tile_groups, int32_t* tile_perm,
+                       hipStream_t s);
 
 void launch_pack_kmajor(const uint16_t* W, int n, int G, int d, uint16_t* Wp, hipStream_t s);
 

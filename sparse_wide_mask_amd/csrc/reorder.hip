@@ -159,20 +159,27 @@ __global__ void __launch_bounds__(kGroupThreads)
 constexpr int kSortThreads = 1024;
 constexpr int kSortWaves = kSortThreads / kWave;
 constexpr int kSortBins = 256;  // key = the whole mask pattern (n <= 8 groups)
+constexpr int kSortMaxTiles = 256;  // tiles ranked for tile_perm (256-token tiles of 65536)
 
 // One work-group; keys (the tokens' 8-bit patterns) are staged in LDS.  Wave w
 // owns the contiguous tokens [w c, (w + 1) c) and (1) counts its keys, (2) one
 // scan over (key, wave) gives each wave's first slot per key, (3) each wave
 // places its tokens in order, 64 at a time; lanes with equal keys are ranked by a
 // ballot match.  (4) A tile of the new order covers a run of whole key ranges,
-// so its group union is the OR of the keys whose range meets it.
+// so its group union is the OR of the keys whose range meets it.  (5) When
+// tile_perm is given: the K-masked kernel's XCD x takes the tile slots
+// m x .. m x + m - 1 (m = tiles / 8) whenever the tile count is a multiple of 32,
+// and a tile's time grows with its union; so the tiles, largest union first,
+// are dealt to the XCDs in snake order (XCD x gets ranks x, 15 - x, 16 + x, ...)
+// and tile_perm[slot] names the tile of each slot (identity otherwise).
 __global__ void __launch_bounds__(kSortThreads)
     reorder_token_sort(const uint64_t* __restrict__ packed, int T, int n, int nw, int tile_m,
                        int32_t* __restrict__ order, int32_t* __restrict__ tile_count,
-                       int32_t* __restrict__ tile_groups) {
+                       int32_t* __restrict__ tile_groups, int32_t* __restrict__ tile_perm) {
   extern __shared__ uint8_t sKey[];  // [T]
   __shared__ int sHist[kSortWaves][kSortBins];
   __shared__ int sStart[kSortBins + 1];
+  __shared__ int sUnion[kSortMaxTiles];
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
   for (int i = tid; i < kSortWaves * kSortBins; i += kSortThreads) (&sHist[0][0])[i] = 0;
   for (int t0 = 0; t0 < T; t0 += 4 * kSortThreads) {
@@ -254,12 +261,34 @@ __global__ void __launch_bounds__(kSortThreads)
     if (has) out[popc64(hb & ((1ull << lane) - 1ull))] = lane;
     const int written = popc64(hb);
     for (int q = written + lane; q < n; q += kWave) out[q] = -1;
-    if (lane == 0) tile_count[tile] = written;
+    if (lane == 0) {
+      tile_count[tile] = written;
+      if (tile < kSortMaxTiles) sUnion[tile] = written;
+    }
+  }
+  if (!tile_perm) return;
+  __syncthreads();
+  const bool snake = n_tiles % 32 == 0 && n_tiles <= kSortMaxTiles;
+  for (int i = tid; i < n_tiles; i += kSortThreads) {
+    int slot = i;
+    if (snake) {
+      const int u = sUnion[i];
+      int rank = 0;  // position among the tiles by union, descending (ties by index)
+      for (int k = 0; k < n_tiles; ++k) {
+        const int v = sUnion[k];
+        rank += (v > u || (v == u && k < i)) ? 1 : 0;
+      }
+      const int round = rank >> 3, pos = rank & 7;
+      const int x = (round & 1) ? 7 - pos : pos;
+      slot = (n_tiles >> 3) * x + round;
+    }
+    tile_perm[slot] = i;
   }
 }
 
 void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
-                       int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
+                       int32_t* tile_count, int32_t* tile_groups, int32_t* tile_perm,
+                       hipStream_t s) {
   // the key array may take the whole 64 KB of dynamic LDS next to the static part
   static const hipError_t attr = hipFuncSetAttribute(
       reinterpret_cast<const void*>(&reorder_token_sort),
@@ -267,7 +296,8 @@ void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t
   (void)attr;
   WIDE_TRACE("reorder_token_sort", s);
   reorder_token_sort<<<1, kSortThreads, (size_t)T, s>>>(packed, T, n, (n + 63) / 64, tile_m,
-                                                        order, tile_count, tile_groups);
+                                                        order, tile_count, tile_groups,
+                                                        tile_perm);
 }
 
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
