@@ -110,3 +110,21 @@ def test_attn_prefill_outlier_key_second_pass():
     rows = np.flatnonzero(good)
     err = np.abs(got[rows] - ref[rows]).max(axis=1) / np.abs(ref[rows]).max(axis=1)
     assert err.max() <= TOL
+
+
+@needs_gpu
+def test_attn_prefill_max_tokens_sampled():
+    """The maximum token count, 65536, at a small width (d = 256, 8 query and 8 KV
+    heads, top-k 4 of 8 groups, RoPE up to position 65535): 256 pattern-sorted row
+    tiles dealt to the XCDs in snake order for the O projection, and about 16
+    query tiles per bin in the core.  The oracle computes 48 sampled rows (each
+    over all of its group's earlier kept tokens); every row must be finite."""
+    dev()
+    T = 65536
+    log(f"attn prefill T={T} (maximum), sampled")
+    c = attn_case("attn_max", T, 256, 8, 8, 128, 0.5, "topk")
+    got = _gpu_attn(c, 500000.0)
+    assert np.all(np.isfinite(got))
+    rows = np.sort(np.random.default_rng(3).choice(T, 48, replace=False))
+    rows[0], rows[-1] = 0, T - 1
+    assert rel_err(got[rows], _oracle(c, 500000.0, rows=rows)) <= TOL

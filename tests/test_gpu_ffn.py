@@ -84,3 +84,21 @@ def test_ffn_prefill_llama32_3b_sampled():
     rows[0], rows[-1] = 0, 4095
     ref = ffn_masked(c["X"][rows], c["mask"][rows], c["W_gate"], c["W_up"], c["W_down"])
     assert rel_err(got[rows], ref) <= TOL
+
+
+@needs_gpu
+def test_ffn_prefill_max_tokens_sampled():
+    """The maximum token count, 65536, at a small width (d = 256, d_ff = 1024 in 8
+    groups of 128, top-k 4 of 8): about 128 row tiles per group and group tails at
+    the end of the grid in the up projection, 256 row tiles in the down
+    projection.  64 sampled rows against the oracle; every row finite."""
+    dev()
+    T = 65536
+    log(f"ffn prefill T={T} (maximum), sampled")
+    c = ffn_case("ffn_max", T, 256, 1024, 8, 0.5, "topk")
+    got = _gpu_ffn(c)
+    assert np.all(np.isfinite(got))
+    rows = np.sort(np.random.default_rng(4).choice(T, 64, replace=False))
+    rows[0], rows[-1] = 0, T - 1
+    ref = ffn_masked(c["X"][rows], c["mask"][rows], c["W_gate"], c["W_up"], c["W_down"])
+    assert rel_err(got[rows], ref) <= TOL

@@ -151,3 +151,19 @@ def test_layer_prefill_back_to_back_shared_workspace():
     torch.cuda.synchronize()
     for c, Y in zip(cases, outs):
         assert rel_err(host(Y), oracle_layer(c)) <= TOL
+
+
+@needs_gpu
+def test_layer_prefill_max_tokens_sampled():
+    """The whole layer at the maximum token count, 65536, at a small width (d = 256,
+    d_ff = 1024 in 8 groups, 8 query and 8 KV heads, router masks keeping 50 %):
+    48 sampled rows against the oracle; every row finite."""
+    dev()
+    T = 65536
+    log(f"layer prefill T={T} (maximum), sampled")
+    c = layer_case("layer_max", T, 256, 1024, 8, 8, 8, 128, 0.5, "router")
+    got = gpu_layer(c)
+    assert np.all(np.isfinite(got))
+    rows = np.sort(np.random.default_rng(5).choice(T, 48, replace=False))
+    rows[0], rows[-1] = 0, T - 1
+    assert rel_err(got[rows], oracle_layer(c, rows=rows)) <= TOL
