@@ -140,7 +140,7 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
           const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
           const uint32_t off =
               full || row < rows ? (uint32_t)(sTok[row] * F + col) * 2u : kSkip;
-          __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(gt[e]) * up[e]), hr, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(gt[e]) * up[e]), hr, (int)off, 0, kNtStore);
         }
       }
     }
@@ -368,7 +368,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
         for (int e = 0; e < 16; ++e) {
           const uint32_t off = col < d && tok[e] != kSkip ? tok[e] + 2u * col : kSkip;
           const float v = acc.acc[i][j0 + jj][e] + __uint_as_float(rv[jj][e] << 16);
-          __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), yr, (int)off, 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), yr, (int)off, 0, kNtStore);
         }
       }
     }

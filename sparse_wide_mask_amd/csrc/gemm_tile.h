@@ -30,6 +30,10 @@ namespace wide {
 constexpr int kBK = 64;
 constexpr int kStages = 2;
 constexpr uint32_t kSkip = 0x7fffff00u;  // buffer offset past any num_records: zeros
+// Cache policy of the large outputs' buffer stores: non-temporal (the next
+// kernel reads them back from memory anyway).  Fewer dirty L2 lines are left
+// to write back when a kernel ends: about 24 us less per 8B layer prefill step.
+constexpr int kNtStore = 2;
 
 typedef __amdgpu_buffer_rsrc_t rsrc_t;
 
