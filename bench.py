@@ -133,12 +133,13 @@ class LayerPrefill:
 
 
 class FfnPrefill:
-    """Llama-3.2-3B-shaped FFN prefill (T=4096, d=3072, d_ff=8192 in 64 groups)."""
+    """Llama-3.2-3B-shaped FFN prefill (T=4096, d=3072, d_ff=8192 in 64 groups of 128,
+    or groups of ffn_group channels)."""
 
-    def __init__(self, T=4096):
+    def __init__(self, T=4096, ffn_group=128):
         from synth.workloads import ffn_prefill_3b
-        self.name = "ffn_prefill_3b"
-        self.c = ffn_prefill_3b(T)
+        self.name = "ffn_prefill_3b" + ("" if ffn_group == 128 else f"_g{ffn_group}")
+        self.c = ffn_prefill_3b(T, ffn_group)
         m = self.c["meta"]
         self.m, self.T = m, T
         self.config = dict(workload=self.name, T=T, d_model=m["d"], d_ff=m["F"], n_groups=m["n"],
@@ -673,6 +674,8 @@ def main():
     if args.workload.startswith("layer_"):
         W = WORKLOADS[args.workload](keep=args.keep, kind=args.masks, ffn_group=args.ffn_group,
                                      attn_keep=args.attn_keep)
+    elif args.workload == "ffn_prefill_3b":
+        W = FfnPrefill(ffn_group=args.ffn_group)
     else:
         W = WORKLOADS[args.workload]()
     W.upload(torch, wide, bf16, u8)

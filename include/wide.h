@@ -88,6 +88,7 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m,
  * o_proj.weight transposed).  W_packed [n_groups, d_model, G] holds, for every
  * group g, the block W[gG:(g+1)G, :] transposed, so each group's block is one
  * contiguous region with the contraction index innermost.  Run once at weight load.
+ * G a multiple of 64, or 32; d_model a multiple of 64.
  */
 /*
  * wide_router_topk - router and top-k selection, the step before the masked path
@@ -141,7 +142,9 @@ int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16
  * Y             [T, d_model] bf16 (a token that keeps no group gets exact zeros)
  * mode          WIDE_PREFILL (any T) or WIDE_DECODE (T = batch; weight streaming over
  *               the groups the batch keeps when T <= 64)
- * Needs G = d_ff / n_groups a multiple of 64 and d_model a multiple of 64.
+ * Needs G = d_ff / n_groups a multiple of 64, or 32 (groups of 32 run at a lower
+ * rate: every kept row is multiplied by 64 weight columns at a time), and d_model
+ * a multiple of 64.
  */
 size_t wide_ffn_masked_workspace(int T, int d_model, int d_ff, int n_groups, int mode);
 int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_gate,

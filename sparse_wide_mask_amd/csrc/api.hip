@@ -71,7 +71,7 @@ int ffn_check(int T, int d, int F, int n, int mode) {
   if (n > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
   if (!fits(T, d) || !fits(F, d) || !fits(T, F)) return WIDE_EUNSUPPORTED;
   const int G = F / n;
-  if (G % 64 || d % 64) return WIDE_EUNSUPPORTED;
+  if ((G % 64 && G != 32) || d % 64) return WIDE_EUNSUPPORTED;  // groups of 64k or 32
   return WIDE_OK;
 }
 
@@ -324,7 +324,7 @@ int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16
                      void* stream) {
   if (n_groups < 1 || G < 1 || d_model < 1) return WIDE_EINVAL;
   if (!aligned16(W) || !aligned16(W_packed) || W == W_packed) return WIDE_EINVAL;
-  if (G % 64 || d_model % 64 || n_groups > 65535) return WIDE_EUNSUPPORTED;
+  if ((G % 64 && G != 32) || d_model % 64 || n_groups > 65535) return WIDE_EUNSUPPORTED;
   (void)hipGetLastError();
   launch_pack_kmajor(W, n_groups, G, d_model, W_packed, as_stream(stream));
   return launch_status();

@@ -437,7 +437,7 @@ int kmask_decode_col_blocks(int d) { return (d + kKmCols - 1) / kKmCols; }
 // K splits: enough work-groups to fill the 256 CUs, at most 16 partial sums, and
 // no more splits than the largest possible union has units.
 int kmask_decode_splits(int d, int n, int G) {
-  const int units = n * (G % 128 == 0 ? G / 128 : G / 64);
+  const int units = n * (G % 128 == 0 ? G / 128 : G % 64 == 0 ? G / 64 : G / 32);
   const int ncb = kmask_decode_col_blocks(d);
   int s = (256 + ncb - 1) / ncb;
   s = s < 16 ? s : 16;
@@ -924,8 +924,11 @@ void launch_kmask_decode(KmUse use, const uint16_t* A, const uint16_t* Wp, const
   using D = std::integral_constant<int, kUseFfnDown>;
   using K4 = std::integral_constant<int, 4>;
   using K2 = std::integral_constant<int, 2>;
+  using K1 = std::integral_constant<int, 1>;
   auto k = use == kUseAttnO ? (G % 128 == 0 ? pick(O{}, K4{}) : pick(O{}, K2{}))
-                            : (G % 128 == 0 ? pick(D{}, K4{}) : pick(D{}, K2{}));
+           : G % 128 == 0   ? pick(D{}, K4{})
+           : G % 64 == 0    ? pick(D{}, K2{})
+                            : pick(D{}, K1{});  // groups of 32: 32-wide units
   k<<<kmask_decode_col_blocks(d) * S, kKmThreads, 0, s>>>(A, Wp, mask, B, d, F, G, n, S, residual,
                                                          part, Y);
   if (S > 1) kmask_decode_reduce<<<(B * d / 4 + 255) / 256, 256, 0, s>>>(part, S, B, d, residual, Y);

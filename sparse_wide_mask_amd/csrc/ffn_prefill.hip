@@ -162,13 +162,13 @@ static_assert(TailCfg::kThreads == kGemmThreads, "one launch shape");
 // work-groups after them take exactly those tails, one per (group, channel tile).
 // Being last in the grid, the tails run on the compute units that finish their
 // share of full tiles first.
-template <int BM, int BN, bool TAILS>
+template <int BM, int BN, int NWM, int NWN, bool TAILS>
 __global__ void __launch_bounds__(kGemmThreads, 1)
     ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
                    const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gcount,
                    const int32_t* __restrict__ gperm, int T, int d, int F, int n, int G,
                    int mtiles, int ntn, int n_main, uint16_t* __restrict__ H) {
-  using C = TileCfg<BM, BN>;
+  using C = TileCfg<BM, BN, NWM, NWN>;
   constexpr int kMain = kStages * (C::SA + C::SB);
   constexpr int kTail = TAILS ? kTailStages * (TailCfg::SA + TailCfg::SB) : 0;
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kMain > kTail ? kMain : kTail];
@@ -193,11 +193,15 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   if (row0 >= cnt) return;  // l=0: no kept token left in this tile
   const int rows = min(BM, cnt - row0);
   if (TAILS && row0 + BM >= cnt && rows <= kUpTailRows) return;  // a tail work-group's
-  ffn_up_tile<BM, BN, kGemmWM, kGemmWN, kStages>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt,
-                                                  sbuf, sbuf + kStages * C::SA, sTok, H);
+  ffn_up_tile<BM, BN, NWM, NWN, kStages>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
+                                          sbuf + kStages * C::SA, sTok, H);
 }
 
-template <int BM, int BN, int USE>
+// GPS = groups per 64-wide K slice: 1 for groups of 64 or more channels; 2 for
+// groups of 32, where a slice covers groups 2p and 2p + 1 (K runs over the tile's
+// union of such pairs; each lane's 16-byte chunk belongs to one of the two
+// groups, which decides its row's keep bit and its weight block).
+template <int BM, int BN, int USE, int GPS>
 __global__ void __launch_bounds__(kGemmThreads, 1)
     kmask_gemm_prefill(const uint16_t* __restrict__ H, const uint16_t* __restrict__ Wdp,
                        const uint64_t* __restrict__ packed, const int32_t* __restrict__ tcount,
@@ -211,6 +215,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   __shared__ int sTok[BM];  // token of each tile row
   __shared__ int sGroups[256];
   __shared__ uint8_t sLive[256 * C::kWaves];
+  __shared__ int sNsg;
 
   // XCD x takes a contiguous stretch of the block-rasterised tile order.
   const int mtiles = (T + BM - 1) / BM, n_tiles = mtiles * ntn;
@@ -240,6 +245,19 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   }
   for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
   __syncthreads();
+  int nsg = ng;  // the tile's K units: groups, or pairs of groups when GPS == 2
+  if constexpr (GPS == 2) {
+    if (tid == 0) {  // ascending groups -> ascending distinct pairs, in place
+      int m = 0;
+      for (int i = 0; i < ng; ++i) {
+        const int pr = sGroups[i] >> 1;
+        if (m == 0 || sGroups[m - 1] != pr) sGroups[m++] = pr;
+      }
+      sNsg = m;
+    }
+    __syncthreads();
+    nsg = sNsg;
+  }
 
   const int chunk8 = dma_chunk(dma_row(wave, 0, lane), lane) * 8;
   const i32x4 rH = make_srd(H, (uint32_t)T * F * 2u);
@@ -251,54 +269,61 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     aRow[q] = dma_row(wave, q, lane);
     aBase[q] = (uint32_t)(sTok[aRow[q]] * F + chunk8) * 2u;
   }
+  // GPS == 2: this lane's chunk lies in the pair's second group when chunk8 >= 32
+  const int half_l = GPS == 2 && chunk8 >= 32 ? 1 : 0;
 #pragma unroll
   for (int q = 0; q < C::B_INST; ++q) {
     const int nrow = n0 + dma_row(wave, q, lane);
-    bOff[q] = nrow < d ? (uint32_t)(nrow * G + chunk8) * 2u : kSkip;
+    const uint32_t o = GPS == 2 ? (uint32_t)(nrow * G + (chunk8 & 31)) * 2u
+                                : (uint32_t)(nrow * G + chunk8) * 2u;
+    bOff[q] = nrow < d ? o : kSkip;
   }
-  const int kpg = G / kBK;  // K slices per group
-  const int nk = ng * kpg;
+  const int kpg = GPS == 2 ? 1 : G / kBK;  // K slices per K unit
+  const int nk = nsg * kpg;
   // The issues walk the slices in order, so the slice's group comes from running
   // counters; the next group is read from LDS one call ahead, and each lane keeps
   // the mask word of its A rows that holds the current group's bit (reloaded
   // only when the group crosses a 64-group word).
   int is_gi = 0, is_s = 0, is_w = -1;
-  int is_gv = ng > 0 ? sGroups[0] : 0;  // read ahead; made scalar when used
+  int is_gv = nsg > 0 ? sGroups[0] : 0;  // read ahead; made scalar when used
   uint64_t rw[C::A_INST];
   auto issue = [&](int, int st) {
-    const int g = __builtin_amdgcn_readfirstlane(is_gv);
-    if ((g >> 6) != is_w) {
-      is_w = g >> 6;
+    const int g = __builtin_amdgcn_readfirstlane(is_gv);  // group, or pair (GPS == 2)
+    const int g0 = GPS * g;  // first group of the slice
+    if ((g0 >> 6) != is_w) {
+      is_w = g0 >> 6;
 #pragma unroll
       for (int q = 0; q < C::A_INST; ++q)
         rw[q] = aRow[q] < rows ? sBits[aRow[q] * 4 + is_w] : 0ull;
     }
     const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
     const int kk = is_s * kBK;
-    const uint32_t ka = (uint32_t)(g * G + kk) * 2u;
+    // this lane's group: the slice's, or its chunk's of the pair
+    const int gl = g0 + half_l;
+    const uint32_t ka = (uint32_t)(g0 * G + kk) * 2u;
 #pragma unroll
     for (int q = 0; q < C::A_INST; ++q) {
-      // l=1: rows of tokens that dropped g (or past T) are not fetched (zeros)
-      const bool keep = (rw[q] >> (g & 63)) & 1ull;
+      // l=1: rows of tokens that dropped the group (or past T) are not fetched (zeros)
+      const bool keep = (rw[q] >> (gl & 63)) & 1ull;
       lds_dma16(rH, dma_dst(a, wave, q), keep ? aBase[q] + ka : kSkip);
     }
-    const uint32_t kb = (uint32_t)(g * d * G + kk) * 2u;
+    const uint32_t kb = (uint32_t)(gl * d * G + kk) * 2u;
 #pragma unroll
     for (int q = 0; q < C::B_INST; ++q)
       lds_dma16(rW, dma_dst(b, wave, q), bOff[q] == kSkip ? kSkip : bOff[q] + kb);
     if (++is_s == kpg) {
       is_s = 0;
-      if (++is_gi < ng) is_gv = sGroups[is_gi];
+      if (++is_gi < nsg) is_gv = sGroups[is_gi];
     }
   };
-  // l=2: per group of the tile, the row blocks of each wave that hold at least one
-  // token keeping it (sLive[group index][wave]); a wave whose blocks are all live
-  // for every group runs the branch-free loop.
+  // l=2: per K unit of the tile, the row blocks of each wave that hold at least one
+  // token keeping it (either group of a pair; sLive[unit index][wave]); a wave
+  // whose blocks are all live for every unit runs the branch-free loop.
   bool all_live = true;
-  for (int gi = 0; gi < ng; ++gi) {
-    const int g = sGroups[gi];
-    const uint64_t sel = 1ull << (g & 63);
-    const int w = g >> 6;
+  for (int gi = 0; gi < nsg; ++gi) {
+    const int g0 = GPS * sGroups[gi];
+    const uint64_t sel = (GPS == 2 ? 3ull : 1ull) << (g0 & 63);
+    const int w = g0 >> 6;
     uint32_t live = 0;
 #pragma unroll
     for (int i = 0; i < C::RB; ++i) {
@@ -318,12 +343,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   } else {
     // live row blocks of the slices in order, the next group's read one call ahead
     int lv_gi = 0, lv_s = 0;
-    uint32_t lv = ng > 0 ? sLive[wave] : 0u;
+    uint32_t lv = nsg > 0 ? sLive[wave] : 0u;
     acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, [&](int) {
       const uint32_t v = lv;
       if (++lv_s == kpg) {
         lv_s = 0;
-        if (++lv_gi < ng) lv = sLive[lv_gi * C::kWaves + wave];
+        if (++lv_gi < nsg) lv = sLive[lv_gi * C::kWaves + wave];
       }
       return v;
     });
@@ -400,8 +425,16 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   const int ntn = (d + best_bn - 1) / best_bn;
   const int grid = 8 * ((mtiles * ntn + 7) / 8);
   WIDE_TRACE(USE == kUseAttnO ? "attn_o" : "ffn_down", s);
-  auto k = best_bn == 256 ? kmask_gemm_prefill<kDownBM, 256, USE>
-                          : kmask_gemm_prefill<kDownBM, 128, USE>;
+  auto pick = [&](auto gps_tag) {
+    constexpr int P = decltype(gps_tag)::value;
+    return best_bn == 256 ? kmask_gemm_prefill<kDownBM, 256, USE, P>
+                          : kmask_gemm_prefill<kDownBM, 128, USE, P>;
+  };
+  using G1 = std::integral_constant<int, 1>;
+  using G2 = std::integral_constant<int, 2>;
+  auto k = pick(G1{});
+  if constexpr (USE == kUseFfnDown)
+    if (G % 64 != 0) k = pick(G2{});  // groups of 32: pairs per slice
   k<<<grid, kGemmThreads, 0, s>>>(A, Wp, rv.packed, rv.tile_count, rv.tile_groups, rv.order,
                                   rv.tile_perm, T, d, F, n, G, nw, ntn, residual, Y);
 }
@@ -426,16 +459,27 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     {
       WIDE_TRACE("ffn_up_prefill", s);
       const int n_main = n * mtiles * ntn;
-      ffn_up_prefill<BM, BN, true><<<n_main + n * ntn, kGemmThreads, 0, s>>>(
+      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, true><<<n_main + n * ntn, kGemmThreads, 0, s>>>(
           X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
-  } else {
+  } else if (G % 64 == 0) {
     constexpr int BM = 256, BN = 128;
     const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
     {
       WIDE_TRACE("ffn_up_prefill", s);
       const int n_main = n * mtiles * ntn;
-      ffn_up_prefill<BM, BN, false><<<n_main, kGemmThreads, 0, s>>>(
+      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, false><<<n_main, kGemmThreads, 0, s>>>(
+          X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
+    }
+  } else {
+    // groups of 32 channels: 64-column tiles (32 gate + 32 up), eight waves of
+    // 32 rows, each holding gate and up of the tile's 32 channels
+    constexpr int BM = 256, BN = 64;
+    const int mtiles = (T + BM - 1) / BM, ntn = G / (BN / 2);
+    {
+      WIDE_TRACE("ffn_up_prefill", s);
+      const int n_main = n * mtiles * ntn;
+      ffn_up_prefill<BM, BN, 8, 1, false><<<n_main, kGemmThreads, 0, s>>>(
           X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   }

@@ -130,10 +130,13 @@ def tiny_ffn():
     return ffn_case("tiny_ffn", 64, 256, 1024, 16, 0.5, "topk")
 
 
-def ffn_prefill_3b(T: int = 4096):
-    """Llama-3.2-3B FFN prefill: d=3072, d_ff=8192 in 64 groups of 128, keep 32 of 64
-    by top-k of x @ R, R [3072, 64] ~ N(0, 1/3072)."""
-    return ffn_case("ffn_prefill_3b", T, 3072, 8192, 64, 0.5, "router")
+def ffn_prefill_3b(T: int = 4096, ffn_group: int = 128):
+    """Llama-3.2-3B FFN prefill: d=3072, d_ff=8192 in groups of ``ffn_group`` channels
+    (64 groups of 128 by default), keeping half of them by top-k of x @ R,
+    R [3072, n] ~ N(0, 1/3072).  Inputs and weights do not depend on the group size."""
+    if 8192 % ffn_group:
+        raise ValueError("ffn_group must divide 8192")
+    return ffn_case("ffn_prefill_3b", T, 3072, 8192, 8192 // ffn_group, 0.5, "router")
 
 
 def ffn_decode_8b(B: int):

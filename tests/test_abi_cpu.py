@@ -49,6 +49,8 @@ def test_ffn_workspace_queries(L):
     assert ws >= 4096 * 8192 * 2                      # H is held in the workspace
     assert b.ffn_masked_workspace(64, 256, 1000, 16) == 0   # d_ff % n != 0 -> invalid -> 0
     assert b.ffn_masked_workspace(64, 256, 16 * 96, 16) == 0  # G = 96: unsupported -> 0
+    assert b.ffn_masked_workspace(64, 256, 16 * 16, 16) == 0  # G = 16: unsupported -> 0
+    assert b.ffn_masked_workspace(64, 256, 16 * 32, 16) > 0   # G = 32: supported
 
 
 def test_validation_before_any_launch(L):
@@ -64,6 +66,9 @@ def test_validation_before_any_launch(L):
     assert L.wide_ffn_masked(z, z, z, z, z, 8, 256, 1024, 16, 7, z, z, 0, 0, z) == 1
     assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 0, z) == 0
     assert L.wide_pack_kmajor(z, 4, 64, 256, z, z) == 1
+    buf = C.c_void_p(16)  # aligned, never dereferenced: the shape is rejected first
+    other = C.c_void_p(32)
+    assert L.wide_pack_kmajor(buf, 4, 16, 256, other, z) == 2   # G = 16: unsupported
 
 
 def test_router_validation_before_any_launch(L):

@@ -28,7 +28,8 @@ def _gpu_ffn(c, mode):
                                           (17, 384, 1536, 12, "topk"), (64, 256, 2048, 32, "clustered"),
                                           (33, 256, 1024, 8, "ones"), (9, 256, 1024, 8, "zeros"),
                                           (100, 256, 1024, 8, "topk"), (24, 128, 512, 8, "topk"),
-                                          (48, 448, 1024, 16, "bernoulli")])
+                                          (48, 448, 1024, 16, "bernoulli"),
+                                          (8, 256, 512, 16, "topk"), (40, 384, 1024, 32, "bernoulli")])
 def test_ffn_decode_shapes(B, d, F, n, kind):
     dev()
     log(f"ffn decode B={B} d={d} F={F} n={n} {kind}")

@@ -24,10 +24,10 @@ def _gpu_ffn(c, mode="prefill"):
 
 
 @needs_gpu
-def test_pack_kmajor_is_the_blockwise_transpose():
+@pytest.mark.parametrize("n,G,d", [(5, 128, 192), (7, 32, 192), (3, 64, 64)])
+def test_pack_kmajor_is_the_blockwise_transpose(n, G, d):
     dev()
     r = np.random.default_rng(0)
-    n, G, d = 5, 128, 192
     from synth import bf16_round
     W = bf16_round(r.standard_normal((n * G, d)).astype(np.float32))
     P = host(wide.pack_kmajor(bf16(W), n))
@@ -54,6 +54,11 @@ SHAPES = [
     (257, 256, 1024, 8, 1.0, "ones"),
     (257, 256, 1024, 8, 0.0, "zeros"),
     (1, 256, 1024, 16, 0.5, "topk"),
+    # groups of 32 channels: 64-wide FFN up tiles; FFN down K slices over pairs of groups
+    (300, 256, 512, 16, 0.5, "topk"),
+    (1100, 512, 1024, 32, 0.75, "bernoulli"),
+    (257, 256, 2048, 64, 0.25, "clustered"),
+    (129, 384, 256, 8, 1.0, "ones"),
 ]
 
 
@@ -100,5 +105,21 @@ def test_ffn_prefill_max_tokens_sampled():
     assert np.all(np.isfinite(got))
     rows = np.sort(np.random.default_rng(4).choice(T, 64, replace=False))
     rows[0], rows[-1] = 0, T - 1
+    ref = ffn_masked(c["X"][rows], c["mask"][rows], c["W_gate"], c["W_up"], c["W_down"])
+    assert rel_err(got[rows], ref) <= TOL
+
+
+@needs_gpu
+def test_ffn_prefill_3b_groups_of_32_sampled():
+    """The Llama-3.2-3B FFN shape (T=4096, d=3072, d_ff=8192) in 256 groups of 32
+    channels, the most groups the library takes, router-style top-k 128 of 256:
+    64 sampled rows against the oracle; every row finite."""
+    dev()
+    log("ffn prefill 3B, 256 groups of 32 (sampled)")
+    c = ffn_case("ffn_3b_g32", 4096, 3072, 8192, 256, 0.5, "topk")
+    got = _gpu_ffn(c)
+    assert np.all(np.isfinite(got))
+    rows = np.sort(np.random.default_rng(6).choice(4096, 64, replace=False))
+    rows[0], rows[-1] = 0, 4095
     ref = ffn_masked(c["X"][rows], c["mask"][rows], c["W_gate"], c["W_up"], c["W_down"])
     assert rel_err(got[rows], ref) <= TOL

@@ -43,6 +43,7 @@ SHAPES = [
     (513, 512, 2048, 16, 16, 4, 0.5, "bernoulli"),
     (300, 256, 1536, 12, 8, 8, 0.75, "clustered"),
     (64, 256, 1024, 8, 8, 2, 1.0, "ones"),
+    (400, 256, 512, 16, 8, 2, 0.5, "router"),   # FFN groups of 32 channels
 ]
 
 
