@@ -421,6 +421,65 @@ class AttnDecodeMaskedCache:
         return time.perf_counter() - t0
 
 
+class AttnDecodePaged(AttnDecodeMaskedCache):
+    """AttnDecodeMaskedCache's caches and lengths held in a paged pool: pages of
+    `page_size` slots dealt to the (sequence, group) caches in a seeded random order,
+    one page table per pair."""
+
+    def __init__(self, B=16, pos=8192, page_size=16):
+        super().__init__(B, pos)
+        m = self.m
+        self.name = f"attn_decode_paged_8b_p{page_size}"
+        self.ps = page_size
+        self.max_pages = (pos + 1 + page_size - 1) // page_size
+        self.n_pages = B * m["n_kv"] * self.max_pages
+        perm = np.random.default_rng(page_size).permutation(self.n_pages)
+        self.table = perm.reshape(B, m["n_kv"], self.max_pages).astype(np.int32)
+        self.config.update(workload=self.name, kv_cap=self.max_pages * page_size,
+                           page_size=page_size, pages_per_pair=self.max_pages,
+                           pool_pages=self.n_pages, page_order="shuffled")
+
+    def _pool(self, cache):
+        B, n_kv, cap, _ = cache.shape
+        pad = np.zeros((B, n_kv, self.max_pages * self.ps, HD), cache.dtype)
+        pad[:, :, :cap] = cache
+        pool = np.empty((self.n_pages, self.ps, HD), cache.dtype)
+        pool[self.table.reshape(-1)] = pad.reshape(-1, self.ps, HD)
+        return pool
+
+    def upload(self, torch, wide, bf16, u8):
+        super().upload(torch, wide, bf16, u8)
+        c = self.c
+        pools = self._pool(c["K_cache"]), self._pool(c["V_cache"])
+        self.sets = [s[:4] + (bf16(pools[0]), bf16(pools[1])) for s in self.sets]
+        self.pt = torch.from_numpy(self.table).cuda()
+        m = self.m
+        self.ws = torch.empty(wide.attn_proj_masked_workspace(
+            self.T, m["d"], m["n_q"], m["n_kv"], mode="decode", kv_cap=self.max_pages * self.ps),
+            dtype=torch.uint8, device="cuda")
+
+    def step(self, ones=False):
+        m = self.m
+        Wq, Wk, Wv, Wo, Kp, Vp = self.sets[self.i % len(self.sets)]
+        self.i += 1
+        self.wide.attn_decode_masked_paged(self.X, self.ones if ones else self.mask, Wq, Wk, Wv,
+                                           Wo, n_q=m["n_q"], n_kv=m["n_kv"], K_pool=Kp,
+                                           V_pool=Vp, page_table=self.pt,
+                                           kv_len=self.full if ones else self.L, pos=self.pos,
+                                           out=self.Y, workspace=self.ws)
+
+    def oracle_sample(self, S):
+        from oracle import attn_masked, paged_to_contiguous
+        c, m = self.c, self.m
+        t0 = time.perf_counter()
+        Kc, Vc, L = paged_to_contiguous(self._pool(c["K_cache"]), self._pool(c["V_cache"]),
+                                        self.table[:S], self.lens[:S])
+        attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
+                    n_kv=m["n_kv"], head_dim=HD, decode=True, K_cache=Kc, V_cache=Vc,
+                    kv_len=L, pos=self.pos)
+        return time.perf_counter() - t0
+
+
 class LayerDecode:
     """Llama-3.1-8B-shaped decoder layer, decode: batch 32 over an 8192-entry cache."""
 
@@ -531,7 +590,9 @@ WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
              "attn_decode_8b": AttnDecode, "ffn_decode_8b_B1": lambda: FfnDecode(1),
              "ffn_decode_8b_B8": lambda: FfnDecode(8), "ffn_decode_8b_B32": lambda: FfnDecode(32),
              "ffn_decode_8b_B64": lambda: FfnDecode(64), "router_prefill_8b": RouterPrefill,
-             "attn_decode_masked_cache_8b": AttnDecodeMaskedCache}
+             "attn_decode_masked_cache_8b": AttnDecodeMaskedCache,
+             "attn_decode_paged_8b_p16": lambda: AttnDecodePaged(page_size=16),
+             "attn_decode_paged_8b_p128": lambda: AttnDecodePaged(page_size=128)}
 
 
 # ------------------------------------------------------------- measurement

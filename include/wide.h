@@ -217,6 +217,40 @@ int wide_attn_decode_masked_cache(const uint16_t* X, const uint8_t* mask, const 
                                   void* stream);
 
 /*
+ * wide_attn_decode_masked_paged - wide_attn_decode_masked_cache over a paged cache:
+ * the (sequence, group) caches live in pages of a shared pool, found through a page
+ * table (the paged layout of the masked-cache decode, gist.science §2.A groups;
+ * the pages give no page format, this one is the library's own).
+ *
+ * K_pool, V_pool [n_pages, page_size, 128] bf16 (device, in/out): page p holds
+ *         page_size consecutive slots of one (sequence, group) cache.
+ * page_size   power of two, >= 16.
+ * page_table  [B, n_kv_heads, max_pages] int32 (device, input): slot s of pair
+ *         (b, g) is row s % page_size of page page_table[b, g, s / page_size];
+ *         a pair holds up to max_pages * page_size slots.  An entry outside
+ *         [0, n_pages) is an unmapped page: its slots read as zero keys and values
+ *         and take no write.  A pair whose new slot kv_len[b, g] is on an unmapped
+ *         page behaves like a dropped pair (nothing written, zero output).
+ *         Pages may be shared between pairs for reading; the new slots of the kept
+ *         pairs must be distinct pool rows (two writes to one row race).
+ * kv_len  [B, n_kv_heads] int32 (device, input): as in
+ *         wide_attn_decode_masked_cache, with kv_cap = max_pages * page_size.
+ * Other arguments as wide_attn_decode_masked_cache; workspace:
+ * wide_attn_proj_masked_workspace(B, d_model, cfg, WIDE_DECODE, max_pages * page_size).
+ * All pointers 16-byte aligned.  Returns WIDE_EINVAL for a bad page size, pool or
+ * table, WIDE_EUNSUPPORTED when n_pages * page_size or max_pages * page_size rows
+ * of 256 bytes pass 2 GiB.
+ */
+int wide_attn_decode_masked_paged(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
+                                  const uint16_t* Wk, const uint16_t* Wv,
+                                  const uint16_t* Wo_packed, int B, int d_model,
+                                  const wide_attn_cfg* cfg, uint16_t* K_pool, uint16_t* V_pool,
+                                  int n_pages, int page_size, const int32_t* page_table,
+                                  int max_pages, const int32_t* kv_len, int pos, uint16_t* Y,
+                                  void* workspace, size_t workspace_bytes, uint32_t flags,
+                                  void* stream);
+
+/*
  * wide_layer_masked - one pre-norm decoder layer with both masked sublayers:
  *   u = RMSNorm(x; rms1), h = x + Attn(u; attn_mask), w = RMSNorm(h; rms2),
  *   y = h + FFN(w; ffn_mask),  RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma.

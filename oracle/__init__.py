@@ -13,7 +13,7 @@ each function follows on the pages, and for the readings taken where the pages
 are silent.
 """
 from .wide_oracle import (attn_masked, ffn_masked, layer_masked, mask_reorder,
-                          rmsnorm, rope, router_topk)
+                          paged_to_contiguous, rmsnorm, rope, router_topk)
 
 __all__ = ["mask_reorder", "ffn_masked", "attn_masked", "layer_masked", "rmsnorm", "rope",
-           "router_topk"]
+           "router_topk", "paged_to_contiguous"]

@@ -50,6 +50,12 @@ design notes):
   one binary execute/skip decision per group [gist §2A] and that routing is
   learned per token [abstract]; the router's form and the top-k rule are the
   plainest reading of a fixed keep ratio.
+* R10 paged masked cache: the pages name a paged layout for the decode caches
+  but give no page format.  The one taken here: K and V pools [n_pages, page_size,
+  hd]; a page table [B, n_kv, max_pages] gives the page of each page_size-slot
+  stretch of a (sequence, group) cache.  A slot on an unmapped page (entry outside
+  [0, n_pages)) holds zeros; a pair whose new slot is on one is treated like an
+  out-of-range length (R5).  Everything else is R5 on the gathered caches.
 """
 from __future__ import annotations
 
@@ -252,6 +258,36 @@ def attn_masked(X, mask, Wq, Wk, Wv, Wo, *, n_q: int, n_kv: int, head_dim: int,
     Y = O.reshape(T, n_q * hd) @ Wo
     out = (Y, K, V)
     return out + (O,) if return_o else out
+
+
+def paged_to_contiguous(K_pool, V_pool, page_table, kv_len):
+    """Reading R10: the (sequence, group) caches a paged pool holds, gathered into
+    the contiguous layout of R5, and the lengths R5 then takes.
+
+    K_pool, V_pool [n_pages, page_size, hd]; page_table [B, n_kv, max_pages];
+    kv_len [B, n_kv].  Returns (K_cache, V_cache, kv_len_eff) with caches
+    [B, n_kv, max_pages * page_size, hd]: slot s of pair (b, g) is row
+    s % page_size of page page_table[b, g, s // page_size], or zeros when that
+    entry is outside [0, n_pages).  kv_len_eff is kv_len, except -1 (out of range)
+    for a pair whose new slot kv_len[b, g] lies on an unmapped page."""
+    n_pages, ps = K_pool.shape[0], K_pool.shape[1]
+    table = np.asarray(page_table)
+    B, n_kv, max_pages = table.shape
+    cap = max_pages * ps
+    K = np.zeros((B, n_kv, cap) + K_pool.shape[2:], K_pool.dtype)
+    V = np.zeros_like(K)
+    L = np.array(kv_len, dtype=np.int64, copy=True)
+    for b in range(B):
+        for g in range(n_kv):
+            for p in range(max_pages):
+                e = int(table[b, g, p])
+                if 0 <= e < n_pages:
+                    K[b, g, p * ps:(p + 1) * ps] = K_pool[e]
+                    V[b, g, p * ps:(p + 1) * ps] = V_pool[e]
+            lb = int(L[b, g])
+            if 0 <= lb < cap and not 0 <= int(table[b, g, lb // ps]) < n_pages:
+                L[b, g] = -1
+    return K, V, L
 
 
 # -------------------------------------------------------------------- layer

@@ -7,7 +7,8 @@ status; every step of the computation runs in the HIP kernels of the library.
 There is no fallback: without the built library, or without a GPU, the calls
 raise.
 """
-from .binding import (LIB_PATH, WideError, attn_decode_masked_cache, attn_proj_masked,
+from .binding import (LIB_PATH, WideError, attn_decode_masked_cache, attn_decode_masked_paged,
+                      attn_proj_masked,
                       attn_proj_masked_workspace,
                       ffn_masked, ffn_masked_workspace, layer_masked, layer_masked_workspace,
                       lib, mask_reorder, pack_kmajor, pack_router, router_topk, trace_collect,
@@ -16,7 +17,7 @@ from .binding import (LIB_PATH, WideError, attn_decode_masked_cache, attn_proj_m
 __all__ = [
     "LIB_PATH", "WideError", "lib", "mask_reorder", "pack_kmajor", "pack_router", "router_topk", "ffn_masked",
     "ffn_masked_workspace", "attn_proj_masked", "attn_proj_masked_workspace",
-    "attn_decode_masked_cache", "layer_masked",
+    "attn_decode_masked_cache", "attn_decode_masked_paged", "layer_masked",
     "layer_masked_workspace", "trace_enable", "trace_reset", "trace_collect", "WIDE_PREFILL",
     "WIDE_DECODE",
 ]

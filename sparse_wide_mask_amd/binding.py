@@ -45,6 +45,9 @@ _SIGS = {
     "wide_layer_masked_workspace": ([_i, C.POINTER(WideLayerCfg), _i, _i], _sz),
     "wide_attn_decode_masked_cache": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _p,
                                        _p, _i, _p, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+    "wide_attn_decode_masked_paged": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg),
+                                       _p, _p, _i, _i, _p, _i, _p, _i, _p, _p, _sz, C.c_uint32,
+                                       _p], _i),
     "wide_trace_enable": ([_i], _i),
     "wide_trace_collect": ([], _i),
     "wide_trace_get": ([_i, C.c_char_p, _i, C.POINTER(_i), C.POINTER(C.c_double)], _i),
@@ -300,6 +303,39 @@ def attn_decode_masked_cache(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, K_cac
                                              _ptr(V_cache), kv_cap, _ptr(kv_len), int(pos), _ptr(Y),
                                              _ptr(ws), ws.numel(), 0, _stream())
     _check("wide_attn_decode_masked_cache", st)
+    return Y
+
+
+def attn_decode_masked_paged(X, mask, Wq, Wk, Wv, Wo_packed, *, n_q, n_kv, K_pool, V_pool,
+                             page_table, kv_len, pos, head_dim=128, rope_theta=0.0, out=None,
+                             workspace=None):
+    """wide_attn_decode_masked_paged: attn_decode_masked_cache over a paged cache.
+    K_pool, V_pool [n_pages, page_size, head_dim] bf16; page_table [B, n_kv, max_pages]
+    int32 (slot s of pair (b, g) is row s % page_size of page page_table[b, g,
+    s // page_size]); kv_len int32 [B, n_kv], not modified.  Returns Y [B, d] bf16;
+    writes the kept pairs' new K/V into their pages."""
+    for t, nm in ((X, "X"), (Wq, "Wq"), (Wk, "Wk"), (Wv, "Wv"), (Wo_packed, "Wo_packed"),
+                  (K_pool, "K_pool"), (V_pool, "V_pool")):
+        _dev(t, torch.bfloat16, nm)
+    _dev(mask, torch.uint8, "mask")
+    _dev(kv_len, torch.int32, "kv_len")
+    _dev(page_table, torch.int32, "page_table")
+    B, d = X.shape
+    n_pages, page_size = K_pool.shape[0], K_pool.shape[1]
+    if tuple(V_pool.shape) != tuple(K_pool.shape) or page_table.dim() != 3:
+        raise ValueError("K_pool and V_pool must match; page_table must be [B, n_kv, max_pages]")
+    max_pages = page_table.shape[2]
+    cfg = _attn_cfg(n_q, n_kv, head_dim, rope_theta)
+    ws_bytes = int(lib().wide_attn_proj_masked_workspace(B, d, C.byref(cfg), WIDE_DECODE,
+                                                         max_pages * page_size))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((B, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_attn_decode_masked_paged(_ptr(X), _ptr(mask), _ptr(Wq), _ptr(Wk), _ptr(Wv),
+                                             _ptr(Wo_packed), B, d, C.byref(cfg), _ptr(K_pool),
+                                             _ptr(V_pool), n_pages, page_size, _ptr(page_table),
+                                             max_pages, _ptr(kv_len), int(pos), _ptr(Y), _ptr(ws),
+                                             ws.numel(), 0, _stream())
+    _check("wide_attn_decode_masked_paged", st)
     return Y
 
 

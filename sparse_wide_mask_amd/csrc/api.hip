@@ -188,12 +188,13 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
               const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
               int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
               const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s,
-              const int32_t* pair_len = nullptr, int pos = -1, bool reorder = true) {
+              const int32_t* pair_len = nullptr, int pos = -1, bool reorder = true,
+              const PagedKV* paged = nullptr) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
                        kv_cap, pair_len, pos < 0 ? kv_len : pos, w.Qc, w.Opart, w.Mpart, w.Lpart,
-                       w.O, s);
+                       w.O, s, paged);
     launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, w.kpart,
                         Y, s);
     return;
@@ -426,6 +427,47 @@ int wide_attn_decode_masked_cache(const uint16_t* X, const uint8_t* mask, const 
   (void)hipGetLastError();
   attn_run(X, mask, Wq, Wk, Wv, Wo_packed, B, d_model, cfg, WIDE_DECODE, K_cache, V_cache, 0,
            kv_cap, nullptr, Y, w, as_stream(stream), kv_len, pos);
+  return launch_status();
+}
+
+int wide_attn_decode_masked_paged(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
+                                  const uint16_t* Wk, const uint16_t* Wv,
+                                  const uint16_t* Wo_packed, int B, int d_model,
+                                  const wide_attn_cfg* cfg, uint16_t* K_pool, uint16_t* V_pool,
+                                  int n_pages, int page_size, const int32_t* page_table,
+                                  int max_pages, const int32_t* kv_len, int pos, uint16_t* Y,
+                                  void* workspace, size_t workspace_bytes, uint32_t flags,
+                                  void* stream) {
+  int st = attn_check(B, d_model, cfg, WIDE_DECODE);
+  if (st != WIDE_OK) return st;
+  if (flags != 0 || pos < 0) return WIDE_EINVAL;
+  if (page_size < 16 || (page_size & (page_size - 1)) || n_pages < 1 || max_pages < 1)
+    return WIDE_EINVAL;
+  if (!aligned16(K_pool) || !aligned16(V_pool) || K_pool == V_pool) return WIDE_EINVAL;
+  // pool rows and one pair's slots each addressable by a 32-bit byte offset
+  if (!fits((int64_t)n_pages * page_size, kHeadDim) ||
+      !fits((int64_t)max_pages * page_size, kHeadDim))
+    return WIDE_EUNSUPPORTED;
+  const int kv_cap = max_pages * page_size;
+  if (B == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(mask) || !aligned16(Wq) || !aligned16(Wk) || !aligned16(Wv) ||
+      !aligned16(Wo_packed) || !aligned16(Y) || !aligned16(kv_len) || !aligned16(page_table) ||
+      (void*)Y == (void*)X)
+    return WIDE_EINVAL;
+  for (const void* p : {(const void*)kv_len, (const void*)page_table})
+    if (p == (const void*)K_pool || p == (const void*)V_pool) return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_attn(probe, B, d_model, cfg, WIDE_DECODE, kv_cap);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  AttnWs w = carve_attn(c, B, d_model, cfg, WIDE_DECODE, kv_cap);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const PagedKV pg{page_table, shift, n_pages};
+  (void)hipGetLastError();
+  attn_run(X, mask, Wq, Wk, Wv, Wo_packed, B, d_model, cfg, WIDE_DECODE, K_pool, V_pool, 0, kv_cap,
+           nullptr, Y, w, as_stream(stream), kv_len, pos, true, &pg);
   return launch_status();
 }
 

@@ -69,13 +69,37 @@ WIDE_DEV bf16x8 xload(rsrc_t r, uint32_t off) {
 // tokens that skipped the group left no entry).  A length outside [0, kv_cap)
 // makes the pair write nothing and output zero.  pos is the new token's RoPE
 // position.
+// Layout: contiguous (pt null), slot s of pair (b, g) at row (b n_groups + g)
+// kv_cap + s; or paged, a pool of n_pages pages of 2^page_shift rows and a page
+// table pt [B, n_groups, kv_cap >> page_shift] that maps the pair's slot s to row
+// s mod 2^page_shift of page pt[b, g, s >> page_shift].  A slot on an unmapped
+// page (entry outside [0, n_pages)) reads as zeros and takes no write; a pair
+// whose new slot is on one takes no part, like an out-of-range length.
 struct DecCache {
   const int32_t* kvl;
   int kv_len, kv_cap, pos;
+  const int32_t* pt;
+  int page_shift, n_pages;
   WIDE_DEV int len(int b, int g, int n_groups) const {
     return kvl ? kvl[b * n_groups + g] : kv_len;
   }
   WIDE_DEV bool ok(int l) const { return l >= 0 && l < kv_cap; }
+  // cache row of slot s in [0, kv_cap) of pair (b, g); -1 on an unmapped page
+  WIDE_DEV long long row(int b, int g, int n_groups, int s) const {
+    const size_t pair = (size_t)b * n_groups + g;
+    if (!pt) return (long long)(pair * kv_cap + s);
+    const int p = pt[pair * (size_t)(kv_cap >> page_shift) + (s >> page_shift)];
+    return p >= 0 && p < n_pages ? ((long long)p << page_shift) + (s & ((1 << page_shift) - 1))
+                                 : -1;
+  }
+  // the pair takes part: its length is in range and its new slot is mapped
+  WIDE_DEV bool live(int b, int g, int n_groups, int l) const {
+    return ok(l) && (!pt || row(b, g, n_groups, l) >= 0);
+  }
+  // rows of the cache buffers
+  WIDE_DEV size_t rows(int B, int n_groups) const {
+    return pt ? (size_t)n_pages << page_shift : (size_t)B * n_groups * kv_cap;
+  }
 };
 
 template <int MODE>
@@ -122,8 +146,8 @@ struct NmCol {
         out0[((size_t)tok * (n_groups * r) + g * r + hh) * kHdD + jrow] = bits;
       } else {
         const int slot = dc.len(tok, g, n_groups);
-        if (dc.ok(slot))
-          (hh == r ? Kc : Vc)[(((size_t)tok * n_groups + g) * dc.kv_cap + slot) * kHdD + jrow] = bits;
+        const long long row = dc.ok(slot) ? dc.row(tok, g, n_groups, slot) : -1;
+        if (row >= 0) (hh == r ? Kc : Vc)[(size_t)row * kHdD + jrow] = bits;
       }
     }
   }
@@ -649,6 +673,10 @@ constexpr int kKeySlices = kKeyChunk / 32;                // 32-key slices of th
 //   P V     thread = (4 head dims, 32 keys) for all r heads, then a sum over
 //           the key slices through LDS.
 // Writes unnormalised partial outputs and the chunk's (max, sum) per head.
+// PAGED: the cache rows come through the page table (DecCache).  Pages hold at
+// least 16 slots, so a 16-key MFMA block and a 4-row V group never cross a page,
+// and a chunk spans at most 8 pages, whose entries lanes 0..7 load once.
+template <bool PAGED>
 __global__ void __launch_bounds__(kKeyChunk)
     attn_decode_partial(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
                         const uint16_t* __restrict__ Vc, const uint8_t* __restrict__ mask, int B,
@@ -661,29 +689,55 @@ __global__ void __launch_bounds__(kKeyChunk)
   __shared__ float sRed[8][kAttnWaves];
   const int c = blockIdx.x % nch, rest = blockIdx.x / nch;
   const int g = rest % n_kv, b = rest / n_kv;
-  if (!mask[(size_t)b * n_kv + g]) return;  // l=0: the token dropped this group
-  // this pair's keys: its cache entries 0..len-1 and the new token at slot len
-  const int len = dc.len(b, g, n_kv);
-  const int k0 = c * kKeyChunk;
-  if (!dc.ok(len) || k0 > len) return;  // no such chunk for this pair
-  const int nkeys = min(kKeyChunk, len + 1 - k0);
+  const int k0 = c * kKeyChunk;  // < kv_cap: the grid has the chunks of kv_cap slots
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // The pair's keep bit, its length (its keys are cache entries 0..len-1 and the new
+  // token at slot len) and, paged, the chunk's page entries (lane l = page l of the
+  // chunk) depend on none of each other: all are requested before the first test.
+  int pgv = -1;
+  if constexpr (PAGED) {
+    const int first = k0 >> dc.page_shift, max_pages = dc.kv_cap >> dc.page_shift;
+    const int npg = min(max(kKeyChunk >> dc.page_shift, 1), max_pages - first);
+    if (lane < npg) pgv = dc.pt[((size_t)b * n_kv + g) * (size_t)max_pages + first + lane];
+  }
+  const int keep = mask[(size_t)b * n_kv + g];
+  const int len = dc.len(b, g, n_kv);
+  asm volatile("" ::"v"(keep), "s"(len), "v"(pgv));
+  if (!keep) return;  // l=0: the token dropped this group
+  // no such chunk for this pair.  (A paged pair whose new slot is unmapped still
+  // runs: the combine outputs zero for it without reading these partials.)
+  if (!dc.ok(len) || k0 > len) return;
+  const int nkeys = min(kKeyChunk, len + 1 - k0);
   const int nq = n_kv * r;
-  const int kv_cap = dc.kv_cap;
-  const size_t kvbase = ((size_t)b * n_kv + g) * kv_cap + k0;  // first key row of the chunk
-  const uint32_t cache_bytes = (uint32_t)((size_t)B * n_kv * kv_cap * kHdD * 2);
+  const uint32_t cache_bytes = (uint32_t)(dc.rows(B, n_kv) * kHdD * 2);
   const int m16 = lane & 15, q4 = lane >> 4;
+  // cache row of the chunk's key rel (rel a multiple of 4, wave-uniform), -1 if unmapped
+  const size_t kvbase = ((size_t)b * n_kv + g) * dc.kv_cap + k0;
+  auto row_of = [&](int rel) -> long long {
+    if constexpr (!PAGED) {
+      return (long long)(kvbase + rel);
+    } else {
+      const int s = k0 + rel;
+      const int p = __builtin_amdgcn_readlane(
+          pgv, __builtin_amdgcn_readfirstlane((s >> dc.page_shift) - (k0 >> dc.page_shift)));
+      return p >= 0 && p < dc.n_pages
+                 ? ((long long)p << dc.page_shift) + (s & ((1 << dc.page_shift) - 1))
+                 : -1;
+    }
+  };
 
   // K operand: block i of wave w = keys 16 (4 w + i) + m16, dims 32 ks + 8 q4 .. +7
   const rsrc_t kr = make_rsrc(Kc, cache_bytes);
   bf16x8 kf[kKeyBlocks][4];
 #pragma unroll
   for (int i = 0; i < kKeyBlocks; ++i) {
-    const int key = 16 * (kKeyBlocks * wave + i) + m16;
+    const int rel0 = 16 * (kKeyBlocks * wave + i), key = rel0 + m16;
+    const long long r0 = row_of(rel0);
+    const bool in = key < nkeys && r0 >= 0;
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks)
       kf[i][ks] =
-          xload(kr, key < nkeys ? (uint32_t)(((kvbase + key) * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
+          xload(kr, in ? (uint32_t)(((r0 + m16) * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
   }
   // V: instruction q of wave w fills the 4 rows from 4 (kAttnWaves q + w) (1 KB);
   // rows past the chunk's keys read as zeros
@@ -693,8 +747,10 @@ __global__ void __launch_bounds__(kKeyChunk)
 #pragma unroll
     for (int q = 0; q < kKeyChunk / (4 * kAttnWaves); ++q) {
       const int row0 = 4 * (kAttnWaves * q + wave), row = row0 + q4;
-      const uint32_t off =
-          row < nkeys ? (uint32_t)(((kvbase + row) * kHdD + m16 * 8) * 2) : kSkip;
+      const long long r0 = row_of(row0);
+      const uint32_t off = row < nkeys && r0 >= 0
+                               ? (uint32_t)(((r0 + q4) * kHdD + m16 * 8) * 2)
+                               : kSkip;
       lds_dma16(vsrd, vlds + row0 * kHdD * 2, off);
     }
   }
@@ -836,7 +892,7 @@ __global__ void __launch_bounds__(kCmbThreads)
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int j = tid % kHdD, sl = tid / kHdD;
   const int len = dc.len(b, g, n_kv);
-  if (!dc.ok(len)) {  // a pair with an out-of-range length outputs zero
+  if (!dc.live(b, g, n_kv, len)) {  // a pair with an out-of-range length outputs zero
     if (sl == 0) O[((size_t)b * nq + h) * kHdD + j] = 0;
     return;
   }
@@ -945,10 +1001,17 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
                         const uint16_t* Wk, const uint16_t* Wv, int B, int d,
                         int n_kv, int r, float rope_theta, uint16_t* Kc, uint16_t* Vc, int kv_len,
                         int kv_cap, const int32_t* kvl, int pos, uint16_t* Qd, float* Opart,
-                        float* Mpart, float* Lpart, uint16_t* O, hipStream_t s) {
+                        float* Mpart, float* Lpart, uint16_t* O, hipStream_t s,
+                        const PagedKV* paged) {
   const int chunks = (r + 2) * 8;  // 16-row chunks of the group's q, k, v heads
   const float log2_theta = rope_theta > 0.f ? log2f(rope_theta) : 0.f;
-  const DecCache dc{kvl, kv_len, kv_cap, pos};
+  const DecCache dc{kvl,
+                    kv_len,
+                    kv_cap,
+                    pos,
+                    paged ? paged->table : nullptr,
+                    paged ? paged->page_shift : 0,
+                    paged ? paged->n_pages : 0};
   {
     WIDE_TRACE("attn_qkv_decode", s);
     const int nrb = (B + 15) / 16;
@@ -973,8 +1036,9 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
   const float scale_log2 = 1.4426950408889634f / sqrtf((float)kHdD);
   {
     WIDE_TRACE("attn_core_decode", s);
-    attn_decode_partial<<<B * n_kv * nch, kKeyChunk, 0, s>>>(Qd, Kc, Vc, mask, B, n_kv, r, dc, nch,
-                                                             scale_log2, Opart, Mpart, Lpart);
+    auto k = paged ? attn_decode_partial<true> : attn_decode_partial<false>;
+    k<<<B * n_kv * nch, kKeyChunk, 0, s>>>(Qd, Kc, Vc, mask, B, n_kv, r, dc, nch, scale_log2, Opart,
+                                           Mpart, Lpart);
   }
   {
     WIDE_TRACE("attn_combine_decode", s);

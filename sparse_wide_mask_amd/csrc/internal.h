@@ -82,11 +82,19 @@ void launch_kmask_decode(KmUse use, const uint16_t* A, const uint16_t* Wp,
                          const uint16_t* residual, float* part, uint16_t* Y, hipStream_t s);
 // Key chunks of a decode attention over kv_len cache entries plus the new token.
 int attn_decode_chunks(int kv_len);
+// A paged K/V cache: pools of n_pages pages of 2^page_shift rows (K and V alike)
+// and the page table [B, n_kv, kv_cap >> page_shift] of each (sequence, group).
+struct PagedKV {
+  const int32_t* table;
+  int page_shift, n_pages;
+};
+
 void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq,
                         const uint16_t* Wk, const uint16_t* Wv, int B, int d,
                         int n_kv, int r, float rope_theta, uint16_t* Kc, uint16_t* Vc, int kv_len,
                         int kv_cap, const int32_t* kvl, int pos, uint16_t* Qd, float* Opart,
-                        float* Mpart, float* Lpart, uint16_t* O, hipStream_t s);
+                        float* Mpart, float* Lpart, uint16_t* O, hipStream_t s,
+                        const PagedKV* paged = nullptr);
 
 // Router logits X R^T and the top-k mask (ties to the lower group index), with
 // the mask's packed bit words; logits and packed may be null.  n <= 256.  R in

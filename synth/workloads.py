@@ -91,6 +91,38 @@ def attn_case(cfg: str, T: int, d: int = 4096, n_q: int = 32, n_kv: int = 8, hd:
     return out
 
 
+def paged_cache(cfg: str, B: int, n_kv: int, page_size: int, max_pages: int, hd: int = 128, *,
+                spare_pages: int = 5, unmapped: float = 0.0, shared_pages: int = 0) -> dict:
+    """A paged K/V cache for B sequences x n_kv groups: pools [n_pages, page_size, hd]
+    ~ N(0,1), a page table [B, n_kv, max_pages] int32 that deals the pages out in a
+    seeded random order (spare_pages pages stay unused), and per-pair lengths
+    kv_len [B, n_kv] int32 uniform over the capacity (the first pair at 0 and the last
+    at capacity - 1 when nothing is shared).
+
+    unmapped: the fraction of table entries replaced by unmapped ones (half -1, half
+    past the pool).  shared_pages: every pair's first shared_pages entries name the
+    first pair's, and every length is at least shared_pages * page_size, so the new
+    slots fall past the shared pages."""
+    r = rng(cfg, "page_table")
+    n_pages = B * n_kv * max_pages + spare_pages
+    table = r.permutation(n_pages)[:B * n_kv * max_pages].reshape(B, n_kv, max_pages)
+    if shared_pages:
+        table[:, :, :shared_pages] = table[0, 0, :shared_pages]
+    if unmapped:
+        hit = r.random(table.shape) < unmapped
+        table[hit] = np.where(r.random(table.shape) < 0.5, -1, n_pages + 3)[hit]
+    cap = max_pages * page_size
+    lo = shared_pages * page_size
+    L = rng(cfg, "kv_len").integers(lo, cap, size=(B, n_kv))
+    if not shared_pages:
+        L.flat[0], L.flat[-1] = 0, cap - 1
+    return dict(K_pool=normal(cfg, "K_pool", (n_pages, page_size, hd)),
+                V_pool=normal(cfg, "V_pool", (n_pages, page_size, hd)),
+                page_table=table.astype(np.int32), kv_len=L.astype(np.int32),
+                meta=dict(B=B, n_kv=n_kv, page_size=page_size, max_pages=max_pages,
+                          n_pages=n_pages, unmapped=unmapped, shared_pages=shared_pages))
+
+
 def layer_case(cfg: str, T: int, d: int = 4096, F: int = 14336, n_ffn: int = 112,
                n_q: int = 32, n_kv: int = 8, hd: int = 128, keep: float = 0.5,
                mask_kind: str = "router", *, decode: bool = False, kv_len: int = 0,

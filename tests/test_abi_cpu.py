@@ -94,6 +94,29 @@ def test_masked_cache_decode_validation_before_any_launch(L):
     assert L.wide_attn_decode_masked_cache(*args(4, 4096, C.byref(cfg), 10, 0)) == 1   # NULL caches
 
 
+def test_paged_decode_validation_before_any_launch(L):
+    from sparse_wide_mask_amd import binding as b
+    z = C.c_void_p(0)
+    k, v = C.c_void_p(16), C.c_void_p(32)  # aligned, never dereferenced
+    cfg = b.WideAttnCfg(32, 8, 128, 0.0)
+
+    def call(B=4, cfgp=None, pages=8, ps=16, maxp=4, pos=0, kp=k, vp=v):
+        return L.wide_attn_decode_masked_paged(z, z, z, z, z, z, B, 4096, cfgp or C.byref(cfg),
+                                               kp, vp, pages, ps, z, maxp, z, pos, z, z, 0, 0, z)
+    assert call(pos=-1) == 1                      # pos < 0
+    assert call(ps=8) == 1                        # page below 16 slots
+    assert call(ps=48) == 1                       # not a power of two
+    assert call(pages=0) == 1                     # empty pool
+    assert call(maxp=0) == 1                      # no pages per pair
+    assert call(kp=z) == 1                        # NULL pool
+    assert call(vp=k) == 1                        # K and V pools alias
+    assert call(B=65) == 2                        # batch > 64
+    assert call(pages=1 << 20, ps=64) == 2        # pool past 2 GiB
+    assert call(maxp=1 << 20, ps=64) == 2         # a pair's slots past 2 GiB
+    assert call(B=0) == 0                         # empty batch: no-op
+    assert call() == 1                            # NULL X, table, lengths
+
+
 def test_pack_router_validation(L):
     z = C.c_void_p(0)
     assert L.wide_pack_router(z, 16, 256, z, z) == 1

@@ -256,3 +256,84 @@ def test_per_pair_lengths_equal_the_uniform_length():
                     K_cache=Kc, V_cache=Vc, kv_len=L0)
     np.testing.assert_allclose(c[0], e[0], rtol=1e-12, atol=1e-12)
     assert np.all(c[1][0] == 0) and np.all(c[2][0] == 0)
+
+
+# --------------------------------------------------------- paged caches (R10)
+
+def _scatter_pages(C, table, n_pages, fill):
+    """Pool [n_pages, ps, hd] holding the contiguous caches C [B, n_kv, cap, hd] at
+    the pages the table names; unnamed pages hold `fill`."""
+    B, n_kv, max_pages = table.shape
+    ps = C.shape[2] // max_pages
+    pool = np.full((n_pages, ps, C.shape[3]), fill)
+    for b, g, p in itertools.product(range(B), range(n_kv), range(max_pages)):
+        if 0 <= table[b, g, p] < n_pages:
+            pool[table[b, g, p]] = C[b, g, p * ps:(p + 1) * ps]
+    return pool
+
+
+def test_paged_gather_inverts_a_scatter():
+    """Any one-to-one table: gathering the pool that the table scattered gives back
+    the contiguous caches bit for bit, whatever the unused pages hold."""
+    from oracle import paged_to_contiguous
+    rng = np.random.default_rng(21)
+    B, n_kv, max_pages, ps, hd, n_pages = 3, 2, 4, 4, 3, 30
+    K, V = rng.standard_normal((2, B, n_kv, max_pages * ps, hd))
+    table = rng.permutation(n_pages)[:B * n_kv * max_pages].reshape(B, n_kv, max_pages)
+    L = rng.integers(0, max_pages * ps, (B, n_kv))
+    Kg, Vg, Lg = paged_to_contiguous(_scatter_pages(K, table, n_pages, 7.0),
+                                     _scatter_pages(V, table, n_pages, -7.0), table, L)
+    np.testing.assert_array_equal(Kg, K)
+    np.testing.assert_array_equal(Vg, V)
+    np.testing.assert_array_equal(Lg, L)
+
+
+def test_paged_gather_unmapped_and_shared_pages():
+    """Unmapped entries (negative or past the pool) give zero slots, and a pair whose
+    new slot is on one gets length -1; a pair whose unmapped page lies before its new
+    slot keeps its length; two pairs on one page read the same rows."""
+    from oracle import paged_to_contiguous
+    ps, hd, n_pages = 2, 1, 3
+    pool = np.arange(n_pages * ps, dtype=float).reshape(n_pages, ps, hd) + 1.0
+    table = np.array([[[0, -1, 2]], [[3, 1, 1]]])           # B = 2, n_kv = 1, 3 pages
+    L = np.array([[3], [4]])                               # slot 3 on page -1; slot 4 on 1
+    Kg, Vg, Lg = paged_to_contiguous(pool, -pool, table, L)
+    np.testing.assert_array_equal(Kg[0, 0, :, 0], [1, 2, 0, 0, 5, 6])
+    np.testing.assert_array_equal(Kg[1, 0, :, 0], [0, 0, 3, 4, 3, 4])
+    np.testing.assert_array_equal(Vg, -Kg)
+    np.testing.assert_array_equal(Lg, [[-1], [4]])
+    # a length past the capacity stays out of range
+    _, _, Lg2 = paged_to_contiguous(pool, pool, table, np.array([[6], [-1]]))
+    np.testing.assert_array_equal(Lg2, [[6], [-1]])
+
+
+def test_paged_decode_steps_reproduce_prefill():
+    """Reading R10 with R4 across steps: token-by-token decode through a pool of
+    shuffled pages (each step gathers the caches, decodes, and writes the new k/v
+    into the new slot's page row) gives the prefill rows."""
+    from oracle import paged_to_contiguous
+    rng = np.random.default_rng(13)
+    B, S, d, n_q, n_kv, hd, ps = 2, 10, 16, 4, 2, 4, 4
+    max_pages = S // ps + 1
+    n_pages = B * n_kv * max_pages + 3
+    table = rng.permutation(n_pages)[:B * n_kv * max_pages].reshape(B, n_kv, max_pages)
+    X = rng.standard_normal((B, S, d))
+    M = (rng.random((B, S, n_kv)) < 0.6).astype(np.uint8)
+    W = _w(d, n_q, n_kv, hd, 4)
+    Kp = rng.standard_normal((n_pages, ps, hd))   # stale contents past the lengths
+    Vp = rng.standard_normal((n_pages, ps, hd))
+    L = np.zeros((B, n_kv), np.int64)
+    Ys = []
+    for s in range(S):
+        Kc, Vc, Le = paged_to_contiguous(Kp, Vp, table, L)
+        Y, Kn, Vn = attn_masked(X[:, s], M[:, s], W["Wq"], W["Wk"], W["Wv"], W["Wo"], n_q=n_q,
+                                n_kv=n_kv, head_dim=hd, rope_theta=10000.0, decode=True,
+                                K_cache=Kc, V_cache=Vc, kv_len=Le, pos=s)
+        Ys.append(Y)
+        for b, g in zip(*np.nonzero(M[:, s])):
+            Kp[table[b, g, L[b, g] // ps], L[b, g] % ps] = Kn[b, g]
+            Vp[table[b, g, L[b, g] // ps], L[b, g] % ps] = Vn[b, g]
+            L[b, g] += 1
+    for b in range(B):
+        ref = _run(X[b], M[b], W, n_q, n_kv, hd, 10000.0)
+        np.testing.assert_allclose(np.stack(Ys, axis=1)[b], ref, rtol=1e-10, atol=1e-12)
