@@ -29,7 +29,9 @@ def _gpu_ffn(c, mode):
                                           (33, 256, 1024, 8, "ones"), (9, 256, 1024, 8, "zeros"),
                                           (100, 256, 1024, 8, "topk"), (24, 128, 512, 8, "topk"),
                                           (48, 448, 1024, 16, "bernoulli"),
-                                          (8, 256, 512, 16, "topk"), (40, 384, 1024, 32, "bernoulli")])
+                                          (8, 256, 512, 16, "topk"), (40, 384, 1024, 32, "bernoulli"),
+                                          (2, 256, 1024, 16, "topk"), (4, 256, 1024, 8, "zeros"),
+                                          (3, 384, 1536, 24, "clustered")])
 def test_ffn_decode_shapes(B, d, F, n, kind):
     dev()
     log(f"ffn decode B={B} d={d} F={F} n={n} {kind}")
@@ -95,6 +97,7 @@ ATT = [
     (40, 320, 8, 2, 130, 131, 0.5, "topk", 500000.0),     # batch over 16: LDS-shared rows
     (20, 128, 8, 4, 10, 12, 0.5, "bernoulli", 0.0),       # d below one 256-wide K batch
     (64, 512, 16, 4, 33, 40, 0.75, "clustered", 10000.0),
+    (48, 256, 16, 16, 140, 141, 0.5, "topk", 500000.0),   # r = 1, 16 groups
 ]
 
 

@@ -65,6 +65,7 @@ CASES = [
     (64, 512, 16, 4, 260, 1000, 0.75, "clustered", 10000.0),
     (5, 256, 16, 4, 1, 0, 1.0, "ones", 0.0),              # one slot: every length is 0
     (7, 384, 12, 4, 700, 699, 0.5, "bernoulli", 500000.0),  # r = 3
+    (40, 256, 16, 16, 150, 149, 0.5, "topk", 500000.0),     # r = 1, 16 groups
 ]
 
 
