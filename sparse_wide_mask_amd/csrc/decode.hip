@@ -710,19 +710,21 @@ constexpr int kKeyBlocks = kKeyChunk / 16 / kAttnWaves;  // 16-key MFMA blocks p
 constexpr int kKeySlices = kKeyChunk / 32;                // 32-key slices of the P V step
 
 // One work-group = (token b, group g, chunk of kKeyChunk cache keys).  All of the
-// chunk's bytes are requested up front: the K rows into registers as MFMA
-// operands, the V rows straight into LDS by buffer->LDS loads, which land while
-// the scores are computed.
-//   scores  S^T[key, h] = K[key, :] . Q[h, :] with v_mfma_f32_16x16x32_bf16:
-//           16 keys x 16 head columns (the group's r heads, the rest zero) per
-//           block, 4 blocks per wave;
+// chunk's bytes are requested up front, every load instruction reading whole
+// rows: the K rows straight into LDS by buffer->LDS loads (4 rows of 256 B per
+// instruction), the V rows into registers (two rows per instruction), where the
+// P V step uses them.  Loads of 16 rows x 64 B per instruction (K fragments read
+// as MFMA operands from memory) held the kernel 5-7 % lower.
+//   scores  S^T[key, h] = K[key, :] . Q[h, :] with v_mfma_f32_16x16x32_bf16, the
+//           K fragments read from LDS: 16 keys x 16 head columns (the group's r
+//           heads, the rest zero) per block, 4 blocks per wave;
 //   softmax per-head max and sum over the chunk (thread t = key t);
 //   P V     thread = (4 head dims, 32 keys) for all r heads, then a sum over
 //           the key slices through LDS.
 // Writes unnormalised partial outputs and the chunk's (max, sum) per head.
 // PAGED: the cache rows come through the page table (DecCache).  Pages hold at
-// least 16 slots, so a 16-key MFMA block and a 4-row V group never cross a page,
-// and a chunk spans at most 8 pages, whose entries lanes 0..7 load once.
+// least 16 slots, so a 16-key block and a 4-row group never cross a page, and a
+// chunk spans at most 8 pages, whose entries lanes 0..7 load once.
 template <bool PAGED>
 __global__ void __launch_bounds__(kKeyChunk)
     attn_decode_partial(const uint16_t* __restrict__ Q, const uint16_t* __restrict__ Kc,
@@ -730,8 +732,9 @@ __global__ void __launch_bounds__(kKeyChunk)
                         int n_kv, int r, DecCache dc, int nch, float scale_log2,
                         float* __restrict__ Opart, float* __restrict__ Mpart,
                         float* __restrict__ Lpart) {
-  // V rows (row-major, 256 B each); reused for the key-slice partial sums
-  __shared__ __attribute__((aligned(16))) uint16_t sV[kKeyChunk * kHdD];
+  // K rows (256 B each; 16-byte chunk c of key k at slot c ^ (k mod 16)); reused
+  // for the key-slice partial sums
+  __shared__ __attribute__((aligned(16))) uint16_t sK[kKeyChunk * kHdD];
   __shared__ __attribute__((aligned(16))) float sP[8][kKeyChunk];
   __shared__ float sRed[8][kAttnWaves];
   const int c = blockIdx.x % nch, rest = blockIdx.x / nch;
@@ -758,47 +761,37 @@ __global__ void __launch_bounds__(kKeyChunk)
   const int nq = n_kv * r;
   const uint32_t cache_bytes = (uint32_t)(dc.rows(B, n_kv) * kHdD * 2);
   const int m16 = lane & 15, q4 = lane >> 4;
-  // cache row of the chunk's key rel (rel a multiple of 4, wave-uniform), -1 if unmapped
   const size_t kvbase = ((size_t)b * n_kv + g) * dc.kv_cap + k0;
-  auto row_of = [&](int rel) -> long long {
+  // cache row of the chunk's key rel, -1 if unmapped.  UNIFORM: rel is the same
+  // for the whole wave (the page entry is read with readlane), else any lane's own
+  // (a lane shuffle).  Pages hold at least 16 slots, so the 16-key blocks and the
+  // 4-row groups used below never cross a page.
+  auto row_of = [&](int rel, auto uniform) -> long long {
     if constexpr (!PAGED) {
       return (long long)(kvbase + rel);
     } else {
-      const int s = k0 + rel;
-      const int p = __builtin_amdgcn_readlane(
-          pgv, __builtin_amdgcn_readfirstlane((s >> dc.page_shift) - (k0 >> dc.page_shift)));
+      const int s = k0 + rel, i = (s >> dc.page_shift) - (k0 >> dc.page_shift);
+      const int p = decltype(uniform)::value
+                        ? __builtin_amdgcn_readlane(pgv, __builtin_amdgcn_readfirstlane(i))
+                        : __shfl(pgv, i);
       return p >= 0 && p < dc.n_pages
                  ? ((long long)p << dc.page_shift) + (s & ((1 << dc.page_shift) - 1))
                  : -1;
     }
   };
-
-  // K operand: block i of wave w = keys 16 (4 w + i) + m16, dims 32 ks + 8 q4 .. +7
-  const rsrc_t kr = make_rsrc(Kc, cache_bytes);
-  bf16x8 kf[kKeyBlocks][4];
-#pragma unroll
-  for (int i = 0; i < kKeyBlocks; ++i) {
-    const int rel0 = 16 * (kKeyBlocks * wave + i), key = rel0 + m16;
-    const long long r0 = row_of(rel0);
-    const bool in = key < nkeys && r0 >= 0;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      kf[i][ks] =
-          xload(kr, in ? (uint32_t)(((r0 + m16) * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
-  }
-  // V: instruction q of wave w fills the 4 rows from 4 (kAttnWaves q + w) (1 KB);
-  // rows past the chunk's keys read as zeros
+  // K: instruction q of wave w fills the 4 rows from 4 (kAttnWaves q + w), each
+  // whole (lane (q4, m16) loads chunk m16 ^ (row mod 16) of row 4 (..) + q4)
   {
-    const i32x4 vsrd = make_srd(Vc, cache_bytes);
-    const uint32_t vlds = lds_addr(sV);
+    const i32x4 ksrd = make_srd(Kc, cache_bytes);
+    const uint32_t klds = lds_addr(sK);
 #pragma unroll
     for (int q = 0; q < kKeyChunk / (4 * kAttnWaves); ++q) {
       const int row0 = 4 * (kAttnWaves * q + wave), row = row0 + q4;
-      const long long r0 = row_of(row0);
+      const long long r0 = row_of(row0, std::true_type{});
       const uint32_t off = row < nkeys && r0 >= 0
-                               ? (uint32_t)(((r0 + q4) * kHdD + m16 * 8) * 2)
+                               ? (uint32_t)(((r0 + q4) * kHdD + ((m16 ^ (row & 15)) * 8)) * 2)
                                : kSkip;
-      lds_dma16(vsrd, vlds + row0 * kHdD * 2, off);
+      lds_dma16(ksrd, klds + row0 * kHdD * 2, off);
     }
   }
   // Q operand: column m16 = head of the group (zero past r)
@@ -809,21 +802,45 @@ __global__ void __launch_bounds__(kKeyChunk)
     for (int ks = 0; ks < 4; ++ks)
       qf[ks] = xload(qr, m16 < r ? (uint32_t)((m16 * kHdD + 32 * ks + 8 * q4) * 2) : kSkip);
   }
+  // V into registers: thread = (dims 4 j4 .. +3, keys 32 kslice .. +31), 8 bytes of
+  // each of its rows; one load of a wave reads two whole rows
+  const int j4 = tid & 31, kslice = tid >> 5;
+  u32x2 vr[32];
+  {
+    const rsrc_t vrs = make_rsrc(Vc, cache_bytes);
+    const long long vb[2] = {row_of(32 * kslice, std::false_type{}),
+                             row_of(32 * kslice + 16, std::false_type{})};
+#pragma unroll
+    for (int e = 0; e < 32; ++e) {
+      const int key = 32 * kslice + e;
+      const long long r0 = vb[e / 16];
+      vr[e] = __builtin_amdgcn_raw_buffer_load_b64(
+          vrs, key < nkeys && r0 >= 0 ? (int)(((r0 + e % 16) * kHdD + 4 * j4) * 2) : (int)kSkip,
+          0, 0);
+    }
+  }
+  // K rows of every wave in LDS (and the Q operand); the V loads stay in flight
+  asm volatile("s_waitcnt vmcnt(32)" ::: "memory");
+  __syncthreads();
 #pragma unroll
   for (int i = 0; i < kKeyBlocks; ++i) {
+    const int key = 16 * (kKeyBlocks * wave + i) + m16;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) acc = mfma16(kf[i][ks], qf[ks], acc);
+    for (int ks = 0; ks < 4; ++ks) {
+      const bf16x8 kfr = *reinterpret_cast<const bf16x8*>(
+          sK + key * kHdD + (((4 * ks + q4) ^ (key & 15)) * 8));
+      acc = mfma16(kfr, qf[ks], acc);
+    }
     if (m16 < r) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const int key = 16 * (kKeyBlocks * wave + i) + acc16_row(lane, e);
-        sP[m16][key] = key < nkeys ? acc[e] * scale_log2 : -INFINITY;
+        const int kk = 16 * (kKeyBlocks * wave + i) + acc16_row(lane, e);
+        sP[m16][kk] = kk < nkeys ? acc[e] * scale_log2 : -INFINITY;
       }
     }
   }
   __syncthreads();
-  // per-head max and sum over the chunk (thread t = key t)
   float mh[8], lh[8];
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
@@ -851,8 +868,6 @@ __global__ void __launch_bounds__(kKeyChunk)
     for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
     if (lane == 0) sRed[h][wave] = l;
   }
-  // the V rows of every wave have landed in LDS before anyone reads them
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
@@ -862,21 +877,19 @@ __global__ void __launch_bounds__(kKeyChunk)
     for (int w = 1; w < kAttnWaves; ++w) l += sRed[h][w];
     lh[h] = l;
   }
-  // P V: thread = (dims 4 j4 .. +3, keys 32 ks .. +31); P is zero and V rows are
-  // zero past nkeys
-  const int j4 = tid & 31, kslice = tid >> 5;
+  // P V: P is zero and the V rows are zero past nkeys
   float o[8][4];
 #pragma unroll
   for (int h = 0; h < 8; ++h)
 #pragma unroll
     for (int e = 0; e < 4; ++e) o[h][e] = 0.f;
-#pragma unroll 2
+#pragma unroll
   for (int kq = 0; kq < 32; kq += 4) {
     const int kk = 32 * kslice + kq;
     float vf[4][4];
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
-      const u32x2 v2 = *reinterpret_cast<const u32x2*>(sV + (kk + e) * kHdD + 4 * j4);
+      const u32x2 v2 = vr[kq + e];
       vf[e][0] = __uint_as_float(v2[0] << 16);
       vf[e][1] = __uint_as_float(v2[0] & 0xffff0000u);
       vf[e][2] = __uint_as_float(v2[1] << 16);
@@ -892,8 +905,8 @@ __global__ void __launch_bounds__(kKeyChunk)
         for (int x = 0; x < 4; ++x) o[h][x] += p[e] * vf[e][x];
     }
   }
-  __syncthreads();  // every thread is done with sV
-  float* sO = reinterpret_cast<float*>(sV);  // [kKeySlices][r][128]
+  // sK was last read before the softmax barriers
+  float* sO = reinterpret_cast<float*>(sK);  // [kKeySlices][r][128]
 #pragma unroll
   for (int h = 0; h < 8; ++h) {
     if (h >= r) break;
