@@ -74,6 +74,7 @@ CASES = [
     (7, 384, 12, 4, 256, 3, 767, 0.5, "bernoulli", 500000.0, 0.0),  # r = 3, chunk in a page
     (5, 256, 16, 4, 1024, 1, 5, 1.0, "ones", 0.0, 0.0),            # one page per pair
     (9, 256, 8, 2, 32, 12, 383, 0.75, "topk", 500000.0, 0.3),     # unmapped entries
+    (24, 256, 16, 16, 32, 6, 191, 0.5, "bernoulli", 500000.0, 0.0),  # r = 1, 16 groups
 ]
 
 
@@ -86,6 +87,31 @@ def test_paged_cache_shapes(B, d, n_q, n_kv, ps, max_pages, pos, keep, kind, the
     c = attn_case(f"paged_{B}_{ps}_{kind}", B, d, n_q, n_kv, 128, keep, kind)
     p = paged_cache(f"paged_{B}_{ps}_{max_pages}", B, n_kv, ps, max_pages, unmapped=unmapped)
     _check(c, p, pos, theta)
+
+
+@needs_gpu
+def test_paged_cache_unmapped_new_slots_and_bad_lengths():
+    """Pairs whose new slot is on an unmapped page (entry -1 or past the pool) and
+    pairs with lengths outside the capacity behave like dropped pairs: zero output
+    for their heads, nothing written."""
+    dev()
+    log("paged decode, unmapped new slots and out-of-range lengths")
+    B, d, n_q, n_kv, ps, max_pages = 6, 256, 8, 2, 16, 4
+    c = attn_case("paged_bad", B, d, n_q, n_kv, 128, 1.0, "ones")
+    p = paged_cache("paged_bad", B, n_kv, ps, max_pages)
+    t, L = p["page_table"], p["kv_len"]
+    L[0, 0], t[0, 0, 40 // ps] = 40, -1                 # new slot on an unmapped page (-1)
+    L[1, 1], t[1, 1, 17 // ps] = 17, p["meta"]["n_pages"]  # ... on an entry past the pool
+    L[2, 0], L[3, 1] = -1, max_pages * ps                # lengths outside the capacity
+    _check(c, p, 63, 500000.0)
+    # the same call with those four pairs dropped by the mask instead: the same
+    # output bit for bit (both feed zeros for those heads into the O projection)
+    Y, _, _ = _gpu_paged(c, p, 63, 500000.0)
+    c2 = dict(c, mask=c["mask"].copy())
+    for b, g in ((0, 0), (1, 1), (2, 0), (3, 1)):
+        c2["mask"][b, g] = 0
+    Y2, _, _ = _gpu_paged(c2, p, 63, 500000.0)
+    assert np.array_equal(Y, Y2)
 
 
 @needs_gpu
