@@ -779,8 +779,8 @@ __global__ void __launch_bounds__(kKeyChunk)
                  : -1;
     }
   };
-  // K: instruction q of wave w fills the 4 rows from 4 (kAttnWaves q + w), each
-  // whole (lane (q4, m16) loads chunk m16 ^ (row mod 16) of row 4 (..) + q4)
+  // K: instruction q of wave w fills the 4 whole rows from row0 = 4 (kAttnWaves q + w);
+  // lane (q4, m16) loads chunk m16 ^ (row mod 16) of row row0 + q4 into slot m16
   {
     const i32x4 ksrd = make_srd(Kc, cache_bytes);
     const uint32_t klds = lds_addr(sK);
