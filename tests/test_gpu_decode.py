@@ -98,6 +98,7 @@ ATT = [
     (20, 128, 8, 4, 10, 12, 0.5, "bernoulli", 0.0),       # d below one 256-wide K batch
     (64, 512, 16, 4, 33, 40, 0.75, "clustered", 10000.0),
     (48, 256, 16, 16, 140, 141, 0.5, "topk", 500000.0),   # r = 1, 16 groups
+    (2, 256, 8, 2, 16500, 16501, 0.5, "topk", 500000.0),  # over 128 key chunks
 ]
 
 

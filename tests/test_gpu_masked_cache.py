@@ -66,6 +66,7 @@ CASES = [
     (5, 256, 16, 4, 1, 0, 1.0, "ones", 0.0),              # one slot: every length is 0
     (7, 384, 12, 4, 700, 699, 0.5, "bernoulli", 500000.0),  # r = 3
     (40, 256, 16, 16, 150, 149, 0.5, "topk", 500000.0),     # r = 1, 16 groups
+    (2, 256, 8, 2, 17000, 16999, 0.5, "bernoulli", 500000.0),  # over 128 chunks a pair
 ]
 
 
