@@ -505,13 +505,14 @@ constexpr int kKmThreads = 64 * kKmWaves;
 
 int kmask_decode_col_blocks(int d) { return (d + kKmCols - 1) / kKmCols; }
 
-// K splits: enough work-groups to fill the 256 CUs, at most 16 partial sums, and
-// no more splits than the largest possible union has units.
+// K splits: enough work-groups to fill the 256 CUs, at most kMaxDecSplits partial
+// sums, and no more splits than the largest possible union has units.
+constexpr int kMaxDecSplits = 16;
 int kmask_decode_splits(int d, int n, int G) {
   const int units = n * (G % 128 == 0 ? G / 128 : G % 64 == 0 ? G / 64 : G / 32);
   const int ncb = kmask_decode_col_blocks(d);
   int s = (256 + ncb - 1) / ncb;
-  s = s < 16 ? s : 16;
+  s = s < kMaxDecSplits ? s : kMaxDecSplits;
   s = s < units ? s : units;
   return s > 1 ? s : 1;
 }
@@ -686,11 +687,15 @@ __global__ void __launch_bounds__(256)
   const int i = (blockIdx.x * 256 + threadIdx.x) * 4;
   if (i >= B * d) return;
   const size_t plane = (size_t)B * d;
-  f32x4 v = *reinterpret_cast<const f32x4*>(part + i);
-  for (int s2 = 1; s2 < S; ++s2) {
-    const f32x4 w = *reinterpret_cast<const f32x4*>(part + s2 * plane + i);
-    v[0] += w[0], v[1] += w[1], v[2] += w[2], v[3] += w[3];
-  }
+  // all S partials are requested before the first add (S <= kMaxDecSplits)
+  f32x4 p[kMaxDecSplits];
+#pragma unroll
+  for (int s2 = 0; s2 < kMaxDecSplits; ++s2)
+    if (s2 < S) p[s2] = *reinterpret_cast<const f32x4*>(part + s2 * plane + i);
+  f32x4 v = p[0];
+#pragma unroll
+  for (int s2 = 1; s2 < kMaxDecSplits; ++s2)
+    if (s2 < S) v[0] += p[s2][0], v[1] += p[s2][1], v[2] += p[s2][2], v[3] += p[s2][3];
   if (residual) {
     const u32x2 r = *reinterpret_cast<const u32x2*>(residual + i);
     v[0] += __uint_as_float(r[0] << 16), v[1] += __uint_as_float(r[0] & 0xffff0000u);
