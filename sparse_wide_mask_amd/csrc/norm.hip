@@ -12,9 +12,15 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const uint16_t* __restrict__
   __shared__ float red[4];
   const size_t row = blockIdx.x;
   const uint16_t* xr = x + row * d;
+  // rows up to kNormHeld * 2048 elements stay in registers for the second pass
+  constexpr int kNormHeld = 4;
+  u32x4 held[kNormHeld];
   float ss = 0.f;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
+  for (int c = threadIdx.x * 8, it = 0; c < d; c += 256 * 8, ++it) {
     const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+#pragma unroll
+    for (int q = 0; q < kNormHeld; ++q)
+      if (q == it) held[q] = v;
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       const float a = __uint_as_float(v[k] << 16), b = __uint_as_float(v[k] & 0xffff0000u);
@@ -27,8 +33,15 @@ __global__ void __launch_bounds__(256) rmsnorm_rows(const uint16_t* __restrict__
   const float tot = red[0] + red[1] + red[2] + red[3];
   const float inv = rsqrtf(tot / (float)d + eps);
   uint16_t* yr = y + row * d;
-  for (int c = threadIdx.x * 8; c < d; c += 256 * 8) {
-    const u32x4 v = *reinterpret_cast<const u32x4*>(xr + c);
+  for (int c = threadIdx.x * 8, it = 0; c < d; c += 256 * 8, ++it) {
+    u32x4 v;
+    if (it < kNormHeld) {
+#pragma unroll
+      for (int q = 0; q < kNormHeld; ++q)
+        if (q == it) v = held[q];
+    } else {
+      v = *reinterpret_cast<const u32x4*>(xr + c);
+    }
     const u32x4 gm = *reinterpret_cast<const u32x4*>(gamma + c);
     u32x4 o;
 #pragma unroll
