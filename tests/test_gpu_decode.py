@@ -152,14 +152,47 @@ def _gpu_layer_decode(c):
                       n_q=m["n_q"], n_kv=m["n_kv"], rope_theta=m["rope_theta"], eps=m["eps"],
                       mode="decode", K_cache=Kc, V_cache=Vc, kv_len=m["kv_len"], out=Y)
     torch.cuda.synchronize()
-    return host(Y)
+    return host(Y), host(Kc), host(Vc)
 
 
 def _oracle_layer_decode(c):
     m = c["meta"]
     return layer_masked(c["X"], c["attn_mask"], c["ffn_mask"], c, n_q=m["n_q"], n_kv=m["n_kv"],
                         head_dim=128, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"], eps=m["eps"],
-                        decode=True, K_cache=c["K_cache"], V_cache=c["V_cache"], kv_len=m["kv_len"])
+                        decode=True, K_cache=c["K_cache"], V_cache=c["V_cache"], kv_len=m["kv_len"],
+                        return_parts=True)
+
+
+def _check_layer_decode(c):
+    """y against the oracle, and what y hides behind the residual x: the layer's
+    own cache writes (slot kv_len of the kept pairs only), its update y - x against
+    the oracle's attention-plus-FFN term (bound: the tolerance on that term plus the
+    bf16 roundings of h and y), and each sublayer alone on the oracle's bf16-rounded
+    intermediate input (u for attention, w for the FFN)."""
+    m = c["meta"]
+    L = m["kv_len"]
+    y, Kg, Vg = _gpu_layer_decode(c)
+    ref, parts = _oracle_layer_decode(c)
+    assert rel_err(y, ref) <= TOL
+    keep = c["attn_mask"] != 0
+    assert rel_err(Kg[:, :, L][keep], parts["K_new"][keep]) <= TOL
+    assert rel_err(Vg[:, :, L][keep], parts["V_new"][keep]) <= TOL
+    K0, V0 = c["K_cache"].copy(), c["V_cache"].copy()
+    K0[:, :, L][keep] = Kg[:, :, L][keep]
+    V0[:, :, L][keep] = Vg[:, :, L][keep]
+    assert np.array_equal(Kg, K0) and np.array_equal(Vg, V0), "cache written outside kept slots"
+    # the layer rounds h = x + a and y to bf16 (half an ulp each, 2^-9 relative)
+    delta = parts["a"] + parts["f"]
+    bound = TOL * np.abs(delta).max() + 2.0 ** -8 * (np.abs(parts["h"]).max() + np.abs(ref).max())
+    assert np.abs((y - c["X"]) - delta).max() <= bound
+    # attention sublayer alone on u (same caches, same slot), FFN sublayer alone on w
+    u = bf16_round(parts["u"].astype(np.float32))
+    ca = dict(c, X=u, mask=c["attn_mask"])
+    _check_attn_decode(ca, m["rope_theta"])
+    w = bf16_round(parts["w"].astype(np.float32))
+    cf = dict(X=w, mask=c["ffn_mask"], W_gate=c["W_gate"], W_up=c["W_up"], W_down=c["W_down"])
+    assert rel_err(_gpu_ffn(cf, "decode"),
+                   ffn_masked(w, c["ffn_mask"], c["W_gate"], c["W_up"], c["W_down"])) <= TOL
 
 
 @needs_gpu
@@ -169,7 +202,7 @@ def test_layer_decode_shapes(B, L, kind):
     log(f"layer decode B={B} L={L} {kind}")
     c = layer_case(f"layer_dec_{B}_{L}_{kind}", B, 256, 1024, 8, 8, 2, 128, 0.5, kind,
                    decode=True, kv_len=L, kv_cap=L + 3)
-    assert rel_err(_gpu_layer_decode(c), _oracle_layer_decode(c)) <= TOL
+    _check_layer_decode(c)
 
 
 @needs_gpu
@@ -178,4 +211,4 @@ def test_layer_decode_llama31_8b_full():
     dev()
     log("layer decode 8B B=32 L=8192")
     c = layer_8b(32, decode=True, L=8192)
-    assert rel_err(_gpu_layer_decode(c), _oracle_layer_decode(c)) <= TOL
+    _check_layer_decode(c)

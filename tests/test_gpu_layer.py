@@ -64,16 +64,16 @@ def test_layer_prefill_shapes(T, d, F, n_ffn, n_q, n_kv, keep, kind):
 def _check_sublayers(c, parts, rows=None):
     m = c["meta"]
     R = slice(None) if rows is None else rows
-    u = bf16_round(parts["u"].astype(np.float32)) if rows is None else None
-    if u is not None:
-        Ya = nan_bf16(u.shape)
-        wide.attn_proj_masked(bf16(u), u8(c["attn_mask"]), bf16(c["Wq"]), bf16(c["Wk"]),
-                              bf16(c["Wv"]), wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]),
-                              n_q=m["n_q"], n_kv=m["n_kv"], rope_theta=m["rope_theta"], out=Ya)
-        torch.cuda.synchronize()
-        ra = attn_masked(u, c["attn_mask"], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
-                         n_kv=m["n_kv"], head_dim=128, rope_theta=m["rope_theta"])
-        assert rel_err(host(Ya), ra) <= TOL
+    # u = RMSNorm(x) is produced for every token (the attention keys need them all)
+    u = bf16_round(parts["u"].astype(np.float32))
+    Ya = nan_bf16(u.shape)
+    wide.attn_proj_masked(bf16(u), u8(c["attn_mask"]), bf16(c["Wq"]), bf16(c["Wk"]),
+                          bf16(c["Wv"]), wide.pack_kmajor(bf16(c["Wo"]), m["n_kv"]),
+                          n_q=m["n_q"], n_kv=m["n_kv"], rope_theta=m["rope_theta"], out=Ya)
+    torch.cuda.synchronize()
+    ra = attn_masked(u, c["attn_mask"], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
+                     n_kv=m["n_kv"], head_dim=128, rope_theta=m["rope_theta"], rows=rows)
+    assert rel_err(host(Ya)[R], ra) <= TOL
     w = bf16_round(parts["w"].astype(np.float32))
     fm = c["ffn_mask"][R]
     Yf = nan_bf16(w.shape)
@@ -110,9 +110,10 @@ def test_layer_all_zero_masks_is_identity():
 def test_layer_prefill_llama31_8b_sampled(ffn_group):
     """Full Llama-3.1-8B layer shape at T=8192, router top-k masks keeping 50%, FFN
     groups of 128 (112 groups) and of 64 (224 groups, the group-size sweep); the
-    oracle computes 24 sampled token rows (keys/values of all tokens).  The FFN
-    sublayer is also checked alone at this shape on the oracle's intermediate
-    input (bf16-rounded), where the residual does not hide its error."""
+    oracle computes 24 sampled token rows (keys/values of all tokens).  The attention
+    sublayer (RoPE theta 5e5) and the FFN sublayer are also checked alone at this
+    shape on the oracle's intermediate inputs (bf16-rounded), where the residual does
+    not hide their error."""
     dev()
     log(f"layer prefill 8B T=8192 G={ffn_group} (sampled)")
     c = layer_8b(8192, ffn_group=ffn_group)
@@ -123,7 +124,7 @@ def test_layer_prefill_llama31_8b_sampled(ffn_group):
     assert np.all(np.isfinite(got))
     ref, parts = oracle_layer(c, rows=rows, parts=True)
     assert rel_err(got[rows], ref) <= TOL
-    # FFN sublayer at the layer shape on w = RMSNorm(h) of the oracle (sampled rows)
+    # attention on u = RMSNorm(x), FFN on w = RMSNorm(h) of the oracle (sampled rows)
     _check_sublayers(c, parts, rows=rows)
 
 
