@@ -14,7 +14,12 @@
  *
  * Conventions shared by every entry point
  *   - All pointers except `cfg`/`W` structs are DEVICE pointers, owned by the
- *     caller, 16-byte aligned.  The library allocates nothing and keeps no state.
+ *     caller, 16-byte aligned.  Calls allocate no device memory; scratch comes
+ *     from the caller's workspace (wide_ffn_masked_noalloc: from a fixed array in
+ *     the library).  Process-wide state, each item created on first use and kept
+ *     until the process ends: per device, the layer call's second stream and its
+ *     events (wide_layer_masked) and the scratch address (wide_ffn_masked_noalloc);
+ *     the kernel trace while enabled.
  *   - bf16 tensors are passed as uint16_t bit patterns, row-major, contiguous.
  *   - Masks are uint8 [T, n_groups] row-major; any nonzero byte means "keep".
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work:
@@ -151,6 +156,31 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
                     const uint16_t* W_up, const uint16_t* W_down_packed, int T, int d_model,
                     int d_ff, int n_groups, int mode, uint16_t* Y, void* workspace,
                     size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * wide_ffn_masked_noalloc - wide_ffn_masked for callers that cannot allocate device
+ * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It takes no workspace and allocates nothing (no hipMalloc, hipFree or
+ * allocating library call); the caller still passes the inputs and Y.
+ *
+ * Scratch: a fixed device array of WIDE_NOALLOC_SCRATCH_BYTES inside the library,
+ * one per GPU, held from the library's load on that GPU until the process ends.
+ * Its device address is looked up once per device, on the first call there.
+ * Limit: a call whose wide_ffn_masked_workspace(T, d_model, d_ff, n_groups, mode)
+ * exceeds WIDE_NOALLOC_SCRATCH_BYTES returns WIDE_EWORKSPACE and launches nothing
+ * (e.g. decode batches up to 64 fit at d_model 4096, d_ff 14336 in 112 groups).
+ * Concurrency: every call on one GPU uses that GPU's one array.  Calls ordered on one
+ * stream are safe; calls that may run at the same time on one GPU (different
+ * streams, or several host threads) race on the scratch and give wrong results.
+ * The scratch keeps the last call's contents; nothing in it needs to start at zero.
+ * Arguments, results and errors otherwise as wide_ffn_masked; WIDE_EHIP also when
+ * HIP cannot give the scratch address.
+ */
+#define WIDE_NOALLOC_SCRATCH_BYTES (16u << 20)
+int wide_ffn_masked_noalloc(const uint16_t* X, const uint8_t* mask, const uint16_t* W_gate,
+                            const uint16_t* W_up, const uint16_t* W_down_packed, int T,
+                            int d_model, int d_ff, int n_groups, int mode, uint16_t* Y,
+                            uint32_t flags, void* stream);
 
 /*
  * wide_attn_proj_masked - masked attention sublayer over GQA-aligned head groups

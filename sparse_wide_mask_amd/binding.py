@@ -39,6 +39,7 @@ _SIGS = {
     "wide_pack_router": ([_p, _i, _i, _p, _p], _i),
     "wide_ffn_masked_workspace": ([_i, _i, _i, _i, _i], _sz),
     "wide_ffn_masked": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+    "wide_ffn_masked_noalloc": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, C.c_uint32, _p], _i),
     "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i, _i], _sz),
     "wide_attn_proj_masked": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _i, _p, _p,
                                _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
@@ -242,6 +243,31 @@ def ffn_masked(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out=None
                                T, d, F, n, m, _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
     _check("wide_ffn_masked", st)
     return Y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20  # WIDE_NOALLOC_SCRATCH_BYTES
+
+
+def ffn_masked_noalloc(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out):
+    """wide_ffn_masked_noalloc: ffn_masked with the library's fixed per-GPU scratch
+    instead of a workspace; ``out`` (Y [T, d] bf16) is required, nothing is allocated.
+    Calls that may overlap on one GPU race on the scratch."""
+    for t, nm in ((X, "X"), (W_gate, "W_gate"), (W_up, "W_up"), (W_down_packed, "W_down_packed"),
+                  (out, "out")):
+        _dev(t, torch.bfloat16, nm)
+    _dev(mask, torch.uint8, "mask")
+    T, d = X.shape
+    F = W_gate.shape[0]
+    n = mask.shape[1]
+    if mask.shape[0] != T or W_gate.shape != (F, d) or W_up.shape != (F, d) or out.shape != (T, d):
+        raise ValueError("shape mismatch")
+    if W_down_packed.shape != (n, d, F // n):
+        raise ValueError("W_down_packed must be [n_groups, d_model, d_ff / n_groups]")
+    st = lib().wide_ffn_masked_noalloc(_ptr(X), _ptr(mask), _ptr(W_gate), _ptr(W_up),
+                                       _ptr(W_down_packed), T, d, F, n, _mode(mode), _ptr(out), 0,
+                                       _stream())
+    _check("wide_ffn_masked_noalloc", st)
+    return out
 
 
 # ---------------------------------------------------------------- attention

@@ -260,6 +260,35 @@ LayerWs carve_layer(Carver& c, int T, const wide_layer_cfg* cfg, int mode, int k
   return w;
 }
 
+// ------------------------------------------------ allocation-free FFN entry point
+
+// The scratch memory of wide_ffn_masked_noalloc: a fixed array in device memory,
+// one copy per GPU (held from the library's load on that device until the process
+// ends).  In host code `scratch` only names the symbol; its device address on the
+// current GPU comes from hipGetSymbolAddress, once per device, and only that
+// address is handed to kernels.
+static __device__ __align__(256) unsigned char scratch[WIDE_NOALLOC_SCRATCH_BYTES];
+
+struct ScratchAddr {
+  std::once_flag once;
+  void* ptr = nullptr;
+  hipError_t err = hipSuccess;
+};
+ScratchAddr g_scratch[kMaxDevices];
+
+// Device address of the current GPU's scratch array, or nullptr if HIP cannot
+// give it (the call then fails with WIDE_EHIP).
+void* scratch_address() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  ScratchAddr& a = g_scratch[dev];
+  std::call_once(a.once, [&a] {
+    a.err = hipGetSymbolAddress(&a.ptr, HIP_SYMBOL(scratch));
+    if (a.err != hipSuccess) a.ptr = nullptr;
+  });
+  return a.ptr;
+}
+
 }  // namespace
 
 extern "C" {
@@ -354,6 +383,32 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
   if (!aligned16(workspace)) return probe.used ? WIDE_EINVAL : WIDE_OK;
   if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
   Carver c(workspace);
+  FfnWs w = carve_ffn(c, T, d_model, d_ff, n_groups, mode);
+  (void)hipGetLastError();
+  ffn_run(X, mask, W_gate, W_up, W_down_packed, T, d_model, d_ff, n_groups, mode, nullptr, Y, w,
+          as_stream(stream));
+  return launch_status();
+}
+
+int wide_ffn_masked_noalloc(const uint16_t* X, const uint8_t* mask, const uint16_t* W_gate,
+                            const uint16_t* W_up, const uint16_t* W_down_packed, int T,
+                            int d_model, int d_ff, int n_groups, int mode, uint16_t* Y,
+                            uint32_t flags, void* stream) {
+  int st = ffn_check(T, d_model, d_ff, n_groups, mode);
+  if (st != WIDE_OK) return st;
+  if (flags != 0) return WIDE_EINVAL;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(mask) || !aligned16(W_gate) || !aligned16(W_up) ||
+      !aligned16(W_down_packed) || !aligned16(Y) || (void*)Y == (void*)X)
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_ffn(probe, T, d_model, d_ff, n_groups, mode);
+  if (probe.used > (size_t)WIDE_NOALLOC_SCRATCH_BYTES) return WIDE_EWORKSPACE;
+  void* ws = scratch_address();
+  if (!ws) return WIDE_EHIP;
+  // nothing in the scratch needs to start at zero: every element a kernel reads
+  // there was written earlier in the same call
+  Carver c(ws);
   FfnWs w = carve_ffn(c, T, d_model, d_ff, n_groups, mode);
   (void)hipGetLastError();
   ffn_run(X, mask, W_gate, W_up, W_down_packed, T, d_model, d_ff, n_groups, mode, nullptr, Y, w,
