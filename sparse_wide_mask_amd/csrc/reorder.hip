@@ -3,12 +3,12 @@
 // the per-tile union of kept groups that block-level skipping reads (§2.C, l=0).
 //
 // Two launches, no host synchronisation:
-//   1. reorder_pack   : one thread per token packs its mask row into 64-bit words.
-//   2. reorder_groups : one work-group per group (each thread owns a run of
-//                       consecutive tokens; a wave shuffle scan plus one LDS pass
-//                       over the waves gives the kept tokens before each run, and
-//                       the thread places its tokens), plus one work-group per
-//                       token tile for the tile's union of kept groups.
+//   1. reorder_pack   : one wave per token row packs its mask bytes into 64-bit
+//                       words by ballot.
+//   2. reorder_groups : one work-group per group (chunks of 64 tokens, a ballot
+//                       per chunk, a scan over the waves, then each lane places its
+//                       token by mbcnt), plus one work-group per token tile for
+//                       the tile's union of kept groups.
 #include "wide.h"
 #include "common.h"
 #include "gemm_tile.h"
@@ -16,56 +16,47 @@
 
 namespace wide {
 
-// One thread per token: it reads its mask row with 4-byte loads (all issued
-// before any is used) and packs the nonzero bytes into 64-bit words.
+// Packing: one wave per token row at a time, lane j reading mask byte 64 w + j
+// (64 consecutive bytes per load); the ballot of "nonzero" is word w.  A wave
+// takes kPackTok rows and issues all of their loads before the first ballot.
 constexpr int kPackThreads = 256;
+constexpr int kPackWaves = kPackThreads / kWave;
+constexpr int kPackTok = 8;
 
-template <bool ALIGNED4>
 __global__ void __launch_bounds__(kPackThreads)
     reorder_pack(const uint8_t* __restrict__ mask, int T, int n, int nw,
                  uint64_t* __restrict__ packed) {
-  const int t = blockIdx.x * kPackThreads + threadIdx.x;
-  if (t >= T) return;
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int t0 = (blockIdx.x * kPackWaves + wave) * kPackTok;
+  if (t0 >= T) return;
   const rsrc_t mr = make_rsrc(mask, (uint32_t)((size_t)T * n));
-  const uint32_t row = (uint32_t)((size_t)t * n);
+  uint32_t v[kPackTok][4];
 #pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    if (w >= nw) break;
-    uint64_t word = 0;
-    if (ALIGNED4) {
-      uint32_t v[16];
+  for (int k = 0; k < kPackTok; ++k)
 #pragma unroll
-      for (int u = 0; u < 16; ++u) {
-        const int b = 64 * w + 4 * u;
-        v[u] = b < n ? __builtin_amdgcn_raw_buffer_load_b32(mr, (int)(row + b), 0, 0) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 16; ++u)
-#pragma unroll
-        for (int k = 0; k < 4; ++k)
-          word |= (uint64_t)(((v[u] >> (8 * k)) & 0xffu) != 0u) << (4 * u + k);
-    } else {
-      uint32_t v[64];
-#pragma unroll
-      for (int u = 0; u < 64; ++u) {
-        const int b = 64 * w + u;
-        v[u] = b < n ? ldbuf1(mr, row + b) : 0u;
-      }
-#pragma unroll
-      for (int u = 0; u < 64; ++u) word |= (uint64_t)(v[u] != 0u) << u;
+    for (int w = 0; w < 4; ++w) {
+      const int t = t0 + k, g = 64 * w + lane;
+      v[k][w] = ldbuf1(mr, t < T && g < n ? (uint32_t)(t * n + g) : kSkip);
     }
-    packed[(size_t)t * nw + w] = word;
-  }
+#pragma unroll
+  for (int k = 0; k < kPackTok; ++k)
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint64_t word = ballot(v[k][w] != 0u);
+      if (lane == 0 && w < nw && t0 + k < T) packed[(size_t)(t0 + k) * nw + w] = word;
+    }
 }
 
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / kWave;
+constexpr int kGroupMaxChunks = WIDE_MAX_TOKENS / kWave;
 
-// Work-groups 0..n-1: one per group.  Thread i owns the contiguous tokens
-// [i*per, (i+1)*per), per <= 64: it loads their mask bits once into a register
-// bitmask, one work-group exclusive scan of the kept counts gives the number
-// kept before its run, and it places its tokens: kept ones at (#kept before t),
-// dropped ones at cnt + (#dropped before t).
+// Work-groups 0..n-1: one per group.  The tokens go in chunks of 64 (lane = token);
+// wave w takes a contiguous run of chunks.  Pass 1: the ballot of each chunk's
+// keep bits (kept in LDS) and the wave's count; a scan over the waves gives each
+// wave's kept and dropped tokens before its run.  Pass 2: a kept lane goes to
+// (kept before it), a dropped one to count + (dropped before it): mbcnt of the
+// ballot inside the chunk, so a wave's stores of a chunk are two contiguous runs.
 // Work-groups n..: one per token tile (when tile unions are asked for): the OR of
 // the tile's packed words, compacted into an ascending group list, -1 padded.
 __global__ void __launch_bounds__(kGroupThreads)
@@ -75,6 +66,7 @@ __global__ void __launch_bounds__(kGroupThreads)
                    int32_t* __restrict__ tile_groups) {
   __shared__ int sWave[kGroupWaves];
   __shared__ uint32_t sU[8];
+  __shared__ uint64_t sBallot[kGroupMaxChunks];
   const int lane = lane_id(), wave = threadIdx.x / kWave;
   if ((int)blockIdx.x >= n) {
     const int tile = blockIdx.x - n;
@@ -115,43 +107,53 @@ __global__ void __launch_bounds__(kGroupThreads)
   }
   const int g = blockIdx.x;
   const int w = g >> 6, j = g & 63;
-  const int per = (T + kGroupThreads - 1) / kGroupThreads;
-  const int t0 = min(T, (int)threadIdx.x * per), t1 = min(T, t0 + per);
-  uint64_t bits = 0;
-  for (int c = 0; c < t1 - t0; c += 8) {
-    uint64_t v[8];
+  const int nch = (T + kWave - 1) / kWave;
+  const int per = (nch + kGroupWaves - 1) / kGroupWaves;
+  const int c0 = min(nch, wave * per), c1 = min(nch, c0 + per);
+  const rsrc_t pr = make_rsrc(packed, (uint32_t)((size_t)T * nw * 8));
+  int mine = 0;
+  for (int c = c0; c < c1; c += 8) {
+    uint32_t v[8];  // the 32-bit half of word w that holds bit j
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const int t = t0 + c + u;
-      v[u] = t < t1 ? packed[(size_t)t * nw + w] : 0ull;
+      const int t = (c + u) * kWave + lane;
+      v[u] = __builtin_amdgcn_raw_buffer_load_b32(
+          pr, (c + u < c1 && t < T) ? (uint32_t)((t * nw + w) * 8 + (j >> 5) * 4) : kSkip, 0, 0);
     }
 #pragma unroll
-    for (int u = 0; u < 8; ++u) bits |= ((v[u] >> j) & 1ull) << (c + u);
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t b = ballot((v[u] >> (j & 31)) & 1u);
+      if (c + u < c1) {
+        if (lane == 0) sBallot[c + u] = b;
+        mine += popc64(b);
+      }
+    }
   }
-  const int mine = popc64(bits);
-  // inclusive scan inside the wave, then across the 16 waves
-  int incl = mine;
-  for (int off = 1; off < kWave; off <<= 1) {
-    const int v = __shfl_up(incl, off);
-    if (lane >= off) incl += v;
-  }
-  if (lane == kWave - 1) sWave[wave] = incl;
+  if (lane == 0) sWave[wave] = mine;
   __syncthreads();
-  int before = incl - mine, cnt = 0;
+  int kept = 0, cnt = 0;
   for (int i = 0; i < kGroupWaves; ++i) {
-    const int v = sWave[i];
-    if (i < wave) before += v;
-    cnt += v;
+    const int x = sWave[i];
+    if (i < wave) kept += x;
+    cnt += x;
   }
+  int dropped = c0 * kWave - kept;  // tokens before this wave's run that dropped g
   int32_t* perm = group_perm + (size_t)g * T;
   int32_t* rank = group_rank ? group_rank + (size_t)g * T : nullptr;
-  for (int i = 0; i < t1 - t0; ++i) {
-    const int t = t0 + i;
-    const bool bit = (bits >> i) & 1ull;
-    const int r = bit ? before : cnt + (t - before);
-    before += bit;
-    if (rank) rank[t] = r;
-    perm[r] = t;
+  for (int c = c0; c < c1; ++c) {
+    const uint64_t b = sBallot[c];
+    const int t = c * kWave + lane;
+    const int valid = min(kWave, T - c * kWave);
+    const uint64_t vm = valid == kWave ? ~0ull : ((1ull << valid) - 1ull);
+    const uint64_t d = ~b & vm;
+    if (t < T) {
+      const bool k = (b >> lane) & 1ull;
+      const int r = k ? kept + mbcnt(b) : cnt + dropped + mbcnt(d);
+      perm[r] = t;
+      if (rank) rank[t] = r;
+    }
+    kept += popc64(b);
+    dropped += popc64(d);
   }
   if (threadIdx.x == 0) group_count[g] = cnt;
 }
@@ -300,25 +302,28 @@ void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t
                                                         tile_perm);
 }
 
+void launch_reorder_packed(const uint64_t* packed, int T, int n, int tile_m,
+                           int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                           int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
+  const int nw = (n + 63) / 64;
+  const int n_tiles = tile_count ? (T + tile_m - 1) / tile_m : 0;
+  WIDE_TRACE("reorder_groups", s);
+  reorder_groups<<<n + n_tiles, kGroupThreads, 0, s>>>(packed, T, n, nw, tile_m, group_count,
+                                                        group_perm, group_rank, tile_count,
+                                                        tile_groups);
+}
+
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
   const int nw = (n + 63) / 64;
-  const int n_tiles = tile_count ? (T + tile_m - 1) / tile_m : 0;
   {
     WIDE_TRACE("reorder_pack", s);
-    const int grid = (T + kPackThreads - 1) / kPackThreads;
-    if (n % 4 == 0)
-      reorder_pack<true><<<grid, kPackThreads, 0, s>>>(mask, T, n, nw, packed);
-    else
-      reorder_pack<false><<<grid, kPackThreads, 0, s>>>(mask, T, n, nw, packed);
+    const int per_block = kPackWaves * kPackTok;
+    reorder_pack<<<(T + per_block - 1) / per_block, kPackThreads, 0, s>>>(mask, T, n, nw, packed);
   }
-  {
-    WIDE_TRACE("reorder_groups", s);
-    reorder_groups<<<n + n_tiles, kGroupThreads, 0, s>>>(packed, T, n, nw, tile_m, group_count,
-                                                          group_perm, group_rank, tile_count,
-                                                          tile_groups);
-  }
+  launch_reorder_packed(packed, T, n, tile_m, group_count, group_perm, group_rank, tile_count,
+                        tile_groups, s);
 }
 
 }  // namespace wide
