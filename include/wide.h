@@ -86,15 +86,18 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m,
                       void* stream);
 
 /*
- * wide_pack_kmajor - lay out a K-masked weight for the library (a pure permutation).
- *
- * W [n_groups * G, d_model] is the mathematical matrix of Y = H @ W (FFN down:
- * W_down [d_ff, d_model]; attention out: Wo [n_q*head_dim, d_model], which is
- * o_proj.weight transposed).  W_packed [n_groups, d_model, G] holds, for every
- * group g, the block W[gG:(g+1)G, :] transposed, so each group's block is one
- * contiguous region with the contraction index innermost.  Run once at weight load.
- * G a multiple of 64, or 32; d_model a multiple of 64.
+ * wide_mask_reorder_packed - wide_mask_reorder from packed mask words (as
+ * wide_router_topk writes them) instead of mask bytes: the same group_count,
+ * group_perm, group_rank, tile_count and tile_groups, without the packing step
+ * (gist.science technical summary §2.A router decisions feeding the §2.B
+ * reordering directly).
+ * packed [T, ceil(n_groups/64)] uint64 (input); bits past n_groups must be 0.
+ * Other arguments, limits and errors as wide_mask_reorder.
  */
+int wide_mask_reorder_packed(const uint64_t* packed, int T, int n_groups, int tile_m,
+                             int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                             int32_t* tile_count, int32_t* tile_groups, void* stream);
+
 /*
  * wide_router_topk - router and top-k selection, the step before the masked path
  * (gist.science technical summary §2.A: a router gives every token one binary
@@ -131,6 +134,16 @@ int wide_router_topk(const uint16_t* X, const uint16_t* R_packed, int T, int d_m
 int wide_pack_router(const uint16_t* R, int n_groups, int d_model, uint16_t* R_packed,
                      void* stream);
 
+/*
+ * wide_pack_kmajor - lay out a K-masked weight for the library (a pure permutation).
+ *
+ * W [n_groups * G, d_model] is the mathematical matrix of Y = H @ W (FFN down:
+ * W_down [d_ff, d_model]; attention out: Wo [n_q*head_dim, d_model], which is
+ * o_proj.weight transposed).  W_packed [n_groups, d_model, G] holds, for every
+ * group g, the block W[gG:(g+1)G, :] transposed, so each group's block is one
+ * contiguous region with the contraction index innermost.  Run once at weight load.
+ * G a multiple of 64, or 32; d_model a multiple of 64.
+ */
 int wide_pack_kmajor(const uint16_t* W, int n_groups, int G, int d_model, uint16_t* W_packed,
                      void* stream);
 
@@ -294,7 +307,12 @@ int wide_attn_decode_masked_paged(const uint16_t* X, const uint8_t* mask, const 
  * before its later work (this is also the fork/join pattern that stream capture
  * accepts).  Calls that enqueue on one device at the same time are serialised
  * by a lock while they enqueue.  If the second stream cannot be created the
- * call runs on `stream` alone.
+ * call runs on `stream` alone.  Limits of the second stream: it is shared by
+ * all layer calls on the device, so layer calls on different streams of one
+ * device are ordered with each other through it (they stay correct); under
+ * stream capture it joins the capture until the captured call's events are
+ * waited on.  If an event operation fails after the reorders were enqueued
+ * there, the call returns WIDE_EHIP with that work possibly still running.
  */
 typedef struct {
   const uint16_t* rms1;
@@ -321,6 +339,67 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
                       const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
                       uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap, uint16_t* Y,
                       void* workspace, size_t workspace_bytes, uint32_t flags, void* stream);
+
+/*
+ * wide_layer_masked_routed - wide_layer_masked with the masks chosen on the GPU by
+ * two linear routers on the layer input (gist.science technical summary §2.A: a
+ * router gives every token one binary execute/skip decision per group; its
+ * decisions go straight to the §2.B reordering):
+ *   attn_mask = top-k_attn of X R_attn^T,  ffn_mask = top-k_ffn of X R_ffn^T
+ * with wide_router_topk's rule (ties to the lower group index).  In prefill the
+ * routers' packed words feed the mask reorders directly (no packing step).
+ *
+ * router->R_attn_packed  wide_pack_router of R_attn [n_kv_heads, d_model] (input)
+ * router->R_ffn_packed   wide_pack_router of R_ffn [n_ffn_groups, d_model] (input)
+ * router->k_attn, k_ffn  groups each token keeps (0 .. n_kv_heads, 0 .. n_ffn_groups)
+ * attn_mask [T, n_kv_heads], ffn_mask [T, n_ffn_groups] uint8 (outputs, 1 = keep)
+ * Other arguments as wide_layer_masked; workspace: wide_layer_masked_workspace.
+ */
+typedef struct {
+  const uint16_t* R_attn_packed;
+  const uint16_t* R_ffn_packed;
+  int k_attn;
+  int k_ffn;
+} wide_layer_router;
+
+int wide_layer_masked_routed(const uint16_t* X, const wide_layer_router* router,
+                             const wide_layer_weights* W, const wide_layer_cfg* cfg, int T,
+                             int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len,
+                             int kv_cap, uint8_t* attn_mask, uint8_t* ffn_mask, uint16_t* Y,
+                             void* workspace, size_t workspace_bytes, uint32_t flags,
+                             void* stream);
+
+/*
+ * wide_layer_decode_masked_cache - one decode step of the whole layer over attention
+ * caches in which tokens that skipped a group left no entry (gist.science §2.A
+ * groups; the reading of wide_attn_decode_masked_cache carried across decode
+ * steps): u = RMSNorm(x), h = x + Attn(u) with per-(sequence, group) cache
+ * lengths kv_len [B, n_kv_heads] (device, input, not modified: the caller
+ * advances it by attn_mask after the call) and RoPE position pos for the new
+ * tokens, w = RMSNorm(h), y = h + FFN(w; ffn_mask).
+ * Cache rules as wide_attn_decode_masked_cache (kept pairs append at slot
+ * kv_len[b, g]; a length outside [0, kv_cap) acts as a dropped pair).
+ * B <= 64; workspace: wide_layer_masked_workspace(B, cfg, WIDE_DECODE, kv_cap).
+ */
+int wide_layer_decode_masked_cache(const uint16_t* X, const uint8_t* attn_mask,
+                                   const uint8_t* ffn_mask, const wide_layer_weights* W,
+                                   const wide_layer_cfg* cfg, int B, uint16_t* K_cache,
+                                   uint16_t* V_cache, int kv_cap, const int32_t* kv_len, int pos,
+                                   uint16_t* Y, void* workspace, size_t workspace_bytes,
+                                   uint32_t flags, void* stream);
+
+/*
+ * wide_layer_decode_masked_paged - wide_layer_decode_masked_cache over a paged
+ * cache: pools, page table and lengths exactly as wide_attn_decode_masked_paged.
+ * Workspace: wide_layer_masked_workspace(B, cfg, WIDE_DECODE, max_pages * page_size).
+ */
+int wide_layer_decode_masked_paged(const uint16_t* X, const uint8_t* attn_mask,
+                                   const uint8_t* ffn_mask, const wide_layer_weights* W,
+                                   const wide_layer_cfg* cfg, int B, uint16_t* K_pool,
+                                   uint16_t* V_pool, int n_pages, int page_size,
+                                   const int32_t* page_table, int max_pages,
+                                   const int32_t* kv_len, int pos, uint16_t* Y, void* workspace,
+                                   size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
  * Kernel timing, for benchmarking (not part of the method).  While enabled, each

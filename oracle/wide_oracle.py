@@ -294,14 +294,16 @@ def paged_to_contiguous(K_pool, V_pool, page_table, kv_len):
 
 def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q: int, n_kv: int, head_dim: int,
                  n_ffn: int, rope_theta: float, eps: float, decode: bool = False,
-                 K_cache=None, V_cache=None, kv_len: int = 0, dtype=np.float64,
+                 K_cache=None, V_cache=None, kv_len=0, pos=None, dtype=np.float64,
                  return_parts: bool = False, rows=None):
     """Pre-norm decoder layer with masked attention and masked FFN (reading R6).
 
     u = RMSNorm(x; rms1); h = x + Attn(u; attn_mask); w = RMSNorm(h; rms2);
     y = h + FFN(w; ffn_mask).  W holds rms1, rms2, Wq, Wk, Wv, Wo, W_gate, W_up,
     W_down.  ``n_ffn`` is the FFN group count (the mask's width).  With ``rows``
-    (prefill only) just those token rows of y are produced.
+    (prefill only) just those token rows of y are produced.  In decode, ``kv_len``
+    and ``pos`` are passed to the attention sublayer as they are (one length, or
+    per-(sequence, group) lengths with the new tokens' position, reading R5).
     """
     X = _f(X, dtype)
     if np.asarray(ffn_mask).shape[1] != n_ffn:
@@ -309,7 +311,7 @@ def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q: int, n_kv: int, head_d
     u = rmsnorm(X, W["rms1"], eps, dtype=dtype)
     att = attn_masked(u, attn_mask, W["Wq"], W["Wk"], W["Wv"], W["Wo"], n_q=n_q, n_kv=n_kv,
                       head_dim=head_dim, rope_theta=rope_theta, decode=decode,
-                      K_cache=K_cache, V_cache=V_cache, kv_len=kv_len, dtype=dtype,
+                      K_cache=K_cache, V_cache=V_cache, kv_len=kv_len, pos=pos, dtype=dtype,
                       rows=None if decode else rows)
     a = att[0] if decode else att
     R = slice(None) if (rows is None or decode) else np.asarray(rows)

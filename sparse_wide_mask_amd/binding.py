@@ -25,6 +25,10 @@ class WideLayerWeights(C.Structure):
                                   "W_down_packed")]
 
 
+class WideLayerRouter(C.Structure):
+    _fields_ = [("R_attn_packed", _p), ("R_ffn_packed", _p), ("k_attn", _i), ("k_ffn", _i)]
+
+
 class WideLayerCfg(C.Structure):
     _fields_ = [("d_model", _i), ("d_ff", _i), ("n_ffn_groups", _i), ("attn", WideAttnCfg),
                 ("rms_eps", C.c_float)]
@@ -34,6 +38,7 @@ _SIGS = {
     "wide_status_string": ([_i], C.c_char_p),
     "wide_version": ([], _i),
     "wide_mask_reorder": ([_p, _i, _i, _i, _p, _p, _p, _p, _p, _p, _p], _i),
+    "wide_mask_reorder_packed": ([_p, _i, _i, _i, _p, _p, _p, _p, _p, _p], _i),
     "wide_pack_kmajor": ([_p, _i, _i, _i, _p, _p], _i),
     "wide_router_topk": ([_p, _p, _i, _i, _i, _i, _p, _p, _p, _p], _i),
     "wide_pack_router": ([_p, _i, _i, _p, _p], _i),
@@ -55,6 +60,15 @@ _SIGS = {
     "wide_trace_reset": ([], None),
     "wide_layer_masked": ([_p, _p, _p, C.POINTER(WideLayerWeights), C.POINTER(WideLayerCfg), _i, _i,
                            _p, _p, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+    "wide_layer_masked_routed": ([_p, C.POINTER(WideLayerRouter), C.POINTER(WideLayerWeights),
+                                  C.POINTER(WideLayerCfg), _i, _i, _p, _p, _i, _i, _p, _p, _p, _p,
+                                  _sz, C.c_uint32, _p], _i),
+    "wide_layer_decode_masked_cache": ([_p, _p, _p, C.POINTER(WideLayerWeights),
+                                        C.POINTER(WideLayerCfg), _i, _p, _p, _i, _p, _i, _p, _p,
+                                        _sz, C.c_uint32, _p], _i),
+    "wide_layer_decode_masked_paged": ([_p, _p, _p, C.POINTER(WideLayerWeights),
+                                        C.POINTER(WideLayerCfg), _i, _p, _p, _i, _i, _p, _i, _p,
+                                        _i, _p, _p, _sz, C.c_uint32, _p], _i),
 }
 
 _lib = None
@@ -167,6 +181,33 @@ def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None) -> di
                                  _ptr(out["group_rank"]), _ptr(out["tile_count"]),
                                  _ptr(out["tile_groups"]), _stream())
     _check("wide_mask_reorder", st)
+    return out
+
+
+def mask_reorder_packed(packed: torch.Tensor, n_groups: int, tile_m: int,
+                        out: dict | None = None) -> dict:
+    """wide_mask_reorder_packed on packed mask words [T, ceil(n/64)] (int64 view of
+    the uint64 words, e.g. router_topk's "packed"); returns the five reorder outputs."""
+    _dev(packed, torch.int64, "packed")
+    T = packed.shape[0]
+    n = n_groups
+    if packed.shape[1] != (n + 63) // 64:
+        raise ValueError("packed must be [T, ceil(n_groups / 64)]")
+    dev = packed.device
+    nt = -(-T // tile_m) if T else 0
+    if out is None:
+        out = dict(
+            group_count=torch.empty(n, dtype=torch.int32, device=dev),
+            group_perm=torch.empty((n, T), dtype=torch.int32, device=dev),
+            group_rank=torch.empty((n, T), dtype=torch.int32, device=dev),
+            tile_count=torch.empty(nt, dtype=torch.int32, device=dev),
+            tile_groups=torch.empty((nt, n), dtype=torch.int32, device=dev),
+        )
+    st = lib().wide_mask_reorder_packed(_ptr(packed), T, n, tile_m, _ptr(out["group_count"]),
+                                        _ptr(out["group_perm"]), _ptr(out["group_rank"]),
+                                        _ptr(out["tile_count"]), _ptr(out["tile_groups"]),
+                                        _stream())
+    _check("wide_mask_reorder_packed", st)
     return out
 
 
@@ -406,4 +447,110 @@ def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, head_dim=128,
                                  C.byref(cfg), T, m, _ptr(K_cache), _ptr(V_cache), kv_len, kv_cap,
                                  _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
     _check("wide_layer_masked", st)
+    return Y
+
+
+_LAYER_KEYS = ("rms1", "Wq", "Wk", "Wv", "Wo_packed", "rms2", "W_gate", "W_up", "W_down_packed")
+
+
+def _layer_weights(W: dict):
+    for k in _LAYER_KEYS:
+        _dev(W[k], torch.bfloat16, k)
+    return WideLayerWeights(*[W[k].data_ptr() for k in _LAYER_KEYS])
+
+
+def layer_masked_routed(X, R_attn_packed, k_attn, R_ffn_packed, k_ffn, W: dict, *, n_q, n_kv,
+                        n_ffn, head_dim=128, rope_theta=500000.0, eps=1e-5, mode="prefill",
+                        K_cache=None, V_cache=None, kv_len=0, out=None, attn_mask=None,
+                        ffn_mask=None, workspace=None):
+    """wide_layer_masked_routed: the layer with masks chosen on the GPU by two linear
+    routers on X (R_*_packed from pack_router).  Returns (Y, attn_mask, ffn_mask)."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(R_attn_packed, torch.bfloat16, "R_attn_packed")
+    _dev(R_ffn_packed, torch.bfloat16, "R_ffn_packed")
+    m = _mode(mode)
+    T, d = X.shape
+    F = W["W_gate"].shape[0]
+    kv_cap = 0
+    if m == WIDE_DECODE:
+        _dev(K_cache, torch.bfloat16, "K_cache")
+        _dev(V_cache, torch.bfloat16, "V_cache")
+        kv_cap = K_cache.shape[2]
+    cfg = _layer_cfg(d, F, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
+    wts = _layer_weights(W)
+    rt = WideLayerRouter(R_attn_packed.data_ptr(), R_ffn_packed.data_ptr(), int(k_attn),
+                         int(k_ffn))
+    ws_bytes = int(lib().wide_layer_masked_workspace(T, C.byref(cfg), m, kv_cap))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
+    am = attn_mask if attn_mask is not None else torch.empty((T, n_kv), dtype=torch.uint8,
+                                                             device=X.device)
+    fm = ffn_mask if ffn_mask is not None else torch.empty((T, n_ffn), dtype=torch.uint8,
+                                                           device=X.device)
+    st = lib().wide_layer_masked_routed(_ptr(X), C.byref(rt), C.byref(wts), C.byref(cfg), T, m,
+                                        _ptr(K_cache), _ptr(V_cache), kv_len, kv_cap, _ptr(am),
+                                        _ptr(fm), _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_layer_masked_routed", st)
+    return Y, am, fm
+
+
+def layer_decode_masked_cache(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, K_cache, V_cache,
+                              kv_len, pos, head_dim=128, rope_theta=500000.0, eps=1e-5, out=None,
+                              workspace=None):
+    """wide_layer_decode_masked_cache: one layer decode step over per-(sequence, group)
+    cache lengths kv_len (int32 [B, n_kv], not modified).  Returns Y [B, d]."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(attn_mask, torch.uint8, "attn_mask")
+    _dev(ffn_mask, torch.uint8, "ffn_mask")
+    _dev(K_cache, torch.bfloat16, "K_cache")
+    _dev(V_cache, torch.bfloat16, "V_cache")
+    _dev(kv_len, torch.int32, "kv_len")
+    B, d = X.shape
+    F = W["W_gate"].shape[0]
+    n_ffn = ffn_mask.shape[1]
+    kv_cap = K_cache.shape[2]
+    cfg = _layer_cfg(d, F, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
+    wts = _layer_weights(W)
+    ws_bytes = int(lib().wide_layer_masked_workspace(B, C.byref(cfg), WIDE_DECODE, kv_cap))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((B, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_layer_decode_masked_cache(_ptr(X), _ptr(attn_mask), _ptr(ffn_mask),
+                                              C.byref(wts), C.byref(cfg), B, _ptr(K_cache),
+                                              _ptr(V_cache), kv_cap, _ptr(kv_len), int(pos),
+                                              _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_layer_decode_masked_cache", st)
+    return Y
+
+
+def layer_decode_masked_paged(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, K_pool, V_pool,
+                              page_table, kv_len, pos, head_dim=128, rope_theta=500000.0,
+                              eps=1e-5, out=None, workspace=None):
+    """wide_layer_decode_masked_paged: layer_decode_masked_cache over a paged pool
+    (K_pool, V_pool [n_pages, page_size, head_dim]; page_table [B, n_kv, max_pages])."""
+    _dev(X, torch.bfloat16, "X")
+    _dev(attn_mask, torch.uint8, "attn_mask")
+    _dev(ffn_mask, torch.uint8, "ffn_mask")
+    _dev(K_pool, torch.bfloat16, "K_pool")
+    _dev(V_pool, torch.bfloat16, "V_pool")
+    _dev(kv_len, torch.int32, "kv_len")
+    _dev(page_table, torch.int32, "page_table")
+    B, d = X.shape
+    F = W["W_gate"].shape[0]
+    n_ffn = ffn_mask.shape[1]
+    n_pages, page_size = K_pool.shape[0], K_pool.shape[1]
+    if tuple(V_pool.shape) != tuple(K_pool.shape) or page_table.dim() != 3:
+        raise ValueError("K_pool and V_pool must match; page_table must be [B, n_kv, max_pages]")
+    max_pages = page_table.shape[2]
+    cfg = _layer_cfg(d, F, n_ffn, n_q, n_kv, head_dim, rope_theta, eps)
+    wts = _layer_weights(W)
+    ws_bytes = int(lib().wide_layer_masked_workspace(B, C.byref(cfg), WIDE_DECODE,
+                                                     max_pages * page_size))
+    ws = _workspace(ws_bytes, X.device, workspace)
+    Y = out if out is not None else torch.empty((B, d), dtype=torch.bfloat16, device=X.device)
+    st = lib().wide_layer_decode_masked_paged(_ptr(X), _ptr(attn_mask), _ptr(ffn_mask),
+                                              C.byref(wts), C.byref(cfg), B, _ptr(K_pool),
+                                              _ptr(V_pool), n_pages, page_size, _ptr(page_table),
+                                              max_pages, _ptr(kv_len), int(pos), _ptr(Y),
+                                              _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_layer_decode_masked_paged", st)
     return Y

@@ -172,15 +172,31 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
 // Prefill: group partitions for the QKV projection and the core; for the O
 // projection with few groups, tiles of tokens sorted by their head-group
 // pattern, so that row blocks and whole tiles share dropped groups.
-void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s) {
-  if (nkv <= kSortMaxGroups) {
-    launch_reorder(mask, T, nkv, w.rv.tile_m, w.rv.packed, w.rv.count, w.rv.perm, w.rv.rank,
-                   nullptr, nullptr, s);
-    launch_token_sort(w.rv.packed, T, nkv, w.rv.tile_m, w.rv.order, w.rv.tile_count,
-                      w.rv.tile_groups, w.rv.tile_perm, s);
-  } else {
-    run_reorder(mask, T, nkv, w.rv, s);
-  }
+// packed_ready: the reorder's packed words already hold the mask (the router
+// wrote them), so the packing launch is skipped.
+void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
+                  bool packed_ready = false) {
+  const ReorderView& v = w.rv;
+  const bool sort = nkv <= kSortMaxGroups;
+  if (packed_ready)
+    launch_reorder_packed(v.packed, T, nkv, v.tile_m, v.count, v.perm, v.rank,
+                          sort ? nullptr : v.tile_count, sort ? nullptr : v.tile_groups, s);
+  else
+    launch_reorder(mask, T, nkv, v.tile_m, v.packed, v.count, v.perm, v.rank,
+                   sort ? nullptr : v.tile_count, sort ? nullptr : v.tile_groups, s);
+  if (sort)
+    launch_token_sort(v.packed, T, nkv, v.tile_m, v.order, v.tile_count, v.tile_groups,
+                      v.tile_perm, s);
+}
+
+void ffn_reorder(const uint8_t* mask, int T, int n, const FfnWs& w, hipStream_t s,
+                 bool packed_ready = false) {
+  const ReorderView& v = w.rv;
+  if (packed_ready)
+    launch_reorder_packed(v.packed, T, n, v.tile_m, v.count, v.perm, v.rank, v.tile_count,
+                          v.tile_groups, s);
+  else
+    run_reorder(mask, T, n, v, s);
 }
 
 // reorder = false: attn_reorder of this call was already enqueued
@@ -260,6 +276,69 @@ LayerWs carve_layer(Carver& c, int T, const wide_layer_cfg* cfg, int mode, int k
   return w;
 }
 
+// Decode cache of a layer call: one length for the batch (kv_len), or lengths per
+// (sequence, group) in device memory (pair_len) with the new tokens' RoPE
+// position, optionally in a paged pool.
+struct LayerCache {
+  uint16_t *K = nullptr, *V = nullptr;
+  int kv_len = 0, kv_cap = 0;
+  const int32_t* pair_len = nullptr;
+  int pos = -1;
+  const PagedKV* paged = nullptr;
+};
+
+// Launch sequence of a layer call (arguments validated).  packed_ready: the
+// reorders' packed words already hold both masks (the router wrote them).
+// Prefill enqueues the two mask reorders on the device's second stream, beside
+// the first RMSNorm and the attention kernels, joined back by events.
+int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_mask,
+              const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
+              const LayerCache& kv, uint16_t* Y, const LayerWs& w, hipStream_t s,
+              bool packed_ready) {
+  const int d = cfg->d_model, nkv = cfg->attn.n_kv_heads, n = cfg->n_ffn_groups;
+  auto attention = [&]() {
+    attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode, kv.K,
+             kv.V, kv.kv_len, kv.kv_cap, X, w.h, w.attn, s, kv.pair_len, kv.pos, false,
+             kv.paged);
+  };
+  auto ffn = [&]() {
+    ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, n, mode, w.h,
+            Y, w.ffn, s, false);
+  };
+  if (mode == WIDE_PREFILL) {
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = side_stream();
+    if (side && hipEventRecord(side->fork, s) == hipSuccess &&
+        hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess) {
+      attn_reorder(attn_mask, T, nkv, w.attn, side->s, packed_ready);
+      if (hipEventRecord(side->attn_done, side->s) != hipSuccess) return WIDE_EHIP;
+      ffn_reorder(ffn_mask, T, n, w.ffn, side->s, packed_ready);
+      if (hipEventRecord(side->ffn_done, side->s) != hipSuccess) return WIDE_EHIP;
+      launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
+      if (hipStreamWaitEvent(s, side->attn_done, 0) != hipSuccess) return WIDE_EHIP;
+      attention();
+      launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
+      if (hipStreamWaitEvent(s, side->ffn_done, 0) != hipSuccess) return WIDE_EHIP;
+      ffn();
+      return launch_status();
+    }
+    (void)hipGetLastError();
+    attn_reorder(attn_mask, T, nkv, w.attn, s, packed_ready);
+    ffn_reorder(ffn_mask, T, n, w.ffn, s, packed_ready);
+  }
+  launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
+  attention();
+  launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
+  ffn();
+  return launch_status();
+}
+
+bool layer_weights_ok(const wide_layer_weights* W) {
+  return W && aligned16(W->rms1) && aligned16(W->rms2) && aligned16(W->Wq) &&
+         aligned16(W->Wk) && aligned16(W->Wv) && aligned16(W->Wo_packed) &&
+         aligned16(W->W_gate) && aligned16(W->W_up) && aligned16(W->W_down_packed);
+}
+
 // ------------------------------------------------ allocation-free FFN entry point
 
 // The scratch memory of wide_ffn_masked_noalloc: a fixed array in device memory,
@@ -319,6 +398,21 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m, uint
   (void)hipGetLastError();
   launch_reorder(mask, T, n_groups, tile_m, packed, group_count, group_perm, group_rank,
                  tile_count, tile_groups, as_stream(stream));
+  return launch_status();
+}
+
+int wide_mask_reorder_packed(const uint64_t* packed, int T, int n_groups, int tile_m,
+                             int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                             int32_t* tile_count, int32_t* tile_groups, void* stream) {
+  if (T < 0 || n_groups < 1 || tile_m < 1 || tile_m > 1024) return WIDE_EINVAL;
+  if (n_groups > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(packed) || !aligned16(group_count) || !aligned16(group_perm) ||
+      !aligned16(group_rank) || !aligned16(tile_count) || !aligned16(tile_groups))
+    return WIDE_EINVAL;
+  (void)hipGetLastError();
+  launch_reorder_packed(packed, T, n_groups, tile_m, group_count, group_perm, group_rank,
+                        tile_count, tile_groups, as_stream(stream));
   return launch_status();
 }
 
@@ -547,9 +641,7 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
   }
   if (T == 0) return WIDE_OK;
   if (!aligned16(X) || !aligned16(attn_mask) || !aligned16(ffn_mask) || !aligned16(Y) ||
-      (void*)Y == (void*)X || !aligned16(W->rms1) || !aligned16(W->rms2) || !aligned16(W->Wq) ||
-      !aligned16(W->Wk) || !aligned16(W->Wv) || !aligned16(W->Wo_packed) ||
-      !aligned16(W->W_gate) || !aligned16(W->W_up) || !aligned16(W->W_down_packed))
+      (void*)Y == (void*)X || !layer_weights_ok(W))
     return WIDE_EINVAL;
   Carver probe(nullptr);
   carve_layer(probe, T, cfg, mode, kv_cap);
@@ -557,38 +649,123 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
   if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
   Carver c(workspace);
   LayerWs w = carve_layer(c, T, cfg, mode, kv_cap);
-  const int d = cfg->d_model;
-  hipStream_t s = as_stream(stream);
+  LayerCache kv;
+  kv.K = K_cache, kv.V = V_cache, kv.kv_len = kv_len, kv.kv_cap = kv_cap;
   (void)hipGetLastError();
-  if (mode == WIDE_PREFILL) {
-    // the mask reorders on the side stream, beside RMSNorm and attention
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* side = side_stream();
-    if (side && hipEventRecord(side->fork, s) == hipSuccess &&
-        hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess) {
-      attn_reorder(attn_mask, T, cfg->attn.n_kv_heads, w.attn, side->s);
-      if (hipEventRecord(side->attn_done, side->s) != hipSuccess) return WIDE_EHIP;
-      run_reorder(ffn_mask, T, cfg->n_ffn_groups, w.ffn.rv, side->s);
-      if (hipEventRecord(side->ffn_done, side->s) != hipSuccess) return WIDE_EHIP;
-      launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
-      if (hipStreamWaitEvent(s, side->attn_done, 0) != hipSuccess) return WIDE_EHIP;
-      attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode,
-               K_cache, V_cache, kv_len, kv_cap, X, w.h, w.attn, s, nullptr, -1, false);
-      launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
-      if (hipStreamWaitEvent(s, side->ffn_done, 0) != hipSuccess) return WIDE_EHIP;
-      ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff,
-              cfg->n_ffn_groups, mode, w.h, Y, w.ffn, s, false);
-      return launch_status();
-    }
-    (void)hipGetLastError();
+  return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, as_stream(stream), false);
+}
+
+int wide_layer_masked_routed(const uint16_t* X, const wide_layer_router* router,
+                             const wide_layer_weights* W, const wide_layer_cfg* cfg, int T,
+                             int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len,
+                             int kv_cap, uint8_t* attn_mask, uint8_t* ffn_mask, uint16_t* Y,
+                             void* workspace, size_t workspace_bytes, uint32_t flags,
+                             void* stream) {
+  int st = layer_check(T, cfg, mode);
+  if (st != WIDE_OK) return st;
+  if (flags != 0 || !W || !router) return WIDE_EINVAL;
+  const int nkv = cfg->attn.n_kv_heads, n = cfg->n_ffn_groups;
+  if (router->k_attn < 0 || router->k_attn > nkv || router->k_ffn < 0 || router->k_ffn > n)
+    return WIDE_EINVAL;
+  if (mode == WIDE_DECODE) {
+    st = attn_decode_check(T, &cfg->attn, K_cache, V_cache, kv_len, kv_cap);
+    if (st != WIDE_OK) return st;
   }
-  launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
-  attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode, K_cache,
-           V_cache, kv_len, kv_cap, X, w.h, w.attn, s);
-  launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
-  ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, cfg->n_ffn_groups,
-          mode, w.h, Y, w.ffn, s);
-  return launch_status();
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(attn_mask) || !aligned16(ffn_mask) || !aligned16(Y) ||
+      (void*)Y == (void*)X || !layer_weights_ok(W) || !aligned16(router->R_attn_packed) ||
+      !aligned16(router->R_ffn_packed) || (void*)attn_mask == (void*)ffn_mask ||
+      (const void*)attn_mask == (const void*)X || (const void*)ffn_mask == (const void*)X)
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_layer(probe, T, cfg, mode, kv_cap);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  LayerWs w = carve_layer(c, T, cfg, mode, kv_cap);
+  LayerCache kv;
+  kv.K = K_cache, kv.V = V_cache, kv.kv_len = kv_len, kv.kv_cap = kv_cap;
+  hipStream_t s = as_stream(stream);
+  const bool prefill = mode == WIDE_PREFILL;
+  (void)hipGetLastError();
+  // the routers read the layer input; in prefill their packed words go straight
+  // to the reorders' buffers
+  launch_router_topk(X, router->R_attn_packed, T, cfg->d_model, nkv, router->k_attn, nullptr,
+                     attn_mask, prefill ? w.attn.rv.packed : nullptr, s);
+  launch_router_topk(X, router->R_ffn_packed, T, cfg->d_model, n, router->k_ffn, nullptr,
+                     ffn_mask, prefill ? w.ffn.rv.packed : nullptr, s);
+  return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, s, prefill);
+}
+
+int wide_layer_decode_masked_cache(const uint16_t* X, const uint8_t* attn_mask,
+                                   const uint8_t* ffn_mask, const wide_layer_weights* W,
+                                   const wide_layer_cfg* cfg, int B, uint16_t* K_cache,
+                                   uint16_t* V_cache, int kv_cap, const int32_t* kv_len, int pos,
+                                   uint16_t* Y, void* workspace, size_t workspace_bytes,
+                                   uint32_t flags, void* stream) {
+  int st = layer_check(B, cfg, WIDE_DECODE);
+  if (st != WIDE_OK) return st;
+  if (flags != 0 || !W || pos < 0) return WIDE_EINVAL;
+  st = attn_decode_check(B, &cfg->attn, K_cache, V_cache, kv_cap - 1, kv_cap);
+  if (st != WIDE_OK) return st;
+  if (B == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(attn_mask) || !aligned16(ffn_mask) || !aligned16(Y) ||
+      !aligned16(kv_len) || (void*)Y == (void*)X || !layer_weights_ok(W))
+    return WIDE_EINVAL;
+  if ((const void*)kv_len == (const void*)K_cache || (const void*)kv_len == (const void*)V_cache)
+    return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_layer(probe, B, cfg, WIDE_DECODE, kv_cap);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  LayerWs w = carve_layer(c, B, cfg, WIDE_DECODE, kv_cap);
+  LayerCache kv;
+  kv.K = K_cache, kv.V = V_cache, kv.kv_cap = kv_cap, kv.pair_len = kv_len, kv.pos = pos;
+  (void)hipGetLastError();
+  return layer_run(X, attn_mask, ffn_mask, W, cfg, B, WIDE_DECODE, kv, Y, w, as_stream(stream),
+                   false);
+}
+
+int wide_layer_decode_masked_paged(const uint16_t* X, const uint8_t* attn_mask,
+                                   const uint8_t* ffn_mask, const wide_layer_weights* W,
+                                   const wide_layer_cfg* cfg, int B, uint16_t* K_pool,
+                                   uint16_t* V_pool, int n_pages, int page_size,
+                                   const int32_t* page_table, int max_pages,
+                                   const int32_t* kv_len, int pos, uint16_t* Y, void* workspace,
+                                   size_t workspace_bytes, uint32_t flags, void* stream) {
+  int st = layer_check(B, cfg, WIDE_DECODE);
+  if (st != WIDE_OK) return st;
+  if (flags != 0 || !W || pos < 0) return WIDE_EINVAL;
+  if (page_size < 16 || (page_size & (page_size - 1)) || n_pages < 1 || max_pages < 1)
+    return WIDE_EINVAL;
+  if (!aligned16(K_pool) || !aligned16(V_pool) || K_pool == V_pool) return WIDE_EINVAL;
+  if (!fits((int64_t)n_pages * page_size, kHeadDim) ||
+      !fits((int64_t)max_pages * page_size, kHeadDim))
+    return WIDE_EUNSUPPORTED;
+  const int kv_cap = max_pages * page_size;
+  if (B == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(attn_mask) || !aligned16(ffn_mask) || !aligned16(Y) ||
+      !aligned16(kv_len) || !aligned16(page_table) || (void*)Y == (void*)X ||
+      !layer_weights_ok(W))
+    return WIDE_EINVAL;
+  for (const void* p : {(const void*)kv_len, (const void*)page_table})
+    if (p == (const void*)K_pool || p == (const void*)V_pool) return WIDE_EINVAL;
+  Carver probe(nullptr);
+  carve_layer(probe, B, cfg, WIDE_DECODE, kv_cap);
+  if (!aligned16(workspace)) return WIDE_EINVAL;
+  if (workspace_bytes < probe.used) return WIDE_EWORKSPACE;
+  Carver c(workspace);
+  LayerWs w = carve_layer(c, B, cfg, WIDE_DECODE, kv_cap);
+  int shift = 0;
+  while ((1 << shift) < page_size) ++shift;
+  const PagedKV pg{page_table, shift, n_pages};
+  LayerCache kv;
+  kv.K = K_pool, kv.V = V_pool, kv.kv_cap = kv_cap, kv.pair_len = kv_len, kv.pos = pos;
+  kv.paged = &pg;
+  (void)hipGetLastError();
+  return layer_run(X, attn_mask, ffn_mask, W, cfg, B, WIDE_DECODE, kv, Y, w, as_stream(stream),
+                   false);
 }
 
 }  // extern "C"

@@ -35,6 +35,10 @@ struct ReorderView {
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
+// The same from packed mask words (the router's output): no packing launch.
+void launch_reorder_packed(const uint64_t* packed, int T, int n, int tile_m,
+                           int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                           int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
 // Token order sorted by mask pattern (stable; n <= kSortMaxGroups, so the key is
 // the whole pattern), and the group union of each tile of tile_m consecutive
 // tokens in that order.  T <= WIDE_MAX_TOKENS (the keys take T bytes of LDS).
