@@ -46,8 +46,10 @@ enum { kNmFfn = 0, kNmQkv = 1 };
 // Weight loads of this many 32-wide K steps are issued before their MFMAs, with
 // the matching activation loads: W takes 4 VGPRs per step and X 4 per step and
 // row block, so fewer steps are batched when the batch spans more row blocks.
-template <int NRB>
-constexpr int dec_unroll() { return NRB == 1 ? 16 : NRB == 2 ? 8 : 4; }
+template <int NRB, int NCB = 1>
+constexpr int dec_unroll() {
+  return NRB == 1 ? (NCB == 1 ? 16 : 8) : NRB == 2 ? (NCB == 1 ? 8 : 4) : 4;
+}
 
 // Activation operand of one 16x16x32 step: a buffer load whose offset is past the
 // buffer for rows without a token, so it returns zeros and is never a branch.
@@ -163,7 +165,8 @@ constexpr int kDecCompactRows = 4;
 // ones (a read kernel of the same bytes with every other run of 16 work-groups
 // empty took 27 us instead of 22 us; with the empty ones last, 22 us).  Thread
 // t < n_groups reads group t's mask column; returns the group (-1: none) and
-// its column's token bits.  A 256-thread work-group, n_groups <= 256.
+// its column's token bits.  A work-group of NW >= 4 waves, n_groups <= 256.
+template <int NW>
 WIDE_DEV int union_group_nth(const uint8_t* mask, int B, int n_groups, int q, int* sSel,
                              int* sWc, uint32_t* colbits_out) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -188,18 +191,25 @@ WIDE_DEV int union_group_nth(const uint8_t* mask, int B, int n_groups, int q, in
   return sSel[0];
 }
 
-template <int MODE, int NRB>
-__global__ void __launch_bounds__(256)
+// NCB: MFMA column blocks per wave (consecutive chunks of the group).  Each wave
+// reads an activation fragment once for its NCB weight fragments, so a larger
+// NCB reads the activation rows fewer times from L2 (they are as many bytes as
+// the weights when every 16 columns read them); the grid has NCB times fewer
+// work-groups.
+template <int MODE, int NRB, int NCB, int NW>
+__global__ void __launch_bounds__(64 * NW)
     nmask_decode(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W0,
                  const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2,
                  const uint8_t* __restrict__ mask, int B, int d, int G, int chunks, int r,
                  DecCache dc, float log2_theta, uint16_t* __restrict__ out0,
                  uint16_t* __restrict__ Kc, uint16_t* __restrict__ Vc, int n_groups) {
+  constexpr int NEL = NCB * NRB * 256;  // output elements of the work-group
   __shared__ int sTok[kDecRows];
-  __shared__ float sRed[3][kDecRows][16];
-  __shared__ int sSel[2], sWc[4];
+  __shared__ float sRed[NW][NEL];
+  __shared__ int sSel[2], sWc[NW];
 
-  const int q = blockIdx.x / chunks, cb = blockIdx.x % chunks;
+  const int cpw = chunks / NCB;  // work-groups per group
+  const int q = blockIdx.x / cpw, cb0 = (blockIdx.x % cpw) * NCB;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // group g and its mask column (one token per bit): kept tokens in order are the
   // MFMA rows
@@ -207,7 +217,7 @@ __global__ void __launch_bounds__(256)
   uint64_t mcol;
   if (B <= kDecCompactRows) {
     uint32_t colbits;
-    g = union_group_nth(mask, B, n_groups, q, sSel, sWc, &colbits);
+    g = union_group_nth<NW>(mask, B, n_groups, q, sSel, sWc, &colbits);
     if (g < 0) return;  // l=0: past the batch's union
     mcol = colbits;
   } else {
@@ -226,16 +236,20 @@ __global__ void __launch_bounds__(256)
   const int nrb = (cnt + 15) / 16;  // l=2: row blocks past the count are skipped
 
   const int ch = lane & 15;
-  const NmCol<MODE> col(g, cb, ch, W0, W1, W2, G, d, r, dc.pos, log2_theta);
-  const uint16_t* wrow = col.wrow;
-
-  f32x4 acc[NRB];
-#pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int nsteps = d / 32;  // 32-wide K steps, split evenly over the 4 waves
-  const int kbeg = (wave * nsteps / 4) * 32, kend = ((wave + 1) * nsteps / 4) * 32;
   const int koff = 8 * (lane >> 4);
+  const uint16_t* wp[NCB];
+#pragma unroll
+  for (int j = 0; j < NCB; ++j)
+    wp[j] = NmCol<MODE>(g, cb0 + j, ch, W0, W1, W2, G, d, r, dc.pos, 0.f).wrow + koff;
+
+  f32x4 acc[NRB][NCB];
+#pragma unroll
+  for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+    for (int j = 0; j < NCB; ++j) acc[rb][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int nsteps = d / 32;  // 32-wide K steps, split evenly over the NW waves
+  const int kbeg = (wave * nsteps / NW) * 32, kend = ((wave + 1) * nsteps / NW) * 32;
   // X byte offsets of this lane's rows (k = koff); kSkip for rows without a token
   const rsrc_t xr = make_rsrc(X, (uint32_t)((size_t)B * d * 2));
   uint32_t xoff[NRB];
@@ -244,10 +258,9 @@ __global__ void __launch_bounds__(256)
     const int tok = sTok[rb * 16 + ch];
     xoff[rb] = tok >= 0 ? (uint32_t)(((size_t)tok * d + koff) * 2) : kSkip;
   }
-  const uint16_t* wp = wrow + koff;
   // Every work-group reads the same activation rows; each starts its K walk at
   // a different batch so that they do not all hit the same L2 lines at once.
-  constexpr int U = dec_unroll<NRB>();
+  constexpr int U = dec_unroll<NRB, NCB>();
   const int S = (kend - kbeg) / 32;
   const int nbat = S / U;
   const int rot = nbat > 0 ? (int)((blockIdx.x * 7u) % (unsigned)nbat) * U : 0;
@@ -260,19 +273,19 @@ __global__ void __launch_bounds__(256)
     // few rows: MFMA fragments straight from global memory
 #pragma unroll 1
     for (int j0 = 0; j0 < nbat * U; j0 += U) {
-      bf16x8 wf[U], xf[U][NRB];
-#pragma unroll
-      for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + kat(j0 + u));
+      bf16x8 wf[U][NCB], xf[U];
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) xf[u][rb] = xload(xr, xoff[rb] + kat(j0 + u) * 2);
+        for (int j = 0; j < NCB; ++j)
+          wf[u][j] = *reinterpret_cast<const bf16x8*>(wp[j] + kat(j0 + u));
+#pragma unroll
+      for (int u = 0; u < U; ++u) xf[u] = xload(xr, xoff[0] + kat(j0 + u) * 2);
       __builtin_amdgcn_sched_barrier(0);  // all loads of the batch before its MFMAs
 #pragma unroll
       for (int u = 0; u < U; ++u)
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb)
-          if (rb < nrb) acc[rb] = mfma16(xf[u][rb], wf[u], acc[rb]);
+        for (int j = 0; j < NCB; ++j) acc[0][j] = mfma16(xf[u], wf[u][j], acc[0][j]);
     }
   } else {
     // Many rows (used when there are too few column blocks to fill the chip
@@ -283,7 +296,7 @@ __global__ void __launch_bounds__(256)
     constexpr int CPR = 4 * U;          // 16-byte chunks per row per batch
     constexpr int RPI = 64 / CPR;       // rows per load instruction
     constexpr int NI = 16 * NRB / RPI;  // load instructions per batch
-    __shared__ __attribute__((aligned(16))) uint16_t sX[4][16 * NRB * CPR * 8];
+    __shared__ __attribute__((aligned(16))) uint16_t sX[NW][16 * NRB * CPR * 8];
     uint16_t* myX = sX[wave];
     const int lrow = lane / CPR, lch = lane % CPR;
     uint32_t rowoff[NI];
@@ -295,10 +308,13 @@ __global__ void __launch_bounds__(256)
 #pragma unroll 1
     for (int j0 = 0; j0 < nbat * U; j0 += U) {
       const int k0 = kat(j0);
-      bf16x8 wf[U];
+      bf16x8 wf[U][NCB];
       u32x4 xv[NI];
 #pragma unroll
-      for (int u = 0; u < U; ++u) wf[u] = *reinterpret_cast<const bf16x8*>(wp + k0 + 32 * u);
+      for (int u = 0; u < U; ++u)
+#pragma unroll
+        for (int j = 0; j < NCB; ++j)
+          wf[u][j] = *reinterpret_cast<const bf16x8*>(wp[j] + k0 + 32 * u);
 #pragma unroll
       for (int i = 0; i < NI; ++i) xv[i] = ldbuf16(xr, rowoff[i] + k0 * 2);
 #pragma unroll
@@ -315,39 +331,54 @@ __global__ void __launch_bounds__(256)
           const int row = rb * 16 + ch, c = 4 * u + (lane >> 4);
           const bf16x8 xf =
               *reinterpret_cast<const bf16x8*>(myX + (row * CPR + (c ^ (row % CPR))) * 8);
-          acc[rb] = mfma16(xf, wf[u], acc[rb]);
+#pragma unroll
+          for (int j = 0; j < NCB; ++j) acc[rb][j] = mfma16(xf, wf[u][j], acc[rb][j]);
         }
       __builtin_amdgcn_wave_barrier();  // fragment reads before the next batch's writes
     }
   }
   for (int j0 = nbat * U; j0 < S; ++j0) {
     const int k0 = kat(j0);
-    const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wp + k0);
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb)
-      if (rb < nrb) acc[rb] = mfma16(xload(xr, xoff[rb] + k0 * 2), wf, acc[rb]);
+    for (int j = 0; j < NCB; ++j) {
+      const bf16x8 wf = *reinterpret_cast<const bf16x8*>(wp[j] + k0);
+#pragma unroll
+      for (int rb = 0; rb < NRB; ++rb)
+        if (rb < nrb) acc[rb][j] = mfma16(xload(xr, xoff[rb] + k0 * 2), wf, acc[rb][j]);
+    }
   }
 
-  // reduce the 4 K-quarters: waves 1..3 park partials in LDS, wave 0 adds
-  if (wave > 0) {
+  // reduce the NW K-stretches: every wave parks its partial sums in LDS, the
+  // work-group adds them (one element per thread at a time), wave 0 stores
 #pragma unroll
-    for (int rb = 0; rb < NRB; ++rb) {
-      if (rb >= nrb) break;
+  for (int j = 0; j < NCB; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) sRed[wave - 1][rb * 16 + acc16_row(lane, i)][ch] = acc[rb][i];
-    }
+    for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        sRed[wave][((j * NRB + rb) * 16 + acc16_row(lane, i)) * 16 + ch] = acc[rb][j][i];
+  __syncthreads();
+  for (int e = tid; e < NEL; e += 64 * NW) {
+    float v = sRed[0][e];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) v += sRed[w][e];
+    sRed[0][e] = v;
   }
   __syncthreads();
   if (wave > 0) return;
 #pragma unroll
-  for (int rb = 0; rb < NRB; ++rb) {
-    if (rb >= nrb) break;
+  for (int j = 0; j < NCB; ++j) {
+    const NmCol<MODE> col(g, cb0 + j, ch, W0, W1, W2, G, d, r, dc.pos, log2_theta);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = rb * 16 + acc16_row(lane, i);
-      const float v = acc[rb][i] + sRed[0][row][ch] + sRed[1][row][ch] + sRed[2][row][ch];
-      col.store(v, row < cnt ? sTok[row] : -1, g, cb, ch, G, r, n_groups, dc, out0,
-                Kc, Vc);
+    for (int rb = 0; rb < NRB; ++rb) {
+      if (rb >= nrb) break;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int row = rb * 16 + acc16_row(lane, i);
+        const float v = sRed[0][((j * NRB + rb) * 16 + acc16_row(lane, i)) * 16 + ch];
+        col.store(v, row < cnt ? sTok[row] : -1, g, cb0 + j, ch, G, r, n_groups, dc, out0,
+                  Kc, Vc);
+      }
     }
   }
 }
@@ -1003,6 +1034,35 @@ __global__ void __launch_bounds__(kCmbThreads)
 // otherwise the K-split kernel (16 columns per work-group, 4x the work-groups).
 static bool use_cols(int nrb, int col_blocks) { return nrb > 1 && col_blocks >= 256; }
 
+// Column blocks per wave of the attention q/k/v decode projection (batches of 1
+// or 2 row blocks): 2 when the group's chunks divide and at least kDecMinWg
+// work-groups remain, else 1.  (The FFN projection has enough work-groups with
+// one column block per wave, and measured slower with more.)
+constexpr int kDecMinWg = 192;
+static int dec_ncb(int nrb, int groups, int chunks) {
+  if (nrb > 2) return 1;
+  for (int c : {2})
+    if (chunks % c == 0 && groups * (chunks / c) >= kDecMinWg) return c;
+  return 1;
+}
+
+// nmask_decode instantiation for nrb row blocks and ncb column blocks per wave
+template <int MODE, int NW>
+static auto nmask_pick(int nrb, int ncb) {
+  if (nrb == 1) return ncb == 4 ? nmask_decode<MODE, 1, 4, NW>
+                      : ncb == 2 ? nmask_decode<MODE, 1, 2, NW>
+                                 : nmask_decode<MODE, 1, 1, NW>;
+  if (nrb == 2) return ncb == 4 ? nmask_decode<MODE, 2, 4, 4>
+                      : ncb == 2 ? nmask_decode<MODE, 2, 2, 4>
+                                 : nmask_decode<MODE, 2, 1, 4>;
+  return nrb == 3 ? nmask_decode<MODE, 3, 1, 4> : nmask_decode<MODE, 4, 1, 4>;
+}
+// waves per work-group of nmask_decode with one row block (each takes d / NW of
+// K).  8 and 16 waves (fewer K steps per wave) measured 1-8 us slower on the
+// 8B attention and FFN decode workloads than 4.
+constexpr int kDecWaves1 = 4;
+static int dec_waves(int nrb) { return nrb == 1 ? kDecWaves1 : 4; }
+
 void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg,
                        const uint16_t* Wu, const uint16_t* Wdp, int B, int d, int F, int n,
                        const uint16_t* residual, uint16_t* H, float* kpart, uint16_t* Y,
@@ -1012,12 +1072,10 @@ void launch_ffn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* W
     WIDE_TRACE("ffn_up_decode", s);
     const int nrb = (B + 15) / 16;
     if (!use_cols(nrb, n * (chunks / 4))) {
-      auto k = nrb == 1   ? nmask_decode<kNmFfn, 1>
-               : nrb == 2 ? nmask_decode<kNmFfn, 2>
-               : nrb == 3 ? nmask_decode<kNmFfn, 3>
-                          : nmask_decode<kNmFfn, 4>;
-      k<<<n * chunks, 256, 0, s>>>(X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, DecCache{nullptr, 0, 0, 0}, 0.f, H,
-                                   nullptr, nullptr, n);
+      const int ncb = 1;
+      nmask_pick<kNmFfn, kDecWaves1>(nrb, ncb)<<<n * (chunks / ncb), 64 * dec_waves(nrb), 0, s>>>(
+          X, Wg, Wu, nullptr, mask, B, d, G, chunks, 0, DecCache{nullptr, 0, 0, 0}, 0.f, H,
+          nullptr, nullptr, n);
     } else {
       auto k = nrb == 2   ? nmask_decode_cols<kNmFfn, 2>
                : nrb == 3 ? nmask_decode_cols<kNmFfn, 3>
@@ -1081,12 +1139,9 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
     WIDE_TRACE("attn_qkv_decode", s);
     const int nrb = (B + 15) / 16;
     if (!use_cols(nrb, n_kv * (chunks / 4))) {
-      auto k = nrb == 1   ? nmask_decode<kNmQkv, 1>
-               : nrb == 2 ? nmask_decode<kNmQkv, 2>
-               : nrb == 3 ? nmask_decode<kNmQkv, 3>
-                          : nmask_decode<kNmQkv, 4>;
-      k<<<n_kv * chunks, 256, 0, s>>>(X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, dc, log2_theta,
-                                      Qd, Kc, Vc, n_kv);
+      const int ncb = dec_ncb(nrb, n_kv, chunks);
+      nmask_pick<kNmQkv, kDecWaves1>(nrb, ncb)<<<n_kv * (chunks / ncb), 64 * dec_waves(nrb), 0, s>>>(
+          X, Wq, Wk, Wv, mask, B, d, kHdD, chunks, r, dc, log2_theta, Qd, Kc, Vc, n_kv);
     } else {
       auto k = nrb == 2   ? nmask_decode_cols<kNmQkv, 2>
                : nrb == 3 ? nmask_decode_cols<kNmQkv, 3>
