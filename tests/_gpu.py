@@ -24,14 +24,34 @@ def u8(a) -> torch.Tensor:
     return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).to(dev())
 
 
+CANARY = 4096          # bf16 elements placed after every output buffer
+CANARY_BITS = 0x5A5A   # their bit pattern (a finite value no kernel writes by chance)
+
+
+def _check_canary(t: torch.Tensor):
+    base = getattr(t, "_wide_canary", None)
+    if base is not None:
+        tail = base[t.numel():].view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.all(tail == CANARY_BITS), "an output buffer was written past its end"
+
+
 def host(t: torch.Tensor) -> np.ndarray:
+    _check_canary(t)
     if t.dtype == torch.bfloat16:
         return bits_to_f32(t.view(torch.int16).cpu().numpy().view(np.uint16))
     return t.cpu().numpy()
 
 
 def nan_bf16(shape) -> torch.Tensor:
-    return torch.full(shape, float("nan"), dtype=torch.bfloat16, device=dev())
+    """An output buffer: NaN everywhere (an element the call leaves unwritten stays
+    NaN), followed by a canary region that host() checks is untouched."""
+    n = int(np.prod(shape))
+    base = torch.empty(n + CANARY, dtype=torch.bfloat16, device=dev())
+    base.view(torch.int16)[n:] = np.int16(np.uint16(CANARY_BITS).view(np.int16))
+    base[:n] = float("nan")
+    y = base[:n].view(shape)
+    y._wide_canary = base
+    return y
 
 
 def rel_err(got, ref) -> float:

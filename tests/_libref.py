@@ -60,8 +60,11 @@ def sdpa(q, k, v, causal):
     return o[0].transpose(0, 1).numpy()                           # [Tq, Hq, hd]
 
 
-def llama_layer(X, W, n_q, n_kv, hd, theta, eps):
-    """Dense transformers LlamaDecoderLayer (float64) with the given weights, causal."""
+def llama_layer(X, W, n_q, n_kv, hd, theta, eps, part="layer"):
+    """Dense transformers LlamaDecoderLayer (float64) with the given weights, causal.
+    part="attn": x + self_attn(input_layernorm(x)) only; part="mlp":
+    x + mlp(post_attention_layernorm(x)) only (each sublayer of the library layer
+    with its residual, on the layer input)."""
     T, d = X.shape
     F = W["W_gate"].shape[0]
     cfg = llama_config(d, F, n_q, n_kv, hd, theta, eps)
@@ -80,6 +83,12 @@ def llama_layer(X, W, n_q, n_kv, hd, theta, eps):
     cos, sin = rot(x, pos)
     mask = torch.full((T, T), float("-inf"), dtype=F64).triu(1)[None, None]
     with torch.no_grad():
+        if part == "attn":
+            a = layer.self_attn(layer.input_layernorm(x), attention_mask=mask,
+                                position_embeddings=(cos, sin))[0]
+            return (x + a)[0].numpy()
+        if part == "mlp":
+            return (x + layer.mlp(layer.post_attention_layernorm(x)))[0].numpy()
         y = layer(x, attention_mask=mask, position_ids=pos, position_embeddings=(cos, sin))
     y = y[0] if isinstance(y, tuple) else y
     return y[0].numpy()

@@ -35,6 +35,32 @@ def test_pack_kmajor_is_the_blockwise_transpose(n, G, d):
 
 
 @needs_gpu
+def test_tiny_fp32_configuration_raw_input_difference():
+    """The tiny configuration is declared fp32; the library computes on its inputs
+    rounded to bf16.  Parity is judged on the rounded inputs (the oracle in fp64, and
+    in fp32); the difference to the oracle on the raw fp32 inputs is reported and must
+    stay within the bf16 input rounding's own effect (the fp64 oracle on rounded
+    against raw inputs) plus the tolerance."""
+    dev()
+    from synth import normal
+    c = tiny_ffn()
+    raw = {k: normal("tiny_ffn", k, c[k].shape, 1.0 if k == "X" else 0.02, round_bf16=False)
+           for k in ("X", "W_gate", "W_up", "W_down")}
+    assert all(np.array_equal(np.asarray(raw[k], np.float32), np.asarray(raw[k])) for k in raw)
+    got = _gpu_ffn(c)
+    ref64 = ffn_masked(c["X"], c["mask"], c["W_gate"], c["W_up"], c["W_down"])
+    ref32 = ffn_masked(c["X"], c["mask"], c["W_gate"], c["W_up"], c["W_down"], dtype=np.float32)
+    raw64 = ffn_masked(raw["X"], c["mask"], raw["W_gate"], raw["W_up"], raw["W_down"])
+    e64, e32, eraw = rel_err(got, ref64), rel_err(got, ref32), rel_err(got, raw64)
+    e_round = rel_err(ref64, raw64)
+    log(f"tiny fp32 configuration: GPU vs oracle fp64 {e64:.2e}, vs oracle fp32 {e32:.2e}, "
+        f"vs oracle on raw fp32 inputs {eraw:.2e}; oracle rounded vs raw inputs {e_round:.2e}; "
+        f"oracle fp32 vs fp64 {rel_err(ref32, ref64):.2e}")
+    assert e64 <= TOL and e32 <= TOL
+    assert eraw <= e_round + TOL
+
+
+@needs_gpu
 def test_tiny_ffn():
     dev()
     c = tiny_ffn()

@@ -2,8 +2,9 @@
 
 All-ones masks: the layer equals transformers' dense LlamaDecoderLayer in
 float64 (RMSNorm, rotate-half RoPE with theta, GQA, SwiGLU).  All-zero masks:
-y == x exactly, because both sublayers add an exact zero.  RMSNorm against
-torch.nn.functional.rms_norm.
+y == x exactly, because both sublayers add an exact zero.  Mixed masks (one
+sublayer all-ones, the other all-zero): y equals the library's other sublayer
+with its residual alone.  RMSNorm against torch.nn.functional.rms_norm.
 """
 import numpy as np
 import pytest
@@ -63,3 +64,20 @@ def test_rows_option_selects_rows():
     full = layer_masked(X, am, fm, W, **kw)
     part = layer_masked(X, am, fm, W, rows=rows, **kw)
     np.testing.assert_allclose(part, full[rows], rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("which", ["attn", "mlp"])
+def test_mixed_masks_leave_one_library_sublayer(which):
+    """Attention all-ones with the FFN all-zero gives x + attention(RMSNorm(x)); the
+    FFN all-ones with attention all-zero gives x + MLP(RMSNorm(x)) (transformers'
+    LlamaDecoderLayer pieces, float64)."""
+    T, d, F, n_q, n_kv, hd, n_ffn = 17, 32, 48, 4, 2, 8, 6
+    W = _weights(d, F, n_q, n_kv, hd, 8)
+    X = np.random.default_rng(9).standard_normal((T, d))
+    ones_a = which == "attn"
+    am = np.full((T, n_kv), 1 if ones_a else 0, np.uint8)
+    fm = np.full((T, n_ffn), 0 if ones_a else 1, np.uint8)
+    y = layer_masked(X, am, fm, W, n_q=n_q, n_kv=n_kv, head_dim=hd, n_ffn=n_ffn,
+                     rope_theta=500000.0, eps=1e-5)
+    ref = llama_layer(X, W, n_q, n_kv, hd, 500000.0, 1e-5, part=which)
+    np.testing.assert_allclose(y, ref, rtol=0, atol=50.0 * T * 2.0 ** -23)
