@@ -294,22 +294,71 @@ __global__ void __launch_bounds__(64 * kCoreWaves, kCoreWgPerCU)
   __shared__ __attribute__((aligned(16))) uint16_t sV[2 * kStageV];
   __shared__ int sRedo;  // some wave's rows outgrew their reference max
 
-  // work-group -> (group, bin j of B = nbins, chunk of 4 query heads).  Query
-  // tile qt of a group takes qt / 2 + 1 key steps.  The group's tiles, heaviest
-  // first, are dealt to its B bins in snake order: bin j takes the tiles of rank
-  // j, 2B-1-j, 2B+j, 4B-1-j, ..., so the bins of a group do nearly the same
-  // number of key steps whatever the group's count (with B = half the tiles this
-  // is the heavy + light pairing; a count a little over 2B tiles adds at most one
-  // light tile to a bin instead of a second round of work-groups).  With one
-  // group per XCD, its K and V stay in that XCD's L2.
-  const int g = blockIdx.x % n_kv;
-  const int rest = blockIdx.x / n_kv;
-  const int j = rest % nbins;
-  const int hc = rest / nbins;
+  // work-group -> (group, bin j of the group's B bins, chunk of 4 query heads).
+  // Query tile qt of a group takes qt / 2 + 1 key steps, so a group's work grows
+  // with the square of its count.  The grid's nbins * n_kv bin slots are shared
+  // out among the groups by that work (each group keeps at least one; near-equal
+  // counts get an equal share, nbins each), and the groups' slots are laid out
+  // XCD by XCD (slot p on XCD p / (slots / 8)), so a group's K and V stay in one
+  // or few XCDs' L2.  The group's tiles, heaviest first, are dealt to its B bins
+  // in snake order: bin j takes the tiles of rank j, 2B-1-j, 2B+j, 4B-1-j, ...,
+  // so the bins of a group do nearly the same number of key steps (with B = half
+  // the tiles this is the heavy + light pairing).
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int sSlot[3];  // group, bin, bins of the group (-1: no work)
+  const int nslots = nbins * n_kv;
+  const int hc = blockIdx.x / nslots;
+  if (wave == 0) {
+    const int w = blockIdx.x % nslots;
+    const int p = (nslots & 7) == 0 ? (w & 7) * (nslots >> 3) + (w >> 3) : w;
+    // per-group work (key steps, about qtiles^2 / 4) and its total
+    long long tot = 0, wmax = 0;
+    for (int g0 = 0; g0 < n_kv; g0 += 64) {
+      const int g = g0 + lane;
+      const long long q = g < n_kv ? (gcount[g] + kBQ - 1) / kBQ : 0;
+      const long long wg = q * (q + 3) / 4;
+      long long sum = wg, mx = wg;
+      for (int off = 32; off >= 1; off >>= 1) {
+        sum += __shfl_xor(sum, off);
+        mx = max(mx, (long long)__shfl_xor(mx, off));
+      }
+      tot += sum;
+      wmax = max(wmax, mx);
+    }
+    const bool equal = 4 * wmax * n_kv <= 5 * tot;  // every group within 25 % of the mean
+    if (lane == 0) sSlot[0] = -1;
+    int base = 0;
+    for (int g0 = 0; g0 < n_kv && tot > 0; g0 += 64) {
+      const int g = g0 + lane;
+      int b = 0;
+      if (g < n_kv) {
+        const int q = (gcount[g] + kBQ - 1) / kBQ;
+        const long long wg = (long long)q * (q + 3) / 4;
+        b = equal ? nbins
+                  : (q > 0 ? 1 + (int)((long long)(nslots - n_kv) * wg / tot) : 0);
+        b = min(b, q);  // a bin takes at least one tile
+      }
+      int incl = b;  // inclusive prefix over the lanes
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      const int start = base + incl - b;
+      if (b > 0 && p >= start && p < start + b) {
+        sSlot[0] = g;
+        sSlot[1] = p - start;
+        sSlot[2] = b;
+      }
+      base += __shfl(incl, 63);
+    }
+  }
+  __syncthreads();
+  const int g = sSlot[0];
+  if (g < 0) return;  // l=0: a slot no group's tiles need
+  const int j = sSlot[1];
+  nbins = sSlot[2];
   const int cnt = gcount[g];
   const int qtiles = (cnt + kBQ - 1) / kBQ;
-  if (j >= qtiles) return;  // l=0: past the group's kept tokens
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hw = wave;  // head of the chunk
   const bool head_ok = hc * 4 + hw < r;  // waves past the group's heads only help load
   const int h = g * r + min(hc * 4 + hw, r - 1);
