@@ -208,6 +208,8 @@ WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restric
 }
 
 
+constexpr int kCoreCUs = 256;   // compute units of the chip
+
 // The QKV projection.  A group's tiles are units of 256 kept tokens x 256
 // columns (two heads), U = ceil(count / 256) * ntn of them, dealt in row-major
 // order; P = compute units per group.  The units past the last full round of P,
@@ -219,7 +221,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     attn_qkv_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
                      const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
                      const int32_t* __restrict__ gcount, const int32_t* __restrict__ gperm, int T,
-                     int d, int n_kv, int r, int P, int vtp, float log2_theta,
+                     int d, int n_kv, int r, int P, bool lanes, int vtp, float log2_theta,
                      uint16_t* __restrict__ Qc, uint16_t* __restrict__ Kc,
                      uint16_t* __restrict__ Vt) {
   using Big = TileCfg<256, 256>;
@@ -228,15 +230,65 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kBig > kHalf ? kBig : kHalf];
   __shared__ int sTok[256];
   const int ntn = (r + 1) / 2 + 1;
-  int g, w;
-  if ((n_kv & 7) == 0) {  // groups g = x, x + 8, ... on XCD x
-    const int per = n_kv >> 3;
-    g = (blockIdx.x & 7) + 8 * ((blockIdx.x >> 3) % per);
-    w = (blockIdx.x >> 3) / per;
-  } else {
-    g = blockIdx.x % n_kv;
-    w = blockIdx.x / n_kv;
+  // Compute-unit lanes: lane l = 32 x + c is CU slot c of XCD x; work-group b runs
+  // in lane 32 (b mod 8) + (b / 8) mod 32, round (b / 8) / 32.  The 256 lanes are
+  // shared out among the groups by their units (each group with units keeps at
+  // least one; near-equal unit counts get P = 256 / n_kv lanes each), as
+  // contiguous lane ranges, so a group's weights and rows stay in one or few XCDs'
+  // L2.  Work-group (lane, round) of group g takes its sequence index w = round *
+  // P_g + (lane - first lane of g).
+  __shared__ int sLane[3];  // group, its lanes P, the sequence index (-1: no group)
+  if (!lanes) {  // many groups: group b mod n_kv, P lanes each
+    if (threadIdx.x == 0) {
+      sLane[0] = blockIdx.x % n_kv;
+      sLane[1] = P;
+      sLane[2] = blockIdx.x / n_kv;
+    }
+  } else if (threadIdx.x < 64) {
+    const int lane = threadIdx.x;
+    const int b = blockIdx.x, s = b >> 3;
+    const int ln = 32 * (b & 7) + (s & 31), round = s >> 5;
+    int tot = 0, umax = 0;
+    for (int g0 = 0; g0 < n_kv; g0 += 64) {
+      const int g = g0 + lane;
+      const int u = g < n_kv ? ntn * ((gcount[g] + 255) / 256) : 0;
+      int sum = u, mx = u;
+      for (int off = 32; off >= 1; off >>= 1) {
+        sum += __shfl_xor(sum, off);
+        mx = max(mx, __shfl_xor(mx, off));
+      }
+      tot += sum;
+      umax = max(umax, mx);
+    }
+    const bool equal = 4 * umax * n_kv <= 5 * tot;  // every group within 25 % of the mean
+    if (lane == 0) sLane[0] = -1;
+    int base = 0;
+    for (int g0 = 0; g0 < n_kv && tot > 0; g0 += 64) {
+      const int g = g0 + lane;
+      int pl = 0;
+      if (g < n_kv) {
+        const int u = ntn * ((gcount[g] + 255) / 256);
+        pl = equal ? P : (u > 0 ? 1 + (int)((long long)(kCoreCUs - n_kv) * u / tot) : 0);
+      }
+      int incl = pl;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int v = __shfl_up(incl, off);
+        if (lane >= off) incl += v;
+      }
+      const int start = base + incl - pl;
+      if (pl > 0 && ln >= start && ln < start + pl) {
+        sLane[0] = g;
+        sLane[1] = pl;
+        sLane[2] = round * pl + (ln - start);
+      }
+      base += __shfl(incl, 63);
+    }
   }
+  __syncthreads();
+  const int g = sLane[0];
+  if (g < 0) return;  // l=0: a lane no group needs
+  P = sLane[1];
+  const int w = sLane[2];
   const int cnt = gcount[g];
   const int U = ntn * ((cnt + 255) / 256);
   int rem = U % P;
@@ -267,7 +319,6 @@ constexpr int kBQ = 32;        // queries per tile: one wave of 32 per head
 constexpr int kBKey = 64;  // keys per step
 constexpr int kCoreWaves = 4;  // one per query head of a 4-head chunk
 constexpr int kCoreWgPerCU = 2;  // resident work-groups per CU (LDS 64 KB, <= 256 VGPRs each)
-constexpr int kCoreCUs = 256;   // compute units of the chip
 // One LDS stage: K block [64 keys][128 hd] (16-byte chunk c of key row k at slot
 // c ^ (k & 15)) and V^T block [128 hd][64 keys] (chunk c of row j at slot
 // c ^ ((j >> 1) & 7)); both 16 KB, filled by buffer->LDS loads.
@@ -561,10 +612,18 @@ void launch_attn_prefill(const uint16_t* X, const uint16_t* Wq, const uint16_t* 
   {
     // compute units per group; a group has at most mtiles * ntn units and P / 2
     // extra work-groups for halves
+    // Up to 64 groups: lanes shared out by units; the rounds of the 256 lanes
+    // cover the units of every group at any counts (a group's lanes are at least
+    // its share of 256 - n_kv, rounded down, plus one; its halves add under one
+    // round).  More groups: P lanes per group, one after another.
     const int P = std::max(1, kCoreCUs / n_kv);
+    const bool lanes = n_kv <= 64;
+    const int units = n_kv * mtiles * ntn;
+    const int grid = lanes ? kCoreCUs * ((units + kCoreCUs - n_kv - 1) / (kCoreCUs - n_kv) + 2)
+                           : n_kv * (mtiles * ntn + P / 2);
     WIDE_TRACE("attn_qkv_prefill", s);
-    attn_qkv_prefill<<<n_kv * (mtiles * ntn + P / 2), kGemmThreads, 0, s>>>(
-        X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv, r, P, vtp, log2_theta, Qc, Kc, Vt);
+    attn_qkv_prefill<<<grid, kGemmThreads, 0, s>>>(X, Wq, Wk, Wv, rv.count, rv.perm, T, d, n_kv,
+                                                   r, P, lanes, vtp, log2_theta, Qc, Kc, Vt);
   }
   // bins per group: half the most tiles a group can have, but no more than fill
   // the CUs once (256 CUs, kCoreWgPerCU work-groups each)
