@@ -35,6 +35,7 @@ PEAK_BF16_TFLOPS = 2516.6   # MI355X dense bf16 MFMA: 256 CU x 2.4 GHz x 4096 FL
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 METRIC = "masked tokens/s + % of MFMA (prefill) / HBM (decode) roofline at 50% sparsity"
 HD = 128
+ORACLE_DTYPE = np.float32   # the CPU baseline times the oracle in fp32 (its parity runs use fp64)
 
 
 def log(msg):
@@ -128,7 +129,111 @@ class LayerPrefill:
         t0 = time.perf_counter()
         layer_masked(c["X"][:S], c["attn_mask"][:S], c["ffn_mask"][:S], W, n_q=m["n_q"],
                      n_kv=m["n_kv"], head_dim=HD, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"],
-                     eps=m["eps"])
+                     eps=m["eps"], dtype=ORACLE_DTYPE)
+        return time.perf_counter() - t0
+
+
+class LayerPrefillRouted(LayerPrefill):
+    """LayerPrefill with the masks chosen on the GPU inside the step: the layer input's
+    two linear routers (R_attn [8, d], R_ffn [112, d], the input generator's router
+    weights rounded to bf16) keep 4 of 8 head groups and 56 of 112 FFN groups, and
+    their packed words go straight to the mask reorders (wide_layer_masked_routed)."""
+
+    def __init__(self, T=8192, keep=0.5, kind="router", ffn_group=128, attn_keep=None):
+        super().__init__(T, keep, "router", ffn_group, attn_keep)
+        from synth import bf16_round, normal
+        m, c = self.m, self.c
+        cfg = f"layer_8b_pre_router_{int(round(keep * 100))}"
+        # the generator's routers: logits x @ R with R [d, n]; the GPU takes R^T [n, d]
+        self.R_attn = bf16_round(normal(cfg, "attn_mask.R", (m["d"], m["n_kv"]), 1.0 / 64,
+                                        round_bf16=False).T)
+        self.R_ffn = bf16_round(normal(cfg, "ffn_mask.R", (m["d"], m["n_ffn"]), 1.0 / 64,
+                                       round_bf16=False).T)
+        self.k_attn = int(round((attn_keep if attn_keep is not None else keep) * m["n_kv"]))
+        self.k_ffn = int(round(keep * m["n_ffn"]))
+        self.name = self.name.replace("layer_prefill_8b", "layer_prefill_8b_routed", 1)
+        self.config.update(workload=self.name, masks="GPU router top-k (in the step)")
+
+    def upload(self, torch, wide, bf16, u8):
+        super().upload(torch, wide, bf16, u8)
+        m = self.m
+        self.Ra, self.Rf = wide.pack_router(bf16(self.R_attn)), wide.pack_router(bf16(self.R_ffn))
+        # mask outputs: one pair for the masked steps, one for the all-ones steps
+        self.masks_out = [(torch.empty((self.T, m["n_kv"]), dtype=torch.uint8, device="cuda"),
+                           torch.empty((self.T, m["n_ffn"]), dtype=torch.uint8, device="cuda"))
+                          for _ in range(2)]
+        self.am, self.fm = self.masks_out[0]
+
+    def step(self, ones=False):
+        m = self.m
+        ka, kf = (m["n_kv"], m["n_ffn"]) if ones else (self.k_attn, self.k_ffn)
+        am, fm = self.masks_out[1 if ones else 0]
+        self.wide.layer_masked_routed(self.X, self.Ra, ka, self.Rf, kf, self.W, n_q=m["n_q"],
+                                      n_kv=m["n_kv"], n_ffn=m["n_ffn"], head_dim=HD,
+                                      rope_theta=m["rope_theta"], eps=m["eps"], out=self.Y,
+                                      attn_mask=am, ffn_mask=fm, workspace=self.ws)
+
+    def work(self, ones=False):
+        # counted from the masks the GPU routers chose (read back after the run)
+        if not ones and self.am is not None:
+            self.c = dict(self.c, attn_mask=self.am.cpu().numpy(), ffn_mask=self.fm.cpu().numpy())
+            self.config.update(measured_keep(self.c))
+        return super().work(ones)
+
+
+class LayerDecodeMaskedCache:
+    """Llama-3.1-8B-shaped layer decode over masked caches: batch 32 at position 8192,
+    each (sequence, group) cache holding only the earlier tokens that kept the group
+    (binomial(8192, 1/2) entries at keep 4 of 8); wide_layer_decode_masked_cache.
+    All-ones comparison: every group kept, every cache full."""
+
+    def __init__(self, B=32, pos=8192, keep=0.5, kind="router", ffn_group=128, attn_keep=None):
+        self.inner = LayerDecode(B, pos, keep, kind, ffn_group, attn_keep)
+        self.c, self.m, self.T, self.pos = self.inner.c, self.inner.m, B, pos
+        rng = np.random.default_rng(8193)
+        self.lens = rng.binomial(pos, 0.5, size=(B, self.m["n_kv"])).astype(np.int32)
+        self.name = self.inner.name.replace("layer_decode_8b", "layer_decode_masked_cache_8b", 1)
+        self.config = dict(self.inner.config, workload=self.name, position=pos,
+                           kv_cap=pos + 1, mean_cache_len=round(float(self.lens.mean()), 1))
+        self.config.pop("kv_len", None)
+        self.bound = "hbm"
+
+    def upload(self, torch, wide, bf16, u8):
+        self.inner.upload(torch, wide, bf16, u8)
+        self.L = torch.from_numpy(self.lens).cuda()
+        self.full = torch.full_like(self.L, self.pos)
+        self.wide = wide
+
+    def step(self, ones=False):
+        inn, m = self.inner, self.m
+        S = inn.sets[inn.i % len(inn.sets)]
+        inn.i += 1
+        am, fm = inn.ones if ones else inn.masks
+        self.wide.layer_decode_masked_cache(inn.X, am, fm, S, n_q=m["n_q"], n_kv=m["n_kv"],
+                                            K_cache=S["K_cache"], V_cache=S["V_cache"],
+                                            kv_len=self.full if ones else self.L, pos=self.pos,
+                                            head_dim=HD, rope_theta=m["rope_theta"],
+                                            eps=m["eps"], out=inn.Y, workspace=inn.ws)
+
+    def work(self, ones=False):
+        w = self.inner.work(ones)
+        m = self.m
+        am = np.ones_like(self.c["attn_mask"]) if ones else (self.c["attn_mask"] != 0)
+        lens = np.full_like(self.lens, self.pos) if ones else self.lens
+        r = m["n_q"] // m["n_kv"]
+        w["attn_core_decode"] = (float(((lens + 1) * am).sum()) * 2 * HD * 2
+                                 + float(am.sum()) * r * HD * 2)
+        return w
+
+    def oracle_sample(self, S):
+        from oracle import layer_masked
+        c, m = self.c, self.m
+        W = {k: c[k] for k in ("rms1", "rms2", "Wq", "Wk", "Wv", "Wo", "W_gate", "W_up", "W_down")}
+        t0 = time.perf_counter()
+        layer_masked(c["X"][:S], c["attn_mask"][:S], c["ffn_mask"][:S], W, n_q=m["n_q"],
+                     n_kv=m["n_kv"], head_dim=HD, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"],
+                     eps=m["eps"], decode=True, K_cache=c["K_cache"][:S], V_cache=c["V_cache"][:S],
+                     kv_len=self.lens[:S], pos=self.pos, dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -170,7 +275,8 @@ class FfnPrefill:
         from oracle import ffn_masked
         c = self.c
         t0 = time.perf_counter()
-        ffn_masked(c["X"][:S], c["mask"][:S], c["W_gate"], c["W_up"], c["W_down"])
+        ffn_masked(c["X"][:S], c["mask"][:S], c["W_gate"], c["W_up"], c["W_down"],
+                   dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -218,7 +324,7 @@ class AttnPrefill:
         c, m = self.c, self.m
         t0 = time.perf_counter()
         attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
-                    n_kv=m["n_kv"], head_dim=HD)
+                    n_kv=m["n_kv"], head_dim=HD, dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -283,7 +389,8 @@ class FfnDecode:
         from oracle import ffn_masked
         c = self.c
         t0 = time.perf_counter()
-        ffn_masked(c["X"][:S], c["mask"][:S], c["W_gate"], c["W_up"], c["W_down"])
+        ffn_masked(c["X"][:S], c["mask"][:S], c["W_gate"], c["W_up"], c["W_down"],
+                   dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -349,7 +456,7 @@ class AttnDecode:
         t0 = time.perf_counter()
         attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
                     n_kv=m["n_kv"], head_dim=HD, decode=True, K_cache=c["K_cache"][:S],
-                    V_cache=c["V_cache"][:S], kv_len=self.L)
+                    V_cache=c["V_cache"][:S], kv_len=self.L, dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -417,7 +524,8 @@ class AttnDecodeMaskedCache:
         t0 = time.perf_counter()
         attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
                     n_kv=m["n_kv"], head_dim=HD, decode=True, K_cache=c["K_cache"][:S],
-                    V_cache=c["V_cache"][:S], kv_len=self.lens[:S], pos=self.pos)
+                    V_cache=c["V_cache"][:S], kv_len=self.lens[:S], pos=self.pos,
+                    dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -476,7 +584,7 @@ class AttnDecodePaged(AttnDecodeMaskedCache):
                                         self.table[:S], self.lens[:S])
         attn_masked(c["X"][:S], c["mask"][:S], c["Wq"], c["Wk"], c["Wv"], c["Wo"], n_q=m["n_q"],
                     n_kv=m["n_kv"], head_dim=HD, decode=True, K_cache=Kc, V_cache=Vc,
-                    kv_len=L, pos=self.pos)
+                    kv_len=L, pos=self.pos, dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -546,7 +654,7 @@ class LayerDecode:
         layer_masked(c["X"][:S], c["attn_mask"][:S], c["ffn_mask"][:S], W, n_q=m["n_q"],
                      n_kv=m["n_kv"], head_dim=HD, n_ffn=m["n_ffn"], rope_theta=m["rope_theta"],
                      eps=m["eps"], decode=True, K_cache=c["K_cache"][:S], V_cache=c["V_cache"][:S],
-                     kv_len=self.L)
+                     kv_len=self.L, dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -581,7 +689,7 @@ class RouterPrefill:
     def oracle_sample(self, S):
         from oracle import router_topk
         t0 = time.perf_counter()
-        router_topk(self.X[:S], self.R, self.k)
+        router_topk(self.X[:S], self.R, self.k, dtype=ORACLE_DTYPE)
         return time.perf_counter() - t0
 
 
@@ -592,7 +700,9 @@ WORKLOADS = {"layer_prefill_8b": LayerPrefill, "ffn_prefill_3b": FfnPrefill,
              "ffn_decode_8b_B64": lambda: FfnDecode(64), "router_prefill_8b": RouterPrefill,
              "attn_decode_masked_cache_8b": AttnDecodeMaskedCache,
              "attn_decode_paged_8b_p16": lambda: AttnDecodePaged(page_size=16),
-             "attn_decode_paged_8b_p128": lambda: AttnDecodePaged(page_size=128)}
+             "attn_decode_paged_8b_p128": lambda: AttnDecodePaged(page_size=128),
+             "layer_prefill_8b_routed": LayerPrefillRouted,
+             "layer_decode_masked_cache_8b": LayerDecodeMaskedCache}
 
 
 # ------------------------------------------------------------- measurement
@@ -664,6 +774,43 @@ def gemm_ceiling(torch):
     return out
 
 
+def cpu_info():
+    """CPU model (from /proc/cpuinfo) and the BLAS NumPy uses (threadpoolctl)."""
+    model, blas = None, None
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:  # pragma: no cover
+        pass
+    try:
+        from threadpoolctl import threadpool_info
+        for p in threadpool_info():
+            if p.get("user_api") == "blas":
+                blas = f"{p.get('internal_api')} {p.get('version')}"
+                break
+    except Exception:  # pragma: no cover
+        pass
+    return model, blas
+
+
+def c1_single_thread():
+    """The oracle (fp32) on the tiny FFN configuration (64 tokens, d 256, d_ff 1024 in 16
+    groups), one BLAS thread: tokens/s (median of 5)."""
+    from threadpoolctl import threadpool_limits
+    from oracle import ffn_masked
+    from synth.workloads import tiny_ffn
+    c = tiny_ffn()
+    runs = []
+    with threadpool_limits(1, "blas"):
+        for _ in range(6):
+            t0 = time.perf_counter()
+            ffn_masked(c["X"], c["mask"], c["W_gate"], c["W_up"], c["W_down"], dtype=ORACLE_DTYPE)
+            runs.append(time.perf_counter() - t0)
+    return round(c["X"].shape[0] / float(np.median(runs[1:])), 1)
+
+
 def blas_threads():
     try:
         from threadpoolctl import threadpool_info
@@ -709,7 +856,15 @@ def main():
 
     import torch
     import sparse_wide_mask_amd as wide
-    from tests._gpu import bf16, u8
+    from synth import bf16_bits
+
+    def bf16(a):
+        """float32 array of bf16-exact values -> bf16 device tensor with the same bits"""
+        bits = bf16_bits(np.asarray(a, np.float32))
+        return torch.from_numpy(bits.view(np.int16)).cuda().view(torch.bfloat16)
+
+    def u8(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.uint8)).cuda()
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
@@ -821,13 +976,17 @@ def main():
         S = args.oracle_tokens or W.T
         log(f"timing the CPU oracle on {S} tokens")
         secs = W.oracle_sample(S)
+        model, blas = cpu_info()
         result["cpu_baseline"] = {
             "value": round(S / secs, 2),
             "unit": "tokens/s",
             "cores": blas_threads() or len(os.sched_getaffinity(0)),
             "kind": "oracle",
-            "sample": f"first {S} of {W.T} tokens of the same inputs, dense fp64 NumPy oracle "
+            "sample": f"first {S} of {W.T} tokens of the same inputs, dense fp32 NumPy oracle "
                       f"({secs:.1f} s)",
+            "cpu_model": model,
+            "blas": blas,
+            "tiny_ffn_single_thread_tokens_per_s": c1_single_thread(),
         }
     print(json.dumps(result), flush=True)
 
