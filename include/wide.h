@@ -78,6 +78,8 @@ int wide_version(void);
  * packed      [T, ceil(n_groups/64)] uint64    (output)
  * group_count [n_groups] int32;  group_perm, group_rank [n_groups, T] int32
  * tile_count  [ceil(T/tile_m)] int32;  tile_groups [ceil(T/tile_m), n_groups] int32
+ *             (both NULL: no tile unions; the grouping and the packing then take one
+ *             launch instead of two; one of them NULL: WIDE_EINVAL)
  * 1 <= tile_m <= 1024.  Results are bit-exact and deterministic.
  */
 int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m,

@@ -160,8 +160,10 @@ def trace_collect() -> dict:
 
 # ------------------------------------------------------------------ reorder
 
-def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None) -> dict:
-    """wide_mask_reorder on a uint8 [T, n] device mask; returns the six outputs."""
+def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None,
+                 unions: bool = True) -> dict:
+    """wide_mask_reorder on a uint8 [T, n] device mask; returns the six outputs
+    (four without tile unions: unions=False passes null tile_count / tile_groups)."""
     _dev(mask, torch.uint8, "mask")
     T, n = mask.shape
     dev = mask.device
@@ -173,13 +175,15 @@ def mask_reorder(mask: torch.Tensor, tile_m: int, out: dict | None = None) -> di
             group_count=torch.empty(n, dtype=torch.int32, device=dev),
             group_perm=torch.empty((n, T), dtype=torch.int32, device=dev),
             group_rank=torch.empty((n, T), dtype=torch.int32, device=dev),
-            tile_count=torch.empty(nt, dtype=torch.int32, device=dev),
-            tile_groups=torch.empty((nt, n), dtype=torch.int32, device=dev),
         )
+        if unions:
+            out["tile_count"] = torch.empty(nt, dtype=torch.int32, device=dev)
+            out["tile_groups"] = torch.empty((nt, n), dtype=torch.int32, device=dev)
+    tc = _ptr(out["tile_count"]) if unions else None
+    tg = _ptr(out["tile_groups"]) if unions else None
     st = lib().wide_mask_reorder(_ptr(mask), T, n, tile_m, _ptr(out["packed"]),
                                  _ptr(out["group_count"]), _ptr(out["group_perm"]),
-                                 _ptr(out["group_rank"]), _ptr(out["tile_count"]),
-                                 _ptr(out["tile_groups"]), _stream())
+                                 _ptr(out["group_rank"]), tc, tg, _stream())
     _check("wide_mask_reorder", st)
     return out
 

@@ -13,6 +13,7 @@ namespace {
 using namespace wide;
 
 bool aligned16(const void* p) { return p && (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+bool null_or_aligned16(const void* p) { return !p || aligned16(p); }
 
 constexpr size_t kAlign = 256;
 size_t round_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -174,8 +175,11 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
 // pattern, so that row blocks and whole tiles share dropped groups.
 // packed_ready: the reorder's packed words already hold the mask (the router
 // wrote them), so the packing launch is skipped.
-void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
-                  bool packed_ready = false) {
+// The QKV projection and the core read the group partitions (attn_reorder_groups);
+// only the O projection reads the token sort (attn_reorder_sort), which can run
+// later.
+void attn_reorder_groups(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
+                         bool packed_ready) {
   const ReorderView& v = w.rv;
   const bool sort = nkv <= kSortMaxGroups;
   if (packed_ready)
@@ -184,9 +188,19 @@ void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStrea
   else
     launch_reorder(mask, T, nkv, v.tile_m, v.packed, v.count, v.perm, v.rank,
                    sort ? nullptr : v.tile_count, sort ? nullptr : v.tile_groups, s);
-  if (sort)
+}
+
+void attn_reorder_sort(int T, int nkv, const AttnWs& w, hipStream_t s) {
+  const ReorderView& v = w.rv;
+  if (nkv <= kSortMaxGroups)
     launch_token_sort(v.packed, T, nkv, v.tile_m, v.order, v.tile_count, v.tile_groups,
                       v.tile_perm, s);
+}
+
+void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
+                  bool packed_ready = false) {
+  attn_reorder_groups(mask, T, nkv, w, s, packed_ready);
+  attn_reorder_sort(T, nkv, w, s);
 }
 
 void ffn_reorder(const uint8_t* mask, int T, int n, const FfnWs& w, hipStream_t s,
@@ -199,13 +213,14 @@ void ffn_reorder(const uint8_t* mask, int T, int n, const FfnWs& w, hipStream_t 
     run_reorder(mask, T, n, v, s);
 }
 
-// reorder = false: attn_reorder of this call was already enqueued
-void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
-              const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
-              int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
-              const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s,
-              const int32_t* pair_len = nullptr, int pos = -1, bool reorder = true,
-              const PagedKV* paged = nullptr) {
+// reorder = false: attn_reorder of this call was already enqueued.  before_o: an
+// event the O projection waits for (the token sort on another stream), or null.
+int attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
+             const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
+             int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
+             const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s,
+             const int32_t* pair_len = nullptr, int pos = -1, bool reorder = true,
+             const PagedKV* paged = nullptr, hipEvent_t before_o = nullptr) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
@@ -213,11 +228,13 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
                        w.O, s, paged);
     launch_kmask_decode(kUseAttnO, w.O, Wop, mask, T, d, nq * kHeadDim, nkv, residual, w.kpart,
                         Y, s);
-    return;
+    return WIDE_OK;
   }
   if (reorder) attn_reorder(mask, T, nkv, w, s);
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
+  if (before_o && hipStreamWaitEvent(s, before_o, 0) != hipSuccess) return WIDE_EHIP;
   launch_kmask_gemm(kUseAttnO, w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
+  return WIDE_OK;
 }
 
 // -------------------------------------------------------------------- layer
@@ -229,7 +246,7 @@ void attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const 
 // events are shared, so a layer call enqueues under a lock.
 struct SideStream {
   hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, attn_done = nullptr, ffn_done = nullptr;
+  hipEvent_t fork = nullptr, attn_done = nullptr, sort_done = nullptr, ffn_done = nullptr;
   bool tried = false, ok = false;
 };
 constexpr int kMaxDevices = 64;
@@ -247,6 +264,7 @@ SideStream* side_stream() {
     x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
            hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
            hipEventCreateWithFlags(&x.attn_done, hipEventDisableTiming) == hipSuccess &&
+           hipEventCreateWithFlags(&x.sort_done, hipEventDisableTiming) == hipSuccess &&
            hipEventCreateWithFlags(&x.ffn_done, hipEventDisableTiming) == hipSuccess;
   }
   return x.ok ? &x : nullptr;
@@ -296,10 +314,10 @@ int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_ma
               const LayerCache& kv, uint16_t* Y, const LayerWs& w, hipStream_t s,
               bool packed_ready) {
   const int d = cfg->d_model, nkv = cfg->attn.n_kv_heads, n = cfg->n_ffn_groups;
-  auto attention = [&]() {
-    attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode, kv.K,
-             kv.V, kv.kv_len, kv.kv_cap, X, w.h, w.attn, s, kv.pair_len, kv.pos, false,
-             kv.paged);
+  auto attention = [&](hipEvent_t before_o) {
+    return attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode,
+                    kv.K, kv.V, kv.kv_len, kv.kv_cap, X, w.h, w.attn, s, kv.pair_len, kv.pos,
+                    false, kv.paged, before_o);
   };
   auto ffn = [&]() {
     ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, n, mode, w.h,
@@ -310,13 +328,17 @@ int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_ma
     SideStream* side = side_stream();
     if (side && hipEventRecord(side->fork, s) == hipSuccess &&
         hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess) {
-      attn_reorder(attn_mask, T, nkv, w.attn, side->s, packed_ready);
+      // side stream: the attention partitions (read by the QKV projection), the
+      // token sort (read by the O projection), the FFN reorder
+      attn_reorder_groups(attn_mask, T, nkv, w.attn, side->s, packed_ready);
       if (hipEventRecord(side->attn_done, side->s) != hipSuccess) return WIDE_EHIP;
+      attn_reorder_sort(T, nkv, w.attn, side->s);
+      if (hipEventRecord(side->sort_done, side->s) != hipSuccess) return WIDE_EHIP;
       ffn_reorder(ffn_mask, T, n, w.ffn, side->s, packed_ready);
       if (hipEventRecord(side->ffn_done, side->s) != hipSuccess) return WIDE_EHIP;
       launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
       if (hipStreamWaitEvent(s, side->attn_done, 0) != hipSuccess) return WIDE_EHIP;
-      attention();
+      if (attention(side->sort_done) != WIDE_OK) return WIDE_EHIP;
       launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
       if (hipStreamWaitEvent(s, side->ffn_done, 0) != hipSuccess) return WIDE_EHIP;
       ffn();
@@ -327,7 +349,7 @@ int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_ma
     ffn_reorder(ffn_mask, T, n, w.ffn, s, packed_ready);
   }
   launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
-  attention();
+  attention(nullptr);
   launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
   ffn();
   return launch_status();
@@ -392,8 +414,8 @@ int wide_mask_reorder(const uint8_t* mask, int T, int n_groups, int tile_m, uint
   if (n_groups > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
   if (T == 0) return WIDE_OK;
   if (!aligned16(mask) || !aligned16(packed) || !aligned16(group_count) ||
-      !aligned16(group_perm) || !aligned16(group_rank) || !aligned16(tile_count) ||
-      !aligned16(tile_groups))
+      !aligned16(group_perm) || !aligned16(group_rank) || !null_or_aligned16(tile_count) ||
+      !null_or_aligned16(tile_groups) || (tile_count == nullptr) != (tile_groups == nullptr))
     return WIDE_EINVAL;
   (void)hipGetLastError();
   launch_reorder(mask, T, n_groups, tile_m, packed, group_count, group_perm, group_rank,

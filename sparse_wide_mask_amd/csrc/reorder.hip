@@ -2,13 +2,16 @@
 // partition of the tokens into "kept" (a contiguous prefix) and "dropped", plus
 // the per-tile union of kept groups that block-level skipping reads (§2.C, l=0).
 //
-// Two launches, no host synchronisation:
+// No host synchronisation; one or two launches:
 //   1. reorder_pack   : one wave per token row packs its mask bytes into 64-bit
 //                       words by ballot.
 //   2. reorder_groups : one work-group per group (chunks of 64 tokens, a ballot
 //                       per chunk, a scan over the waves, then each lane places its
 //                       token by mbcnt), plus one work-group per token tile for
 //                       the tile's union of kept groups.
+// When no tile unions are asked for, one launch does both: the group work-groups
+// read the mask bytes themselves and further work-groups of the same grid pack the
+// words (which later kernels read).
 #include "wide.h"
 #include "common.h"
 #include "gemm_tile.h"
@@ -23,12 +26,9 @@ constexpr int kPackThreads = 256;
 constexpr int kPackWaves = kPackThreads / kWave;
 constexpr int kPackTok = 8;
 
-__global__ void __launch_bounds__(kPackThreads)
-    reorder_pack(const uint8_t* __restrict__ mask, int T, int n, int nw,
-                 uint64_t* __restrict__ packed) {
-  const int lane = lane_id(), wave = threadIdx.x / kWave;
-  const int t0 = (blockIdx.x * kPackWaves + wave) * kPackTok;
-  if (t0 >= T) return;
+// The kPackTok rows from t0 (one wave).
+WIDE_DEV void pack_rows(const uint8_t* __restrict__ mask, int T, int n, int nw,
+                        uint64_t* __restrict__ packed, int t0, int lane) {
   const rsrc_t mr = make_rsrc(mask, (uint32_t)((size_t)T * n));
   uint32_t v[kPackTok][4];
 #pragma unroll
@@ -47,6 +47,14 @@ __global__ void __launch_bounds__(kPackThreads)
     }
 }
 
+__global__ void __launch_bounds__(kPackThreads)
+    reorder_pack(const uint8_t* __restrict__ mask, int T, int n, int nw,
+                 uint64_t* __restrict__ packed) {
+  const int wave = threadIdx.x / kWave;
+  const int t0 = (blockIdx.x * kPackWaves + wave) * kPackTok;
+  if (t0 < T) pack_rows(mask, T, n, nw, packed, t0, lane_id());
+}
+
 constexpr int kGroupThreads = 1024;
 constexpr int kGroupWaves = kGroupThreads / kWave;
 constexpr int kGroupMaxChunks = WIDE_MAX_TOKENS / kWave;
@@ -59,15 +67,23 @@ constexpr int kGroupMaxChunks = WIDE_MAX_TOKENS / kWave;
 // ballot inside the chunk, so a wave's stores of a chunk are two contiguous runs.
 // Work-groups n..: one per token tile (when tile unions are asked for): the OR of
 // the tile's packed words, compacted into an ascending group list, -1 padded.
+// mask != nullptr (no tile unions then): the group work-groups read the keep bits
+// from the mask bytes, and the work-groups from n on pack the words, kPackTok rows
+// per wave.
 __global__ void __launch_bounds__(kGroupThreads)
-    reorder_groups(const uint64_t* __restrict__ packed, int T, int n, int nw, int tile_m,
-                   int32_t* __restrict__ group_count, int32_t* __restrict__ group_perm,
-                   int32_t* __restrict__ group_rank, int32_t* __restrict__ tile_count,
-                   int32_t* __restrict__ tile_groups) {
+    reorder_groups(const uint8_t* __restrict__ mask, uint64_t* __restrict__ packed, int T, int n,
+                   int nw, int tile_m, int32_t* __restrict__ group_count,
+                   int32_t* __restrict__ group_perm, int32_t* __restrict__ group_rank,
+                   int32_t* __restrict__ tile_count, int32_t* __restrict__ tile_groups) {
   __shared__ int sWave[kGroupWaves];
   __shared__ uint32_t sU[8];
   __shared__ uint64_t sBallot[kGroupMaxChunks];
   const int lane = lane_id(), wave = threadIdx.x / kWave;
+  if (mask && (int)blockIdx.x >= n) {
+    const int t0 = (((int)blockIdx.x - n) * kGroupWaves + wave) * kPackTok;
+    if (t0 < T) pack_rows(mask, T, n, nw, packed, t0, lane);
+    return;
+  }
   if ((int)blockIdx.x >= n) {
     const int tile = blockIdx.x - n;
     if (threadIdx.x < 8) sU[threadIdx.x] = 0u;
@@ -110,19 +126,24 @@ __global__ void __launch_bounds__(kGroupThreads)
   const int nch = (T + kWave - 1) / kWave;
   const int per = (nch + kGroupWaves - 1) / kGroupWaves;
   const int c0 = min(nch, wave * per), c1 = min(nch, c0 + per);
-  const rsrc_t pr = make_rsrc(packed, (uint32_t)((size_t)T * nw * 8));
+  const rsrc_t pr = make_rsrc(packed, mask ? 0u : (uint32_t)((size_t)T * nw * 8));
+  const rsrc_t mr = make_rsrc(mask, mask ? (uint32_t)((size_t)T * n) : 0u);
+  // keep bit of lane's token: bit j of the loaded half word, or the mask byte
+  const int shift = mask ? 0 : (j & 31);
   int mine = 0;
   for (int c = c0; c < c1; c += 8) {
-    uint32_t v[8];  // the 32-bit half of word w that holds bit j
+    uint32_t v[8];  // the 32-bit half of word w that holds bit j, or the mask byte
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
       const int t = (c + u) * kWave + lane;
-      v[u] = __builtin_amdgcn_raw_buffer_load_b32(
-          pr, (c + u < c1 && t < T) ? (uint32_t)((t * nw + w) * 8 + (j >> 5) * 4) : kSkip, 0, 0);
+      const bool in = c + u < c1 && t < T;
+      v[u] = mask ? ldbuf1(mr, in ? (uint32_t)(t * n + g) : kSkip)
+                  : __builtin_amdgcn_raw_buffer_load_b32(
+                        pr, in ? (uint32_t)((t * nw + w) * 8 + (j >> 5) * 4) : kSkip, 0, 0);
     }
 #pragma unroll
     for (int u = 0; u < 8; ++u) {
-      const uint64_t b = ballot((v[u] >> (j & 31)) & 1u);
+      const uint64_t b = ballot(mask ? v[u] != 0u : ((v[u] >> shift) & 1u) != 0u);
       if (c + u < c1) {
         if (lane == 0) sBallot[c + u] = b;
         mine += popc64(b);
@@ -308,15 +329,22 @@ void launch_reorder_packed(const uint64_t* packed, int T, int n, int tile_m,
   const int nw = (n + 63) / 64;
   const int n_tiles = tile_count ? (T + tile_m - 1) / tile_m : 0;
   WIDE_TRACE("reorder_groups", s);
-  reorder_groups<<<n + n_tiles, kGroupThreads, 0, s>>>(packed, T, n, nw, tile_m, group_count,
-                                                        group_perm, group_rank, tile_count,
-                                                        tile_groups);
+  reorder_groups<<<n + n_tiles, kGroupThreads, 0, s>>>(nullptr, const_cast<uint64_t*>(packed), T,
+                                                        n, nw, tile_m, group_count, group_perm,
+                                                        group_rank, tile_count, tile_groups);
 }
 
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
   const int nw = (n + 63) / 64;
+  if (!tile_count) {  // one launch: groups from the mask bytes, packing beside them
+    const int per_block = kGroupWaves * kPackTok;
+    WIDE_TRACE("reorder_groups", s);
+    reorder_groups<<<n + (T + per_block - 1) / per_block, kGroupThreads, 0, s>>>(
+        mask, packed, T, n, nw, tile_m, group_count, group_perm, group_rank, nullptr, nullptr);
+    return;
+  }
   {
     WIDE_TRACE("reorder_pack", s);
     const int per_block = kPackWaves * kPackTok;

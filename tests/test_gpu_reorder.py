@@ -43,6 +43,26 @@ def test_reorder_bit_exact(T, n, tile_m, kind, keep):
 
 
 @needs_gpu
+@pytest.mark.parametrize("T,n,kind", [(1, 1, "bernoulli"), (63, 8, "topk"), (1000, 8, "topk"),
+                                      (4097, 4, "clustered"), (3000, 129, "bernoulli"),
+                                      (8192, 8, "bernoulli"), (65536, 8, "topk")])
+def test_reorder_without_unions_bit_exact(T, n, kind):
+    """Null tile outputs: grouping and packing in one launch, the group work-groups
+    reading the mask bytes; packed words, counts, permutations and ranks bit-exact."""
+    dev()
+    log(f"reorder without unions T={T} n={n} {kind}")
+    m = make_mask(f"reorder_nu_{T}_{n}", T, n, 0.5, kind)
+    m = m * np.random.default_rng(T + 1).integers(1, 256, m.shape).astype(np.uint8)
+    out = wide.mask_reorder(u8(m), 256, unions=False)
+    torch.cuda.synchronize()
+    assert set(out) == {"packed", "group_count", "group_perm", "group_rank"}
+    ref = mask_reorder(m, 256)
+    assert np.array_equal(host(out["packed"]).view(np.uint64), ref["packed"].astype(np.uint64))
+    for k in ("group_count", "group_perm", "group_rank"):
+        assert np.array_equal(host(out[k]), ref[k]), k
+
+
+@needs_gpu
 @pytest.mark.parametrize("T,n", [(8192, 112), (8192, 8), (65536, 8)])
 def test_reorder_full_size(T, n):
     """The layer's mask sizes (8192 tokens x 112 FFN / 8 attention groups), and the
