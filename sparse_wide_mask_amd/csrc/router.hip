@@ -13,15 +13,19 @@
 // L2) are whole cache lines instead of 16 rows x 64 bytes.
 //
 // One work-group = 32 tokens, 8 waves.  The 32-wide K steps are dealt to the
-// waves round-robin, so each wave reads only its share of X and R and keeps
-// several steps of loads in flight (K is short and a step's MFMAs are few: the
-// kernel is bound by load latency, not arithmetic).  Each wave accumulates all
-// the 16-group MFMA column tiles (v_mfma_f32_16x16x32_bf16) of its steps; the
-// eight partial sums are added through LDS in a fixed tree order, so the logits
-// (and therefore the selection) are the same on every run.  Then one wave per
-// token selects: the k-th largest logit by a 32-step bisection over
-// order-preserving integer keys (counts by ballot + popcount), then the ties at
-// that value in group order.
+// waves in pairs (wave w takes steps 2w, 2w + 1, 2w + 16, 2w + 17, ...), so both
+// halves of an X row's 128-byte line are read by one wave one step apart, and
+// each wave reads only its share of X and R.  K is short and a step's MFMAs are
+// few, so the kernel is bound by load latency: a wave keeps two register sets of
+// U steps and issues the loads of one set before the MFMAs of the other (one set
+// when 16 column tiles take most of the registers).  Each
+// wave accumulates all the 16-group MFMA column tiles (v_mfma_f32_16x16x32_bf16)
+// of its steps; the eight partial sums are added through LDS in a fixed tree
+// order, so the logits (and therefore the selection) are the same on every run.
+// Then each wave selects for 4 tokens at once (four independent chains of
+// ballots): the k-th largest logit by a 32-step bisection over order-preserving
+// integer keys (counts by ballot + popcount), then the ties at that value in
+// group order.
 #include "common.h"
 #include "gemm_tile.h"
 #include "internal.h"
@@ -44,13 +48,15 @@ WIDE_DEV uint32_t order_key(float v) {
 }
 
 // NT: 16-group column tiles computed (>= the n_groups / 16 rounded up); U: K steps
-// whose loads are issued together.
+// per register set.
 template <int NT, int U>
 __global__ void __launch_bounds__(kRtThreads)
     router_topk_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Rp, int T,
                        int d, int n, int k, float* __restrict__ logits,
                        uint8_t* __restrict__ mask, uint64_t* __restrict__ packed) {
   constexpr int NG = 16 * NT;
+  constexpr int NWC = (NG + 63) / 64;  // 64-group words of a token's logits
+  constexpr int TPW = kRtTok / kRtWaves;  // tokens per wave in the selection
   // partial sums of waves 4..7 (then 2..3, then 1), and at the end the logits
   __shared__ float sP[4][kRtTok][NG + 1];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -64,14 +70,16 @@ __global__ void __launch_bounds__(kRtThreads)
   f32x4 acc[NT][2];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // this wave's K steps: wave, wave + 8, ...  (d % 64 == 0: d / 32 is even)
-  const int mine = (nsteps - wave + kRtWaves - 1) / kRtWaves;
-  for (int i0 = 0; i0 < mine; i0 += U) {
-    bf16x8 a[U][2], b[U][NT];
+  // this wave's steps, in pairs: i-th step = 2 wave + (i & 1) + 16 (i >> 1)
+  // (d % 64 == 0: d / 32 is even)
+  const int mine = 2 * ((nsteps / 2 - wave + kRtWaves - 1) / kRtWaves);
+  // steps i0 .. i0 + U - 1 of the wave; past `mine` every load reads zeros
+  auto load = [&](int i0, bf16x8 (&a)[U][2], bf16x8 (&b)[U][NT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
-      const bool live = i0 + u < mine;
-      const int step = wave + kRtWaves * (i0 + u);
+      const int i = i0 + u;
+      const bool live = i < mine;
+      const int step = 2 * wave + (i & 1) + 2 * kRtWaves * (i >> 1);
       const int col = step * 32 + koff;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -86,12 +94,31 @@ __global__ void __launch_bounds__(kRtThreads)
         b[u][j] = *reinterpret_cast<const bf16x8*>(&v);
       }
     }
+  };
+  auto mma = [&](const bf16x8 (&a)[U][2], const bf16x8 (&b)[U][NT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
       for (int j = 0; j < NT; ++j)
 #pragma unroll
         for (int rb = 0; rb < 2; ++rb) acc[j][rb] = mfma16(a[u][rb], b[u][j], acc[j][rb]);
+  };
+  if constexpr (NT <= 8) {
+    bf16x8 a0[U][2], b0[U][NT], a1[U][2], b1[U][NT];
+    load(0, a0, b0);
+    for (int i0 = 0; i0 < mine; i0 += 2 * U) {
+      load(i0 + U, a1, b1);
+      mma(a0, b0);
+      if (i0 + U >= mine) break;
+      load(i0 + 2 * U, a0, b0);
+      mma(a1, b1);
+    }
+  } else {  // 16 tiles: the accumulators leave room for one register set
+    for (int i0 = 0; i0 < mine; i0 += U) {
+      bf16x8 a[U][2], b[U][NT];
+      load(i0, a, b);
+      mma(a, b);
+    }
   }
 
   // fixed-order tree over the waves: 4..7 -> 0..3, 2..3 -> 0..1, 1 -> 0
@@ -128,54 +155,69 @@ __global__ void __launch_bounds__(kRtThreads)
   }
   __syncthreads();
 
-  // selection: one wave per token; group g = lane + 64 i
+  // selection: wave w takes tokens w, w + 8, w + 16, w + 24 together; group
+  // g = lane + 64 i
   const int nw = (n + 63) / 64;
-  for (int tt = wave; tt < rows; tt += kRtWaves) {
-    const size_t t = (size_t)(t0 + tt);
-    float v[4];
-    uint32_t key[4];
-    bool valid[4], keep[4];
+  bool valid[NWC];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int g = lane + 64 * i;
-      valid[i] = g < n;
-      v[i] = valid[i] ? sL[tt][g] : 0.f;
-      key[i] = valid[i] ? order_key(v[i]) : 0u;
-      keep[i] = valid[i] && k >= n;
+  for (int i = 0; i < NWC; ++i) valid[i] = lane + 64 * i < n;
+  float v[TPW][NWC];
+  uint32_t key[TPW][NWC];
+  bool keep[TPW][NWC];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) {
+      v[q][i] = valid[i] ? sL[wave + kRtWaves * q][lane + 64 * i] : 0.f;
+      key[q][i] = valid[i] ? order_key(v[q][i]) : 0u;
+      keep[q][i] = valid[i] && k >= n;
     }
-    if (k > 0 && k < n) {
-      // the k-th largest key: the largest value with at least k keys >= it
-      uint32_t kth = 0u;
-      for (int b = 31; b >= 0; --b) {
-        const uint32_t cand = kth | (1u << b);
+  if (k > 0 && k < n) {
+    // the k-th largest key: the largest value with at least k keys >= it
+    uint32_t kth[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) kth[q] = 0u;
+    for (int b = 31; b >= 0; --b) {
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const uint32_t cand = kth[q] | (1u << b);
         int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) cnt += popc64(ballot(valid[i] && key[i] >= cand));
-        if (cnt >= k) kth = cand;
+        for (int i = 0; i < NWC; ++i) cnt += popc64(ballot(valid[i] && key[q][i] >= cand));
+        if (cnt >= k) kth[q] = cand;
       }
+    }
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
       int above = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) above += popc64(ballot(valid[i] && key[i] > kth));
+      for (int i = 0; i < NWC; ++i) above += popc64(ballot(valid[i] && key[q][i] > kth[q]));
       // keys equal to the k-th: the first k - above of them in group order
       const int need = k - above;
       int before = 0;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const bool eq = valid[i] && key[i] == kth;
+      for (int i = 0; i < NWC; ++i) {
+        const bool eq = valid[i] && key[q][i] == kth[q];
         const uint64_t bal = ballot(eq);
         const int rank = before + popc64(bal & ((1ull << lane) - 1ull));
-        keep[i] = (valid[i] && key[i] > kth) || (eq && rank < need);
+        keep[q][i] = (valid[i] && key[q][i] > kth[q]) || (eq && rank < need);
         before += popc64(bal);
       }
     }
+  }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
+  for (int q = 0; q < TPW; ++q) {
+    const int tt = wave + kRtWaves * q;
+    if (tt >= rows) break;
+    const size_t t = (size_t)(t0 + tt);
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) {
       const int g = lane + 64 * i;
-      const uint64_t word = ballot(keep[i]);
+      const uint64_t word = ballot(keep[q][i]);
       if (i < nw && lane == 0 && packed) packed[t * nw + i] = word;
       if (g < n) {
-        mask[t * n + g] = keep[i] ? 1 : 0;
-        if (logits) logits[t * n + g] = v[i];
+        mask[t * n + g] = keep[q][i] ? 1 : 0;
+        if (logits) logits[t * n + g] = v[q][i];
       }
     }
   }
@@ -210,10 +252,10 @@ void launch_router_topk(const uint16_t* X, const uint16_t* R, int T, int d, int 
   WIDE_TRACE("router_topk", s);
   const int ntiles = (n + 15) / 16;
   const dim3 grid((T + kRtTok - 1) / kRtTok);
-  auto kern = ntiles <= 1   ? router_topk_kernel<1, 8>
-              : ntiles <= 2 ? router_topk_kernel<2, 8>
-              : ntiles <= 4 ? router_topk_kernel<4, 6>
-              : ntiles <= 8 ? router_topk_kernel<8, 4>
+  auto kern = ntiles <= 1   ? router_topk_kernel<1, 4>
+              : ntiles <= 2 ? router_topk_kernel<2, 4>
+              : ntiles <= 4 ? router_topk_kernel<4, 4>
+              : ntiles <= 8 ? router_topk_kernel<8, 2>
                             : router_topk_kernel<16, 2>;
   kern<<<grid, kRtThreads, 0, s>>>(X, R, T, d, n, k, logits, mask, packed);
 }
