@@ -712,10 +712,9 @@ int wide_layer_masked_routed(const uint16_t* X, const wide_layer_router* router,
   (void)hipGetLastError();
   // the routers read the layer input; in prefill their packed words go straight
   // to the reorders' buffers
-  launch_router_topk(X, router->R_attn_packed, T, cfg->d_model, nkv, router->k_attn, nullptr,
-                     attn_mask, prefill ? w.attn.rv.packed : nullptr, s);
-  launch_router_topk(X, router->R_ffn_packed, T, cfg->d_model, n, router->k_ffn, nullptr,
-                     ffn_mask, prefill ? w.ffn.rv.packed : nullptr, s);
+  launch_router_topk2(X, T, cfg->d_model, router->R_ffn_packed, n, router->k_ffn, ffn_mask,
+                      prefill ? w.ffn.rv.packed : nullptr, router->R_attn_packed, nkv,
+                      router->k_attn, attn_mask, prefill ? w.attn.rv.packed : nullptr, s);
   return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, s, prefill);
 }
 

@@ -106,6 +106,11 @@ void launch_attn_decode(const uint16_t* X, const uint8_t* mask, const uint16_t* 
 void launch_pack_router(const uint16_t* R, int n, int d, uint16_t* Rp, hipStream_t s);
 void launch_router_topk(const uint16_t* X, const uint16_t* Rp, int T, int d, int n, int k,
                         float* logits, uint8_t* mask, uint64_t* packed, hipStream_t s);
+// Two routers over the same X (router a's column tiles, then router b's): one
+// launch when together they have at most 16 tiles, else two; no logits.
+void launch_router_topk2(const uint16_t* X, int T, int d, const uint16_t* Ra, int na, int ka,
+                         uint8_t* mask_a, uint64_t* packed_a, const uint16_t* Rb, int nb, int kb,
+                         uint8_t* mask_b, uint64_t* packed_b, hipStream_t s);
 
 void launch_rmsnorm(const uint16_t* x, const uint16_t* gamma, int T, int d, float eps, uint16_t* y,
                     hipStream_t s);

@@ -47,13 +47,100 @@ WIDE_DEV uint32_t order_key(float v) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// NT: 16-group column tiles computed (>= the n_groups / 16 rounded up); U: K steps
-// per register set.
+// One router of a launch: its groups are the logit columns col0 .. col0 + n - 1
+// (whole 16-column tiles from col0); outputs as wide_router_topk (logits and
+// packed may be null).
+struct RtSet {
+  int col0, n, k;
+  float* logits;
+  uint8_t* mask;
+  uint64_t* packed;
+};
+
+// Selection of one router for the wave's TPW tokens (w, w + 8, ...) from the
+// logits in LDS: groups g = lane + 64 i, i < the set's word count (uniform).
+template <int NWC, int TPW, int LD>
+WIDE_DEV void rt_select(const float* __restrict__ sL, const RtSet& st, int wave, int lane,
+                        int t0, int rows) {
+  const int n = st.n, k = st.k, nw = (n + 63) / 64;
+  bool valid[NWC];
+#pragma unroll
+  for (int i = 0; i < NWC; ++i) valid[i] = lane + 64 * i < n;
+  float v[TPW][NWC];
+  uint32_t key[TPW][NWC];
+  bool keep[TPW][NWC];
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) {
+      v[q][i] = valid[i] ? sL[(wave + kRtWaves * q) * LD + st.col0 + lane + 64 * i] : 0.f;
+      key[q][i] = valid[i] ? order_key(v[q][i]) : 0u;
+      keep[q][i] = valid[i] && k >= n;
+    }
+  if (k > 0 && k < n) {
+    // the k-th largest key: the largest value with at least k keys >= it
+    uint32_t kth[TPW];
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) kth[q] = 0u;
+    for (int b = 31; b >= 0; --b) {
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const uint32_t cand = kth[q] | (1u << b);
+        int cnt = 0;
+#pragma unroll
+        for (int i = 0; i < NWC; ++i)
+          if (i < nw) cnt += popc64(ballot(valid[i] && key[q][i] >= cand));
+        if (cnt >= k) kth[q] = cand;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      int above = 0;
+#pragma unroll
+      for (int i = 0; i < NWC; ++i)
+        if (i < nw) above += popc64(ballot(valid[i] && key[q][i] > kth[q]));
+      // keys equal to the k-th: the first k - above of them in group order
+      const int need = k - above;
+      int before = 0;
+#pragma unroll
+      for (int i = 0; i < NWC; ++i) {
+        if (i >= nw) break;
+        const bool eq = valid[i] && key[q][i] == kth[q];
+        const uint64_t bal = ballot(eq);
+        const int rank = before + popc64(bal & ((1ull << lane) - 1ull));
+        keep[q][i] = (valid[i] && key[q][i] > kth[q]) || (eq && rank < need);
+        before += popc64(bal);
+      }
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < TPW; ++q) {
+    const int tt = wave + kRtWaves * q;
+    if (tt >= rows) break;
+    const size_t t = (size_t)(t0 + tt);
+#pragma unroll
+    for (int i = 0; i < NWC; ++i) {
+      if (i >= nw) break;
+      const int g = lane + 64 * i;
+      const uint64_t word = ballot(keep[q][i]);
+      if (lane == 0 && st.packed) st.packed[t * nw + i] = word;
+      if (g < n) {
+        st.mask[t * n + g] = keep[q][i] ? 1 : 0;
+        if (st.logits) st.logits[t * n + g] = v[q][i];
+      }
+    }
+  }
+}
+
+// NT: 16-group column tiles computed (>= the tiles of both routers); U: K steps
+// per register set.  Tiles 0 .. ntA - 1 come from RpA (router a, columns from 0),
+// tiles ntA .. ntA + ntB - 1 from RpB (router b, columns from 16 ntA; ntB = 0:
+// one router).
 template <int NT, int U>
 __global__ void __launch_bounds__(kRtThreads)
-    router_topk_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Rp, int T,
-                       int d, int n, int k, float* __restrict__ logits,
-                       uint8_t* __restrict__ mask, uint64_t* __restrict__ packed) {
+    router_topk_kernel(const uint16_t* __restrict__ X, const uint16_t* __restrict__ RpA,
+                       int ntA, const uint16_t* __restrict__ RpB, int ntB, int T, int d,
+                       RtSet sa, RtSet sb) {
   constexpr int NG = 16 * NT;
   constexpr int NWC = (NG + 63) / 64;  // 64-group words of a token's logits
   constexpr int TPW = kRtTok / kRtWaves;  // tokens per wave in the selection
@@ -64,8 +151,9 @@ __global__ void __launch_bounds__(kRtThreads)
   const int rows = min(kRtTok, T - t0);
   const int ch = lane & 15, koff = 8 * (lane >> 4);
   const rsrc_t xr = make_rsrc(X + (size_t)t0 * d, (uint32_t)((size_t)rows * d * 2));
-  const int ntiles = (n + 15) / 16, nsteps = d / 32;
-  const rsrc_t rr = make_rsrc(Rp, (uint32_t)((size_t)ntiles * 16 * d * 2));
+  const int nsteps = d / 32;
+  const rsrc_t ra = make_rsrc(RpA, (uint32_t)((size_t)ntA * 16 * d * 2));
+  const rsrc_t rb2 = make_rsrc(RpB, RpB ? (uint32_t)((size_t)ntB * 16 * d * 2) : 0u);
 
   f32x4 acc[NT][2];
 #pragma unroll
@@ -88,9 +176,12 @@ __global__ void __launch_bounds__(kRtThreads)
       }
 #pragma unroll
       for (int j = 0; j < NT; ++j) {
-        const u32x4 v = ldbuf16(rr, live && j < ntiles
-                                        ? (uint32_t)((((size_t)j * nsteps + step) * 64 + lane) * 16)
-                                        : kSkip);
+        const bool first = j < ntA;
+        const int jt = first ? j : j - ntA;
+        const u32x4 v = ldbuf16(first ? ra : rb2,
+                                live && j < ntA + ntB
+                                    ? (uint32_t)((((size_t)jt * nsteps + step) * 64 + lane) * 16)
+                                    : kSkip);
         b[u][j] = *reinterpret_cast<const bf16x8*>(&v);
       }
     }
@@ -155,72 +246,9 @@ __global__ void __launch_bounds__(kRtThreads)
   }
   __syncthreads();
 
-  // selection: wave w takes tokens w, w + 8, w + 16, w + 24 together; group
-  // g = lane + 64 i
-  const int nw = (n + 63) / 64;
-  bool valid[NWC];
-#pragma unroll
-  for (int i = 0; i < NWC; ++i) valid[i] = lane + 64 * i < n;
-  float v[TPW][NWC];
-  uint32_t key[TPW][NWC];
-  bool keep[TPW][NWC];
-#pragma unroll
-  for (int q = 0; q < TPW; ++q)
-#pragma unroll
-    for (int i = 0; i < NWC; ++i) {
-      v[q][i] = valid[i] ? sL[wave + kRtWaves * q][lane + 64 * i] : 0.f;
-      key[q][i] = valid[i] ? order_key(v[q][i]) : 0u;
-      keep[q][i] = valid[i] && k >= n;
-    }
-  if (k > 0 && k < n) {
-    // the k-th largest key: the largest value with at least k keys >= it
-    uint32_t kth[TPW];
-#pragma unroll
-    for (int q = 0; q < TPW; ++q) kth[q] = 0u;
-    for (int b = 31; b >= 0; --b) {
-#pragma unroll
-      for (int q = 0; q < TPW; ++q) {
-        const uint32_t cand = kth[q] | (1u << b);
-        int cnt = 0;
-#pragma unroll
-        for (int i = 0; i < NWC; ++i) cnt += popc64(ballot(valid[i] && key[q][i] >= cand));
-        if (cnt >= k) kth[q] = cand;
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      int above = 0;
-#pragma unroll
-      for (int i = 0; i < NWC; ++i) above += popc64(ballot(valid[i] && key[q][i] > kth[q]));
-      // keys equal to the k-th: the first k - above of them in group order
-      const int need = k - above;
-      int before = 0;
-#pragma unroll
-      for (int i = 0; i < NWC; ++i) {
-        const bool eq = valid[i] && key[q][i] == kth[q];
-        const uint64_t bal = ballot(eq);
-        const int rank = before + popc64(bal & ((1ull << lane) - 1ull));
-        keep[q][i] = (valid[i] && key[q][i] > kth[q]) || (eq && rank < need);
-        before += popc64(bal);
-      }
-    }
-  }
-#pragma unroll
-  for (int q = 0; q < TPW; ++q) {
-    const int tt = wave + kRtWaves * q;
-    if (tt >= rows) break;
-    const size_t t = (size_t)(t0 + tt);
-#pragma unroll
-    for (int i = 0; i < NWC; ++i) {
-      const int g = lane + 64 * i;
-      const uint64_t word = ballot(keep[q][i]);
-      if (i < nw && lane == 0 && packed) packed[t * nw + i] = word;
-      if (g < n) {
-        mask[t * n + g] = keep[q][i] ? 1 : 0;
-        if (logits) logits[t * n + g] = v[q][i];
-      }
-    }
-  }
+  // selection, router by router
+  rt_select<NWC, TPW, NG + 1>(&sL[0][0], sa, wave, lane, t0, rows);
+  if (ntB > 0) rt_select<NWC, TPW, NG + 1>(&sL[0][0], sb, wave, lane, t0, rows);
 }
 
 // R [n, d] -> fragment order [ceil(n/16)][d/32][64 lanes][8]: lane l of block
@@ -247,17 +275,38 @@ void launch_pack_router(const uint16_t* R, int n, int d, uint16_t* Rp, hipStream
   pack_router_kernel<<<grid, 256, 0, s>>>(R, n, d, Rp);
 }
 
+static auto router_kernel_for(int ntiles) {
+  return ntiles <= 1   ? router_topk_kernel<1, 4>
+         : ntiles <= 2 ? router_topk_kernel<2, 4>
+         : ntiles <= 4 ? router_topk_kernel<4, 4>
+         : ntiles <= 8 ? router_topk_kernel<8, 2>
+                       : router_topk_kernel<16, 2>;
+}
+
 void launch_router_topk(const uint16_t* X, const uint16_t* R, int T, int d, int n, int k,
                         float* logits, uint8_t* mask, uint64_t* packed, hipStream_t s) {
   WIDE_TRACE("router_topk", s);
   const int ntiles = (n + 15) / 16;
   const dim3 grid((T + kRtTok - 1) / kRtTok);
-  auto kern = ntiles <= 1   ? router_topk_kernel<1, 4>
-              : ntiles <= 2 ? router_topk_kernel<2, 4>
-              : ntiles <= 4 ? router_topk_kernel<4, 4>
-              : ntiles <= 8 ? router_topk_kernel<8, 2>
-                            : router_topk_kernel<16, 2>;
-  kern<<<grid, kRtThreads, 0, s>>>(X, R, T, d, n, k, logits, mask, packed);
+  router_kernel_for(ntiles)<<<grid, kRtThreads, 0, s>>>(
+      X, R, ntiles, nullptr, 0, T, d, RtSet{0, n, k, logits, mask, packed},
+      RtSet{0, 0, 0, nullptr, nullptr, nullptr});
+}
+
+void launch_router_topk2(const uint16_t* X, int T, int d, const uint16_t* Ra, int na, int ka,
+                         uint8_t* mask_a, uint64_t* packed_a, const uint16_t* Rb, int nb, int kb,
+                         uint8_t* mask_b, uint64_t* packed_b, hipStream_t s) {
+  const int ta = (na + 15) / 16, tb = (nb + 15) / 16;
+  if (ta + tb > 16) {
+    launch_router_topk(X, Ra, T, d, na, ka, nullptr, mask_a, packed_a, s);
+    launch_router_topk(X, Rb, T, d, nb, kb, nullptr, mask_b, packed_b, s);
+    return;
+  }
+  WIDE_TRACE("router_topk", s);
+  const dim3 grid((T + kRtTok - 1) / kRtTok);
+  router_kernel_for(ta + tb)<<<grid, kRtThreads, 0, s>>>(
+      X, Ra, ta, Rb, tb, T, d, RtSet{0, na, ka, nullptr, mask_a, packed_a},
+      RtSet{16 * ta, nb, kb, nullptr, mask_b, packed_b});
 }
 
 }  // namespace wide
