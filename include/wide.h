@@ -17,9 +17,9 @@
  *     caller, 16-byte aligned.  Calls allocate no device memory; scratch comes
  *     from the caller's workspace (wide_ffn_masked_noalloc: from a fixed array in
  *     the library).  Process-wide state, each item created on first use and kept
- *     until the process ends: per device, the layer call's second stream and its
- *     events (wide_layer_masked) and the scratch address (wide_ffn_masked_noalloc);
- *     the kernel trace while enabled.
+ *     until the process ends: per device, the scratch address
+ *     (wide_ffn_masked_noalloc); the kernel trace while enabled.  Every call runs
+ *     on `stream` alone.
  *   - bf16 tensors are passed as uint16_t bit patterns, row-major, contiguous.
  *   - Masks are uint8 [T, n_groups] row-major; any nonzero byte means "keep".
  *   - `stream` is a hipStream_t (NULL = the null stream).  Calls only enqueue work:
@@ -301,20 +301,9 @@ int wide_attn_decode_masked_paged(const uint16_t* X, const uint8_t* mask, const 
  *   y = h + FFN(w; ffn_mask),  RMSNorm(x) = x / sqrt(mean(x^2) + eps) * gamma.
  * Weights as in the two calls above; rms1, rms2 [d_model] bf16.  Same prefill /
  * decode and cache rules as wide_attn_proj_masked.  With all-zero masks y == x.
- * Streams (prefill): the two mask reorders, which read only the masks, run on a
- * second stream of the current device that the library creates on first use;
- * it is forked from `stream` by an event recorded at the start of the call and
- * joined back by events before the kernels that read its results, so all of
- * the call's work stays ordered after the caller's earlier work on `stream` and
- * before its later work (this is also the fork/join pattern that stream capture
- * accepts).  Calls that enqueue on one device at the same time are serialised
- * by a lock while they enqueue.  If the second stream cannot be created the
- * call runs on `stream` alone.  Limits of the second stream: it is shared by
- * all layer calls on the device, so layer calls on different streams of one
- * device are ordered with each other through it (they stay correct); under
- * stream capture it joins the capture until the captured call's events are
- * waited on.  If an event operation fails after the reorders were enqueued
- * there, the call returns WIDE_EHIP with that work possibly still running.
+ * Prefill runs the first RMSNorm and both mask reorders in one launch (the
+ * reorders read only the masks, so they run beside the norm rows), then the
+ * attention kernels, the second RMSNorm and the FFN kernels, all on `stream`.
  */
 typedef struct {
   const uint16_t* rms1;

@@ -173,54 +173,48 @@ AttnWs carve_attn(Carver& c, int T, int d, const wide_attn_cfg* cfg, int mode, i
 // Prefill: group partitions for the QKV projection and the core; for the O
 // projection with few groups, tiles of tokens sorted by their head-group
 // pattern, so that row blocks and whole tiles share dropped groups.
-// packed_ready: the reorder's packed words already hold the mask (the router
-// wrote them), so the packing launch is skipped.
-// The QKV projection and the core read the group partitions (attn_reorder_groups);
-// only the O projection reads the token sort (attn_reorder_sort), which can run
-// later.
-void attn_reorder_groups(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
-                         bool packed_ready) {
+// The reorder jobs of the attention and FFN masks.  packed_ready: the packed words
+// already hold the mask (the router wrote them) and are the input.  With few
+// groups the attention job also sorts the tokens by pattern (the O projection's
+// tiles and unions).
+MaskJob attn_job(const uint8_t* mask, int T, int nkv, const AttnWs& w, bool packed_ready) {
   const ReorderView& v = w.rv;
   const bool sort = nkv <= kSortMaxGroups;
-  if (packed_ready)
-    launch_reorder_packed(v.packed, T, nkv, v.tile_m, v.count, v.perm, v.rank,
-                          sort ? nullptr : v.tile_count, sort ? nullptr : v.tile_groups, s);
-  else
-    launch_reorder(mask, T, nkv, v.tile_m, v.packed, v.count, v.perm, v.rank,
-                   sort ? nullptr : v.tile_count, sort ? nullptr : v.tile_groups, s);
+  MaskJob j;
+  j.mask = packed_ready ? nullptr : mask;
+  j.packed = v.packed;
+  j.n = nkv, j.nw = (nkv + 63) / 64, j.tile_m = v.tile_m;
+  j.count = v.count, j.perm = v.perm, j.rank = v.rank;
+  j.tile_count = v.tile_count, j.tile_groups = v.tile_groups;
+  j.order = sort ? v.order : nullptr;
+  j.tile_perm = sort ? v.tile_perm : nullptr;
+  return j;
 }
 
-void attn_reorder_sort(int T, int nkv, const AttnWs& w, hipStream_t s) {
+MaskJob ffn_job(const uint8_t* mask, int T, int n, const FfnWs& w, bool packed_ready) {
   const ReorderView& v = w.rv;
-  if (nkv <= kSortMaxGroups)
-    launch_token_sort(v.packed, T, nkv, v.tile_m, v.order, v.tile_count, v.tile_groups,
-                      v.tile_perm, s);
+  MaskJob j;
+  j.mask = packed_ready ? nullptr : mask;
+  j.packed = v.packed;
+  j.n = n, j.nw = (n + 63) / 64, j.tile_m = v.tile_m;
+  j.count = v.count, j.perm = v.perm, j.rank = v.rank;
+  j.tile_count = v.tile_count, j.tile_groups = v.tile_groups;
+  return j;
 }
 
 void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
                   bool packed_ready = false) {
-  attn_reorder_groups(mask, T, nkv, w, s, packed_ready);
-  attn_reorder_sort(T, nkv, w, s);
+  const MaskJob j = attn_job(mask, T, nkv, w, packed_ready);
+  launch_reorder_jobs(T, &j, nullptr, nullptr, s);
 }
 
-void ffn_reorder(const uint8_t* mask, int T, int n, const FfnWs& w, hipStream_t s,
-                 bool packed_ready = false) {
-  const ReorderView& v = w.rv;
-  if (packed_ready)
-    launch_reorder_packed(v.packed, T, n, v.tile_m, v.count, v.perm, v.rank, v.tile_count,
-                          v.tile_groups, s);
-  else
-    run_reorder(mask, T, n, v, s);
-}
-
-// reorder = false: attn_reorder of this call was already enqueued.  before_o: an
-// event the O projection waits for (the token sort on another stream), or null.
+// reorder = false: attn_reorder of this call was already enqueued.
 int attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const uint16_t* Wk,
              const uint16_t* Wv, const uint16_t* Wop, int T, int d, const wide_attn_cfg* cfg,
              int mode, uint16_t* K_cache, uint16_t* V_cache, int kv_len, int kv_cap,
              const uint16_t* residual, uint16_t* Y, const AttnWs& w, hipStream_t s,
              const int32_t* pair_len = nullptr, int pos = -1, bool reorder = true,
-             const PagedKV* paged = nullptr, hipEvent_t before_o = nullptr) {
+             const PagedKV* paged = nullptr) {
   const int nq = cfg->n_q_heads, nkv = cfg->n_kv_heads, r = nq / nkv;
   if (mode == WIDE_DECODE) {
     launch_attn_decode(X, mask, Wq, Wk, Wv, T, d, nkv, r, cfg->rope_theta, K_cache, V_cache, kv_len,
@@ -232,43 +226,13 @@ int attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const u
   }
   if (reorder) attn_reorder(mask, T, nkv, w, s);
   launch_attn_prefill(X, Wq, Wk, Wv, w.rv, T, d, nkv, r, cfg->rope_theta, w.Qc, w.Kc, w.Vt, w.O, s);
-  if (before_o && hipStreamWaitEvent(s, before_o, 0) != hipSuccess) return WIDE_EHIP;
   launch_kmask_gemm(kUseAttnO, w.O, Wop, w.rv, T, d, nq * kHeadDim, nkv, residual, Y, s);
   return WIDE_OK;
 }
 
 // -------------------------------------------------------------------- layer
 
-// A second stream per device for the work of a layer call that reads only the
-// call's inputs (the two mask reorders): it runs beside the first RMSNorm and
-// the attention sublayer, and events join it back to the caller's stream before
-// the kernels that consume it.  Default priority.  Created on first use; the
-// events are shared, so a layer call enqueues under a lock.
-struct SideStream {
-  hipStream_t s = nullptr;
-  hipEvent_t fork = nullptr, attn_done = nullptr, sort_done = nullptr, ffn_done = nullptr;
-  bool tried = false, ok = false;
-};
 constexpr int kMaxDevices = 64;
-SideStream g_side[kMaxDevices];
-std::mutex g_side_mu;
-
-// The current device's side stream, or nullptr if it cannot be made (the layer
-// then runs on the caller's stream alone).  g_side_mu must be held.
-SideStream* side_stream() {
-  int dev = -1;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
-  SideStream& x = g_side[dev];
-  if (!x.tried) {
-    x.tried = true;
-    x.ok = hipStreamCreateWithFlags(&x.s, hipStreamNonBlocking) == hipSuccess &&
-           hipEventCreateWithFlags(&x.fork, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&x.attn_done, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&x.sort_done, hipEventDisableTiming) == hipSuccess &&
-           hipEventCreateWithFlags(&x.ffn_done, hipEventDisableTiming) == hipSuccess;
-  }
-  return x.ok ? &x : nullptr;
-}
 
 int layer_check(int T, const wide_layer_cfg* cfg, int mode) {
   if (!cfg) return WIDE_EINVAL;
@@ -305,53 +269,30 @@ struct LayerCache {
   const PagedKV* paged = nullptr;
 };
 
-// Launch sequence of a layer call (arguments validated).  packed_ready: the
-// reorders' packed words already hold both masks (the router wrote them).
-// Prefill enqueues the two mask reorders on the device's second stream, beside
-// the first RMSNorm and the attention kernels, joined back by events.
+// Launch sequence of a layer call (arguments validated), on the caller's stream
+// alone.  Prefill: one launch does the first RMSNorm and both mask reorders (the
+// reorders read only the call's inputs, so they run beside the norm rows), then
+// the attention kernels, the second RMSNorm and the FFN kernels.  packed_ready:
+// the reorders' packed words already hold both masks (the router wrote them).
 int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_mask,
               const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
               const LayerCache& kv, uint16_t* Y, const LayerWs& w, hipStream_t s,
               bool packed_ready) {
   const int d = cfg->d_model, nkv = cfg->attn.n_kv_heads, n = cfg->n_ffn_groups;
-  auto attention = [&](hipEvent_t before_o) {
-    return attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode,
-                    kv.K, kv.V, kv.kv_len, kv.kv_cap, X, w.h, w.attn, s, kv.pair_len, kv.pos,
-                    false, kv.paged, before_o);
-  };
-  auto ffn = [&]() {
-    ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, n, mode, w.h,
-            Y, w.ffn, s, false);
-  };
   if (mode == WIDE_PREFILL) {
-    std::lock_guard<std::mutex> lock(g_side_mu);
-    SideStream* side = side_stream();
-    if (side && hipEventRecord(side->fork, s) == hipSuccess &&
-        hipStreamWaitEvent(side->s, side->fork, 0) == hipSuccess) {
-      // side stream: the attention partitions (read by the QKV projection), the
-      // token sort (read by the O projection), the FFN reorder
-      attn_reorder_groups(attn_mask, T, nkv, w.attn, side->s, packed_ready);
-      if (hipEventRecord(side->attn_done, side->s) != hipSuccess) return WIDE_EHIP;
-      attn_reorder_sort(T, nkv, w.attn, side->s);
-      if (hipEventRecord(side->sort_done, side->s) != hipSuccess) return WIDE_EHIP;
-      ffn_reorder(ffn_mask, T, n, w.ffn, side->s, packed_ready);
-      if (hipEventRecord(side->ffn_done, side->s) != hipSuccess) return WIDE_EHIP;
-      launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
-      if (hipStreamWaitEvent(s, side->attn_done, 0) != hipSuccess) return WIDE_EHIP;
-      if (attention(side->sort_done) != WIDE_OK) return WIDE_EHIP;
-      launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
-      if (hipStreamWaitEvent(s, side->ffn_done, 0) != hipSuccess) return WIDE_EHIP;
-      ffn();
-      return launch_status();
-    }
-    (void)hipGetLastError();
-    attn_reorder(attn_mask, T, nkv, w.attn, s, packed_ready);
-    ffn_reorder(ffn_mask, T, n, w.ffn, s, packed_ready);
+    const MaskJob aj = attn_job(attn_mask, T, nkv, w.attn, packed_ready);
+    const MaskJob fj = ffn_job(ffn_mask, T, n, w.ffn, packed_ready);
+    NormJob nj;
+    nj.x = X, nj.gamma = W->rms1, nj.d = d, nj.eps = cfg->rms_eps, nj.y = w.u;
+    launch_reorder_jobs(T, &aj, &fj, &nj, s);
+  } else {
+    launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
   }
-  launch_rmsnorm(X, W->rms1, T, d, cfg->rms_eps, w.u, s);
-  attention(nullptr);
+  attn_run(w.u, attn_mask, W->Wq, W->Wk, W->Wv, W->Wo_packed, T, d, &cfg->attn, mode, kv.K, kv.V,
+           kv.kv_len, kv.kv_cap, X, w.h, w.attn, s, kv.pair_len, kv.pos, false, kv.paged);
   launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
-  ffn();
+  ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, n, mode, w.h, Y,
+          w.ffn, s, false);
   return launch_status();
 }
 

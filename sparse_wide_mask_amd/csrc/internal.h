@@ -32,6 +32,35 @@ struct ReorderView {
   int tile_m = 0;
 };
 
+// The reorder of one mask, as one role set of the reorder launch.  mask null:
+// the packed words are the input (the router wrote them); otherwise they are
+// written.  tile_count / tile_groups null: no tile unions.  order non-null: also
+// the token order sorted by the whole pattern (n <= kSortMaxGroups), whose tiles'
+// unions then fill tile_count / tile_groups, and tile_perm (may be null).
+struct MaskJob {
+  const uint8_t* mask = nullptr;
+  uint64_t* packed = nullptr;
+  int n = 0, nw = 0, tile_m = 0;
+  int32_t* count = nullptr;
+  int32_t* perm = nullptr;
+  int32_t* rank = nullptr;
+  int32_t* tile_count = nullptr;
+  int32_t* tile_groups = nullptr;
+  int32_t* order = nullptr;
+  int32_t* tile_perm = nullptr;
+};
+// RMSNorm rows folded into the reorder launch (x null: none).
+struct NormJob {
+  const uint16_t* x = nullptr;
+  const uint16_t* gamma = nullptr;
+  int d = 0;
+  float eps = 0.f;
+  uint16_t* y = nullptr;
+};
+// One launch for up to two masks' reorders (a, b may be null) and the norm of the
+// T rows (may be null); every role reads only the call's inputs.
+void launch_reorder_jobs(int T, const MaskJob* a, const MaskJob* b, const NormJob* norm,
+                         hipStream_t s);
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
@@ -39,13 +68,9 @@ void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* pac
 void launch_reorder_packed(const uint64_t* packed, int T, int n, int tile_m,
                            int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                            int32_t* tile_count, int32_t* tile_groups, hipStream_t s);
-// Token order sorted by mask pattern (stable; n <= kSortMaxGroups, so the key is
-// the whole pattern), and the group union of each tile of tile_m consecutive
-// tokens in that order.  T <= WIDE_MAX_TOKENS (the keys take T bytes of LDS).
+// Few groups: the attention reorder also sorts the tokens by their whole pattern
+// (the key of at most 8 bits; T <= WIDE_MAX_TOKENS keys fit in LDS).
 constexpr int kSortMaxGroups = 8;
-void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
-                       int32_t* tile_count, int32_t* tile_groups, int32_t* tile_perm,
-                       hipStream_t s);
 
 void launch_pack_kmajor(const uint16_t* W, int n, int G, int d, uint16_t* Wp, hipStream_t s);
 

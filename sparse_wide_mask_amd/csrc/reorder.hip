@@ -1,32 +1,45 @@
 // Mask reordering (gist.science technical summary §2.B): per group, a stable
 // partition of the tokens into "kept" (a contiguous prefix) and "dropped", plus
-// the per-tile union of kept groups that block-level skipping reads (§2.C, l=0).
+// the per-tile union of kept groups that block-level skipping reads (§2.C, l=0),
+// the mask's packed bit words, and for few groups a token order sorted by the
+// whole mask pattern.
 //
-// No host synchronisation; one or two launches:
-//   1. reorder_pack   : one wave per token row packs its mask bytes into 64-bit
-//                       words by ballot.
-//   2. reorder_groups : one work-group per group (chunks of 64 tokens, a ballot
-//                       per chunk, a scan over the waves, then each lane places its
-//                       token by mbcnt), plus one work-group per token tile for
-//                       the tile's union of kept groups.
-// When no tile unions are asked for, one launch does both: the group work-groups
-// read the mask bytes themselves and further work-groups of the same grid pack the
-// words (which later kernels read).
+// Everything for one or two masks runs in one launch of 1024-thread work-groups,
+// each taking one role (no host synchronisation, no dependencies inside the
+// launch: every role reads the mask bytes, or the packed words when those are the
+// input; a mask of more than 16 groups is packed by a launch of its own first):
+//   sort    one work-group per sorted mask: a stable counting sort of the tokens
+//           by their pattern (n <= 8) and the unions of tiles of that order;
+//   groups  one per group: chunks of 64 tokens (lane = token), a ballot per chunk,
+//           a scan over the waves, then each lane places its token by mbcnt;
+//   unions  one per token tile: the OR of the tile's keep bits, compacted into an
+//           ascending group list, -1 padded;
+//   pack    one per 128 tokens: the mask's little-endian 64-bit words by ballot;
+//   norm    four token rows of the layer's first RMSNorm (a layer call folds it
+//           into this launch, so the reorders run beside it on one stream).
 #include "wide.h"
 #include "common.h"
 #include "gemm_tile.h"
 #include "internal.h"
+#include "norm_row.h"
+
+#include <algorithm>
 
 namespace wide {
 
-// Packing: one wave per token row at a time, lane j reading mask byte 64 w + j
-// (64 consecutive bytes per load); the ballot of "nonzero" is word w.  A wave
-// takes kPackTok rows and issues all of their loads before the first ballot.
-constexpr int kPackThreads = 256;
-constexpr int kPackWaves = kPackThreads / kWave;
-constexpr int kPackTok = 8;
+constexpr int kRoThreads = 1024;
+constexpr int kRoWaves = kRoThreads / kWave;
+constexpr int kPackTok = 8;                          // rows per wave of a pack work-group
+constexpr int kPackPerWg = kRoWaves * kPackTok;      // 128
+constexpr int kNormPerWg = kRoThreads / 256;         // 4 rows per norm work-group
+constexpr int kSortBins = 256;                       // key = the whole pattern (n <= 8)
+constexpr int kSortMaxTiles = 256;                   // tiles ranked for tile_perm
 
-// The kPackTok rows from t0 (one wave).
+// ------------------------------------------------------------------ roles
+
+// Packing: one wave per token row at a time, lane j reading mask byte 64 w + j
+// (64 consecutive bytes per load); the ballot of "nonzero" is word w.  The kPackTok
+// rows from t0 (one wave); all loads are issued before the first ballot.
 WIDE_DEV void pack_rows(const uint8_t* __restrict__ mask, int T, int n, int nw,
                         uint64_t* __restrict__ packed, int t0, int lane) {
   const rsrc_t mr = make_rsrc(mask, (uint32_t)((size_t)T * n));
@@ -47,53 +60,115 @@ WIDE_DEV void pack_rows(const uint8_t* __restrict__ mask, int T, int n, int nw,
     }
 }
 
-__global__ void __launch_bounds__(kPackThreads)
-    reorder_pack(const uint8_t* __restrict__ mask, int T, int n, int nw,
-                 uint64_t* __restrict__ packed) {
-  const int wave = threadIdx.x / kWave;
-  const int t0 = (blockIdx.x * kPackWaves + wave) * kPackTok;
-  if (t0 < T) pack_rows(mask, T, n, nw, packed, t0, lane_id());
+// Group g's stable partition.  Wave w takes a contiguous run of 64-token chunks.
+// Pass 1: the ballot of each chunk's keep bits (kept in LDS) and the wave's count;
+// a scan over the waves gives each wave's kept and dropped tokens before its run.
+// Pass 2: a kept lane goes to (kept before it), a dropped one to count + (dropped
+// before it): mbcnt of the ballot inside the chunk, so a wave's stores of a chunk
+// are two contiguous runs.  Keep bits come from the mask bytes, or from bit j of
+// the packed words.
+WIDE_DEV void group_partition(const MaskJob& J, int T, int g, uint64_t* sBallot, int* sWave) {
+  const int lane = lane_id(), wave = threadIdx.x / kWave;
+  const int n = J.n, nw = J.nw, w = g >> 6, j = g & 63;
+  const int nch = (T + kWave - 1) / kWave;
+  const int per = (nch + kRoWaves - 1) / kRoWaves;
+  const int c0 = min(nch, wave * per), c1 = min(nch, c0 + per);
+  const bool bytes = J.mask != nullptr;
+  const rsrc_t pr = make_rsrc(J.packed, bytes ? 0u : (uint32_t)((size_t)T * nw * 8));
+  const rsrc_t mr = make_rsrc(J.mask, bytes ? (uint32_t)((size_t)T * n) : 0u);
+  const int shift = bytes ? 0 : (j & 31);
+  int mine = 0;
+  for (int c = c0; c < c1; c += 8) {
+    uint32_t v[8];  // the mask byte, or the 32-bit half of word w that holds bit j
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const int t = (c + u) * kWave + lane;
+      const bool in = c + u < c1 && t < T;
+      v[u] = bytes ? ldbuf1(mr, in ? (uint32_t)(t * n + g) : kSkip)
+                   : __builtin_amdgcn_raw_buffer_load_b32(
+                         pr, in ? (uint32_t)((t * nw + w) * 8 + (j >> 5) * 4) : kSkip, 0, 0);
+    }
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const uint64_t b = ballot(bytes ? v[u] != 0u : ((v[u] >> shift) & 1u) != 0u);
+      if (c + u < c1) {
+        if (lane == 0) sBallot[c + u] = b;
+        mine += popc64(b);
+      }
+    }
+  }
+  if (lane == 0) sWave[wave] = mine;
+  __syncthreads();
+  int kept = 0, cnt = 0;
+  for (int i = 0; i < kRoWaves; ++i) {
+    const int x = sWave[i];
+    if (i < wave) kept += x;
+    cnt += x;
+  }
+  int dropped = c0 * kWave - kept;  // tokens before this wave's run that dropped g
+  int32_t* perm = J.perm + (size_t)g * T;
+  int32_t* rank = J.rank ? J.rank + (size_t)g * T : nullptr;
+  for (int c = c0; c < c1; ++c) {
+    const uint64_t b = sBallot[c];
+    const int t = c * kWave + lane;
+    const int valid = min(kWave, T - c * kWave);
+    const uint64_t vm = valid == kWave ? ~0ull : ((1ull << valid) - 1ull);
+    const uint64_t dmask = ~b & vm;
+    if (t < T) {
+      const bool k = (b >> lane) & 1ull;
+      const int r = k ? kept + mbcnt(b) : cnt + dropped + mbcnt(dmask);
+      perm[r] = t;
+      if (rank) rank[t] = r;
+    }
+    kept += popc64(b);
+    dropped += popc64(dmask);
+  }
+  if (threadIdx.x == 0) J.count[g] = cnt;
 }
 
-constexpr int kGroupThreads = 1024;
-constexpr int kGroupWaves = kGroupThreads / kWave;
-constexpr int kGroupMaxChunks = WIDE_MAX_TOKENS / kWave;
-
-// Work-groups 0..n-1: one per group.  The tokens go in chunks of 64 (lane = token);
-// wave w takes a contiguous run of chunks.  Pass 1: the ballot of each chunk's
-// keep bits (kept in LDS) and the wave's count; a scan over the waves gives each
-// wave's kept and dropped tokens before its run.  Pass 2: a kept lane goes to
-// (kept before it), a dropped one to count + (dropped before it): mbcnt of the
-// ballot inside the chunk, so a wave's stores of a chunk are two contiguous runs.
-// Work-groups n..: one per token tile (when tile unions are asked for): the OR of
-// the tile's packed words, compacted into an ascending group list, -1 padded.
-// mask != nullptr (no tile unions then): the group work-groups read the keep bits
-// from the mask bytes, and the work-groups from n on pack the words, kPackTok rows
-// per wave.
-__global__ void __launch_bounds__(kGroupThreads)
-    reorder_groups(const uint8_t* __restrict__ mask, uint64_t* __restrict__ packed, int T, int n,
-                   int nw, int tile_m, int32_t* __restrict__ group_count,
-                   int32_t* __restrict__ group_perm, int32_t* __restrict__ group_rank,
-                   int32_t* __restrict__ tile_count, int32_t* __restrict__ tile_groups) {
-  __shared__ int sWave[kGroupWaves];
-  __shared__ uint32_t sU[8];
-  __shared__ uint64_t sBallot[kGroupMaxChunks];
+// The group union of tile `tile` (tile_m consecutive tokens).  From the bytes:
+// wave w takes rows w, w + 16, ...; lane holds groups lane + 64 i; a ballot per
+// word, OR-ed over the waves in LDS.  From the packed words: the OR of the rows'
+// words.  Then wave 0 compacts the union into an ascending list, -1 padded.
+WIDE_DEV void tile_union(const MaskJob& J, int T, int tile, uint32_t* sU) {
   const int lane = lane_id(), wave = threadIdx.x / kWave;
-  if (mask && (int)blockIdx.x >= n) {
-    const int t0 = (((int)blockIdx.x - n) * kGroupWaves + wave) * kPackTok;
-    if (t0 < T) pack_rows(mask, T, n, nw, packed, t0, lane);
-    return;
-  }
-  if ((int)blockIdx.x >= n) {
-    const int tile = blockIdx.x - n;
-    if (threadIdx.x < 8) sU[threadIdx.x] = 0u;
-    __syncthreads();
-    const int t0 = tile * tile_m, t1 = min(T, t0 + tile_m);
+  const int n = J.n, nw = J.nw;
+  if (threadIdx.x < 8) sU[threadIdx.x] = 0u;
+  __syncthreads();
+  const int t0 = tile * J.tile_m, t1 = min(T, t0 + J.tile_m);
+  if (J.mask) {
+    const rsrc_t mr = make_rsrc(J.mask, (uint32_t)((size_t)T * n));
+    bool any[4] = {false, false, false, false};
+    for (int r0 = t0 + wave; r0 < t1; r0 += 8 * kRoWaves) {
+      uint32_t v[8][4];
+#pragma unroll
+      for (int u = 0; u < 8; ++u) {
+        const int t = r0 + u * kRoWaves;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          const int g = 64 * w + lane;
+          v[u][w] = ldbuf1(mr, t < t1 && g < n ? (uint32_t)(t * n + g) : kSkip);
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 8; ++u)
+#pragma unroll
+        for (int w = 0; w < 4; ++w) any[w] = any[w] || v[u][w] != 0u;
+    }
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      const uint64_t word = ballot(any[w]);
+      if (lane == 0 && w < nw && word) {
+        if ((uint32_t)word) atomicOr(&sU[2 * w], (uint32_t)word);
+        if ((uint32_t)(word >> 32)) atomicOr(&sU[2 * w + 1], (uint32_t)(word >> 32));
+      }
+    }
+  } else {
     uint64_t uni[4] = {0, 0, 0, 0};
-    for (int t = t0 + (int)threadIdx.x; t < t1; t += kGroupThreads) {
+    for (int t = t0 + (int)threadIdx.x; t < t1; t += kRoThreads) {
 #pragma unroll
       for (int w = 0; w < 4; ++w)
-        if (w < nw) uni[w] |= packed[(size_t)t * nw + w];
+        if (w < nw) uni[w] |= J.packed[(size_t)t * nw + w];
     }
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -104,129 +179,73 @@ __global__ void __launch_bounds__(kGroupThreads)
         if (hi) atomicOr(&sU[2 * w + 1], hi);
       }
     }
-    __syncthreads();
-    if (wave == 0) {
-      int32_t* out = tile_groups + (size_t)tile * n;
-      int written = 0;
-#pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        if (w >= nw) break;
-        const uint64_t u = ((uint64_t)sU[2 * w + 1] << 32) | sU[2 * w];
-        const int g = 64 * w + lane;
-        if (g < n && ((u >> lane) & 1ull)) out[written + popc64(u & ((1ull << lane) - 1ull))] = g;
-        written += popc64(u);
-      }
-      for (int p = written + lane; p < n; p += kWave) out[p] = -1;
-      if (lane == 0) tile_count[tile] = written;
-    }
-    return;
   }
-  const int g = blockIdx.x;
-  const int w = g >> 6, j = g & 63;
-  const int nch = (T + kWave - 1) / kWave;
-  const int per = (nch + kGroupWaves - 1) / kGroupWaves;
-  const int c0 = min(nch, wave * per), c1 = min(nch, c0 + per);
-  const rsrc_t pr = make_rsrc(packed, mask ? 0u : (uint32_t)((size_t)T * nw * 8));
-  const rsrc_t mr = make_rsrc(mask, mask ? (uint32_t)((size_t)T * n) : 0u);
-  // keep bit of lane's token: bit j of the loaded half word, or the mask byte
-  const int shift = mask ? 0 : (j & 31);
-  int mine = 0;
-  for (int c = c0; c < c1; c += 8) {
-    uint32_t v[8];  // the 32-bit half of word w that holds bit j, or the mask byte
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const int t = (c + u) * kWave + lane;
-      const bool in = c + u < c1 && t < T;
-      v[u] = mask ? ldbuf1(mr, in ? (uint32_t)(t * n + g) : kSkip)
-                  : __builtin_amdgcn_raw_buffer_load_b32(
-                        pr, in ? (uint32_t)((t * nw + w) * 8 + (j >> 5) * 4) : kSkip, 0, 0);
-    }
-#pragma unroll
-    for (int u = 0; u < 8; ++u) {
-      const uint64_t b = ballot(mask ? v[u] != 0u : ((v[u] >> shift) & 1u) != 0u);
-      if (c + u < c1) {
-        if (lane == 0) sBallot[c + u] = b;
-        mine += popc64(b);
-      }
-    }
-  }
-  if (lane == 0) sWave[wave] = mine;
   __syncthreads();
-  int kept = 0, cnt = 0;
-  for (int i = 0; i < kGroupWaves; ++i) {
-    const int x = sWave[i];
-    if (i < wave) kept += x;
-    cnt += x;
-  }
-  int dropped = c0 * kWave - kept;  // tokens before this wave's run that dropped g
-  int32_t* perm = group_perm + (size_t)g * T;
-  int32_t* rank = group_rank ? group_rank + (size_t)g * T : nullptr;
-  for (int c = c0; c < c1; ++c) {
-    const uint64_t b = sBallot[c];
-    const int t = c * kWave + lane;
-    const int valid = min(kWave, T - c * kWave);
-    const uint64_t vm = valid == kWave ? ~0ull : ((1ull << valid) - 1ull);
-    const uint64_t d = ~b & vm;
-    if (t < T) {
-      const bool k = (b >> lane) & 1ull;
-      const int r = k ? kept + mbcnt(b) : cnt + dropped + mbcnt(d);
-      perm[r] = t;
-      if (rank) rank[t] = r;
+  if (wave == 0) {
+    int32_t* out = J.tile_groups + (size_t)tile * n;
+    int written = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      if (w >= nw) break;
+      const uint64_t u = ((uint64_t)sU[2 * w + 1] << 32) | sU[2 * w];
+      const int g = 64 * w + lane;
+      if (g < n && ((u >> lane) & 1ull)) out[written + popc64(u & ((1ull << lane) - 1ull))] = g;
+      written += popc64(u);
     }
-    kept += popc64(b);
-    dropped += popc64(d);
+    for (int p = written + lane; p < n; p += kWave) out[p] = -1;
+    if (lane == 0) J.tile_count[tile] = written;
   }
-  if (threadIdx.x == 0) group_count[g] = cnt;
 }
 
-constexpr int kSortThreads = 1024;
-constexpr int kSortWaves = kSortThreads / kWave;
-constexpr int kSortBins = 256;  // key = the whole mask pattern (n <= 8 groups)
-constexpr int kSortMaxTiles = 256;  // tiles ranked for tile_perm (256-token tiles of 65536)
-
-// One work-group; keys (the tokens' 8-bit patterns) are staged in LDS.  Wave w
-// owns the contiguous tokens [w c, (w + 1) c) and (1) counts its keys, (2) one
-// scan over (key, wave) gives each wave's first slot per key, (3) each wave
-// places its tokens in order, 64 at a time; lanes with equal keys are ranked by a
-// ballot match.  (4) A tile of the new order covers a run of whole key ranges,
-// so its group union is the OR of the keys whose range meets it.  (5) When
-// tile_perm is given: the K-masked kernel's XCD x takes the tile slots
-// m x .. m x + m - 1 (m = tiles / 8) whenever the tile count is a multiple of 32,
-// and a tile's time grows with its union; so the tiles, largest union first,
-// are dealt to the XCDs in snake order (XCD x gets ranks x, 15 - x, 16 + x, ...)
-// and tile_perm[slot] names the tile of each slot (identity otherwise).
-__global__ void __launch_bounds__(kSortThreads)
-    reorder_token_sort(const uint64_t* __restrict__ packed, int T, int n, int nw, int tile_m,
-                       int32_t* __restrict__ order, int32_t* __restrict__ tile_count,
-                       int32_t* __restrict__ tile_groups, int32_t* __restrict__ tile_perm) {
-  extern __shared__ uint8_t sKey[];  // [T]
-  __shared__ int sHist[kSortWaves][kSortBins];
-  __shared__ int sStart[kSortBins + 1];
-  __shared__ int sUnion[kSortMaxTiles];
+// Stable counting sort of the tokens by their whole pattern (n <= 8, key < 256),
+// keys staged in LDS (sKey [T]).  Wave w owns the contiguous tokens [w c, (w+1) c)
+// and (1) counts its keys, (2) one scan over (key, wave) gives each wave's first
+// slot per key, (3) each wave places its tokens in order, 64 at a time; lanes with
+// equal keys are ranked by a ballot match.  (4) A tile of the new order covers a
+// run of whole key ranges, so its group union is the OR of the keys whose range
+// meets it.  (5) When tile_perm is given: the K-masked kernel's XCD x takes the
+// tile slots m x .. m x + m - 1 (m = tiles / 8) whenever the tile count is a
+// multiple of 32, and a tile's time grows with its union; so the tiles, largest
+// union first, are dealt to the XCDs in snake order (XCD x gets ranks x, 15 - x,
+// 16 + x, ...) and tile_perm[slot] names the tile of each slot (identity otherwise).
+WIDE_DEV void token_sort(const MaskJob& J, int T, uint8_t* sKey, int (*sHist)[kSortBins],
+                         int* sStart, int* sUnion) {
   const int tid = threadIdx.x, lane = lane_id(), wave = tid / kWave;
-  for (int i = tid; i < kSortWaves * kSortBins; i += kSortThreads) (&sHist[0][0])[i] = 0;
-  for (int t0 = 0; t0 < T; t0 += 4 * kSortThreads) {
-    uint64_t v[4];
+  const int n = J.n;
+  for (int i = tid; i < kRoWaves * kSortBins; i += kRoThreads) (&sHist[0][0])[i] = 0;
+  // keys: bit g = (mask byte g != 0), or the low byte of the first packed word
+  const rsrc_t mr = make_rsrc(J.mask, J.mask ? (uint32_t)((size_t)T * n) : 0u);
+  for (int t0 = 0; t0 < T; t0 += 4 * kRoThreads) {
+    uint32_t key[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = t0 + u * kSortThreads + tid;
-      v[u] = t < T ? packed[(size_t)t * nw] : 0ull;
+      const int t = t0 + u * kRoThreads + tid;
+      key[u] = 0u;
+      if (J.mask) {
+        uint32_t b[8];
+#pragma unroll
+        for (int g = 0; g < 8; ++g) b[g] = ldbuf1(mr, t < T && g < n ? (uint32_t)(t * n + g) : kSkip);
+#pragma unroll
+        for (int g = 0; g < 8; ++g) key[u] |= (b[g] != 0u ? 1u : 0u) << g;
+      } else if (t < T) {
+        key[u] = (uint32_t)(J.packed[(size_t)t * J.nw] & 0xffull);
+      }
     }
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int t = t0 + u * kSortThreads + tid;
-      if (t < T) sKey[t] = (uint8_t)v[u];
+      const int t = t0 + u * kRoThreads + tid;
+      if (t < T) sKey[t] = (uint8_t)key[u];
     }
   }
   __syncthreads();
-  const int per = (T + kSortWaves - 1) / kSortWaves;
+  const int per = (T + kRoWaves - 1) / kRoWaves;
   const int c0 = min(T, wave * per), c1 = min(T, c0 + per);
   for (int t = c0 + lane; t < c1; t += kWave) atomicAdd(&sHist[wave][sKey[t]], 1);
   __syncthreads();
   // exclusive scan in (key, wave) order: thread k < 256 owns key k
   if (tid < kSortBins) {
     int run = 0;
-    for (int w = 0; w < kSortWaves; ++w) {
+    for (int w = 0; w < kRoWaves; ++w) {
       const int v = sHist[w][tid];
       sHist[w][tid] = run;
       run += v;
@@ -261,15 +280,15 @@ __global__ void __launch_bounds__(kSortThreads)
     }
     if (ok) {
       const uint64_t below = same & ((1ull << lane) - 1ull);
-      order[sStart[key] + sHist[wave][key] + popc64(below)] = t;
+      J.order[sStart[key] + sHist[wave][key] + popc64(below)] = t;
       // the last lane of each key bumps the wave's slot for that key
       if ((same >> lane) == 1ull) sHist[wave][key] += popc64(same);
     }
   }
   // tile unions from the key ranges: wave w takes tiles w, w + 16, ...
-  const int n_tiles = (T + tile_m - 1) / tile_m;
-  for (int tile = wave; tile < n_tiles; tile += kSortWaves) {
-    const int p0 = tile * tile_m, p1 = min(T, p0 + tile_m);
+  const int n_tiles = (T + J.tile_m - 1) / J.tile_m;
+  for (int tile = wave; tile < n_tiles; tile += kRoWaves) {
+    const int p0 = tile * J.tile_m, p1 = min(T, p0 + J.tile_m);
     uint32_t u = 0;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -278,21 +297,21 @@ __global__ void __launch_bounds__(kSortThreads)
       if (a < e && a < p1 && e > p0) u |= (uint32_t)k;
     }
     for (int off = 32; off >= 1; off >>= 1) u |= __shfl_xor(u, off);
-    int32_t* out = tile_groups + (size_t)tile * n;
+    int32_t* out = J.tile_groups + (size_t)tile * n;
     const bool has = lane < n && ((u >> lane) & 1u);
     const uint64_t hb = ballot(has);
     if (has) out[popc64(hb & ((1ull << lane) - 1ull))] = lane;
     const int written = popc64(hb);
     for (int q = written + lane; q < n; q += kWave) out[q] = -1;
     if (lane == 0) {
-      tile_count[tile] = written;
+      J.tile_count[tile] = written;
       if (tile < kSortMaxTiles) sUnion[tile] = written;
     }
   }
-  if (!tile_perm) return;
+  if (!J.tile_perm) return;
   __syncthreads();
   const bool snake = n_tiles % 32 == 0 && n_tiles <= kSortMaxTiles;
-  for (int i = tid; i < n_tiles; i += kSortThreads) {
+  for (int i = tid; i < n_tiles; i += kRoThreads) {
     int slot = i;
     if (snake) {
       const int u = sUnion[i];
@@ -305,53 +324,161 @@ __global__ void __launch_bounds__(kSortThreads)
       const int x = (round & 1) ? 7 - pos : pos;
       slot = (n_tiles >> 3) * x + round;
     }
-    tile_perm[slot] = i;
+    J.tile_perm[slot] = i;
   }
 }
 
-void launch_token_sort(const uint64_t* packed, int T, int n, int tile_m, int32_t* order,
-                       int32_t* tile_count, int32_t* tile_groups, int32_t* tile_perm,
-                       hipStream_t s) {
-  // the key array may take the whole 64 KB of dynamic LDS next to the static part
-  static const hipError_t attr = hipFuncSetAttribute(
-      reinterpret_cast<const void*>(&reorder_token_sort),
-      hipFuncAttributeMaxDynamicSharedMemorySize, WIDE_MAX_TOKENS);
-  (void)attr;
-  WIDE_TRACE("reorder_token_sort", s);
-  reorder_token_sort<<<1, kSortThreads, (size_t)T, s>>>(packed, T, n, (n + 63) / 64, tile_m,
-                                                        order, tile_count, tile_groups,
-                                                        tile_perm);
+// Norm rows 4 w .. 4 w + 3, 256 threads each.  Every thread of the work-group
+// passes the same barriers, so a row past T computes on row T - 1 and does not
+// store.
+WIDE_DEV void norm_rows(const NormJob& nm, int T, int w, float* sRed) {
+  const int quarter = threadIdx.x >> 8;
+  const int row = kNormPerWg * w + quarter;
+  const int rr = min(row, T - 1);
+  rms_row(nm.x + (size_t)rr * nm.d, nm.gamma, nm.d, nm.eps,
+          row < T ? nm.y + (size_t)rr * nm.d : nullptr, threadIdx.x & 255, sRed + 4 * quarter);
 }
 
-void launch_reorder_packed(const uint64_t* packed, int T, int n, int tile_m,
-                           int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
-                           int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
-  const int nw = (n + 63) / 64;
-  const int n_tiles = tile_count ? (T + tile_m - 1) / tile_m : 0;
-  WIDE_TRACE("reorder_groups", s);
-  reorder_groups<<<n + n_tiles, kGroupThreads, 0, s>>>(nullptr, const_cast<uint64_t*>(packed), T,
-                                                        n, nw, tile_m, group_count, group_perm,
-                                                        group_rank, tile_count, tile_groups);
+// ------------------------------------------------------------------ the launch
+
+// Work-group counts of the roles, in grid order: the sorts (the longest single
+// work-groups) first, then the norm rows (most of the launch's memory traffic),
+// then the short group, union and pack work-groups, which fill the compute units
+// as the norm rows drain.
+struct RoGrid {
+  int sort[2], groups[2], unions[2], pack[2], norm;  // norm: after the sorts
+};
+
+// Dynamic LDS of the launch: the largest role present.
+struct RoLds {
+  static constexpr size_t align16(size_t x) { return (x + 15) / 16 * 16; }
+  static size_t sort(int T) {
+    return align16((size_t)T) + sizeof(int) * ((size_t)kRoWaves * kSortBins + kSortBins + 1 + kSortMaxTiles) + 16;
+  }
+  static size_t groups(int T) { return 64 * sizeof(int) + 8 * (size_t)((T + kWave - 1) / kWave); }
+};
+
+// Runs f(r) when r falls in the next segment of `count` work-groups; else steps r
+// past it.
+template <class F>
+WIDE_DEV bool segment(int& r, int count, F&& f) {
+  if (r < count) {
+    f(r);
+    return true;
+  }
+  r -= count;
+  return false;
+}
+
+// Two work-groups per compute unit (8 waves per SIMD): the norm rows need the
+// memory parallelism of a full CU.
+__global__ void __launch_bounds__(kRoThreads) __attribute__((amdgpu_waves_per_eu(8, 8)))
+    reorder_all(MaskJob a, MaskJob b, NormJob nm, int T, RoGrid grid) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  int r = blockIdx.x;
+  uint8_t* sKey = smem;
+  int(*sHist)[kSortBins] = reinterpret_cast<int(*)[kSortBins]>(smem + RoLds::align16(T));
+  int* sStart = &sHist[kRoWaves][0];
+  int* sUnion = sStart + kSortBins + 1;
+  uint64_t* sBallot = reinterpret_cast<uint64_t*>(smem + 64 * sizeof(int));
+  int* sWave = reinterpret_cast<int*>(smem);
+  uint32_t* sU = reinterpret_cast<uint32_t*>(smem);
+  const int t0p = (int)threadIdx.x / kWave * kPackTok;  // this wave's first row of a pack unit
+  if (segment(r, grid.sort[0], [&](int) { token_sort(a, T, sKey, sHist, sStart, sUnion); }) ||
+      segment(r, grid.sort[1], [&](int) { token_sort(b, T, sKey, sHist, sStart, sUnion); }) ||
+      segment(r, grid.norm, [&](int w) { norm_rows(nm, T, w, reinterpret_cast<float*>(smem)); }) ||
+      segment(r, grid.groups[0], [&](int g) { group_partition(a, T, g, sBallot, sWave); }) ||
+      segment(r, grid.groups[1], [&](int g) { group_partition(b, T, g, sBallot, sWave); }) ||
+      segment(r, grid.unions[0], [&](int t) { tile_union(a, T, t, sU); }) ||
+      segment(r, grid.unions[1], [&](int t) { tile_union(b, T, t, sU); }) ||
+      segment(r, grid.pack[0], [&](int p) {
+        const int t0 = p * kPackPerWg + t0p;
+        if (t0 < T) pack_rows(a.mask, T, a.n, a.nw, a.packed, t0, lane_id());
+      }) ||
+      segment(r, grid.pack[1], [&](int p) {
+        const int t0 = p * kPackPerWg + t0p;
+        if (t0 < T) pack_rows(b.mask, T, b.n, b.nw, b.packed, t0, lane_id());
+      }))
+    return;
+}
+
+// A group's partition reads one byte per token from the [T, n] mask, so for many
+// groups every work-group would pull the whole mask through L2 (112 groups: 100 MB
+// for a 0.9 MB mask).  Masks with more groups than this are packed by a launch of
+// their own first, and the roles of the main launch read the packed words.
+constexpr int kBytesMaxGroups = 16;
+
+static RoGrid ro_grid(int T, const MaskJob* const (&J)[2], const NormJob* norm, bool pack_only,
+                      size_t& lds) {
+  RoGrid g{};
+  lds = 64;
+  for (int q = 0; q < 2; ++q) {
+    const MaskJob* j = J[q];
+    if (!j) continue;
+    g.pack[q] = j->mask ? (T + kPackPerWg - 1) / kPackPerWg : 0;
+    if (pack_only) continue;
+    const bool sort = j->order != nullptr;
+    g.sort[q] = sort ? 1 : 0;
+    g.groups[q] = j->n;
+    g.unions[q] = (!sort && j->tile_count) ? (T + j->tile_m - 1) / j->tile_m : 0;
+    if (sort) lds = std::max(lds, RoLds::sort(T));
+    lds = std::max(lds, RoLds::groups(T));
+  }
+  g.norm = norm && !pack_only ? (T + kNormPerWg - 1) / kNormPerWg : 0;
+  return g;
+}
+
+static int ro_blocks(const RoGrid& g) {
+  return g.sort[0] + g.sort[1] + g.groups[0] + g.groups[1] + g.unions[0] + g.unions[1] +
+         g.pack[0] + g.pack[1] + g.norm;
+}
+
+void launch_reorder_jobs(int T, const MaskJob* a, const MaskJob* b, const NormJob* norm,
+                         hipStream_t s) {
+  if (T <= 0) return;
+  // the sort's keys may take the whole 64 KB of tokens next to its tables
+  static const hipError_t attr = hipFuncSetAttribute(
+      reinterpret_cast<const void*>(&reorder_all), hipFuncAttributeMaxDynamicSharedMemorySize,
+      (int)RoLds::sort(WIDE_MAX_TOKENS));
+  (void)attr;
+  const MaskJob none{};
+  MaskJob local[2];
+  const MaskJob* J[2] = {a, b};
+  const MaskJob* P[2] = {nullptr, nullptr};  // jobs packed first
+  for (int q = 0; q < 2; ++q)
+    if (J[q] && J[q]->mask && J[q]->n > kBytesMaxGroups) {
+      P[q] = J[q];
+      local[q] = *J[q];
+      local[q].mask = nullptr;  // the main launch reads the packed words
+      J[q] = &local[q];
+    }
+  size_t lds = 0;
+  if (P[0] || P[1]) {
+    WIDE_TRACE("reorder_pack", s);
+    const RoGrid g = ro_grid(T, P, nullptr, true, lds);
+    reorder_all<<<ro_blocks(g), kRoThreads, lds, s>>>(P[0] ? *P[0] : none, P[1] ? *P[1] : none,
+                                                      NormJob{}, T, g);
+  }
+  const RoGrid g = ro_grid(T, J, norm, false, lds);
+  WIDE_TRACE(norm ? "norm_reorder" : "reorder", s);
+  reorder_all<<<ro_blocks(g), kRoThreads, lds, s>>>(J[0] ? *J[0] : none, J[1] ? *J[1] : none,
+                                                    norm ? *norm : NormJob{}, T, g);
 }
 
 void launch_reorder(const uint8_t* mask, int T, int n, int tile_m, uint64_t* packed,
                     int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
                     int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
-  const int nw = (n + 63) / 64;
-  if (!tile_count) {  // one launch: groups from the mask bytes, packing beside them
-    const int per_block = kGroupWaves * kPackTok;
-    WIDE_TRACE("reorder_groups", s);
-    reorder_groups<<<n + (T + per_block - 1) / per_block, kGroupThreads, 0, s>>>(
-        mask, packed, T, n, nw, tile_m, group_count, group_perm, group_rank, nullptr, nullptr);
-    return;
-  }
-  {
-    WIDE_TRACE("reorder_pack", s);
-    const int per_block = kPackWaves * kPackTok;
-    reorder_pack<<<(T + per_block - 1) / per_block, kPackThreads, 0, s>>>(mask, T, n, nw, packed);
-  }
-  launch_reorder_packed(packed, T, n, tile_m, group_count, group_perm, group_rank, tile_count,
-                        tile_groups, s);
+  const MaskJob j{mask, packed, n, (n + 63) / 64, tile_m, group_count, group_perm, group_rank,
+                  tile_count, tile_groups, nullptr, nullptr};
+  launch_reorder_jobs(T, &j, nullptr, nullptr, s);
+}
+
+void launch_reorder_packed(const uint64_t* packed, int T, int n, int tile_m,
+                           int32_t* group_count, int32_t* group_perm, int32_t* group_rank,
+                           int32_t* tile_count, int32_t* tile_groups, hipStream_t s) {
+  const MaskJob j{nullptr, const_cast<uint64_t*>(packed), n, (n + 63) / 64, tile_m, group_count,
+                  group_perm, group_rank, tile_count, tile_groups, nullptr, nullptr};
+  launch_reorder_jobs(T, &j, nullptr, nullptr, s);
 }
 
 }  // namespace wide
