@@ -146,6 +146,9 @@ WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restric
   // epilogue.  This wave's 128 columns are one head, hsel = hsel0 + wn of the
   // tile: q head 2*nt + hsel, or k / v.  (With an odd head ratio the last q
   // tile's second head reads zeros or the next group's rows and is not written.)
+  // Every wave is past its last fragment read here, so the stages are free for
+  // the q / k rows' staging below.
+  __syncthreads();
   const int hsel = hsel0 + wn;
   if (!kv_tile && 2 * nt + hsel >= r) return;
   const bool is_v = kv_tile && hsel == 1;
@@ -155,6 +158,15 @@ WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restric
   const RopeFreq f0 = rope ? RopeFreq(exp2f(-(2.f * c0 / kHd) * log2_theta)) : RopeFreq(0.f);
   const RopeFreq f1 =
       rope ? RopeFreq(exp2f(-(2.f * (c0 + 32) / kHd) * log2_theta)) : RopeFreq(0.f);
+  // this wave's staging rows: WM x 128 bf16, in the A stages (and the B stages
+  // for the upper half of the waves when the A stages cannot hold them all)
+  constexpr int kRegion = C::WM * kHd;
+  constexpr bool kSplit = C::kWaves * kRegion > kStages * C::SA;
+  static_assert(!kSplit || (C::kWaves / 2 * kRegion <= kStages * C::SA &&
+                            C::kWaves / 2 * kRegion <= kStages * C::SB),
+                "q / k staging fits the stages");
+  uint16_t* const sQK = kSplit ? (wave < C::kWaves / 2 ? sA : sB) + (wave % (C::kWaves / 2)) * kRegion
+                               : sA + wave * kRegion;
   uint16_t* qdst = Qc + ((size_t)(g * r + 2 * nt + hsel) * T) * kHd;
   uint16_t* kdst = Kc + (size_t)g * T * kHd;
   uint16_t* vdst = Vt + (size_t)g * kHd * vtp;
@@ -198,12 +210,27 @@ WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restric
         const float r1 = v1 * co1 - v3 * s1, r3 = v3 * co1 + v1 * s1;
         v0 = r0, v1 = r1, v2 = r2, v3 = r3;
       }
-      uint16_t* p = (kv_tile ? kdst : qdst) + (size_t)(row0 + row) * kHd + c0;
+      uint16_t* p = sQK + (i * 32 + acc32_row(lane, e)) * kHd + c0;
       p[0] = f2bf(v0);
       p[32] = f2bf(v1);
       p[64] = f2bf(v2);
       p[96] = f2bf(v3);
     }
+  }
+  if (is_v) return;
+  // q / k: the wave's rows are consecutive rows of the group's compacted list,
+  // 256 bytes each, so they leave LDS as 16-byte chunks of one contiguous block
+  // (one bf16 per lane per store, the accumulator layout, cost about as much as
+  // the kernel's last K slices)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  uint16_t* dst = (kv_tile ? kdst : qdst) + (size_t)(row0 + wm * C::WM) * kHd;
+#pragma unroll
+  for (int it = 0; it < C::WM / 4; ++it) {
+    const int rr = it * 4 + (lane >> 4), c = lane & 15;
+    if (wm * C::WM + rr < rows)
+      *reinterpret_cast<u32x4*>(dst + (size_t)rr * kHd + c * 8) =
+          *reinterpret_cast<const u32x4*>(sQK + rr * kHd + c * 8);
   }
 }
 

@@ -124,31 +124,42 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
   else  // tail tile of the group: l=2 skips the row blocks with no kept token
     run(std::false_type{});
 
-  // epilogue: H[token, gG + ch] = silu(gate) * up, 32-bit byte offsets into H
-  // (T F 2 < 2^31); rows past the count only exist in a group's last tile
-  const rsrc_t hr = make_rsrc(H, (uint32_t)((size_t)T * F * 2));
-  auto store = [&](bool full) {
+  // epilogue: H[token, gG + ch] = silu(gate) * up.  Each wave parks its WM x WN/2
+  // bf16 results in LDS (the stages are free once every wave is past its last
+  // fragment read) and writes them back as 16-byte chunks of its rows, a whole
+  // 128-byte line per row (64 channels) where the tile is 256 wide; one bf16 per
+  // lane per store (the accumulator layout) made the epilogue cost as much as a
+  // tenth of the kernel.  32-bit byte offsets into H (T F 2 < 2^31); rows past the
+  // count exist only in a group's last tile and are not written.
+  constexpr int HCH = C::WN / 2;  // channels of the wave
+  constexpr int CPR = HCH / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  static_assert(NW * C::WM * HCH <= NS * C::SA && C::WM % RPI == 0, "epilogue tile fits the stages");
+  __syncthreads();
+  uint16_t* sH = sA + wave * C::WM * HCH;
 #pragma unroll
-    for (int i = 0; i < C::RB; ++i) {
-      if (!((rb_live >> i) & 1u)) continue;
+  for (int i = 0; i < C::RB; ++i) {
+    if (!((rb_live >> i) & 1u)) continue;
 #pragma unroll
-      for (int jp = 0; jp < C::CB / 2; ++jp) {
-        const f32x16 gt = acc.acc[i][2 * jp], up = acc.acc[i][2 * jp + 1];
-        const int col = g * G + nt * BNH + wn * (C::WN / 2) + jp * 32 + (lane & 31);
+    for (int jp = 0; jp < C::CB / 2; ++jp) {
+      const f32x16 gt = acc.acc[i][2 * jp], up = acc.acc[i][2 * jp + 1];
 #pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
-          const uint32_t off =
-              full || row < rows ? (uint32_t)(sTok[row] * F + col) * 2u : kSkip;
-          __builtin_amdgcn_raw_buffer_store_b16(f2bf(silu(gt[e]) * up[e]), hr, (int)off, 0, kNtStore);
-        }
-      }
+      for (int e = 0; e < 16; ++e)
+        sH[(i * 32 + acc32_row(lane, e)) * HCH + jp * 32 + (lane & 31)] = f2bf(silu(gt[e]) * up[e]);
     }
-  };
-  if (rows == BM)
-    store(true);
-  else
-    store(false);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  const rsrc_t hr = make_rsrc(H, (uint32_t)((size_t)T * F * 2));
+  const int chbase = g * G + nt * BNH + wn * HCH;
+#pragma unroll
+  for (int it = 0; it < C::WM / RPI; ++it) {
+    const int r = it * RPI + lane / CPR, c = lane % CPR;
+    const int row = wm * C::WM + r;
+    const u32x4 v = *reinterpret_cast<const u32x4*>(sH + r * HCH + c * 8);
+    const uint32_t off = row < rows ? (uint32_t)(sTok[row] * F + chbase + c * 8) * 2u : kSkip;
+    __builtin_amdgcn_raw_buffer_store_b128(v, hr, (int)off, 0, kNtStore);
+  }
 }
 
 // Tail tiles: 64 rows in a 2 x 4 wave layout (each wave still holds gate and up
@@ -354,50 +365,64 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     });
   }
 
-  // Epilogue: Y[token, col] = acc (+ residual), with 32-bit byte offsets
-  // (T d 2 < 2^31).  Rows past the tile's tokens and columns past d take the
-  // kSkip offset, so their loads read 0 and their stores are dropped; without a
-  // residual the descriptor has no records and every load reads 0.  A row
-  // block's residual loads (32 per lane) are issued together before the stores.  The
+  // Epilogue: Y[token, col] = acc (+ residual).  Each wave parks one 32-row block
+  // of its fp32 accumulators in LDS at a time (waves 0-3 in the A stages, 4-7 in
+  // the B stages, free once every wave is past its last fragment read) and moves
+  // it as 8-column chunks: one 16-byte residual load and one 16-byte store per
+  // lane, the residual loads of the block issued before the first store (Y may
+  // alias the residual: a lane reads its chunk before it writes it).  Rows past
+  // the tile's tokens and columns past d take the kSkip offset, so their loads
+  // read 0 and their stores are dropped; without a residual the descriptor has no
+  // records and every load reads 0.  32-bit byte offsets (T d 2 < 2^31).  The
   // residual pointer passes through an empty asm so the loads are not scheduled
-  // into the K loop, where they would push accumulators out of registers.
+  // into the K loop.
+  constexpr int CPR = C::WN / 8;  // 8-column chunks per row of the wave
+  constexpr int RPI = 64 / CPR;   // rows per instruction
+  constexpr int NIT = 32 / RPI;   // instructions per 32-row block
+  constexpr int kHalfWaves = C::kWaves / 2;
+  static_assert(kHalfWaves * 32 * C::WN * 4 <= kStages * C::SA * 2 &&
+                    kHalfWaves * 32 * C::WN * 4 <= kStages * C::SB * 2,
+                "epilogue blocks fit the stages");
+  __syncthreads();
+  float* sY = reinterpret_cast<float*>(wave < kHalfWaves ? sA : sB) +
+              (wave % kHalfWaves) * 32 * C::WN;
   const uint16_t* res = residual;
   asm volatile("" : "+s"(res));
   const rsrc_t yr = make_rsrc(Y, (uint32_t)((size_t)T * d * 2));
   const rsrc_t rr = make_rsrc(res, res ? (uint32_t)((size_t)T * d * 2) : 0u);
 #pragma unroll
   for (int i = 0; i < C::RB; ++i) {
-    uint32_t tok[16];
 #pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int row = wm * C::WM + i * 32 + acc32_row(lane, e);
-      tok[e] = row < rows ? (uint32_t)(sTok[row] * d) * 2u : kSkip;
+    for (int j = 0; j < C::CB; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e)
+        sY[acc32_row(lane, e) * C::WN + j * 32 + (lane & 31)] = acc.acc[i][j][e];
+    uint32_t off[NIT];
+    u32x4 rv[NIT];
+#pragma unroll
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + lane / CPR, c = lane % CPR;
+      const int row = wm * C::WM + i * 32 + r, col = n0 + wn * C::WN + c * 8;
+      off[it] = row < rows && col < d ? (uint32_t)(sTok[row] * d + col) * 2u : kSkip;
+      rv[it] = ldbuf16(rr, off[it]);
     }
-    // two 32-column blocks (32 loads per lane) at a time
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j0 = 0; j0 < C::CB; j0 += 2) {
-      uint32_t rv[2][16];
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = n0 + wn * C::WN + (j0 + jj) * 32 + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t off = col < d && tok[e] != kSkip ? tok[e] + 2u * col : kSkip;
-          rv[jj][e] = __builtin_amdgcn_raw_buffer_load_b16(rr, (int)off, 0, 0);
-        }
-      }
-#pragma unroll
-      for (int jj = 0; jj < 2; ++jj) {
-        const int col = n0 + wn * C::WN + (j0 + jj) * 32 + (lane & 31);
-#pragma unroll
-        for (int e = 0; e < 16; ++e) {
-          const uint32_t off = col < d && tok[e] != kSkip ? tok[e] + 2u * col : kSkip;
-          const float v = acc.acc[i][j0 + jj][e] + __uint_as_float(rv[jj][e] << 16);
-          __builtin_amdgcn_raw_buffer_store_b16(f2bf(v), yr, (int)off, 0, kNtStore);
-        }
-      }
+    for (int it = 0; it < NIT; ++it) {
+      const int r = it * RPI + lane / CPR, c = lane % CPR;
+      const f32x4 a0 = *reinterpret_cast<const f32x4*>(sY + r * C::WN + c * 8);
+      const f32x4 a1 = *reinterpret_cast<const f32x4*>(sY + r * C::WN + c * 8 + 4);
+      const u32x4 q = rv[it];
+      u32x4 o;
+      o[0] = pack_bf2(a0[0] + __uint_as_float(q[0] << 16), a0[1] + __uint_as_float(q[0] & 0xffff0000u));
+      o[1] = pack_bf2(a0[2] + __uint_as_float(q[1] << 16), a0[3] + __uint_as_float(q[1] & 0xffff0000u));
+      o[2] = pack_bf2(a1[0] + __uint_as_float(q[2] << 16), a1[1] + __uint_as_float(q[2] & 0xffff0000u));
+      o[3] = pack_bf2(a1[2] + __uint_as_float(q[3] << 16), a1[3] + __uint_as_float(q[3] & 0xffff0000u));
+      __builtin_amdgcn_raw_buffer_store_b128(o, yr, (int)off[it], 0, kNtStore);
     }
-    __builtin_amdgcn_sched_barrier(0);
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    __builtin_amdgcn_wave_barrier();  // the block's reads before the next block's writes
   }
 }
 
