@@ -732,6 +732,35 @@ def timed(torch, fn, steps, stream):
     return e0.elapsed_time(e1) / steps
 
 
+def graph_step(torch, W, ones=False):
+    """The workload's step recorded into HIP graphs (torch.cuda.graph), one graph per
+    input set, replayed in the same rotation, as a serving loop may launch a decode
+    step.  Every call of a decode step writes the same cache slots from the same
+    inputs, so a replay repeats the eager step."""
+    sets = W.sets if hasattr(W, "sets") else W.inner.sets
+    fn = lambda: W.step(ones=ones)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # one eager pass over the sets on a side stream first
+        for _ in range(len(sets)):
+            fn()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for _ in range(len(sets)):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            fn()
+        graphs.append(g)
+    torch.cuda.synchronize()
+    k = [0]
+
+    def replay():
+        graphs[k[0] % len(graphs)].replay()
+        k[0] += 1
+    return replay
+
+
 def traffic_from_profiles(kernel: str, workload: str):
     """HBM bytes per launch from the committed rocprofv3 --pmc summary, if it was
     taken on the current kernel source (its recorded hash must match)."""
@@ -838,6 +867,11 @@ def main():
                          "the FFN's)")
     ap.add_argument("--ffn-group", type=int, default=128,
                     help="layer workloads: channels per FFN group (d_ff 14336 = groups x this)")
+    ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
+                    help="how the timed steps are launched: eager calls, or replays of HIP graphs "
+                         "that recorded the calls (as a serving loop may run decode; measured "
+                         "4-5 us per step slower than eager calls on the 8B decode workloads, "
+                         "whose steps are GPU-bound)")
     ap.add_argument("--skip-ones", action="store_true",
                     help="skip the all-ones comparison (profiler runs: only masked launches)")
     ap.add_argument("--copy-bytes", type=int, default=0,
@@ -896,15 +930,25 @@ def main():
         W = WORKLOADS[args.workload]()
     W.upload(torch, wide, bf16, u8)
     stream = torch.cuda.current_stream()
+    graph = args.launch == "graph"
 
     warm(torch, W.step, args.warmup)
+    ms_eager = None
+    if graph:
+        ms_eager = timed(torch, W.step, args.steps, stream)
+        log(f"masked, eager calls: {ms_eager:.3f} ms/step")
+        step = graph_step(torch, W)
+        warm(torch, step, args.warmup)
+    else:
+        step = W.step
 
     # timed region: K masked steps as a caller runs them (no instrumentation)
-    ms = timed(torch, W.step, args.steps, stream)
-    log(f"masked: {ms:.3f} ms/step")
-    # the same K steps again with a HIP event pair around every kernel launch, on
-    # the launch's stream: per-kernel times for the roofline (the events add a few
-    # microseconds per launch, so the step time above is taken without them)
+    ms = timed(torch, step, args.steps, stream)
+    log(f"masked: {ms:.3f} ms/step" + (" (graph replays)" if graph else ""))
+    # the same K steps again, as eager calls, with a HIP event pair around every
+    # kernel launch, on the launch's stream: per-kernel times for the roofline (the
+    # events add a few microseconds per launch, so the step time above is taken
+    # without them)
     wide.trace_reset()
     wide.trace_enable(True)
     ms_traced = timed(torch, W.step, args.steps, stream)
@@ -917,8 +961,11 @@ def main():
     ms_ones = None
     if not args.skip_ones:
         warm(torch, lambda: W.step(ones=True), args.warmup)
-        # timed like the masked region (no instrumentation)
-        ms_ones = timed(torch, lambda: W.step(ones=True), max(3, args.steps // 2), stream)
+        # timed like the masked region (no instrumentation, the same launch kind)
+        ones_step = graph_step(torch, W, ones=True) if graph else (lambda: W.step(ones=True))
+        if graph:
+            warm(torch, ones_step, args.warmup)
+        ms_ones = timed(torch, ones_step, max(3, args.steps // 2), stream)
         log(f"all-ones: {ms_ones:.3f} ms/step")
 
     work = W.work()
@@ -966,6 +1013,8 @@ def main():
         "step_roofline": {"unit": unit, "achieved": round(step_rate, 1),
                           "frac": round(step_rate / peak, 4),
                           "work": "touched bytes" if hbm else "active FLOPs"},
+        "launch": "hip_graph" if graph else "eager",
+        "eager_ms_per_step": round(ms_eager, 4) if ms_eager else None,
         "traced_ms_per_step": round(ms_traced, 4),
         "all_ones_ms_per_step": round(ms_ones, 4) if ms_ones else None,
         "speedup_vs_all_ones": round(ms_ones / ms, 3) if ms_ones else None,
