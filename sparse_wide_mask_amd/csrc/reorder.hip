@@ -197,13 +197,17 @@ WIDE_DEV void tile_union(const MaskJob& J, int T, int tile, uint32_t* sU) {
   }
 }
 
-// Stable counting sort of the tokens by their whole pattern (n <= 8, key < 256),
-// keys staged in LDS (sKey [T]).  Wave w owns the contiguous tokens [w c, (w+1) c)
-// and (1) counts its keys, (2) one scan over (key, wave) gives each wave's first
-// slot per key, (3) each wave places its tokens in order, 64 at a time; lanes with
-// equal keys are ranked by a ballot match.  (4) A tile of the new order covers a
-// run of whole key ranges, so its group union is the OR of the keys whose range
-// meets it.  (5) When tile_perm is given: the K-masked kernel's XCD x takes the
+// Stable counting sort of the tokens by their whole pattern (n <= 8, pattern <
+// 256), patterns taken in reflected Gray-code order: the key of pattern p is its
+// rank k with k ^ (k >> 1) = p, so the patterns of neighbouring key ranges differ
+// in few groups and a tile that spans several ranges keeps a smaller union (top-4
+// of 8 groups at T = 8192: 5.66 instead of 6.16 groups per 256-token tile on
+// average, at most 7 instead of 8).  Keys staged in LDS (sKey [T]).  Wave w owns
+// the contiguous tokens [w c, (w+1) c) and (1) counts its keys, (2) one scan over
+// (key, wave) gives each wave's first slot per key, (3) each wave places its
+// tokens in order, 64 at a time; lanes with equal keys are ranked by a ballot
+// match.  (4) A tile of the new order covers a run of whole key ranges, so its
+// group union is the OR of the patterns whose range meets it.  (5) When tile_perm is given: the K-masked kernel's XCD x takes the
 // tile slots m x .. m x + m - 1 (m = tiles / 8) whenever the tile count is a
 // multiple of 32, and a tile's time grows with its union; so the tiles, largest
 // union first, are dealt to the XCDs in snake order (XCD x gets ranks x, 15 - x,
@@ -234,7 +238,11 @@ WIDE_DEV void token_sort(const MaskJob& J, int T, uint8_t* sKey, int (*sHist)[kS
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + u * kRoThreads + tid;
-      if (t < T) sKey[t] = (uint8_t)key[u];
+      uint32_t k = key[u];  // pattern -> its Gray-code rank
+      k ^= k >> 1;
+      k ^= k >> 2;
+      k ^= k >> 4;
+      if (t < T) sKey[t] = (uint8_t)k;
     }
   }
   __syncthreads();
@@ -294,7 +302,7 @@ WIDE_DEV void token_sort(const MaskJob& J, int T, uint8_t* sKey, int (*sHist)[kS
     for (int i = 0; i < 4; ++i) {
       const int k = 4 * lane + i;
       const int a = sStart[k], e = sStart[k + 1];
-      if (a < e && a < p1 && e > p0) u |= (uint32_t)k;
+      if (a < e && a < p1 && e > p0) u |= (uint32_t)(k ^ (k >> 1));
     }
     for (int off = 32; off >= 1; off >>= 1) u |= __shfl_xor(u, off);
     int32_t* out = J.tile_groups + (size_t)tile * n;
