@@ -98,7 +98,7 @@ FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
 }
 
 // reorder = false: the mask reorder of this call was already enqueued (by the
-// layer, on its side stream)
+// layer's norm + reorder launch, on the same stream)
 int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const uint16_t* Wu,
             const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
             uint16_t* Y, const FfnWs& w, hipStream_t s, bool reorder = true) {
@@ -232,8 +232,6 @@ int attn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wq, const u
 
 // -------------------------------------------------------------------- layer
 
-constexpr int kMaxDevices = 64;
-
 int layer_check(int T, const wide_layer_cfg* cfg, int mode) {
   if (!cfg) return WIDE_EINVAL;
   if (!(cfg->rms_eps >= 0.f)) return WIDE_EINVAL;
@@ -310,6 +308,8 @@ bool layer_weights_ok(const wide_layer_weights* W) {
 // current GPU comes from hipGetSymbolAddress, once per device, and only that
 // address is handed to kernels.
 static __device__ __align__(256) unsigned char scratch[WIDE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
 
 struct ScratchAddr {
   std::once_flag once;
