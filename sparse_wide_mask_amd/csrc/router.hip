@@ -67,6 +67,9 @@ WIDE_DEV void rt_select(const float* __restrict__ sL, const RtSet& st, int wave,
 #pragma unroll
   for (int i = 0; i < NWC; ++i) valid[i] = lane + 64 * i < n;
   float v[TPW][NWC];
+  // key 0 for groups past n: every threshold the search tests is at least 1, so
+  // they never count, and each ballot is one compare with no branch on the word
+  // count (words past it hold only such lanes)
   uint32_t key[TPW][NWC];
   bool keep[TPW][NWC];
 #pragma unroll
@@ -78,7 +81,8 @@ WIDE_DEV void rt_select(const float* __restrict__ sL, const RtSet& st, int wave,
       keep[q][i] = valid[i] && k >= n;
     }
   if (k > 0 && k < n) {
-    // the k-th largest key: the largest value with at least k keys >= it
+    // the k-th largest key: the largest value with at least k keys >= it (the
+    // TPW tokens' searches are independent chains of ballots)
     uint32_t kth[TPW];
 #pragma unroll
     for (int q = 0; q < TPW; ++q) kth[q] = 0u;
@@ -88,27 +92,24 @@ WIDE_DEV void rt_select(const float* __restrict__ sL, const RtSet& st, int wave,
         const uint32_t cand = kth[q] | (1u << b);
         int cnt = 0;
 #pragma unroll
-        for (int i = 0; i < NWC; ++i)
-          if (i < nw) cnt += popc64(ballot(valid[i] && key[q][i] >= cand));
-        if (cnt >= k) kth[q] = cand;
+        for (int i = 0; i < NWC; ++i) cnt += popc64(ballot(key[q][i] >= cand));
+        kth[q] = cnt >= k ? cand : kth[q];
       }
     }
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
       int above = 0;
 #pragma unroll
-      for (int i = 0; i < NWC; ++i)
-        if (i < nw) above += popc64(ballot(valid[i] && key[q][i] > kth[q]));
+      for (int i = 0; i < NWC; ++i) above += popc64(ballot(key[q][i] > kth[q]));
       // keys equal to the k-th: the first k - above of them in group order
       const int need = k - above;
       int before = 0;
 #pragma unroll
       for (int i = 0; i < NWC; ++i) {
-        if (i >= nw) break;
         const bool eq = valid[i] && key[q][i] == kth[q];
         const uint64_t bal = ballot(eq);
         const int rank = before + popc64(bal & ((1ull << lane) - 1ull));
-        keep[q][i] = (valid[i] && key[q][i] > kth[q]) || (eq && rank < need);
+        keep[q][i] = key[q][i] > kth[q] || (eq && rank < need);
         before += popc64(bal);
       }
     }
