@@ -15,7 +15,11 @@
 // One work-group = 32 tokens, 8 waves.  The 32-wide K steps are dealt to the
 // waves in pairs (wave w takes steps 2w, 2w + 1, 2w + 16, 2w + 17, ...), so both
 // halves of an X row's 128-byte line are read by one wave one step apart, and
-// each wave reads only its share of X and R.  K is short and a step's MFMAs are
+// each wave reads only its share of X and R.  A wave walks its pairs from a
+// start that differs between the work-groups of an XCD (all of which read the
+// whole of R), so that they do not all request the same lines of R at once
+// (8192 tokens x 112 groups: 34.0 -> 29.5 us); each token's sums still run in
+// one fixed order.  K is short and a step's MFMAs are
 // few, so the kernel is bound by load latency: a wave keeps two register sets of
 // U steps and issues the loads of one set before the MFMAs of the other (one set
 // when 16 column tiles take most of the registers).  Each
@@ -159,16 +163,23 @@ __global__ void __launch_bounds__(kRtThreads)
   f32x4 acc[NT][2];
 #pragma unroll
   for (int j = 0; j < NT; ++j) acc[j][0] = acc[j][1] = f32x4{0.f, 0.f, 0.f, 0.f};
-  // this wave's steps, in pairs: i-th step = 2 wave + (i & 1) + 16 (i >> 1)
-  // (d % 64 == 0: d / 32 is even)
+  // this wave's steps, in pairs: the i-th is 2 wave + (i & 1) + 16 j with
+  // j = (i >> 1) + rot mod mine / 2 (d % 64 == 0: d / 32 is even)
   const int mine = 2 * ((nsteps / 2 - wave + kRtWaves - 1) / kRtWaves);
-  // steps i0 .. i0 + U - 1 of the wave; past `mine` every load reads zeros
+  // this wave's pairs, mine / 2 of them, from pair rot on (XCD x runs work-groups
+  // x, x + 8, ...: neighbours there get different starts)
+  const int jw = mine / 2 > 0 ? mine / 2 : 1;
+  const int rot = (int)((blockIdx.x >> 3) % (unsigned)jw);
+  // steps i0 .. i0 + U - 1 of the wave; past `mine` every load reads zeros (and
+  // its step index, which may then pass the wave's pairs, is not used)
   auto load = [&](int i0, bf16x8 (&a)[U][2], bf16x8 (&b)[U][NT]) {
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       const int i = i0 + u;
       const bool live = i < mine;
-      const int step = 2 * wave + (i & 1) + 2 * kRtWaves * (i >> 1);
+      int pj = (i >> 1) + rot;
+      pj = pj >= jw ? pj - jw : pj;
+      const int step = 2 * wave + (i & 1) + 2 * kRtWaves * pj;
       const int col = step * 32 + koff;
 #pragma unroll
       for (int rb = 0; rb < 2; ++rb) {
@@ -247,9 +258,18 @@ __global__ void __launch_bounds__(kRtThreads)
   }
   __syncthreads();
 
-  // selection, router by router
-  rt_select<NWC, TPW, NG + 1>(&sL[0][0], sa, wave, lane, t0, rows);
-  if (ntB > 0) rt_select<NWC, TPW, NG + 1>(&sL[0][0], sb, wave, lane, t0, rows);
+  // selection, router by router, over as many 64-group words as the router has
+  auto select = [&](const RtSet& st) {
+    if constexpr (NWC > 1) {
+      if (st.n <= 64) {
+        rt_select<1, TPW, NG + 1>(&sL[0][0], st, wave, lane, t0, rows);
+        return;
+      }
+    }
+    rt_select<NWC, TPW, NG + 1>(&sL[0][0], st, wave, lane, t0, rows);
+  };
+  select(sa);
+  if (ntB > 0) select(sb);
 }
 
 // R [n, d] -> fragment order [ceil(n/16)][d/32][64 lanes][8]: lane l of block
