@@ -737,17 +737,19 @@ def graph_step(torch, W, ones=False):
     input set, replayed in the same rotation, as a serving loop may launch a decode
     step.  Every call of a decode step writes the same cache slots from the same
     inputs, so a replay repeats the eager step."""
-    sets = W.sets if hasattr(W, "sets") else W.inner.sets
+    # decode workloads rotate weight (and cache) sets; prefill ones use one set
+    holder = getattr(W, "inner", W)
+    n_sets = len(getattr(holder, "sets", [None]))
     fn = lambda: W.step(ones=ones)
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # one eager pass over the sets on a side stream first
-        for _ in range(len(sets)):
+        for _ in range(n_sets):
             fn()
     torch.cuda.current_stream().wait_stream(side)
     torch.cuda.synchronize()
     graphs = []
-    for _ in range(len(sets)):
+    for _ in range(n_sets):
         g = torch.cuda.CUDAGraph()
         with torch.cuda.graph(g):
             fn()
