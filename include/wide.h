@@ -173,6 +173,29 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
                     size_t workspace_bytes, uint32_t flags, void* stream);
 
 /*
+ * wide_ffn_masked_f32 - the masked SwiGLU FFN of wide_ffn_masked (gist.science §2.A)
+ * computed in fp32 throughout: fp32 inputs, weights, intermediate H and output, fp32
+ * products and sums on the vector units (no bf16 rounding anywhere).  For problems
+ * that are checked at fp32 precision, such as a tiny FFN layer given in fp32; it
+ * runs far below the bf16 path's rate.
+ *
+ * X              [T, d_model] fp32
+ * mask           [T, n_groups] uint8
+ * W_gate, W_up   [d_ff, d_model] fp32 (group g = rows gG..gG+G-1)
+ * W_down         [d_ff, d_model] fp32, as is (the matrix of Y = H @ W_down; no packing)
+ * Y              [T, d_model] fp32 (a token that keeps no group gets exact zeros)
+ * Any group size G = d_ff / n_groups and any d_model.  Workspace:
+ * wide_ffn_masked_f32_workspace() bytes (H).  Each output is one fixed-order sum, so a
+ * repeated call gives the same bits.  Errors and conventions as wide_ffn_masked
+ * (pointers 16-byte aligned, T <= WIDE_MAX_TOKENS, n_groups <= WIDE_MAX_GROUPS).
+ */
+size_t wide_ffn_masked_f32_workspace(int T, int d_model, int d_ff, int n_groups);
+int wide_ffn_masked_f32(const float* X, const uint8_t* mask, const float* W_gate,
+                        const float* W_up, const float* W_down, int T, int d_model, int d_ff,
+                        int n_groups, float* Y, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream);
+
+/*
  * wide_ffn_masked_noalloc - wide_ffn_masked for callers that cannot allocate device
  * memory: code under HIP graph capture, tight serving loops, harnesses that forbid
  * hipMalloc.  It takes no workspace and allocates nothing (no hipMalloc, hipFree or

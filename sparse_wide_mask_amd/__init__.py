@@ -10,15 +10,17 @@ raise.
 from .binding import (LIB_PATH, WideError, attn_decode_masked_cache, attn_decode_masked_paged,
                       attn_proj_masked,
                       attn_proj_masked_workspace,
-                      ffn_masked, ffn_masked_noalloc, ffn_masked_workspace, layer_decode_masked_cache,
+                      ffn_masked, ffn_masked_f32, ffn_masked_f32_workspace, ffn_masked_noalloc,
+                      ffn_masked_workspace, layer_decode_masked_cache,
                       layer_decode_masked_paged, layer_masked, layer_masked_routed,
                       layer_masked_workspace, mask_reorder_packed,
                       lib, mask_reorder, pack_kmajor, pack_router, router_topk, trace_collect,
                       trace_enable, trace_reset, WIDE_DECODE, WIDE_PREFILL)
 
 __all__ = [
-    "LIB_PATH", "WideError", "lib", "mask_reorder", "pack_kmajor", "pack_router", "router_topk", "ffn_masked",
-    "ffn_masked_noalloc", "ffn_masked_workspace", "attn_proj_masked", "attn_proj_masked_workspace",
+    "LIB_PATH", "WideError", "lib", "mask_reorder", "pack_kmajor", "pack_router", "router_topk",
+    "ffn_masked", "ffn_masked_f32", "ffn_masked_f32_workspace", "ffn_masked_noalloc",
+    "ffn_masked_workspace", "attn_proj_masked", "attn_proj_masked_workspace",
     "attn_decode_masked_cache", "attn_decode_masked_paged", "layer_masked", "layer_masked_routed",
     "layer_decode_masked_cache", "layer_decode_masked_paged", "mask_reorder_packed",
     "layer_masked_workspace", "trace_enable", "trace_reset", "trace_collect", "WIDE_PREFILL",

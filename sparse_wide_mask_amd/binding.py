@@ -44,6 +44,8 @@ _SIGS = {
     "wide_pack_router": ([_p, _i, _i, _p, _p], _i),
     "wide_ffn_masked_workspace": ([_i, _i, _i, _i, _i], _sz),
     "wide_ffn_masked": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
+    "wide_ffn_masked_f32_workspace": ([_i, _i, _i, _i], _sz),
+    "wide_ffn_masked_f32": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _p, _p, _sz, C.c_uint32, _p], _i),
     "wide_ffn_masked_noalloc": ([_p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _p, C.c_uint32, _p], _i),
     "wide_attn_proj_masked_workspace": ([_i, _i, C.POINTER(WideAttnCfg), _i, _i], _sz),
     "wide_attn_proj_masked": ([_p, _p, _p, _p, _p, _p, _i, _i, C.POINTER(WideAttnCfg), _i, _p, _p,
@@ -287,6 +289,30 @@ def ffn_masked(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out=None
     st = lib().wide_ffn_masked(_ptr(X), _ptr(mask), _ptr(W_gate), _ptr(W_up), _ptr(W_down_packed),
                                T, d, F, n, m, _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
     _check("wide_ffn_masked", st)
+    return Y
+
+
+def ffn_masked_f32_workspace(T, d_model, d_ff, n_groups) -> int:
+    return int(lib().wide_ffn_masked_f32_workspace(T, d_model, d_ff, n_groups))
+
+
+def ffn_masked_f32(X, mask, W_gate, W_up, W_down, *, out=None, workspace=None):
+    """wide_ffn_masked_f32: the masked FFN in fp32 throughout.  X [T, d] fp32, mask
+    [T, n] uint8, W_gate/W_up/W_down [F, d] fp32 (W_down as is, not packed).
+    Returns Y [T, d] fp32."""
+    for t, nm in ((X, "X"), (W_gate, "W_gate"), (W_up, "W_up"), (W_down, "W_down")):
+        _dev(t, torch.float32, nm)
+    _dev(mask, torch.uint8, "mask")
+    T, d = X.shape
+    F = W_gate.shape[0]
+    n = mask.shape[1]
+    if mask.shape[0] != T or any(w.shape != (F, d) for w in (W_gate, W_up, W_down)):
+        raise ValueError("shape mismatch")
+    ws = _workspace(ffn_masked_f32_workspace(T, d, F, n), X.device, workspace)
+    Y = out if out is not None else torch.empty((T, d), dtype=torch.float32, device=X.device)
+    st = lib().wide_ffn_masked_f32(_ptr(X), _ptr(mask), _ptr(W_gate), _ptr(W_up), _ptr(W_down),
+                                   T, d, F, n, _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+    _check("wide_ffn_masked_f32", st)
     return Y
 
 

@@ -65,6 +65,13 @@ void run_reorder(const uint8_t* mask, int T, int n, const ReorderView& v, hipStr
 constexpr int64_t kMaxBytes = 0x7fffff00LL;
 bool fits(int64_t a, int64_t b) { return a * b * 2 <= kMaxBytes; }
 
+// fp32 FFN: H [T, d_ff] fp32 in the workspace; 64-bit element offsets in the kernels
+int ffn_f32_check(int T, int d, int F, int n) {
+  if (T < 0 || d <= 0 || F <= 0 || n <= 0 || F % n) return WIDE_EINVAL;
+  if (n > WIDE_MAX_GROUPS || T > WIDE_MAX_TOKENS) return WIDE_EUNSUPPORTED;
+  return WIDE_OK;
+}
+
 int ffn_check(int T, int d, int F, int n, int mode) {
   if (T < 0 || d <= 0 || F <= 0 || n <= 0) return WIDE_EINVAL;
   if (mode != WIDE_PREFILL && mode != WIDE_DECODE) return WIDE_EINVAL;
@@ -444,6 +451,30 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
   (void)hipGetLastError();
   ffn_run(X, mask, W_gate, W_up, W_down_packed, T, d_model, d_ff, n_groups, mode, nullptr, Y, w,
           as_stream(stream));
+  return launch_status();
+}
+
+size_t wide_ffn_masked_f32_workspace(int T, int d_model, int d_ff, int n_groups) {
+  if (ffn_f32_check(T, d_model, d_ff, n_groups) != WIDE_OK) return 0;
+  return round_up((size_t)T * d_ff * sizeof(float));
+}
+
+int wide_ffn_masked_f32(const float* X, const uint8_t* mask, const float* W_gate,
+                        const float* W_up, const float* W_down, int T, int d_model, int d_ff,
+                        int n_groups, float* Y, void* workspace, size_t workspace_bytes,
+                        uint32_t flags, void* stream) {
+  const int st = ffn_f32_check(T, d_model, d_ff, n_groups);
+  if (st != WIDE_OK) return st;
+  if (flags != 0) return WIDE_EINVAL;
+  if (T == 0) return WIDE_OK;
+  if (!aligned16(X) || !aligned16(mask) || !aligned16(W_gate) || !aligned16(W_up) ||
+      !aligned16(W_down) || !aligned16(Y) || (void*)Y == (void*)X || !aligned16(workspace))
+    return WIDE_EINVAL;
+  if (workspace_bytes < wide_ffn_masked_f32_workspace(T, d_model, d_ff, n_groups))
+    return WIDE_EWORKSPACE;
+  (void)hipGetLastError();
+  launch_ffn_f32(X, mask, W_gate, W_up, W_down, T, d_model, d_ff, n_groups,
+                 static_cast<float*>(workspace), Y, as_stream(stream));
   return launch_status();
 }
 

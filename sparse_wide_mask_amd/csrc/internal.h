@@ -79,6 +79,12 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
                         const uint16_t* Wdp, const ReorderView& rv, int T, int d, int F, int n,
                         const uint16_t* residual, uint16_t* H, uint16_t* Y, hipStream_t s);
 
+// The masked SwiGLU FFN in fp32 (vector FMA): H [T, F] fp32 scratch, W_down [F, d]
+// unpacked; any group size and d.
+void launch_ffn_f32(const float* X, const uint8_t* mask, const float* Wg, const float* Wu,
+                    const float* Wd, int T, int d, int F, int n, float* H, float* Y,
+                    hipStream_t s);
+
 // Which projection a K-masked kernel computes.  The kernels are the same; each
 // use gets its own instantiation so profilers report them apart.
 enum KmUse { kUseFfnDown = 0, kUseAttnO = 1 };

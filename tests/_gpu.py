@@ -28,9 +28,16 @@ CANARY = 4096          # bf16 elements placed after every output buffer
 CANARY_BITS = 0x5A5A   # their bit pattern (a finite value no kernel writes by chance)
 
 
+CANARY_BITS32 = 0x5A5A5A5A  # the same for fp32 output buffers
+
+
 def _check_canary(t: torch.Tensor):
     base = getattr(t, "_wide_canary", None)
     if base is not None:
+        if base.dtype == torch.float32:
+            tail = base[t.numel():].view(torch.int32).cpu().numpy().view(np.uint32)
+            assert np.all(tail == CANARY_BITS32), "an output buffer was written past its end"
+            return
         tail = base[t.numel():].view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.all(tail == CANARY_BITS), "an output buffer was written past its end"
 
@@ -48,6 +55,17 @@ def nan_bf16(shape) -> torch.Tensor:
     n = int(np.prod(shape))
     base = torch.empty(n + CANARY, dtype=torch.bfloat16, device=dev())
     base.view(torch.int16)[n:] = np.int16(np.uint16(CANARY_BITS).view(np.int16))
+    base[:n] = float("nan")
+    y = base[:n].view(shape)
+    y._wide_canary = base
+    return y
+
+
+def nan_f32(shape) -> torch.Tensor:
+    """nan_bf16 for an fp32 output buffer."""
+    n = int(np.prod(shape))
+    base = torch.empty(n + CANARY, dtype=torch.float32, device=dev())
+    base.view(torch.int32)[n:] = np.int32(np.uint32(CANARY_BITS32).view(np.int32))
     base[:n] = float("nan")
     y = base[:n].view(shape)
     y._wide_canary = base

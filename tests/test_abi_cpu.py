@@ -71,6 +71,23 @@ def test_validation_before_any_launch(L):
     assert L.wide_pack_kmajor(buf, 4, 16, 256, other, z) == 2   # G = 16: unsupported
 
 
+def test_ffn_f32_validation_and_workspace(L):
+    from sparse_wide_mask_amd import binding as b
+    z = C.c_void_p(0)
+    assert b.ffn_masked_f32_workspace(64, 256, 1024, 16) >= 64 * 1024 * 4   # H in fp32
+    assert b.ffn_masked_f32_workspace(37, 100, 16 * 24, 16) >= 37 * 384 * 4  # any G and d
+    assert b.ffn_masked_f32_workspace(64, 256, 1000, 16) == 0   # d_ff % n != 0
+    assert b.ffn_masked_f32_workspace(64, 256, 1200, 300) == 0  # too many groups
+    f = L.wide_ffn_masked_f32
+    assert f(z, z, z, z, z, 8, 256, 1000, 16, z, z, 0, 0, z) == 1   # d_ff % n != 0
+    assert f(z, z, z, z, z, 8, 256, 1200, 300, z, z, 0, 0, z) == 2  # n > 256
+    assert f(z, z, z, z, z, 8, 256, 1024, 16, z, z, 0, 0, z) == 1   # NULL pointers
+    assert f(z, z, z, z, z, 8, 256, 1024, 16, z, z, 0, 1, z) == 1   # flags != 0
+    assert f(z, z, z, z, z, 0, 256, 1024, 16, z, z, 0, 0, z) == 0   # T == 0: no-op
+    p = [C.c_void_p(16 * (i + 1)) for i in range(7)]  # aligned, never dereferenced
+    assert f(*p[:5], 8, 256, 1024, 16, p[5], p[6], 16, 0, z) == 3   # workspace too small
+
+
 def test_router_validation_before_any_launch(L):
     z = C.c_void_p(0)
     assert L.wide_router_topk(z, z, 8, 256, 16, 8, z, z, z, z) == 1     # NULL X / R / mask
