@@ -376,9 +376,9 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   // records and every load reads 0.  32-bit byte offsets (T d 2 < 2^31).  The
   // residual pointer passes through an empty asm so the loads are not scheduled
   // into the K loop.
-  constexpr int CPR = C::WN / 8;  // 8-column chunks per row of the wave
-  constexpr int RPI = 64 / CPR;   // rows per instruction
-  constexpr int NIT = 32 / RPI;   // instructions per 32-row block
+  constexpr int CPR = C::WN / 8;        // 8-column chunks per row of the wave
+  constexpr int NIT = 32 * CPR / 64;    // instructions per 32-row block: lane l of
+  static_assert(32 * CPR % 64 == 0, "");  // instruction it takes chunk 64 it + l
   constexpr int kHalfWaves = C::kWaves / 2;
   static_assert(kHalfWaves * 32 * C::WN * 4 <= kStages * C::SA * 2 &&
                     kHalfWaves * 32 * C::WN * 4 <= kStages * C::SB * 2,
@@ -401,7 +401,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     u32x4 rv[NIT];
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int r = it * RPI + lane / CPR, c = lane % CPR;
+      const int r = (it * 64 + lane) / CPR, c = (it * 64 + lane) % CPR;
       const int row = wm * C::WM + i * 32 + r, col = n0 + wn * C::WN + c * 8;
       off[it] = row < rows && col < d ? (uint32_t)(sTok[row] * d + col) * 2u : kSkip;
       rv[it] = ldbuf16(rr, off[it]);
@@ -410,7 +410,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     __builtin_amdgcn_wave_barrier();
 #pragma unroll
     for (int it = 0; it < NIT; ++it) {
-      const int r = it * RPI + lane / CPR, c = lane % CPR;
+      const int r = (it * 64 + lane) / CPR, c = (it * 64 + lane) % CPR;
       const f32x4 a0 = *reinterpret_cast<const f32x4*>(sY + r * C::WN + c * 8);
       const f32x4 a1 = *reinterpret_cast<const f32x4*>(sY + r * C::WN + c * 8 + 4);
       const u32x4 q = rv[it];
@@ -430,9 +430,11 @@ constexpr int kDownBM = 256;
 int ffn_down_tile_m() { return kDownBM; }
 
 // K-masked GEMM Y[t] = sum over groups g kept by t of A[t, gG:(g+1)G] Wp[g]^T
-// (+ residual), A token-major [T, F], Wp packed [n, d, G].  The column tile is
-// chosen to fill the 256 CUs best (rounds x tile width).  `tname` labels the
-// launch in the kernel trace (FFN down or attention output projection).
+// (+ residual), A token-major [T, F], Wp packed [n, d, G].  The column tile (256,
+// 192 or 128 columns) is chosen to fill the 256 CUs best (rounds x tile width; the
+// wider tile on a tie): at d = 3072 and 4096 tokens, 192 columns make exactly 256
+// tiles where 256 columns leave a quarter of the CUs idle.  The trace labels the
+// launch as FFN down or attention output projection.
 template <int USE>
 void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderView& rv, int T,
                           int d, int F, int n, const uint16_t* residual, uint16_t* Y,
@@ -442,7 +444,7 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   const int mtiles = (T + kDownBM - 1) / kDownBM;
   int best_bn = 256;
   long best_cost = -1;
-  for (int bn : {256, 128}) {
+  for (int bn : {256, 192, 128}) {
     const long tiles = (long)mtiles * ((d + bn - 1) / bn);
     const long cost = ((tiles + 255) / 256) * bn;
     if (best_cost < 0 || cost < best_cost) best_cost = cost, best_bn = bn;
@@ -452,8 +454,9 @@ void launch_kmask_gemm_as(const uint16_t* A, const uint16_t* Wp, const ReorderVi
   WIDE_TRACE(USE == kUseAttnO ? "attn_o" : "ffn_down", s);
   auto pick = [&](auto gps_tag) {
     constexpr int P = decltype(gps_tag)::value;
-    return best_bn == 256 ? kmask_gemm_prefill<kDownBM, 256, USE, P>
-                          : kmask_gemm_prefill<kDownBM, 128, USE, P>;
+    return best_bn == 256   ? kmask_gemm_prefill<kDownBM, 256, USE, P>
+           : best_bn == 192 ? kmask_gemm_prefill<kDownBM, 192, USE, P>
+                            : kmask_gemm_prefill<kDownBM, 128, USE, P>;
   };
   using G1 = std::integral_constant<int, 1>;
   using G2 = std::integral_constant<int, 2>;
