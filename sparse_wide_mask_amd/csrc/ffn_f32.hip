@@ -34,12 +34,9 @@ __global__ void __launch_bounds__(kF32Threads)
   __shared__ float sG[kF32Cols][kF32Pad];
   __shared__ float sU[kF32Cols][kF32Pad];
   __shared__ uint8_t sKeep[kF32Rows][kF32Cols];
-  __shared__ int sAny;
   const int tid = threadIdx.x, ty = tid / 16, tx = tid % 16;
   const int c0 = blockIdx.x * kF32Cols, t0 = blockIdx.y * kF32Rows;
   const int G = F / n, t = t0 + ty;
-  if (tid == 0) sAny = 0;
-  __syncthreads();
   bool any = false;
   for (int i = tid; i < kF32Rows * kF32Cols; i += kF32Threads) {
     const int r = i / kF32Cols, cc = i % kF32Cols, tt = t0 + r, c = c0 + cc;
@@ -47,9 +44,7 @@ __global__ void __launch_bounds__(kF32Threads)
     sKeep[r][cc] = k ? 1 : 0;
     any = any || k;
   }
-  if (any) sAny = 1;  // every writer writes the same value
-  __syncthreads();
-  if (!sAny) {  // l=0: no token of the tile keeps a group of these channels
+  if (!__syncthreads_or(any)) {  // l=0: no token of the tile keeps a group of these channels
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int c = c0 + tx + 16 * j;
