@@ -44,6 +44,8 @@ SHAPES = [
     (300, 256, 1536, 12, 8, 8, 0.75, "clustered"),
     (64, 256, 1024, 8, 8, 2, 1.0, "ones"),
     (400, 256, 512, 16, 8, 2, 0.5, "router"),   # FFN groups of 32 channels
+    (1, 256, 1024, 8, 8, 2, 0.5, "router"),     # one token
+    (17, 320, 640, 10, 8, 2, 0.5, "bernoulli"),  # a few tokens, 192-column K-masked tiles
     # wide rows: the RMSNorm keeps rows of up to 8192 elements in registers between
     # its two passes and reads longer ones again
     (40, 8192, 1024, 8, 8, 2, 0.5, "router"),
