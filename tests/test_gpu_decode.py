@@ -206,9 +206,13 @@ def test_layer_decode_shapes(B, L, kind):
 
 
 @needs_gpu
-def test_layer_decode_llama31_8b_full():
-    """Llama-3.1-8B layer decode at batch 32 over an 8192-entry cache."""
+@pytest.mark.parametrize("kind,keep,attn_keep", [("router", 0.5, None), ("clustered", 0.5, None),
+                                                 ("router", 0.72, 0.34)])
+def test_layer_decode_llama31_8b_full(kind, keep, attn_keep):
+    """Llama-3.1-8B layer decode at batch 32 over an 8192-entry cache: router top-k masks
+    at 50 %, clustered masks, and the asymmetric keep (3 of 8 head groups, 81 of 112 FFN
+    groups)."""
     dev()
-    log("layer decode 8B B=32 L=8192")
-    c = layer_8b(32, decode=True, L=8192)
+    log(f"layer decode 8B B=32 L=8192 {kind} keep={keep} attn_keep={attn_keep}")
+    c = layer_8b(32, decode=True, L=8192, kind=kind, keep=keep, attn_keep=attn_keep)
     _check_layer_decode(c)
