@@ -112,19 +112,22 @@ def test_layer_all_zero_masks_is_identity():
 
 
 @needs_gpu
-@pytest.mark.parametrize("ffn_group,kind", [(128, "router"), (64, "router"), (128, "clustered")])
-def test_layer_prefill_llama31_8b_sampled(ffn_group, kind):
-    """Full Llama-3.1-8B layer shape at T=8192, masks keeping 50%: router top-k with FFN
-    groups of 128 (112 groups) and of 64 (224 groups, the group-size sweep), and
-    clustered masks (tokens around 8 prototypes: uneven group counts, which the QKV
-    and attention-core kernels share the compute units out by, and few distinct head
-    patterns for the O projection's token sort).  The oracle computes 24 sampled token
+@pytest.mark.parametrize("ffn_group,kind,keep", [(128, "router", 0.5), (64, "router", 0.5),
+                                                (128, "clustered", 0.5), (128, "router", 0.25),
+                                                (128, "bernoulli", 0.75)])
+def test_layer_prefill_llama31_8b_sampled(ffn_group, kind, keep):
+    """Full Llama-3.1-8B layer shape at T=8192: router top-k at 50 % with FFN groups of
+    128 (112 groups) and of 64 (224 groups, the group-size sweep), router top-k at 25 %
+    and Bernoulli at 75 % (the keep sweep), and clustered masks at 50 % (tokens around
+    8 prototypes: uneven group counts, which the QKV and attention-core kernels share
+    the compute units out by, and few distinct head patterns for the O projection's
+    token sort).  The oracle computes 24 sampled token
     rows (keys/values of all tokens).  The attention sublayer (RoPE theta 5e5) and the
     FFN sublayer are also checked alone at this shape on the oracle's intermediate
     inputs (bf16-rounded), where the residual does not hide their error."""
     dev()
-    log(f"layer prefill 8B T=8192 G={ffn_group} {kind} (sampled)")
-    c = layer_8b(8192, ffn_group=ffn_group, kind=kind)
+    log(f"layer prefill 8B T=8192 G={ffn_group} {kind} keep={keep} (sampled)")
+    c = layer_8b(8192, ffn_group=ffn_group, kind=kind, keep=keep)
     m = c["meta"]
     rows = np.sort(np.random.default_rng(2).choice(8192, 24, replace=False))
     rows[0], rows[-1] = 0, 8191
