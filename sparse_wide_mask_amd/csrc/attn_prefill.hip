@@ -69,10 +69,13 @@ struct RopeFreq {
 
 // One tile of the QKV projection: rows row0 .. row0 + rows - 1 of group g's
 // kept-token list (at most 256), and BN / 128 heads of the 256-column tile nt of
-// the group's (q heads | k, v) columns, starting at head hsel0 of that tile.
+// the group's (q heads | k, v) columns, starting at head hsel0 of that tile.  NS
+// LDS stages: 2 for the two-head units, 3 for the one-head halves, whose smaller
+// weight stages leave room for a third (2048-token 8B attention, where every unit
+// is split: QKV 66.1 -> 60.1 us).
 // Waves: 256 / (8 / NWN) rows x one 128-column head each, so the RoPE pair
 // (j, j + 64) of a head sits in one lane.
-template <int BN, int NWN>
+template <int BN, int NWN, int NS>
 WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
                        const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
                        const int32_t* __restrict__ gperm, int T, int d, int n_kv, int r, int g,
@@ -138,10 +141,17 @@ WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restric
   acc.zero();
   const int nk = d / kBK;
   auto live = [&](int) { return rb_live; };
-  if (rb_live == C::kAllRows)
-    acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
-  else
-    acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+  if constexpr (NS == 3) {
+    if (rb_live == C::kAllRows)
+      acc.template run3<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+    else
+      acc.template run3<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+  } else {
+    if (rb_live == C::kAllRows)
+      acc.template run<true, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+    else
+      acc.template run<false, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
+  }
 
   // epilogue.  This wave's 128 columns are one head, hsel = hsel0 + wn of the
   // tile: q head 2*nt + hsel, or k / v.  (With an odd head ratio the last q
@@ -161,9 +171,9 @@ WIDE_DEV void qkv_tile(const uint16_t* __restrict__ X, const uint16_t* __restric
   // this wave's staging rows: WM x 128 bf16, in the A stages (and the B stages
   // for the upper half of the waves when the A stages cannot hold them all)
   constexpr int kRegion = C::WM * kHd;
-  constexpr bool kSplit = C::kWaves * kRegion > kStages * C::SA;
-  static_assert(!kSplit || (C::kWaves / 2 * kRegion <= kStages * C::SA &&
-                            C::kWaves / 2 * kRegion <= kStages * C::SB),
+  constexpr bool kSplit = C::kWaves * kRegion > NS * C::SA;
+  static_assert(!kSplit || (C::kWaves / 2 * kRegion <= NS * C::SA &&
+                            C::kWaves / 2 * kRegion <= NS * C::SB),
                 "q / k staging fits the stages");
   uint16_t* const sQK = kSplit ? (wave < C::kWaves / 2 ? sA : sB) + (wave % (C::kWaves / 2)) * kRegion
                                : sA + wave * kRegion;
@@ -241,9 +251,9 @@ constexpr int kCoreCUs = 256;   // compute units of the chip
 // columns (two heads), U = ceil(count / 256) * ntn of them, dealt in row-major
 // order; P = compute units per group.  The units past the last full round of P,
 // rem = U mod P, are split into two one-head tiles each (256 x 128, eight waves
-// of 32 rows) when the 2 rem halves fit in one round: they then take about half
-// a unit's time instead of a whole second round of units.  The halves come after
-// all full units of every group in the grid.
+// of 32 rows, three LDS stages) when the 2 rem halves fit in one round: they then
+// take about half a unit's time instead of a whole second round of units.  The
+// halves come after all full units of every group in the grid.
 __global__ void __launch_bounds__(kGemmThreads, 1)
     attn_qkv_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wq,
                      const uint16_t* __restrict__ Wk, const uint16_t* __restrict__ Wv,
@@ -253,7 +263,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
                      uint16_t* __restrict__ Vt) {
   using Big = TileCfg<256, 256>;
   using Half = TileCfg<256, 128, 8, 1>;
-  constexpr int kBig = kStages * (Big::SA + Big::SB), kHalf = kStages * (Half::SA + Half::SB);
+  constexpr int kBig = kStages * (Big::SA + Big::SB), kHalf = 3 * (Half::SA + Half::SB);
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kBig > kHalf ? kBig : kHalf];
   __shared__ int sTok[256];
   const int ntn = (r + 1) / 2 + 1;
@@ -333,11 +343,12 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   const int mt = unit / ntn, nt = unit % ntn;
   const int row0 = mt * 256, rows = min(256, cnt - row0);
   if (half < 0)
-    qkv_tile<256, kGemmWN>(X, Wq, Wk, Wv, gperm, T, d, n_kv, r, g, row0, rows, nt, 0, vtp,
-                           log2_theta, sbuf, sbuf + kStages * Big::SA, sTok, Qc, Kc, Vt);
+    qkv_tile<256, kGemmWN, kStages>(X, Wq, Wk, Wv, gperm, T, d, n_kv, r, g, row0, rows, nt, 0,
+                                    vtp, log2_theta, sbuf, sbuf + kStages * Big::SA, sTok, Qc,
+                                    Kc, Vt);
   else
-    qkv_tile<128, 1>(X, Wq, Wk, Wv, gperm, T, d, n_kv, r, g, row0, rows, nt, half, vtp,
-                     log2_theta, sbuf, sbuf + kStages * Half::SA, sTok, Qc, Kc, Vt);
+    qkv_tile<128, 1, 3>(X, Wq, Wk, Wv, gperm, T, d, n_kv, r, g, row0, rows, nt, half, vtp,
+                        log2_theta, sbuf, sbuf + 3 * Half::SA, sTok, Qc, Kc, Vt);
 }
 
 // ---------------------------------------------------------- attention core
