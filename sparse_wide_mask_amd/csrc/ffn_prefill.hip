@@ -44,11 +44,6 @@ WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& m
   nt = c % ntn;
 }
 
-#define WIDE_STAGE_ARRAYS(C)                                               \
-  __shared__ __attribute__((aligned(16))) uint16_t sA[kStages * C::SA];      \
-  __shared__ __attribute__((aligned(16))) uint16_t sB[kStages * C::SB];      \
-  const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB)
-
 // A group's last row tile with at most this many rows is left by ffn_up_prefill
 // to ffn_up_tail (64-row tiles, three LDS stages).  Such a tile streams all of the
 // group's weight columns for a few rows; with two 256-row stages in flight it is
