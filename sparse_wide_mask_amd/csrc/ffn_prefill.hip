@@ -175,7 +175,11 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
                    const int32_t* __restrict__ gperm, int T, int d, int F, int n, int G,
                    int mtiles, int ntn, int n_main, uint16_t* __restrict__ H) {
   using C = TileCfg<BM, BN, NWM, NWN>;
-  constexpr int kMain = kStages * (C::SA + C::SB);
+  // LDS stages of the row tiles: three when the weight tile is at most 128 columns
+  // (groups of 64 or 32 channels; at the 8B layer with groups of 64 FFN up went
+  // 1137 -> 944 us), two beside 256-column weight tiles, where a third does not fit
+  constexpr int NSM = BN <= 128 ? 3 : kStages;
+  constexpr int kMain = NSM * (C::SA + C::SB);
   constexpr int kTail = TAILS ? kTailStages * (TailCfg::SA + TailCfg::SB) : 0;
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kMain > kTail ? kMain : kTail];
   __shared__ int sTok[BM];
@@ -199,8 +203,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   if (row0 >= cnt) return;  // l=0: no kept token left in this tile
   const int rows = min(BM, cnt - row0);
   if (TAILS && row0 + BM >= cnt && rows <= kUpTailRows) return;  // a tail work-group's
-  ffn_up_tile<BM, BN, NWM, NWN, kStages>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
-                                          sbuf + kStages * C::SA, sTok, H);
+  ffn_up_tile<BM, BN, NWM, NWN, NSM>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
+                                      sbuf + NSM * C::SA, sTok, H);
 }
 
 // GPS = groups per 64-wide K slice: 1 for groups of 64 or more channels; 2 for
