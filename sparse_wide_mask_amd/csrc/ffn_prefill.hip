@@ -51,8 +51,11 @@ WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& m
 constexpr int kUpTailRows = 64;
 
 // One output tile of the up projection: rows row0 .. row0 + rows - 1 of group g's
-// kept-token list, channel tile nt.  NS = LDS stages (2 or 3).
-template <int BM, int BN, int NWM, int NWN, int NS>
+// kept-token list, channel tile nt.  NSA / NSB = LDS stages of A and B (2 / 2,
+// 3 / 3, or 2 / 3).  TL: the tile's token list is staged in LDS (sTok); without
+// it (when the stages fill the LDS) each lane reads the tokens of its own load
+// and store rows from group_perm.
+template <int BM, int BN, int NWM, int NWN, int NSA, int NSB, bool TL>
 WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
                           const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gperm,
                           int T, int d, int F, int G, int g, int row0, int rows, int nt,
@@ -62,9 +65,14 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
   constexpr int BNH = BN / 2;  // channels per tile (gate and up each)
   const uint32_t ldsA = lds_addr(sA), ldsB = lds_addr(sB);
 
+  constexpr bool kTokLds = TL;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / NWN, wn = wave % NWN;
-  for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gperm[(size_t)g * T + row0 + r] : -1;
-  __syncthreads();
+  const int32_t* gp = gperm + (size_t)g * T + row0;
+  if constexpr (kTokLds) {
+    for (int r = tid; r < BM; r += C::kThreads) sTok[r] = r < rows ? gp[r] : -1;
+    __syncthreads();
+  }
+  auto tok = [&](int r) { return kTokLds ? sTok[r] : (r < rows ? gp[r] : -1); };
 
   const int chunk8 = dma_chunk(dma_row<NW>(wave, 0, lane), lane) * 8;
   const i32x4 rX = make_srd(X, (uint32_t)T * d * 2u);
@@ -73,8 +81,8 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
   uint32_t aOff[C::A_INST];
 #pragma unroll
   for (int q = 0; q < C::A_INST; ++q) {
-    const int tok = sTok[dma_row<NW>(wave, q, lane)];
-    aOff[q] = tok >= 0 ? (uint32_t)(tok * d + chunk8) * 2u : kSkip;  // l=1: no load
+    const int t = tok(dma_row<NW>(wave, q, lane));
+    aOff[q] = t >= 0 ? (uint32_t)(t * d + chunk8) * 2u : kSkip;  // l=1: no load
   }
   // B row nrow: wave column nrow / WN; 32-row slabs alternate gate / up so that a
   // lane holds gate and up of the same channel.
@@ -88,15 +96,29 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
     bOff[q] = (uint32_t)((g * G + ch) * d + chunk8) * 2u;
     bUp[q] = __builtin_amdgcn_readfirstlane(blk & 1);
   }
-  auto issue = [&](int kt, int st) {
-    const uint32_t a = ldsA + st * C::SA * 2, b = ldsB + st * C::SB * 2;
-    const uint32_t kb = (uint32_t)kt * kBK * 2u;
+  auto issueA = [&](int kt, int st) {
+    const uint32_t a = ldsA + st * C::SA * 2, kb = (uint32_t)kt * kBK * 2u;
 #pragma unroll
     for (int q = 0; q < C::A_INST; ++q) lds_dma16(rX, dma_dst<NW>(a, wave, q), aOff[q] + kb);
+  };
+  auto issueB = [&](int kt, int st) {
+    const uint32_t b = ldsB + st * C::SB * 2, kb = (uint32_t)kt * kBK * 2u;
 #pragma unroll
     for (int q = 0; q < C::B_INST; ++q)
       lds_dma16(bUp[q] ? rU : rG, dma_dst<NW>(b, wave, q), bOff[q] + kb);
   };
+  auto issue = [&](int kt, int st) {
+    issueA(kt, st);
+    issueB(kt, st);
+  };
+  // store rows of this lane in the epilogue (below): their tokens, read now
+  constexpr int HCH = C::WN / 2;  // channels of the wave
+  constexpr int CPR = HCH / 8;    // 16-byte chunks per row
+  constexpr int RPI = 64 / CPR;   // rows per store instruction
+  constexpr int NST = C::WM / RPI;
+  int stTok[NST];
+#pragma unroll
+  for (int it = 0; it < NST; ++it) stTok[it] = kTokLds ? 0 : tok(wm * C::WM + it * RPI + lane / CPR);
 
   uint32_t rb_live = 0;
 #pragma unroll
@@ -109,7 +131,9 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
   auto live = [&](int) { return rb_live; };
   auto run = [&](auto all_tag) {
     constexpr bool ALL = decltype(all_tag)::value;
-    if constexpr (NS == 3)
+    if constexpr (NSA == 2 && NSB == 3)
+      acc.template run_a2b3<ALL, C::B_INST>(nk, sA, sB, wm, wn, lane, issueA, issueB, live);
+    else if constexpr (NSA == 3)
       acc.template run3<ALL, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
     else
       acc.template run<ALL, C::LOADS>(nk, sA, sB, wm, wn, lane, issue, live);
@@ -126,10 +150,7 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
   // lane per store (the accumulator layout) made the epilogue cost as much as a
   // tenth of the kernel.  32-bit byte offsets into H (T F 2 < 2^31); rows past the
   // count exist only in a group's last tile and are not written.
-  constexpr int HCH = C::WN / 2;  // channels of the wave
-  constexpr int CPR = HCH / 8;    // 16-byte chunks per row
-  constexpr int RPI = 64 / CPR;   // rows per store instruction
-  static_assert(NW * C::WM * HCH <= NS * C::SA && C::WM % RPI == 0, "epilogue tile fits the stages");
+  static_assert(NW * C::WM * HCH <= NSA * C::SA && C::WM % RPI == 0, "epilogue tile fits the stages");
   __syncthreads();
   uint16_t* sH = sA + wave * C::WM * HCH;
 #pragma unroll
@@ -152,7 +173,8 @@ WIDE_DEV void ffn_up_tile(const uint16_t* __restrict__ X, const uint16_t* __rest
     const int r = it * RPI + lane / CPR, c = lane % CPR;
     const int row = wm * C::WM + r;
     const u32x4 v = *reinterpret_cast<const u32x4*>(sH + r * HCH + c * 8);
-    const uint32_t off = row < rows ? (uint32_t)(sTok[row] * F + chbase + c * 8) * 2u : kSkip;
+    const int t = kTokLds ? (row < rows ? sTok[row] : -1) : stTok[it];
+    const uint32_t off = t >= 0 ? (uint32_t)(t * F + chbase + c * 8) * 2u : kSkip;
     __builtin_amdgcn_raw_buffer_store_b128(v, hr, (int)off, 0, kNtStore);
   }
 }
@@ -168,7 +190,7 @@ static_assert(TailCfg::kThreads == kGemmThreads, "one launch shape");
 // work-groups after them take exactly those tails, one per (group, channel tile).
 // Being last in the grid, the tails run on the compute units that finish their
 // share of full tiles first.
-template <int BM, int BN, int NWM, int NWN, bool TAILS>
+template <int BM, int BN, int NWM, int NWN, bool TAILS, bool B3>
 __global__ void __launch_bounds__(kGemmThreads, 1)
     ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
                    const uint16_t* __restrict__ Wu, const int32_t* __restrict__ gcount,
@@ -177,12 +199,17 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   using C = TileCfg<BM, BN, NWM, NWN>;
   // LDS stages of the row tiles: three when the weight tile is at most 128 columns
   // (groups of 64 or 32 channels; at the 8B layer with groups of 64 FFN up went
-  // 1137 -> 944 us), two beside 256-column weight tiles, where a third does not fit
-  constexpr int NSM = BN <= 128 ? 3 : kStages;
-  constexpr int kMain = NSM * (C::SA + C::SB);
+  // 1137 -> 944 us), two beside 256-column weight tiles, where a third does not
+  // fit.  B3: three stages of the 256-column weight tiles beside two of A, which
+  // fill the LDS, so the tiles' token lists stay in registers (TL false).
+  constexpr int NSA = BN <= 128 ? 3 : kStages;
+  constexpr int NSB = BN <= 128 || B3 ? 3 : kStages;
+  constexpr bool TL = !B3;
+  constexpr int kMain = NSA * C::SA + NSB * C::SB;
   constexpr int kTail = TAILS ? kTailStages * (TailCfg::SA + TailCfg::SB) : 0;
-  __shared__ __attribute__((aligned(16))) uint16_t sbuf[kMain > kTail ? kMain : kTail];
-  __shared__ int sTok[BM];
+  constexpr int kStg = kMain > kTail ? kMain : kTail;
+  __shared__ __attribute__((aligned(16))) uint16_t sbuf[kStg + (TL ? 2 * BM : 0)];
+  int* sTok = reinterpret_cast<int*>(sbuf + kStg);  // the token list (TL only)
   if (TAILS && (int)blockIdx.x >= n_main) {
     const int id = blockIdx.x - n_main;
     const int g = id / ntn, nt = id % ntn;
@@ -191,7 +218,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
     const int row0 = (cnt - 1) / BM * BM;  // the group's last row tile
     const int rows = cnt - row0;
     if (rows > kUpTailRows) return;  // a large last tile is a row tile like the others
-    ffn_up_tile<kUpTailRows, 256, kTailNWM, kTailNWN, kTailStages>(
+    ffn_up_tile<kUpTailRows, 256, kTailNWM, kTailNWN, kTailStages, kTailStages, TL>(
         X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
         sbuf + kTailStages * TailCfg::SA, sTok, H);
     return;
@@ -203,8 +230,8 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   if (row0 >= cnt) return;  // l=0: no kept token left in this tile
   const int rows = min(BM, cnt - row0);
   if (TAILS && row0 + BM >= cnt && rows <= kUpTailRows) return;  // a tail work-group's
-  ffn_up_tile<BM, BN, NWM, NWN, NSM>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
-                                      sbuf + NSM * C::SA, sTok, H);
+  ffn_up_tile<BM, BN, NWM, NWN, NSA, NSB, TL>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt,
+                                               sbuf, sbuf + NSA * C::SA, sTok, H);
 }
 
 // GPS = groups per 64-wide K slice: 1 for groups of 64 or more channels; 2 for
@@ -498,7 +525,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     {
       WIDE_TRACE("ffn_up_prefill", s);
       const int n_main = n * mtiles * ntn;
-      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, true><<<n_main + n * ntn, kGemmThreads, 0, s>>>(
+      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, true, true><<<n_main + n * ntn, kGemmThreads, 0, s>>>(
           X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   } else if (G % 64 == 0) {
@@ -507,7 +534,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     {
       WIDE_TRACE("ffn_up_prefill", s);
       const int n_main = n * mtiles * ntn;
-      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, false><<<n_main, kGemmThreads, 0, s>>>(
+      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, false, false><<<n_main, kGemmThreads, 0, s>>>(
           X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   } else {
@@ -518,7 +545,7 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     {
       WIDE_TRACE("ffn_up_prefill", s);
       const int n_main = n * mtiles * ntn;
-      ffn_up_prefill<BM, BN, 8, 1, false><<<n_main, kGemmThreads, 0, s>>>(
+      ffn_up_prefill<BM, BN, 8, 1, false, false><<<n_main, kGemmThreads, 0, s>>>(
           X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   }

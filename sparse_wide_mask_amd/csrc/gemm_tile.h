@@ -6,7 +6,8 @@
 // wave's LDS reads and waits overlap the other's MFMAs.
 //
 // Global -> LDS uses buffer loads that write LDS directly (no VGPR staging).  Two
-// LDS stages: slice kt+1 loads while slice kt computes.  One load instruction of
+// LDS stages: slice kt+1 loads while slice kt computes (variants: three stages for
+// tiles that leave room, and two A stages with three B stages).  One load instruction of
 // a wave fills 8 rows of 128 bytes (a whole cache line per row); 16 rows of 64
 // bytes per instruction, as 32-wide slices give, is about 3x slower from L2.  A
 // lane whose buffer offset is past num_records reads zeros without touching
@@ -207,6 +208,61 @@ struct WaveAcc {
       __builtin_amdgcn_sched_barrier(0);
       mma<ALL>(hi, lv);
       __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+
+  // Two A stages and three B stages (at 256 x 256 exactly the 160 KB of LDS):
+  // slice kt+1's A rows and slice kt+2's B rows load while slice kt computes, so
+  // the B stream has two slices of lead.  A stage of slice kt = kt mod 2, B stage
+  // = kt mod 3; both refill stages that slice kt-1 used.  Per slice a wave issues
+  // its A loads before its B loads, so waiting for vmcnt <= BLOADS before slice
+  // kt+1 leaves only slice kt+2's B loads in flight.
+  template <bool ALL, int BLOADS, class IssueA, class IssueB, class Live>
+  WIDE_DEV void run_a2b3(int nk, const uint16_t* sA, const uint16_t* sB, int wm, int wn,
+                         int lane, IssueA&& issueA, IssueB&& issueB, Live&& live) {
+    if (nk <= 0) return;
+    issueA(0, 0);
+    issueB(0, 0);
+    if (nk > 1) {
+      issueB(1, 1);
+      stage_barrier<BLOADS>();
+    } else {
+      stage_barrier<0>();
+    }
+    Frags lo, hi;
+    read(lo, sA, sB, wm, wn, lane, 0);
+    int sb = 0;
+    for (int kt = 0; kt < nk; ++kt) {
+      const int sa = kt & 1;
+      const uint32_t lv = ALL ? C::kAllRows : live(kt);
+      const uint16_t* cA = sA + sa * C::SA;
+      const uint16_t* cB = sB + sb * C::SB;
+      const int sb1 = sb == 2 ? 0 : sb + 1, sb2 = sb1 == 2 ? 0 : sb1 + 1;
+      if (kt + 1 < nk) issueA(kt + 1, sa ^ 1);
+      if (kt + 2 < nk) issueB(kt + 2, sb2);
+      read(hi, cA, cB, wm, wn, lane, 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(lo, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      read(lo, cA, cB, wm, wn, lane, 2);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(hi, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      read(hi, cA, cB, wm, wn, lane, 3);
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(lo, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      if (kt + 1 < nk) {
+        if (kt + 2 < nk)
+          stage_barrier<BLOADS>();
+        else
+          stage_barrier<0>();
+        read(lo, sA + (sa ^ 1) * C::SA, sB + sb1 * C::SB, wm, wn, lane, 0);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mma<ALL>(hi, lv);
+      __builtin_amdgcn_sched_barrier(0);
+      sb = sb1;
     }
   }
 
