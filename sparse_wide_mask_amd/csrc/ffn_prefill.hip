@@ -44,11 +44,14 @@ WIDE_DEV void up_tile(int bid, int n_groups, int mtiles, int ntn, int& g, int& m
   nt = c % ntn;
 }
 
-// A group's last row tile with at most this many rows is left by ffn_up_prefill
-// to ffn_up_tail (64-row tiles, three LDS stages).  Such a tile streams all of the
-// group's weight columns for a few rows; with two 256-row stages in flight it is
-// bound by load latency and takes most of a full tile's time, in the last round.
+// A group's last row tile with at most kUpTailParts * kUpTailRows rows is left by
+// the row tiles to the tail work-groups (64-row tiles, three LDS stages; a tile of
+// 65-128 rows is two of them, on two compute units).  Such a tile streams all of
+// the group's weight columns for few rows; as a 256-row tile it is bound by load
+// latency, takes most of a full tile's time and, coming last in the raster, adds a
+// round of its own (masks whose counts spread past 64 rows over a multiple of 256).
 constexpr int kUpTailRows = 64;
+constexpr int kUpTailParts = 2;
 
 // One output tile of the up projection: rows row0 .. row0 + rows - 1 of group g's
 // kept-token list, channel tile nt.  NSA / NSB = LDS stages of A and B (2 / 2,
@@ -186,10 +189,11 @@ using TailCfg = TileCfg<kUpTailRows, 256, kTailNWM, kTailNWN>;
 static_assert(TailCfg::kThreads == kGemmThreads, "one launch shape");
 
 // The up projection.  Work-groups below n_main take the row tiles (up_tile) but,
-// when TAILS, not a group's last tile of at most kUpTailRows rows; the n * ntn
-// work-groups after them take exactly those tails, one per (group, channel tile).
-// Being last in the grid, the tails run on the compute units that finish their
-// share of full tiles first.
+// when TAILS, not a group's last tile of at most kUpTailParts * kUpTailRows rows;
+// the kUpTailParts * n * ntn work-groups after them take exactly those tails, one
+// per (64-row part, group, channel tile), first parts first.  Being last in the
+// grid, the tails run on the compute units that finish their share of full tiles
+// first.
 template <int BM, int BN, int NWM, int NWN, bool TAILS, bool B3>
 __global__ void __launch_bounds__(kGemmThreads, 1)
     ffn_up_prefill(const uint16_t* __restrict__ X, const uint16_t* __restrict__ Wg,
@@ -211,15 +215,16 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   __shared__ __attribute__((aligned(16))) uint16_t sbuf[kStg + (TL ? 2 * BM : 0)];
   int* sTok = reinterpret_cast<int*>(sbuf + kStg);  // the token list (TL only)
   if (TAILS && (int)blockIdx.x >= n_main) {
-    const int id = blockIdx.x - n_main;
-    const int g = id / ntn, nt = id % ntn;
+    const int id = blockIdx.x - n_main, per = n * ntn;
+    const int part = id / per, g = (id % per) / ntn, nt = id % ntn;
     const int cnt = gcount[g];
     if (cnt == 0) return;
-    const int row0 = (cnt - 1) / BM * BM;  // the group's last row tile
-    const int rows = cnt - row0;
-    if (rows > kUpTailRows) return;  // a large last tile is a row tile like the others
+    const int last = (cnt - 1) / BM * BM;  // the group's last row tile
+    if (cnt - last > kUpTailParts * kUpTailRows) return;  // a row tile like the others
+    const int row0 = last + part * kUpTailRows;
+    if (row0 >= cnt) return;
     ffn_up_tile<kUpTailRows, 256, kTailNWM, kTailNWN, kTailStages, kTailStages, TL>(
-        X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt, sbuf,
+        X, Wg, Wu, gperm, T, d, F, G, g, row0, min(kUpTailRows, cnt - row0), nt, sbuf,
         sbuf + kTailStages * TailCfg::SA, sTok, H);
     return;
   }
@@ -229,7 +234,7 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   const int row0 = mt * BM;
   if (row0 >= cnt) return;  // l=0: no kept token left in this tile
   const int rows = min(BM, cnt - row0);
-  if (TAILS && row0 + BM >= cnt && rows <= kUpTailRows) return;  // a tail work-group's
+  if (TAILS && row0 + BM >= cnt && rows <= kUpTailParts * kUpTailRows) return;  // the tails
   ffn_up_tile<BM, BN, NWM, NWN, NSA, NSB, TL>(X, Wg, Wu, gperm, T, d, F, G, g, row0, rows, nt,
                                                sbuf, sbuf + NSA * C::SA, sTok, H);
 }
@@ -525,7 +530,8 @@ void launch_ffn_prefill(const uint16_t* X, const uint16_t* Wg, const uint16_t* W
     {
       WIDE_TRACE("ffn_up_prefill", s);
       const int n_main = n * mtiles * ntn;
-      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, true, true><<<n_main + n * ntn, kGemmThreads, 0, s>>>(
+      ffn_up_prefill<BM, BN, kGemmWM, kGemmWN, true, true>
+          <<<n_main + kUpTailParts * n * ntn, kGemmThreads, 0, s>>>(
           X, Wg, Wu, rv.count, rv.perm, T, d, F, n, G, mtiles, ntn, n_main, H);
     }
   } else if (G % 64 == 0) {

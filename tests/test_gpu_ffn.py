@@ -102,6 +102,28 @@ def test_ffn_prefill_shapes(T, d, F, n, keep, kind):
 
 
 @needs_gpu
+def test_ffn_up_last_tile_sizes():
+    """Per-group kept counts placed at the boundaries of the up projection's row
+    tiles (256 rows) and of its tail parts (64-row tiles for a last tile of at most
+    128 rows): 0, 1, 64, 65, 128, 129, 356 and 639 kept tokens in the 8 groups of
+    128 channels, so last tiles of 1, 64, 65, 128, 129, 100 and 127 rows."""
+    dev()
+    T, d, F, n = 700, 256, 1024, 8
+    counts = [0, 1, 64, 65, 128, 129, 356, 639]
+    log(f"ffn prefill T={T} per-group counts {counts}")
+    c = ffn_case("ffn_tail_sizes", T, d, F, n, 0.5, "bernoulli")
+    r = np.random.default_rng(11)
+    mask = np.zeros((T, n), np.uint8)
+    for g, k in enumerate(counts):
+        mask[r.choice(T, k, replace=False), g] = 1
+    c["mask"] = mask
+    got = _gpu_ffn(c)
+    ref = ffn_masked(c["X"], c["mask"], c["W_gate"], c["W_up"], c["W_down"])
+    assert rel_err(got, ref) <= TOL
+    assert np.array_equal(got[mask.sum(1) == 0], np.zeros((int((mask.sum(1) == 0).sum()), d)))
+
+
+@needs_gpu
 def test_ffn_prefill_llama32_3b_sampled():
     """Full Llama-3.2-3B FFN prefill shape (T=4096, d=3072, d_ff=8192, 64 groups,
     router top-k 32 of 64); the oracle computes 96 sampled token rows (rows are
