@@ -7,7 +7,7 @@
 // Everything for one or two masks runs in one launch of 1024-thread work-groups,
 // each taking one role (no host synchronisation, no dependencies inside the
 // launch: every role reads the mask bytes, or the packed words when those are the
-// input):
+// input; a mask of more than 4 MB is packed by a launch of its own first):
 //   sort    one work-group per sorted mask: a stable counting sort of the tokens
 //           by their pattern (n <= 8) and the unions of tiles of that order;
 //   groups  one per group: chunks of 64 tokens (lane = token), a ballot per chunk,
@@ -410,13 +410,19 @@ __global__ void __launch_bounds__(kRoThreads) __attribute__((amdgpu_waves_per_eu
     return;
 }
 
-static RoGrid ro_grid(int T, const MaskJob* const (&J)[2], const NormJob* norm, size_t& lds) {
+// Masks of more bytes than this (an XCD's L2) are packed by a launch of their own
+// first (see launch_reorder_jobs).
+constexpr size_t kBytesMaxMask = size_t(4) << 20;
+
+static RoGrid ro_grid(int T, const MaskJob* const (&J)[2], const NormJob* norm, bool pack_only,
+                      size_t& lds) {
   RoGrid g{};
   lds = 64;
   for (int q = 0; q < 2; ++q) {
     const MaskJob* j = J[q];
     if (!j) continue;
     g.pack[q] = j->mask ? (T + kPackPerWg - 1) / kPackPerWg : 0;
+    if (pack_only) continue;
     const bool sort = j->order != nullptr;
     g.sort[q] = sort ? 1 : 0;
     g.groups[q] = j->n;
@@ -424,7 +430,7 @@ static RoGrid ro_grid(int T, const MaskJob* const (&J)[2], const NormJob* norm, 
     if (sort) lds = std::max(lds, RoLds::sort(T));
     lds = std::max(lds, RoLds::groups(T));
   }
-  g.norm = norm ? (T + kNormPerWg - 1) / kNormPerWg : 0;
+  g.norm = norm && !pack_only ? (T + kNormPerWg - 1) / kNormPerWg : 0;
   return g;
 }
 
@@ -441,15 +447,32 @@ void launch_reorder_jobs(int T, const MaskJob* a, const MaskJob* b, const NormJo
       reinterpret_cast<const void*>(&reorder_all), hipFuncAttributeMaxDynamicSharedMemorySize,
       (int)RoLds::sort(WIDE_MAX_TOKENS));
   (void)attr;
-  // Every role reads the mask bytes (or the packed words when those are the
-  // input), also for many groups: a group's work-group then reads one byte per
-  // token at a stride of n bytes, and the 112 groups of the 8B FFN pull the 0.9 MB
-  // mask through L2 about 100 times, which costs the launch ≈7 us beside the norm
-  // rows; packing such a mask in a launch of its own first took ≈11 us.
+  // The roles read the mask bytes (or the packed words when those are the input).
+  // A group's work-group reads one byte per token at a stride of n bytes, so the
+  // 112 groups of the 8B FFN pull the 0.9 MB mask through L2 about 100 times,
+  // which costs the launch ≈7 us beside the norm rows; packing it in a launch of
+  // its own first took ≈11 us.  A mask larger than an XCD's L2 would be re-read
+  // from beyond it by every group, so such a mask is still packed first and the
+  // roles of the main launch read its words.
   const MaskJob none{};
+  MaskJob local[2];
   const MaskJob* J[2] = {a, b};
+  const MaskJob* P[2] = {nullptr, nullptr};  // jobs packed first
+  for (int q = 0; q < 2; ++q)
+    if (J[q] && J[q]->mask && (size_t)T * J[q]->n > kBytesMaxMask) {
+      P[q] = J[q];
+      local[q] = *J[q];
+      local[q].mask = nullptr;  // the main launch reads the packed words
+      J[q] = &local[q];
+    }
   size_t lds = 0;
-  const RoGrid g = ro_grid(T, J, norm, lds);
+  if (P[0] || P[1]) {
+    WIDE_TRACE("reorder_pack", s);
+    const RoGrid g = ro_grid(T, P, nullptr, true, lds);
+    reorder_all<<<ro_blocks(g), kRoThreads, lds, s>>>(P[0] ? *P[0] : none, P[1] ? *P[1] : none,
+                                                      NormJob{}, T, g);
+  }
+  const RoGrid g = ro_grid(T, J, norm, false, lds);
   WIDE_TRACE(norm ? "norm_reorder" : "reorder", s);
   reorder_all<<<ro_blocks(g), kRoThreads, lds, s>>>(J[0] ? *J[0] : none, J[1] ? *J[1] : none,
                                                     norm ? *norm : NormJob{}, T, g);

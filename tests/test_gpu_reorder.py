@@ -63,10 +63,11 @@ def test_reorder_without_unions_bit_exact(T, n, kind):
 
 
 @needs_gpu
-@pytest.mark.parametrize("T,n", [(8192, 112), (8192, 8), (65536, 8)])
+@pytest.mark.parametrize("T,n", [(8192, 112), (8192, 8), (65536, 8), (32768, 160)])
 def test_reorder_full_size(T, n):
-    """The layer's mask sizes (8192 tokens x 112 FFN / 8 attention groups), and the
-    maximum token count; the oracle checks group 0..n-1 exactly."""
+    """The layer's mask sizes (8192 tokens x 112 FFN / 8 attention groups), the
+    maximum token count, and a mask of more than 4 MB (packed by a launch of its own
+    before the other roles); the oracle checks group 0..n-1 exactly."""
     dev()
     log(f"reorder full T={T} n={n}")
     m = make_mask(f"reorder_full_{T}_{n}", T, n, 0.5, "topk")
