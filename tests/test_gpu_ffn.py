@@ -85,9 +85,10 @@ SHAPES = [
     (1100, 512, 1024, 32, 0.75, "bernoulli"),
     (257, 256, 2048, 64, 0.25, "clustered"),
     (129, 384, 256, 8, 1.0, "ones"),
-    # uneven group counts over a multiple of 8 groups: FFN up deals the groups to the
-    # XCDs by count
+    # uneven group counts over a multiple of 8 groups
     (2000, 256, 2048, 16, 0.5, "clustered"),
+    # groups of 256 channels: two FFN up channel tiles per group, each with its own tails
+    (600, 256, 2048, 8, 0.5, "bernoulli"),
 ]
 
 
