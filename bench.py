@@ -66,6 +66,8 @@ def measured_keep(c):
 class LayerPrefill:
     """Llama-3.1-8B-shaped decoder layer, prefill."""
 
+    sort_ffn = False  # WIDE_FLAG_FFN_TOKEN_SORT (bench.py --sort-ffn)
+
     def __init__(self, T=8192, keep=0.5, kind="router", ffn_group=128, attn_keep=None):
         from synth.workloads import layer_8b
         self.name = layer_name("layer_prefill_8b", keep, kind, ffn_group, attn_keep)
@@ -99,7 +101,7 @@ class LayerPrefill:
         am, fm = self.ones if ones else self.masks
         self.wide.layer_masked(self.X, am, fm, self.W, n_q=m["n_q"], n_kv=m["n_kv"], head_dim=HD,
                                rope_theta=m["rope_theta"], eps=m["eps"], out=self.Y,
-                               workspace=self.ws)
+                               workspace=self.ws, sort_ffn_tokens=self.sort_ffn)
 
     def work(self, ones=False):
         """Algorithmic FLOPs per launch of each kernel, from the actual masks."""
@@ -171,7 +173,8 @@ class LayerPrefillRouted(LayerPrefill):
         self.wide.layer_masked_routed(self.X, self.Ra, ka, self.Rf, kf, self.W, n_q=m["n_q"],
                                       n_kv=m["n_kv"], n_ffn=m["n_ffn"], head_dim=HD,
                                       rope_theta=m["rope_theta"], eps=m["eps"], out=self.Y,
-                                      attn_mask=am, ffn_mask=fm, workspace=self.ws)
+                                      attn_mask=am, ffn_mask=fm, workspace=self.ws,
+                                      sort_ffn_tokens=self.sort_ffn)
 
     def work(self, ones=False):
         # counted from the masks the GPU routers chose (read back after the run)
@@ -867,6 +870,9 @@ def main():
     ap.add_argument("--attn-keep", type=float, default=None,
                     help="layer workloads: the attention mask's own keep ratio (--keep is then "
                          "the FFN's)")
+    ap.add_argument("--sort-ffn", action="store_true",
+                    help="layer prefill workloads: sort the tokens of the FFN down projection "
+                         "by the pattern of their first 8 FFN groups (WIDE_FLAG_FFN_TOKEN_SORT)")
     ap.add_argument("--ffn-group", type=int, default=128,
                     help="layer workloads: channels per FFN group (d_ff 14336 = groups x this)")
     ap.add_argument("--launch", choices=("eager", "graph"), default="eager",
@@ -930,6 +936,12 @@ def main():
         W = FfnPrefill(ffn_group=args.ffn_group)
     else:
         W = WORKLOADS[args.workload]()
+    if args.sort_ffn:
+        if not isinstance(W, LayerPrefill):
+            raise SystemExit("--sort-ffn applies to the layer prefill workloads")
+        W.sort_ffn = True
+        W.name += "_sortffn"
+        W.config.update(workload=W.name, ffn_token_sort=True)
     W.upload(torch, wide, bf16, u8)
     stream = torch.cuda.current_stream()
     graph = args.launch == "graph"

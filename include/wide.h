@@ -29,7 +29,7 @@
  *     returns an error has launched nothing.  T == 0 is a no-op returning WIDE_OK.
  *   - Inputs are never written.  Outputs must not alias inputs.  Every element of
  *     every output is written on success; dropped groups give an exact 0.
- *   - `flags` must be 0.
+ *   - `flags` must be 0, except where a call names the bits it takes.
  *   - Concurrent calls are safe on different streams with distinct workspaces.
  */
 #ifndef WIDE_H
@@ -54,6 +54,19 @@ enum { WIDE_PREFILL = 0, WIDE_DECODE = 1 };
 /* Limits: 1 <= n_groups <= 256, T <= 65536 (prefill); attention decode batch
  * <= 64 with at most 8 query heads per KV head.  A "decode" FFN call with more
  * than 64 tokens runs the prefill kernels. */
+/* flags bit of wide_ffn_masked, wide_layer_masked and wide_layer_masked_routed
+ * (prefill): besides the per-group partition, sort the tokens by the pattern of
+ * their first 8 FFN groups (reflected Gray-code order) and run the K-masked FFN
+ * down projection over that order, each 256-token tile over the union of its own
+ * tokens' groups (the mask-pattern token permutation of gist.science technical
+ * summary §2.B, and franklineh.com "Considerations for Implementation": tokens
+ * with similar masks share the tiles whose dropped groups are skipped).  It pays
+ * when masks cluster (tiles of one prototype share dropped blocks); with random
+ * masks every tile keeps every group either way.  Results are bit-identical with
+ * and without it: a token's sum runs over its own kept groups in ascending order
+ * in any tile. */
+#define WIDE_FLAG_FFN_TOKEN_SORT 0x2u
+
 #define WIDE_MAX_GROUPS 256
 #define WIDE_MAX_TOKENS 65536
 #define WIDE_MAX_DECODE_BATCH 64

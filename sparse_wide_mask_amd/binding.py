@@ -9,6 +9,7 @@ import torch
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libwide.so")
 
 WIDE_OK, WIDE_EINVAL, WIDE_EUNSUPPORTED, WIDE_EWORKSPACE, WIDE_EHIP = range(5)
+WIDE_FLAG_FFN_TOKEN_SORT = 0x2
 WIDE_PREFILL, WIDE_DECODE = 0, 1
 
 _p = C.c_void_p
@@ -269,9 +270,11 @@ def ffn_masked_workspace(T, d_model, d_ff, n_groups, mode="prefill") -> int:
     return int(lib().wide_ffn_masked_workspace(T, d_model, d_ff, n_groups, _mode(mode)))
 
 
-def ffn_masked(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out=None, workspace=None):
+def ffn_masked(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out=None, workspace=None,
+               sort_tokens=False):
     """wide_ffn_masked.  X [T, d] bf16, mask [T, n] uint8, W_gate/W_up [F, d] bf16,
-    W_down_packed [n, d, G] bf16 (see pack_kmajor).  Returns Y [T, d] bf16."""
+    W_down_packed [n, d, G] bf16 (see pack_kmajor).  Returns Y [T, d] bf16.
+    sort_tokens: WIDE_FLAG_FFN_TOKEN_SORT."""
     for t, nm in ((X, "X"), (W_gate, "W_gate"), (W_up, "W_up"), (W_down_packed, "W_down_packed")):
         _dev(t, torch.bfloat16, nm)
     _dev(mask, torch.uint8, "mask")
@@ -287,7 +290,8 @@ def ffn_masked(X, mask, W_gate, W_up, W_down_packed, *, mode="prefill", out=None
     ws = _workspace(ws_bytes, X.device, workspace)
     Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
     st = lib().wide_ffn_masked(_ptr(X), _ptr(mask), _ptr(W_gate), _ptr(W_up), _ptr(W_down_packed),
-                               T, d, F, n, m, _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+                               T, d, F, n, m, _ptr(Y), _ptr(ws), ws.numel(),
+                               WIDE_FLAG_FFN_TOKEN_SORT if sort_tokens else 0, _stream())
     _check("wide_ffn_masked", st)
     return Y
 
@@ -450,9 +454,9 @@ def layer_masked_workspace(T, d_model, d_ff, n_ffn, n_q, n_kv, head_dim=128, rop
 
 def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, head_dim=128,
                  rope_theta=500000.0, eps=1e-5, mode="prefill", K_cache=None, V_cache=None,
-                 kv_len=0, out=None, workspace=None):
+                 kv_len=0, out=None, workspace=None, sort_ffn_tokens=False):
     """wide_layer_masked.  W: rms1, rms2 [d]; Wq, Wk, Wv; Wo_packed; W_gate, W_up;
-    W_down_packed (all bf16 device tensors)."""
+    W_down_packed (all bf16 device tensors).  sort_ffn_tokens: WIDE_FLAG_FFN_TOKEN_SORT."""
     _dev(X, torch.bfloat16, "X")
     _dev(attn_mask, torch.uint8, "attn_mask")
     _dev(ffn_mask, torch.uint8, "ffn_mask")
@@ -475,7 +479,8 @@ def layer_masked(X, attn_mask, ffn_mask, W: dict, *, n_q, n_kv, head_dim=128,
     Y = out if out is not None else torch.empty((T, d), dtype=torch.bfloat16, device=X.device)
     st = lib().wide_layer_masked(_ptr(X), _ptr(attn_mask), _ptr(ffn_mask), C.byref(wts),
                                  C.byref(cfg), T, m, _ptr(K_cache), _ptr(V_cache), kv_len, kv_cap,
-                                 _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+                                 _ptr(Y), _ptr(ws), ws.numel(),
+                                 WIDE_FLAG_FFN_TOKEN_SORT if sort_ffn_tokens else 0, _stream())
     _check("wide_layer_masked", st)
     return Y
 
@@ -492,9 +497,10 @@ def _layer_weights(W: dict):
 def layer_masked_routed(X, R_attn_packed, k_attn, R_ffn_packed, k_ffn, W: dict, *, n_q, n_kv,
                         n_ffn, head_dim=128, rope_theta=500000.0, eps=1e-5, mode="prefill",
                         K_cache=None, V_cache=None, kv_len=0, out=None, attn_mask=None,
-                        ffn_mask=None, workspace=None):
+                        ffn_mask=None, workspace=None, sort_ffn_tokens=False):
     """wide_layer_masked_routed: the layer with masks chosen on the GPU by two linear
-    routers on X (R_*_packed from pack_router).  Returns (Y, attn_mask, ffn_mask)."""
+    routers on X (R_*_packed from pack_router).  Returns (Y, attn_mask, ffn_mask).
+    sort_ffn_tokens: WIDE_FLAG_FFN_TOKEN_SORT."""
     _dev(X, torch.bfloat16, "X")
     _dev(R_attn_packed, torch.bfloat16, "R_attn_packed")
     _dev(R_ffn_packed, torch.bfloat16, "R_ffn_packed")
@@ -519,7 +525,9 @@ def layer_masked_routed(X, R_attn_packed, k_attn, R_ffn_packed, k_ffn, W: dict, 
                                                            device=X.device)
     st = lib().wide_layer_masked_routed(_ptr(X), C.byref(rt), C.byref(wts), C.byref(cfg), T, m,
                                         _ptr(K_cache), _ptr(V_cache), kv_len, kv_cap, _ptr(am),
-                                        _ptr(fm), _ptr(Y), _ptr(ws), ws.numel(), 0, _stream())
+                                        _ptr(fm), _ptr(Y), _ptr(ws), ws.numel(),
+                                        WIDE_FLAG_FFN_TOKEN_SORT if sort_ffn_tokens else 0,
+                                        _stream())
     _check("wide_layer_masked_routed", st)
     return Y, am, fm
 

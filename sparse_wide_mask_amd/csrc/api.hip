@@ -96,7 +96,10 @@ bool ffn_streaming(int T, int mode) { return mode == WIDE_DECODE && T <= kMaxDec
 FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
   FfnWs w;
   // streaming decode reorders inside its kernels
-  if (!ffn_streaming(T, mode)) w.rv = carve_reorder(c, T, n, ffn_down_tile_m(), false);
+  if (!ffn_streaming(T, mode)) {
+    w.rv = carve_reorder(c, T, n, ffn_down_tile_m(), false);
+    w.rv.order = c.take<int32_t>(T);  // the down projection's token order, when sorted
+  }
   w.H = c.take<uint16_t>((size_t)T * F);
   if (ffn_streaming(T, mode)) {
     w.kpart = c.take<float>(kmask_decode_part_floats(T, d, n, F / n));
@@ -104,16 +107,41 @@ FfnWs carve_ffn(Carver& c, int T, int d, int F, int n, int mode) {
   return w;
 }
 
+// The FFN mask's reorder job.  sort: the tokens are also sorted by the pattern of
+// their first groups (WIDE_FLAG_FFN_TOKEN_SORT) for the down projection, which then
+// computes its tiles' unions itself.
+MaskJob ffn_job(const uint8_t* mask, int T, int n, const FfnWs& w, bool packed_ready, bool sort) {
+  const ReorderView& v = w.rv;
+  MaskJob j;
+  j.mask = packed_ready ? nullptr : mask;
+  j.packed = v.packed;
+  j.n = n, j.nw = (n + 63) / 64, j.tile_m = v.tile_m;
+  j.count = v.count, j.perm = v.perm, j.rank = v.rank;
+  j.tile_count = sort ? nullptr : v.tile_count;
+  j.tile_groups = sort ? nullptr : v.tile_groups;
+  j.order = sort ? v.order : nullptr;
+  return j;
+}
+
 // reorder = false: the mask reorder of this call was already enqueued (by the
 // layer's norm + reorder launch, on the same stream)
 int ffn_run(const uint16_t* X, const uint8_t* mask, const uint16_t* Wg, const uint16_t* Wu,
             const uint16_t* Wdp, int T, int d, int F, int n, int mode, const uint16_t* residual,
-            uint16_t* Y, const FfnWs& w, hipStream_t s, bool reorder = true) {
+            uint16_t* Y, const FfnWs& w, hipStream_t s, bool reorder = true, bool sort = false) {
   if (ffn_streaming(T, mode)) {
     launch_ffn_decode(X, mask, Wg, Wu, Wdp, T, d, F, n, residual, w.H, w.kpart, Y, s);
   } else {
-    if (reorder) run_reorder(mask, T, n, w.rv, s);
-    launch_ffn_prefill(X, Wg, Wu, Wdp, w.rv, T, d, F, n, residual, w.H, Y, s);
+    if (reorder) {
+      const MaskJob j = ffn_job(mask, T, n, w, false, sort);
+      launch_reorder_jobs(T, &j, nullptr, nullptr, s);
+    }
+    ReorderView rv = w.rv;
+    if (sort) {
+      rv.tile_count = rv.tile_groups = nullptr;
+    } else {
+      rv.order = nullptr;
+    }
+    launch_ffn_prefill(X, Wg, Wu, Wdp, rv, T, d, F, n, residual, w.H, Y, s);
   }
   return WIDE_OK;
 }
@@ -198,17 +226,6 @@ MaskJob attn_job(const uint8_t* mask, int T, int nkv, const AttnWs& w, bool pack
   return j;
 }
 
-MaskJob ffn_job(const uint8_t* mask, int T, int n, const FfnWs& w, bool packed_ready) {
-  const ReorderView& v = w.rv;
-  MaskJob j;
-  j.mask = packed_ready ? nullptr : mask;
-  j.packed = v.packed;
-  j.n = n, j.nw = (n + 63) / 64, j.tile_m = v.tile_m;
-  j.count = v.count, j.perm = v.perm, j.rank = v.rank;
-  j.tile_count = v.tile_count, j.tile_groups = v.tile_groups;
-  return j;
-}
-
 void attn_reorder(const uint8_t* mask, int T, int nkv, const AttnWs& w, hipStream_t s,
                   bool packed_ready = false) {
   const MaskJob j = attn_job(mask, T, nkv, w, packed_ready);
@@ -282,11 +299,11 @@ struct LayerCache {
 int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_mask,
               const wide_layer_weights* W, const wide_layer_cfg* cfg, int T, int mode,
               const LayerCache& kv, uint16_t* Y, const LayerWs& w, hipStream_t s,
-              bool packed_ready) {
+              bool packed_ready, bool sort_ffn = false) {
   const int d = cfg->d_model, nkv = cfg->attn.n_kv_heads, n = cfg->n_ffn_groups;
   if (mode == WIDE_PREFILL) {
     const MaskJob aj = attn_job(attn_mask, T, nkv, w.attn, packed_ready);
-    const MaskJob fj = ffn_job(ffn_mask, T, n, w.ffn, packed_ready);
+    const MaskJob fj = ffn_job(ffn_mask, T, n, w.ffn, packed_ready, sort_ffn);
     NormJob nj;
     nj.x = X, nj.gamma = W->rms1, nj.d = d, nj.eps = cfg->rms_eps, nj.y = w.u;
     launch_reorder_jobs(T, &aj, &fj, &nj, s);
@@ -297,7 +314,7 @@ int layer_run(const uint16_t* X, const uint8_t* attn_mask, const uint8_t* ffn_ma
            kv.kv_len, kv.kv_cap, X, w.h, w.attn, s, kv.pair_len, kv.pos, false, kv.paged);
   launch_rmsnorm(w.h, W->rms2, T, d, cfg->rms_eps, w.u, s);
   ffn_run(w.u, ffn_mask, W->W_gate, W->W_up, W->W_down_packed, T, d, cfg->d_ff, n, mode, w.h, Y,
-          w.ffn, s, false);
+          w.ffn, s, false, sort_ffn);
   return launch_status();
 }
 
@@ -437,7 +454,7 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
                     size_t workspace_bytes, uint32_t flags, void* stream) {
   int st = ffn_check(T, d_model, d_ff, n_groups, mode);
   if (st != WIDE_OK) return st;
-  if (flags != 0) return WIDE_EINVAL;
+  if (flags & ~WIDE_FLAG_FFN_TOKEN_SORT) return WIDE_EINVAL;
   if (T == 0) return WIDE_OK;
   if (!aligned16(X) || !aligned16(mask) || !aligned16(W_gate) || !aligned16(W_up) ||
       !aligned16(W_down_packed) || !aligned16(Y) || (void*)Y == (void*)X)
@@ -450,7 +467,7 @@ int wide_ffn_masked(const uint16_t* X, const uint8_t* mask, const uint16_t* W_ga
   FfnWs w = carve_ffn(c, T, d_model, d_ff, n_groups, mode);
   (void)hipGetLastError();
   ffn_run(X, mask, W_gate, W_up, W_down_packed, T, d_model, d_ff, n_groups, mode, nullptr, Y, w,
-          as_stream(stream));
+          as_stream(stream), true, (flags & WIDE_FLAG_FFN_TOKEN_SORT) != 0);
   return launch_status();
 }
 
@@ -628,7 +645,7 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
                       void* workspace, size_t workspace_bytes, uint32_t flags, void* stream) {
   int st = layer_check(T, cfg, mode);
   if (st != WIDE_OK) return st;
-  if (flags != 0 || !W) return WIDE_EINVAL;
+  if ((flags & ~WIDE_FLAG_FFN_TOKEN_SORT) || !W) return WIDE_EINVAL;
   if (mode == WIDE_DECODE) {
     st = attn_decode_check(T, &cfg->attn, K_cache, V_cache, kv_len, kv_cap);
     if (st != WIDE_OK) return st;
@@ -646,7 +663,8 @@ int wide_layer_masked(const uint16_t* X, const uint8_t* attn_mask, const uint8_t
   LayerCache kv;
   kv.K = K_cache, kv.V = V_cache, kv.kv_len = kv_len, kv.kv_cap = kv_cap;
   (void)hipGetLastError();
-  return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, as_stream(stream), false);
+  return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, as_stream(stream), false,
+                   (flags & WIDE_FLAG_FFN_TOKEN_SORT) != 0);
 }
 
 int wide_layer_masked_routed(const uint16_t* X, const wide_layer_router* router,
@@ -657,7 +675,7 @@ int wide_layer_masked_routed(const uint16_t* X, const wide_layer_router* router,
                              void* stream) {
   int st = layer_check(T, cfg, mode);
   if (st != WIDE_OK) return st;
-  if (flags != 0 || !W || !router) return WIDE_EINVAL;
+  if ((flags & ~WIDE_FLAG_FFN_TOKEN_SORT) || !W || !router) return WIDE_EINVAL;
   const int nkv = cfg->attn.n_kv_heads, n = cfg->n_ffn_groups;
   if (router->k_attn < 0 || router->k_attn > nkv || router->k_ffn < 0 || router->k_ffn > n)
     return WIDE_EINVAL;
@@ -687,7 +705,8 @@ int wide_layer_masked_routed(const uint16_t* X, const wide_layer_router* router,
   launch_router_topk2(X, T, cfg->d_model, router->R_ffn_packed, n, router->k_ffn, ffn_mask,
                       prefill ? w.ffn.rv.packed : nullptr, router->R_attn_packed, nkv,
                       router->k_attn, attn_mask, prefill ? w.attn.rv.packed : nullptr, s);
-  return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, s, prefill);
+  return layer_run(X, attn_mask, ffn_mask, W, cfg, T, mode, kv, Y, w, s, prefill,
+                   (flags & WIDE_FLAG_FFN_TOKEN_SORT) != 0);
 }
 
 int wide_layer_decode_masked_cache(const uint16_t* X, const uint8_t* attn_mask,

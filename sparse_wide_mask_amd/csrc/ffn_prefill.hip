@@ -280,18 +280,49 @@ __global__ void __launch_bounds__(kGemmThreads, 1)
   }
   const int t0 = mt * BM, rows = min(BM, T - t0), n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, wm = wave / kGemmWN, wn = wave % kGemmWN;
-  const int ng = tcount[mt];
+  // tgroups null: the tile's union is the OR of its rows' mask words (tokens in a
+  // pattern order whose key ranges do not give the unions)
+  __shared__ uint32_t sU32[8];
+  __shared__ int sNg;
+  int ng = tgroups ? tcount[mt] : 0;
   // tile rows are tokens t0.. in order, or order[t0..] (tokens sorted by mask
   // pattern, so row blocks share dropped groups)
   for (int i = tid; i < BM; i += C::kThreads)
     sTok[i] = i < rows ? (order ? order[t0 + i] : t0 + i) : 0;
+  if (tid < 8) sU32[tid] = 0u;
   __syncthreads();
   for (int i = tid; i < BM * nw; i += C::kThreads) {
     const int r = i / nw, w = i % nw;
     sBits[r * 4 + w] = r < rows ? packed[(size_t)sTok[r] * nw + w] : 0ull;
   }
-  for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
-  __syncthreads();
+  if (tgroups) {
+    for (int i = tid; i < ng; i += C::kThreads) sGroups[i] = tgroups[(size_t)mt * n + i];
+    __syncthreads();
+  } else {
+    __syncthreads();
+    for (int w = 0; w < nw; ++w) {
+      uint64_t v = 0;
+      for (int r = tid; r < rows; r += C::kThreads) v |= sBits[r * 4 + w];
+      uint32_t lo = (uint32_t)v, hi = (uint32_t)(v >> 32);
+      for (int off = 32; off >= 1; off >>= 1) lo |= __shfl_xor(lo, off), hi |= __shfl_xor(hi, off);
+      if (lane == 0) {
+        if (lo) atomicOr(&sU32[2 * w], lo);
+        if (hi) atomicOr(&sU32[2 * w + 1], hi);
+      }
+    }
+    __syncthreads();
+    if (wave == 0) {  // ascending group list
+      int written = 0;
+      for (int w = 0; w < nw; ++w) {
+        const uint64_t u = ((uint64_t)sU32[2 * w + 1] << 32) | sU32[2 * w];
+        if ((u >> lane) & 1ull) sGroups[written + popc64(u & ((1ull << lane) - 1ull))] = 64 * w + lane;
+        written += popc64(u);
+      }
+      if (lane == 0) sNg = written;
+    }
+    __syncthreads();
+    ng = sNg;
+  }
   int nsg = ng;  // the tile's K units: groups, or pairs of groups when GPS == 2
   if constexpr (GPS == 2) {
     if (tid == 0) {  // ascending groups -> ascending distinct pairs, in place

@@ -36,7 +36,9 @@ struct ReorderView {
 // the packed words are the input (the router wrote them); otherwise they are
 // written.  tile_count / tile_groups null: no tile unions.  order non-null: also
 // the token order sorted by the whole pattern (n <= kSortMaxGroups), whose tiles'
-// unions then fill tile_count / tile_groups, and tile_perm (may be null).
+// unions then fill tile_count / tile_groups, and tile_perm (may be null); with
+// more groups, sorted by the pattern of the first kSortMaxGroups, and no unions
+// (the K-masked GEMM computes its tiles' unions from the rows' mask words).
 struct MaskJob {
   const uint8_t* mask = nullptr;
   uint64_t* packed = nullptr;

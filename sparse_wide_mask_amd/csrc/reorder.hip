@@ -198,7 +198,8 @@ WIDE_DEV void tile_union(const MaskJob& J, int T, int tile, uint32_t* sU) {
 }
 
 // Stable counting sort of the tokens by their whole pattern (n <= 8, pattern <
-// 256), patterns taken in reflected Gray-code order: the key of pattern p is its
+// 256; with more groups, by the pattern of the first 8), patterns taken in
+// reflected Gray-code order: the key of pattern p is its
 // rank k with k ^ (k >> 1) = p, so the patterns of neighbouring key ranges differ
 // in few groups and a tile that spans several ranges keeps a smaller union (top-4
 // of 8 groups at T = 8192: 5.66 instead of 6.16 groups per 256-token tile on
@@ -225,7 +226,17 @@ WIDE_DEV void token_sort(const MaskJob& J, int T, uint8_t* sKey, int (*sHist)[kS
     for (int u = 0; u < 4; ++u) {
       const int t = t0 + u * kRoThreads + tid;
       key[u] = 0u;
-      if (J.mask) {
+      if (J.mask && n % 8 == 0) {
+        // the first 8 bytes of the row in one load (rows start 8-byte aligned)
+        const uint32_t off = t < T ? (uint32_t)(t * n) : kSkip;
+        const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b32(mr, (int)off, 0, 0);
+        const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b32(mr, (int)(off + 4u), 0, 0);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          key[u] |= (((lo >> (8 * g)) & 0xffu) != 0u ? 1u : 0u) << g;
+          key[u] |= (((hi >> (8 * g)) & 0xffu) != 0u ? 1u : 0u) << (g + 4);
+        }
+      } else if (J.mask) {
         uint32_t b[8];
 #pragma unroll
         for (int g = 0; g < 8; ++g) b[g] = ldbuf1(mr, t < T && g < n ? (uint32_t)(t * n + g) : kSkip);
@@ -293,6 +304,10 @@ WIDE_DEV void token_sort(const MaskJob& J, int T, uint8_t* sKey, int (*sHist)[kS
       if ((same >> lane) == 1ull) sHist[wave][key] += popc64(same);
     }
   }
+  // More than 8 groups: the key is the pattern of the first 8 only, so a key range
+  // does not give its tokens' union; the K-masked GEMM that runs over this order
+  // ORs the mask words of its tile's rows itself (tile_count / tile_groups null).
+  if (n > kSortMaxGroups || !J.tile_groups) return;
   // tile unions from the key ranges: wave w takes tiles w, w + 16, ...
   const int n_tiles = (T + J.tile_m - 1) / J.tile_m;
   for (int tile = wave; tile < n_tiles; tile += kRoWaves) {

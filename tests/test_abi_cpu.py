@@ -65,6 +65,10 @@ def test_validation_before_any_launch(L):
     assert L.wide_ffn_masked(z, z, z, z, z, 8, 200, 1024, 16, 0, z, z, 0, 0, z) == 2
     assert L.wide_ffn_masked(z, z, z, z, z, 8, 256, 1024, 16, 7, z, z, 0, 0, z) == 1
     assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 0, z) == 0
+    # flags: the FFN token sort bit is taken, every other bit rejected
+    assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 2, z) == 0
+    assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 1, z) == 1
+    assert L.wide_ffn_masked(z, z, z, z, z, 0, 256, 1024, 16, 0, z, z, 0, 6, z) == 1
     assert L.wide_pack_kmajor(z, 4, 64, 256, z, z) == 1
     buf = C.c_void_p(16)  # aligned, never dereferenced: the shape is rejected first
     other = C.c_void_p(32)

@@ -13,12 +13,13 @@ from synth.workloads import ffn_case, ffn_prefill_3b, tiny_ffn
 from tests._gpu import TOL, bf16, dev, host, log, nan_bf16, needs_gpu, rel_err, u8
 
 
-def _gpu_ffn(c, mode="prefill"):
+def _gpu_ffn(c, mode="prefill", sort_tokens=False):
     n = c["mask"].shape[1]
     T, d = c["X"].shape
     Y = nan_bf16((T, d))
     wide.ffn_masked(bf16(c["X"]), u8(c["mask"]), bf16(c["W_gate"]), bf16(c["W_up"]),
-                    wide.pack_kmajor(bf16(c["W_down"]), n), mode=mode, out=Y)
+                    wide.pack_kmajor(bf16(c["W_down"]), n), mode=mode, out=Y,
+                    sort_tokens=sort_tokens)
     torch.cuda.synchronize()
     return host(Y)
 
@@ -102,6 +103,30 @@ def test_ffn_prefill_shapes(T, d, F, n, keep, kind):
     ref = ffn_masked(c["X"], c["mask"], c["W_gate"], c["W_up"], c["W_down"])
     if kind == "zeros":
         assert np.all(got == 0.0)
+    assert rel_err(got, ref) <= TOL
+
+
+@needs_gpu
+@pytest.mark.parametrize("T,d,F,n,keep,kind", [
+    (777, 384, 1536, 12, 0.25, "clustered"),   # 12 groups: key of the first 8
+    (2000, 256, 2048, 16, 0.5, "clustered"),
+    (257, 256, 2048, 64, 0.25, "clustered"),   # groups of 32: pairs per K slice
+    (1100, 512, 1024, 32, 0.75, "bernoulli"),
+    (600, 256, 2048, 8, 0.5, "bernoulli"),     # 8 groups: the whole pattern
+    (1, 256, 1024, 16, 0.5, "topk"),
+])
+def test_ffn_token_sort_bit_identical(T, d, F, n, keep, kind):
+    """WIDE_FLAG_FFN_TOKEN_SORT: the down projection over tokens sorted by their
+    first groups' pattern, each tile over the union of its own rows.  A token's
+    sum runs over its kept groups in ascending order in any tile, so the output
+    equals the unsorted call's bit for bit; and the oracle's within tolerance."""
+    dev()
+    log(f"ffn token sort T={T} d={d} F={F} n={n} keep={keep} {kind}")
+    c = ffn_case(f"ffn_sort_{T}_{d}_{F}_{n}_{kind}", T, d, F, n, keep, kind)
+    plain = _gpu_ffn(c)
+    got = _gpu_ffn(c, sort_tokens=True)
+    assert np.array_equal(got.view(np.uint32), plain.view(np.uint32))
+    ref = ffn_masked(c["X"], c["mask"], c["W_gate"], c["W_up"], c["W_down"])
     assert rel_err(got, ref) <= TOL
 
 

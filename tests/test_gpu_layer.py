@@ -104,6 +104,25 @@ def test_layer_prefill_asymmetric_keep():
 
 
 @needs_gpu
+@pytest.mark.parametrize("kind", ["clustered", "router"])
+def test_layer_prefill_8b_ffn_token_sort_bit_identical(kind):
+    """The benchmarked layer shape (T = 8192, 112 FFN groups of 128) with the FFN
+    token sort (WIDE_FLAG_FFN_TOKEN_SORT): every output element equals the
+    unsorted call's bit for bit (the unsorted output is checked against the oracle
+    row by row elsewhere); 16 sampled rows against the oracle as well."""
+    dev()
+    log(f"layer prefill 8B T=8192 {kind} with the FFN token sort")
+    c = layer_8b(8192, kind=kind, keep=0.5)
+    W = gpu_weights(c)
+    plain = gpu_layer(c, W)
+    got = gpu_layer(c, W, sort_ffn_tokens=True)
+    assert np.array_equal(got.view(np.uint32), plain.view(np.uint32))
+    rows = np.sort(np.random.default_rng(9).choice(8192, 16, replace=False))
+    ref = oracle_layer(c, rows=rows)
+    assert rel_err(got[rows], ref) <= TOL
+
+
+@needs_gpu
 def test_layer_all_zero_masks_is_identity():
     dev()
     c = layer_case("layer_zero", 300, 256, 1024, 8, 8, 2, 128, 0.0, "zeros")

@@ -96,6 +96,23 @@ def test_routed_layer_prefill(T, d, F, n_ffn, n_q, n_kv, k_attn, k_ffn):
 
 
 @needs_gpu
+def test_routed_layer_prefill_ffn_token_sort_bit_identical():
+    """The router-fed layer with the FFN token sort (WIDE_FLAG_FFN_TOKEN_SORT; the
+    sort keys come from the router's packed words): the same masks and the same
+    output bit for bit as without it."""
+    dev()
+    T, d, F, n_ffn, n_q, n_kv = 700, 256, 2048, 16, 8, 2
+    log(f"routed layer prefill T={T} n_ffn={n_ffn} with the FFN token sort")
+    tag = "routed_sort"
+    c = layer_case(tag, T, d, F, n_ffn, n_q, n_kv, 128, 0.5, "router")
+    R_attn, R_ffn = _routers(c, tag, n_kv, n_ffn, d)
+    Y0, am0, fm0 = _routed(c, R_attn, R_ffn, 1, 8)
+    Y1, am1, fm1 = _routed(c, R_attn, R_ffn, 1, 8, sort_ffn_tokens=True)
+    assert torch.equal(am0, am1) and torch.equal(fm0, fm1)
+    assert torch.equal(Y0.view(torch.int16), Y1.view(torch.int16))
+
+
+@needs_gpu
 def test_routed_layer_prefill_llama31_8b_sampled():
     """Llama-3.1-8B layer at T = 8192 with the routers on the GPU (keep 4 of 8 head
     groups and 56 of 112 FFN groups): masks bit-exact against the standalone router,
