@@ -9,7 +9,8 @@
 // launch: every role reads the mask bytes, or the packed words when those are the
 // input; a mask of more than 4 MB is packed by a launch of its own first):
 //   sort    one work-group per sorted mask: a stable counting sort of the tokens
-//           by their pattern (n <= 8) and the unions of tiles of that order;
+//           by their pattern (n <= 8) and the unions of tiles of that order; with
+//           more groups by the pattern of the first 8, without unions;
 //   groups  one per group: chunks of 64 tokens (lane = token), a ballot per chunk,
 //           a scan over the waves, then each lane places its token by mbcnt;
 //   unions  one per token tile: the OR of the tile's keep bits, compacted into an
